@@ -1,0 +1,457 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test fixes part of the oracle against something other than itself: the
+pages' printed example, closed forms that follow from the definitions, textbook
+identities, brute force on tiny inputs, and an independent FFT library
+(numpy's pocketfft).  ``test_planted_mistakes_are_caught`` builds throw-away
+copies of the C oracle with one plausible mistake planted each and checks that
+these pins reject every one of them.
+"""
+import cmath
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def rel_rms(y, ref):
+    y = np.asarray(y, dtype=np.complex128)
+    ref = np.asarray(ref, dtype=np.complex128)
+    return float(np.linalg.norm((y - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+
+
+def crand(rng, *shape):
+    return rng.standard_normal(shape) + 1j * rng.standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# The pages' printed examples and statements
+# --------------------------------------------------------------------------
+
+def test_bitrev_matches_printed_order():
+    (row,) = _golden_rows("bitrev8.txt")
+    assert oracle.bitrev_order(8) == [int(v) for v in row]
+
+
+def test_bitrev_is_the_repeated_even_odd_split():
+    # The page derives the order by splitting into evens and odds recursively.
+    def split(seq):
+        if len(seq) == 1:
+            return seq
+        return split(seq[0::2]) + split(seq[1::2])
+    for n in (1, 2, 4, 8, 16, 64, 256):
+        assert oracle.bitrev_order(n) == split(list(range(n)))
+
+
+def test_butterfly_pairing_at_half_2():
+    rows = _golden_rows("butterfly_pairing_half2.txt")
+    # Probe each thread with a unit impulse at its own index: a lower member
+    # reads itself as `a` and returns a + w*0 = 1, an upper member reads itself
+    # as `b` and returns 0 - w*1 = -w.
+    half = 2
+    for i, j in ((int(r[0]), int(r[1])) for r in rows):
+        x = [0j] * 8
+        x[i] = 1.0
+        out = oracle.butterfly_pass_half(x, half)
+        if j == 0:
+            assert out[i] == 1.0            # a + w*0 with a = x[i]
+        else:
+            r = i % half
+            w = cmath.exp(-1j * math.pi * r / half)
+            assert abs(out[i] - (-w)) < 1e-15   # 0 - w*b with b = x[i]
+
+
+def test_butterfly_pair_members_share_inputs_and_twiddle():
+    # Both members of a pair read the same two elements and the same w; they
+    # differ only in the sign (page "The Butterfly", pairing paragraph).
+    rng = np.random.default_rng(0)
+    x = list(crand(rng, 8))
+    for half in (1, 2, 4):
+        out = oracle.butterfly_pass_half(x, half)
+        for i in range(8):
+            j = (i // half) % 2
+            partner = i + half if j == 0 else i - half
+            lo, hi = (i, partner) if j == 0 else (partner, i)
+            a, b = x[lo], x[lo + half]
+            # out_lo + out_hi = 2a and out_lo - out_hi = 2 w b for one w
+            assert abs(out[lo] + out[hi] - 2 * a) < 1e-13
+            w = (out[lo] - out[hi]) / (2 * b)
+            assert abs(abs(w) - 1) < 1e-13
+            assert abs(w - cmath.exp(-1j * math.pi * (lo % half) / half)) < 1e-13
+
+
+def test_butterfly_half_1_is_pure_add_sub_and_sign_shows_at_half_2():
+    rng = np.random.default_rng(1)
+    x = list(crand(rng, 8))
+    out = oracle.butterfly_pass_half(x, 1)
+    for p in range(0, 8, 2):
+        assert out[p] == x[p] + x[p + 1]
+        assert out[p + 1] == x[p] - x[p + 1]
+    # A flipped twiddle sign is invisible at half = 1 and visible at half = 2, 4
+    # (page "The Butterfly", Hint 2).
+    flipped = oracle.butterfly_pass_half(x, 1, twiddle_sign=+1.0)
+    assert np.allclose(flipped, out, atol=1e-15)
+    for half in (2, 4):
+        good = np.array(oracle.butterfly_pass_half(x, half))
+        bad = np.array(oracle.butterfly_pass_half(x, half, twiddle_sign=+1.0))
+        assert np.max(np.abs(good - bad)) > 0.1
+
+
+def test_butterfly_chain_is_the_8_point_dft_and_counts_twelve_butterflies():
+    (row,) = _golden_rows("butterfly_count.txt")
+    n, passes, butterflies = (int(v) for v in row)
+    rng = np.random.default_rng(2)
+    x = list(crand(rng, n))
+    y = [x[i] for i in oracle.bitrev_order(n)]
+    count = 0
+    half = 1
+    while half < n:
+        y = oracle.butterfly_pass_half(y, half)
+        count += n // 2   # one butterfly per pair: n/2 pairs per pass
+        half *= 2
+    assert count == butterflies and int(math.log2(n)) == passes
+    assert rel_rms(y, np.fft.fft(x)) < 1e-15
+    assert rel_rms(y, oracle.dft_py(x)) < 1e-15
+    # The chain with the twiddle sign flipped throughout is N times the inverse.
+    z = [x[i] for i in oracle.bitrev_order(n)]
+    half = 1
+    while half < n:
+        z = oracle.butterfly_pass_half(z, half, twiddle_sign=+1.0)
+        half *= 2
+    assert rel_rms(z, n * np.fft.ifft(x)) < 1e-15
+    assert rel_rms(z, np.fft.fft(x)) > 0.5
+
+
+def test_butterfly_chain_dft_larger_n():
+    rng = np.random.default_rng(3)
+    for n in (2, 4, 16, 32, 64):
+        x = list(crand(rng, n))
+        y = [x[i] for i in oracle.bitrev_order(n)]
+        half = 1
+        while half < n:
+            y = oracle.butterfly_pass_half(y, half)
+            half *= 2
+        assert rel_rms(y, np.fft.fft(x)) < 1e-14
+
+
+def test_stockham_passes_give_the_dft_in_natural_order():
+    # M = log2 N passes of the page's Stockham stage, from natural-order input,
+    # with no bit-reversal anywhere.
+    rng = np.random.default_rng(4)
+    for m in range(1, 7):
+        n = 1 << m
+        x = list(crand(rng, n))
+        y = x
+        for s in range(m):
+            y = oracle.stockham_pass(y, s)
+        assert rel_rms(y, np.fft.fft(x)) < 1e-14
+        assert rel_rms(y, oracle.dft_py(x)) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# The DFT definition: closed forms and brute force
+# --------------------------------------------------------------------------
+
+def test_dft4_worked_example():
+    rows = [[float(v) for v in r] for r in _golden_rows("dft4_worked.txt")]
+    x = [complex(r[1], r[2]) for r in rows]
+    X = [complex(r[3], r[4]) for r in rows]
+    assert np.allclose(oracle.dft_py(x), X, atol=1e-13)
+    assert np.allclose(oracle.dft(np.array(x)), X, atol=1e-13)
+    assert np.allclose(oracle.fft(np.array(x)), X, atol=1e-13)
+
+
+@pytest.mark.parametrize("fn", ["dft_py", "dft", "fft"])
+def test_closed_forms(fn):
+    f = {"dft_py": lambda v: np.array(oracle.dft_py(v)),
+         "dft": lambda v: oracle.dft(np.asarray(v)),
+         "fft": lambda v: oracle.fft(np.asarray(v))}[fn]
+    for n in (1, 2, 4, 8, 16, 64, 256):
+        if fn == "dft_py" and n > 64:
+            continue
+        k = np.arange(n)
+        # delta at 0 -> all ones
+        d = np.zeros(n, complex)
+        d[0] = 1
+        assert np.allclose(f(d), np.ones(n), atol=1e-13)
+        # delta at m -> w^{mk}, w = e^{-2 pi i / N}
+        for m in sorted({0, min(1, n - 1), n // 2, n - 1}):
+            d = np.zeros(n, complex)
+            d[m] = 1
+            ref = np.exp(-2j * np.pi * ((m * k) % n) / n)
+            assert np.allclose(f(d), ref, atol=1e-13)
+        # constant c -> N c at bin 0, zero elsewhere
+        c = 0.75 - 0.25j
+        ref = np.zeros(n, complex)
+        ref[0] = n * c
+        assert np.allclose(f(np.full(n, c)), ref, atol=1e-12 * n)
+        # single tone e^{2 pi i f n / N} -> N at bin f
+        for fr in sorted({0, min(1, n - 1), n // 2, n - 1}):
+            tone = np.exp(2j * np.pi * ((fr * k) % n) / n)
+            ref = np.zeros(n, complex)
+            ref[fr] = n
+            assert np.allclose(f(tone), ref, atol=1e-11 * n)
+
+
+def test_small_sizes_exact():
+    # N = 1 is the identity; N = 2 is [a + b, a - b].
+    for f in (oracle.dft, oracle.fft):
+        assert f(np.array([3 - 2j]))[0] == 3 - 2j
+        out = f(np.array([1 + 2j, 3 - 1j]))
+        assert np.allclose(out, [4 + 1j, -2 + 3j], atol=0)
+
+
+def test_direct_dft_matches_brute_force_and_numpy():
+    rng = np.random.default_rng(5)
+    for n in (1, 3, 5, 7, 8, 12, 31, 64, 100):
+        x = crand(rng, n)
+        assert rel_rms(oracle.dft(x), oracle.dft_py(x)) < 1e-13
+        assert rel_rms(oracle.dft(x), np.fft.fft(x)) < 1e-13
+        assert rel_rms(oracle.dft(x, inverse=True), np.fft.ifft(x)) < 1e-13
+
+
+def test_radix2_matches_direct_dft():
+    rng = np.random.default_rng(6)
+    for m in range(0, 9):
+        n = 1 << m
+        x = crand(rng, 3, n)
+        assert rel_rms(oracle.fft(x), oracle.dft(x)) < 1e-13
+        assert rel_rms(oracle.ifft(x), oracle.dft(x, inverse=True)) < 1e-13
+
+
+@pytest.mark.parametrize("n,batch", [(1024, 8), (2048, 4), (4096, 4), (8192, 2),
+                                     (1 << 16, 1), (1 << 19, 1)])
+def test_radix2_matches_numpy(n, batch):
+    rng = np.random.default_rng(n)
+    x = crand(rng, batch, n)
+    err = max(rel_rms(oracle.fft(x)[b], np.fft.fft(x[b])) for b in range(batch))
+    assert err < 1e-15 * math.log2(n) * 10
+    err = max(rel_rms(oracle.ifft(x)[b], np.fft.ifft(x[b])) for b in range(batch))
+    assert err < 1e-15 * math.log2(n) * 10
+
+
+def test_radix2_large_single_transform_matches_numpy():
+    # The single large transform (2^24 points) takes the threaded top levels.
+    n = 1 << 24
+    rng = np.random.default_rng(7)
+    x = (rng.random(n) * 2 - 1) + 1j * (rng.random(n) * 2 - 1)
+    err = rel_rms(oracle.fft(x), np.fft.fft(x))
+    assert err < 1e-14
+
+
+def test_identities():
+    rng = np.random.default_rng(8)
+    n = 512
+    x, y = crand(rng, n), crand(rng, n)
+    a, b = 0.3 - 1.1j, -2.0 + 0.5j
+    X, Y = oracle.fft(x), oracle.fft(y)
+    # linearity
+    assert rel_rms(oracle.fft(a * x + b * y), a * X + b * Y) < 1e-14
+    # Parseval: sum |x|^2 = (1/N) sum |X|^2
+    assert abs(np.sum(abs(x) ** 2) - np.sum(abs(X) ** 2) / n) < 1e-10 * np.sum(abs(x) ** 2)
+    # round trip
+    assert rel_rms(oracle.ifft(X), x) < 1e-15
+    assert rel_rms(oracle.fft(oracle.ifft(x)), x) < 1e-15
+    # conjugate symmetry for real input: X_{N-k} = conj(X_k)
+    r = rng.standard_normal(n)
+    R = oracle.fft(r)
+    assert np.allclose(R[1:][::-1], np.conj(R[1:]), atol=1e-11)
+    assert abs(R[0].imag) < 1e-12 and abs(R[n // 2].imag) < 1e-12
+    # shift theorem: x[(t - m) mod N] -> X_k w^{mk}
+    m = 37
+    k = np.arange(n)
+    assert rel_rms(oracle.fft(np.roll(x, m)), X * np.exp(-2j * np.pi * ((m * k) % n) / n)) < 1e-13
+    # modulation: x_t e^{2 pi i f t / N} -> X_{k - f}
+    f = 11
+    mod = x * np.exp(2j * np.pi * ((f * k) % n) / n)
+    assert rel_rms(oracle.fft(mod), np.roll(X, f)) < 1e-13
+
+
+def test_precision_widening_is_exact():
+    rng = np.random.default_rng(9)
+    x32 = (rng.standard_normal(64) + 1j * rng.standard_normal(64)).astype(np.complex64)
+    assert np.array_equal(oracle.fft(x32), oracle.fft(x32.astype(np.complex128)))
+
+
+# --------------------------------------------------------------------------
+# 2D
+# --------------------------------------------------------------------------
+
+def test_fft2_matches_numpy_and_separability():
+    rng = np.random.default_rng(10)
+    for h, w in ((1, 8), (8, 1), (4, 16), (32, 8), (64, 64)):
+        x = crand(rng, 2, h, w)
+        assert rel_rms(oracle.fft2(x), np.fft.fft2(x)) < 1e-14
+        assert rel_rms(oracle.ifft2(x), np.fft.ifft2(x)) < 1e-14
+        assert rel_rms(oracle.ifft2(oracle.fft2(x)), x) < 1e-14
+    u, v = crand(rng, 16), crand(rng, 32)
+    assert rel_rms(oracle.fft2(np.outer(u, v)), np.outer(np.fft.fft(u), np.fft.fft(v))) < 1e-14
+
+
+def test_fft2_plane_waves_closed_form():
+    from fft_convolution_amd import workloads as wl
+    h, w = 64, 32
+    img, (fy, fx, phi) = wl.plane_waves_2d(h, w, 2, seed=4, noise_std=0.0,
+                                           dtype=np.complex128, with_params=True)
+    X = oracle.fft2(img)
+    for b in range(2):
+        ref = np.zeros((h, w), complex)
+        for m in range(16):
+            ref[fy[b, m], fx[b, m]] += h * w * np.exp(1j * phi[b, m])
+        assert np.max(np.abs(X[b] - ref)) < 1e-9 * h * w
+    # With the 0.01 noise the 16 largest bins are still exactly the waves.
+    noisy, (fy, fx, _) = wl.plane_waves_2d(h, w, 2, seed=4, with_params=True)
+    X = np.abs(oracle.fft2(noisy))
+    for b in range(2):
+        top = set(np.argsort(X[b].ravel())[-16:].tolist())
+        assert top == set((fy[b] * w + fx[b]).tolist())
+
+
+# --------------------------------------------------------------------------
+# Polynomial multiplication
+# --------------------------------------------------------------------------
+
+def test_polymul_worked_example():
+    rows = {r[0]: [int(v) for v in r[1:]] for r in _golden_rows("polymul_worked.txt")}
+    a, b, c = rows["a"], rows["b"], rows["c"]
+    assert oracle.schoolbook(a, b)[0].tolist() == c
+    assert oracle.polymul_fft(a, b)[0][0].tolist() == c
+
+
+def test_polymul_tiny_exhaustive_against_schoolbook():
+    rng = np.random.default_rng(11)
+    for la in list(range(1, 12)) + [31, 64]:
+        for lb in (1, 2, 3, 7, 16, 33, 64):
+            a = rng.integers(-1000, 1000, size=(2, la))
+            b = rng.integers(-1000, 1000, size=(2, lb))
+            ref = oracle.schoolbook(a, b)
+            # schoolbook itself against numpy's integer convolution
+            for p in range(2):
+                assert np.array_equal(ref[p], np.convolve(a[p], b[p]))
+            c, resid = oracle.polymul_fft(a, b)
+            assert np.array_equal(c, ref)
+            assert resid < 1e-6
+
+
+def test_polymul_closed_forms():
+    L = 1 << 10
+    k = np.arange(2 * L - 1)
+    tri = np.minimum(k + 1, 2 * L - 1 - k)
+    ones = np.ones(L, np.int64)
+    c, _ = oracle.polymul_fft(ones, ones)
+    assert np.array_equal(c[0], tri)
+    n999 = np.full(L, 999, np.int64)
+    c, _ = oracle.polymul_fft(n999, n999)
+    assert np.array_equal(c[0], 999 * 999 * tri)
+    # (1 + x)^p (1 + x)^q = (1 + x)^{p+q}: binomial coefficients
+    p, q = 20, 13
+    ap = [math.comb(p, i) for i in range(p + 1)]
+    aq = [math.comb(q, i) for i in range(q + 1)]
+    c, _ = oracle.polymul_fft(ap, aq)
+    assert c[0].tolist() == [math.comb(p + q, i) for i in range(p + q + 1)]
+
+
+def test_polymul_invariants_and_mod_p_at_scale():
+    # Pairs of the full coefficient count at reduced batch; every coefficient
+    # is covered by the evaluation at random z mod p (Schwartz-Zippel).
+    from fft_convolution_amd import workloads as wl
+    a, b = wl.random_polys(1 << 18, 2, seed=5)
+    c, resid = oracle.polymul_fft(a, b, n=1 << 19)
+    assert c.shape == (2, (1 << 19) - 1)
+    assert resid < 0.1
+    for p in range(2):
+        assert int(c[p].sum()) == int(a[p].sum()) * int(b[p].sum())
+        alt = lambda v: int(v[0::2].sum()) - int(v[1::2].sum())
+        assert alt(c[p]) == alt(a[p]) * alt(b[p])
+        rng = np.random.default_rng(100 + p)
+        for _ in range(2):
+            z = int(rng.integers(2, oracle.MOD_P - 1))
+            assert oracle.poly_eval_mod(c[p], z) == \
+                oracle.poly_eval_mod(a[p], z) * oracle.poly_eval_mod(b[p], z) % oracle.MOD_P
+    ks = np.array([0, 1, (1 << 18) - 1, 1 << 18, (1 << 19) - 3, (1 << 19) - 2])
+    s = oracle.schoolbook_sample(a, b, ks)
+    assert np.array_equal(s, c[:, ks])
+
+
+def test_schoolbook_sample_matches_full():
+    rng = np.random.default_rng(12)
+    a = rng.integers(0, 1000, size=(3, 40))
+    b = rng.integers(0, 1000, size=(3, 25))
+    full = oracle.schoolbook(a, b)
+    ks = np.array([0, 5, 24, 39, 63])
+    assert np.array_equal(oracle.schoolbook_sample(a, b, ks), full[:, ks])
+    with pytest.raises(ValueError):
+        oracle.schoolbook_sample(a, b, np.array([64]))
+
+
+# --------------------------------------------------------------------------
+# The pins reject plausible mistakes planted in throw-away copies of the oracle
+# --------------------------------------------------------------------------
+
+def _build_mutant(tmp_path, macro):
+    src = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+    so = str(tmp_path / ("mut_%s.so" % macro))
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-D" + macro, "-o", so, src, "-lm"], check=True)
+    lib = ctypes.CDLL(so)
+    lib.oracle_fft.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                               ctypes.c_int64, ctypes.c_int]
+    lib.oracle_polymul_fft.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.POINTER(ctypes.c_double)]
+    return lib
+
+
+def _pins_hold(lib):
+    """The closed-form and round-trip pins, run on a given build."""
+    def fft(x, inv=False):
+        x = np.ascontiguousarray(x, np.complex128)
+        out = np.empty_like(x)
+        assert lib.oracle_fft(x.ctypes.data, out.ctypes.data, x.shape[-1],
+                              x.size // x.shape[-1], int(inv)) == 0
+        return out
+    n = 64
+    k = np.arange(n)
+    for fr in (1, 5):
+        tone = np.exp(2j * np.pi * ((fr * k) % n) / n)
+        ref = np.zeros(n, complex)
+        ref[fr] = n
+        if not np.allclose(fft(tone), ref, atol=1e-9):
+            return False
+    rng = np.random.default_rng(0)
+    x = crand(rng, n)
+    if rel_rms(fft(fft(x), inv=True), x) > 1e-12:
+        return False
+    a = rng.integers(0, 1000, size=(1, 37))
+    b = rng.integers(0, 1000, size=(1, 20))
+    c = np.empty((1, 56), np.int64)
+    r = ctypes.c_double()
+    assert lib.oracle_polymul_fft(a.ctypes.data, 37, b.ctypes.data, 20, c.ctypes.data,
+                                  64, 1, ctypes.byref(r)) == 0
+    return np.array_equal(c[0], np.convolve(a[0], b[0]))
+
+
+def test_planted_mistakes_are_caught(tmp_path):
+    clean = _build_mutant(tmp_path, "ORACLE_NO_PLANT")
+    assert _pins_hold(clean)
+    for macro in ("ORACLE_PLANT_TWIDDLE_SIGN", "ORACLE_PLANT_NO_INVERSE_SCALE",
+                  "ORACLE_PLANT_TWIDDLE_STEP", "ORACLE_PLANT_CONJ_PRODUCT",
+                  "ORACLE_PLANT_POLY_SHIFT"):
+        assert not _pins_hold(_build_mutant(tmp_path, macro)), macro
