@@ -1,0 +1,298 @@
+"""Python binding of ``libfftmi.so``, the MI355X (gfx950) power-of-two FFT library.
+
+The functions below carry the names of the C ABI in ``include/fftmi.h`` and do
+argument marshalling only: device pointers come from PyTorch tensors (or plain
+integers), streams from ``torch.cuda.current_stream()``, and every step of a
+transform runs in the library's HIP kernels.  A nonzero status raises
+:class:`FFTError`.  There is no fallback: if the library is not built, or a
+call fails, the error propagates.
+
+Thin conveniences built on those calls:
+
+* :class:`Plan` -- owns a plan handle; ``fft``/``ifft`` (rank 1), ``fft2``/``ifft2``
+  (rank 2) and ``poly_mul`` (rank 1, complex128) on contiguous device tensors.
+* :func:`poly_mul` -- one-shot integer polynomial products.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "FFTError", "FFT_C32", "FFT_C64", "FFT_FORWARD", "FFT_INVERSE",
+    "FFT_OK", "FFT_ERR_INVALID_ARG", "FFT_ERR_NOT_POW2", "FFT_ERR_UNSUPPORTED_SIZE",
+    "FFT_ERR_PRECISION", "FFT_ERR_RANK", "FFT_ERR_ALIGN", "FFT_ERR_OVERLAP",
+    "FFT_ERR_WORKSPACE", "FFT_ERR_DEVICE",
+    "FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64", "FFT_MAX_N_C32", "FFT_MAX_N_C64",
+    "lib", "lib_path", "EXPORTS",
+    "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
+    "fft_exec_c2c", "fft_exec_2d", "fft_poly_mul_workspace_size", "fft_poly_mul",
+    "fft_status_string", "fft_last_error",
+    "Plan", "poly_mul",
+]
+
+FFT_C32, FFT_C64 = 0, 1
+FFT_FORWARD, FFT_INVERSE = 0, 1
+FFT_OK = 0
+FFT_ERR_INVALID_ARG = -1
+FFT_ERR_NOT_POW2 = -2
+FFT_ERR_UNSUPPORTED_SIZE = -3
+FFT_ERR_PRECISION = -4
+FFT_ERR_RANK = -5
+FFT_ERR_ALIGN = -6
+FFT_ERR_OVERLAP = -7
+FFT_ERR_WORKSPACE = -8
+FFT_ERR_DEVICE = -9
+FFT_MAX_LDS_N_C32 = 8192
+FFT_MAX_LDS_N_C64 = 4096
+FFT_MAX_N_C32 = 1 << 26
+FFT_MAX_N_C64 = 1 << 24
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libfftmi.so")
+
+# Every symbol include/fftmi.h declares.
+EXPORTS = (
+    "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
+    "fft_exec_c2c", "fft_exec_2d", "fft_poly_mul_workspace_size", "fft_poly_mul",
+    "fft_status_string", "fft_last_error",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FFTError(RuntimeError):
+    """A nonzero status from the library."""
+
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = "%s failed: %s" % (where, fft_status_string(status))
+        if detail:
+            msg += " (%s)" % detail
+        super().__init__(msg)
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(lib_path):
+            raise ImportError(
+                "libfftmi.so is not built (expected at %s); run "
+                "`python -m fft_convolution_amd.build`" % lib_path)
+        L = ctypes.CDLL(lib_path)
+        vp, i64, c_int, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.fft_plan_create.argtypes = [ctypes.POINTER(vp), c_int, ctypes.POINTER(i64), c_int]
+        L.fft_plan_destroy.argtypes = [vp]
+        L.fft_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
+        L.fft_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
+        L.fft_exec_c2c.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
+        L.fft_exec_2d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
+        L.fft_poly_mul_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
+        L.fft_poly_mul.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, vp, vp]
+        L.fft_status_string.argtypes = [c_int]
+        L.fft_status_string.restype = ctypes.c_char_p
+        L.fft_last_error.argtypes = []
+        L.fft_last_error.restype = ctypes.c_char_p
+        for name in EXPORTS[:-2]:
+            getattr(L, name).restype = c_int
+        _lib = L
+        return L
+
+
+def _ptr(x) -> int | None:
+    """Device address of a tensor, or an integer address, or None for NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr() or None
+    raise TypeError("expected a tensor, an integer address or None, got %r" % type(x))
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _check(status: int, where: str) -> None:
+    if status != FFT_OK:
+        raise FFTError(status, where, fft_last_error())
+
+
+def fft_status_string(status: int) -> str:
+    return lib().fft_status_string(int(status)).decode()
+
+
+def fft_last_error() -> str:
+    return lib().fft_last_error().decode()
+
+
+def fft_plan_create(rank: int, dims, prec: int = FFT_C32) -> int:
+    """Create a plan (rank 1: dims = [N]; rank 2: dims = [H, W]); returns its handle."""
+    dims = [int(d) for d in dims]
+    arr = (ctypes.c_int64 * max(len(dims), 1))(*dims)
+    h = ctypes.c_void_p()
+    _check(lib().fft_plan_create(ctypes.byref(h), int(rank), arr if dims else None, int(prec)),
+           "fft_plan_create")
+    return h.value
+
+
+def fft_plan_destroy(plan) -> None:
+    _check(lib().fft_plan_destroy(plan), "fft_plan_destroy")
+
+
+def fft_plan_describe(plan) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fft_plan_describe(plan, buf, 256), "fft_plan_describe")
+    return buf.value.decode()
+
+
+def fft_workspace_size(plan, batch: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().fft_workspace_size(plan, int(batch), ctypes.byref(out)), "fft_workspace_size")
+    return out.value
+
+
+def fft_exec_c2c(plan, dir: int, in_, out, batch: int, workspace=None, stream=None) -> None:
+    _check(lib().fft_exec_c2c(plan, int(dir), _ptr(in_), _ptr(out), int(batch), _ptr(workspace),
+                              _stream(stream)), "fft_exec_c2c")
+
+
+def fft_exec_2d(plan, dir: int, in_, out, batch: int, workspace=None, stream=None) -> None:
+    _check(lib().fft_exec_2d(plan, int(dir), _ptr(in_), _ptr(out), int(batch), _ptr(workspace),
+                             _stream(stream)), "fft_exec_2d")
+
+
+def fft_poly_mul_workspace_size(plan, batch: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().fft_poly_mul_workspace_size(plan, int(batch), ctypes.byref(out)),
+           "fft_poly_mul_workspace_size")
+    return out.value
+
+
+def fft_poly_mul(plan, a, la: int, b, lb: int, c, batch: int, workspace=None,
+                 d_max_residual=None, stream=None) -> None:
+    _check(lib().fft_poly_mul(plan, _ptr(a), int(la), _ptr(b), int(lb), _ptr(c), int(batch),
+                              _ptr(workspace), _ptr(d_max_residual), _stream(stream)),
+           "fft_poly_mul")
+
+
+# --------------------------------------------------------------------------
+# Conveniences over torch tensors (allocation and shape checks only)
+# --------------------------------------------------------------------------
+
+class Plan:
+    """A plan handle.  ``Plan(n)`` or ``Plan((h, w))``; dtype torch.complex64/128."""
+
+    def __init__(self, dims, dtype=None):
+        import torch
+        if dtype is None:
+            dtype = torch.complex64
+        if dtype not in (torch.complex64, torch.complex128):
+            raise TypeError("dtype must be torch.complex64 or torch.complex128")
+        self.dtype = dtype
+        self.prec = FFT_C32 if dtype == torch.complex64 else FFT_C64
+        self.dims = (int(dims),) if isinstance(dims, int) else tuple(int(d) for d in dims)
+        self.rank = len(self.dims)
+        self.handle = fft_plan_create(self.rank, self.dims, self.prec)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                fft_plan_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+    def describe(self) -> str:
+        return fft_plan_describe(self.handle)
+
+    def _check_tensor(self, x):
+        import torch
+        if not isinstance(x, torch.Tensor) or not x.is_cuda:
+            raise TypeError("expected a device tensor")
+        if x.dtype != self.dtype:
+            raise TypeError("expected %s, got %s" % (self.dtype, x.dtype))
+        if not x.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        if tuple(x.shape[-self.rank:]) != self.dims:
+            raise ValueError("trailing dims %s do not match the plan %s" % (tuple(x.shape), self.dims))
+        n = 1
+        for d in self.dims:
+            n *= d
+        return x.numel() // n
+
+    def _exec(self, x, out, direction, fn):
+        import torch
+        batch = self._check_tensor(x)
+        if out is None:
+            out = torch.empty_like(x)
+        else:
+            self._check_tensor(out)
+        ws_bytes = fft_workspace_size(self.handle, batch)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
+        fn(self.handle, direction, x, out, batch, ws)
+        return out
+
+    def fft(self, x, out=None):
+        if self.rank != 1:
+            raise ValueError("fft needs a rank-1 plan")
+        return self._exec(x, out, FFT_FORWARD, fft_exec_c2c)
+
+    def ifft(self, x, out=None):
+        if self.rank != 1:
+            raise ValueError("ifft needs a rank-1 plan")
+        return self._exec(x, out, FFT_INVERSE, fft_exec_c2c)
+
+    def fft2(self, x, out=None):
+        if self.rank != 2:
+            raise ValueError("fft2 needs a rank-2 plan")
+        return self._exec(x, out, FFT_FORWARD, fft_exec_2d)
+
+    def ifft2(self, x, out=None):
+        if self.rank != 2:
+            raise ValueError("ifft2 needs a rank-2 plan")
+        return self._exec(x, out, FFT_INVERSE, fft_exec_2d)
+
+    def poly_mul(self, a, b, out=None, residual=False):
+        """Products of the rows of int64 device tensors a [batch, la], b [batch, lb]."""
+        import torch
+        if self.rank != 1:
+            raise ValueError("poly_mul needs a rank-1 plan")
+        for t in (a, b):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int64 \
+                    or not t.is_contiguous():
+                raise TypeError("a and b must be contiguous int64 device tensors")
+        a2 = a.reshape(-1, a.shape[-1])
+        b2 = b.reshape(-1, b.shape[-1])
+        if a2.shape[0] != b2.shape[0]:
+            raise ValueError("a and b must have the same batch")
+        batch, la, lb = a2.shape[0], a2.shape[1], b2.shape[1]
+        if out is None:
+            out = torch.empty((batch, la + lb - 1), dtype=torch.int64, device=a.device)
+        ws_bytes = fft_poly_mul_workspace_size(self.handle, batch)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
+        resid = torch.empty(1, dtype=torch.float64, device=a.device) if residual else None
+        fft_poly_mul(self.handle, a2, la, b2, lb, out, batch, ws, resid)
+        return (out, resid) if residual else out
+
+
+def poly_mul(a, b, residual=False):
+    """Integer polynomial products with the smallest power-of-two N >= la + lb - 1."""
+    import torch
+    la, lb = a.shape[-1], b.shape[-1]
+    n = 1
+    while n < la + lb - 1:
+        n *= 2
+    return Plan(n, torch.complex128).poly_mul(a, b, residual=residual)

@@ -1,0 +1,514 @@
+// api.cpp -- the C ABI of include/fftmi.h: argument validation, plans and
+// their twiddle tables, and dispatch to the kernels.
+//
+// Every argument is validated before the first HIP call, so validation
+// errors are reported the same way with or without a GPU.
+#include "fftmi.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "radix_plan.hpp"
+
+using namespace fftmi;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(FFT_ERR_DEVICE, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+int ilog2(int64_t n)
+{
+    int l = 0;
+    while ((int64_t(1) << l) < n) ++l;
+    return l;
+}
+
+bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+
+// e^{-2 pi i m / M} in fp64 for a power-of-two M, with the angle reduced to
+// [0, pi/4] by the symmetries of the unit circle before calling libm, so the
+// value carries one rounding of a small angle instead of the rounding of
+// 2 pi m / M for large m.
+void root_of_unity(int64_t m, int64_t M, double* re, double* im)
+{
+    m %= M;
+    if (m < 0) m += M;
+    double c, s;  // cos, sin of 2 pi m / M
+    if (M < 8) {
+        // multiples of an eighth of a turn
+        const int q = (int)(m * (8 / M));
+        static const double h = 0.70710678118654752440084436210485;
+        static const double cs[8][2] = {{1, 0}, {h, h}, {0, 1}, {-h, h}, {-1, 0}, {-h, -h}, {0, -1}, {h, -h}};
+        c = cs[q][0];
+        s = cs[q][1];
+    } else {
+        const int64_t quarter = M / 4, eighth = M / 8;
+        const int64_t quad = m / quarter, x = m % quarter;
+        double cx, sx;
+        if (x <= eighth) {
+            const double th = 2.0 * M_PI * ((double)x / (double)M);
+            cx = std::cos(th);
+            sx = std::sin(th);
+        } else {
+            const double th = 2.0 * M_PI * ((double)(quarter - x) / (double)M);
+            cx = std::sin(th);
+            sx = std::cos(th);
+        }
+        switch (quad) {
+            case 0: c = cx; s = sx; break;
+            case 1: c = -sx; s = cx; break;
+            case 2: c = -cx; s = -sx; break;
+            default: c = sx; s = -cx; break;
+        }
+    }
+    *re = c;
+    *im = -s;
+}
+
+// Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
+// interleaved doubles: stage s >= 1 holds [r - 1][k] = w_{Ns R}^{r k}.
+std::vector<double> stage_table(int logn)
+{
+    std::vector<double> t(2 * (size_t)plan_tw_entries(logn));
+    for (int s = 1; s < plan_nstages(logn); ++s) {
+        const int R = 1 << plan_stage_logr(logn, s);
+        const int64_t ns = int64_t(1) << plan_stage_lns(logn, s);
+        const long off = plan_tw_offset(logn, s);
+        for (int r = 1; r < R; ++r)
+            for (int64_t k = 0; k < ns; ++k) {
+                const size_t e = (size_t)(off + (r - 1) * ns + k);
+                root_of_unity(r * k, ns * R, &t[2 * e], &t[2 * e + 1]);
+            }
+    }
+    return t;
+}
+
+struct DeviceTable {
+    void* ptr = nullptr;
+};
+
+}  // namespace
+
+enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_FOURSTEP = 2, PATH_2D = 3 };
+
+struct fft_plan {
+    int rank = 0;
+    int64_t dims[2] = {1, 1};
+    int prec = 0;
+    int device = 0;
+    int path = PATH_COPY;
+    int64_t n = 1;          // points per transform (H*W for 2D)
+    int logn = 0;
+    // rank 1, rows:      tw_a = table for N
+    // rank 1, four-step: tw_a = rows (N1), tw_b = columns (N2), big_* = w_N
+    // rank 2:            tw_a = rows (W), tw_b = columns (H)
+    int log_a = 0, log_b = 0;
+    void* tw_a = nullptr;
+    void* tw_b = nullptr;
+    void* big_hi = nullptr;
+    void* big_lo = nullptr;
+    int big_lbits = 0;
+    size_t elem = 8;
+};
+
+namespace {
+
+size_t elem_bytes(int prec) { return prec == FFT_C32 ? 8 : 16; }
+
+int64_t max_lds_n(int prec) { return prec == FFT_C32 ? FFT_MAX_LDS_N_C32 : FFT_MAX_LDS_N_C64; }
+int64_t max_n(int prec) { return prec == FFT_C32 ? FFT_MAX_N_C32 : FFT_MAX_N_C64; }
+
+// Upload interleaved fp64 values rounded to the plan precision.
+int upload(const std::vector<double>& host, int prec, void** dev)
+{
+    *dev = nullptr;
+    if (host.empty()) return FFT_OK;
+    const size_t count = host.size();
+    const size_t bytes = prec == FFT_C32 ? count * sizeof(float) : count * sizeof(double);
+    std::vector<float> f;
+    const void* src = host.data();
+    if (prec == FFT_C32) {
+        f.resize(count);
+        for (size_t i = 0; i < count; ++i) f[i] = (float)host[i];
+        src = f.data();
+    }
+    hipError_t e = hipMalloc(dev, bytes);
+    if (e != hipSuccess) {
+        *dev = nullptr;
+        return hip_fail(e, "hipMalloc(twiddles)");
+    }
+    e = hipMemcpy(*dev, src, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        hipFree(*dev);
+        *dev = nullptr;
+        return hip_fail(e, "hipMemcpy(twiddles)");
+    }
+    return FFT_OK;
+}
+
+void free_plan(fft_plan* p)
+{
+    if (!p) return;
+    void* ptrs[] = {p->tw_a, p->tw_b, p->big_hi, p->big_lo};
+    for (void* q : ptrs)
+        if (q) hipFree(q);
+    delete p;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Common checks of an exec call; returns FFT_OK or an error, sets *noop.
+int check_exec(const fft_plan* plan, int dir, int rank, const void* in, void* out, int64_t batch,
+               void* workspace, size_t ws_needed, bool* noop)
+{
+    *noop = false;
+    if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
+    if (dir != FFT_FORWARD && dir != FFT_INVERSE) return fail(FFT_ERR_INVALID_ARG, "dir %d is not FFT_FORWARD/FFT_INVERSE", dir);
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch %lld < 0", (long long)batch);
+    if (plan->rank != rank)
+        return fail(FFT_ERR_RANK, "plan has rank %d, this call needs rank %d", plan->rank, rank);
+    if (batch == 0) {
+        *noop = true;
+        return FFT_OK;
+    }
+    if (!in || !out) return fail(FFT_ERR_INVALID_ARG, "in or out is NULL");
+    if (batch > INT64_MAX / (int64_t)(plan->n * plan->elem))
+        return fail(FFT_ERR_INVALID_ARG, "batch %lld overflows the buffer size", (long long)batch);
+    if (((uintptr_t)in | (uintptr_t)out) % plan->elem)
+        return fail(FFT_ERR_ALIGN, "in/out must be aligned to %zu bytes", plan->elem);
+    const size_t bytes = (size_t)batch * (size_t)plan->n * plan->elem;
+    if (in != out && ranges_overlap(in, bytes, out, bytes))
+        return fail(FFT_ERR_OVERLAP, "in and out overlap partially");
+    if (ws_needed) {
+        if (!workspace) return fail(FFT_ERR_WORKSPACE, "workspace of %zu bytes required", ws_needed);
+        if ((uintptr_t)workspace % plan->elem) return fail(FFT_ERR_ALIGN, "workspace misaligned");
+        if (ranges_overlap(workspace, ws_needed, in, bytes) || ranges_overlap(workspace, ws_needed, out, bytes))
+            return fail(FFT_ERR_WORKSPACE, "workspace overlaps in or out");
+    }
+    return FFT_OK;
+}
+
+int check_device(const fft_plan* plan)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != plan->device)
+        return fail(FFT_ERR_DEVICE, "plan was created on device %d, current device is %d", plan->device, dev);
+    return FFT_OK;
+}
+
+size_t c2c_workspace(const fft_plan* p, int64_t batch)
+{
+    return p->path == PATH_FOURSTEP ? (size_t)batch * (size_t)p->n * p->elem : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fft_status_string(int status)
+{
+    switch (status) {
+        case FFT_OK: return "FFT_OK";
+        case FFT_ERR_INVALID_ARG: return "FFT_ERR_INVALID_ARG: invalid argument";
+        case FFT_ERR_NOT_POW2: return "FFT_ERR_NOT_POW2: length is not a power of two";
+        case FFT_ERR_UNSUPPORTED_SIZE: return "FFT_ERR_UNSUPPORTED_SIZE: size outside the supported range";
+        case FFT_ERR_PRECISION: return "FFT_ERR_PRECISION: operation needs another precision";
+        case FFT_ERR_RANK: return "FFT_ERR_RANK: plan rank does not match the call";
+        case FFT_ERR_ALIGN: return "FFT_ERR_ALIGN: pointer not aligned to its element size";
+        case FFT_ERR_OVERLAP: return "FFT_ERR_OVERLAP: buffers overlap";
+        case FFT_ERR_WORKSPACE: return "FFT_ERR_WORKSPACE: workspace missing or overlapping";
+        case FFT_ERR_DEVICE: return "FFT_ERR_DEVICE: HIP call failed";
+        default: return "unknown status";
+    }
+}
+
+const char* fft_last_error(void) { return g_last_error.c_str(); }
+
+int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec)
+{
+    if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
+    *out_plan = nullptr;
+    if (rank != 1 && rank != 2) return fail(FFT_ERR_INVALID_ARG, "rank %d not supported (1 or 2)", rank);
+    if (!dims) return fail(FFT_ERR_INVALID_ARG, "dims is NULL");
+    if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
+    for (int d = 0; d < rank; ++d) {
+        if (dims[d] < 1) return fail(FFT_ERR_INVALID_ARG, "dims[%d] = %lld < 1", d, (long long)dims[d]);
+        if (!is_pow2(dims[d]))
+            return fail(FFT_ERR_NOT_POW2, "dims[%d] = %lld is not a power of two", d, (long long)dims[d]);
+        const int64_t lim = rank == 1 ? max_n(prec) : max_lds_n(prec);
+        if (dims[d] > lim)
+            return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", d, (long long)dims[d],
+                        (long long)lim);
+    }
+
+    fft_plan* p = new (std::nothrow) fft_plan;
+    if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
+    p->rank = rank;
+    p->prec = prec;
+    p->elem = elem_bytes(prec);
+    p->dims[0] = dims[0];
+    p->dims[1] = rank == 2 ? dims[1] : 1;
+    p->n = p->dims[0] * p->dims[1];
+    p->logn = ilog2(p->n);
+
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "hipGetDevice");
+    }
+
+    int st = FFT_OK;
+    if (rank == 1) {
+        const int64_t n = dims[0];
+        if (n == 1) {
+            p->path = PATH_COPY;
+        } else if (n <= max_lds_n(prec)) {
+            p->path = PATH_ROWS;
+            p->log_a = p->logn;
+            st = upload(stage_table(p->log_a), prec, &p->tw_a);
+        } else {
+            p->path = PATH_FOURSTEP;
+            p->log_b = (p->logn + 1) / 2;  // N2, the column length
+            p->log_a = p->logn - p->log_b; // N1, the row length
+            st = upload(stage_table(p->log_a), prec, &p->tw_a);
+            if (st == FFT_OK) st = upload(stage_table(p->log_b), prec, &p->tw_b);
+            // w_N^m = hi[m >> L] lo[m & (2^L - 1)]
+            p->big_lbits = (p->logn + 1) / 2;
+            const int64_t nlo = int64_t(1) << p->big_lbits, nhi = p->n >> p->big_lbits;
+            std::vector<double> lo(2 * nlo), hi(2 * nhi);
+            for (int64_t q = 0; q < nlo; ++q) root_of_unity(q, p->n, &lo[2 * q], &lo[2 * q + 1]);
+            for (int64_t q = 0; q < nhi; ++q) root_of_unity(q << p->big_lbits, p->n, &hi[2 * q], &hi[2 * q + 1]);
+            if (st == FFT_OK) st = upload(lo, prec, &p->big_lo);
+            if (st == FFT_OK) st = upload(hi, prec, &p->big_hi);
+        }
+    } else {
+        p->path = PATH_2D;
+        p->log_a = ilog2(p->dims[1]);  // W
+        p->log_b = ilog2(p->dims[0]);  // H
+        if (p->log_a > 0) st = upload(stage_table(p->log_a), prec, &p->tw_a);
+        if (st == FFT_OK && p->log_b > 0) st = upload(stage_table(p->log_b), prec, &p->tw_b);
+    }
+    if (st != FFT_OK) {
+        free_plan(p);
+        return st;
+    }
+    *out_plan = p;
+    return FFT_OK;
+}
+
+int fft_plan_destroy(fft_plan* plan)
+{
+    free_plan(plan);
+    return FFT_OK;
+}
+
+int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
+{
+    if (!p || !buf || len == 0) return fail(FFT_ERR_INVALID_ARG, "plan or buf is NULL");
+    const char* prec = p->prec == FFT_C32 ? "c32" : "c64";
+    switch (p->path) {
+        case PATH_COPY:
+            snprintf(buf, len, "rank=%d n=%lld prec=%s path=copy", p->rank, (long long)p->n, prec);
+            break;
+        case PATH_ROWS:
+            snprintf(buf, len, "rank=1 n=%lld prec=%s path=rows stages=%d", (long long)p->n, prec,
+                     plan_nstages(p->log_a));
+            break;
+        case PATH_FOURSTEP:
+            snprintf(buf, len, "rank=1 n=%lld prec=%s path=fourstep n1=%lld n2=%lld cols_per_wg=%d rows_per_wg=%d",
+                     (long long)p->n, prec, 1LL << p->log_a, 1LL << p->log_b, tile_lines(p->prec, p->log_b),
+                     tile_lines(p->prec, p->log_a));
+            break;
+        default:
+            snprintf(buf, len, "rank=2 h=%lld w=%lld prec=%s path=2d cols_per_wg=%d", (long long)p->dims[0],
+                     (long long)p->dims[1], prec, p->log_b > 0 ? tile_lines(p->prec, p->log_b) : 0);
+            break;
+    }
+    return FFT_OK;
+}
+
+int fft_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
+{
+    if (!plan || !bytes) return fail(FFT_ERR_INVALID_ARG, "plan or bytes is NULL");
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
+    if (batch > INT64_MAX / (int64_t)(plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
+    *bytes = c2c_workspace(plan, batch);
+    return FFT_OK;
+}
+
+int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
+                 void* stream)
+{
+    bool noop = false;
+    const size_t ws = plan && batch > 0 ? c2c_workspace(plan, batch) : 0;
+    int st = check_exec(plan, dir, 1, in, out, batch, workspace, ws, &noop);
+    if (st != FFT_OK || noop) return st;
+    if ((st = check_device(plan)) != FFT_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool inv = dir == FFT_INVERSE;
+    const double scale = 1.0 / (double)plan->n;
+    hipError_t e = hipSuccess;
+    switch (plan->path) {
+        case PATH_COPY:
+            if (in != out) e = hipMemcpyAsync(out, in, (size_t)batch * plan->elem, hipMemcpyDeviceToDevice, s);
+            break;
+        case PATH_ROWS:
+            e = launch_rows(plan->prec, plan->log_a, inv, inv, in, out, batch, plan->tw_a, scale, s);
+            break;
+        case PATH_FOURSTEP: {
+            const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
+            const int64_t n1 = int64_t(1) << plan->log_a, n2 = int64_t(1) << plan->log_b;
+            e = launch_fourstep_a(plan->prec, plan->log_b, n1, in, workspace, batch, plan->tw_b, big, inv, s);
+            if (e == hipSuccess)
+                e = launch_fourstep_b(plan->prec, plan->log_a, n2, workspace, out, batch, plan->tw_a, inv, scale, s);
+            break;
+        }
+        default:
+            return fail(FFT_ERR_RANK, "plan path is not rank 1");
+    }
+    if (e != hipSuccess) return hip_fail(e, "fft_exec_c2c launch");
+    if (getenv("FFTMI_SYNC")) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "fft_exec_c2c (FFTMI_SYNC)");
+    }
+    return FFT_OK;
+}
+
+int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
+                void* stream)
+{
+    (void)workspace;
+    bool noop = false;
+    int st = check_exec(plan, dir, 2, in, out, batch, nullptr, 0, &noop);
+    if (st != FFT_OK || noop) return st;
+    if ((st = check_device(plan)) != FFT_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool inv = dir == FFT_INVERSE;
+    const double scale = 1.0 / (double)plan->n;
+    const int64_t h = plan->dims[0], w = plan->dims[1];
+    hipError_t e = hipSuccess;
+    if (h == 1 && w == 1) {
+        if (in != out) e = hipMemcpyAsync(out, in, (size_t)batch * plan->elem, hipMemcpyDeviceToDevice, s);
+    } else if (h == 1) {
+        e = launch_rows(plan->prec, plan->log_a, inv, inv, in, out, batch, plan->tw_a, scale, s);
+    } else if (w == 1) {
+        // the columns are contiguous
+        e = launch_rows(plan->prec, plan->log_b, inv, inv, in, out, batch, plan->tw_b, scale, s);
+    } else {
+        e = launch_rows(plan->prec, plan->log_a, inv, false, in, out, batch * h, plan->tw_a, 1.0, s);
+        if (e == hipSuccess) e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, w, plan->tw_b, inv, scale, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "fft_exec_2d launch");
+    if (getenv("FFTMI_SYNC")) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "fft_exec_2d (FFTMI_SYNC)");
+    }
+    return FFT_OK;
+}
+
+int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
+{
+    if (!plan || !bytes) return fail(FFT_ERR_INVALID_ARG, "plan or bytes is NULL");
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
+    if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
+    if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
+    if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
+    *bytes = plan->path == PATH_FOURSTEP ? (size_t)2 * batch * (size_t)plan->n * plan->elem : 0;
+    return FFT_OK;
+}
+
+int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, int64_t* c,
+                 int64_t batch, void* workspace, double* d_max_residual, void* stream)
+{
+    if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
+    if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
+    if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
+    if (la > plan->n || lb > plan->n || la + lb - 1 > plan->n)
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "la + lb - 1 = %lld exceeds the plan's N = %lld",
+                    (long long)(la + lb - 1), (long long)plan->n);
+    if (batch == 0) return FFT_OK;
+    if (!a || !b || !c) return fail(FFT_ERR_INVALID_ARG, "a, b or c is NULL");
+    const int64_t lc = la + lb - 1;
+    if (batch > INT64_MAX / (int64_t)(2 * plan->n * 16)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
+    if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) % 8) return fail(FFT_ERR_ALIGN, "a, b, c must be 8-byte aligned");
+    if ((uintptr_t)d_max_residual % 8) return fail(FFT_ERR_ALIGN, "d_max_residual must be 8-byte aligned");
+    const size_t ba = (size_t)batch * la * 8, bb = (size_t)batch * lb * 8, bc = (size_t)batch * lc * 8;
+    if (ranges_overlap(c, bc, a, ba) || ranges_overlap(c, bc, b, bb))
+        return fail(FFT_ERR_OVERLAP, "c overlaps a or b");
+    if (d_max_residual && (ranges_overlap(d_max_residual, 8, c, bc) || ranges_overlap(d_max_residual, 8, a, ba) ||
+                           ranges_overlap(d_max_residual, 8, b, bb)))
+        return fail(FFT_ERR_OVERLAP, "d_max_residual overlaps a, b or c");
+    size_t ws = 0;
+    fft_poly_mul_workspace_size(plan, batch, &ws);
+    if (ws) {
+        if (!workspace) return fail(FFT_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
+        if ((uintptr_t)workspace % 16) return fail(FFT_ERR_ALIGN, "workspace must be 16-byte aligned");
+        if (ranges_overlap(workspace, ws, a, ba) || ranges_overlap(workspace, ws, b, bb) ||
+            ranges_overlap(workspace, ws, c, bc) ||
+            (d_max_residual && ranges_overlap(workspace, ws, d_max_residual, 8)))
+            return fail(FFT_ERR_WORKSPACE, "workspace overlaps an operand");
+    }
+    int st = check_device(plan);
+    if (st != FFT_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (d_max_residual) e = launch_zero_resid(d_max_residual, s);
+    if (e == hipSuccess) {
+        if (plan->path == PATH_FOURSTEP) {
+            const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
+            e = launch_polymul_fourstep(plan->log_a, plan->log_b, a, la, b, lb, c, batch, workspace, plan->tw_a,
+                                        plan->tw_b, big, d_max_residual, s);
+        } else if (plan->path == PATH_ROWS) {
+            e = launch_polymul_rows(plan->log_a, a, la, b, lb, c, batch, plan->tw_a, d_max_residual, s);
+        } else {
+            // N = 1: c_0 = a_0 b_0, done by the N = 2 kernel (la + lb - 1 = 1 <= 2) with no table
+            // needed beyond the single radix-2 stage.
+            e = launch_polymul_rows(1, a, la, b, lb, c, batch, nullptr, d_max_residual, s);
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "fft_poly_mul launch");
+    if (getenv("FFTMI_SYNC")) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "fft_poly_mul (FFTMI_SYNC)");
+    }
+    return FFT_OK;
+}
+
+}  // extern "C"

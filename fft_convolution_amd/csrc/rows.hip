@@ -1,0 +1,92 @@
+// rows.hip -- the LDS-resident row kernel: each workgroup transforms RPW
+// contiguous rows of N = 2^LOGN points.  One coalesced global read of every
+// row straight into registers, all log2 N butterfly levels fused into the
+// radix stages of radix_plan.hpp with LDS exchanges between them, one
+// coalesced global write ("Stockham FFT Butterfly Algorithm in Parallel
+// GLSL", section "Performance and Pipeline Evaluation": stages batched in
+// on-chip memory instead of one global round trip per stage).
+#include "launch.hpp"
+#include "stockham.hpp"
+
+namespace fftmi {
+
+// Rows per workgroup: at least 256 threads per workgroup.
+template <int LOGN> constexpr int rows_per_wg() { return Geometry<LOGN>::T >= 256 ? 1 : 256 / Geometry<LOGN>::T; }
+
+template <typename V, int LOGN, bool CONJ_IN, bool CONJ_OUT>
+__global__ __launch_bounds__(Geometry<LOGN>::T * rows_per_wg<LOGN>())
+void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
+                 typename real_of<V>::type scale)
+{
+    using G = Geometry<LOGN>;
+    constexpr int RPW = rows_per_wg<LOGN>();
+    __shared__ V lds[G::LDS > 0 ? G::LDS * RPW : 1];
+
+    const int tid = threadIdx.x;
+    const int rloc = tid / G::T;
+    const int t = tid % G::T;
+    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
+    const bool live = row < nrows;
+    const int64_t base = row * G::N + t;
+
+    V v[G::E];
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) {
+        V x = live ? in[base + i * G::T] : V{0, 0};
+        v[i] = CONJ_IN ? cconj(x) : x;
+    }
+    V* my = lds + rloc * G::LDS;
+    fft_regs<LOGN>(v, t, tw, [my](int pos) { return my + pos + (pos >> 4); });
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < G::E; ++i) {
+            V y = v[i];
+            out[base + i * G::T] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
+        }
+    }
+}
+
+template <typename V, int LOGN, bool CI, bool CO>
+static hipError_t launch_rows_t(const void* in, void* out, int64_t nrows, const void* tw, double scale,
+                                hipStream_t stream)
+{
+    constexpr int RPW = rows_per_wg<LOGN>();
+    const int64_t blocks = (nrows + RPW - 1) / RPW;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    using Rl = typename real_of<V>::type;
+    hipLaunchKernelGGL((rows_kernel<V, LOGN, CI, CO>), dim3((unsigned)blocks),
+                       dim3(Geometry<LOGN>::T * RPW), 0, stream, (const V*)in, (V*)out, nrows,
+                       (const V*)tw, (Rl)scale);
+    return hipGetLastError();
+}
+
+template <typename V, int LOGN>
+static hipError_t launch_rows_dir(bool ci, bool co, const void* in, void* out, int64_t nrows,
+                                  const void* tw, double scale, hipStream_t s)
+{
+    if (!ci && !co) return launch_rows_t<V, LOGN, false, false>(in, out, nrows, tw, scale, s);
+    if (ci && co) return launch_rows_t<V, LOGN, true, true>(in, out, nrows, tw, scale, s);
+    if (ci) return launch_rows_t<V, LOGN, true, false>(in, out, nrows, tw, scale, s);
+    return launch_rows_t<V, LOGN, false, true>(in, out, nrows, tw, scale, s);
+}
+
+hipError_t launch_rows(int prec, int logn, bool ci, bool co, const void* in, void* out, int64_t nrows,
+                       const void* tw, double scale, hipStream_t s)
+{
+#define FFTMI_ROW_CASE(L) \
+    case L: return prec == 0 ? launch_rows_dir<float2, L>(ci, co, in, out, nrows, tw, scale, s) \
+                             : launch_rows_dir<double2, L>(ci, co, in, out, nrows, tw, scale, s);
+    if (prec == 1 && logn > 12) return hipErrorInvalidValue;
+    switch (logn) {
+        FFTMI_ROW_CASE(1) FFTMI_ROW_CASE(2) FFTMI_ROW_CASE(3) FFTMI_ROW_CASE(4)
+        FFTMI_ROW_CASE(5) FFTMI_ROW_CASE(6) FFTMI_ROW_CASE(7) FFTMI_ROW_CASE(8)
+        FFTMI_ROW_CASE(9) FFTMI_ROW_CASE(10) FFTMI_ROW_CASE(11) FFTMI_ROW_CASE(12)
+        case 13:
+            if (prec == 0) return launch_rows_dir<float2, 13>(ci, co, in, out, nrows, tw, scale, s);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+#undef FFTMI_ROW_CASE
+}
+
+}  // namespace fftmi

@@ -1,0 +1,248 @@
+// stockham.hpp -- device-side building blocks of the Stockham FFT kernels.
+//
+//  * complex arithmetic on float2 / double2 (interleaved re, im);
+//  * R-point DFTs in registers (R = 2 .. 32) with compile-time constant
+//    twiddles: the butterfly a + w b / a - w b of "The Butterfly: One Thread,
+//    One Output", fused over log2 R levels;
+//  * the workgroup engine `fft_regs`: every thread owns E elements of one
+//    transform (positions t + i T); the stages of radix_plan.hpp run in
+//    registers, and between stages the outputs go through LDS, written in the
+//    Stockham output order and read back in the next stage's input order (the
+//    ping-pong of "Stockham FFT ... in Parallel GLSL", section "Execution via
+//    GLSL Compute Shaders and Textures", between registers and LDS instead of
+//    two textures).  The first stage reads and the last stage writes the
+//    positions t + i T, so the kernels' global loads and stores are coalesced.
+//
+// Every transform here is forward (e^{-i}); the inverse is obtained as
+// conj(F(conj(x))) / N by conjugating on load and on store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "radix_plan.hpp"
+
+namespace fftmi {
+
+template <typename Rl> struct cvec;
+template <> struct cvec<float> { using type = float2; };
+template <> struct cvec<double> { using type = double2; };
+
+template <typename V> struct real_of;
+template <> struct real_of<float2> { using type = float; };
+template <> struct real_of<double2> { using type = double; };
+
+template <typename V> __device__ __forceinline__ V cadd(V a, V b) { return V{a.x + b.x, a.y + b.y}; }
+template <typename V> __device__ __forceinline__ V csub(V a, V b) { return V{a.x - b.x, a.y - b.y}; }
+template <typename V> __device__ __forceinline__ V cmul(V a, V w)
+{
+    return V{a.x * w.x - a.y * w.y, a.x * w.y + a.y * w.x};
+}
+template <typename V> __device__ __forceinline__ V cconj(V a) { return V{a.x, -a.y}; }
+// a * (-i)
+template <typename V> __device__ __forceinline__ V cmul_mi(V a) { return V{a.y, -a.x}; }
+// a * (+i)
+template <typename V> __device__ __forceinline__ V cmul_pi(V a) { return V{-a.y, a.x}; }
+
+// ---------------------------------------------------------------------------
+// Constant twiddles w_R^m = e^{-2 pi i m / R} for R | 32, in 32nds of a turn.
+// ---------------------------------------------------------------------------
+// cos(2 pi q / 32) for q = 0 .. 8.
+constexpr double kCos32[9] = {
+    1.0,
+    0.98078528040323044912618223613424,
+    0.92387953251128675612818318939679,
+    0.83146961230254523707878837761791,
+    0.70710678118654752440084436210485,
+    0.55557023301960222474283081394853,
+    0.38268343236508977172845998403040,
+    0.19509032201612826784828486847702,
+    0.0,
+};
+
+constexpr double cos32(int q)
+{
+    q = ((q % 32) + 32) % 32;
+    return q <= 8 ? kCos32[q] : q <= 16 ? -kCos32[16 - q] : q <= 24 ? -kCos32[q - 16] : kCos32[32 - q];
+}
+constexpr double sin32(int q) { return cos32(q - 8); }
+
+// v *= w_R^m, with the multiples of an eighth turn done by swaps and adds.
+template <int M, int R, typename V>
+__device__ __forceinline__ V mul_const_tw(V v)
+{
+    using Rl = typename real_of<V>::type;
+    constexpr int q = ((M * (32 / R)) % 32 + 32) % 32;
+    constexpr Rl h = (Rl)0.70710678118654752440084436210485;
+    if constexpr (q == 0) {
+        return v;
+    } else if constexpr (q == 8) {
+        return cmul_mi(v);
+    } else if constexpr (q == 16) {
+        return V{-v.x, -v.y};
+    } else if constexpr (q == 24) {
+        return cmul_pi(v);
+    } else if constexpr (q == 4) {  // (1 - i)/sqrt2
+        return V{(v.x + v.y) * h, (v.y - v.x) * h};
+    } else if constexpr (q == 12) {  // (-1 - i)/sqrt2
+        return V{(v.y - v.x) * h, -(v.x + v.y) * h};
+    } else if constexpr (q == 20) {  // (-1 + i)/sqrt2
+        return V{-(v.x + v.y) * h, (v.x - v.y) * h};
+    } else if constexpr (q == 28) {  // (1 + i)/sqrt2
+        return V{(v.x - v.y) * h, (v.x + v.y) * h};
+    } else {
+        constexpr Rl c = (Rl)cos32(q);
+        constexpr Rl s = (Rl)(-sin32(q));
+        return cmul(v, V{c, s});
+    }
+}
+
+// ---------------------------------------------------------------------------
+// R-point DFT in registers, natural order in and out:  u[k] <- sum_n u[n] w_R^{nk}.
+// R = P Q: Q-point DFTs over n2 of u[P n2 + n1], twiddle w_R^{n1 k1}, then
+// P-point DFTs over n1, giving X[k1 + Q k2].
+// ---------------------------------------------------------------------------
+template <int R> struct Dft;
+
+template <> struct Dft<1> {
+    template <typename V> __device__ __forceinline__ static void run(V*) {}
+};
+
+template <> struct Dft<2> {
+    template <typename V> __device__ __forceinline__ static void run(V* u)
+    {
+        V a = u[0], b = u[1];
+        u[0] = cadd(a, b);
+        u[1] = csub(a, b);
+    }
+};
+
+template <> struct Dft<4> {
+    template <typename V> __device__ __forceinline__ static void run(V* u)
+    {
+        V a0 = cadd(u[0], u[2]), a1 = csub(u[0], u[2]);
+        V a2 = cadd(u[1], u[3]), a3 = cmul_mi(csub(u[1], u[3]));
+        u[0] = cadd(a0, a2);
+        u[2] = csub(a0, a2);
+        u[1] = cadd(a1, a3);
+        u[3] = csub(a1, a3);
+    }
+};
+
+template <int P, int Q> struct DftSplit {
+    template <typename V> __device__ __forceinline__ static void run(V* u)
+    {
+        constexpr int R = P * Q;
+        V y[R];  // y[n1 * Q + k1]
+#pragma unroll
+        for (int n1 = 0; n1 < P; ++n1) {
+            V w[Q];
+#pragma unroll
+            for (int n2 = 0; n2 < Q; ++n2) w[n2] = u[P * n2 + n1];
+            Dft<Q>::run(w);
+#pragma unroll
+            for (int k1 = 0; k1 < Q; ++k1) y[n1 * Q + k1] = w[k1];
+        }
+        twiddle_rows<0>(y);
+#pragma unroll
+        for (int k1 = 0; k1 < Q; ++k1) {
+            V z[P];
+#pragma unroll
+            for (int n1 = 0; n1 < P; ++n1) z[n1] = y[n1 * Q + k1];
+            Dft<P>::run(z);
+#pragma unroll
+            for (int k2 = 0; k2 < P; ++k2) u[k1 + Q * k2] = z[k2];
+        }
+    }
+    // y[n1 * Q + k1] *= w_R^{n1 k1}, unrolled at compile time.
+    template <int I, typename V> __device__ __forceinline__ static void twiddle_rows(V* y)
+    {
+        if constexpr (I < P * Q) {
+            constexpr int n1 = I / Q, k1 = I % Q;
+            y[I] = mul_const_tw<n1 * k1, P * Q>(y[I]);
+            twiddle_rows<I + 1>(y);
+        }
+    }
+};
+
+template <> struct Dft<8> : DftSplit<2, 4> {};
+template <> struct Dft<16> : DftSplit<4, 4> {};
+template <> struct Dft<32> : DftSplit<4, 8> {};
+
+// ---------------------------------------------------------------------------
+// The workgroup engine.
+// ---------------------------------------------------------------------------
+template <int LOGN> struct Geometry {
+    static constexpr int N = 1 << LOGN;
+    static constexpr int LOGE = plan_loge(LOGN);
+    static constexpr int E = 1 << LOGE;         // elements per thread
+    static constexpr int T = N / E;             // threads per transform
+    static constexpr int S = plan_nstages(LOGN);
+    static constexpr int LDS = S > 1 ? lds_padded(N) : 0;  // LDS slots per transform
+};
+
+// One Stockham stage of radix 2^LR over span Ns = 2^LNS on the registers of
+// thread t.  Not the last stage: outputs go to LDS.  Last stage: outputs
+// stay in v (position t + i T in v[i]).
+template <int LOGN, int STAGE, typename V, typename LdsAt>
+__device__ __forceinline__ void fft_stage(V (&v)[Geometry<LOGN>::E], int t, const V* __restrict__ tw,
+                                          LdsAt lds_at)
+{
+    using G = Geometry<LOGN>;
+    constexpr int LR = plan_stage_logr(LOGN, STAGE), R = 1 << LR;
+    constexpr int LNS = plan_stage_lns(LOGN, STAGE), NS = 1 << LNS;
+    constexpr int B = G::E / R;
+    constexpr bool LAST = STAGE == G::S - 1;
+    const V* __restrict__ tws = tw + plan_tw_offset(LOGN, STAGE);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        V u[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) u[r] = v[b + r * B];
+        const int j = t + b * G::T;
+        const int k = j & (NS - 1);
+        if constexpr (NS > 1) {
+#pragma unroll
+            for (int r = 1; r < R; ++r) u[r] = cmul(u[r], tws[(r - 1) * NS + k]);
+        }
+        Dft<R>::run(u);
+        if constexpr (LAST) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) v[b + r * B] = u[r];
+        } else {
+            const int base = ((j >> LNS) << (LNS + LR)) + k;
+#pragma unroll
+            for (int r = 0; r < R; ++r) *lds_at(base + r * NS) = u[r];
+        }
+    }
+}
+
+template <int LOGN, int STAGE, typename V, typename LdsAt>
+__device__ __forceinline__ void fft_stages_from(V (&v)[Geometry<LOGN>::E], int t, const V* __restrict__ tw,
+                                                LdsAt lds_at)
+{
+    using G = Geometry<LOGN>;
+    if constexpr (STAGE < G::S) {
+        if constexpr (STAGE > 0) {
+            __syncthreads();  // the previous stage's LDS writes are visible
+#pragma unroll
+            for (int i = 0; i < G::E; ++i) v[i] = *lds_at(t + i * G::T);
+            if constexpr (STAGE < G::S - 1) __syncthreads();  // all reads done before rewriting
+        }
+        fft_stage<LOGN, STAGE>(v, t, tw, lds_at);
+        fft_stages_from<LOGN, STAGE + 1>(v, t, tw, lds_at);
+    }
+}
+
+// Forward transform of N = 2^LOGN points held as v[i] = x[t + i T]; on return
+// v[i] = X[t + i T].  Every thread of the workgroup must call it (barriers).
+// lds_at(pos) returns this transform's LDS slot for position pos.  If the
+// caller reuses the LDS afterwards it must put a barrier first.
+template <int LOGN, typename V, typename LdsAt>
+__device__ __forceinline__ void fft_regs(V (&v)[Geometry<LOGN>::E], int t, const V* __restrict__ tw,
+                                         LdsAt lds_at)
+{
+    fft_stages_from<LOGN, 0>(v, t, tw, lds_at);
+}
+
+}  // namespace fftmi

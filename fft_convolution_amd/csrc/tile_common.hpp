@@ -1,0 +1,84 @@
+// tile_common.hpp -- pieces shared by the tile kernels (tiles.hip, polymul.hip).
+#pragma once
+
+#include "stockham.hpp"
+
+namespace fftmi {
+
+// Lines per workgroup for a tile kernel over lines of N = 2^LOGN elements:
+// as many as fit in ~70 KB of LDS (two workgroups per CU), at most 64 and at
+// most 1024 threads; rows that fit one thread (N <= 16) need no LDS and take
+// 256 lines.
+template <typename V, int LOGN> struct TileShape {
+    using G = Geometry<LOGN>;
+    static constexpr int pow2_floor(long x) { int p = 1; while ((long)p * 2 <= x) p *= 2; return p; }
+    static constexpr long line_bytes = (long)lds_padded(G::N) * (long)sizeof(V);
+    static constexpr int by_lds = G::S > 1 ? pow2_floor(71680 / line_bytes) : 256;
+    static constexpr int by_threads = 1024 / G::T;
+    static constexpr int C0 = by_lds < by_threads ? by_lds : by_threads;
+    static constexpr int C = G::S > 1 ? (C0 > 64 ? 64 : (C0 < 1 ? 1 : C0)) : 256;
+};
+
+template <int LOGN, int C> constexpr int tile_lds_slots()
+{
+    return Geometry<LOGN>::S > 1 ? lds_padded(C * Geometry<LOGN>::N) : 1;
+}
+
+// LDS slot of position `pos` of line c: the C lines are interleaved
+// (f = pos C + c) so that the lanes of one instruction, which run over c
+// fastest, hit consecutive slots; one pad slot per 16.
+template <typename V, int C> struct TileLds {
+    V* lds;
+    int c;
+    __device__ __forceinline__ V* operator()(int pos) const
+    {
+        const int f = pos * C + c;
+        return lds + f + (f >> 4);
+    }
+};
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b mod 8).  Give each XCD a contiguous range of tiles instead, so that
+// neighbouring tiles -- which share cache lines when a tile's row segment is
+// shorter than a line -- are read through the same L2.
+__device__ __forceinline__ int64_t xcd_tile(unsigned b, unsigned nb)
+{
+    const unsigned per = nb >> 3;
+    if (b < per * 8u) return (int64_t)(b & 7u) * per + (b >> 3);
+    return (int64_t)b;
+}
+
+// w_N^m for large N from two tables: hi[q] = w_N^{q 2^lbits}, lo[q] = w_N^q.
+template <typename V> struct BigTw {
+    const V* __restrict__ hi;
+    const V* __restrict__ lo;
+    int lbits;
+    int logn;
+    __device__ __forceinline__ V operator()(int64_t m) const
+    {
+        m &= ((int64_t)1 << logn) - 1;
+        return cmul(hi[m >> lbits], lo[m & (((int64_t)1 << lbits) - 1)]);
+    }
+};
+
+// v[i] holds position p = t + i T of a line; multiply it by w_N^{line p}.
+// The factors are w0 = w_N^{line t} times products of g_j = w_N^{line T 2^j}
+// over the set bits j of i, every factor read from the exact tables, so each
+// twiddle carries a handful of roundings, not a long recurrence.
+template <int LOGN, typename V>
+__device__ __forceinline__ void apply_big_twiddle(V (&v)[Geometry<LOGN>::E], int64_t line, int t, BigTw<V> bt)
+{
+    using G = Geometry<LOGN>;
+    V p[G::E];
+    p[0] = bt(line * t);
+#pragma unroll
+    for (int j = 0; j < G::LOGE; ++j) {
+        const V g = bt((line * G::T) << j);
+#pragma unroll
+        for (int i = 0; i < (1 << j); ++i) p[i + (1 << j)] = cmul(p[i], g);
+    }
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) v[i] = cmul(v[i], p[i]);
+}
+
+}  // namespace fftmi

@@ -1,0 +1,161 @@
+/*
+ * fftmi.h -- C ABI of a power-of-two complex FFT library for one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The transform computed is the discrete Fourier transform of the page "FFT on
+ * GPU" (elwhyjay.github.io/post/fft), section "Discrete Fourier Transform":
+ *     forward  X_k = sum_{n<N} x_n e^{-2 pi i k n / N}
+ *     inverse  x_n = (1/N) sum_{k<N} X_k e^{+2 pi i k n / N}
+ * (the inverse with w -> w^{-1} and the factor 1/N is from the same page, the
+ * section on why roots of unity are used as evaluation points).  It is
+ * evaluated as log2 N radix-2 butterfly levels (a + w b, a - w b; "The
+ * Butterfly: One Thread, One Output") in the out-of-place Stockham autosort
+ * form of "Stockham FFT Butterfly Algorithm in Parallel GLSL" (section "The
+ * Bit-Reversal Bottleneck and the Stockham Advantage"): no bit-reversal pass,
+ * output in natural order.
+ *
+ * Conventions shared by every entry point
+ *  - Complex data are interleaved (re, im): FFT_C32 = two floats (8 B per
+ *    element), FFT_C64 = two doubles (16 B per element).
+ *  - Every data pointer (in, out, a, b, c, workspace, d_max_residual) is a
+ *    DEVICE pointer on the device that was current when the plan was created.
+ *    The caller owns all of them; the library never frees or retains them.
+ *  - The plan owns only its small twiddle tables (device memory allocated in
+ *    fft_plan_create, freed in fft_plan_destroy).  A plan is immutable after
+ *    creation: concurrent executions on different streams are safe when each
+ *    has its own output and workspace.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Execution calls only enqueue work on it and return; they never
+ *    synchronise.  A device fault surfaces at the caller's next sync.
+ *  - Every call returns an fft_status: 0 on success, a negative code on
+ *    failure.  Arguments are validated before any HIP call is made; on a
+ *    validation error nothing is enqueued.  Nothing is thrown across the ABI.
+ *  - batch == 0 is a no-op that returns FFT_OK (pointers may then be NULL).
+ *  - The output is bitwise deterministic for given inputs and plan.
+ */
+#ifndef FFTMI_H
+#define FFTMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fft_plan fft_plan; /* opaque */
+
+/* Precision of a plan: complex64 (fp32 re, im) or complex128 (fp64). */
+enum fft_precision { FFT_C32 = 0, FFT_C64 = 1 };
+
+/* Direction: forward uses e^{-i}; inverse uses e^{+i} and scales by 1/N
+ * (by 1/(H*W) for a 2D plan), so inverse(forward(x)) = x. */
+enum fft_direction { FFT_FORWARD = 0, FFT_INVERSE = 1 };
+
+enum fft_status {
+    FFT_OK = 0,
+    FFT_ERR_INVALID_ARG = -1,      /* NULL pointer, batch < 0, bad rank/dir/prec value */
+    FFT_ERR_NOT_POW2 = -2,         /* a dimension is not a power of two */
+    FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
+                                      la + lb - 1 > N for fft_poly_mul */
+    FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
+    FFT_ERR_RANK = -5,             /* exec_c2c on a rank-2 plan, exec_2d on a rank-1 plan */
+    FFT_ERR_ALIGN = -6,            /* a pointer is not aligned to its element size */
+    FFT_ERR_OVERLAP = -7,          /* buffers partially overlap (in == out is allowed) */
+    FFT_ERR_WORKSPACE = -8,        /* workspace required but NULL, or overlapping data */
+    FFT_ERR_DEVICE = -9            /* a HIP call failed; text in fft_last_error() */
+};
+
+/* Largest supported transform lengths. */
+#define FFT_MAX_LDS_N_C32 8192        /* one-kernel, LDS-resident rows */
+#define FFT_MAX_LDS_N_C64 4096
+#define FFT_MAX_N_C32 (1LL << 26)     /* four-step beyond the LDS-resident range */
+#define FFT_MAX_N_C64 (1LL << 24)
+
+/*
+ * Create a plan.
+ *   rank 1: dims = {N};      1 <= N <= FFT_MAX_N_C32 (C32) / FFT_MAX_N_C64 (C64).
+ *           N <= FFT_MAX_LDS_N_* runs as one LDS-resident kernel per batch of
+ *           rows; larger N runs as a four-step (column FFTs of length N2,
+ *           twiddle W_N^{n1 k2}, row FFTs of length N1 with a transposing store;
+ *           N = N1 N2) and needs a workspace.
+ *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
+ *           Parallel GLSL", section "Multi-Dimensional Transforms and
+ *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*.
+ *   prec:   FFT_C32 or FFT_C64.
+ * Builds the twiddle tables in fp64 on the host, rounds them to the plan
+ * precision and uploads them (the only synchronous device work of the
+ * library).  On success *plan receives the new plan; on failure *plan is set
+ * to NULL.  Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE, DEVICE.
+ */
+int fft_plan_create(fft_plan** plan, int rank, const int64_t* dims, int prec);
+
+/* Free a plan and its device tables.  NULL is accepted (no-op). */
+int fft_plan_destroy(fft_plan* plan);
+
+/* Describe a plan: rank, dims, precision and the kernel path chosen, as a
+ * NUL-terminated string of at most len bytes.  Host-only. */
+int fft_plan_describe(const fft_plan* plan, char* buf, size_t len);
+
+/* Bytes of device workspace fft_exec_c2c / fft_exec_2d need for `batch`
+ * transforms with this plan (0 when none is needed).  Host-only. */
+int fft_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes);
+
+/*
+ * Batched 1D transform with a rank-1 plan.
+ *   in, out:   [batch][N] complex of the plan's precision, rows contiguous.
+ *              in == out (in place) is allowed; any other overlap is an error.
+ *              in is not modified unless in == out.
+ *   workspace: fft_workspace_size(plan, batch) bytes (NULL when that is 0);
+ *              must not overlap in or out.
+ * Errors: INVALID_ARG, RANK, ALIGN, OVERLAP, WORKSPACE, DEVICE.
+ */
+int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
+                 void* workspace, void* stream);
+
+/*
+ * Batched 2D transform with a rank-2 plan: row transforms of length W over
+ * every row, then column transforms of length H over every column.
+ *   in, out:   [batch][H][W] complex, images contiguous.  in == out allowed.
+ *   workspace: unused (size 0); may be NULL.
+ * Errors: as fft_exec_c2c.
+ */
+int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
+                void* workspace, void* stream);
+
+/* Bytes of device workspace fft_poly_mul needs for `batch` pairs. */
+int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes);
+
+/*
+ * Products of integer polynomials by FFT ("FFT on GPU", polynomial
+ * multiplication and whole-process sections): for each pair p,
+ *     c_p[k] = sum_i a_p[i] b_p[k-i],  0 <= k < la + lb - 1,
+ * computed as: zero-pad a and b to N, forward FFT of both (fp64), pointwise
+ * product, inverse FFT (scaled 1/N), round the real part to the nearest
+ * integer (ties to even).
+ *   plan:  rank 1, FFT_C64, with N >= la + lb - 1.
+ *   a:     [batch][la] int64;  b: [batch][lb] int64;  c: [batch][la+lb-1] int64.
+ *          c must not overlap a, b or the workspace.
+ *   workspace: fft_poly_mul_workspace_size(plan, batch) bytes.
+ *   d_max_residual: NULL, or a device double that receives
+ *          max |Re(y)/N - rint(Re(y)/N)| over all outputs (overwritten, not
+ *          accumulated).  The result is exact when this stays well below 0.5;
+ *          callers with coefficients near the fp64 limit should check it.
+ * Errors: INVALID_ARG, RANK, PRECISION, UNSUPPORTED_SIZE, ALIGN, OVERLAP,
+ *         WORKSPACE, DEVICE.
+ */
+int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64_t* b,
+                 int64_t lb, int64_t* c, int64_t batch, void* workspace,
+                 double* d_max_residual, void* stream);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char* fft_status_string(int status);
+
+/* Text of the last error on the calling thread (empty if none). */
+const char* fft_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFTMI_H */
