@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the batched power-of-two C2C FFT on one MI355X.
+
+Default workload: forward C2C FFT of 16384 rows of N = 4096 complex64 points
+(re, im i.i.d. standard normal, seed 2; 512 MiB in, 512 MiB out), the one-kernel
+LDS-resident path.  One step = one fft_exec_c2c call over the whole batch with
+the input already resident in HBM.
+
+Prints ONE JSON line with:
+  value      GFLOP/s = batch * 5 N log2 N / t  (pseudo-flops, 10 per radix-2 butterfly)
+  roofline   achieved HBM GB/s of the kernel (input + output bytes / average
+             kernel time from HIP events on the launch stream) against 8000 GB/s,
+             plus `traffic`: HBM bytes per launch measured with rocprofv3 counters
+             (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), read
+             from profiles/ and null once the kernel sources have changed
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows
+
+Other workloads (--workload) time the 2^24-point four-step, the 2048x2048x8
+2D transform and the 32 x 2^18 polynomial products the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
+WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
+             "polymul_l262144_b32")
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the HIP sources, to tell whether stored counters still apply."""
+    csrc = os.path.join(ROOT, "fft_convolution_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def ensure_built():
+    import fft_convolution_amd as fm
+    if not os.path.exists(fm.lib_path):
+        from fft_convolution_amd import build
+        build.build()
+    fm.lib()
+    return fm
+
+
+def setup_workload(name, dev, fm, torch):
+    """Returns (step_fn, info) with inputs resident on the device."""
+    from fft_convolution_amd import workloads as wl
+    spec = dict(wl.WORKLOADS[name])
+    if name.startswith("c2c_n"):
+        n, batch = spec["n"], spec["batch"]
+        x = torch.from_numpy(wl.workload_input(name)).to(dev)
+        y = torch.empty_like(x)
+        plan = fm.Plan(n, torch.complex64)
+        wsb = fm.fft_workspace_size(plan.handle, batch)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step():
+            fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, y, batch, ws, stream)
+        flops = batch * 5.0 * n * math.log2(n)
+        info = dict(n=n, batch=batch, dtype="f32", flops=flops, bytes=2 * x.numel() * 8,
+                    plan=plan.describe(), kernels=1 if wsb == 0 else 2,
+                    sample_rows=lambda rows: x[:rows].cpu().numpy(),
+                    oracle_unit=5.0 * n * math.log2(n), keep=(plan, x, y, ws))
+        return step, info
+    if name.startswith("c2c2d"):
+        h, w, batch = spec["h"], spec["w"], spec["batch"]
+        x = torch.from_numpy(wl.workload_input(name)).to(dev)
+        y = torch.empty_like(x)
+        plan = fm.Plan((h, w), torch.complex64)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step():
+            fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, x, y, batch, None, stream)
+        flops = batch * 5.0 * h * w * math.log2(h * w)
+        info = dict(h=h, w=w, batch=batch, dtype="f32", flops=flops, bytes=2 * x.numel() * 8,
+                    plan=plan.describe(), kernels=2, keep=(plan, x, y),
+                    sample_rows=lambda rows: x[:rows].cpu().numpy(),
+                    oracle_unit=5.0 * h * w * math.log2(h * w))
+        return step, info
+    if name.startswith("polymul"):
+        length, batch = spec["length"], spec["batch"]
+        a_np, b_np = wl.workload_input(name)
+        a = torch.from_numpy(a_np).to(dev)
+        b = torch.from_numpy(b_np).to(dev)
+        n = 1
+        while n < 2 * length - 1:
+            n *= 2
+        plan = fm.Plan(n, torch.complex128)
+        c = torch.empty(batch, 2 * length - 1, dtype=torch.int64, device=dev)
+        ws = torch.empty(fm.fft_poly_mul_workspace_size(plan.handle, batch), dtype=torch.uint8, device=dev)
+        resid = torch.empty(1, dtype=torch.float64, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step():
+            fm.fft_poly_mul(plan.handle, a, length, b, length, c, batch, ws, resid, stream)
+        flops = batch * 3 * 5.0 * n * math.log2(n)
+        info = dict(n=n, length=length, batch=batch, dtype="f64", flops=flops,
+                    bytes=(a.numel() + b.numel() + c.numel()) * 8, plan=plan.describe(), kernels=4,
+                    keep=(plan, a, b, c, ws, resid),
+                    sample_pairs=lambda p: (a_np[:p], b_np[:p]), oracle_unit=3 * 5.0 * n * math.log2(n))
+        return step, info
+    raise SystemExit("unknown workload %s" % name)
+
+
+def cpu_baseline(name, info, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    if name.startswith("polymul"):
+        total = info["batch"]
+        a, b = info["sample_pairs"](1)
+        t0 = time.perf_counter()
+        oracle.polymul_fft(a, b, n=info["n"])
+        per = time.perf_counter() - t0
+        pairs = int(max(1, min(total, budget_s / max(per, 1e-9) * min(threads, total) / 2)))
+        a, b = info["sample_pairs"](pairs)
+        t0 = time.perf_counter()
+        oracle.polymul_fft(a, b, n=info["n"])
+        dt = time.perf_counter() - t0
+        units, sample = pairs, "first %d of %d pairs" % (pairs, total)
+    elif name.startswith("c2c2d"):
+        imgs = 1
+        x = info["sample_rows"](imgs)
+        t0 = time.perf_counter()
+        oracle.fft2(x)
+        dt = time.perf_counter() - t0
+        units, sample = imgs, "first %d of %d images" % (imgs, info["batch"])
+    else:
+        total = info["batch"]
+        probe = min(total, 256)
+        x = info["sample_rows"](probe)
+        t0 = time.perf_counter()
+        oracle.fft(x)
+        per_row = (time.perf_counter() - t0) / probe
+        rows = int(max(1, min(total, budget_s / max(per_row, 1e-12))))
+        x = info["sample_rows"](rows)
+        t0 = time.perf_counter()
+        oracle.fft(x)
+        dt = time.perf_counter() - t0
+        units, sample = rows, "first %d of %d rows" % (rows, total)
+    return {"value": units * info["oracle_unit"] / dt / 1e9, "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a device-to-device copy of the input's size (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fm = ensure_built()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    step, info = setup_workload(args.workload, dev, fm, torch)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(info["bytes"] // 2, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    gflops = info["flops"] / (ms * 1e-3) / 1e9
+    tbs = info["bytes"] / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC if args.workload == WORKLOADS[0] else "%s GFLOP/s" % args.workload,
+        "value": round(gflops, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": info["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "plan": info["plan"],
+                   **{k: info[k] for k in ("n", "h", "w", "batch", "length") if k in info}},
+        "hbm_tb_s": round(tbs, 3),
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if info["kernels"] == 1:
+        # One kernel per step: the step time measured with events on the launch
+        # stream is that kernel's average duration.
+        achieved = info["bytes"] / (ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": stored_traffic(args.workload)}
+    else:
+        out["roofline"] = None
+        out["roofline_note"] = ("%d kernels per step; per-kernel durations are in the rocprofv3 "
+                                "summaries under profiles/" % info["kernels"])
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, info, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,26 +92,22 @@ void root_of_unity(int64_t m, int64_t M, double* re, double* im)
 }
 
 // Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
-// interleaved doubles: stage s >= 1 holds [r - 1][k] = w_{Ns R}^{r k}.
+// interleaved doubles: stage s >= 1 holds [l][k] = w_{Ns R}^{k 2^l}.
 std::vector<double> stage_table(int logn)
 {
     std::vector<double> t(2 * (size_t)plan_tw_entries(logn));
     for (int s = 1; s < plan_nstages(logn); ++s) {
-        const int R = 1 << plan_stage_logr(logn, s);
+        const int lr = plan_stage_logr(logn, s);
         const int64_t ns = int64_t(1) << plan_stage_lns(logn, s);
         const long off = plan_tw_offset(logn, s);
-        for (int r = 1; r < R; ++r)
+        for (int l = 0; l < lr; ++l)
             for (int64_t k = 0; k < ns; ++k) {
-                const size_t e = (size_t)(off + (r - 1) * ns + k);
-                root_of_unity(r * k, ns * R, &t[2 * e], &t[2 * e + 1]);
+                const size_t e = (size_t)(off + l * ns + k);
+                root_of_unity(k << l, ns << lr, &t[2 * e], &t[2 * e + 1]);
             }
     }
     return t;
 }
-
-struct DeviceTable {
-    void* ptr = nullptr;
-};
 
 }  // namespace
 

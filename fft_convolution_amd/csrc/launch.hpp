@@ -20,6 +20,22 @@ struct BigTwiddle {
     int logn;
 };
 
+// Workgroups of `kernel` (block threads, static LDS only) the device holds at
+// once: blocks per CU at full occupancy times the CU count.  Cached per kernel
+// (all devices are assumed alike).  Returns 0 if the query fails.
+template <typename K>
+int64_t resident_blocks(K kernel, int block)
+{
+    static const int64_t cached = [&]() -> int64_t {
+        int dev = 0, ncu = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess) return 0;
+        return (int64_t)(per > 0 ? per : 1) * ncu;
+    }();
+    return cached;
+}
+
 // Elements per line that the tile kernels stage in LDS at once, and the
 // number of adjacent lines (columns) one workgroup takes.
 int tile_lines(int prec, int logl);

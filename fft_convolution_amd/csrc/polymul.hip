@@ -52,8 +52,9 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
     const int rloc = tid / G::T, t = tid % G::T;
     const int64_t pair = (int64_t)blockIdx.x * RPW + rloc;
     const bool live = pair < batch;
-    double2* my = lds + rloc * G::LDS;
-    auto at = [my](int pos) { return my + pos + (pos >> 4); };
+    const LdsLines<double2, 1> at{lds + rloc * G::LDS, 0};
+    TwBases<double2, LOGN> tb;
+    tb.load(tw, t);
 
     double2 va[G::E], vb[G::E];
 #pragma unroll
@@ -62,13 +63,13 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
         va[i] = double2{(live && n < la) ? (double)a[pair * la + n] : 0.0, 0.0};
         vb[i] = double2{(live && n < lb) ? (double)b[pair * lb + n] : 0.0, 0.0};
     }
-    fft_regs<LOGN>(va, t, tw, at);
+    fft_regs<LOGN>(va, t, tb, at);
     if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN>(vb, t, tw, at);
+    fft_regs<LOGN>(vb, t, tb, at);
 #pragma unroll
     for (int i = 0; i < G::E; ++i) va[i] = cconj(cmul(va[i], vb[i]));
     if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN>(va, t, tw, at);
+    fft_regs<LOGN>(va, t, tb, at);
 
     const int64_t lc = la + lb - 1;
     const double inv_n = 1.0 / (double)G::N;
@@ -113,7 +114,9 @@ void polymul_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* 
         const int64_t n = col + ((int64_t)(t + i * G::T) << logn1);
         v[i] = double2{n < len ? (double)src[n] : 0.0, 0.0};
     }
-    fft_regs<LOGN2>(v, t, tw, TileLds<double2, C>{lds, c});
+    TwBases<double2, LOGN2> tb;
+    tb.load(tw, t);
+    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, C>{lds, c});
     apply_big_twiddle<LOGN2>(v, col, t, big);
     double2* dst = ws + (sig << (logn1 + LOGN2)) + col;
 #pragma unroll
@@ -136,8 +139,9 @@ void polymul_b_kernel(double2* __restrict__ ws_a, const double2* __restrict__ ws
     const int64_t row = (int64_t)blockIdx.x * RPW + rloc;  // pair * N2 + k2
     const bool live = row < nrows;
     const int64_t k2 = row & (((int64_t)1 << logn2) - 1);
-    double2* my = lds + rloc * G::LDS;
-    auto at = [my](int pos) { return my + pos + (pos >> 4); };
+    const LdsLines<double2, 1> at{lds + rloc * G::LDS, 0};
+    TwBases<double2, LOGN1> tb;
+    tb.load(tw, t);
     const int64_t base = (row << LOGN1) + t;
 
     double2 va[G::E], vb[G::E];
@@ -146,13 +150,13 @@ void polymul_b_kernel(double2* __restrict__ ws_a, const double2* __restrict__ ws
         va[i] = live ? ws_a[base + i * G::T] : double2{0.0, 0.0};
         vb[i] = live ? ws_b[base + i * G::T] : double2{0.0, 0.0};
     }
-    fft_regs<LOGN1>(va, t, tw, at);
+    fft_regs<LOGN1>(va, t, tb, at);
     if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN1>(vb, t, tw, at);
+    fft_regs<LOGN1>(vb, t, tb, at);
 #pragma unroll
     for (int i = 0; i < G::E; ++i) va[i] = cconj(cmul(va[i], vb[i]));
     if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN1>(va, t, tw, at);
+    fft_regs<LOGN1>(va, t, tb, at);
     apply_big_twiddle<LOGN1>(va, k2, t, big);
     if (live) {
 #pragma unroll
@@ -180,7 +184,9 @@ void polymul_a2_kernel(const double2* __restrict__ ws_a, int64_t* __restrict__ c
     double2 v[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) v[i] = src[(int64_t)(t + i * G::T) << logn1];
-    fft_regs<LOGN2>(v, t, tw, TileLds<double2, C>{lds, c});
+    TwBases<double2, LOGN2> tb;
+    tb.load(tw, t);
+    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, C>{lds, c});
 
     const double inv_n = 1.0 / (double)((int64_t)1 << (logn1 + LOGN2));
     double worst = 0.0;

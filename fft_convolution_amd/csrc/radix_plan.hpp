@@ -45,21 +45,28 @@ constexpr int plan_stage_lns(int logn, int s)
     return acc;
 }
 
-// Offset (in complex entries) of stage s's table: stage s >= 1 holds
-// (R - 1) Ns entries laid out [r - 1][k], so consecutive butterflies read
-// consecutive entries.  Stage 0 has Ns = 1 and no table.
+// Twiddle table of stage s >= 1: the bases w_{Ns R}^{k 2^l} for l < log2 R and
+// k < Ns, laid out [l][k] so that consecutive butterflies read consecutive
+// entries.  A thread multiplies its R inputs by w^r = w_{Ns R}^{r k}, built as
+// products of the bases over the set bits of r (at most log2 R factors, each
+// read from the exactly rounded table).  Stage 0 has Ns = 1 and no table.
 constexpr long plan_tw_offset(int logn, int s)
 {
     long off = 0;
     for (int q = 1; q < s; ++q)
-        off += (long)((1 << plan_stage_logr(logn, q)) - 1) << plan_stage_lns(logn, q);
+        off += (long)plan_stage_logr(logn, q) << plan_stage_lns(logn, q);
     return off;
 }
 
 constexpr long plan_tw_entries(int logn) { return plan_tw_offset(logn, plan_nstages(logn)); }
 
 // LDS slots for `n` elements with one pad slot after every 16, which spreads
-// the power-of-two strides of the stage writes over all banks.
+// the power-of-two strides of the stage writes over all banks.  The slot of
+// element f is f + floor(f / 16); for every access the engine makes (a base
+// f0 plus a delta that is a multiple of a power of two g with f0 mod 16 < g,
+// or of 16) the slot of f0 + d is slot(f0) + lds_off(d), a compile-time
+// constant, so the per-element LDS addresses cost no instructions.
 constexpr int lds_padded(int n) { return n + (n >> 4); }
+constexpr int lds_off(int d) { return d + (d >> 4); }
 
 }  // namespace fftmi

@@ -13,6 +13,14 @@ namespace fftmi {
 // Rows per workgroup: at least 256 threads per workgroup.
 template <int LOGN> constexpr int rows_per_wg() { return Geometry<LOGN>::T >= 256 ? 1 : 256 / Geometry<LOGN>::T; }
 
+// Persistent: workgroup b transforms row groups b, b + gridDim.x, ... (grid =
+// the number of workgroups the chip holds at once), loading its twiddle bases
+// once.  Where a thread's share of a row is small enough (<= 128 bytes), the
+// next group's loads are issued before the current group is transformed, so
+// every workgroup keeps HBM reads in flight through its compute and LDS
+// phases; larger shares would cost more occupancy than the prefetch gains.
+template <typename V, int LOGN> constexpr bool rows_prefetch() { return Geometry<LOGN>::E * sizeof(V) <= 128; }
+
 template <typename V, int LOGN, bool CONJ_IN, bool CONJ_OUT>
 __global__ __launch_bounds__(Geometry<LOGN>::T * rows_per_wg<LOGN>())
 void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
@@ -25,23 +33,63 @@ void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
     const int tid = threadIdx.x;
     const int rloc = tid / G::T;
     const int t = tid % G::T;
-    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
-    const bool live = row < nrows;
-    const int64_t base = row * G::N + t;
+    const int64_t ngroups = (nrows + RPW - 1) / RPW;
+    int64_t g = blockIdx.x;
+    if (g >= ngroups) return;  // uniform over the workgroup
 
-    V v[G::E];
+    TwBases<V, LOGN> tb;
+    tb.load(tw, t);
+    const LdsLines<V, 1> L{lds + rloc * G::LDS, 0};
+
+    auto load = [&](V (&v)[G::E], int64_t grp) {
+        const int64_t row = grp * RPW + rloc;
+        if (row < nrows) {
+            const V* p = in + row * G::N + t;
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) {
-        V x = live ? in[base + i * G::T] : V{0, 0};
-        v[i] = CONJ_IN ? cconj(x) : x;
-    }
-    V* my = lds + rloc * G::LDS;
-    fft_regs<LOGN>(v, t, tw, [my](int pos) { return my + pos + (pos >> 4); });
-    if (live) {
+            for (int i = 0; i < G::E; ++i) {
+                const V x = ld_stream(p + i * G::T);
+                v[i] = CONJ_IN ? cconj(x) : x;
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < G::E; ++i) {
-            V y = v[i];
-            out[base + i * G::T] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
+            for (int i = 0; i < G::E; ++i) v[i] = V{0, 0};
+        }
+    };
+
+    auto store = [&](const V (&v)[G::E], int64_t grp) {
+        const int64_t row = grp * RPW + rloc;
+        if (row < nrows) {
+            V* p = out + row * G::N + t;
+#pragma unroll
+            for (int i = 0; i < G::E; ++i) {
+                const V y = v[i];
+                st_stream(p + i * G::T, CONJ_OUT ? V{y.x * scale, -y.y * scale} : y);
+            }
+        }
+    };
+
+    V cur[G::E];
+    if constexpr (rows_prefetch<V, LOGN>()) {
+        load(cur, g);
+        for (;;) {
+            const int64_t gn = g + gridDim.x;
+            const bool more = gn < ngroups;
+            V nxt[G::E];
+            if (more) load(nxt, gn);
+            fft_regs<LOGN>(cur, t, tb, L);
+            store(cur, g);
+            if (!more) break;
+            if constexpr (G::S > 1) __syncthreads();  // LDS reads of this group done
+            g = gn;
+#pragma unroll
+            for (int i = 0; i < G::E; ++i) cur[i] = nxt[i];
+        }
+    } else {
+        for (; g < ngroups; g += gridDim.x) {
+            load(cur, g);
+            fft_regs<LOGN>(cur, t, tb, L);
+            store(cur, g);
+            if constexpr (G::S > 1) __syncthreads();  // LDS reads of this group done
         }
     }
 }
@@ -51,12 +99,14 @@ static hipError_t launch_rows_t(const void* in, void* out, int64_t nrows, const 
                                 hipStream_t stream)
 {
     constexpr int RPW = rows_per_wg<LOGN>();
-    const int64_t blocks = (nrows + RPW - 1) / RPW;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    constexpr int BLOCK = Geometry<LOGN>::T * RPW;
+    const int64_t groups = (nrows + RPW - 1) / RPW;
+    const int64_t resident = resident_blocks(rows_kernel<V, LOGN, CI, CO>, BLOCK);
+    if (resident <= 0) return hipErrorInvalidConfiguration;
+    const int64_t blocks = groups < resident ? groups : resident;
     using Rl = typename real_of<V>::type;
-    hipLaunchKernelGGL((rows_kernel<V, LOGN, CI, CO>), dim3((unsigned)blocks),
-                       dim3(Geometry<LOGN>::T * RPW), 0, stream, (const V*)in, (V*)out, nrows,
-                       (const V*)tw, (Rl)scale);
+    hipLaunchKernelGGL((rows_kernel<V, LOGN, CI, CO>), dim3((unsigned)blocks), dim3(BLOCK), 0, stream,
+                       (const V*)in, (V*)out, nrows, (const V*)tw, (Rl)scale);
     return hipGetLastError();
 }
 

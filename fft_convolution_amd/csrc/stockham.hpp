@@ -170,6 +170,34 @@ template <> struct Dft<16> : DftSplit<4, 4> {};
 template <> struct Dft<32> : DftSplit<4, 8> {};
 
 // ---------------------------------------------------------------------------
+// Streaming global access: every element is read once and written once, so
+// loads and stores are marked nontemporal (they bypass cache retention).
+// ---------------------------------------------------------------------------
+typedef float nt_f2 __attribute__((ext_vector_type(2)));
+typedef double nt_d2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float2 ld_stream(const float2* p)
+{
+    const nt_f2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f2*>(p));
+    return float2{v.x, v.y};
+}
+__device__ __forceinline__ double2 ld_stream(const double2* p)
+{
+    const nt_d2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_d2*>(p));
+    return double2{v.x, v.y};
+}
+__device__ __forceinline__ void st_stream(float2* p, float2 x)
+{
+    const nt_f2 v = {x.x, x.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_f2*>(p));
+}
+__device__ __forceinline__ void st_stream(double2* p, double2 x)
+{
+    const nt_d2 v = {x.x, x.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_d2*>(p));
+}
+
+// ---------------------------------------------------------------------------
 // The workgroup engine.
 // ---------------------------------------------------------------------------
 template <int LOGN> struct Geometry {
@@ -181,68 +209,128 @@ template <int LOGN> struct Geometry {
     static constexpr int LDS = S > 1 ? lds_padded(N) : 0;  // LDS slots per transform
 };
 
-// One Stockham stage of radix 2^LR over span Ns = 2^LNS on the registers of
-// thread t.  Not the last stage: outputs go to LDS.  Last stage: outputs
-// stay in v (position t + i T in v[i]).
-template <int LOGN, int STAGE, typename V, typename LdsAt>
-__device__ __forceinline__ void fft_stage(V (&v)[Geometry<LOGN>::E], int t, const V* __restrict__ tw,
-                                          LdsAt lds_at)
+template <int LOGN, int STAGE> struct StageInfo {
+    using G = Geometry<LOGN>;
+    static constexpr int LR = plan_stage_logr(LOGN, STAGE), R = 1 << LR;
+    static constexpr int LNS = plan_stage_lns(LOGN, STAGE), NS = 1 << LNS;
+    static constexpr int B = G::E / R;           // butterflies per thread
+    static constexpr bool TW = NS > 1;           // stage 0 needs no twiddles
+    static constexpr int NB = TW ? B * LR : 1;   // twiddle bases per thread
+    static constexpr bool LAST = STAGE == G::S - 1;
+};
+
+// The twiddle bases a thread needs for every stage, loaded once (they depend
+// only on the thread's position t) and kept in registers.
+template <typename V, int LOGN, int STAGE = 0, bool END = (STAGE >= Geometry<LOGN>::S)>
+struct TwBases {
+    using I = StageInfo<LOGN, STAGE>;
+    V w[I::NB];
+    TwBases<V, LOGN, STAGE + 1> next;
+    __device__ __forceinline__ void load(const V* __restrict__ tw, int t)
+    {
+        if constexpr (I::TW) {
+            const V* __restrict__ tws = tw + plan_tw_offset(LOGN, STAGE);
+#pragma unroll
+            for (int b = 0; b < I::B; ++b) {
+                const int k = (t + b * Geometry<LOGN>::T) & (I::NS - 1);
+#pragma unroll
+                for (int l = 0; l < I::LR; ++l) w[b * I::LR + l] = tws[l * I::NS + k];
+            }
+        }
+        next.load(tw, t);
+    }
+    template <int Q> __device__ __forceinline__ const V* get() const
+    {
+        if constexpr (Q == STAGE) return w;
+        else return next.template get<Q>();
+    }
+};
+template <typename V, int LOGN, int STAGE> struct TwBases<V, LOGN, STAGE, true> {
+    __device__ __forceinline__ void load(const V*, int) {}
+};
+
+// LDS layout of C interleaved transforms (line c of C): element `pos` of line
+// c sits at f = pos C + c, slot f + floor(f / 16).  C = 1 is one transform.
+template <typename V, int C> struct LdsLines {
+    V* base;
+    int c;
+    __device__ __forceinline__ V* ptr(int pos) const
+    {
+        const int f = pos * C + c;
+        return base + f + (f >> 4);
+    }
+    static constexpr int off(int dpos) { return lds_off(dpos * C); }
+};
+
+// u[r] *= w^r for r = 1 .. R-1, w^r built from the bases w^{2^l} (wb[l]).
+template <int LR, typename V>
+__device__ __forceinline__ void apply_stage_twiddles(V* u, const V* wb)
+{
+    constexpr int R = 1 << LR;
+    V p[R];
+    p[1] = wb[0];
+#pragma unroll
+    for (int l = 1; l < LR; ++l) {
+        p[1 << l] = wb[l];
+#pragma unroll
+        for (int i = 1; i < (1 << l); ++i) p[(1 << l) + i] = cmul(p[i], wb[l]);
+    }
+#pragma unroll
+    for (int r = 1; r < R; ++r) u[r] = cmul(u[r], p[r]);
+}
+
+// One Stockham stage on the registers of thread t.  Not the last stage:
+// outputs go to LDS in the stage's output order.  Last stage: outputs stay in
+// v (position t + i T in v[i]).
+template <int LOGN, int STAGE, typename V, typename TB, typename L>
+__device__ __forceinline__ void fft_stage(V (&v)[Geometry<LOGN>::E], int t, const TB& tb, const L& lds)
 {
     using G = Geometry<LOGN>;
-    constexpr int LR = plan_stage_logr(LOGN, STAGE), R = 1 << LR;
-    constexpr int LNS = plan_stage_lns(LOGN, STAGE), NS = 1 << LNS;
-    constexpr int B = G::E / R;
-    constexpr bool LAST = STAGE == G::S - 1;
-    const V* __restrict__ tws = tw + plan_tw_offset(LOGN, STAGE);
+    using I = StageInfo<LOGN, STAGE>;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        V u[R];
+    for (int b = 0; b < I::B; ++b) {
+        V u[I::R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) u[r] = v[b + r * B];
-        const int j = t + b * G::T;
-        const int k = j & (NS - 1);
-        if constexpr (NS > 1) {
+        for (int r = 0; r < I::R; ++r) u[r] = v[b + r * I::B];
+        if constexpr (I::TW) apply_stage_twiddles<I::LR>(u, tb.template get<STAGE>() + b * I::LR);
+        Dft<I::R>::run(u);
+        if constexpr (I::LAST) {
 #pragma unroll
-            for (int r = 1; r < R; ++r) u[r] = cmul(u[r], tws[(r - 1) * NS + k]);
-        }
-        Dft<R>::run(u);
-        if constexpr (LAST) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) v[b + r * B] = u[r];
+            for (int r = 0; r < I::R; ++r) v[b + r * I::B] = u[r];
         } else {
-            const int base = ((j >> LNS) << (LNS + LR)) + k;
+            const int j = t + b * G::T;
+            const int base = ((j >> I::LNS) << (I::LNS + I::LR)) + (j & (I::NS - 1));
+            V* wp = lds.ptr(base);
 #pragma unroll
-            for (int r = 0; r < R; ++r) *lds_at(base + r * NS) = u[r];
+            for (int r = 0; r < I::R; ++r) wp[L::off(r * I::NS)] = u[r];
         }
     }
 }
 
-template <int LOGN, int STAGE, typename V, typename LdsAt>
-__device__ __forceinline__ void fft_stages_from(V (&v)[Geometry<LOGN>::E], int t, const V* __restrict__ tw,
-                                                LdsAt lds_at)
+template <int LOGN, int STAGE, typename V, typename TB, typename L>
+__device__ __forceinline__ void fft_stages_from(V (&v)[Geometry<LOGN>::E], int t, const TB& tb, const L& lds)
 {
     using G = Geometry<LOGN>;
     if constexpr (STAGE < G::S) {
         if constexpr (STAGE > 0) {
             __syncthreads();  // the previous stage's LDS writes are visible
+            const V* rp = lds.ptr(t);
 #pragma unroll
-            for (int i = 0; i < G::E; ++i) v[i] = *lds_at(t + i * G::T);
+            for (int i = 0; i < G::E; ++i) v[i] = rp[L::off(i * G::T)];
             if constexpr (STAGE < G::S - 1) __syncthreads();  // all reads done before rewriting
         }
-        fft_stage<LOGN, STAGE>(v, t, tw, lds_at);
-        fft_stages_from<LOGN, STAGE + 1>(v, t, tw, lds_at);
+        fft_stage<LOGN, STAGE>(v, t, tb, lds);
+        fft_stages_from<LOGN, STAGE + 1>(v, t, tb, lds);
     }
 }
 
 // Forward transform of N = 2^LOGN points held as v[i] = x[t + i T]; on return
 // v[i] = X[t + i T].  Every thread of the workgroup must call it (barriers).
-// lds_at(pos) returns this transform's LDS slot for position pos.  If the
-// caller reuses the LDS afterwards it must put a barrier first.
-template <int LOGN, typename V, typename LdsAt>
-__device__ __forceinline__ void fft_regs(V (&v)[Geometry<LOGN>::E], int t, const V* __restrict__ tw,
-                                         LdsAt lds_at)
+// If the caller reuses the LDS afterwards it must put a barrier first.
+template <int LOGN, typename V, typename TB, typename L>
+__device__ __forceinline__ void fft_regs(V (&v)[Geometry<LOGN>::E], int t, const TB& tb, const L& lds)
 {
-    fft_stages_from<LOGN, 0>(v, t, tw, lds_at);
+    fft_stages_from<LOGN, 0>(v, t, tb, lds);
 }
 
 }  // namespace fftmi

@@ -24,19 +24,6 @@ template <int LOGN, int C> constexpr int tile_lds_slots()
     return Geometry<LOGN>::S > 1 ? lds_padded(C * Geometry<LOGN>::N) : 1;
 }
 
-// LDS slot of position `pos` of line c: the C lines are interleaved
-// (f = pos C + c) so that the lanes of one instruction, which run over c
-// fastest, hit consecutive slots; one pad slot per 16.
-template <typename V, int C> struct TileLds {
-    V* lds;
-    int c;
-    __device__ __forceinline__ V* operator()(int pos) const
-    {
-        const int f = pos * C + c;
-        return lds + f + (f >> 4);
-    }
-};
-
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
 // b mod 8).  Give each XCD a contiguous range of tiles instead, so that
 // neighbouring tiles -- which share cache lines when a tile's row segment is

@@ -41,7 +41,9 @@ void cols2d_kernel(const V* in, V* out, int64_t tiles_per_img, int64_t w, const 
     V v[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) v[i] = live ? in[base + i * step] : V{0, 0};
-    fft_regs<LOGN>(v, t, tw, TileLds<V, C>{lds, c});
+    TwBases<V, LOGN> tb;
+    tb.load(tw, t);
+    fft_regs<LOGN>(v, t, tb, LdsLines<V, C>{lds, c});
     if (live) {
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
@@ -75,7 +77,9 @@ void fourstep_a_kernel(const V* in, V* ws, int64_t n1, int64_t tiles_per_sig, co
         V x = in[base + i * step];
         v[i] = CONJ_IN ? cconj(x) : x;
     }
-    fft_regs<LOGN>(v, t, tw, TileLds<V, C>{lds, c});
+    TwBases<V, LOGN> tb;
+    tb.load(tw, t);
+    fft_regs<LOGN>(v, t, tb, LdsLines<V, C>{lds, c});
     // element i sits at k2 = t + i T: multiply by w_N^{n1 (t + i T)}
     apply_big_twiddle<LOGN>(v, (int64_t)col, t, BigTw<V>{big_hi, big_lo, lbits, logn_total});
 #pragma unroll
@@ -105,7 +109,9 @@ void fourstep_b_kernel(const V* ws, V* out, int64_t n2, int64_t tiles_per_sig, c
     V v[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) v[i] = ws[in_base + i * G::T];
-    fft_regs<LOGN>(v, t, tw, TileLds<V, C>{lds, c});
+    TwBases<V, LOGN> tb;
+    tb.load(tw, t);
+    fft_regs<LOGN>(v, t, tb, LdsLines<V, C>{lds, c});
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
         V y = v[i];

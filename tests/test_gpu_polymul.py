@@ -1,0 +1,112 @@
+"""Polynomial products on the GPU: bit-exact int64 against the fp64 oracle's
+FFT route, against the exact schoolbook convolution (full on small cases,
+sampled at full size) and against evaluation mod p = 2^61 - 1 at random
+points (Schwartz-Zippel), which covers every coefficient."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fft_convolution_amd as fm
+import oracle
+from fft_convolution_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_mul(a_np, b_np, n, dev):
+    a = torch.from_numpy(np.ascontiguousarray(a_np)).to(dev)
+    b = torch.from_numpy(np.ascontiguousarray(b_np)).to(dev)
+    plan = fm.Plan(n, torch.complex128)
+    c, r = plan.poly_mul(a, b, residual=True)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), float(r.item())
+
+
+@pytest.mark.parametrize("la,lb,batch", [
+    (1, 1, 3), (1, 5, 2), (2, 3, 4), (7, 9, 3), (16, 17, 2), (64, 64, 5), (100, 29, 3),
+    (1000, 24, 2), (2048, 2049, 2), (2048, 2048, 1),
+])
+def test_small_exact(dev, la, lb, batch):
+    print("case la=%d lb=%d batch=%d" % (la, lb, batch), flush=True)
+    rng = np.random.default_rng(la * 1000 + lb)
+    a = rng.integers(-1000, 1000, size=(batch, la))
+    b = rng.integers(-1000, 1000, size=(batch, lb))
+    n = 1 << max(0, math.ceil(math.log2(la + lb - 1)))
+    c, resid = _gpu_mul(a, b, n, dev)
+    assert np.array_equal(c, oracle.schoolbook(a, b))
+    assert resid < 0.1
+
+
+@pytest.mark.parametrize("la,lb,n,batch", [
+    (3000, 1097, 4096, 2),     # LDS-resident, largest fp64 row
+    (4096, 4097, 8192, 2),     # smallest four-step
+    (5000, 3000, 16384, 3),    # four-step, ragged lengths
+    (1 << 15, 1 << 15, 1 << 16, 2),
+    (10, 20, 1 << 16, 1),      # mostly zero padding
+])
+def test_larger_against_oracle(dev, la, lb, n, batch):
+    print("case la=%d lb=%d n=%d batch=%d" % (la, lb, n, batch), flush=True)
+    a, b = wl.random_polys(max(la, lb), batch, seed=la + lb)
+    a, b = a[:, :la], b[:, :lb]
+    c, resid = _gpu_mul(a, b, n, dev)
+    ref, _ = oracle.polymul_fft(a, b, n=n)
+    assert np.array_equal(c, ref)
+    ks = np.unique(np.concatenate([[0, 1, la + lb - 2], np.random.default_rng(0).integers(0, la + lb - 1, 50)]))
+    assert np.array_equal(c[:, ks], oracle.schoolbook_sample(a, b, ks))
+    assert resid < 0.1
+
+
+def test_closed_forms(dev):
+    L = 4096
+    k = np.arange(2 * L - 1)
+    tri = np.minimum(k + 1, 2 * L - 1 - k)
+    c, _ = _gpu_mul(np.full((1, L), 999), np.full((1, L), 999), 2 * L, dev)
+    assert np.array_equal(c[0], 999 * 999 * tri)
+    p, q = 30, 25
+    c, _ = _gpu_mul(np.array([[math.comb(p, i) for i in range(p + 1)]]),
+                    np.array([[math.comb(q, i) for i in range(q + 1)]]), 64, dev)
+    assert c[0].tolist() == [math.comb(p + q, i) for i in range(p + q + 1)]
+
+
+def test_workload_32_pairs_of_2p18(dev):
+    # The full workload in the launch the benchmark times: bit-exact against
+    # the oracle's fp64 FFT route on all 32 x (2^19 - 1) coefficients, sampled
+    # schoolbook, the sum invariants and mod-p evaluation on every pair.
+    L = 1 << 18
+    a, b = wl.workload_input("polymul_l262144_b32")
+    c, resid = _gpu_mul(a, b, 1 << 19, dev)
+    assert c.shape == (32, 2 * L - 1)
+    ref, ref_resid = oracle.polymul_fft(a, b, n=1 << 19)
+    assert np.array_equal(c, ref)
+    assert resid < 0.1
+    rng = np.random.default_rng(5)
+    ks = np.unique(np.concatenate([[0, 1, L - 1, L, 2 * L - 3, 2 * L - 2], rng.integers(0, 2 * L - 1, 250)]))
+    assert np.array_equal(c[:, ks], oracle.schoolbook_sample(a, b, ks))
+    for p in range(32):
+        assert int(c[p].sum()) == int(a[p].sum()) * int(b[p].sum())
+        z = int(rng.integers(2, oracle.MOD_P - 1))
+        assert oracle.poly_eval_mod(c[p], z) == \
+            oracle.poly_eval_mod(a[p], z) * oracle.poly_eval_mod(b[p], z) % oracle.MOD_P
+
+
+def test_validation_on_device(dev):
+    plan32 = fm.Plan(64, torch.complex64)
+    plan = fm.Plan(64, torch.complex128)
+    a = torch.ones(2, 40, dtype=torch.int64, device=dev)
+    b = torch.ones(2, 30, dtype=torch.int64, device=dev)
+    c = torch.empty(2, 69, dtype=torch.int64, device=dev)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul(plan32.handle, a, 40, b, 30, c, 2)
+    assert e.value.status == fm.FFT_ERR_PRECISION
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul(plan.handle, a, 40, b, 30, c, 2)   # 69 > 64
+    assert e.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul(plan.handle, a, 0, b, 30, c, 2)
+    assert e.value.status == fm.FFT_ERR_INVALID_ARG
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul(plan.handle, a, 20, b, 30, a, 2)   # c overlaps a
+    assert e.value.status == fm.FFT_ERR_OVERLAP
+    fm.fft_poly_mul(plan.handle, a, 20, b, 30, c, 0)        # batch 0: no-op
