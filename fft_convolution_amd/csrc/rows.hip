@@ -13,14 +13,11 @@ namespace fftmi {
 // Rows per workgroup: at least 256 threads per workgroup.
 template <int LOGN> constexpr int rows_per_wg() { return Geometry<LOGN>::T >= 256 ? 1 : 256 / Geometry<LOGN>::T; }
 
-// Persistent: workgroup b transforms row groups b, b + gridDim.x, ... (grid =
-// the number of workgroups the chip holds at once), loading its twiddle bases
-// once.  Where a thread's share of a row is small enough (<= 128 bytes), the
-// next group's loads are issued before the current group is transformed, so
-// every workgroup keeps HBM reads in flight through its compute and LDS
-// phases; larger shares would cost more occupancy than the prefetch gains.
-template <typename V, int LOGN> constexpr bool rows_prefetch() { return Geometry<LOGN>::E * sizeof(V) <= 128; }
-
+// One workgroup per group of RPW rows; the hardware dispatcher starts a new
+// workgroup as soon as one retires, so the load, compute and store phases of
+// the workgroups resident on a CU overlap.  (Measured on MI355X for 16384 rows
+// of 4096 points: this beats a persistent grid with a one-row register
+// prefetch, 174 us against 187-201 us per launch.)
 template <typename V, int LOGN, bool CONJ_IN, bool CONJ_OUT>
 __global__ __launch_bounds__(Geometry<LOGN>::T * rows_per_wg<LOGN>())
 void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
@@ -33,63 +30,26 @@ void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
     const int tid = threadIdx.x;
     const int rloc = tid / G::T;
     const int t = tid % G::T;
-    const int64_t ngroups = (nrows + RPW - 1) / RPW;
-    int64_t g = blockIdx.x;
-    if (g >= ngroups) return;  // uniform over the workgroup
+    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
+    const bool live = row < nrows;
 
     TwBases<V, LOGN> tb;
     tb.load(tw, t);
-    const LdsLines<V, 1> L{lds + rloc * G::LDS, 0};
 
-    auto load = [&](V (&v)[G::E], int64_t grp) {
-        const int64_t row = grp * RPW + rloc;
-        if (row < nrows) {
-            const V* p = in + row * G::N + t;
+    V v[G::E];
+    const V* src = in + row * G::N + t;
 #pragma unroll
-            for (int i = 0; i < G::E; ++i) {
-                const V x = ld_stream(p + i * G::T);
-                v[i] = CONJ_IN ? cconj(x) : x;
-            }
-        } else {
+    for (int i = 0; i < G::E; ++i) {
+        const V x = live ? ld_stream(src + i * G::T) : V{0, 0};
+        v[i] = CONJ_IN ? cconj(x) : x;
+    }
+    fft_regs<LOGN>(v, t, tb, LdsLines<V, 1>{lds + rloc * G::LDS, 0});
+    if (live) {
+        V* dst = out + row * G::N + t;
 #pragma unroll
-            for (int i = 0; i < G::E; ++i) v[i] = V{0, 0};
-        }
-    };
-
-    auto store = [&](const V (&v)[G::E], int64_t grp) {
-        const int64_t row = grp * RPW + rloc;
-        if (row < nrows) {
-            V* p = out + row * G::N + t;
-#pragma unroll
-            for (int i = 0; i < G::E; ++i) {
-                const V y = v[i];
-                st_stream(p + i * G::T, CONJ_OUT ? V{y.x * scale, -y.y * scale} : y);
-            }
-        }
-    };
-
-    V cur[G::E];
-    if constexpr (rows_prefetch<V, LOGN>()) {
-        load(cur, g);
-        for (;;) {
-            const int64_t gn = g + gridDim.x;
-            const bool more = gn < ngroups;
-            V nxt[G::E];
-            if (more) load(nxt, gn);
-            fft_regs<LOGN>(cur, t, tb, L);
-            store(cur, g);
-            if (!more) break;
-            if constexpr (G::S > 1) __syncthreads();  // LDS reads of this group done
-            g = gn;
-#pragma unroll
-            for (int i = 0; i < G::E; ++i) cur[i] = nxt[i];
-        }
-    } else {
-        for (; g < ngroups; g += gridDim.x) {
-            load(cur, g);
-            fft_regs<LOGN>(cur, t, tb, L);
-            store(cur, g);
-            if constexpr (G::S > 1) __syncthreads();  // LDS reads of this group done
+        for (int i = 0; i < G::E; ++i) {
+            const V y = v[i];
+            st_stream(dst + i * G::T, CONJ_OUT ? V{y.x * scale, -y.y * scale} : y);
         }
     }
 }
@@ -100,10 +60,8 @@ static hipError_t launch_rows_t(const void* in, void* out, int64_t nrows, const 
 {
     constexpr int RPW = rows_per_wg<LOGN>();
     constexpr int BLOCK = Geometry<LOGN>::T * RPW;
-    const int64_t groups = (nrows + RPW - 1) / RPW;
-    const int64_t resident = resident_blocks(rows_kernel<V, LOGN, CI, CO>, BLOCK);
-    if (resident <= 0) return hipErrorInvalidConfiguration;
-    const int64_t blocks = groups < resident ? groups : resident;
+    const int64_t blocks = (nrows + RPW - 1) / RPW;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
     hipLaunchKernelGGL((rows_kernel<V, LOGN, CI, CO>), dim3((unsigned)blocks), dim3(BLOCK), 0, stream,
                        (const V*)in, (V*)out, nrows, (const V*)tw, (Rl)scale);

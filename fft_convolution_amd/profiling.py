@@ -1,0 +1,153 @@
+"""Summaries of rocprofv3 output for the files under ``profiles/``.
+
+Two subcommands, both reading the CSV output of ``rocprofv3 --output-format csv``:
+
+``stats``   -- per-kernel durations from a ``--kernel-trace --stats`` run:
+               python -m fft_convolution_amd.profiling stats DIR --out profiles/X.md --cmd "..."
+
+``traffic`` -- HBM bytes per launch from two ``--pmc`` runs (FETCH_SIZE, then
+               WRITE_SIZE, each in KiB per dispatch) of a command that also runs
+               a plain elementwise copy of known size (``bench.py
+               --copy-calibration``).  Each counter is scaled by
+               known bytes / the counter's reading for that copy:
+               python -m fft_convolution_amd.profiling traffic --fetch DIR1 --write DIR2 \\
+                   --kernel rows_kernel --copy-bytes B --workload W --out profiles/traffic_W.json
+
+The traffic record carries a digest of the kernel sources; ``bench.py``
+reports it only while the sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+
+def _find(dirpath: str, suffix: str) -> list[str]:
+    hits = sorted(glob.glob(os.path.join(dirpath, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit("no *%s under %s" % (suffix, dirpath))
+    return hits
+
+
+def kernel_stats(dirpath: str) -> list[dict]:
+    rows = []
+    for path in _find(dirpath, "kernel_stats.csv"):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append({"name": r["Name"], "calls": int(r["Calls"]),
+                             "total_ns": float(r["TotalDurationNs"]), "avg_ns": float(r["AverageNs"]),
+                             "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+                             "pct": float(r["Percentage"])})
+    rows.sort(key=lambda r: -r["total_ns"])
+    return rows
+
+
+def counter_values(dirpath: str, counter: str) -> dict[str, list[float]]:
+    """kernel name -> list of per-dispatch values of `counter`."""
+    out: dict[str, list[float]] = {}
+    for path in _find(dirpath, "counter_collection.csv"):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(values: dict[str, list[float]], needle: str) -> tuple[str, list[float]]:
+    names = [k for k in values if needle in k]
+    if not names:
+        raise SystemExit("no kernel matching %r among %s" % (needle, list(values)))
+    name = max(names, key=lambda k: len(values[k]))
+    return name, values[name]
+
+
+def cmd_stats(args):
+    rows = kernel_stats(args.dir)
+    lines = ["# rocprofv3 kernel summary: %s" % args.title, "",
+             "Command:", "", "```", args.cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["name"].replace("HIP_vector_type<float, 2u>", "float2").replace(
+            "HIP_vector_type<double, 2u>", "double2").replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (
+            name, r["calls"], r["avg_ns"] / 1e3, r["min_ns"] / 1e3, r["max_ns"] / 1e3, r["pct"]))
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def cmd_traffic(args):
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from bench import kernel_sources_digest  # the same digest bench.py checks
+    fetch = counter_values(args.fetch, "FETCH_SIZE")
+    write = counter_values(args.write, "WRITE_SIZE")
+    kname, kf = _pick(fetch, args.kernel)
+    _, kw = _pick(write, args.kernel)
+    cname, cf = _pick(fetch, args.copy_kernel)
+    _, cw = _pick(write, args.copy_kernel)
+    kib = 1024.0
+    # The copy moves copy_bytes in and copy_bytes out.
+    f_fetch = args.copy_bytes / (statistics.median(cf) * kib)
+    f_write = args.copy_bytes / (statistics.median(cw) * kib)
+    fetch_b = statistics.median(kf) * kib * f_fetch
+    write_b = statistics.median(kw) * kib * f_write
+    rec = {
+        "workload": args.workload,
+        "kernel": kname,
+        "fetch_kib_per_dispatch_raw": statistics.median(kf),
+        "write_kib_per_dispatch_raw": statistics.median(kw),
+        "copy_kernel": cname,
+        "copy_bytes_each_way": args.copy_bytes,
+        "copy_fetch_kib_raw": statistics.median(cf),
+        "copy_write_kib_raw": statistics.median(cw),
+        "scale_fetch": f_fetch,
+        "scale_write": f_write,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "traffic_bytes_per_launch": fetch_b + write_b,
+        "algorithmic_bytes_per_launch": args.algorithmic_bytes,
+        "commands": args.cmd,
+        "kernel_sources_sha256": kernel_sources_digest(),
+    }
+    with open(args.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--out")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="")
+    s.set_defaults(fn=cmd_stats)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-kernel", default="elementwise")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd", nargs="*", default=[])
+    t.set_defaults(fn=cmd_traffic)
+    args = ap.parse_args(argv)
+    args.fn(args)
+
+
+if __name__ == "__main__":
+    main()
