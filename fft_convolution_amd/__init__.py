@@ -241,6 +241,9 @@ class Plan:
         else:
             self._check_tensor(out)
         ws_bytes = fft_workspace_size(self.handle, batch)
+        # A rank-2 plan uses its workspace only for an in-place call.
+        if self.rank == 2 and out.data_ptr() != x.data_ptr():
+            ws_bytes = 0
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
         fn(self.handle, direction, x, out, batch, ws)
         return out

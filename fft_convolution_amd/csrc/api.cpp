@@ -111,7 +111,16 @@ std::vector<double> stage_table(int logn)
 
 }  // namespace
 
-enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_FOURSTEP = 2, PATH_2D = 3 };
+enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_2D = 3 };
+
+// One super-stage pass of a multi-pass plan.
+struct PassPlan {
+    int logr = 0, logns = 0, kind = 0;
+    const void* tw = nullptr;  // stage table for 2^logr (owned by the plan's table list)
+    void* big_hi = nullptr;    // tables for w_M, M = 2^(logns + logr) (owned)
+    void* big_lo = nullptr;
+    int big_lbits = 0;
+};
 
 struct fft_plan {
     int rank = 0;
@@ -121,15 +130,19 @@ struct fft_plan {
     int path = PATH_COPY;
     int64_t n = 1;          // points per transform (H*W for 2D)
     int logn = 0;
-    // rank 1, rows:      tw_a = table for N
-    // rank 1, four-step: tw_a = rows (N1), tw_b = columns (N2), big_* = w_N
-    // rank 2:            tw_a = rows (W), tw_b = columns (H)
+    // rank 1, rows:      tw_a = stage table for N
+    // rank 1, multipass: passes[], poly-mul four-step: tw_a = rows (N1), tw_b = columns (N2), big_* = w_N
+    // rank 2:            tw_a = rows (W), tw_b = columns (Lc = H / F), big_* = w_H (F > 1)
     int log_a = 0, log_b = 0;
     void* tw_a = nullptr;
     void* tw_b = nullptr;
     void* big_hi = nullptr;
     void* big_lo = nullptr;
     int big_lbits = 0;
+    int logf = 0;  // rank 2: log2 of the column super-stage folded into the row pass
+    int npass = 0;
+    PassPlan passes[4];
+    void* pass_tw[4] = {nullptr, nullptr, nullptr, nullptr};
     size_t elem = 8;
 };
 
@@ -174,7 +187,26 @@ void free_plan(fft_plan* p)
     void* ptrs[] = {p->tw_a, p->tw_b, p->big_hi, p->big_lo};
     for (void* q : ptrs)
         if (q) hipFree(q);
+    for (int i = 0; i < 4; ++i) {
+        if (p->pass_tw[i]) hipFree(p->pass_tw[i]);
+        if (p->passes[i].big_hi) hipFree(p->passes[i].big_hi);
+        if (p->passes[i].big_lo) hipFree(p->passes[i].big_lo);
+    }
     delete p;
+}
+
+// Tables for w_M^m = hi[m >> L] lo[m & (2^L - 1)], M = 2^logm, L = ceil(logm / 2).
+int upload_big(int logm, int prec, void** hi_dev, void** lo_dev, int* lbits)
+{
+    *lbits = (logm + 1) / 2;
+    const int64_t m = int64_t(1) << logm;
+    const int64_t nlo = int64_t(1) << *lbits, nhi = m >> *lbits;
+    std::vector<double> lo(2 * nlo), hi(2 * nhi);
+    for (int64_t q = 0; q < nlo; ++q) root_of_unity(q, m, &lo[2 * q], &lo[2 * q + 1]);
+    for (int64_t q = 0; q < nhi; ++q) root_of_unity(q << *lbits, m, &hi[2 * q], &hi[2 * q + 1]);
+    int st = upload(lo, prec, lo_dev);
+    if (st == FFT_OK) st = upload(hi, prec, hi_dev);
+    return st;
 }
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
@@ -224,10 +256,19 @@ int check_device(const fft_plan* plan)
     return FFT_OK;
 }
 
+// Workspace of an exec call: the multi-pass transform ping-pongs through one
+// signal-sized buffer; the folded 2D transform needs one only in place.
 size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
-    return p->path == PATH_FOURSTEP ? (size_t)batch * (size_t)p->n * p->elem : 0;
+    const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_2D && p->logf > 0);
+    return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
+
+// Largest radix per super-stage pass, and the preferred / largest column
+// length of the 2D column pass (LDS: lines of 128 bytes x length must fit).
+constexpr int kMaxPassLog = 9;
+int col_pref_log(int prec) { return prec == FFT_C32 ? 10 : 9; }
+int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
 
 }  // namespace
 
@@ -295,26 +336,55 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
             p->log_a = p->logn;
             st = upload(stage_table(p->log_a), prec, &p->tw_a);
         } else {
-            p->path = PATH_FOURSTEP;
-            p->log_b = (p->logn + 1) / 2;  // N2, the column length
-            p->log_a = p->logn - p->log_b; // N1, the row length
-            st = upload(stage_table(p->log_a), prec, &p->tw_a);
-            if (st == FFT_OK) st = upload(stage_table(p->log_b), prec, &p->tw_b);
-            // w_N^m = hi[m >> L] lo[m & (2^L - 1)]
-            p->big_lbits = (p->logn + 1) / 2;
-            const int64_t nlo = int64_t(1) << p->big_lbits, nhi = p->n >> p->big_lbits;
-            std::vector<double> lo(2 * nlo), hi(2 * nhi);
-            for (int64_t q = 0; q < nlo; ++q) root_of_unity(q, p->n, &lo[2 * q], &lo[2 * q + 1]);
-            for (int64_t q = 0; q < nhi; ++q) root_of_unity(q << p->big_lbits, p->n, &hi[2 * q], &hi[2 * q + 1]);
-            if (st == FFT_OK) st = upload(lo, prec, &p->big_lo);
-            if (st == FFT_OK) st = upload(hi, prec, &p->big_hi);
+            p->path = PATH_MULTIPASS;
+            // Super-stages of at most 2^9 points, as even as possible, larger first.
+            const int np = (p->logn + kMaxPassLog - 1) / kMaxPassLog;
+            int logns = 0;
+            for (int q = 0; q < np && st == FFT_OK; ++q) {
+                PassPlan& pp = p->passes[q];
+                pp.logr = p->logn / np + (q < p->logn % np ? 1 : 0);
+                pp.logns = logns;
+                pp.kind = q == 0 ? 0 : (q == np - 1 ? 2 : 1);
+                logns += pp.logr;
+                st = upload(stage_table(pp.logr), prec, &p->pass_tw[q]);
+                pp.tw = p->pass_tw[q];
+                if (st == FFT_OK && q > 0) st = upload_big(pp.logns + pp.logr, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
+                const int c = tile_lines_2d(prec, pp.logr);
+                const int64_t bfly = int64_t(1) << (p->logn - pp.logr);
+                if (st == FFT_OK && (c <= 0 || bfly % c || (pp.kind == 1 && (int64_t(1) << pp.logns) % c)))
+                    st = fail(FFT_ERR_UNSUPPORTED_SIZE, "no pass layout for n = %lld", (long long)p->n);
+            }
+            p->npass = np;
+            // The poly-mul four-step tables (fp64 only).
+            if (st == FFT_OK && prec == FFT_C64) {
+                p->log_b = (p->logn + 1) / 2;  // N2, the column length
+                p->log_a = p->logn - p->log_b; // N1, the row length
+                st = upload(stage_table(p->log_a), prec, &p->tw_a);
+                if (st == FFT_OK) st = upload(stage_table(p->log_b), prec, &p->tw_b);
+                if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
+            }
         }
     } else {
         p->path = PATH_2D;
         p->log_a = ilog2(p->dims[1]);  // W
-        p->log_b = ilog2(p->dims[0]);  // H
+        const int logh = ilog2(p->dims[0]);
+        p->logf = 0;
+        if (p->log_a > 0 && logh > col_pref_log(prec)) {
+            // Fold the radix-F column super-stage into the row pass: the
+            // column pass then runs on H / F points.
+            int lf = logh - col_pref_log(prec);
+            while (lf > 0 && (lf > 3 || !fold_supported(prec, p->log_a, lf))) --lf;
+            if (logh - lf > col_cap_log(prec)) {
+                free_plan(p);
+                return fail(FFT_ERR_UNSUPPORTED_SIZE, "no 2D layout for H = %lld, W = %lld", (long long)dims[0],
+                            (long long)dims[1]);
+            }
+            p->logf = lf;
+        }
+        p->log_b = logh - p->logf;  // Lc, the column pass length
         if (p->log_a > 0) st = upload(stage_table(p->log_a), prec, &p->tw_a);
         if (st == FFT_OK && p->log_b > 0) st = upload(stage_table(p->log_b), prec, &p->tw_b);
+        if (st == FFT_OK && p->logf > 0) st = upload_big(logh, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
     }
     if (st != FFT_OK) {
         free_plan(p);
@@ -342,14 +412,16 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             snprintf(buf, len, "rank=1 n=%lld prec=%s path=rows stages=%d", (long long)p->n, prec,
                      plan_nstages(p->log_a));
             break;
-        case PATH_FOURSTEP:
-            snprintf(buf, len, "rank=1 n=%lld prec=%s path=fourstep n1=%lld n2=%lld cols_per_wg=%d rows_per_wg=%d",
-                     (long long)p->n, prec, 1LL << p->log_a, 1LL << p->log_b, tile_lines(p->prec, p->log_b),
-                     tile_lines(p->prec, p->log_a));
+        case PATH_MULTIPASS: {
+            int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
+            for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
+                off += snprintf(buf + off, len - off, q ? "x%lld" : "%lld", 1LL << p->passes[q].logr);
             break;
+        }
         default:
-            snprintf(buf, len, "rank=2 h=%lld w=%lld prec=%s path=2d cols_per_wg=%d", (long long)p->dims[0],
-                     (long long)p->dims[1], prec, p->log_b > 0 ? tile_lines(p->prec, p->log_b) : 0);
+            snprintf(buf, len, "rank=2 h=%lld w=%lld prec=%s path=2d fold=%d col_len=%lld cols_per_wg=%d",
+                     (long long)p->dims[0], (long long)p->dims[1], prec, 1 << p->logf, 1LL << p->log_b,
+                     p->log_b > 0 ? tile_lines_2d(p->prec, p->log_b) : 0);
             break;
     }
     return FFT_OK;
@@ -384,12 +456,17 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
         case PATH_ROWS:
             e = launch_rows(plan->prec, plan->log_a, inv, inv, in, out, batch, plan->tw_a, scale, s);
             break;
-        case PATH_FOURSTEP: {
-            const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
-            const int64_t n1 = int64_t(1) << plan->log_a, n2 = int64_t(1) << plan->log_b;
-            e = launch_fourstep_a(plan->prec, plan->log_b, n1, in, workspace, batch, plan->tw_b, big, inv, s);
-            if (e == hipSuccess)
-                e = launch_fourstep_b(plan->prec, plan->log_a, n2, workspace, out, batch, plan->tw_a, inv, scale, s);
+        case PATH_MULTIPASS: {
+            // in -> ws -> out (two passes) or in -> ws -> out -> out (three, the last in place).
+            const void* src = in;
+            for (int q = 0; q < plan->npass && e == hipSuccess; ++q) {
+                const PassPlan& pp = plan->passes[q];
+                void* dst = q == 0 ? workspace : out;
+                const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, pp.logns + pp.logr};
+                e = launch_stock_pass(plan->prec, pp.logr, pp.kind, src, dst, plan->logn, pp.logns, batch, pp.tw, big,
+                                      inv && q == 0, inv && q == plan->npass - 1, scale, s);
+                src = dst;
+            }
             break;
         }
         default:
@@ -406,9 +483,9 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
 int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
                 void* stream)
 {
-    (void)workspace;
     bool noop = false;
-    int st = check_exec(plan, dir, 2, in, out, batch, nullptr, 0, &noop);
+    const size_t ws = plan && batch > 0 && in == out ? c2c_workspace(plan, batch) : 0;
+    int st = check_exec(plan, dir, 2, in, out, batch, workspace, ws, &noop);
     if (st != FFT_OK || noop) return st;
     if ((st = check_device(plan)) != FFT_OK) return st;
 
@@ -424,9 +501,18 @@ int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_
     } else if (w == 1) {
         // the columns are contiguous
         e = launch_rows(plan->prec, plan->log_b, inv, inv, in, out, batch, plan->tw_b, scale, s);
-    } else {
+    } else if (plan->logf == 0) {
+        const BigTwiddle none{nullptr, nullptr, 0, 0};
         e = launch_rows(plan->prec, plan->log_a, inv, false, in, out, batch * h, plan->tw_a, 1.0, s);
-        if (e == hipSuccess) e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, w, plan->tw_b, inv, scale, s);
+        if (e == hipSuccess)
+            e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, w, 0, plan->tw_b, none, inv, scale, s);
+    } else {
+        // rows + radix-F column super-stage -> mid, then the column pass mid -> out
+        void* mid = in == out ? workspace : out;
+        const BigTwiddle hb{plan->big_hi, plan->big_lo, plan->big_lbits, plan->log_b + plan->logf};
+        e = launch_rows2d_fold(plan->prec, plan->log_a, plan->logf, in, mid, batch, plan->log_b, plan->tw_a, inv, s);
+        if (e == hipSuccess)
+            e = launch_cols2d(plan->prec, plan->log_b, mid, out, batch, w, plan->logf, plan->tw_b, hb, inv, scale, s);
     }
     if (e != hipSuccess) return hip_fail(e, "fft_exec_2d launch");
     if (getenv("FFTMI_SYNC")) {
@@ -443,7 +529,7 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
-    *bytes = plan->path == PATH_FOURSTEP ? (size_t)2 * batch * (size_t)plan->n * plan->elem : 0;
+    *bytes = plan->path == PATH_MULTIPASS ? (size_t)2 * batch * (size_t)plan->n * plan->elem : 0;
     return FFT_OK;
 }
 
@@ -487,7 +573,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
     hipError_t e = hipSuccess;
     if (d_max_residual) e = launch_zero_resid(d_max_residual, s);
     if (e == hipSuccess) {
-        if (plan->path == PATH_FOURSTEP) {
+        if (plan->path == PATH_MULTIPASS) {
             const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
             e = launch_polymul_fourstep(plan->log_a, plan->log_b, a, la, b, lb, c, batch, workspace, plan->tw_a,
                                         plan->tw_b, big, d_max_residual, s);

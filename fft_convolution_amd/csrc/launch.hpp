@@ -20,53 +20,44 @@ struct BigTwiddle {
     int logn;
 };
 
-// Workgroups of `kernel` (block threads, static LDS only) the device holds at
-// once: blocks per CU at full occupancy times the CU count.  Cached per kernel
-// (all devices are assumed alike).  Returns 0 if the query fails.
-template <typename K>
-int64_t resident_blocks(K kernel, int block)
-{
-    static const int64_t cached = [&]() -> int64_t {
-        int dev = 0, ncu = 0, per = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return 0;
-        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess) return 0;
-        return (int64_t)(per > 0 ? per : 1) * ncu;
-    }();
-    return cached;
-}
+// Lines per workgroup of the tile passes (tiles.hip) for lines of 2^logl points.
+int tile_lines_2d(int prec, int logl);
 
-// Elements per line that the tile kernels stage in LDS at once, and the
-// number of adjacent lines (columns) one workgroup takes.
-int tile_lines(int prec, int logl);
+// Whether the folded 2D row pass exists for rows of 2^logw points and fold 2^logf.
+bool fold_supported(int prec, int logw, int logf);
 
 // Rows kernel: `nrows` contiguous rows of 2^logn points, in -> out (may alias).
 // conj_in conjugates on load; conj_out conjugates and multiplies by `scale` on store.
 hipError_t launch_rows(int prec, int logn, bool conj_in, bool conj_out, const void* in, void* out,
                        int64_t nrows, const void* tw, double scale, hipStream_t stream);
 
-// 2D column pass: for each of `nimg` images [2^logh][w], transform every
-// column (length 2^logh) in -> out (may alias).
-hipError_t launch_cols2d(int prec, int logh, const void* in, void* out, int64_t nimg, int64_t w,
-                         const void* tw, bool conj_out, double scale, hipStream_t stream);
+// 2D column pass over `nimg` images [H][w], H = 2^(logf + logl): lines are
+// (column, j'), j' < 2^logf, with points at rows j' + 2^logf r; when logf > 0
+// point r of line j' is first multiplied by w_H^{r j'} (htw: tables for H).
+// in -> out, may alias.  conj_out conjugates and multiplies by `scale`.
+hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t nimg, int64_t w, int logf,
+                         const void* tw, BigTwiddle htw, bool conj_out, double scale, hipStream_t stream);
 
-// Four-step pass A: for each of `batch` signals of N = n1 * 2^logn2 points
-// viewed as [2^logn2][n1], transform every column (length 2^logn2), multiply
-// element (k2, col) by w_N^{col k2}, write to ws in the same layout.
-hipError_t launch_fourstep_a(int prec, int logn2, int64_t n1, const void* in, void* ws,
-                             int64_t batch, const void* tw, BigTwiddle big, bool conj_in,
-                             hipStream_t stream);
+// 2D row pass with the radix-2^logf column super-stage folded in: rows of
+// 2^logw points; image rows j + r Lc (r < 2^logf, Lc = 2^log_lc) are
+// transformed and combined into rows j 2^logf + r.  in -> out, must not alias.
+hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,
+                              const void* tw, bool conj_in, hipStream_t stream);
 
-// Four-step pass B: transform every row k2 (length 2^logn1) of ws [n2][2^logn1]
-// and store element k1 of row k2 at out[k2 + n2 k1].
-hipError_t launch_fourstep_b(int prec, int logn1, int64_t n2, const void* ws, void* out,
-                             int64_t batch, const void* tw, bool conj_out, double scale,
-                             hipStream_t stream);
+// One super-stage pass of a multi-pass Stockham transform of `batch` signals
+// of 2^logn points: radix 2^logr, span 2^logns; kind 0 first, 1 middle, 2
+// last (in place allowed).  big: tables for w_M, M = 2^(logns + logr).
+hipError_t launch_stock_pass(int prec, int logr, int kind, const void* in, void* out, int logn, int logns,
+                             int64_t batch, const void* tw, BigTwiddle big, bool conj_in, bool conj_out,
+                             double scale, hipStream_t stream);
 
 // Polynomial products, N = 2^logn <= LDS range: one fused kernel per row pair.
 hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int64_t* b, int64_t lb,
                                int64_t* c, int64_t batch, const void* tw, double* d_resid,
                                hipStream_t stream);
+
+// Lines per workgroup of the poly-mul column passes for lines of 2^logl points.
+int tile_lines(int prec, int logl);
 
 // Polynomial products, N = n1 * n2 beyond the LDS range (fp64):
 //  A : int64 operands -> column FFTs (length n2) + w_N^{n1 k2}  -> ws_a, ws_b

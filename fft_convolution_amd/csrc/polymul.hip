@@ -309,4 +309,14 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     return e;
 }
 
+int tile_lines(int prec, int logl)
+{
+    switch (logl) {
+#define TL(L) case L: return prec == 0 ? TileShape<float2, L>::C : TileShape<double2, L>::C;
+        TL(1) TL(2) TL(3) TL(4) TL(5) TL(6) TL(7) TL(8) TL(9) TL(10) TL(11) TL(12)
+#undef TL
+        default: return 0;
+    }
+}
+
 }  // namespace fftmi

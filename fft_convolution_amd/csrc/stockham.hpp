@@ -333,4 +333,21 @@ __device__ __forceinline__ void fft_regs(V (&v)[Geometry<LOGN>::E], int t, const
     fft_stages_from<LOGN, 0>(v, t, tb, lds);
 }
 
+// The same transform with the thread <-> (line, t) map changed at the first
+// exchange: stage 0 runs on the registers of thread (line la.c, ta); the LDS
+// exchange hands the data over, and the later stages run on thread (line
+// lb.c, tb_t), which ends with v[i] = X[tb_t + i T] of line lb.c.  Every
+// (line, t) pair must be held by exactly one thread under each map.  The
+// twiddle bases `tb` must have been loaded for tb_t (stage 0 needs none).
+// This lets a kernel load with lanes running across lines and store with
+// lanes running along a line (or the reverse) at no extra LDS traffic.
+template <int LOGN, typename V, typename TB, typename LA, typename LB>
+__device__ __forceinline__ void fft_regs_remap(V (&v)[Geometry<LOGN>::E], int ta, const LA& la, int tb_t,
+                                               const TB& tb, const LB& lb)
+{
+    static_assert(Geometry<LOGN>::S > 1, "a remap needs at least one exchange");
+    fft_stage<LOGN, 0>(v, ta, tb, la);
+    fft_stages_from<LOGN, 1>(v, tb_t, tb, lb);
+}
+
 }  // namespace fftmi

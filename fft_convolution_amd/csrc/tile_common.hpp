@@ -24,6 +24,39 @@ template <int LOGN, int C> constexpr int tile_lds_slots()
     return Geometry<LOGN>::S > 1 ? lds_padded(C * Geometry<LOGN>::N) : 1;
 }
 
+// Tile geometry for passes over lines of L = 2^LOGL points that are not
+// contiguous in memory (matrix columns, Stockham butterflies at a stride).
+// Each thread owns P adjacent lines, loaded together as one 16-byte vector
+// per position; CL threads side by side cover a 128-byte row segment (the
+// unit the memory system moves without waste); a workgroup owns C = CL P
+// lines and runs the P sets of CL lines through LDS one after another.
+template <typename V, int LOGL> struct Tile {
+    using G = Geometry<LOGL>;
+    static constexpr int P = 16 / (int)sizeof(V);      // complex64: 2, complex128: 1
+    static constexpr int CL0 = 256 / G::T;
+    static constexpr int CL = CL0 < 8 ? 8 : (CL0 > 64 ? 64 : CL0);
+    static constexpr int C = CL * P;
+    static constexpr int THREADS = CL * G::T;
+    static constexpr int LDS = G::S > 1 ? lds_padded(CL * G::N) : 1;
+};
+
+typedef float vio_f4 __attribute__((ext_vector_type(4)));
+
+// Load / store P adjacent complex values as one 16-byte access.
+__device__ __forceinline__ void vload(const float2* p, float2 (&d)[2])
+{
+    const vio_f4 q = *reinterpret_cast<const vio_f4*>(p);
+    d[0] = float2{q.x, q.y};
+    d[1] = float2{q.z, q.w};
+}
+__device__ __forceinline__ void vload(const double2* p, double2 (&d)[1]) { d[0] = *p; }
+__device__ __forceinline__ void vstore(float2* p, const float2 (&s)[2])
+{
+    const vio_f4 q = {s[0].x, s[0].y, s[1].x, s[1].y};
+    *reinterpret_cast<vio_f4*>(p) = q;
+}
+__device__ __forceinline__ void vstore(double2* p, const double2 (&s)[1]) { *p = s[0]; }
+
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
 // b mod 8).  Give each XCD a contiguous range of tiles instead, so that
 // neighbouring tiles -- which share cache lines when a tile's row segment is
@@ -48,12 +81,19 @@ template <typename V> struct BigTw {
     }
 };
 
+// w_M^m for a power-of-two M held in one table (small M).
+template <typename V> struct RootTw {
+    const V* __restrict__ tab;
+    int logm;
+    __device__ __forceinline__ V operator()(int64_t m) const { return tab[m & (((int64_t)1 << logm) - 1)]; }
+};
+
 // v[i] holds position p = t + i T of a line; multiply it by w_N^{line p}.
 // The factors are w0 = w_N^{line t} times products of g_j = w_N^{line T 2^j}
 // over the set bits j of i, every factor read from the exact tables, so each
 // twiddle carries a handful of roundings, not a long recurrence.
-template <int LOGN, typename V>
-__device__ __forceinline__ void apply_big_twiddle(V (&v)[Geometry<LOGN>::E], int64_t line, int t, BigTw<V> bt)
+template <int LOGN, typename V, typename TW>
+__device__ __forceinline__ void apply_big_twiddle(V (&v)[Geometry<LOGN>::E], int64_t line, int t, TW bt)
 {
     using G = Geometry<LOGN>;
     V p[G::E];

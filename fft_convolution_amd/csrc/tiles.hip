@@ -1,19 +1,29 @@
-// tiles.hip -- tile kernels: one workgroup transforms C adjacent "lines" that
-// are not contiguous in memory (the columns of a 2D image, the columns and
-// transposed rows of the four-step).  Lanes run over the C lines fastest, so
-// every load and store instruction touches C contiguous elements per line;
-// the workgroup-to-tile map keeps neighbouring tiles on one XCD so that their
-// partial cache lines meet in the same L2.
+// tiles.hip -- passes over lines that are not contiguous in memory: the
+// column pass and the folded row pass of the 2D transform, and the
+// super-stage passes of the multi-pass Stockham transform for N beyond one
+// workgroup's LDS.
 //
-// The 2D column pass follows "Stockham FFT Butterfly Algorithm in Parallel
-// GLSL", section "Multi-Dimensional Transforms and Separability" (rows, then
-// columns).  The four-step splits an N = N1 N2 transform with the same
-// even/odd idea as the radix-2 split of "FFT on GPU" (section "Fast Fourier
-// Transform"), with radix N1 instead of 2:
-//   n = n1 + N1 n2,  k = k2 + N2 k1,
-//   X[k2 + N2 k1] = sum_{n1} w_{N1}^{n1 k1} w_N^{n1 k2} sum_{n2} x[n1 + N1 n2] w_{N2}^{n2 k2}
-// pass A: the inner sums (columns, length N2) and the factor w_N^{n1 k2};
-// pass B: the outer sums (rows, length N1) with a transposing store.
+// Lines run across lanes in 128-byte row segments (Tile in tile_common.hpp);
+// the workgroup-to-tile map gives each XCD a contiguous range of tiles.
+//
+// 2D ("Stockham FFT Butterfly Algorithm in Parallel GLSL", section
+// "Multi-Dimensional Transforms and Separability": rows, then columns).  A
+// column of H = F Lc points is transformed as two Stockham super-stages: the
+// radix-F one (span 1: rows j + r Lc combined into rows j F + r) is folded
+// into the row pass, and the radix-Lc one (span F: rows j' + F r, twiddle
+// w_H^{r j'}) is the column pass, so that the column tiles stay within LDS at
+// 128-byte segments and the whole transform still reads and writes HBM twice.
+//
+// Large 1D: N = R_1 R_2 ... R_p, one pass per super-stage.  Super-stage q with
+// radix R and span Ns (the product of the earlier radices) takes, for every
+// butterfly j < N/R, the R inputs x[j + r N/R], multiplies input r by
+// w_{Ns R}^{r (j mod Ns)}, does an R-point DFT and writes output r to
+// y[(j / Ns) Ns R + (j mod Ns) + r Ns] -- the radix-2 stage of "Stockham FFT
+// ... in Parallel GLSL" (section "Execution via GLSL Compute Shaders and
+// Textures") with radix R, each R-point DFT itself fused in LDS.  The last
+// super-stage writes the positions it reads (in place); the first writes each
+// butterfly's R outputs contiguously, so it hands the data from lanes-across-
+// lines to lanes-along-a-line inside its LDS exchange (fft_regs_remap).
 #include "launch.hpp"
 #include "stockham.hpp"
 #include "tile_common.hpp"
@@ -21,223 +31,398 @@
 namespace fftmi {
 
 // ---------------------------------------------------------------------------
-// 2D column pass
+// 2D column pass: lines (column, j') of [H][W] images, H = F Lc, line points
+// at rows j' + F r (r < Lc); in place allowed.
 // ---------------------------------------------------------------------------
-template <typename V, int LOGN, int C, bool CONJ_OUT>
-__global__ __launch_bounds__(C * Geometry<LOGN>::T)
-void cols2d_kernel(const V* in, V* out, int64_t tiles_per_img, int64_t w, const V* __restrict__ tw,
-                   typename real_of<V>::type scale)
+template <typename V, int LOGL, bool CONJ_OUT>
+__global__ __launch_bounds__((Tile<V, LOGL>::THREADS))
+void cols2d_kernel(const V* in, V* out, int64_t w, int logf, int64_t col_tiles, const V* __restrict__ tw,
+                   BigTw<V> htw, typename real_of<V>::type scale)
 {
-    using G = Geometry<LOGN>;
-    __shared__ V lds[tile_lds_slots<LOGN, C>()];
-    const int c = threadIdx.x % C, t = threadIdx.x / C;
+    using G = Geometry<LOGL>;
+    using TL = Tile<V, LOGL>;
+    __shared__ V lds[TL::LDS];
+    const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t img = tile / tiles_per_img;
-    const int64_t col = (tile % tiles_per_img) * C + c;
+    const int64_t per_img = col_tiles << logf;
+    const int64_t img = tile / per_img;
+    const int64_t rem = tile % per_img;
+    const int jp = (int)(rem / col_tiles);
+    const int64_t col = (rem % col_tiles) * TL::C + c0 * TL::P;
     const bool live = col < w;
-    const int64_t base = img * ((int64_t)G::N * w) + col + (int64_t)t * w;
-    const int64_t step = (int64_t)G::T * w;
+    const int64_t f = (int64_t)1 << logf;
+    const int64_t base = img * ((f << LOGL) * w) + (jp + f * t) * w + col;
+    const int64_t step = f * G::T * w;
 
-    V v[G::E];
+    V v[TL::P][G::E];
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) v[i] = live ? in[base + i * step] : V{0, 0};
-    TwBases<V, LOGN> tb;
+    for (int i = 0; i < G::E; ++i) {
+        V q[TL::P];
+        if (live) vload(in + base + i * step, q);
+        else
+#pragma unroll
+            for (int g = 0; g < TL::P; ++g) q[g] = V{0, 0};
+#pragma unroll
+        for (int g = 0; g < TL::P; ++g) v[g][i] = q[g];
+    }
+    TwBases<V, LOGL> tb;
     tb.load(tw, t);
-    fft_regs<LOGN>(v, t, tb, LdsLines<V, C>{lds, c});
+    if (jp > 0) {  // the column super-stage's twiddle w_H^{j' r}
+#pragma unroll
+        for (int g = 0; g < TL::P; ++g) apply_big_twiddle<LOGL>(v[g], jp, t, htw);
+    }
+#pragma unroll
+    for (int g = 0; g < TL::P; ++g) {
+        if (g > 0) __syncthreads();
+        fft_regs<LOGL>(v[g], t, tb, LdsLines<V, TL::CL>{lds, c0});
+    }
     if (live) {
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
-            V y = v[i];
-            out[base + i * step] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
+            V q[TL::P];
+#pragma unroll
+            for (int g = 0; g < TL::P; ++g) {
+                const V y = v[g][i];
+                q[g] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
+            }
+            vstore(out + base + i * step, q);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass A: columns of [N2][N1] (line = n1, position = n2 -> k2),
-// then the twiddle w_N^{n1 k2}; written back in the same layout.
+// 2D row pass with the column super-stage of radix F folded in: a group of F
+// threads-rows takes rows j + r Lc (r < F) of one image, transforms each row
+// (length W), exchanges through LDS so that every thread holds all F rows at
+// E/F positions, does the F-point DFT across the rows and writes row j F + r'.
+// Out of place (the rows it writes are read by other groups).
 // ---------------------------------------------------------------------------
-template <typename V, int LOGN, int C, bool CONJ_IN>
-__global__ __launch_bounds__(C * Geometry<LOGN>::T)
-void fourstep_a_kernel(const V* in, V* ws, int64_t n1, int64_t tiles_per_sig, const V* __restrict__ tw,
-                       const V* __restrict__ big_hi, const V* __restrict__ big_lo, int lbits, int logn_total)
+template <int LOGW, int LOGF> constexpr int fold_groups()
 {
-    using G = Geometry<LOGN>;
-    __shared__ V lds[tile_lds_slots<LOGN, C>()];
-    const int c = threadIdx.x % C, t = threadIdx.x / C;
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t sig = tile / tiles_per_sig;
-    const int64_t col = (tile % tiles_per_sig) * C + c;  // n1 (< n1 always: C divides n1)
-    const int64_t base = (sig << logn_total) + col + (int64_t)t * n1;
-    const int64_t step = (int64_t)G::T * n1;
+    return (Geometry<LOGW>::T << LOGF) >= 256 ? 1 : 256 / (Geometry<LOGW>::T << LOGF);
+}
 
+template <typename V, int LOGW, int LOGF, bool CONJ_IN>
+__global__ __launch_bounds__(((Geometry<LOGW>::T << LOGF) * fold_groups<LOGW, LOGF>()))
+void rows2d_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* __restrict__ tw)
+{
+    using G = Geometry<LOGW>;
+    constexpr int F = 1 << LOGF;
+    constexpr int GR = fold_groups<LOGW, LOGF>();
+    constexpr int SLOTS = lds_padded(G::N);  // one row, padded (also used when S == 1)
+    constexpr int EF = G::E / F;
+    static_assert(G::E >= F, "each thread needs at least F positions");
+    __shared__ V lds[SLOTS * F * GR];
+    const int tid = threadIdx.x;
+    const int gl = tid / (F * G::T);
+    const int rho = (tid / G::T) % F;
+    const int t = tid % G::T;
+    const int64_t grp = (int64_t)blockIdx.x * GR + gl;
+    const bool live = grp < ngroups;
+    const int64_t lc = (int64_t)1 << log_lc;
+    const int64_t img = grp >> log_lc, j = grp & (lc - 1);
+    const int64_t h = lc << LOGF;
+    V* my = lds + (gl * F) * SLOTS;
+
+    TwBases<V, LOGW> tb;
+    tb.load(tw, t);
     V v[G::E];
+    const V* src = in + ((img * h + j + rho * lc) << LOGW) + t;
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
-        V x = in[base + i * step];
+        const V x = live ? ld_stream(src + i * G::T) : V{0, 0};
         v[i] = CONJ_IN ? cconj(x) : x;
     }
-    TwBases<V, LOGN> tb;
-    tb.load(tw, t);
-    fft_regs<LOGN>(v, t, tb, LdsLines<V, C>{lds, c});
-    // element i sits at k2 = t + i T: multiply by w_N^{n1 (t + i T)}
-    apply_big_twiddle<LOGN>(v, (int64_t)col, t, BigTw<V>{big_hi, big_lo, lbits, logn_total});
+    const LdsLines<V, 1> L{my + rho * SLOTS, 0};
+    fft_regs<LOGW>(v, t, tb, L);
+    __syncthreads();  // every LDS read of the row transforms is done
+    {
+        V* wp = L.ptr(t);
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) ws[base + i * step] = v[i];
+        for (int i = 0; i < G::E; ++i) wp[LdsLines<V, 1>::off(i * G::T)] = v[i];
+    }
+    __syncthreads();
+    V* dst = out + ((img * h + j * F) << LOGW);
+#pragma unroll
+    for (int k = 0; k < EF; ++k) {
+        const int p = t + (rho * EF + k) * G::T;
+        V u[F];
+#pragma unroll
+        for (int r = 0; r < F; ++r) u[r] = *LdsLines<V, 1>{my + r * SLOTS, 0}.ptr(p);
+        Dft<F>::run(u);
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < F; ++r) st_stream(dst + ((int64_t)r << LOGW) + p, u[r]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass B: rows of [N2][N1] (line = k2, position = n1 -> k1), stored
-// transposed: X[k2 + N2 k1].
+// Multi-pass Stockham super-stage (large 1D).  KIND 0: first (span 1, stored
+// along lines after a remap), 1: middle, 2: last (in place).
 // ---------------------------------------------------------------------------
-template <typename V, int LOGN, int C, bool CONJ_OUT>
-__global__ __launch_bounds__(C * Geometry<LOGN>::T)
-void fourstep_b_kernel(const V* ws, V* out, int64_t n2, int64_t tiles_per_sig, const V* __restrict__ tw,
-                       typename real_of<V>::type scale, int logn_total)
+template <typename V, int LOGR, int KIND, bool CONJ_IN, bool CONJ_OUT>
+__global__ __launch_bounds__((Tile<V, LOGR>::THREADS))
+void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_per_sig, const V* __restrict__ tw,
+                       BigTw<V> big, typename real_of<V>::type scale)
 {
-    using G = Geometry<LOGN>;
-    __shared__ V lds[tile_lds_slots<LOGN, C>()];
-    const int c = threadIdx.x % C, t = threadIdx.x / C;
+    using G = Geometry<LOGR>;
+    using TL = Tile<V, LOGR>;
+    __shared__ V lds[TL::LDS];
+    const int tid = threadIdx.x;
+    const int c0 = tid % TL::CL, t = tid / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t sig = tile / tiles_per_sig;
-    const int64_t row = (tile % tiles_per_sig) * C + c;  // k2
-    const int64_t sbase = sig << logn_total;
-    const int64_t in_base = sbase + (row << LOGN) + t;
-    const int64_t out_base = sbase + row + (int64_t)t * n2;
-    const int64_t out_step = (int64_t)G::T * n2;
+    const int64_t j0 = (tile % tiles_per_sig) * TL::C;
+    const int64_t j = j0 + c0 * TL::P;
+    const int64_t sbase = sig << logn;
+    const int64_t stride = (int64_t)1 << (logn - LOGR);  // N / R
 
-    V v[G::E];
+    V v[TL::P][G::E];
+    {
+        const V* src = in + sbase + j + t * stride;
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) v[i] = ws[in_base + i * G::T];
-    TwBases<V, LOGN> tb;
-    tb.load(tw, t);
-    fft_regs<LOGN>(v, t, tb, LdsLines<V, C>{lds, c});
+        for (int i = 0; i < G::E; ++i) {
+            V q[TL::P];
+            vload(src + i * G::T * stride, q);
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) {
-        V y = v[i];
-        out[out_base + i * out_step] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
+            for (int g = 0; g < TL::P; ++g) v[g][i] = CONJ_IN ? cconj(q[g]) : q[g];
+        }
+    }
+    const int64_t ns_mask = ((int64_t)1 << logns) - 1;
+    if constexpr (KIND != 0) {
+#pragma unroll
+        for (int g = 0; g < TL::P; ++g) apply_big_twiddle<LOGR>(v[g], (j + g) & ns_mask, t, big);
+    }
+
+    if constexpr (KIND == 0) {
+        // Lanes along a line for the store: thread -> (line slot cb, tb_t).
+        const int cb = tid / G::T, tb_t = tid % G::T;
+        TwBases<V, LOGR> tb;
+        tb.load(tw, tb_t);
+#pragma unroll
+        for (int g = 0; g < TL::P; ++g) {
+            if (g > 0) __syncthreads();
+            fft_regs_remap<LOGR>(v[g], t, LdsLines<V, TL::CL>{lds, c0}, tb_t, tb, LdsLines<V, TL::CL>{lds, cb});
+        }
+#pragma unroll
+        for (int g = 0; g < TL::P; ++g) {
+            V* dst = out + sbase + ((j0 + cb * TL::P + g) << LOGR) + tb_t;
+#pragma unroll
+            for (int i = 0; i < G::E; ++i) dst[i * G::T] = v[g][i];
+        }
+    } else {
+        TwBases<V, LOGR> tb;
+        tb.load(tw, t);
+#pragma unroll
+        for (int g = 0; g < TL::P; ++g) {
+            if (g > 0) __syncthreads();
+            fft_regs<LOGR>(v[g], t, tb, LdsLines<V, TL::CL>{lds, c0});
+        }
+        const int64_t ns = (int64_t)1 << logns;
+        V* dst = out + sbase + ((j >> logns) << (logns + LOGR)) + (j & ns_mask) + t * ns;
+#pragma unroll
+        for (int i = 0; i < G::E; ++i) {
+            V q[TL::P];
+#pragma unroll
+            for (int g = 0; g < TL::P; ++g) {
+                const V y = v[g][i];
+                q[g] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
+            }
+            vstore(dst + i * G::T * ns, q);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <typename V, int LOGN>
-static hipError_t cols2d_t(const void* in, void* out, int64_t nimg, int64_t w, const void* tw, bool co,
-                           double scale, hipStream_t s)
+static inline dim3 grid_of(int64_t blocks) { return dim3((unsigned)blocks); }
+
+template <typename V, int LOGL>
+static hipError_t cols2d_t(const void* in, void* out, int64_t nimg, int64_t w, int logf, const void* tw,
+                           BigTwiddle htw, bool co, double scale, hipStream_t s)
 {
-    constexpr int C = TileShape<V, LOGN>::C;
-    const int64_t tpi = (w + C - 1) / C;
-    const int64_t blocks = tpi * nimg;
+    using TL = Tile<V, LOGL>;
+    if (TL::THREADS > 1024) return hipErrorInvalidValue;
+    const int64_t col_tiles = (w + TL::C - 1) / TL::C;
+    const int64_t blocks = (col_tiles << logf) * nimg;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
-    const dim3 grid((unsigned)blocks), block(C * Geometry<LOGN>::T);
+    const BigTw<V> big{(const V*)htw.hi, (const V*)htw.lo, htw.lbits, htw.logn};
     if (co)
-        hipLaunchKernelGGL((cols2d_kernel<V, LOGN, C, true>), grid, block, 0, s, (const V*)in, (V*)out, tpi, w,
-                           (const V*)tw, (Rl)scale);
+        hipLaunchKernelGGL((cols2d_kernel<V, LOGL, true>), grid_of(blocks), dim3(TL::THREADS), 0, s, (const V*)in,
+                           (V*)out, w, logf, col_tiles, (const V*)tw, big, (Rl)scale);
     else
-        hipLaunchKernelGGL((cols2d_kernel<V, LOGN, C, false>), grid, block, 0, s, (const V*)in, (V*)out, tpi, w,
-                           (const V*)tw, (Rl)scale);
+        hipLaunchKernelGGL((cols2d_kernel<V, LOGL, false>), grid_of(blocks), dim3(TL::THREADS), 0, s, (const V*)in,
+                           (V*)out, w, logf, col_tiles, (const V*)tw, big, (Rl)scale);
     return hipGetLastError();
 }
 
-template <typename V, int LOGN>
-static hipError_t fourstep_a_t(int64_t n1, const void* in, void* ws, int64_t batch, const void* tw,
-                               BigTwiddle big, bool ci, hipStream_t s)
+template <typename V, int LOGW, int LOGF> constexpr bool fold_ok()
 {
-    constexpr int C = TileShape<V, LOGN>::C;
-    if (n1 % C) return hipErrorInvalidValue;
-    const int64_t tps = n1 / C;
-    const int64_t blocks = tps * batch;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks), block(C * Geometry<LOGN>::T);
-    if (ci)
-        hipLaunchKernelGGL((fourstep_a_kernel<V, LOGN, C, true>), grid, block, 0, s, (const V*)in, (V*)ws, n1, tps,
-                           (const V*)tw, (const V*)big.hi, (const V*)big.lo, big.lbits, big.logn);
-    else
-        hipLaunchKernelGGL((fourstep_a_kernel<V, LOGN, C, false>), grid, block, 0, s, (const V*)in, (V*)ws, n1, tps,
-                           (const V*)tw, (const V*)big.hi, (const V*)big.lo, big.lbits, big.logn);
-    return hipGetLastError();
+    using G = Geometry<LOGW>;
+    constexpr long threads = (long)(G::T << LOGF) * fold_groups<LOGW, LOGF>();
+    constexpr long lds = (long)lds_padded(G::N) * (1 << LOGF) * fold_groups<LOGW, LOGF>() * (long)sizeof(V);
+    return G::E >= (1 << LOGF) && threads <= 1024 && lds <= 160 * 1024;
 }
 
-template <typename V, int LOGN>
-static hipError_t fourstep_b_t(int64_t n2, const void* ws, void* out, int64_t batch, const void* tw, bool co,
-                               double scale, int logn_total, hipStream_t s)
+template <typename V, int LOGW, int LOGF>
+static hipError_t fold_t(const void* in, void* out, int64_t nimg, int log_lc, const void* tw, bool ci, hipStream_t s)
 {
-    constexpr int C = TileShape<V, LOGN>::C;
-    if (n2 % C) return hipErrorInvalidValue;
-    const int64_t tps = n2 / C;
+    if constexpr (!fold_ok<V, LOGW, LOGF>()) {
+        return hipErrorInvalidValue;
+    } else {
+        constexpr int GR = fold_groups<LOGW, LOGF>();
+        const int64_t ngroups = nimg << log_lc;
+        const int64_t blocks = (ngroups + GR - 1) / GR;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        const dim3 block((Geometry<LOGW>::T << LOGF) * GR);
+        if (ci)
+            hipLaunchKernelGGL((rows2d_fold_kernel<V, LOGW, LOGF, true>), grid_of(blocks), block, 0, s, (const V*)in,
+                               (V*)out, ngroups, log_lc, (const V*)tw);
+        else
+            hipLaunchKernelGGL((rows2d_fold_kernel<V, LOGW, LOGF, false>), grid_of(blocks), block, 0, s, (const V*)in,
+                               (V*)out, ngroups, log_lc, (const V*)tw);
+        return hipGetLastError();
+    }
+}
+
+template <typename V, int LOGR, int KIND>
+static hipError_t stock_t(const void* in, void* out, int logn, int logns, int64_t batch, const void* tw,
+                          BigTwiddle bt, bool ci, bool co, double scale, hipStream_t s)
+{
+    using TL = Tile<V, LOGR>;
+    if (TL::THREADS > 1024) return hipErrorInvalidValue;
+    const int64_t butterflies = (int64_t)1 << (logn - LOGR);
+    if (butterflies % TL::C) return hipErrorInvalidValue;
+    if (KIND == 1 && ((int64_t)1 << logns) % TL::C) return hipErrorInvalidValue;
+    const int64_t tps = butterflies / TL::C;
     const int64_t blocks = tps * batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
-    const dim3 grid((unsigned)blocks), block(C * Geometry<LOGN>::T);
-    if (co)
-        hipLaunchKernelGGL((fourstep_b_kernel<V, LOGN, C, true>), grid, block, 0, s, (const V*)ws, (V*)out, n2, tps,
-                           (const V*)tw, (Rl)scale, logn_total);
-    else
-        hipLaunchKernelGGL((fourstep_b_kernel<V, LOGN, C, false>), grid, block, 0, s, (const V*)ws, (V*)out, n2, tps,
-                           (const V*)tw, (Rl)scale, logn_total);
+    const BigTw<V> big{(const V*)bt.hi, (const V*)bt.lo, bt.lbits, bt.logn};
+#define FFTMI_SP(CI, CO)                                                                                  \
+    hipLaunchKernelGGL((stock_pass_kernel<V, LOGR, KIND, CI, CO>), grid_of(blocks), dim3(TL::THREADS), 0, s, \
+                       (const V*)in, (V*)out, logn, logns, tps, (const V*)tw, big, (Rl)scale)
+    if (ci && co) FFTMI_SP(true, true);
+    else if (ci) FFTMI_SP(true, false);
+    else if (co) FFTMI_SP(false, true);
+    else FFTMI_SP(false, false);
+#undef FFTMI_SP
     return hipGetLastError();
 }
 
-#define FFTMI_TILE_SWITCH(PREC, LOGN, CALL_F, CALL_D)                                   \
-    switch (LOGN) {                                                                       \
-        case 1: return PREC == 0 ? CALL_F(1) : CALL_D(1);                                 \
-        case 2: return PREC == 0 ? CALL_F(2) : CALL_D(2);                                 \
-        case 3: return PREC == 0 ? CALL_F(3) : CALL_D(3);                                 \
-        case 4: return PREC == 0 ? CALL_F(4) : CALL_D(4);                                 \
-        case 5: return PREC == 0 ? CALL_F(5) : CALL_D(5);                                 \
-        case 6: return PREC == 0 ? CALL_F(6) : CALL_D(6);                                 \
-        case 7: return PREC == 0 ? CALL_F(7) : CALL_D(7);                                 \
-        case 8: return PREC == 0 ? CALL_F(8) : CALL_D(8);                                 \
-        case 9: return PREC == 0 ? CALL_F(9) : CALL_D(9);                                 \
-        case 10: return PREC == 0 ? CALL_F(10) : CALL_D(10);                              \
-        case 11: return PREC == 0 ? CALL_F(11) : CALL_D(11);                              \
-        case 12: return PREC == 0 ? CALL_F(12) : CALL_D(12);                              \
-        case 13: return PREC == 0 ? CALL_F(13) : hipErrorInvalidValue;                    \
-        default: return hipErrorInvalidValue;                                             \
+#define FFTMI_LOG_SWITCH(PREC, L, CALL_F, CALL_D)                                     \
+    switch (L) {                                                                    \
+        case 1: return PREC == 0 ? CALL_F(1) : CALL_D(1);                           \
+        case 2: return PREC == 0 ? CALL_F(2) : CALL_D(2);                           \
+        case 3: return PREC == 0 ? CALL_F(3) : CALL_D(3);                           \
+        case 4: return PREC == 0 ? CALL_F(4) : CALL_D(4);                           \
+        case 5: return PREC == 0 ? CALL_F(5) : CALL_D(5);                           \
+        case 6: return PREC == 0 ? CALL_F(6) : CALL_D(6);                           \
+        case 7: return PREC == 0 ? CALL_F(7) : CALL_D(7);                           \
+        case 8: return PREC == 0 ? CALL_F(8) : CALL_D(8);                           \
+        case 9: return PREC == 0 ? CALL_F(9) : CALL_D(9);                           \
+        case 10: return PREC == 0 ? CALL_F(10) : CALL_D(10);                        \
+        case 11: return PREC == 0 ? CALL_F(11) : hipErrorInvalidValue;              \
+        default: return hipErrorInvalidValue;                                       \
     }
 
-hipError_t launch_cols2d(int prec, int logh, const void* in, void* out, int64_t nimg, int64_t w, const void* tw,
-                         bool co, double scale, hipStream_t s)
+hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t nimg, int64_t w, int logf,
+                         const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s)
 {
-#define CF(L) cols2d_t<float2, L>(in, out, nimg, w, tw, co, scale, s)
-#define CD(L) cols2d_t<double2, L>(in, out, nimg, w, tw, co, scale, s)
-    FFTMI_TILE_SWITCH(prec, logh, CF, CD)
+#define CF(L) cols2d_t<float2, L>(in, out, nimg, w, logf, tw, htw, co, scale, s)
+#define CD(L) cols2d_t<double2, L>(in, out, nimg, w, logf, tw, htw, co, scale, s)
+    FFTMI_LOG_SWITCH(prec, logl, CF, CD)
 #undef CF
 #undef CD
 }
 
-hipError_t launch_fourstep_a(int prec, int logn2, int64_t n1, const void* in, void* ws, int64_t batch,
-                             const void* tw, BigTwiddle big, bool ci, hipStream_t s)
+hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,
+                              const void* tw, bool ci, hipStream_t s)
 {
-#define CF(L) fourstep_a_t<float2, L>(n1, in, ws, batch, tw, big, ci, s)
-#define CD(L) fourstep_a_t<double2, L>(n1, in, ws, batch, tw, big, ci, s)
-    FFTMI_TILE_SWITCH(prec, logn2, CF, CD)
-#undef CF
-#undef CD
+#define FOLD_F(LW) (logf == 1 ? fold_t<float2, LW, 1>(in, out, nimg, log_lc, tw, ci, s)   \
+                  : logf == 2 ? fold_t<float2, LW, 2>(in, out, nimg, log_lc, tw, ci, s) \
+                  : logf == 3 ? fold_t<float2, LW, 3>(in, out, nimg, log_lc, tw, ci, s) \
+                              : hipErrorInvalidValue)
+#define FOLD_D(LW) (logf == 1 ? fold_t<double2, LW, 1>(in, out, nimg, log_lc, tw, ci, s)   \
+                  : logf == 2 ? fold_t<double2, LW, 2>(in, out, nimg, log_lc, tw, ci, s) \
+                  : logf == 3 ? fold_t<double2, LW, 3>(in, out, nimg, log_lc, tw, ci, s) \
+                              : hipErrorInvalidValue)
+    switch (logw) {
+        case 1: return prec == 0 ? FOLD_F(1) : FOLD_D(1);
+        case 2: return prec == 0 ? FOLD_F(2) : FOLD_D(2);
+        case 3: return prec == 0 ? FOLD_F(3) : FOLD_D(3);
+        case 4: return prec == 0 ? FOLD_F(4) : FOLD_D(4);
+        case 5: return prec == 0 ? FOLD_F(5) : FOLD_D(5);
+        case 6: return prec == 0 ? FOLD_F(6) : FOLD_D(6);
+        case 7: return prec == 0 ? FOLD_F(7) : FOLD_D(7);
+        case 8: return prec == 0 ? FOLD_F(8) : FOLD_D(8);
+        case 9: return prec == 0 ? FOLD_F(9) : FOLD_D(9);
+        case 10: return prec == 0 ? FOLD_F(10) : FOLD_D(10);
+        case 11: return prec == 0 ? FOLD_F(11) : FOLD_D(11);
+        case 12: return prec == 0 ? FOLD_F(12) : FOLD_D(12);
+        case 13: return prec == 0 ? FOLD_F(13) : hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+#undef FOLD_F
+#undef FOLD_D
 }
 
-hipError_t launch_fourstep_b(int prec, int logn1, int64_t n2, const void* ws, void* out, int64_t batch,
-                             const void* tw, bool co, double scale, hipStream_t s)
+hipError_t launch_stock_pass(int prec, int logr, int kind, const void* in, void* out, int logn, int logns,
+                             int64_t batch, const void* tw, BigTwiddle big, bool ci, bool co, double scale,
+                             hipStream_t s)
 {
-    int logn2 = 0;
-    while ((int64_t(1) << logn2) < n2) ++logn2;
-    const int logn_total = logn1 + logn2;
-#define CF(L) fourstep_b_t<float2, L>(n2, ws, out, batch, tw, co, scale, logn_total, s)
-#define CD(L) fourstep_b_t<double2, L>(n2, ws, out, batch, tw, co, scale, logn_total, s)
-    FFTMI_TILE_SWITCH(prec, logn1, CF, CD)
-#undef CF
-#undef CD
+#define SK(L, K, V) stock_t<V, L, K>(in, out, logn, logns, batch, tw, big, ci, co, scale, s)
+#define SF(L) (kind == 0 ? SK(L, 0, float2) : kind == 1 ? SK(L, 1, float2) : SK(L, 2, float2))
+#define SD(L) (kind == 0 ? SK(L, 0, double2) : kind == 1 ? SK(L, 1, double2) : SK(L, 2, double2))
+    switch (logr) {
+        case 5: return prec == 0 ? SF(5) : SD(5);
+        case 6: return prec == 0 ? SF(6) : SD(6);
+        case 7: return prec == 0 ? SF(7) : SD(7);
+        case 8: return prec == 0 ? SF(8) : SD(8);
+        case 9: return prec == 0 ? SF(9) : SD(9);
+        default: return hipErrorInvalidValue;
+    }
+#undef SK
+#undef SF
+#undef SD
 }
 
-int tile_lines(int prec, int logl)
+bool fold_supported(int prec, int logw, int logf)
+{
+#define FS(LW) (prec == 0 ? (logf == 1 ? fold_ok<float2, LW, 1>() : logf == 2 ? fold_ok<float2, LW, 2>() \
+                             : logf == 3 ? fold_ok<float2, LW, 3>() : false)                            \
+                          : (logf == 1 ? fold_ok<double2, LW, 1>() : logf == 2 ? fold_ok<double2, LW, 2>() \
+                             : logf == 3 ? fold_ok<double2, LW, 3>() : false))
+    switch (logw) {
+        case 1: return FS(1);
+        case 2: return FS(2);
+        case 3: return FS(3);
+        case 4: return FS(4);
+        case 5: return FS(5);
+        case 6: return FS(6);
+        case 7: return FS(7);
+        case 8: return FS(8);
+        case 9: return FS(9);
+        case 10: return FS(10);
+        case 11: return FS(11);
+        case 12: return FS(12);
+        case 13: return prec == 0 && (logf == 1 ? fold_ok<float2, 13, 1>() : logf == 2 ? fold_ok<float2, 13, 2>()
+                                      : logf == 3 ? fold_ok<float2, 13, 3>() : false);
+        default: return false;
+    }
+#undef FS
+}
+
+int tile_lines_2d(int prec, int logl)
 {
     switch (logl) {
-#define TL(L) case L: return prec == 0 ? TileShape<float2, L>::C : TileShape<double2, L>::C;
-        TL(1) TL(2) TL(3) TL(4) TL(5) TL(6) TL(7) TL(8) TL(9) TL(10) TL(11) TL(12)
-        case 13: return prec == 0 ? TileShape<float2, 13>::C : 0;
-#undef TL
+#define TL2(L) case L: return prec == 0 ? Tile<float2, L>::C : Tile<double2, L>::C;
+        TL2(1) TL2(2) TL2(3) TL2(4) TL2(5) TL2(6) TL2(7) TL2(8) TL2(9) TL2(10)
+        case 11: return prec == 0 ? Tile<float2, 11>::C : 0;
+#undef TL2
         default: return 0;
     }
 }

@@ -69,19 +69,22 @@ enum fft_status {
 /* Largest supported transform lengths. */
 #define FFT_MAX_LDS_N_C32 8192        /* one-kernel, LDS-resident rows */
 #define FFT_MAX_LDS_N_C64 4096
-#define FFT_MAX_N_C32 (1LL << 26)     /* four-step beyond the LDS-resident range */
+#define FFT_MAX_N_C32 (1LL << 26)     /* multi-pass beyond the LDS-resident range */
 #define FFT_MAX_N_C64 (1LL << 24)
 
 /*
  * Create a plan.
  *   rank 1: dims = {N};      1 <= N <= FFT_MAX_N_C32 (C32) / FFT_MAX_N_C64 (C64).
  *           N <= FFT_MAX_LDS_N_* runs as one LDS-resident kernel per batch of
- *           rows; larger N runs as a four-step (column FFTs of length N2,
- *           twiddle W_N^{n1 k2}, row FFTs of length N1 with a transposing store;
- *           N = N1 N2) and needs a workspace.
+ *           rows; larger N runs as two or three Stockham super-stage passes
+ *           (radix <= 512 each) through HBM and needs a workspace of one
+ *           batch of signals.
  *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
  *           Parallel GLSL", section "Multi-Dimensional Transforms and
- *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*.
+ *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*,
+ *           except very tall, narrow shapes whose column transform cannot be
+ *           split between the two passes (e.g. H = 8192 with W = 2, FFT_C32),
+ *           which give FFT_ERR_UNSUPPORTED_SIZE.
  *   prec:   FFT_C32 or FFT_C64.
  * Builds the twiddle tables in fp64 on the host, rounds them to the plan
  * precision and uploads them (the only synchronous device work of the
@@ -117,7 +120,11 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
  * Batched 2D transform with a rank-2 plan: row transforms of length W over
  * every row, then column transforms of length H over every column.
  *   in, out:   [batch][H][W] complex, images contiguous.  in == out allowed.
- *   workspace: unused (size 0); may be NULL.
+ *   workspace: used only by an in-place call (in == out) on a plan that folds
+ *              part of the column transform into the row pass (H > 1024 for
+ *              FFT_C32, H > 512 for FFT_C64; fft_plan_describe shows fold > 1);
+ *              it then needs fft_workspace_size(plan, batch) bytes.  Otherwise
+ *              it may be NULL.
  * Errors: as fft_exec_c2c.
  */
 int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,

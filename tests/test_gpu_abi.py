@@ -43,5 +43,5 @@ def test_exec_validation(dev):
     ws = torch.empty(2 * (1 << 16) * 8, dtype=torch.uint8, device=dev)
     assert _status(fm.fft_exec_c2c, pbig.handle, 0, xb, yb, 2, ws) == fm.FFT_OK
     torch.cuda.synchronize()
-    assert "path=rows" in p1.describe() and "path=fourstep" in pbig.describe()
+    assert "path=rows" in p1.describe() and "path=multipass" in pbig.describe()
     assert "path=2d" in p2.describe()

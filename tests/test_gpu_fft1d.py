@@ -55,11 +55,11 @@ def test_c2c_c128_sweep(dev, logn, batch):
 
 
 @pytest.mark.parametrize("logn,batch", [(14, 2), (15, 3), (16, 1), (18, 2), (20, 1), (22, 1)])
-def test_c2c_c64_fourstep(dev, logn, batch):
+def test_c2c_c64_multipass(dev, logn, batch):
     n = 1 << logn
     x = _case(n, batch, np.complex64, 300 + logn)
     plan = fm.Plan(n, torch.complex64)
-    assert "fourstep" in plan.describe()
+    assert "multipass" in plan.describe()
     for inverse in (False, True):
         y = _run(plan, x, dev, inverse)
         ref = oracle.fft(x, inverse=inverse)
@@ -67,11 +67,11 @@ def test_c2c_c64_fourstep(dev, logn, batch):
 
 
 @pytest.mark.parametrize("logn,batch", [(13, 2), (14, 1), (16, 3), (19, 1)])
-def test_c2c_c128_fourstep(dev, logn, batch):
+def test_c2c_c128_multipass(dev, logn, batch):
     n = 1 << logn
     x = _case(n, batch, np.complex128, 400 + logn)
     plan = fm.Plan(n, torch.complex128)
-    assert "fourstep" in plan.describe()
+    assert "multipass" in plan.describe()
     for inverse in (False, True):
         y = _run(plan, x, dev, inverse)
         ref = oracle.fft(x, inverse=inverse)

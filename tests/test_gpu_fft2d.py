@@ -84,3 +84,26 @@ def test_fft2_round_trip_and_in_place(dev):
     torch.cuda.synchronize()
     assert torch.equal(X, z)
     assert rel_rms_rows(_flat(back.cpu().numpy()), _flat(x_np)).max() <= fft_tol(h * w)
+
+
+def test_fft2_folded_in_place_needs_workspace(dev):
+    # 2048 rows fold a radix-2 column super-stage into the row pass; in place
+    # that pass cannot write its output over rows other groups still read, so
+    # an in-place call takes a workspace (and is rejected without one).
+    h, w = 2048, 64
+    plan = fm.Plan((h, w), torch.complex64)
+    assert "fold=2" in plan.describe()
+    x_np = wl.batched_normal(h * w, 2, seed=11).reshape(2, h, w)
+    x = torch.from_numpy(x_np).to(dev)
+    ws_bytes = fm.fft_workspace_size(plan.handle, 2)
+    assert ws_bytes == 2 * h * w * 8
+    z = x.clone()
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, z, z, 2, None)
+    assert e.value.status == fm.FFT_ERR_WORKSPACE
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, z, z, 2, ws)
+    y = plan.fft2(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, z)
+    assert rel_rms_rows(_flat(y.cpu().numpy()), _flat(oracle.fft2(x_np))).max() <= fft_tol(h * w)
