@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -267,6 +268,7 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
 // Largest radix per super-stage pass, and the preferred / largest column
 // length of the 2D column pass (LDS: lines of 128 bytes x length must fit).
 constexpr int kMaxPassLog = 9;
+constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
 int col_pref_log(int prec) { return prec == FFT_C32 ? 10 : 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
 
@@ -355,10 +357,12 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
                     st = fail(FFT_ERR_UNSUPPORTED_SIZE, "no pass layout for n = %lld", (long long)p->n);
             }
             p->npass = np;
-            // The poly-mul four-step tables (fp64 only).
-            if (st == FFT_OK && prec == FFT_C64) {
-                p->log_b = (p->logn + 1) / 2;  // N2, the column length
-                p->log_a = p->logn - p->log_b; // N1, the row length
+            // The poly-mul split N = N1 N2 (fp64 only): columns of at most 512
+            // (1024 beyond 2^21) points, rows of at most 4096.
+            if (st == FFT_OK && prec == FFT_C64 && p->logn <= kPolyMaxLog) {
+                p->log_b = std::min(9, (p->logn + 1) / 2);  // N2, the column length
+                if (p->logn - p->log_b > 12) p->log_b = p->logn - 12;
+                p->log_a = p->logn - p->log_b;               // N1, the row length
                 st = upload(stage_table(p->log_a), prec, &p->tw_a);
                 if (st == FFT_OK) st = upload(stage_table(p->log_b), prec, &p->tw_b);
                 if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
@@ -529,7 +533,8 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
-    *bytes = plan->path == PATH_MULTIPASS ? (size_t)2 * batch * (size_t)plan->n * plan->elem : 0;
+    if (plan->logn > kPolyMaxLog) return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
+    *bytes = plan->path == PATH_MULTIPASS ? (size_t)batch * (size_t)plan->n * plan->elem : 0;
     return FFT_OK;
 }
 
@@ -541,6 +546,8 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
     if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
+    if (plan->logn > kPolyMaxLog)
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
     if (la > plan->n || lb > plan->n || la + lb - 1 > plan->n)
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "la + lb - 1 = %lld exceeds the plan's N = %lld",
                     (long long)(la + lb - 1), (long long)plan->n);

@@ -56,14 +56,11 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
                                int64_t* c, int64_t batch, const void* tw, double* d_resid,
                                hipStream_t stream);
 
-// Lines per workgroup of the poly-mul column passes for lines of 2^logl points.
-int tile_lines(int prec, int logl);
-
-// Polynomial products, N = n1 * n2 beyond the LDS range (fp64):
-//  A : int64 operands -> column FFTs (length n2) + w_N^{n1 k2}  -> ws_a, ws_b
-//  B : per row k2: FFT rows of ws_a and ws_b, product, conjugate, FFT,
-//      multiply by w_N^{n1 k2}                                  -> ws_a
-//  A2: column FFTs of ws_a, real part / N, rint                 -> c
+// Polynomial products, N = 2^(logn1 + logn2) beyond the LDS range (fp64),
+// ws = batch x N complex128:
+//  A : z = a + i b -> column FFTs (length 2^logn2) + w_N^{n1 k2}    -> ws
+//  B : rows k2, N2 - k2: FFT, product spectrum, conj, FFT, w_N^{n1 k2} -> ws
+//  A2: column FFTs, real part / N, rint                            -> c
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la,
                                    const int64_t* b, int64_t lb, int64_t* c, int64_t batch,
                                    void* ws, const void* tw_row, const void* tw_col, BigTwiddle big,

@@ -9,12 +9,12 @@
 // N <= 4096: one fused kernel per pair (int64 load with implicit zero
 // padding, two forward transforms, product, third transform, rint, int64
 // store) -- the whole product never leaves the chip.
-// N > 4096: the four-step split N = N1 N2 (see tiles.hip) with the pointwise
-// product fused between the forward and the inverse row transforms:
-//   A : columns (length N2) of both zero-padded operands, times w_N^{n1 k2}
-//   B : per row k2 (length N1): F(a-row), F(b-row), product, conj, F, times
-//       w_N^{n1 k2}  -- the forward's last pass and the inverse's first pass
-//       are one kernel, and the spectra never go back to memory in between
+// N > 4096: z = a + i b as one complex signal, split N = N1 N2, with the
+// pointwise product fused between the forward and the inverse row transforms:
+//   A : columns (length N2) of z, times w_N^{n1 k2}
+//   B : rows k2 and N2 - k2 (length N1): F of both, the product spectrum
+//       from the pair, conj, F, times w_N^{n1 k2} -- the forward's last pass
+//       and the inverse's first pass are one kernel
 //   A2: columns (length N2) again, Re / N, rint, int64 store.
 #include "launch.hpp"
 #include "stockham.hpp"
@@ -88,105 +88,144 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass A: operand columns.  Tiles run over [operand][pair][n1 tile].
+// N > 4096: the two real operands travel as one complex signal z = a + i b
+// (both have real coefficients), N = N1 N2 split as n = n1 + N1 n2,
+// k = k2 + N2 k1 (the radix-N1 form of the even/odd split of "FFT on GPU",
+// section "Fast Fourier Transform").
+//
+// Pass A: for every column n1, the N2-point transform over n2 of z, times
+// w_N^{n1 k2}; written as rows k2 (Y[k2][n1]).
 // ---------------------------------------------------------------------------
-template <int LOGN2, int C>
-__global__ __launch_bounds__(C * Geometry<LOGN2>::T)
-void polymul_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
-                      double2* __restrict__ ws, int64_t batch, int logn1, const double2* __restrict__ tw,
-                      BigTw<double2> big)
+template <int LOGN2>
+__global__ __launch_bounds__((Tile<double2, LOGN2>::THREADS))
+void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
+                       double2* __restrict__ ws, int logn1, const double2* __restrict__ tw, BigTw<double2> big)
 {
     using G = Geometry<LOGN2>;
-    __shared__ double2 lds[tile_lds_slots<LOGN2, C>()];
-    const int c = threadIdx.x % C, t = threadIdx.x / C;
+    using TL = Tile<double2, LOGN2>;
+    __shared__ double2 lds[TL::LDS];
+    const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t tps = ((int64_t)1 << logn1) / C;
-    const int64_t sig = tile / tps;  // operand * batch + pair
-    const bool is_b = sig >= batch;
-    const int64_t pair = is_b ? sig - batch : sig;
-    const int64_t len = is_b ? lb : la;
-    const int64_t* src = (is_b ? b : a) + pair * len;
-    const int64_t col = (tile % tps) * C + c;  // n1
+    const int64_t tps = ((int64_t)1 << logn1) / TL::C;
+    const int64_t pair = tile / tps;
+    const int64_t col = (tile % tps) * TL::C + c0;  // n1
+    const int64_t* pa = a + pair * la;
+    const int64_t* pb = b + pair * lb;
 
     double2 v[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
         const int64_t n = col + ((int64_t)(t + i * G::T) << logn1);
-        v[i] = double2{n < len ? (double)src[n] : 0.0, 0.0};
+        v[i] = double2{n < la ? (double)pa[n] : 0.0, n < lb ? (double)pb[n] : 0.0};
     }
     TwBases<double2, LOGN2> tb;
     tb.load(tw, t);
-    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, C>{lds, c});
+    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, TL::CL>{lds, c0});
     apply_big_twiddle<LOGN2>(v, col, t, big);
-    double2* dst = ws + (sig << (logn1 + LOGN2)) + col;
+    double2* dst = ws + (pair << (logn1 + LOGN2)) + col;
 #pragma unroll
     for (int i = 0; i < G::E; ++i) dst[(int64_t)(t + i * G::T) << logn1] = v[i];
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass B (fused): rows k2 of both spectra.
+// Pass B, fused: rows k2 and N2 - k2 together (rows 0 and N2/2 pair with
+// themselves).  After the N1-point row transforms a row holds
+// Z[k2 + N2 k1]; the partner row holds Z at -k mod N (row N2 - k2, position
+// N1 - 1 - k1; row 0: position -k1 mod N1).  With A = (Z_k + conj Z_{-k})/2
+// and B = (Z_k - conj Z_{-k})/(2i) the spectra of a and b, the product
+// spectrum is C_k = A_k B_k = (Z_k^2 - conj(Z_{-k})^2) / (4i).  The inverse
+// starts right here: conj(C), the N1-point row transform again, times
+// w_N^{n1 k2}, written back over the row.
 // ---------------------------------------------------------------------------
+template <int LOGN1> constexpr int pack_groups()
+{
+    return 2 * Geometry<LOGN1>::T >= 256 ? 1 : 256 / (2 * Geometry<LOGN1>::T);
+}
+
 template <int LOGN1>
-__global__ __launch_bounds__(Geometry<LOGN1>::T * poly_rows_per_wg<LOGN1>())
-void polymul_b_kernel(double2* __restrict__ ws_a, const double2* __restrict__ ws_b, int64_t nrows, int logn2,
-                      const double2* __restrict__ tw, BigTw<double2> big)
+__global__ __launch_bounds__(2 * Geometry<LOGN1>::T * pack_groups<LOGN1>())
+void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, const double2* __restrict__ tw,
+                       BigTw<double2> big)
 {
     using G = Geometry<LOGN1>;
-    constexpr int RPW = poly_rows_per_wg<LOGN1>();
-    __shared__ double2 lds[G::LDS > 0 ? G::LDS * RPW : 1];
+    constexpr int GR = pack_groups<LOGN1>();
+    constexpr int SLOTS = lds_padded(G::N);
+    __shared__ double2 lds[2 * SLOTS * GR];
     const int tid = threadIdx.x;
-    const int rloc = tid / G::T, t = tid % G::T;
-    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;  // pair * N2 + k2
-    const bool live = row < nrows;
-    const int64_t k2 = row & (((int64_t)1 << logn2) - 1);
-    const LdsLines<double2, 1> at{lds + rloc * G::LDS, 0};
+    const int gl = tid / (2 * G::T);
+    const int rho = (tid / G::T) & 1;
+    const int t = tid % G::T;
+    const int64_t grp = (int64_t)blockIdx.x * GR + gl;
+    const bool live = grp < ngroups;
+    const int64_t half = (int64_t)1 << (logn2 - 1);
+    const int64_t sig = grp >> (logn2 - 1);
+    const int64_t m = grp & (half - 1);
+    const int64_t n2 = half * 2;
+    const int64_t row = m == 0 ? (rho == 0 ? 0 : half) : (rho == 0 ? m : n2 - m);
+    const bool wrap = m == 0 && rho == 0;
+    double2* mine = lds + (gl * 2 + rho) * SLOTS;
+    double2* partner = m == 0 ? mine : lds + (gl * 2 + (1 - rho)) * SLOTS;
+    const LdsLines<double2, 1> L{mine, 0};
+
     TwBases<double2, LOGN1> tb;
     tb.load(tw, t);
-    const int64_t base = (row << LOGN1) + t;
-
-    double2 va[G::E], vb[G::E];
+    double2* rp = ws + (sig << (logn2 + LOGN1)) + (row << LOGN1) + t;
+    double2 v[G::E];
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) v[i] = live ? rp[i * G::T] : double2{0.0, 0.0};
+    fft_regs<LOGN1>(v, t, tb, L);
+    __syncthreads();  // LDS reads of the transforms done
+    {
+        double2* wp = L.ptr(t);
+#pragma unroll
+        for (int i = 0; i < G::E; ++i) wp[LdsLines<double2, 1>::off(i * G::T)] = v[i];
+    }
+    __syncthreads();
+    const LdsLines<double2, 1> Lp{partner, 0};
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
-        va[i] = live ? ws_a[base + i * G::T] : double2{0.0, 0.0};
-        vb[i] = live ? ws_b[base + i * G::T] : double2{0.0, 0.0};
+        const int k1 = t + i * G::T;
+        const int pos = wrap ? ((G::N - k1) & (G::N - 1)) : (G::N - 1 - k1);
+        const double2 zq = *Lp.ptr(pos);
+        const double2 z = v[i];
+        // s = z^2 - conj(zq)^2 ; conj(s / 4i) = (s.y / 4, s.x / 4)
+        const double sx = (z.x * z.x - z.y * z.y) - (zq.x * zq.x - zq.y * zq.y);
+        const double sy = 2.0 * z.x * z.y + 2.0 * zq.x * zq.y;
+        v[i] = double2{0.25 * sy, 0.25 * sx};
     }
-    fft_regs<LOGN1>(va, t, tb, at);
-    if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN1>(vb, t, tb, at);
-#pragma unroll
-    for (int i = 0; i < G::E; ++i) va[i] = cconj(cmul(va[i], vb[i]));
-    if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN1>(va, t, tb, at);
-    apply_big_twiddle<LOGN1>(va, k2, t, big);
+    __syncthreads();  // partner reads done before the LDS is reused
+    fft_regs<LOGN1>(v, t, tb, L);
+    apply_big_twiddle<LOGN1>(v, row, t, big);
     if (live) {
 #pragma unroll
-        for (int i = 0; i < G::E; ++i) ws_a[base + i * G::T] = va[i];
+        for (int i = 0; i < G::E; ++i) rp[i * G::T] = v[i];
     }
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass A2: columns of the product's transform, Re / N, rint.
+// Pass A2: columns again (k2 -> n2), Re / N, rint, int64 store.
 // ---------------------------------------------------------------------------
-template <int LOGN2, int C>
-__global__ __launch_bounds__(C * Geometry<LOGN2>::T)
-void polymul_a2_kernel(const double2* __restrict__ ws_a, int64_t* __restrict__ c_out, int64_t lc, int logn1,
-                       const double2* __restrict__ tw, double* __restrict__ d_resid)
+template <int LOGN2>
+__global__ __launch_bounds__((Tile<double2, LOGN2>::THREADS))
+void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
+                        const double2* __restrict__ tw, double* __restrict__ d_resid)
 {
     using G = Geometry<LOGN2>;
-    __shared__ double2 lds[tile_lds_slots<LOGN2, C>()];
-    const int c = threadIdx.x % C, t = threadIdx.x / C;
+    using TL = Tile<double2, LOGN2>;
+    __shared__ double2 lds[TL::LDS];
+    const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t tps = ((int64_t)1 << logn1) / C;
+    const int64_t tps = ((int64_t)1 << logn1) / TL::C;
     const int64_t pair = tile / tps;
-    const int64_t col = (tile % tps) * C + c;  // n1
-    const double2* src = ws_a + (pair << (logn1 + LOGN2)) + col;
+    const int64_t col = (tile % tps) * TL::C + c0;  // n1
+    const double2* src = ws + (pair << (logn1 + LOGN2)) + col;
 
     double2 v[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) v[i] = src[(int64_t)(t + i * G::T) << logn1];
     TwBases<double2, LOGN2> tb;
     tb.load(tw, t);
-    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, C>{lds, c});
+    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, TL::CL>{lds, c0});
 
     const double inv_n = 1.0 / (double)((int64_t)1 << (logn1 + LOGN2));
     double worst = 0.0;
@@ -237,44 +276,42 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
 }
 
 template <int LOGN2>
-static hipError_t polymul_a_t(int logn1, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* ws,
-                              int64_t batch, const void* tw_col, BigTw<double2> big, hipStream_t s)
+static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* ws,
+                               int64_t batch, const void* tw_col, BigTw<double2> big, hipStream_t s)
 {
-    constexpr int C = TileShape<double2, LOGN2>::C;
+    using TL = Tile<double2, LOGN2>;
     const int64_t n1 = (int64_t)1 << logn1;
-    if (n1 % C) return hipErrorInvalidValue;
-    const int64_t blocks = 2 * batch * (n1 / C);
+    if (n1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
+    const int64_t blocks = batch * (n1 / TL::C);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polymul_a_kernel<LOGN2, C>), dim3((unsigned)blocks), dim3(C * Geometry<LOGN2>::T), 0, s,
-                       a, la, b, lb, (double2*)ws, batch, logn1, (const double2*)tw_col, big);
+    hipLaunchKernelGGL((polypack_a_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s, a, la, b, lb,
+                       (double2*)ws, logn1, (const double2*)tw_col, big);
     return hipGetLastError();
 }
 
 template <int LOGN1>
-static hipError_t polymul_b_t(int logn2, void* ws, int64_t batch, const void* tw_row, BigTw<double2> big,
-                              hipStream_t s)
+static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* tw_row, BigTw<double2> big,
+                               hipStream_t s)
 {
-    constexpr int RPW = poly_rows_per_wg<LOGN1>();
-    const int64_t nrows = batch << logn2;
-    const int64_t blocks = (nrows + RPW - 1) / RPW;
+    constexpr int GR = pack_groups<LOGN1>();
+    const int64_t ngroups = batch << (logn2 - 1);
+    const int64_t blocks = (ngroups + GR - 1) / GR;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    double2* ws_a = (double2*)ws;
-    const double2* ws_b = ws_a + (batch << (LOGN1 + logn2));
-    hipLaunchKernelGGL((polymul_b_kernel<LOGN1>), dim3((unsigned)blocks), dim3(Geometry<LOGN1>::T * RPW), 0, s,
-                       ws_a, ws_b, nrows, logn2, (const double2*)tw_row, big);
+    hipLaunchKernelGGL((polypack_b_kernel<LOGN1>), dim3((unsigned)blocks), dim3(2 * Geometry<LOGN1>::T * GR), 0, s,
+                       (double2*)ws, ngroups, logn2, (const double2*)tw_row, big);
     return hipGetLastError();
 }
 
 template <int LOGN2>
-static hipError_t polymul_a2_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
-                               const void* tw_col, double* d_resid, hipStream_t s)
+static hipError_t polypack_a2_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
+                                const void* tw_col, double* d_resid, hipStream_t s)
 {
-    constexpr int C = TileShape<double2, LOGN2>::C;
+    using TL = Tile<double2, LOGN2>;
     const int64_t n1 = (int64_t)1 << logn1;
-    if (n1 % C) return hipErrorInvalidValue;
-    const int64_t blocks = batch * (n1 / C);
+    if (n1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
+    const int64_t blocks = batch * (n1 / TL::C);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polymul_a2_kernel<LOGN2, C>), dim3((unsigned)blocks), dim3(C * Geometry<LOGN2>::T), 0, s,
+    hipLaunchKernelGGL((polypack_a2_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s,
                        (const double2*)ws, c, lc, logn1, (const double2*)tw_col, d_resid);
     return hipGetLastError();
 }
@@ -286,14 +323,14 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     const BigTw<double2> big{(const double2*)bigt.hi, (const double2*)bigt.lo, bigt.lbits, bigt.logn};
     hipError_t e = hipErrorInvalidValue;
     switch (logn2) {
-#define PA(L) case L: e = polymul_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, s); break;
-        PA(5) PA(6) PA(7) PA(8) PA(9) PA(10) PA(11) PA(12)
+#define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, s); break;
+        PA(5) PA(6) PA(7) PA(8) PA(9) PA(10)
 #undef PA
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     switch (logn1) {
-#define PB(L) case L: e = polymul_b_t<L>(logn2, ws, batch, tw_row, big, s); break;
+#define PB(L) case L: e = polypack_b_t<L>(logn2, ws, batch, tw_row, big, s); break;
         PB(5) PB(6) PB(7) PB(8) PB(9) PB(10) PB(11) PB(12)
 #undef PB
         default: return hipErrorInvalidValue;
@@ -301,22 +338,12 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     if (e != hipSuccess) return e;
     const int64_t lc = la + lb - 1;
     switch (logn2) {
-#define PA2(L) case L: e = polymul_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
-        PA2(5) PA2(6) PA2(7) PA2(8) PA2(9) PA2(10) PA2(11) PA2(12)
+#define PA2(L) case L: e = polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
+        PA2(5) PA2(6) PA2(7) PA2(8) PA2(9) PA2(10)
 #undef PA2
         default: return hipErrorInvalidValue;
     }
     return e;
-}
-
-int tile_lines(int prec, int logl)
-{
-    switch (logl) {
-#define TL(L) case L: return prec == 0 ? TileShape<float2, L>::C : TileShape<double2, L>::C;
-        TL(1) TL(2) TL(3) TL(4) TL(5) TL(6) TL(7) TL(8) TL(9) TL(10) TL(11) TL(12)
-#undef TL
-        default: return 0;
-    }
 }
 
 }  // namespace fftmi

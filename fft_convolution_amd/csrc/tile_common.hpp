@@ -5,25 +5,6 @@
 
 namespace fftmi {
 
-// Lines per workgroup for a tile kernel over lines of N = 2^LOGN elements:
-// as many as fit in ~70 KB of LDS (two workgroups per CU), at most 64 and at
-// most 1024 threads; rows that fit one thread (N <= 16) need no LDS and take
-// 256 lines.
-template <typename V, int LOGN> struct TileShape {
-    using G = Geometry<LOGN>;
-    static constexpr int pow2_floor(long x) { int p = 1; while ((long)p * 2 <= x) p *= 2; return p; }
-    static constexpr long line_bytes = (long)lds_padded(G::N) * (long)sizeof(V);
-    static constexpr int by_lds = G::S > 1 ? pow2_floor(71680 / line_bytes) : 256;
-    static constexpr int by_threads = 1024 / G::T;
-    static constexpr int C0 = by_lds < by_threads ? by_lds : by_threads;
-    static constexpr int C = G::S > 1 ? (C0 > 64 ? 64 : (C0 < 1 ? 1 : C0)) : 256;
-};
-
-template <int LOGN, int C> constexpr int tile_lds_slots()
-{
-    return Geometry<LOGN>::S > 1 ? lds_padded(C * Geometry<LOGN>::N) : 1;
-}
-
 // Tile geometry for passes over lines of L = 2^LOGL points that are not
 // contiguous in memory (matrix columns, Stockham butterflies at a stride).
 // Each thread owns P adjacent lines, loaded together as one 16-byte vector
