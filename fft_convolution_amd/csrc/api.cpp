@@ -94,13 +94,14 @@ void root_of_unity(int64_t m, int64_t M, double* re, double* im)
 
 // Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
 // interleaved doubles: stage s >= 1 holds [l][k] = w_{Ns R}^{k 2^l}.
-std::vector<double> stage_table(int logn)
+std::vector<double> stage_table(int logn, int prec)
 {
-    std::vector<double> t(2 * (size_t)plan_tw_entries(logn));
-    for (int s = 1; s < plan_nstages(logn); ++s) {
-        const int lr = plan_stage_logr(logn, s);
-        const int64_t ns = int64_t(1) << plan_stage_lns(logn, s);
-        const long off = plan_tw_offset(logn, s);
+    const int lem = plan_lem(prec);
+    std::vector<double> t(2 * (size_t)plan_tw_entries(logn, lem));
+    for (int s = 1; s < plan_nstages(logn, lem); ++s) {
+        const int lr = plan_stage_logr(logn, lem, s);
+        const int64_t ns = int64_t(1) << plan_stage_lns(logn, lem, s);
+        const long off = plan_tw_offset(logn, lem, s);
         for (int l = 0; l < lr; ++l)
             for (int64_t k = 0; k < ns; ++k) {
                 const size_t e = (size_t)(off + l * ns + k);
@@ -336,7 +337,7 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
         } else if (n <= max_lds_n(prec)) {
             p->path = PATH_ROWS;
             p->log_a = p->logn;
-            st = upload(stage_table(p->log_a), prec, &p->tw_a);
+            st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
         } else {
             p->path = PATH_MULTIPASS;
             // Super-stages of at most 2^9 points, as even as possible, larger first.
@@ -348,7 +349,7 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
                 pp.logns = logns;
                 pp.kind = q == 0 ? 0 : (q == np - 1 ? 2 : 1);
                 logns += pp.logr;
-                st = upload(stage_table(pp.logr), prec, &p->pass_tw[q]);
+                st = upload(stage_table(pp.logr, prec), prec, &p->pass_tw[q]);
                 pp.tw = p->pass_tw[q];
                 if (st == FFT_OK && q > 0) st = upload_big(pp.logns + pp.logr, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
                 const int c = tile_lines_2d(prec, pp.logr);
@@ -363,8 +364,8 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
                 p->log_b = std::min(9, (p->logn + 1) / 2);  // N2, the column length
                 if (p->logn - p->log_b > 12) p->log_b = p->logn - 12;
                 p->log_a = p->logn - p->log_b;               // N1, the row length
-                st = upload(stage_table(p->log_a), prec, &p->tw_a);
-                if (st == FFT_OK) st = upload(stage_table(p->log_b), prec, &p->tw_b);
+                st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
+                if (st == FFT_OK) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
                 if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
             }
         }
@@ -386,8 +387,8 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
             p->logf = lf;
         }
         p->log_b = logh - p->logf;  // Lc, the column pass length
-        if (p->log_a > 0) st = upload(stage_table(p->log_a), prec, &p->tw_a);
-        if (st == FFT_OK && p->log_b > 0) st = upload(stage_table(p->log_b), prec, &p->tw_b);
+        if (p->log_a > 0) st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
+        if (st == FFT_OK && p->log_b > 0) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
         if (st == FFT_OK && p->logf > 0) st = upload_big(logh, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
     }
     if (st != FFT_OK) {
@@ -414,7 +415,7 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             break;
         case PATH_ROWS:
             snprintf(buf, len, "rank=1 n=%lld prec=%s path=rows stages=%d", (long long)p->n, prec,
-                     plan_nstages(p->log_a));
+                     plan_nstages(p->log_a, plan_lem(p->prec)));
             break;
         case PATH_MULTIPASS: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);

@@ -23,29 +23,39 @@
 namespace fftmi {
 
 // Max of non-negative doubles by their bit patterns (which order like the
-// values), one atomic per wave.
+// values): reduce over the wave, then over the workgroup through LDS, then one
+// vector atomic per workgroup -- skipped when the value already stored is at
+// least as large (a stale read can only make it do an unneeded atomic).  All
+// threads of the workgroup must call it.
 __device__ __forceinline__ void resid_max(double r, double* d_resid)
 {
+    __shared__ double red[16];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) r = fmax(r, __shfl_xor(r, off, 64));
-    if ((threadIdx.x & 63) == 0 && d_resid)
-        atomicMax((unsigned long long*)d_resid, (unsigned long long)__double_as_longlong(r));
+    const int wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = r;
+    __syncthreads();
+    if (threadIdx.x == 0 && d_resid) {
+        for (int w = 1; w < nwaves; ++w) r = fmax(r, red[w]);
+        const unsigned long long bits = (unsigned long long)__double_as_longlong(r);
+        if (bits > *(volatile unsigned long long*)d_resid) atomicMax((unsigned long long*)d_resid, bits);
+    }
 }
 
 __global__ void zero_resid_kernel(double* d) { *d = 0.0; }
 
-template <int LOGN> constexpr int poly_rows_per_wg() { return Geometry<LOGN>::T >= 256 ? 1 : 256 / Geometry<LOGN>::T; }
+template <int LOGN> constexpr int poly_rows_per_wg() { return Geom<double2, LOGN>::T >= 256 ? 1 : 256 / Geom<double2, LOGN>::T; }
 
 // ---------------------------------------------------------------------------
 // Fused single-kernel product for N = 2^LOGN <= 4096.
 // ---------------------------------------------------------------------------
 template <int LOGN>
-__global__ __launch_bounds__(Geometry<LOGN>::T * poly_rows_per_wg<LOGN>())
+__global__ __launch_bounds__((Geom<double2, LOGN>::T * poly_rows_per_wg<LOGN>()))
 void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
                          int64_t* __restrict__ c, int64_t batch, const double2* __restrict__ tw,
                          double* __restrict__ d_resid)
 {
-    using G = Geometry<LOGN>;
+    using G = Geom<double2, LOGN>;
     constexpr int RPW = poly_rows_per_wg<LOGN>();
     __shared__ double2 lds[G::LDS > 0 ? G::LDS * RPW : 1];
     const int tid = threadIdx.x;
@@ -101,7 +111,7 @@ __global__ __launch_bounds__((Tile<double2, LOGN2>::THREADS))
 void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
                        double2* __restrict__ ws, int logn1, const double2* __restrict__ tw, BigTw<double2> big)
 {
-    using G = Geometry<LOGN2>;
+    using G = Geom<double2, LOGN2>;
     using TL = Tile<double2, LOGN2>;
     __shared__ double2 lds[TL::LDS];
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
@@ -139,15 +149,15 @@ void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t*
 // ---------------------------------------------------------------------------
 template <int LOGN1> constexpr int pack_groups()
 {
-    return 2 * Geometry<LOGN1>::T >= 256 ? 1 : 256 / (2 * Geometry<LOGN1>::T);
+    return 2 * Geom<double2, LOGN1>::T >= 256 ? 1 : 256 / (2 * Geom<double2, LOGN1>::T);
 }
 
 template <int LOGN1>
-__global__ __launch_bounds__(2 * Geometry<LOGN1>::T * pack_groups<LOGN1>())
+__global__ __launch_bounds__((2 * Geom<double2, LOGN1>::T * pack_groups<LOGN1>()))
 void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, const double2* __restrict__ tw,
                        BigTw<double2> big)
 {
-    using G = Geometry<LOGN1>;
+    using G = Geom<double2, LOGN1>;
     constexpr int GR = pack_groups<LOGN1>();
     constexpr int SLOTS = lds_padded(G::N);
     __shared__ double2 lds[2 * SLOTS * GR];
@@ -210,7 +220,7 @@ __global__ __launch_bounds__((Tile<double2, LOGN2>::THREADS))
 void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
                         const double2* __restrict__ tw, double* __restrict__ d_resid)
 {
-    using G = Geometry<LOGN2>;
+    using G = Geom<double2, LOGN2>;
     using TL = Tile<double2, LOGN2>;
     __shared__ double2 lds[TL::LDS];
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
@@ -259,7 +269,7 @@ static hipError_t polymul_rows_t(const int64_t* a, int64_t la, const int64_t* b,
     constexpr int RPW = poly_rows_per_wg<LOGN>();
     const int64_t blocks = (batch + RPW - 1) / RPW;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polymul_rows_kernel<LOGN>), dim3((unsigned)blocks), dim3(Geometry<LOGN>::T * RPW), 0, s,
+    hipLaunchKernelGGL((polymul_rows_kernel<LOGN>), dim3((unsigned)blocks), dim3(Geom<double2, LOGN>::T * RPW), 0, s,
                        a, la, b, lb, c, batch, (const double2*)tw, d_resid);
     return hipGetLastError();
 }
@@ -297,7 +307,7 @@ static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* t
     const int64_t ngroups = batch << (logn2 - 1);
     const int64_t blocks = (ngroups + GR - 1) / GR;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polypack_b_kernel<LOGN1>), dim3((unsigned)blocks), dim3(2 * Geometry<LOGN1>::T * GR), 0, s,
+    hipLaunchKernelGGL((polypack_b_kernel<LOGN1>), dim3((unsigned)blocks), dim3(2 * Geom<double2, LOGN1>::T * GR), 0, s,
                        (double2*)ws, ngroups, logn2, (const double2*)tw_row, big);
     return hipGetLastError();
 }

@@ -19,29 +19,35 @@
 
 namespace fftmi {
 
-// log2 of elements per thread: rows up to 16 points live in one thread;
-// 8192 points use 32 per thread (three stages 32 x 16 x 16); the rest 16.
-constexpr int plan_loge(int logn) { return logn <= 4 ? logn : (logn == 13 ? 5 : 4); }
-
-constexpr int plan_nstages(int logn)
+// `lem` is log2 of the elements a thread holds for long rows: 4 (16) for
+// complex64, 3 (8) for complex128, whose registers are twice as wide.
+//
+// log2 of elements per thread: rows up to 2^lem points live in one thread;
+// with lem = 4, 8192 points use 32 per thread (three stages 32 x 16 x 16).
+constexpr int plan_loge(int logn, int lem)
 {
-    return logn <= 4 ? 1 : (logn == 13 ? 3 : (logn + 3) / 4);
+    return logn <= lem ? logn : (lem == 4 && logn == 13 ? 5 : lem);
 }
 
-// log2 of the radix of stage s.  Radix 16 first (the first stage needs no
-// twiddles), the remainder last; 8192 = 32 x 16 x 16.
-constexpr int plan_stage_logr(int logn, int s)
+constexpr int plan_nstages(int logn, int lem)
 {
-    return logn <= 4 ? logn
-         : logn == 13 ? (s == 0 ? 5 : 4)
-         : (s < logn / 4 ? 4 : logn % 4);
+    return logn <= lem ? 1 : (lem == 4 && logn == 13 ? 3 : (logn + lem - 1) / lem);
+}
+
+// log2 of the radix of stage s.  Radix 2^lem first (the first stage needs no
+// twiddles), the remainder last; 8192 = 32 x 16 x 16 with lem = 4.
+constexpr int plan_stage_logr(int logn, int lem, int s)
+{
+    return logn <= lem ? logn
+         : (lem == 4 && logn == 13) ? (s == 0 ? 5 : 4)
+         : (s < logn / lem ? lem : logn % lem);
 }
 
 // log2 of Ns, the span of the sub-transforms a stage combines.
-constexpr int plan_stage_lns(int logn, int s)
+constexpr int plan_stage_lns(int logn, int lem, int s)
 {
     int acc = 0;
-    for (int q = 0; q < s; ++q) acc += plan_stage_logr(logn, q);
+    for (int q = 0; q < s; ++q) acc += plan_stage_logr(logn, lem, q);
     return acc;
 }
 
@@ -50,15 +56,18 @@ constexpr int plan_stage_lns(int logn, int s)
 // entries.  A thread multiplies its R inputs by w^r = w_{Ns R}^{r k}, built as
 // products of the bases over the set bits of r (at most log2 R factors, each
 // read from the exactly rounded table).  Stage 0 has Ns = 1 and no table.
-constexpr long plan_tw_offset(int logn, int s)
+constexpr long plan_tw_offset(int logn, int lem, int s)
 {
     long off = 0;
     for (int q = 1; q < s; ++q)
-        off += (long)plan_stage_logr(logn, q) << plan_stage_lns(logn, q);
+        off += (long)plan_stage_logr(logn, lem, q) << plan_stage_lns(logn, lem, q);
     return off;
 }
 
-constexpr long plan_tw_entries(int logn) { return plan_tw_offset(logn, plan_nstages(logn)); }
+constexpr long plan_tw_entries(int logn, int lem) { return plan_tw_offset(logn, lem, plan_nstages(logn, lem)); }
+
+// lem for a plan precision (0 = complex64, 1 = complex128).
+constexpr int plan_lem(int prec) { return prec == 0 ? 4 : 3; }
 
 // LDS slots for `n` elements with one pad slot after every 16, which spreads
 // the power-of-two strides of the stage writes over all banks.  The slot of

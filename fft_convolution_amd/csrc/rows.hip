@@ -11,7 +11,7 @@
 namespace fftmi {
 
 // Rows per workgroup: at least 256 threads per workgroup.
-template <int LOGN> constexpr int rows_per_wg() { return Geometry<LOGN>::T >= 256 ? 1 : 256 / Geometry<LOGN>::T; }
+template <typename V, int LOGN> constexpr int rows_per_wg() { return Geom<V, LOGN>::T >= 256 ? 1 : 256 / Geom<V, LOGN>::T; }
 
 // One workgroup per group of RPW rows; the hardware dispatcher starts a new
 // workgroup as soon as one retires, so the load, compute and store phases of
@@ -19,12 +19,12 @@ template <int LOGN> constexpr int rows_per_wg() { return Geometry<LOGN>::T >= 25
 // of 4096 points: this beats a persistent grid with a one-row register
 // prefetch, 174 us against 187-201 us per launch.)
 template <typename V, int LOGN, bool CONJ_IN, bool CONJ_OUT>
-__global__ __launch_bounds__(Geometry<LOGN>::T * rows_per_wg<LOGN>())
+__global__ __launch_bounds__((Geom<V, LOGN>::T * rows_per_wg<V, LOGN>()))
 void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
                  typename real_of<V>::type scale)
 {
-    using G = Geometry<LOGN>;
-    constexpr int RPW = rows_per_wg<LOGN>();
+    using G = Geom<V, LOGN>;
+    constexpr int RPW = rows_per_wg<V, LOGN>();
     __shared__ V lds[G::LDS > 0 ? G::LDS * RPW : 1];
 
     const int tid = threadIdx.x;
@@ -58,8 +58,8 @@ template <typename V, int LOGN, bool CI, bool CO>
 static hipError_t launch_rows_t(const void* in, void* out, int64_t nrows, const void* tw, double scale,
                                 hipStream_t stream)
 {
-    constexpr int RPW = rows_per_wg<LOGN>();
-    constexpr int BLOCK = Geometry<LOGN>::T * RPW;
+    constexpr int RPW = rows_per_wg<V, LOGN>();
+    constexpr int BLOCK = Geom<V, LOGN>::T * RPW;
     const int64_t blocks = (nrows + RPW - 1) / RPW;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;

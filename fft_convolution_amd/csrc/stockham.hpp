@@ -200,19 +200,29 @@ __device__ __forceinline__ void st_stream(double2* p, double2 x)
 // ---------------------------------------------------------------------------
 // The workgroup engine.
 // ---------------------------------------------------------------------------
-template <int LOGN> struct Geometry {
+template <typename V> struct lem_of;
+template <> struct lem_of<float2> { static constexpr int value = 4; };
+template <> struct lem_of<double2> { static constexpr int value = 3; };
+
+template <int LOGN, int LEM> struct Geometry {
     static constexpr int N = 1 << LOGN;
-    static constexpr int LOGE = plan_loge(LOGN);
+    static constexpr int LOGE = plan_loge(LOGN, LEM);
     static constexpr int E = 1 << LOGE;         // elements per thread
     static constexpr int T = N / E;             // threads per transform
-    static constexpr int S = plan_nstages(LOGN);
+    static constexpr int S = plan_nstages(LOGN, LEM);
     static constexpr int LDS = S > 1 ? lds_padded(N) : 0;  // LDS slots per transform
 };
 
-template <int LOGN, int STAGE> struct StageInfo {
-    using G = Geometry<LOGN>;
-    static constexpr int LR = plan_stage_logr(LOGN, STAGE), R = 1 << LR;
-    static constexpr int LNS = plan_stage_lns(LOGN, STAGE), NS = 1 << LNS;
+// The geometry of a transform of 2^LOGN points of element type V.
+template <typename V, int LOGN> using Geom = Geometry<LOGN, lem_of<V>::value>;
+// Elements per thread, for array parameters.
+template <typename V, int LOGN> constexpr int kE = Geom<V, LOGN>::E;
+
+template <typename V, int LOGN, int STAGE> struct StageInfo {
+    using G = Geom<V, LOGN>;
+    static constexpr int LEM = lem_of<V>::value;
+    static constexpr int LR = plan_stage_logr(LOGN, LEM, STAGE), R = 1 << LR;
+    static constexpr int LNS = plan_stage_lns(LOGN, LEM, STAGE), NS = 1 << LNS;
     static constexpr int B = G::E / R;           // butterflies per thread
     static constexpr bool TW = NS > 1;           // stage 0 needs no twiddles
     static constexpr int NB = TW ? B * LR : 1;   // twiddle bases per thread
@@ -221,18 +231,18 @@ template <int LOGN, int STAGE> struct StageInfo {
 
 // The twiddle bases a thread needs for every stage, loaded once (they depend
 // only on the thread's position t) and kept in registers.
-template <typename V, int LOGN, int STAGE = 0, bool END = (STAGE >= Geometry<LOGN>::S)>
+template <typename V, int LOGN, int STAGE = 0, bool END = (STAGE >= Geom<V, LOGN>::S)>
 struct TwBases {
-    using I = StageInfo<LOGN, STAGE>;
+    using I = StageInfo<V, LOGN, STAGE>;
     V w[I::NB];
     TwBases<V, LOGN, STAGE + 1> next;
     __device__ __forceinline__ void load(const V* __restrict__ tw, int t)
     {
         if constexpr (I::TW) {
-            const V* __restrict__ tws = tw + plan_tw_offset(LOGN, STAGE);
+            const V* __restrict__ tws = tw + plan_tw_offset(LOGN, I::LEM, STAGE);
 #pragma unroll
             for (int b = 0; b < I::B; ++b) {
-                const int k = (t + b * Geometry<LOGN>::T) & (I::NS - 1);
+                const int k = (t + b * Geom<V, LOGN>::T) & (I::NS - 1);
 #pragma unroll
                 for (int l = 0; l < I::LR; ++l) w[b * I::LR + l] = tws[l * I::NS + k];
             }
@@ -282,11 +292,12 @@ __device__ __forceinline__ void apply_stage_twiddles(V* u, const V* wb)
 // One Stockham stage on the registers of thread t.  Not the last stage:
 // outputs go to LDS in the stage's output order.  Last stage: outputs stay in
 // v (position t + i T in v[i]).
-template <int LOGN, int STAGE, typename V, typename TB, typename L>
-__device__ __forceinline__ void fft_stage(V (&v)[Geometry<LOGN>::E], int t, const TB& tb, const L& lds)
+template <int LOGN, int STAGE, typename V, int E, typename TB, typename L>
+__device__ __forceinline__ void fft_stage(V (&v)[E], int t, const TB& tb, const L& lds)
 {
-    using G = Geometry<LOGN>;
-    using I = StageInfo<LOGN, STAGE>;
+    static_assert(E == kE<V, LOGN>, "register array size");
+    using G = Geom<V, LOGN>;
+    using I = StageInfo<V, LOGN, STAGE>;
 #pragma unroll
     for (int b = 0; b < I::B; ++b) {
         V u[I::R];
@@ -307,10 +318,11 @@ __device__ __forceinline__ void fft_stage(V (&v)[Geometry<LOGN>::E], int t, cons
     }
 }
 
-template <int LOGN, int STAGE, typename V, typename TB, typename L>
-__device__ __forceinline__ void fft_stages_from(V (&v)[Geometry<LOGN>::E], int t, const TB& tb, const L& lds)
+template <int LOGN, int STAGE, typename V, int E, typename TB, typename L>
+__device__ __forceinline__ void fft_stages_from(V (&v)[E], int t, const TB& tb, const L& lds)
 {
-    using G = Geometry<LOGN>;
+    static_assert(E == kE<V, LOGN>, "register array size");
+    using G = Geom<V, LOGN>;
     if constexpr (STAGE < G::S) {
         if constexpr (STAGE > 0) {
             __syncthreads();  // the previous stage's LDS writes are visible
@@ -327,9 +339,10 @@ __device__ __forceinline__ void fft_stages_from(V (&v)[Geometry<LOGN>::E], int t
 // Forward transform of N = 2^LOGN points held as v[i] = x[t + i T]; on return
 // v[i] = X[t + i T].  Every thread of the workgroup must call it (barriers).
 // If the caller reuses the LDS afterwards it must put a barrier first.
-template <int LOGN, typename V, typename TB, typename L>
-__device__ __forceinline__ void fft_regs(V (&v)[Geometry<LOGN>::E], int t, const TB& tb, const L& lds)
+template <int LOGN, typename V, int E, typename TB, typename L>
+__device__ __forceinline__ void fft_regs(V (&v)[E], int t, const TB& tb, const L& lds)
 {
+    static_assert(E == kE<V, LOGN>, "register array size");
     fft_stages_from<LOGN, 0>(v, t, tb, lds);
 }
 
@@ -341,11 +354,12 @@ __device__ __forceinline__ void fft_regs(V (&v)[Geometry<LOGN>::E], int t, const
 // twiddle bases `tb` must have been loaded for tb_t (stage 0 needs none).
 // This lets a kernel load with lanes running across lines and store with
 // lanes running along a line (or the reverse) at no extra LDS traffic.
-template <int LOGN, typename V, typename TB, typename LA, typename LB>
-__device__ __forceinline__ void fft_regs_remap(V (&v)[Geometry<LOGN>::E], int ta, const LA& la, int tb_t,
-                                               const TB& tb, const LB& lb)
+template <int LOGN, typename V, int E, typename TB, typename LA, typename LB>
+__device__ __forceinline__ void fft_regs_remap(V (&v)[E], int ta, const LA& la, int tb_t, const TB& tb,
+                                               const LB& lb)
 {
-    static_assert(Geometry<LOGN>::S > 1, "a remap needs at least one exchange");
+    static_assert(E == kE<V, LOGN>, "register array size");
+    static_assert(Geom<V, LOGN>::S > 1, "a remap needs at least one exchange");
     fft_stage<LOGN, 0>(v, ta, tb, la);
     fft_stages_from<LOGN, 1>(v, tb_t, tb, lb);
 }

@@ -12,7 +12,7 @@ namespace fftmi {
 // unit the memory system moves without waste); a workgroup owns C = CL P
 // lines and runs the P sets of CL lines through LDS one after another.
 template <typename V, int LOGL> struct Tile {
-    using G = Geometry<LOGL>;
+    using G = Geom<V, LOGL>;
     static constexpr int P = 16 / (int)sizeof(V);      // complex64: 2, complex128: 1
     static constexpr int CL0 = 256 / G::T;
     static constexpr int CL = CL0 < 8 ? 8 : (CL0 > 64 ? 64 : CL0);
@@ -73,10 +73,11 @@ template <typename V> struct RootTw {
 // The factors are w0 = w_N^{line t} times products of g_j = w_N^{line T 2^j}
 // over the set bits j of i, every factor read from the exact tables, so each
 // twiddle carries a handful of roundings, not a long recurrence.
-template <int LOGN, typename V, typename TW>
-__device__ __forceinline__ void apply_big_twiddle(V (&v)[Geometry<LOGN>::E], int64_t line, int t, TW bt)
+template <int LOGN, typename V, int E, typename TW>
+__device__ __forceinline__ void apply_big_twiddle(V (&v)[E], int64_t line, int t, TW bt)
 {
-    using G = Geometry<LOGN>;
+    static_assert(E == kE<V, LOGN>, "register array size");
+    using G = Geom<V, LOGN>;
     V p[G::E];
     p[0] = bt(line * t);
 #pragma unroll

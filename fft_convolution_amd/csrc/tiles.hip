@@ -39,7 +39,7 @@ __global__ __launch_bounds__((Tile<V, LOGL>::THREADS))
 void cols2d_kernel(const V* in, V* out, int64_t w, int logf, int64_t col_tiles, const V* __restrict__ tw,
                    BigTw<V> htw, typename real_of<V>::type scale)
 {
-    using G = Geometry<LOGL>;
+    using G = Geom<V, LOGL>;
     using TL = Tile<V, LOGL>;
     __shared__ V lds[TL::LDS];
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
@@ -97,18 +97,18 @@ void cols2d_kernel(const V* in, V* out, int64_t w, int logf, int64_t col_tiles, 
 // E/F positions, does the F-point DFT across the rows and writes row j F + r'.
 // Out of place (the rows it writes are read by other groups).
 // ---------------------------------------------------------------------------
-template <int LOGW, int LOGF> constexpr int fold_groups()
+template <typename V, int LOGW, int LOGF> constexpr int fold_groups()
 {
-    return (Geometry<LOGW>::T << LOGF) >= 256 ? 1 : 256 / (Geometry<LOGW>::T << LOGF);
+    return (Geom<V, LOGW>::T << LOGF) >= 256 ? 1 : 256 / (Geom<V, LOGW>::T << LOGF);
 }
 
 template <typename V, int LOGW, int LOGF, bool CONJ_IN>
-__global__ __launch_bounds__(((Geometry<LOGW>::T << LOGF) * fold_groups<LOGW, LOGF>()))
+__global__ __launch_bounds__(((Geom<V, LOGW>::T << LOGF) * fold_groups<V, LOGW, LOGF>()))
 void rows2d_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* __restrict__ tw)
 {
-    using G = Geometry<LOGW>;
+    using G = Geom<V, LOGW>;
     constexpr int F = 1 << LOGF;
-    constexpr int GR = fold_groups<LOGW, LOGF>();
+    constexpr int GR = fold_groups<V, LOGW, LOGF>();
     constexpr int SLOTS = lds_padded(G::N);  // one row, padded (also used when S == 1)
     constexpr int EF = G::E / F;
     static_assert(G::E >= F, "each thread needs at least F positions");
@@ -166,7 +166,7 @@ __global__ __launch_bounds__((Tile<V, LOGR>::THREADS))
 void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_per_sig, const V* __restrict__ tw,
                        BigTw<V> big, typename real_of<V>::type scale)
 {
-    using G = Geometry<LOGR>;
+    using G = Geom<V, LOGR>;
     using TL = Tile<V, LOGR>;
     __shared__ V lds[TL::LDS];
     const int tid = threadIdx.x;
@@ -261,9 +261,9 @@ static hipError_t cols2d_t(const void* in, void* out, int64_t nimg, int64_t w, i
 
 template <typename V, int LOGW, int LOGF> constexpr bool fold_ok()
 {
-    using G = Geometry<LOGW>;
-    constexpr long threads = (long)(G::T << LOGF) * fold_groups<LOGW, LOGF>();
-    constexpr long lds = (long)lds_padded(G::N) * (1 << LOGF) * fold_groups<LOGW, LOGF>() * (long)sizeof(V);
+    using G = Geom<V, LOGW>;
+    constexpr long threads = (long)(G::T << LOGF) * fold_groups<V, LOGW, LOGF>();
+    constexpr long lds = (long)lds_padded(G::N) * (1 << LOGF) * fold_groups<V, LOGW, LOGF>() * (long)sizeof(V);
     return G::E >= (1 << LOGF) && threads <= 1024 && lds <= 160 * 1024;
 }
 
@@ -273,11 +273,11 @@ static hipError_t fold_t(const void* in, void* out, int64_t nimg, int log_lc, co
     if constexpr (!fold_ok<V, LOGW, LOGF>()) {
         return hipErrorInvalidValue;
     } else {
-        constexpr int GR = fold_groups<LOGW, LOGF>();
+        constexpr int GR = fold_groups<V, LOGW, LOGF>();
         const int64_t ngroups = nimg << log_lc;
         const int64_t blocks = (ngroups + GR - 1) / GR;
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        const dim3 block((Geometry<LOGW>::T << LOGF) * GR);
+        const dim3 block((Geom<V, LOGW>::T << LOGF) * GR);
         if (ci)
             hipLaunchKernelGGL((rows2d_fold_kernel<V, LOGW, LOGF, true>), grid_of(blocks), block, 0, s, (const V*)in,
                                (V*)out, ngroups, log_lc, (const V*)tw);
