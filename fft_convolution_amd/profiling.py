@@ -1,9 +1,15 @@
 """Summaries of rocprofv3 output for the files under ``profiles/``.
 
-Two subcommands, both reading the CSV output of ``rocprofv3 --output-format csv``:
+Three subcommands, all reading the CSV output of ``rocprofv3 --output-format csv``:
 
 ``stats``   -- per-kernel durations from a ``--kernel-trace --stats`` run:
                python -m fft_convolution_amd.profiling stats DIR --out profiles/X.md --cmd "..."
+
+``counters`` -- the same two counters for every kernel of a run, scaled the
+               same way, as a markdown table (kernel, average duration from a
+               kernel-trace run, fetch and write MiB per dispatch, TB/s):
+               python -m fft_convolution_amd.profiling counters --fetch DIR1 --write DIR2 \
+                   --stats DIR3 --copy-bytes B --out profiles/X.md --cmd "..."
 
 ``traffic`` -- HBM bytes per launch from two ``--pmc`` runs (FETCH_SIZE, then
                WRITE_SIZE, each in KiB per dispatch) of a command that also runs
@@ -125,6 +131,46 @@ def cmd_traffic(args):
     print(json.dumps(rec, indent=1))
 
 
+def _scales(fetch, write, copy_kernel, copy_bytes):
+    _, cf = _pick(fetch, copy_kernel)
+    _, cw = _pick(write, copy_kernel)
+    return copy_bytes / (statistics.median(cf) * 1024.0), copy_bytes / (statistics.median(cw) * 1024.0)
+
+
+def _short(name: str) -> str:
+    name = name.replace("HIP_vector_type<float, 2u>", "float2").replace("HIP_vector_type<double, 2u>", "double2")
+    cut = name.find("(")
+    return (name[:cut] if cut > 0 else name).replace("|", "/")
+
+
+def cmd_counters(args):
+    fetch = counter_values(args.fetch, "FETCH_SIZE")
+    write = counter_values(args.write, "WRITE_SIZE")
+    f_fetch, f_write = _scales(fetch, write, args.copy_kernel, args.copy_bytes)
+    durations = {r["name"]: r["avg_ns"] for r in kernel_stats(args.stats)} if args.stats else {}
+    mib = 1024.0 * 1024.0
+    lines = ["# HBM traffic per kernel: %s" % args.title, "",
+             "Commands (R = repository root):", "", "```"] + list(args.cmd) + ["```", "",
+             "FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB) and scaled by the reading of a plain "
+             "elementwise copy of %d bytes each way in the same run: fetch x%.4f, write x%.4f."
+             % (args.copy_bytes, f_fetch, f_write), "",
+             "| kernel | dispatches | avg us | fetch MiB | write MiB | TB/s |", "|---|---|---|---|---|---|"]
+    for name in sorted(fetch, key=lambda k: -statistics.median(fetch[k])):
+        if args.copy_kernel in name or "copyBuffer" in name:
+            continue
+        fb = statistics.median(fetch[name]) * 1024.0 * f_fetch
+        wb = statistics.median(write.get(name, [0.0])) * 1024.0 * f_write
+        us = durations.get(name, 0.0) / 1e3
+        tbs = (fb + wb) / (us * 1e-6) / 1e12 if us else 0.0
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.2f |" % (_short(name), len(fetch[name]), us, fb / mib,
+                                                                  wb / mib, tbs))
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -134,6 +180,16 @@ def main(argv=None):
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", default="")
     s.set_defaults(fn=cmd_stats)
+    c = sub.add_parser("counters")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--stats")
+    c.add_argument("--copy-kernel", default="elementwise")
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--out")
+    c.add_argument("--cmd", nargs="*", default=[])
+    c.set_defaults(fn=cmd_counters)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
