@@ -15,8 +15,9 @@ Prints ONE JSON line with:
              from profiles/ and null once the kernel sources have changed
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows
 
-Other workloads (--workload) time the 2^24-point four-step, the 2048x2048x8
-2D transform and the 32 x 2^18 polynomial products the same way.
+Other workloads (--workload) time the 2^24-point multi-pass transform, the
+2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
+transform the same way.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
-             "polymul_l262144_b32")
+             "polymul_l262144_b32", "c2c3d_256x256x256_b1")
 
 
 def kernel_sources_digest() -> str:
@@ -105,6 +106,20 @@ def setup_workload(name, dev, fm, torch):
                     sample_rows=lambda rows: x[:rows].cpu().numpy(),
                     oracle_unit=5.0 * h * w * math.log2(h * w))
         return step, info
+    if name.startswith("c2c3d"):
+        d, h, w, batch = spec["d"], spec["h"], spec["w"], spec["batch"]
+        x = torch.from_numpy(wl.workload_input(name)).to(dev)
+        y = torch.empty_like(x)
+        plan = fm.Plan((d, h, w), torch.complex64)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step():
+            fm.fft_exec_3d(plan.handle, fm.FFT_FORWARD, x, y, batch, None, stream)
+        n = d * h * w
+        info = dict(d=d, h=h, w=w, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n),
+                    bytes=2 * x.numel() * 8, plan=plan.describe(), kernels=3, keep=(plan, x, y),
+                    sample_rows=lambda rows: x[:rows].cpu().numpy(), oracle_unit=5.0 * n * math.log2(n))
+        return step, info
     if name.startswith("polymul"):
         length, batch = spec["length"], spec["batch"]
         a_np, b_np = wl.workload_input(name)
@@ -148,11 +163,11 @@ def cpu_baseline(name, info, budget_s):
         oracle.polymul_fft(a, b, n=info["n"])
         dt = time.perf_counter() - t0
         units, sample = pairs, "first %d of %d pairs" % (pairs, total)
-    elif name.startswith("c2c2d"):
+    elif name.startswith("c2c2d") or name.startswith("c2c3d"):
         imgs = 1
         x = info["sample_rows"](imgs)
         t0 = time.perf_counter()
-        oracle.fft2(x)
+        (oracle.fft3 if name.startswith("c2c3d") else oracle.fft2)(x)
         dt = time.perf_counter() - t0
         units, sample = imgs, "first %d of %d images" % (imgs, info["batch"])
     else:
@@ -250,7 +265,7 @@ def main():
         "dtype": info["dtype"],
         "data": "synthetic",
         "config": {"workload": args.workload, "plan": info["plan"],
-                   **{k: info[k] for k in ("n", "h", "w", "batch", "length") if k in info}},
+                   **{k: info[k] for k in ("n", "d", "h", "w", "batch", "length") if k in info}},
         "hbm_tb_s": round(tbs, 3),
         "gpu": torch.cuda.get_device_name(dev),
     }

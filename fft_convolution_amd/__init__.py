@@ -10,7 +10,8 @@ call fails, the error propagates.
 Thin conveniences built on those calls:
 
 * :class:`Plan` -- owns a plan handle; ``fft``/``ifft`` (rank 1), ``fft2``/``ifft2``
-  (rank 2) and ``poly_mul`` (rank 1, complex128) on contiguous device tensors.
+  (rank 2), ``fft3``/``ifft3`` (rank 3) and ``poly_mul`` (rank 1, complex128) on
+  contiguous device tensors.
 * :func:`poly_mul` -- one-shot integer polynomial products.
 """
 from __future__ import annotations
@@ -27,7 +28,7 @@ __all__ = [
     "FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64", "FFT_MAX_N_C32", "FFT_MAX_N_C64",
     "lib", "lib_path", "EXPORTS",
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
-    "fft_exec_c2c", "fft_exec_2d", "fft_poly_mul_workspace_size", "fft_poly_mul",
+    "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
     "fft_status_string", "fft_last_error",
     "Plan", "poly_mul",
 ]
@@ -55,7 +56,7 @@ lib_path = os.path.join(_HERE, "libfftmi.so")
 # Every symbol include/fftmi.h declares.
 EXPORTS = (
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
-    "fft_exec_c2c", "fft_exec_2d", "fft_poly_mul_workspace_size", "fft_poly_mul",
+    "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
     "fft_status_string", "fft_last_error",
 )
 
@@ -92,6 +93,7 @@ def lib():
         L.fft_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_exec_c2c.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
         L.fft_exec_2d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
+        L.fft_exec_3d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
         L.fft_poly_mul_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_poly_mul.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, vp, vp]
         L.fft_status_string.argtypes = [c_int]
@@ -173,6 +175,11 @@ def fft_exec_2d(plan, dir: int, in_, out, batch: int, workspace=None, stream=Non
                              _stream(stream)), "fft_exec_2d")
 
 
+def fft_exec_3d(plan, dir: int, in_, out, batch: int, workspace=None, stream=None) -> None:
+    _check(lib().fft_exec_3d(plan, int(dir), _ptr(in_), _ptr(out), int(batch), _ptr(workspace),
+                             _stream(stream)), "fft_exec_3d")
+
+
 def fft_poly_mul_workspace_size(plan, batch: int) -> int:
     out = ctypes.c_size_t()
     _check(lib().fft_poly_mul_workspace_size(plan, int(batch), ctypes.byref(out)),
@@ -241,8 +248,8 @@ class Plan:
         else:
             self._check_tensor(out)
         ws_bytes = fft_workspace_size(self.handle, batch)
-        # A rank-2 plan uses its workspace only for an in-place call.
-        if self.rank == 2 and out.data_ptr() != x.data_ptr():
+        # A rank-2/3 plan uses its workspace only for an in-place call.
+        if self.rank >= 2 and out.data_ptr() != x.data_ptr():
             ws_bytes = 0
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
         fn(self.handle, direction, x, out, batch, ws)
@@ -267,6 +274,16 @@ class Plan:
         if self.rank != 2:
             raise ValueError("ifft2 needs a rank-2 plan")
         return self._exec(x, out, FFT_INVERSE, fft_exec_2d)
+
+    def fft3(self, x, out=None):
+        if self.rank != 3:
+            raise ValueError("fft3 needs a rank-3 plan")
+        return self._exec(x, out, FFT_FORWARD, fft_exec_3d)
+
+    def ifft3(self, x, out=None):
+        if self.rank != 3:
+            raise ValueError("ifft3 needs a rank-3 plan")
+        return self._exec(x, out, FFT_INVERSE, fft_exec_3d)
 
     def poly_mul(self, a, b, out=None, residual=False):
         """Products of the rows of int64 device tensors a [batch, la], b [batch, lb]."""

@@ -113,7 +113,7 @@ std::vector<double> stage_table(int logn, int prec)
 
 }  // namespace
 
-enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_2D = 3 };
+enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_ND = 3 };
 
 // One super-stage pass of a multi-pass plan.
 struct PassPlan {
@@ -126,7 +126,7 @@ struct PassPlan {
 
 struct fft_plan {
     int rank = 0;
-    int64_t dims[2] = {1, 1};
+    int64_t dims[3] = {1, 1, 1};
     int prec = 0;
     int device = 0;
     int path = PATH_COPY;
@@ -141,7 +141,13 @@ struct fft_plan {
     void* big_hi = nullptr;
     void* big_lo = nullptr;
     int big_lbits = 0;
-    int logf = 0;  // rank 2: log2 of the column super-stage folded into the row pass
+    // rank 2 / 3: the axes longer than 1, outer to inner (nd_k of them), and
+    // tw_a = innermost axis, tw_b = next axis (length 2^log_b after the fold),
+    // tw_c = outermost axis of three, big_* = w of the folded axis.
+    int nd_k = 0;
+    int eff_log[3] = {0, 0, 0};
+    void* tw_c = nullptr;
+    int logf = 0;  // log2 of the column super-stage folded into the row pass
     int npass = 0;
     PassPlan passes[4];
     void* pass_tw[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -186,7 +192,7 @@ int upload(const std::vector<double>& host, int prec, void** dev)
 void free_plan(fft_plan* p)
 {
     if (!p) return;
-    void* ptrs[] = {p->tw_a, p->tw_b, p->big_hi, p->big_lo};
+    void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo};
     for (void* q : ptrs)
         if (q) hipFree(q);
     for (int i = 0; i < 4; ++i) {
@@ -262,7 +268,7 @@ int check_device(const fft_plan* plan)
 // signal-sized buffer; the folded 2D transform needs one only in place.
 size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
-    const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_2D && p->logf > 0);
+    const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_ND && p->logf > 0);
     return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
 
@@ -272,6 +278,108 @@ constexpr int kMaxPassLog = 9;
 constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
 int col_pref_log(int prec) { return prec == FFT_C32 ? 10 : 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
+
+// Chooses the kernel path and its sizes; host only.
+int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
+{
+    if (rank == 1) {
+        const int64_t n = dims[0];
+        if (n == 1) {
+            p->path = PATH_COPY;
+        } else if (n <= max_lds_n(prec)) {
+            p->path = PATH_ROWS;
+            p->log_a = p->logn;
+        } else {
+            p->path = PATH_MULTIPASS;
+            // Super-stages of at most 2^9 points, as even as possible, larger first.
+            const int np = (p->logn + kMaxPassLog - 1) / kMaxPassLog;
+            int logns = 0;
+            for (int q = 0; q < np; ++q) {
+                PassPlan& pp = p->passes[q];
+                pp.logr = p->logn / np + (q < p->logn % np ? 1 : 0);
+                pp.logns = logns;
+                pp.kind = q == 0 ? 0 : (q == np - 1 ? 2 : 1);
+                logns += pp.logr;
+                const int c = tile_lines_2d(prec, pp.logr);
+                const int64_t bfly = int64_t(1) << (p->logn - pp.logr);
+                if (c <= 0 || bfly % c || (pp.kind == 1 && (int64_t(1) << pp.logns) % c))
+                    return fail(FFT_ERR_UNSUPPORTED_SIZE, "no pass layout for n = %lld", (long long)p->n);
+            }
+            p->npass = np;
+            // The poly-mul split N = N1 N2 (fp64 only): columns of at most 512
+            // (1024 beyond 2^21) points, rows of at most 4096.
+            if (prec == FFT_C64 && p->logn <= kPolyMaxLog) {
+                p->log_b = std::min(9, (p->logn + 1) / 2);  // N2, the column length
+                if (p->logn - p->log_b > 12) p->log_b = p->logn - 12;
+                p->log_a = p->logn - p->log_b;               // N1, the row length
+            }
+        }
+        return FFT_OK;
+    }
+    // Separable transform over rank 2 or 3 axes ("Stockham FFT ... in Parallel
+    // GLSL", Multi-Dimensional Transforms and Separability).  Axes of length 1
+    // drop out; the innermost remaining axis is contiguous.
+    p->path = PATH_ND;
+    for (int d = 0; d < rank; ++d)
+        if (dims[d] > 1) p->eff_log[p->nd_k++] = ilog2(dims[d]);
+    const int k = p->nd_k;
+    if (k >= 1) p->log_a = p->eff_log[k - 1];
+    if (k >= 2) {
+        const int logh = p->eff_log[k - 2];
+        if (logh > col_pref_log(prec)) {
+            // Fold the radix-F column super-stage into the row pass: the column
+            // pass then runs on H / F points.
+            int lf = logh - col_pref_log(prec);
+            while (lf > 0 && (lf > 3 || !fold_supported(prec, p->log_a, lf))) --lf;
+            p->logf = lf;
+        }
+        p->log_b = logh - p->logf;
+        if (p->log_b > col_cap_log(prec))
+            return fail(FFT_ERR_UNSUPPORTED_SIZE, "no layout for a %lld-point axis over %lld-point rows",
+                        1LL << logh, 1LL << p->log_a);
+    }
+    if (k == 3 && p->eff_log[0] > col_cap_log(prec))
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "outer axis of %lld points exceeds %lld", 1LL << p->eff_log[0],
+                    1LL << col_cap_log(prec));
+    return FFT_OK;
+}
+
+// Builds and uploads the twiddle tables the layout needs.
+int upload_tables(fft_plan* p)
+{
+    const int prec = p->prec;
+    int st = FFT_OK;
+    switch (p->path) {
+        case PATH_COPY:
+            break;
+        case PATH_ROWS:
+            st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
+            break;
+        case PATH_MULTIPASS:
+            for (int q = 0; q < p->npass && st == FFT_OK; ++q) {
+                PassPlan& pp = p->passes[q];
+                st = upload(stage_table(pp.logr, prec), prec, &p->pass_tw[q]);
+                pp.tw = p->pass_tw[q];
+                if (st == FFT_OK && q > 0) st = upload_big(pp.logns + pp.logr, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
+            }
+            if (st == FFT_OK && p->log_a > 0) {
+                st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
+                if (st == FFT_OK) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
+                if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
+            }
+            break;
+        default:
+            if (p->nd_k >= 1) st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
+            if (st == FFT_OK && p->nd_k >= 2) {
+                st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
+                if (st == FFT_OK && p->logf > 0)
+                    st = upload_big(p->log_b + p->logf, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
+            }
+            if (st == FFT_OK && p->nd_k == 3) st = upload(stage_table(p->eff_log[0], prec), prec, &p->tw_c);
+            break;
+    }
+    return st;
+}
 
 }  // namespace
 
@@ -300,7 +408,7 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
 {
     if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
     *out_plan = nullptr;
-    if (rank != 1 && rank != 2) return fail(FFT_ERR_INVALID_ARG, "rank %d not supported (1 or 2)", rank);
+    if (rank < 1 || rank > 3) return fail(FFT_ERR_INVALID_ARG, "rank %d not supported (1, 2 or 3)", rank);
     if (!dims) return fail(FFT_ERR_INVALID_ARG, "dims is NULL");
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
     for (int d = 0; d < rank; ++d) {
@@ -318,79 +426,26 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
     p->rank = rank;
     p->prec = prec;
     p->elem = elem_bytes(prec);
-    p->dims[0] = dims[0];
-    p->dims[1] = rank == 2 ? dims[1] : 1;
-    p->n = p->dims[0] * p->dims[1];
+    p->n = 1;
+    for (int d = 0; d < rank; ++d) {
+        p->dims[d] = dims[d];
+        p->n *= dims[d];
+    }
     p->logn = ilog2(p->n);
 
+    // 1. Layout, on the host only: every size check happens before any HIP call.
+    int st = plan_layout(p, rank, dims, prec);
+    if (st != FFT_OK) {
+        delete p;
+        return st;
+    }
+    // 2. Device tables.
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) {
         delete p;
         return hip_fail(e, "hipGetDevice");
     }
-
-    int st = FFT_OK;
-    if (rank == 1) {
-        const int64_t n = dims[0];
-        if (n == 1) {
-            p->path = PATH_COPY;
-        } else if (n <= max_lds_n(prec)) {
-            p->path = PATH_ROWS;
-            p->log_a = p->logn;
-            st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
-        } else {
-            p->path = PATH_MULTIPASS;
-            // Super-stages of at most 2^9 points, as even as possible, larger first.
-            const int np = (p->logn + kMaxPassLog - 1) / kMaxPassLog;
-            int logns = 0;
-            for (int q = 0; q < np && st == FFT_OK; ++q) {
-                PassPlan& pp = p->passes[q];
-                pp.logr = p->logn / np + (q < p->logn % np ? 1 : 0);
-                pp.logns = logns;
-                pp.kind = q == 0 ? 0 : (q == np - 1 ? 2 : 1);
-                logns += pp.logr;
-                st = upload(stage_table(pp.logr, prec), prec, &p->pass_tw[q]);
-                pp.tw = p->pass_tw[q];
-                if (st == FFT_OK && q > 0) st = upload_big(pp.logns + pp.logr, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
-                const int c = tile_lines_2d(prec, pp.logr);
-                const int64_t bfly = int64_t(1) << (p->logn - pp.logr);
-                if (st == FFT_OK && (c <= 0 || bfly % c || (pp.kind == 1 && (int64_t(1) << pp.logns) % c)))
-                    st = fail(FFT_ERR_UNSUPPORTED_SIZE, "no pass layout for n = %lld", (long long)p->n);
-            }
-            p->npass = np;
-            // The poly-mul split N = N1 N2 (fp64 only): columns of at most 512
-            // (1024 beyond 2^21) points, rows of at most 4096.
-            if (st == FFT_OK && prec == FFT_C64 && p->logn <= kPolyMaxLog) {
-                p->log_b = std::min(9, (p->logn + 1) / 2);  // N2, the column length
-                if (p->logn - p->log_b > 12) p->log_b = p->logn - 12;
-                p->log_a = p->logn - p->log_b;               // N1, the row length
-                st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
-                if (st == FFT_OK) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
-                if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
-            }
-        }
-    } else {
-        p->path = PATH_2D;
-        p->log_a = ilog2(p->dims[1]);  // W
-        const int logh = ilog2(p->dims[0]);
-        p->logf = 0;
-        if (p->log_a > 0 && logh > col_pref_log(prec)) {
-            // Fold the radix-F column super-stage into the row pass: the
-            // column pass then runs on H / F points.
-            int lf = logh - col_pref_log(prec);
-            while (lf > 0 && (lf > 3 || !fold_supported(prec, p->log_a, lf))) --lf;
-            if (logh - lf > col_cap_log(prec)) {
-                free_plan(p);
-                return fail(FFT_ERR_UNSUPPORTED_SIZE, "no 2D layout for H = %lld, W = %lld", (long long)dims[0],
-                            (long long)dims[1]);
-            }
-            p->logf = lf;
-        }
-        p->log_b = logh - p->logf;  // Lc, the column pass length
-        if (p->log_a > 0) st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
-        if (st == FFT_OK && p->log_b > 0) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
-        if (st == FFT_OK && p->logf > 0) st = upload_big(logh, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
-    }
+    st = upload_tables(p);
     if (st != FFT_OK) {
         free_plan(p);
         return st;
@@ -424,9 +479,10 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             break;
         }
         default:
-            snprintf(buf, len, "rank=2 h=%lld w=%lld prec=%s path=2d fold=%d col_len=%lld cols_per_wg=%d",
-                     (long long)p->dims[0], (long long)p->dims[1], prec, 1 << p->logf, 1LL << p->log_b,
-                     p->log_b > 0 ? tile_lines_2d(p->prec, p->log_b) : 0);
+            snprintf(buf, len, "rank=%d dims=%lldx%lldx%lld prec=%s path=nd axes=%d fold=%d col_len=%lld",
+                     p->rank, (long long)p->dims[0], (long long)(p->rank > 1 ? p->dims[1] : 1),
+                     (long long)(p->rank > 2 ? p->dims[2] : 1), prec, p->nd_k, 1 << p->logf,
+                     p->nd_k >= 2 ? 1LL << p->log_b : 0LL);
             break;
     }
     return FFT_OK;
@@ -485,46 +541,69 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
     return FFT_OK;
 }
 
-int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
-                void* stream)
+static int exec_nd(const fft_plan* plan, int rank, const char* what, int dir, const void* in, void* out,
+                   int64_t batch, void* workspace, void* stream)
 {
     bool noop = false;
     const size_t ws = plan && batch > 0 && in == out ? c2c_workspace(plan, batch) : 0;
-    int st = check_exec(plan, dir, 2, in, out, batch, workspace, ws, &noop);
+    int st = check_exec(plan, dir, rank, in, out, batch, workspace, ws, &noop);
     if (st != FFT_OK || noop) return st;
     if ((st = check_device(plan)) != FFT_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
     const bool inv = dir == FFT_INVERSE;
     const double scale = 1.0 / (double)plan->n;
-    const int64_t h = plan->dims[0], w = plan->dims[1];
+    const int k = plan->nd_k;
+    const BigTwiddle none{nullptr, nullptr, 0, 0};
     hipError_t e = hipSuccess;
-    if (h == 1 && w == 1) {
+    if (k == 0) {
         if (in != out) e = hipMemcpyAsync(out, in, (size_t)batch * plan->elem, hipMemcpyDeviceToDevice, s);
-    } else if (h == 1) {
+    } else if (k == 1) {
         e = launch_rows(plan->prec, plan->log_a, inv, inv, in, out, batch, plan->tw_a, scale, s);
-    } else if (w == 1) {
-        // the columns are contiguous
-        e = launch_rows(plan->prec, plan->log_b, inv, inv, in, out, batch, plan->tw_b, scale, s);
-    } else if (plan->logf == 0) {
-        const BigTwiddle none{nullptr, nullptr, 0, 0};
-        e = launch_rows(plan->prec, plan->log_a, inv, false, in, out, batch * h, plan->tw_a, 1.0, s);
-        if (e == hipSuccess)
-            e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, w, 0, plan->tw_b, none, inv, scale, s);
     } else {
-        // rows + radix-F column super-stage -> mid, then the column pass mid -> out
-        void* mid = in == out ? workspace : out;
-        const BigTwiddle hb{plan->big_hi, plan->big_lo, plan->big_lbits, plan->log_b + plan->logf};
-        e = launch_rows2d_fold(plan->prec, plan->log_a, plan->logf, in, mid, batch, plan->log_b, plan->tw_a, inv, s);
-        if (e == hipSuccess)
-            e = launch_cols2d(plan->prec, plan->log_b, mid, out, batch, w, plan->logf, plan->tw_b, hb, inv, scale, s);
+        // innermost axis (rows) + next axis (columns of stride W); the first
+        // pass conjugates the input, the last conjugates and scales the output.
+        const int64_t w = int64_t(1) << plan->log_a;
+        const int logh = plan->log_b + plan->logf;
+        const int64_t nimg = batch * (plan->n >> (plan->log_a + logh));
+        const bool last2 = k == 2;
+        if (plan->logf == 0) {
+            e = launch_rows(plan->prec, plan->log_a, inv, false, in, out, nimg << logh, plan->tw_a, 1.0, s);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, out, out, nimg, w, 0, plan->tw_b, none, inv && last2,
+                                  last2 ? scale : 1.0, s);
+        } else {
+            void* mid = in == out ? workspace : out;
+            const BigTwiddle hb{plan->big_hi, plan->big_lo, plan->big_lbits, logh};
+            e = launch_rows2d_fold(plan->prec, plan->log_a, plan->logf, in, mid, nimg, plan->log_b, plan->tw_a, inv,
+                                   s);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, mid, out, nimg, w, plan->logf, plan->tw_b, hb,
+                                  inv && last2, last2 ? scale : 1.0, s);
+        }
+        // outer axis of three: columns of stride H W, in place
+        if (e == hipSuccess && k == 3)
+            e = launch_cols2d(plan->prec, plan->eff_log[0], out, out, batch, w << logh, 0, plan->tw_c, none, inv,
+                              scale, s);
     }
-    if (e != hipSuccess) return hip_fail(e, "fft_exec_2d launch");
+    if (e != hipSuccess) return hip_fail(e, what);
     if (getenv("FFTMI_SYNC")) {
         e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return hip_fail(e, "fft_exec_2d (FFTMI_SYNC)");
+        if (e != hipSuccess) return hip_fail(e, what);
     }
     return FFT_OK;
+}
+
+int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
+                void* stream)
+{
+    return exec_nd(plan, 2, "fft_exec_2d", dir, in, out, batch, workspace, stream);
+}
+
+int fft_exec_3d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
+                void* stream)
+{
+    return exec_nd(plan, 3, "fft_exec_3d", dir, in, out, batch, workspace, stream);
 }
 
 int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)

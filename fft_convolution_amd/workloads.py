@@ -18,6 +18,7 @@ stated):
   noise of std 0.01 on re and im.  2048 x 2048 x 8 images (seed 4).
 * ``random_polys`` -- pairs of integer polynomials with coefficients i.i.d.
   uniform in [0, 1000).  32 pairs of 2^18 coefficients (seed 5).
+* a 256^3 volume, re and im uniform [-1, 1) (seed 6), for the 3D transform.
 """
 from __future__ import annotations
 
@@ -30,6 +31,8 @@ WORKLOADS = {
     "c2c_n16777216_b1": dict(kind="uniform", n=1 << 24, batch=1, seed=3),
     "c2c2d_2048x2048_b8": dict(kind="plane_waves", h=2048, w=2048, batch=8, seed=4),
     "polymul_l262144_b32": dict(kind="polys", length=1 << 18, batch=32, seed=5),
+    # 3D separable transform (beyond the five workloads above): one 256^3 volume.
+    "c2c3d_256x256x256_b1": dict(kind="uniform3d", d=256, h=256, w=256, batch=1, seed=6),
 }
 
 
@@ -130,4 +133,7 @@ def workload_input(name: str, **overrides):
         return plane_waves_2d(spec["h"], spec["w"], spec["batch"], spec["seed"])
     if kind == "polys":
         return random_polys(spec["length"], spec["batch"], spec["seed"])
+    if kind == "uniform3d":
+        d, h, w = spec["d"], spec["h"], spec["w"]
+        return batched_uniform(d * h * w, spec["batch"], spec["seed"]).reshape(spec["batch"], d, h, w)
     raise KeyError(kind)

@@ -59,7 +59,7 @@ enum fft_status {
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
-    FFT_ERR_RANK = -5,             /* exec_c2c on a rank-2 plan, exec_2d on a rank-1 plan */
+    FFT_ERR_RANK = -5,             /* plan rank differs from the call (exec_c2c: 1, exec_2d: 2, exec_3d: 3) */
     FFT_ERR_ALIGN = -6,            /* a pointer is not aligned to its element size */
     FFT_ERR_OVERLAP = -7,          /* buffers partially overlap (in == out is allowed) */
     FFT_ERR_WORKSPACE = -8,        /* workspace required but NULL, or overlapping data */
@@ -85,6 +85,11 @@ enum fft_status {
  *           except very tall, narrow shapes whose column transform cannot be
  *           split between the two passes (e.g. H = 8192 with W = 2, FFT_C32),
  *           which give FFT_ERR_UNSUPPORTED_SIZE.
+ *   rank 3: dims = {D, H, W}, row-major: the 2D transform of every [H][W]
+ *           slice, then the D-point transform along the depth axis of every
+ *           (y, x) (the same separability, one axis after another); each
+ *           dimension as for rank 2, and the depth D <= 2048 (C32) / 1024 (C64)
+ *           unless H = W = 1.
  *   prec:   FFT_C32 or FFT_C64.
  * Builds the twiddle tables in fp64 on the host, rounds them to the plan
  * precision and uploads them (the only synchronous device work of the
@@ -128,6 +133,15 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
  * Errors: as fft_exec_c2c.
  */
 int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
+                void* workspace, void* stream);
+
+/*
+ * Batched 3D transform with a rank-3 plan.
+ *   in, out:   [batch][D][H][W] complex, volumes contiguous.  in == out allowed.
+ *   workspace: as fft_exec_2d (needed only in place when the plan folds).
+ * Errors: as fft_exec_c2c.
+ */
+int fft_exec_3d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
                 void* workspace, void* stream);
 
 /* Bytes of device workspace fft_poly_mul needs for `batch` pairs. */

@@ -15,7 +15,8 @@ What it computes, and the passage each part follows:
   inverse swaps w for w^{-1} and scales by 1/N (same page, the section on why
   roots of unity are used as evaluation points).
 * ``fft2`` / ``ifft2`` -- rows then columns ("Stockham FFT Butterfly Algorithm in
-  Parallel GLSL", section "Multi-Dimensional Transforms and Separability").
+  Parallel GLSL", section "Multi-Dimensional Transforms and Separability");
+  ``fft3`` / ``ifft3`` -- the same, one axis after another, for 3D data.
 * ``polymul_fft`` -- forward both zero-padded operands, pointwise product,
   inverse, rint ("FFT on GPU", polynomial-multiplication and whole-process
   sections); ``schoolbook`` / ``schoolbook_sample`` -- the exact convolution
@@ -50,7 +51,7 @@ _lib = None
 
 __all__ = [
     "build", "load", "set_threads", "get_threads",
-    "dft", "fft", "ifft", "fft2", "ifft2",
+    "dft", "fft", "ifft", "fft2", "ifft2", "fft3", "ifft3",
     "polymul_fft", "schoolbook", "schoolbook_sample",
     "dft_py", "bitrev_order", "butterfly_pass_half", "stockham_pass",
     "poly_eval_mod", "MOD_P",
@@ -84,6 +85,7 @@ def load():
         lib.oracle_dft_direct.argtypes = [dbl_p, dbl_p, i64, i64, c_int]
         lib.oracle_fft.argtypes = [dbl_p, dbl_p, i64, i64, c_int]
         lib.oracle_fft2.argtypes = [dbl_p, dbl_p, i64, i64, i64, c_int]
+        lib.oracle_fft3.argtypes = [dbl_p, dbl_p, i64, i64, i64, i64, c_int]
         lib.oracle_schoolbook.argtypes = [i64_p, i64, i64_p, i64, i64_p, i64]
         lib.oracle_schoolbook_sample.argtypes = [i64_p, i64, i64_p, i64, i64, i64_p, i64, i64_p]
         lib.oracle_schoolbook_coeff.argtypes = [i64_p, i64, i64_p, i64, i64]
@@ -92,7 +94,7 @@ def load():
                                            ctypes.POINTER(ctypes.c_double)]
         lib.oracle_set_threads.argtypes = [c_int]
         lib.oracle_get_threads.restype = c_int
-        for name in ("oracle_dft_direct", "oracle_fft", "oracle_fft2",
+        for name in ("oracle_dft_direct", "oracle_fft", "oracle_fft2", "oracle_fft3",
                      "oracle_schoolbook", "oracle_schoolbook_sample",
                      "oracle_polymul_fft", "oracle_set_threads"):
             if name != "oracle_set_threads":
@@ -160,6 +162,20 @@ def fft2(x, inverse: bool = False) -> np.ndarray:
 
 def ifft2(X) -> np.ndarray:
     return fft2(X, inverse=True)
+
+
+def fft3(x, inverse: bool = False) -> np.ndarray:
+    """Separable 3D transform over the last three axes ([..., D, H, W])."""
+    x = _as_c128(x)
+    d, h, w = x.shape[-3], x.shape[-2], x.shape[-1]
+    out = np.empty_like(x)
+    batch = x.size // (d * h * w) if d * h * w else 0
+    _check(load().oracle_fft3(_ptr(x), _ptr(out), d, h, w, batch, int(inverse)), "fft3")
+    return out
+
+
+def ifft3(X) -> np.ndarray:
+    return fft3(X, inverse=True)
 
 
 def _as_i64(a) -> np.ndarray:

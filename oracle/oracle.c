@@ -18,7 +18,7 @@
  *                                                                  oracle_schoolbook_*
  *   - "Stockham FFT Butterfly Algorithm in Parallel GLSL", section
  *     "Multi-Dimensional Transforms and Separability": rows, then columns
- *                                                               -> oracle_fft2
+ *     (2D), and one axis after another for 3D data       -> oracle_fft2, oracle_fft3
  *
  * The ORACLE_PLANT_* macros exist only so that a test can build a throw-away
  * copy with one plausible mistake planted and check that the pins catch it;
@@ -227,6 +227,47 @@ int oracle_fft2(const double* x, double* X, int64_t h, int64_t w, int64_t batch,
     }
     free(twr);
     free(twc);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Separable 3D transform: the same separability ("Stockham FFT ... in      */
+/* Parallel GLSL" names 2D and 3D data), one axis after another: the 2D      */
+/* transform of every depth slice [h][w], then the 1D transform along the    */
+/* depth axis of every (y, x).  x is [batch][d][h][w]; the inverse scales by  */
+/* 1/(d h w) (1/d here, 1/(h w) inside the 2D step).                          */
+/* ------------------------------------------------------------------------ */
+int oracle_fft3(const double* x, double* X, int64_t d, int64_t h, int64_t w, int64_t batch, int inverse)
+{
+    if (!is_pow2(d) || !is_pow2(h) || !is_pow2(w) || batch < 0 || !x || !X || x == X) return -1;
+    int rc = oracle_fft2(x, X, h, w, batch * d, inverse);
+    if (rc) return rc;
+    double* twd = make_roots(d, inverse);
+    if (!twd) return -2;
+    const int64_t plane = h * w;
+    for (int64_t b = 0; b < batch; ++b) {
+        double* Xi = X + 2 * d * plane * b;
+#pragma omp parallel
+        {
+            double* col = (double*)malloc(sizeof(double) * 2 * d);
+            double* res = (double*)malloc(sizeof(double) * 2 * d);
+#pragma omp for schedule(static)
+            for (int64_t p = 0; p < plane; ++p) {
+                for (int64_t z = 0; z < d; ++z) {
+                    col[2 * z] = Xi[2 * (z * plane + p)];
+                    col[2 * z + 1] = Xi[2 * (z * plane + p) + 1];
+                }
+                fft_one(col, res, d, twd, inverse, 0);
+                for (int64_t z = 0; z < d; ++z) {
+                    Xi[2 * (z * plane + p)] = res[2 * z];
+                    Xi[2 * (z * plane + p) + 1] = res[2 * z + 1];
+                }
+            }
+            free(col);
+            free(res);
+        }
+    }
+    free(twd);
     return 0;
 }
 

@@ -66,7 +66,7 @@ def _create_status(rank, dims, prec):
 
 @pytest.mark.parametrize("rank,dims,prec,status", [
     (0, [8], 0, fm.FFT_ERR_INVALID_ARG),
-    (3, [8, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
+    (4, [8, 8, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
     (1, None, 0, fm.FFT_ERR_INVALID_ARG),
     (1, [8], 2, fm.FFT_ERR_INVALID_ARG),
     (1, [0], 0, fm.FFT_ERR_INVALID_ARG),
@@ -78,6 +78,12 @@ def _create_status(rank, dims, prec):
     (1, [1 << 25], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [8192, 2], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # column axis cannot be split over 2-point rows
+    (3, [8, 6, 8], 0, fm.FFT_ERR_NOT_POW2),
+    (3, [0, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
+    (3, [4096, 8, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # depth beyond the column-pass range
+    (3, [2048, 8, 8], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (3, [8, 8, 16384], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
 ])
 def test_plan_create_rejects(rank, dims, prec, status):
     st, h = _create_status(rank, dims, prec)
@@ -93,7 +99,8 @@ def test_plan_create_null_out_pointer():
 
 @pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
 def test_valid_plan_without_gpu_is_a_device_error():
-    for rank, dims, prec in ((1, [1024], 0), (1, [1 << 24], 0), (2, [64, 32], 1), (1, [1], 0)):
+    for rank, dims, prec in ((1, [1024], 0), (1, [1 << 24], 0), (2, [64, 32], 1), (1, [1], 0),
+                             (3, [16, 8, 32], 0), (3, [4096, 1, 1], 0), (2, [8192, 8], 0)):
         st, h = _create_status(rank, dims, prec)
         assert st == fm.FFT_ERR_DEVICE and h is None
         assert "hipGetDevice" in fm.fft_last_error()
@@ -103,6 +110,7 @@ def test_exec_and_queries_with_null_plan():
     L = fm.lib()
     assert L.fft_exec_c2c(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_exec_2d(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_exec_3d(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_poly_mul(None, None, 1, None, 1, None, 1, None, None, None) == fm.FFT_ERR_INVALID_ARG
     sz = ctypes.c_size_t()
     assert L.fft_workspace_size(None, 1, ctypes.byref(sz)) == fm.FFT_ERR_INVALID_ARG

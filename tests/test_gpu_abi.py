@@ -44,4 +44,8 @@ def test_exec_validation(dev):
     assert _status(fm.fft_exec_c2c, pbig.handle, 0, xb, yb, 2, ws) == fm.FFT_OK
     torch.cuda.synchronize()
     assert "path=rows" in p1.describe() and "path=multipass" in pbig.describe()
-    assert "path=2d" in p2.describe()
+    assert "path=nd" in p2.describe()
+    p3 = fm.Plan((4, 8, 16), torch.complex64)
+    assert _status(fm.fft_exec_3d, p2.handle, 0, x, y, 1) == fm.FFT_ERR_RANK
+    assert _status(fm.fft_exec_2d, p3.handle, 0, x, y, 1) == fm.FFT_ERR_RANK
+    assert _status(fm.fft_exec_3d, p3.handle, 0, x, y, 2) == fm.FFT_OK

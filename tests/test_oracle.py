@@ -324,6 +324,27 @@ def test_fft2_plane_waves_closed_form():
         assert top == set((fy[b] * w + fx[b]).tolist())
 
 
+def test_fft3_matches_numpy_separability_and_closed_form():
+    rng = np.random.default_rng(13)
+    for d, h, w in ((1, 4, 8), (4, 1, 8), (8, 4, 1), (2, 2, 2), (8, 16, 4), (16, 8, 32)):
+        x = crand(rng, 2, d, h, w)
+        assert rel_rms(oracle.fft3(x), np.fft.fftn(x, axes=(1, 2, 3))) < 1e-14
+        assert rel_rms(oracle.ifft3(oracle.fft3(x)), x) < 1e-14
+    # outer product of three 1D signals -> outer product of their spectra
+    a, b, c = crand(rng, 8), crand(rng, 4), crand(rng, 16)
+    x = a[:, None, None] * b[None, :, None] * c[None, None, :]
+    ref = (np.fft.fft(a)[:, None, None] * np.fft.fft(b)[None, :, None] * np.fft.fft(c)[None, None, :])
+    assert rel_rms(oracle.fft3(x), ref) < 1e-14
+    # a 3D plane wave e^{2 pi i (fz z/D + fy y/H + fx x/W)} -> D H W at (fz, fy, fx)
+    d, h, w = 8, 16, 4
+    z, y, xx = np.meshgrid(np.arange(d), np.arange(h), np.arange(w), indexing="ij")
+    wave = np.exp(2j * np.pi * (((3 * z) % d) / d + ((5 * y) % h) / h + ((1 * xx) % w) / w))
+    X = oracle.fft3(wave)
+    ref = np.zeros((d, h, w), complex)
+    ref[3, 5, 1] = d * h * w
+    assert np.max(np.abs(X - ref)) < 1e-10 * d * h * w
+
+
 # --------------------------------------------------------------------------
 # Polynomial multiplication
 # --------------------------------------------------------------------------
