@@ -25,7 +25,7 @@ __all__ = [
     "FFT_OK", "FFT_ERR_INVALID_ARG", "FFT_ERR_NOT_POW2", "FFT_ERR_UNSUPPORTED_SIZE",
     "FFT_ERR_PRECISION", "FFT_ERR_RANK", "FFT_ERR_ALIGN", "FFT_ERR_OVERLAP",
     "FFT_ERR_WORKSPACE", "FFT_ERR_DEVICE",
-    "FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64", "FFT_MAX_N_C32", "FFT_MAX_N_C64",
+    "FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64", "FFT_MAX_N_C32", "FFT_MAX_N_C64", "FFT_MAX_BLUESTEIN_N",
     "lib", "lib_path", "EXPORTS",
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
@@ -49,6 +49,7 @@ FFT_MAX_LDS_N_C32 = 8192
 FFT_MAX_LDS_N_C64 = 4096
 FFT_MAX_N_C32 = 1 << 26
 FFT_MAX_N_C64 = 1 << 24
+FFT_MAX_BLUESTEIN_N = 1 << 23
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfftmi.so")

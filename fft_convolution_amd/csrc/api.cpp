@@ -113,7 +113,7 @@ std::vector<double> stage_table(int logn, int prec)
 
 }  // namespace
 
-enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_ND = 3 };
+enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_ND = 3, PATH_BLUESTEIN = 4 };
 
 // One super-stage pass of a multi-pass plan.
 struct PassPlan {
@@ -148,6 +148,12 @@ struct fft_plan {
     int eff_log[3] = {0, 0, 0};
     void* tw_c = nullptr;
     int logf = 0;  // log2 of the column super-stage folded into the row pass
+    // rank 1, any N (Bluestein): chirp c_j (N entries), B = F_M(b) (M entries),
+    // the power-of-two plan of length M = 2^logm it runs on.
+    int logm = 0;
+    void* chirp = nullptr;
+    void* bspec = nullptr;
+    fft_plan* inner = nullptr;
     int npass = 0;
     PassPlan passes[4];
     void* pass_tw[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -192,7 +198,7 @@ int upload(const std::vector<double>& host, int prec, void** dev)
 void free_plan(fft_plan* p)
 {
     if (!p) return;
-    void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo};
+    void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo, p->chirp, p->bspec};
     for (void* q : ptrs)
         if (q) hipFree(q);
     for (int i = 0; i < 4; ++i) {
@@ -200,6 +206,7 @@ void free_plan(fft_plan* p)
         if (p->passes[i].big_hi) hipFree(p->passes[i].big_hi);
         if (p->passes[i].big_lo) hipFree(p->passes[i].big_lo);
     }
+    if (p->inner) free_plan(p->inner);
     delete p;
 }
 
@@ -268,6 +275,8 @@ int check_device(const fft_plan* plan)
 // signal-sized buffer; the folded 2D transform needs one only in place.
 size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
+    if (p->path == PATH_BLUESTEIN)
+        return ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
     const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_ND && p->logf > 0);
     return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
@@ -276,6 +285,7 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
 // length of the 2D column pass (LDS: lines of 128 bytes x length must fit).
 constexpr int kMaxPassLog = 9;
 constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
+constexpr int64_t kBluesteinMax = FFT_MAX_BLUESTEIN_N;  // largest length that is not a power of two
 int col_pref_log(int prec) { return prec == FFT_C32 ? 10 : 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
 
@@ -284,7 +294,10 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
 {
     if (rank == 1) {
         const int64_t n = dims[0];
-        if (n == 1) {
+        if (!is_pow2(n)) {
+            p->path = PATH_BLUESTEIN;
+            while ((int64_t(1) << p->logm) < 2 * n - 1) ++p->logm;
+        } else if (n == 1) {
             p->path = PATH_COPY;
         } else if (n <= max_lds_n(prec)) {
             p->path = PATH_ROWS;
@@ -344,6 +357,85 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
     return FFT_OK;
 }
 
+// c_j = e^{-i pi j^2 / N} in fp64: j^2 is reduced mod 2N in integers and the
+// angle folded into [0, pi/2] before libm is called.
+void chirp_value(int64_t j, int64_t n, double* re, double* im)
+{
+    int64_t q = (int64_t)(((unsigned __int128)j * (unsigned __int128)j) % (unsigned __int128)(2 * n));
+    double sign = 1.0;
+    if (q >= n) {  // e^{-i pi (q - n)/N} e^{-i pi}
+        q -= n;
+        sign = -1.0;
+    }
+    double c, sn;  // cos, sin of pi q / N, q in [0, N)
+    if (2 * q <= n) {
+        const double th = M_PI * ((double)q / (double)n);
+        c = std::cos(th);
+        sn = std::sin(th);
+    } else {
+        const double th = M_PI * ((double)(n - q) / (double)n);
+        c = -std::cos(th);
+        sn = std::sin(th);
+    }
+    *re = sign * c;
+    *im = -sign * sn;
+}
+
+// Bluestein tables: the chirp, and B = F_M(b) computed on the device with an
+// fp64 power-of-two plan, rounded to the plan precision; plus the plan of
+// length M the transforms run on.
+int bluestein_tables(fft_plan* p)
+{
+    const int64_t n = p->n, m = int64_t(1) << p->logm;
+    std::vector<double> c(2 * n), b(2 * m, 0.0);
+    for (int64_t j = 0; j < n; ++j) chirp_value(j, n, &c[2 * j], &c[2 * j + 1]);
+    for (int64_t j = 0; j < n; ++j) {
+        b[2 * j] = c[2 * j];
+        b[2 * j + 1] = -c[2 * j + 1];
+        if (j > 0) {
+            b[2 * (m - j)] = c[2 * j];
+            b[2 * (m - j) + 1] = -c[2 * j + 1];
+        }
+    }
+    int st = upload(c, p->prec, &p->chirp);
+    if (st != FFT_OK) return st;
+    void* bdev = nullptr;
+    st = upload(b, FFT_C64, &bdev);
+    if (st != FFT_OK) return st;
+    fft_plan* sub = nullptr;
+    const int64_t mdim = m;
+    st = fft_plan_create(&sub, 1, &mdim, FFT_C64);
+    void* ws = nullptr;
+    const size_t wsb = st == FFT_OK ? c2c_workspace(sub, 1) : 0;
+    if (st == FFT_OK && wsb) {
+        hipError_t e = hipMalloc(&ws, wsb);
+        if (e != hipSuccess) st = hip_fail(e, "hipMalloc(plan workspace)");
+    }
+    if (st == FFT_OK) st = fft_exec_c2c(sub, FFT_FORWARD, bdev, bdev, 1, ws, nullptr);
+    if (st == FFT_OK) {
+        if (p->prec == FFT_C32) {
+            hipError_t e = hipMalloc(&p->bspec, (size_t)m * 8);
+            if (e != hipSuccess) st = hip_fail(e, "hipMalloc(bluestein table)");
+            if (st == FFT_OK) {
+                e = launch_narrow(bdev, p->bspec, m, nullptr);
+                if (e != hipSuccess) st = hip_fail(e, "narrow");
+            }
+        } else {
+            p->bspec = bdev;
+            bdev = nullptr;
+        }
+    }
+    if (st == FFT_OK) {
+        hipError_t e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize(plan)");
+    }
+    if (ws) hipFree(ws);
+    if (bdev) hipFree(bdev);
+    if (sub) fft_plan_destroy(sub);
+    if (st == FFT_OK) st = fft_plan_create(&p->inner, 1, &mdim, p->prec);
+    return st;
+}
+
 // Builds and uploads the twiddle tables the layout needs.
 int upload_tables(fft_plan* p)
 {
@@ -351,6 +443,9 @@ int upload_tables(fft_plan* p)
     int st = FFT_OK;
     switch (p->path) {
         case PATH_COPY:
+            break;
+        case PATH_BLUESTEIN:
+            st = bluestein_tables(p);
             break;
         case PATH_ROWS:
             st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
@@ -413,8 +508,14 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
     for (int d = 0; d < rank; ++d) {
         if (dims[d] < 1) return fail(FFT_ERR_INVALID_ARG, "dims[%d] = %lld < 1", d, (long long)dims[d]);
-        if (!is_pow2(dims[d]))
-            return fail(FFT_ERR_NOT_POW2, "dims[%d] = %lld is not a power of two", d, (long long)dims[d]);
+        if (!is_pow2(dims[d])) {
+            if (rank > 1)
+                return fail(FFT_ERR_NOT_POW2, "dims[%d] = %lld is not a power of two", d, (long long)dims[d]);
+            if (dims[d] > kBluesteinMax)
+                return fail(FFT_ERR_UNSUPPORTED_SIZE, "length %lld (not a power of two) exceeds %lld",
+                            (long long)dims[d], (long long)kBluesteinMax);
+            continue;
+        }
         const int64_t lim = rank == 1 ? max_n(prec) : max_lds_n(prec);
         if (dims[d] > lim)
             return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", d, (long long)dims[d],
@@ -472,6 +573,10 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             snprintf(buf, len, "rank=1 n=%lld prec=%s path=rows stages=%d", (long long)p->n, prec,
                      plan_nstages(p->log_a, plan_lem(p->prec)));
             break;
+        case PATH_BLUESTEIN:
+            snprintf(buf, len, "rank=1 n=%lld prec=%s path=bluestein m=%lld", (long long)p->n, prec,
+                     1LL << p->logm);
+            break;
         case PATH_MULTIPASS: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
             for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
@@ -528,6 +633,21 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
                                       inv && q == 0, inv && q == plan->npass - 1, scale, s);
                 src = dst;
             }
+            break;
+        }
+        case PATH_BLUESTEIN: {
+            // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
+            void* w = workspace;
+            void* inner_ws = (char*)workspace + ((size_t)batch << plan->logm) * plan->elem;
+            e = launch_chirp_pre(plan->prec, in, w, plan->n, plan->logm, batch, plan->chirp, inv, s);
+            if (e != hipSuccess) break;
+            st = fft_exec_c2c(plan->inner, FFT_FORWARD, w, w, batch, inner_ws, stream);
+            if (st != FFT_OK) return st;
+            e = launch_cmul_table(plan->prec, w, plan->logm, batch, plan->bspec, s);
+            if (e != hipSuccess) break;
+            st = fft_exec_c2c(plan->inner, FFT_INVERSE, w, w, batch, inner_ws, stream);
+            if (st != FFT_OK) return st;
+            e = launch_chirp_post(plan->prec, w, out, plan->n, plan->logm, batch, plan->chirp, inv, scale, s);
             break;
         }
         default:
@@ -613,6 +733,7 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
+    if (plan->path == PATH_BLUESTEIN) return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
     if (plan->logn > kPolyMaxLog) return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
     *bytes = plan->path == PATH_MULTIPASS ? (size_t)batch * (size_t)plan->n * plan->elem : 0;
     return FFT_OK;
@@ -626,6 +747,8 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
     if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
+    if (plan->path == PATH_BLUESTEIN)
+        return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
     if (plan->logn > kPolyMaxLog)
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
     if (la > plan->n || lb > plan->n || la + lb - 1 > plan->n)

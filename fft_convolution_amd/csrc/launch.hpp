@@ -66,6 +66,15 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
                                    void* ws, const void* tw_row, const void* tw_col, BigTwiddle big,
                                    double* d_resid, hipStream_t stream);
 
+// Bluestein element-wise steps (bluestein.hip): rows of n points padded to 2^logm.
+hipError_t launch_chirp_pre(int prec, const void* in, void* w, int64_t n, int logm, int64_t batch, const void* chirp,
+                            bool conj_in, hipStream_t stream);
+hipError_t launch_cmul_table(int prec, void* w, int logm, int64_t batch, const void* tab, hipStream_t stream);
+hipError_t launch_chirp_post(int prec, const void* w, void* out, int64_t n, int logm, int64_t batch,
+                             const void* chirp, bool conj_out, double scale, hipStream_t stream);
+// complex128 -> complex64, `total` elements.
+hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t stream);
+
 // d_resid[0] = 0 (a kernel, not a memset, so the call is safe to capture).
 hipError_t launch_zero_resid(double* d_resid, hipStream_t stream);
 

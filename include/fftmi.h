@@ -55,7 +55,8 @@ enum fft_direction { FFT_FORWARD = 0, FFT_INVERSE = 1 };
 enum fft_status {
     FFT_OK = 0,
     FFT_ERR_INVALID_ARG = -1,      /* NULL pointer, batch < 0, bad rank/dir/prec value */
-    FFT_ERR_NOT_POW2 = -2,         /* a dimension is not a power of two */
+    FFT_ERR_NOT_POW2 = -2,         /* a dimension of a rank-2/3 plan, or the length of a
+                                      poly-mul plan, is not a power of two */
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
@@ -71,6 +72,7 @@ enum fft_status {
 #define FFT_MAX_LDS_N_C64 4096
 #define FFT_MAX_N_C32 (1LL << 26)     /* multi-pass beyond the LDS-resident range */
 #define FFT_MAX_N_C64 (1LL << 24)
+#define FFT_MAX_BLUESTEIN_N (1LL << 23) /* rank-1 lengths that are not powers of two */
 
 /*
  * Create a plan.
@@ -79,6 +81,14 @@ enum fft_status {
  *           rows; larger N runs as two or three Stockham super-stage passes
  *           (radix <= 512 each) through HBM and needs a workspace of one
  *           batch of signals.
+ *           N not a power of two (N <= FFT_MAX_BLUESTEIN_N): the chirp-z
+ *           (Bluestein) route that "FFT on GPU" (section "Algorithm per
+ *           signal Length") names for such lengths: X_k = c_k (x.c * conj c)_k
+ *           with c_j = e^{-i pi j^2/N}, the convolution done cyclically at the
+ *           power-of-two M >= 2N - 1 by the library's own transforms.  Plan
+ *           creation then also runs one fp64 M-point transform on the device
+ *           (the spectrum of the chirp), and execution needs a workspace of
+ *           batch * M elements plus that of the M-point plan.
  *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
  *           Parallel GLSL", section "Multi-Dimensional Transforms and
  *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*,
@@ -94,7 +104,7 @@ enum fft_status {
  * Builds the twiddle tables in fp64 on the host, rounds them to the plan
  * precision and uploads them (the only synchronous device work of the
  * library).  On success *plan receives the new plan; on failure *plan is set
- * to NULL.  Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE, DEVICE.
+ * to NULL.  Errors: INVALID_ARG, NOT_POW2 (rank 2/3), UNSUPPORTED_SIZE, DEVICE.
  */
 int fft_plan_create(fft_plan** plan, int rank, const int64_t* dims, int prec);
 
@@ -154,7 +164,8 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
  * computed as: zero-pad a and b to N, forward FFT of both (fp64), pointwise
  * product, inverse FFT (scaled 1/N), round the real part to the nearest
  * integer (ties to even).
- *   plan:  rank 1, FFT_C64, with N >= la + lb - 1.
+ *   plan:  rank 1, FFT_C64, N a power of two (else FFT_ERR_NOT_POW2) with
+ *          N >= la + lb - 1.
  *   a:     [batch][la] int64;  b: [batch][lb] int64;  c: [batch][la+lb-1] int64.
  *          c must not overlap a, b or the workspace.
  *   workspace: fft_poly_mul_workspace_size(plan, batch) bytes.
@@ -162,8 +173,8 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
  *          max |Re(y)/N - rint(Re(y)/N)| over all outputs (overwritten, not
  *          accumulated).  The result is exact when this stays well below 0.5;
  *          callers with coefficients near the fp64 limit should check it.
- * Errors: INVALID_ARG, RANK, PRECISION, UNSUPPORTED_SIZE, ALIGN, OVERLAP,
- *         WORKSPACE, DEVICE.
+ * Errors: INVALID_ARG, RANK, PRECISION, NOT_POW2, UNSUPPORTED_SIZE, ALIGN,
+ *         OVERLAP, WORKSPACE, DEVICE.
  */
 int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64_t* b,
                  int64_t lb, int64_t* c, int64_t batch, void* workspace,

@@ -9,7 +9,8 @@ constant generators.
 What it computes, and the passage each part follows:
 
 * ``dft`` -- the direct O(N^2) definition X_k = sum_n x_n e^{-2 pi i k n / N}
-  ("FFT on GPU", section "Discrete Fourier Transform"), in C (``oracle.c``).
+  ("FFT on GPU", section "Discrete Fourier Transform"), in C (``oracle.c``), for
+  any N; ``dft_sample`` -- the same definition for selected outputs only.
 * ``fft`` / ``ifft`` -- recursive radix-2 decimation in time, X_k = E_k + w^k O_k,
   X_{k+N/2} = E_k - w^k O_k ("FFT on GPU", section "Fast Fourier Transform"); the
   inverse swaps w for w^{-1} and scales by 1/N (same page, the section on why
@@ -51,7 +52,7 @@ _lib = None
 
 __all__ = [
     "build", "load", "set_threads", "get_threads",
-    "dft", "fft", "ifft", "fft2", "ifft2", "fft3", "ifft3",
+    "dft", "dft_sample", "fft", "ifft", "fft2", "ifft2", "fft3", "ifft3",
     "polymul_fft", "schoolbook", "schoolbook_sample",
     "dft_py", "bitrev_order", "butterfly_pass_half", "stockham_pass",
     "poly_eval_mod", "MOD_P",
@@ -84,6 +85,7 @@ def load():
         i64, dbl_p, i64_p, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
         lib.oracle_dft_direct.argtypes = [dbl_p, dbl_p, i64, i64, c_int]
         lib.oracle_fft.argtypes = [dbl_p, dbl_p, i64, i64, c_int]
+        lib.oracle_dft_sample.argtypes = [dbl_p, i64, i64, i64_p, i64, dbl_p, c_int]
         lib.oracle_fft2.argtypes = [dbl_p, dbl_p, i64, i64, i64, c_int]
         lib.oracle_fft3.argtypes = [dbl_p, dbl_p, i64, i64, i64, i64, c_int]
         lib.oracle_schoolbook.argtypes = [i64_p, i64, i64_p, i64, i64_p, i64]
@@ -94,7 +96,7 @@ def load():
                                            ctypes.POINTER(ctypes.c_double)]
         lib.oracle_set_threads.argtypes = [c_int]
         lib.oracle_get_threads.restype = c_int
-        for name in ("oracle_dft_direct", "oracle_fft", "oracle_fft2", "oracle_fft3",
+        for name in ("oracle_dft_direct", "oracle_dft_sample", "oracle_fft", "oracle_fft2", "oracle_fft3",
                      "oracle_schoolbook", "oracle_schoolbook_sample",
                      "oracle_polymul_fft", "oracle_set_threads"):
             if name != "oracle_set_threads":
@@ -132,6 +134,20 @@ def dft(x, inverse: bool = False) -> np.ndarray:
     out = np.empty_like(x)
     batch = x.size // n if n else 0
     _check(load().oracle_dft_direct(_ptr(x), _ptr(out), n, batch, int(inverse)), "dft")
+    return out
+
+
+def dft_sample(x, ks, inverse: bool = False) -> np.ndarray:
+    """Selected outputs X_k, k in ks, of the direct DFT of each row (any N),
+    each computed from the definition in O(N): returns [batch, len(ks)]."""
+    x = _as_c128(x)
+    if x.ndim == 1:
+        x = x[None]
+    n = x.shape[-1]
+    ks = np.ascontiguousarray(np.asarray(ks), dtype=np.int64)
+    out = np.empty((x.size // n, ks.size), dtype=np.complex128)
+    _check(load().oracle_dft_sample(_ptr(x), n, x.size // n, _ptr(ks), ks.size, _ptr(out), int(inverse)),
+           "dft_sample")
     return out
 
 

@@ -73,6 +73,35 @@ int oracle_dft_direct(const double* x, double* X, int64_t n, int64_t batch, int 
     return 0;
 }
 
+/* Selected outputs of the direct DFT: X[b][j] = X_{ks[j]} of row b (any N),
+ * each one by the definition in O(N). */
+int oracle_dft_sample(const double* x, int64_t n, int64_t batch, const int64_t* ks, int64_t nk,
+                      double* X, int inverse)
+{
+    if (n < 1 || batch < 0 || nk < 0 || !x || !ks || !X) return -1;
+    for (int64_t j = 0; j < nk; ++j)
+        if (ks[j] < 0 || ks[j] >= n) return -1;
+    const double sgn = inverse ? 1.0 : -1.0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t j = 0; j < nk; ++j) {
+            const int64_t k = ks[j];
+            const double* xr = x + 2 * n * b;
+            double sr = 0.0, si = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                const int64_t m = (int64_t)(((unsigned __int128)k * (unsigned __int128)t) % (unsigned __int128)n);
+                const double ang = TWO_PI * ((double)m / (double)n);
+                const double wr = cos(ang), wi = sgn * sin(ang);
+                sr += xr[2 * t] * wr - xr[2 * t + 1] * wi;
+                si += xr[2 * t] * wi + xr[2 * t + 1] * wr;
+            }
+            if (inverse) { sr /= (double)n; si /= (double)n; }
+            X[2 * (b * nk + j)] = sr;
+            X[2 * (b * nk + j) + 1] = si;
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Recursive radix-2 decimation in time ("FFT on GPU", Fast Fourier          */
 /* Transform).  The transform of x[0], x[s], x[2s], ... (n points) is built  */

@@ -40,7 +40,7 @@ def test_header_constants_match_binding():
     for name in ("FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64"):
         m = re.search(r"#define %s (\d+)" % name, text)
         assert int(m.group(1)) == getattr(fm, name)
-    for name in ("FFT_MAX_N_C32", "FFT_MAX_N_C64"):
+    for name in ("FFT_MAX_N_C32", "FFT_MAX_N_C64", "FFT_MAX_BLUESTEIN_N"):
         m = re.search(r"#define %s \(1LL << (\d+)\)" % name, text)
         assert (1 << int(m.group(1))) == getattr(fm, name)
 
@@ -71,9 +71,10 @@ def _create_status(rank, dims, prec):
     (1, [8], 2, fm.FFT_ERR_INVALID_ARG),
     (1, [0], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [-4], 0, fm.FFT_ERR_INVALID_ARG),
-    (1, [1000], 0, fm.FFT_ERR_NOT_POW2),
-    (1, [12], 1, fm.FFT_ERR_NOT_POW2),
+    (1, [(1 << 23) + 1], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # beyond the Bluestein range
+    (1, [3 << 22], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 6], 0, fm.FFT_ERR_NOT_POW2),
+    (2, [12, 8], 1, fm.FFT_ERR_NOT_POW2),
     (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 25], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -100,7 +101,8 @@ def test_plan_create_null_out_pointer():
 @pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
 def test_valid_plan_without_gpu_is_a_device_error():
     for rank, dims, prec in ((1, [1024], 0), (1, [1 << 24], 0), (2, [64, 32], 1), (1, [1], 0),
-                             (3, [16, 8, 32], 0), (3, [4096, 1, 1], 0), (2, [8192, 8], 0)):
+                             (3, [16, 8, 32], 0), (3, [4096, 1, 1], 0), (2, [8192, 8], 0),
+                             (1, [1000], 0), (1, [12], 1), (1, [1 << 23], 0)):
         st, h = _create_status(rank, dims, prec)
         assert st == fm.FFT_ERR_DEVICE and h is None
         assert "hipGetDevice" in fm.fft_last_error()
@@ -121,6 +123,6 @@ def test_exec_and_queries_with_null_plan():
 
 def test_binding_raises_fft_error():
     with pytest.raises(fm.FFTError) as ei:
-        fm.fft_plan_create(1, [6], fm.FFT_C32)
+        fm.fft_plan_create(2, [6, 8], fm.FFT_C32)
     assert ei.value.status == fm.FFT_ERR_NOT_POW2
     assert "not a power of two" in str(ei.value)

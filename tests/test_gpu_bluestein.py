@@ -1,0 +1,78 @@
+"""Transforms of lengths that are not powers of two (chirp-z / Bluestein on
+the power-of-two path), against the fp64 oracle's direct DFT: every output
+for small N, sampled outputs computed one by one for large N (GPU).
+
+Bar: per-transform relative RMS <= 1e-6 log2 M (complex64) / 1e-14 log2 M
+(complex128), M the power-of-two length the convolution runs at (2N - 1 <= M
+< 4N): the chirp products add a few roundings to those of two length-M
+transforms."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fft_convolution_amd as fm
+import oracle
+from fft_convolution_amd import workloads as wl
+
+from conftest import fft_tol, rel_rms_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _m(n):
+    m = 1
+    while m < 2 * n - 1:
+        m *= 2
+    return m
+
+
+@pytest.mark.parametrize("n,batch", [(3, 4), (5, 1), (6, 3), (7, 2), (12, 5), (100, 3), (1000, 2), (4095, 2),
+                                     (4097, 1), (10007, 1), (3 * 1024, 2)])
+@pytest.mark.parametrize("dtype", [np.complex64, np.complex128])
+def test_bluestein_small_full(dev, n, batch, dtype):
+    print("case n=%d batch=%d %s" % (n, batch, dtype.__name__), flush=True)
+    x_np = wl.batched_uniform(n, batch, seed=n, dtype=dtype)
+    plan = fm.Plan(n, torch.complex64 if dtype == np.complex64 else torch.complex128)
+    assert "bluestein" in plan.describe()
+    x = torch.from_numpy(x_np).to(dev)
+    tol = fft_tol(_m(n), dtype == np.complex128)
+    for inverse in (False, True):
+        y = (plan.ifft(x) if inverse else plan.fft(x)).cpu().numpy()
+        ref = oracle.dft(x_np, inverse=inverse)
+        assert rel_rms_rows(y, ref).max() <= tol, (inverse, rel_rms_rows(y, ref).max())
+
+
+@pytest.mark.parametrize("n", [100003, (1 << 20) + 1, 3 << 18])
+def test_bluestein_large_sampled(dev, n):
+    print("case n=%d" % n, flush=True)
+    x_np = wl.batched_normal(n, 1, seed=n % 1000)
+    plan = fm.Plan(n, torch.complex64)
+    x = torch.from_numpy(x_np).to(dev)
+    y = plan.fft(x).cpu().numpy()
+    ks = np.unique(np.concatenate([[0, 1, n // 2, n - 1], np.random.default_rng(1).integers(0, n, 60)]))
+    ref = oracle.dft_sample(x_np, ks)
+    # relative to the RMS of the whole spectrum (sampled bins alone can be small)
+    err = np.sqrt(np.mean(np.abs(y[:, ks] - ref) ** 2)) / np.sqrt(np.mean(np.abs(y) ** 2))
+    assert err <= fft_tol(_m(n))
+    back = plan.ifft(torch.from_numpy(y).to(dev)).cpu().numpy()
+    assert rel_rms_rows(back, x_np).max() <= 2 * fft_tol(_m(n))
+
+
+def test_bluestein_in_place_and_poly_mul_rejected(dev):
+    n = 777
+    x_np = wl.batched_uniform(n, 3, seed=9)
+    plan = fm.Plan(n, torch.complex64)
+    x = torch.from_numpy(x_np).to(dev)
+    y = plan.fft(x)
+    z = x.clone()
+    plan.fft(z, out=z)
+    torch.cuda.synchronize()
+    assert torch.equal(y, z)
+    p64 = fm.Plan(1000, torch.complex128)
+    a = torch.ones(1, 400, dtype=torch.int64, device=dev)
+    c = torch.empty(1, 799, dtype=torch.int64, device=dev)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul(p64.handle, a, 400, a, 400, c, 1)
+    assert e.value.status == fm.FFT_ERR_NOT_POW2

@@ -227,6 +227,20 @@ def test_direct_dft_matches_brute_force_and_numpy():
         assert rel_rms(oracle.dft(x, inverse=True), np.fft.ifft(x)) < 1e-13
 
 
+def test_dft_sample_matches_full_dft_and_numpy():
+    rng = np.random.default_rng(14)
+    for n in (1, 7, 12, 97, 1000, 4099):
+        x = crand(rng, 2, n)
+        ks = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 9)]))
+        full = np.fft.fft(x, axis=-1)
+        assert rel_rms(oracle.dft_sample(x, ks), full[:, ks]) < 1e-13
+        if n <= 1000:
+            assert rel_rms(oracle.dft_sample(x, ks), oracle.dft(x)[:, ks]) < 1e-13
+        assert rel_rms(oracle.dft_sample(x, ks, inverse=True), np.fft.ifft(x, axis=-1)[:, ks]) < 1e-13
+    with pytest.raises(ValueError):
+        oracle.dft_sample(crand(rng, 5), [5])
+
+
 def test_radix2_matches_direct_dft():
     rng = np.random.default_rng(6)
     for m in range(0, 9):
