@@ -18,6 +18,12 @@ What it computes, and the passage each part follows:
 * ``fft2`` / ``ifft2`` -- rows then columns ("Stockham FFT Butterfly Algorithm in
   Parallel GLSL", section "Multi-Dimensional Transforms and Separability");
   ``fft3`` / ``ifft3`` -- the same, one axis after another, for 3D data.
+* ``rfft`` / ``irfft`` -- transforms of real rows: the first N/2 + 1 outputs of
+  ``fft`` of the row widened to complex (the other half follows from
+  X_{N-k} = conj X_k, since the inputs are real), and back: the real part of
+  ``ifft`` of the Hermitian extension of N/2 + 1 values, the imaginary parts
+  of X_0 and X_{N/2} taken as zero.  The operands of polynomial multiplication
+  are real ("FFT on GPU", polynomial-multiplication section).
 * ``polymul_fft`` -- forward both zero-padded operands, pointwise product,
   inverse, rint ("FFT on GPU", polynomial-multiplication and whole-process
   sections); ``schoolbook`` / ``schoolbook_sample`` -- the exact convolution
@@ -164,6 +170,34 @@ def fft(x, inverse: bool = False) -> np.ndarray:
 def ifft(X) -> np.ndarray:
     """Inverse of :func:`fft`: conjugate twiddles and 1/N."""
     return fft(X, inverse=True)
+
+
+def rfft(x) -> np.ndarray:
+    """X_0 .. X_{N/2} of the transform of each real row (N a power of two):
+    [..., N] real -> [..., N // 2 + 1] complex128."""
+    x = np.asarray(x)
+    if np.iscomplexobj(x):
+        raise TypeError("rfft takes real rows")
+    n = x.shape[-1]
+    return fft(x.astype(np.float64))[..., : n // 2 + 1]
+
+
+def irfft(X, n: int) -> np.ndarray:
+    """The real rows of length n whose transform has X_0 .. X_{n/2} equal to
+    the rows of X ([..., n // 2 + 1]): every bin k > n/2 is set to
+    conj X_{n-k}, the imaginary parts of X_0 and X_{n/2} are dropped (a real
+    row has real values there), then the real part of :func:`ifft`."""
+    X = _as_c128(X)
+    h = n // 2
+    if X.shape[-1] != h + 1:
+        raise ValueError("irfft of length %d takes %d values per row" % (n, h + 1))
+    full = np.empty(X.shape[:-1] + (n,), dtype=np.complex128)
+    full[..., : h + 1] = X[..., : h + 1] if n > 1 else X[..., :1]
+    full[..., 0] = full[..., 0].real
+    if n > 1:
+        full[..., h] = full[..., h].real
+        full[..., h + 1:] = np.conj(X[..., 1:h][..., ::-1])
+    return ifft(full).real
 
 
 def fft2(x, inverse: bool = False) -> np.ndarray:

@@ -363,6 +363,52 @@ def test_fft3_matches_numpy_separability_and_closed_form():
 # Polynomial multiplication
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 64, 4096, 1 << 17])
+def test_rfft_irfft_match_numpy(n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal((3, n))
+    X = oracle.rfft(x)
+    assert X.shape == (3, n // 2 + 1)
+    ref = np.fft.rfft(x)
+    assert np.abs(X - ref).max() <= 1e-13 * max(1.0, math.log2(n)) * np.abs(ref).max()
+    back = oracle.irfft(X, n)
+    assert np.abs(back - x).max() <= 1e-13 * max(1.0, math.log2(n))
+    # a spectrum that is not the half of a real row's: numpy's pocketfft c2r
+    # also takes the DC and Nyquist bins as real
+    Y = rng.standard_normal((2, n // 2 + 1)) + 1j * rng.standard_normal((2, n // 2 + 1))
+    assert np.abs(oracle.irfft(Y, n) - np.fft.irfft(Y, n)).max() <= 1e-13 * max(1.0, math.log2(n))
+
+
+def test_rfft_closed_forms_and_hermitian_half():
+    n = 256
+    t = np.arange(n)
+    for f in (0, 1, 37, n // 2 - 1, n // 2):
+        # cos(2 pi f t / N) = (w^{-ft} + w^{ft}) / 2: N/2 at bins f and N - f,
+        # which coincide (N) at f = 0 and f = N/2
+        X = oracle.rfft(np.cos(2 * np.pi * f * t / n)[None, :])[0]
+        want = np.zeros(n // 2 + 1, dtype=complex)
+        want[f] = n if f in (0, n // 2) else n / 2
+        assert np.abs(X - want).max() < 1e-10
+        # sin: -i N/2 at f (0 < f < N/2)
+        if 0 < f < n // 2:
+            S = oracle.rfft(np.sin(2 * np.pi * f * t / n)[None, :])[0]
+            want = np.zeros(n // 2 + 1, dtype=complex)
+            want[f] = -0.5j * n
+            assert np.abs(S - want).max() < 1e-10
+    # the half is the front of the full complex transform of the same row,
+    # whose other half is conjugate-symmetric (brute force, tiny N)
+    x = np.random.default_rng(3).standard_normal(16)
+    full = np.array(oracle.dft_py(list(x.astype(complex))))
+    assert np.abs(oracle.rfft(x[None, :])[0] - full[:9]).max() < 1e-12
+    assert np.abs(full[1:][::-1] - np.conj(full[1:])).max() < 1e-12
+    # unit impulse at position 3 back from its spectrum w^{3k}
+    k = np.arange(n // 2 + 1)
+    imp = oracle.irfft(np.exp(-2j * np.pi * 3 * k / n)[None, :], n)[0]
+    want = np.zeros(n)
+    want[3] = 1.0
+    assert np.abs(imp - want).max() < 1e-13
+
+
 def test_polymul_worked_example():
     rows = {r[0]: [int(v) for v in r[1:]] for r in _golden_rows("polymul_worked.txt")}
     a, b, c = rows["a"], rows["b"], rows["c"]
