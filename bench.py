@@ -17,7 +17,8 @@ Prints ONE JSON line with:
 
 Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
-transform the same way.
+transform the same way, and the R2C transform of 16384 real rows of 8192
+points (value = batch * 2.5 N log2 N / t, half the complex count).
 """
 from __future__ import annotations
 
@@ -35,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
-             "polymul_l262144_b32", "c2c3d_256x256x256_b1")
+             "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384")
 
 
 def kernel_sources_digest() -> str:
@@ -120,6 +121,23 @@ def setup_workload(name, dev, fm, torch):
                     bytes=2 * x.numel() * 8, plan=plan.describe(), kernels=3, keep=(plan, x, y),
                     sample_rows=lambda rows: x[:rows].cpu().numpy(), oracle_unit=5.0 * n * math.log2(n))
         return step, info
+    if name.startswith("r2c"):
+        n, batch = spec["n"], spec["batch"]
+        x_np = wl.workload_input(name)
+        x = torch.from_numpy(x_np).to(dev)
+        y = torch.empty(batch, n // 2 + 1, dtype=torch.complex64, device=dev)
+        plan = fm.RealPlan(n, torch.float32)
+        wsb = fm.fft_workspace_size(plan.handle, batch)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step():
+            fm.fft_exec_r2c(plan.handle, x, y, batch, ws, stream)
+        info = dict(n=n, batch=batch, dtype="f32", flops=batch * 2.5 * n * math.log2(n),
+                    bytes=x.numel() * 4 + y.numel() * 8, plan=plan.describe(), kernels=1 if wsb == 0 else 2,
+                    sample_rows=lambda rows: x_np[:rows], oracle_unit=2.5 * n * math.log2(n),
+                    oracle_fn="rfft", keep=(plan, x, y, ws))
+        return step, info
     if name.startswith("polymul"):
         length, batch = spec["length"], spec["batch"]
         a_np, b_np = wl.workload_input(name)
@@ -175,16 +193,17 @@ def cpu_baseline(name, info, budget_s):
         # batch takes less, it is transformed repeatedly until the budget is used.
         total = info["batch"]
         probe = min(total, 256)
+        fn = getattr(oracle, info.get("oracle_fn", "fft"))
         x = info["sample_rows"](probe)
         t0 = time.perf_counter()
-        oracle.fft(x)
+        fn(x)
         per_row = (time.perf_counter() - t0) / probe
         rows = int(max(1, min(total, budget_s / max(per_row, 1e-12))))
         x = info["sample_rows"](rows)
         reps, dt = 0, 0.0
         while reps == 0 or dt < budget_s:
             t0 = time.perf_counter()
-            oracle.fft(x)
+            fn(x)
             dt += time.perf_counter() - t0
             reps += 1
         units = rows * reps

@@ -29,8 +29,9 @@ __all__ = [
     "lib", "lib_path", "EXPORTS",
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
+    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r",
     "fft_status_string", "fft_last_error",
-    "Plan", "poly_mul",
+    "Plan", "RealPlan", "poly_mul",
 ]
 
 FFT_C32, FFT_C64 = 0, 1
@@ -58,6 +59,7 @@ lib_path = os.path.join(_HERE, "libfftmi.so")
 EXPORTS = (
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
+    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r",
     "fft_status_string", "fft_last_error",
 )
 
@@ -97,11 +99,16 @@ def lib():
         L.fft_exec_3d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
         L.fft_poly_mul_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_poly_mul.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, vp, vp]
+        L.fft_plan_create_real.argtypes = [ctypes.POINTER(vp), i64, c_int]
+        L.fft_exec_r2c.argtypes = [vp, vp, vp, i64, vp, vp]
+        L.fft_exec_c2r.argtypes = [vp, vp, vp, i64, vp, vp]
         L.fft_status_string.argtypes = [c_int]
         L.fft_status_string.restype = ctypes.c_char_p
         L.fft_last_error.argtypes = []
         L.fft_last_error.restype = ctypes.c_char_p
-        for name in EXPORTS[:-2]:
+        for name in EXPORTS:
+            if name in ("fft_status_string", "fft_last_error"):
+                continue
             getattr(L, name).restype = c_int
         _lib = L
         return L
@@ -193,6 +200,23 @@ def fft_poly_mul(plan, a, la: int, b, lb: int, c, batch: int, workspace=None,
     _check(lib().fft_poly_mul(plan, _ptr(a), int(la), _ptr(b), int(lb), _ptr(c), int(batch),
                               _ptr(workspace), _ptr(d_max_residual), _stream(stream)),
            "fft_poly_mul")
+
+
+def fft_plan_create_real(n: int, prec: int = FFT_C32) -> int:
+    """Create a plan for transforms of real rows of n points; returns its handle."""
+    h = ctypes.c_void_p()
+    _check(lib().fft_plan_create_real(ctypes.byref(h), int(n), int(prec)), "fft_plan_create_real")
+    return h.value
+
+
+def fft_exec_r2c(plan, in_, out, batch: int, workspace=None, stream=None) -> None:
+    _check(lib().fft_exec_r2c(plan, _ptr(in_), _ptr(out), int(batch), _ptr(workspace), _stream(stream)),
+           "fft_exec_r2c")
+
+
+def fft_exec_c2r(plan, in_, out, batch: int, workspace=None, stream=None) -> None:
+    _check(lib().fft_exec_c2r(plan, _ptr(in_), _ptr(out), int(batch), _ptr(workspace), _stream(stream)),
+           "fft_exec_c2r")
 
 
 # --------------------------------------------------------------------------
@@ -307,6 +331,73 @@ class Plan:
         resid = torch.empty(1, dtype=torch.float64, device=a.device) if residual else None
         fft_poly_mul(self.handle, a2, la, b2, lb, out, batch, ws, resid)
         return (out, resid) if residual else out
+
+
+class RealPlan:
+    """A plan for real rows of n points: ``rfft`` [..., n] float32/64 ->
+    [..., n // 2 + 1] complex64/128, ``irfft`` the reverse."""
+
+    def __init__(self, n: int, dtype=None):
+        import torch
+        if dtype is None:
+            dtype = torch.float32
+        if dtype not in (torch.float32, torch.float64):
+            raise TypeError("dtype must be torch.float32 or torch.float64")
+        self.dtype = dtype
+        self.cdtype = torch.complex64 if dtype == torch.float32 else torch.complex128
+        self.prec = FFT_C32 if dtype == torch.float32 else FFT_C64
+        self.n = int(n)
+        self.handle = fft_plan_create_real(self.n, self.prec)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                fft_plan_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+    def describe(self) -> str:
+        return fft_plan_describe(self.handle)
+
+    @staticmethod
+    def _check(x, dtype, last):
+        import torch
+        if not isinstance(x, torch.Tensor) or not x.is_cuda:
+            raise TypeError("expected a device tensor")
+        if x.dtype != dtype:
+            raise TypeError("expected %s, got %s" % (dtype, x.dtype))
+        if not x.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        if x.shape[-1] != last:
+            raise ValueError("last dim %d, expected %d" % (x.shape[-1], last))
+        return x.numel() // last
+
+    def _ws(self, batch, device):
+        import torch
+        nb = fft_workspace_size(self.handle, batch)
+        return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+    def rfft(self, x, out=None):
+        import torch
+        batch = self._check(x, self.dtype, self.n)
+        if out is None:
+            out = torch.empty(x.shape[:-1] + (self.n // 2 + 1,), dtype=self.cdtype, device=x.device)
+        elif self._check(out, self.cdtype, self.n // 2 + 1) != batch:
+            raise ValueError("out has another batch")
+        fft_exec_r2c(self.handle, x, out, batch, self._ws(batch, x.device))
+        return out
+
+    def irfft(self, X, out=None):
+        import torch
+        batch = self._check(X, self.cdtype, self.n // 2 + 1)
+        if out is None:
+            out = torch.empty(X.shape[:-1] + (self.n,), dtype=self.dtype, device=X.device)
+        elif self._check(out, self.dtype, self.n) != batch:
+            raise ValueError("out has another batch")
+        fft_exec_c2r(self.handle, X, out, batch, self._ws(batch, X.device))
+        return out
 
 
 def poly_mul(a, b, residual=False):

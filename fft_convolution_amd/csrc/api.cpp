@@ -113,7 +113,7 @@ std::vector<double> stage_table(int logn, int prec)
 
 }  // namespace
 
-enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_ND = 3, PATH_BLUESTEIN = 4 };
+enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_ND = 3, PATH_BLUESTEIN = 4, PATH_REAL = 5 };
 
 // One super-stage pass of a multi-pass plan.
 struct PassPlan {
@@ -151,6 +151,9 @@ struct fft_plan {
     // rank 1, any N (Bluestein): chirp c_j (N entries), B = F_M(b) (M entries),
     // the power-of-two plan of length M = 2^logm it runs on.
     int logm = 0;
+    // real rows of N = 2H points: inner = the complex plan of length H,
+    // big_* = w_N, log_a = log2 H; real_fused: H within the rows kernel's range.
+    bool real_fused = false;
     void* chirp = nullptr;
     void* bspec = nullptr;
     fft_plan* inner = nullptr;
@@ -210,10 +213,11 @@ void free_plan(fft_plan* p)
     delete p;
 }
 
-// Tables for w_M^m = hi[m >> L] lo[m & (2^L - 1)], M = 2^logm, L = ceil(logm / 2).
-int upload_big(int logm, int prec, void** hi_dev, void** lo_dev, int* lbits)
+// Tables for w_M^m = hi[m >> L] lo[m & (2^L - 1)], M = 2^logm, L = ceil(logm / 2)
+// unless `want_lbits` >= 0 gives L.
+int upload_big(int logm, int prec, void** hi_dev, void** lo_dev, int* lbits, int want_lbits = -1)
 {
-    *lbits = (logm + 1) / 2;
+    *lbits = want_lbits >= 0 ? want_lbits : (logm + 1) / 2;
     const int64_t m = int64_t(1) << logm;
     const int64_t nlo = int64_t(1) << *lbits, nhi = m >> *lbits;
     std::vector<double> lo(2 * nlo), hi(2 * nhi);
@@ -238,6 +242,8 @@ int check_exec(const fft_plan* plan, int dir, int rank, const void* in, void* ou
     if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
     if (dir != FFT_FORWARD && dir != FFT_INVERSE) return fail(FFT_ERR_INVALID_ARG, "dir %d is not FFT_FORWARD/FFT_INVERSE", dir);
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch %lld < 0", (long long)batch);
+    if (plan->path == PATH_REAL)
+        return fail(FFT_ERR_RANK, "plan is for real rows: use fft_exec_r2c / fft_exec_c2r");
     if (plan->rank != rank)
         return fail(FFT_ERR_RANK, "plan has rank %d, this call needs rank %d", plan->rank, rank);
     if (batch == 0) {
@@ -277,6 +283,8 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
     if (p->path == PATH_BLUESTEIN)
         return ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
+    if (p->path == PATH_REAL)  // the H-point spectrum of every row, beyond the one-kernel range
+        return p->real_fused || p->n == 1 ? 0 : (size_t)batch * (size_t)(p->n / 2) * p->elem;
     const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_ND && p->logf > 0);
     return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
@@ -577,6 +585,10 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             snprintf(buf, len, "rank=1 n=%lld prec=%s path=bluestein m=%lld", (long long)p->n, prec,
                      1LL << p->logm);
             break;
+        case PATH_REAL:
+            snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
+                     p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
+            break;
         case PATH_MULTIPASS: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
             for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
@@ -730,7 +742,7 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
 {
     if (!plan || !bytes) return fail(FFT_ERR_INVALID_ARG, "plan or bytes is NULL");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
-    if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
+    if (plan->rank != 1 || plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "poly-mul needs a complex rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
     if (plan->path == PATH_BLUESTEIN) return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
@@ -743,7 +755,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
                  int64_t batch, void* workspace, double* d_max_residual, void* stream)
 {
     if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
-    if (plan->rank != 1) return fail(FFT_ERR_RANK, "poly-mul needs a rank-1 plan");
+    if (plan->rank != 1 || plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "poly-mul needs a complex rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
     if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
@@ -801,6 +813,139 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
         if (e != hipSuccess) return hip_fail(e, "fft_poly_mul (FFTMI_SYNC)");
     }
     return FFT_OK;
+}
+
+int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
+{
+    if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
+    *out_plan = nullptr;
+    if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
+    if (n < 1) return fail(FFT_ERR_INVALID_ARG, "n = %lld < 1", (long long)n);
+    if (!is_pow2(n)) return fail(FFT_ERR_NOT_POW2, "n = %lld is not a power of two", (long long)n);
+    if (n > 2 * max_n(prec))
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "n = %lld exceeds %lld", (long long)n, (long long)(2 * max_n(prec)));
+    fft_plan* p = new (std::nothrow) fft_plan;
+    if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
+    p->rank = 1;
+    p->path = PATH_REAL;
+    p->prec = prec;
+    p->elem = elem_bytes(prec);
+    p->dims[0] = p->n = n;
+    p->logn = ilog2(n);
+    p->log_a = p->logn > 0 ? p->logn - 1 : 0;
+    p->real_fused = n >= 2 && (n / 2) <= max_lds_n(prec);
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "hipGetDevice");
+    }
+    int st = FFT_OK;
+    if (n >= 2) {
+        const int64_t h = n / 2;
+        st = fft_plan_create(&p->inner, 1, &h, prec);
+        // w_N^{t + i T} = hi[i] lo[t] for the fused kernels (T threads per row)
+        const int lem = plan_lem(prec);
+        const int want = p->real_fused ? p->log_a - plan_loge(p->log_a, lem) : -1;
+        if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits, want);
+    }
+    if (st != FFT_OK) {
+        free_plan(p);
+        return st;
+    }
+    *out_plan = p;
+    return FFT_OK;
+}
+
+// Checks of fft_exec_r2c / fft_exec_c2r: `in_bytes` / `out_bytes` per row.
+static int check_real_exec(const fft_plan* plan, const void* in, size_t in_row, const void* out, size_t out_row,
+                           int64_t batch, void* workspace, bool* noop)
+{
+    *noop = false;
+    if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->path != PATH_REAL) return fail(FFT_ERR_RANK, "plan is not for real rows (fft_plan_create_real)");
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch %lld < 0", (long long)batch);
+    if (batch == 0) {
+        *noop = true;
+        return FFT_OK;
+    }
+    if (!in || !out) return fail(FFT_ERR_INVALID_ARG, "in or out is NULL");
+    if (batch > INT64_MAX / (int64_t)((plan->n + 2) * plan->elem))
+        return fail(FFT_ERR_INVALID_ARG, "batch %lld overflows the buffer size", (long long)batch);
+    if (((uintptr_t)in | (uintptr_t)out) % plan->elem)
+        return fail(FFT_ERR_ALIGN, "in/out must be aligned to %zu bytes", plan->elem);
+    const size_t bi = (size_t)batch * in_row, bo = (size_t)batch * out_row;
+    if (ranges_overlap(in, bi, out, bo)) return fail(FFT_ERR_OVERLAP, "in and out overlap");
+    const size_t ws = c2c_workspace(plan, batch);
+    if (ws) {
+        if (!workspace) return fail(FFT_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
+        if ((uintptr_t)workspace % plan->elem) return fail(FFT_ERR_ALIGN, "workspace misaligned");
+        if (ranges_overlap(workspace, ws, in, bi) || ranges_overlap(workspace, ws, out, bo))
+            return fail(FFT_ERR_WORKSPACE, "workspace overlaps in or out");
+    }
+    return check_device(plan);
+}
+
+static int real_done(hipError_t e, const char* what, hipStream_t s)
+{
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (getenv("FFTMI_SYNC")) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    return FFT_OK;
+}
+
+int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream)
+{
+    bool noop = false;
+    const size_t rb = plan ? plan->elem / 2 : 0;  // bytes of one real value
+    int st = check_real_exec(plan, in, plan ? plan->n * rb : 0, out, plan ? (plan->n / 2 + 1) * plan->elem : 0,
+                             batch, workspace, &noop);
+    if (st != FFT_OK || noop) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (plan->n == 1) {
+        e = launch_real_n1(plan->prec, false, in, out, batch, s);
+    } else if (plan->real_fused) {
+        e = launch_real_rows(plan->prec, plan->log_a, false, in, out, batch, plan->inner->tw_a, plan->big_hi,
+                             plan->big_lo, s);
+    } else {
+        // Z = F_H(rows read as complex) into the workspace (the out buffer, which
+        // holds batch (H + 1) >= batch H values, is the H-point plan's scratch),
+        // then the split, two bins per thread.
+        st = fft_exec_c2c(plan->inner, FFT_FORWARD, in, workspace, batch, out, stream);
+        if (st != FFT_OK) return st;
+        const BigTwiddle wn{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
+        e = launch_real_pairs(plan->prec, false, workspace, out, plan->n / 2, batch, wn, s);
+    }
+    return real_done(e, "fft_exec_r2c", s);
+}
+
+int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream)
+{
+    bool noop = false;
+    const size_t rb = plan ? plan->elem / 2 : 0;
+    int st = check_real_exec(plan, in, plan ? (plan->n / 2 + 1) * plan->elem : 0, out, plan ? plan->n * rb : 0,
+                             batch, workspace, &noop);
+    if (st != FFT_OK || noop) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (plan->n == 1) {
+        e = launch_real_n1(plan->prec, true, in, out, batch, s);
+    } else if (plan->real_fused) {
+        e = launch_real_rows(plan->prec, plan->log_a, true, in, out, batch, plan->inner->tw_a, plan->big_hi,
+                             plan->big_lo, s);
+    } else {
+        // Z from the bin pairs straight into out (N reals = H complex per row),
+        // then the inverse H-point transform in place, the workspace its scratch.
+        const BigTwiddle wn{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
+        e = launch_real_pairs(plan->prec, true, in, out, plan->n / 2, batch, wn, s);
+        if (e != hipSuccess) return hip_fail(e, "fft_exec_c2r");
+        st = fft_exec_c2c(plan->inner, FFT_INVERSE, out, out, batch, workspace, stream);
+        if (st != FFT_OK) return st;
+        e = hipSuccess;
+    }
+    return real_done(e, "fft_exec_c2r", s);
 }
 
 }  // extern "C"

@@ -75,6 +75,19 @@ hipError_t launch_chirp_post(int prec, const void* w, void* out, int64_t n, int 
 // complex128 -> complex64, `total` elements.
 hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t stream);
 
+// Real rows (real.hip), N = 2H points.  One-kernel range (H = 2^logh within
+// the rows kernel's): R2C in [nrows][2H] real -> out [nrows][H + 1] complex,
+// C2R the reverse (scaled 1/N overall); tw: stage table for H; whi/wlo: w_N
+// tables split at T (threads per row).  in and out must not alias.
+hipError_t launch_real_rows(int prec, int logh, bool c2r, const void* in, void* out, int64_t nrows, const void* tw,
+                            const void* whi, const void* wlo, hipStream_t stream);
+// Longer rows, around the H-point complex transform: R2C z [batch][H] -> out
+// [batch][H + 1]; C2R x [batch][H + 1] -> z [batch][H].  wn: tables for w_N.
+hipError_t launch_real_pairs(int prec, bool c2r, const void* in, void* out, int64_t h, int64_t batch,
+                             BigTwiddle wn, hipStream_t stream);
+// N = 1: out = in, real <-> complex.
+hipError_t launch_real_n1(int prec, bool c2r, const void* in, void* out, int64_t batch, hipStream_t stream);
+
 // d_resid[0] = 0 (a kernel, not a memset, so the call is safe to capture).
 hipError_t launch_zero_resid(double* d_resid, hipStream_t stream);
 

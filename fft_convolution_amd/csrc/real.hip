@@ -1,0 +1,278 @@
+// real.hip -- transforms of real rows through the complex transform of half
+// their length.
+//
+// A real row x of N = 2H points, read as H complex values z_n = x_{2n} +
+// i x_{2n+1} (the same memory), has the H-point transform Z_k = E_k + i O_k,
+// E and O being the transforms of the even and odd samples.  Both of those
+// are transforms of real rows, so conj Z_{H-k} = E_k - i O_k and
+//     E_k = (Z_k + conj Z_{H-k}) / 2,    O_k = -i (Z_k - conj Z_{H-k}) / 2;
+// the radix-2 combine of "FFT on GPU" (section "Fast Fourier Transform") then
+// gives X_k = E_k + w_N^k O_k for k = 0 .. H (E_H = E_0, O_H = O_0), the
+// N/2 + 1 bins that determine the rest (X_{N-k} = conj X_k).
+// The way back undoes the two steps:
+//     E_k = (X_k + conj X_{H-k}) / 2,   O_k = w_N^{-k} (X_k - conj X_{H-k}) / 2,
+//     Z_k = E_k + i O_k,   z = F_H^{-1} Z,   x_{2n} = Re z_n,  x_{2n+1} = Im z_n,
+// with the imaginary parts of X_0 and X_H taken as zero (a real row's are).
+//
+// H within the one-kernel range: one workgroup per row (group) runs the
+// H-point transform in registers and LDS and does the split (or, backwards,
+// the merge) through one more LDS exchange, so a row crosses HBM once each
+// way.  Longer rows: the H-point multi-pass transform plus one pass that
+// handles the bins k and H - k together.
+#include "launch.hpp"
+#include "stockham.hpp"
+#include "tile_common.hpp"
+
+namespace fftmi {
+
+template <typename V> __device__ __forceinline__ V chalf(V a) { return V{a.x * 0.5f, a.y * 0.5f}; }
+
+// X_k from a = Z_k, b = Z_{H-k} and w = w_N^k.
+template <typename V> __device__ __forceinline__ V real_split(V a, V b, V w)
+{
+    const V zc = cconj(b);
+    const V e = chalf(cadd(a, zc));
+    const V o = cmul_mi(chalf(csub(a, zc)));
+    return cadd(e, cmul(o, w));
+}
+
+// Z_k from a = X_k, b = X_{H-k} and w = w_N^k.
+template <typename V> __device__ __forceinline__ V real_merge(V a, V b, V w)
+{
+    const V xc = cconj(b);
+    const V e = chalf(cadd(a, xc));
+    const V o = cmul(chalf(csub(a, xc)), cconj(w));
+    return cadd(e, cmul_pi(o));
+}
+
+// Slots per row in LDS: the H-point exchange layout plus one for X_H.
+template <int LOGH> constexpr int real_slots() { return lds_padded(1 << LOGH) + 1; }
+
+// R2C, one-kernel range.  in: [nrows][2H] real (read as [nrows][H] complex),
+// out: [nrows][H + 1].  whi/wlo: w_N^{i T} and w_N^t (N = 2H), so that
+// w_N^{t + i T} = whi[i] wlo[t] for the element v[i] of thread t.
+template <typename V, int LOGH>
+__global__ __launch_bounds__((Geom<V, LOGH>::T * rows_per_wg<V, LOGH>()))
+void r2c_rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw, const V* __restrict__ whi,
+                     const V* __restrict__ wlo)
+{
+    using G = Geom<V, LOGH>;
+    constexpr int H = G::N, T = G::T, E = G::E;
+    constexpr int RPW = rows_per_wg<V, LOGH>();
+    constexpr int SLOTS = real_slots<LOGH>();
+    __shared__ V lds[SLOTS * RPW];
+
+    const int tid = threadIdx.x;
+    const int rloc = tid / T;
+    const int t = tid % T;
+    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
+    const bool live = row < nrows;
+
+    TwBases<V, LOGH> tb;
+    tb.load(tw, t);
+    V v[E];
+    const V* src = in + row * H + t;
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = live ? ld_stream(src + i * T) : V{0, 0};
+    const LdsLines<V, 1> L{lds + rloc * SLOTS, 0};
+    if constexpr (LOGH > 0) fft_regs<LOGH>(v, t, tb, L);
+    __syncthreads();  // the transform's last exchange is read by now
+#pragma unroll
+    for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
+    __syncthreads();
+    if (!live) return;
+    const V w0 = wlo[t];
+    V* dst = out + row * (H + 1);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int k = t + i * T;
+        st_stream(dst + k, real_split(v[i], *L.ptr((H - k) & (H - 1)), cmul(whi[i], w0)));
+    }
+    if (t == 0) st_stream(dst + H, V{v[0].x - v[0].y, 0});
+}
+
+// C2R, one-kernel range.  in: [nrows][H + 1], out: [nrows][2H] real (written
+// as [nrows][H] complex).  scale = 1/H (the inverse H-point transform's).
+template <typename V, int LOGH>
+__global__ __launch_bounds__((Geom<V, LOGH>::T * rows_per_wg<V, LOGH>()))
+void c2r_rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw, const V* __restrict__ whi,
+                     const V* __restrict__ wlo, typename real_of<V>::type scale)
+{
+    using G = Geom<V, LOGH>;
+    constexpr int H = G::N, T = G::T, E = G::E;
+    constexpr int RPW = rows_per_wg<V, LOGH>();
+    constexpr int SLOTS = real_slots<LOGH>();
+    __shared__ V lds[SLOTS * RPW];
+
+    const int tid = threadIdx.x;
+    const int rloc = tid / T;
+    const int t = tid % T;
+    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
+    const bool live = row < nrows;
+
+    TwBases<V, LOGH> tb;
+    tb.load(tw, t);
+    V v[E];
+    const V* src = in + row * (H + 1);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = live ? ld_stream(src + t + i * T) : V{0, 0};
+    const LdsLines<V, 1> L{lds + rloc * SLOTS, 0};
+    if (t == 0) {
+        v[0].y = 0;
+        const V xh = live ? src[H] : V{0, 0};
+        *L.ptr(H) = V{xh.x, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
+    __syncthreads();
+    const V w0 = wlo[t];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int k = t + i * T;
+        // inverse transform as conj(F(conj Z)) / H
+        v[i] = cconj(real_merge(v[i], *L.ptr(H - k), cmul(whi[i], w0)));
+    }
+    __syncthreads();  // partners are read before the transform reuses the LDS
+    if constexpr (LOGH > 0) fft_regs<LOGH>(v, t, tb, L);
+    if (!live) return;
+    V* dst = out + row * H + t;
+#pragma unroll
+    for (int i = 0; i < E; ++i) st_stream(dst + i * T, V{v[i].x * scale, -v[i].y * scale});
+}
+
+// Longer rows.  One thread per bin pair (k, H - k), k = 0 .. H/2, of each row.
+// R2C: z [batch][H] (the H-point transform) -> out [batch][H + 1].
+template <typename V>
+__global__ void r2c_pairs_kernel(const V* __restrict__ z, V* __restrict__ out, int64_t h, int64_t batch, BigTw<V> wn)
+{
+    const int64_t npair = h / 2 + 1;
+    for (int64_t row = blockIdx.y; row < batch; row += gridDim.y) {
+        const V* zr = z + row * h;
+        V* xr = out + row * (h + 1);
+        for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < npair;
+             k += (int64_t)gridDim.x * blockDim.x) {
+            if (k == 0) {
+                const V z0 = zr[0];
+                xr[0] = V{z0.x + z0.y, 0};
+                xr[h] = V{z0.x - z0.y, 0};
+                continue;
+            }
+            const V a = zr[k], b = zr[h - k];
+            const V w = wn(k);
+            xr[k] = real_split(a, b, w);
+            if (2 * k != h) xr[h - k] = real_split(b, a, V{-w.x, w.y});  // w_N^{H-k} = -conj w_N^k
+        }
+    }
+}
+
+// C2R: x [batch][H + 1] -> z [batch][H], the spectrum of the packed real row.
+template <typename V>
+__global__ void c2r_pairs_kernel(const V* __restrict__ x, V* __restrict__ z, int64_t h, int64_t batch, BigTw<V> wn)
+{
+    const int64_t npair = h / 2 + 1;
+    for (int64_t row = blockIdx.y; row < batch; row += gridDim.y) {
+        const V* xr = x + row * (h + 1);
+        V* zr = z + row * h;
+        for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < npair;
+             k += (int64_t)gridDim.x * blockDim.x) {
+            if (k == 0) {
+                const auto a = xr[0].x, b = xr[h].x;
+                zr[0] = V{(a + b) * 0.5f, (a - b) * 0.5f};
+                continue;
+            }
+            const V a = xr[k], b = xr[h - k];
+            const V w = wn(k);
+            zr[k] = real_merge(a, b, w);
+            if (2 * k != h) zr[h - k] = real_merge(b, a, V{-w.x, w.y});
+        }
+    }
+}
+
+// N = 1: X_0 = x_0, and back.
+template <typename V>
+__global__ void real_n1_kernel(const void* in, void* out, int64_t batch, int c2r)
+{
+    using Rl = typename real_of<V>::type;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < batch; e += (int64_t)gridDim.x * blockDim.x) {
+        if (c2r)
+            ((Rl*)out)[e] = ((const V*)in)[e].x;
+        else
+            ((V*)out)[e] = V{((const Rl*)in)[e], 0};
+    }
+}
+
+template <typename V, int LOGH>
+static hipError_t launch_real_rows_t(bool c2r, const void* in, void* out, int64_t nrows, const void* tw,
+                                     const void* whi, const void* wlo, hipStream_t s)
+{
+    constexpr int RPW = rows_per_wg<V, LOGH>();
+    constexpr int BLOCK = Geom<V, LOGH>::T * RPW;
+    const int64_t blocks = (nrows + RPW - 1) / RPW;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    using Rl = typename real_of<V>::type;
+    if (c2r)
+        hipLaunchKernelGGL((c2r_rows_kernel<V, LOGH>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, (const V*)in,
+                           (V*)out, nrows, (const V*)tw, (const V*)whi, (const V*)wlo, (Rl)(1.0 / (1 << LOGH)));
+    else
+        hipLaunchKernelGGL((r2c_rows_kernel<V, LOGH>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, (const V*)in,
+                           (V*)out, nrows, (const V*)tw, (const V*)whi, (const V*)wlo);
+    return hipGetLastError();
+}
+
+hipError_t launch_real_rows(int prec, int logh, bool c2r, const void* in, void* out, int64_t nrows, const void* tw,
+                            const void* whi, const void* wlo, hipStream_t s)
+{
+#define FFTMI_REAL_CASE(L) \
+    case L: return prec == 0 ? launch_real_rows_t<float2, L>(c2r, in, out, nrows, tw, whi, wlo, s) \
+                             : launch_real_rows_t<double2, L>(c2r, in, out, nrows, tw, whi, wlo, s);
+    if (prec == 1 && logh > 12) return hipErrorInvalidValue;
+    switch (logh) {
+        FFTMI_REAL_CASE(0) FFTMI_REAL_CASE(1) FFTMI_REAL_CASE(2) FFTMI_REAL_CASE(3) FFTMI_REAL_CASE(4)
+        FFTMI_REAL_CASE(5) FFTMI_REAL_CASE(6) FFTMI_REAL_CASE(7) FFTMI_REAL_CASE(8)
+        FFTMI_REAL_CASE(9) FFTMI_REAL_CASE(10) FFTMI_REAL_CASE(11) FFTMI_REAL_CASE(12)
+        case 13:
+            if (prec == 0) return launch_real_rows_t<float2, 13>(c2r, in, out, nrows, tw, whi, wlo, s);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+#undef FFTMI_REAL_CASE
+}
+
+template <typename V>
+static hipError_t launch_real_pairs_t(bool c2r, const void* in, void* out, int64_t h, int64_t batch, BigTwiddle wn,
+                                      hipStream_t s)
+{
+    const int64_t npair = h / 2 + 1;
+    int64_t bx = (npair + 255) / 256;
+    if (bx > (1 << 16)) bx = 1 << 16;
+    const int64_t by = batch < 65535 ? batch : 65535;
+    const BigTw<V> bt{(const V*)wn.hi, (const V*)wn.lo, wn.lbits, wn.logn};
+    if (c2r)
+        hipLaunchKernelGGL(c2r_pairs_kernel<V>, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, s, (const V*)in,
+                           (V*)out, h, batch, bt);
+    else
+        hipLaunchKernelGGL(r2c_pairs_kernel<V>, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, s, (const V*)in,
+                           (V*)out, h, batch, bt);
+    return hipGetLastError();
+}
+
+hipError_t launch_real_pairs(int prec, bool c2r, const void* in, void* out, int64_t h, int64_t batch,
+                             BigTwiddle wn, hipStream_t s)
+{
+    if (h < 1 || batch < 1) return hipErrorInvalidValue;
+    return prec == 0 ? launch_real_pairs_t<float2>(c2r, in, out, h, batch, wn, s)
+                     : launch_real_pairs_t<double2>(c2r, in, out, h, batch, wn, s);
+}
+
+hipError_t launch_real_n1(int prec, bool c2r, const void* in, void* out, int64_t batch, hipStream_t s)
+{
+    int64_t blocks = (batch + 255) / 256;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
+    if (prec == 0)
+        hipLaunchKernelGGL(real_n1_kernel<float2>, dim3((unsigned)blocks), dim3(256), 0, s, in, out, batch, (int)c2r);
+    else
+        hipLaunchKernelGGL(real_n1_kernel<double2>, dim3((unsigned)blocks), dim3(256), 0, s, in, out, batch, (int)c2r);
+    return hipGetLastError();
+}
+
+}  // namespace fftmi

@@ -10,9 +10,6 @@
 
 namespace fftmi {
 
-// Rows per workgroup: at least 256 threads per workgroup.
-template <typename V, int LOGN> constexpr int rows_per_wg() { return Geom<V, LOGN>::T >= 256 ? 1 : 256 / Geom<V, LOGN>::T; }
-
 // One workgroup per group of RPW rows; the hardware dispatcher starts a new
 // workgroup as soon as one retires, so the load, compute and store phases of
 // the workgroups resident on a CU overlap.  (Measured on MI355X for 16384 rows

@@ -218,6 +218,9 @@ template <typename V, int LOGN> using Geom = Geometry<LOGN, lem_of<V>::value>;
 // Elements per thread, for array parameters.
 template <typename V, int LOGN> constexpr int kE = Geom<V, LOGN>::E;
 
+// Rows per workgroup of the row kernels: at least 256 threads per workgroup.
+template <typename V, int LOGN> constexpr int rows_per_wg() { return Geom<V, LOGN>::T >= 256 ? 1 : 256 / Geom<V, LOGN>::T; }
+
 template <typename V, int LOGN, int STAGE> struct StageInfo {
     using G = Geom<V, LOGN>;
     static constexpr int LEM = lem_of<V>::value;

@@ -19,6 +19,8 @@ stated):
 * ``random_polys`` -- pairs of integer polynomials with coefficients i.i.d.
   uniform in [0, 1000).  32 pairs of 2^18 coefficients (seed 5).
 * a 256^3 volume, re and im uniform [-1, 1) (seed 6), for the 3D transform.
+* ``real_normal`` -- real rows of N points, i.i.d. standard normal: the real
+  operands of the R2C / C2R transforms.  N = 8192 x 16384 rows (seed 7).
 """
 from __future__ import annotations
 
@@ -33,6 +35,8 @@ WORKLOADS = {
     "polymul_l262144_b32": dict(kind="polys", length=1 << 18, batch=32, seed=5),
     # 3D separable transform (beyond the five workloads above): one 256^3 volume.
     "c2c3d_256x256x256_b1": dict(kind="uniform3d", d=256, h=256, w=256, batch=1, seed=6),
+    # real rows, the R2C transform (512 MiB of float32 in)
+    "r2c_n8192_b16384": dict(kind="real_normal", n=8192, batch=16384, seed=7),
 }
 
 
@@ -68,6 +72,23 @@ def batched_normal(n: int, batch: int, seed: int, dtype=np.complex64,
     im = rng.standard_normal((batch, n), dtype=real_dt)
     if rows is not None:
         re, im = re[rows], im[rows]
+    return _complex_from_planes(re, im, dtype)
+
+
+def real_normal(n: int, batch: int, seed: int, dtype=np.float32) -> np.ndarray:
+    """[batch, n] real, i.i.d. standard normal."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((batch, n), dtype=np.dtype(dtype).type)
+
+
+def real_spectrum(n: int, batch: int, seed: int, dtype=np.complex64) -> np.ndarray:
+    """[batch, n // 2 + 1] complex, re then im i.i.d. standard normal: a half
+    spectrum for the C2R transform (its DC and Nyquist imaginary parts need
+    not be zero)."""
+    rng = np.random.default_rng(seed)
+    real_dt = np.float32 if np.dtype(dtype) == np.complex64 else np.float64
+    re = rng.standard_normal((batch, n // 2 + 1), dtype=real_dt)
+    im = rng.standard_normal((batch, n // 2 + 1), dtype=real_dt)
     return _complex_from_planes(re, im, dtype)
 
 
@@ -133,6 +154,8 @@ def workload_input(name: str, **overrides):
         return plane_waves_2d(spec["h"], spec["w"], spec["batch"], spec["seed"])
     if kind == "polys":
         return random_polys(spec["length"], spec["batch"], spec["seed"])
+    if kind == "real_normal":
+        return real_normal(spec["n"], spec["batch"], spec["seed"])
     if kind == "uniform3d":
         d, h, w = spec["d"], spec["h"], spec["w"]
         return batched_uniform(d * h * w, spec["batch"], spec["seed"]).reshape(spec["batch"], d, h, w)

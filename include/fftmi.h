@@ -60,7 +60,8 @@ enum fft_status {
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
-    FFT_ERR_RANK = -5,             /* plan rank differs from the call (exec_c2c: 1, exec_2d: 2, exec_3d: 3) */
+    FFT_ERR_RANK = -5,             /* plan rank or kind differs from the call (exec_c2c: 1,
+                                      exec_2d: 2, exec_3d: 3, exec_r2c/c2r: a real plan) */
     FFT_ERR_ALIGN = -6,            /* a pointer is not aligned to its element size */
     FFT_ERR_OVERLAP = -7,          /* buffers partially overlap (in == out is allowed) */
     FFT_ERR_WORKSPACE = -8,        /* workspace required but NULL, or overlapping data */
@@ -179,6 +180,45 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
 int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64_t* b,
                  int64_t lb, int64_t* c, int64_t batch, void* workspace,
                  double* d_max_residual, void* stream);
+
+/*
+ * Plan for transforms of real rows of N points (N a power of two,
+ * 1 <= N <= 2 * FFT_MAX_N_C32 (C32) / 2 * FFT_MAX_N_C64 (C64)).  The
+ * operands of polynomial multiplication are real ("FFT on GPU",
+ * polynomial-multiplication section); a real row's transform is fixed by
+ * its bins X_0 .. X_{N/2}, since X_{N-k} = conj X_k.  The row is read as N/2
+ * complex values and goes through the N/2-point complex transform, then one
+ * split step (and the reverse for C2R).  prec: FFT_C32 (float rows, complex64
+ * bins) or FFT_C64 (double rows, complex128 bins).  The plan serves only
+ * fft_exec_r2c / fft_exec_c2r (other calls give FFT_ERR_RANK);
+ * fft_workspace_size and fft_plan_describe accept it.
+ * Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE, DEVICE.
+ */
+int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
+
+/*
+ * Forward transform of real rows: out[b][k] = sum_n in[b][n] e^{-2 pi i k n / N},
+ * k = 0 .. N/2.
+ *   in:        [batch][N] real (float for C32, double for C64), rows contiguous.
+ *   out:       [batch][N/2 + 1] complex, rows contiguous.  in and out must not
+ *              overlap (FFT_ERR_OVERLAP); both aligned to the complex element
+ *              size (8 bytes C32, 16 bytes C64).
+ *   workspace: fft_workspace_size(plan, batch) bytes: none for N/2 <=
+ *              FFT_MAX_LDS_N_* (one kernel), batch * N/2 complex values beyond.
+ * Errors: INVALID_ARG, RANK, ALIGN, OVERLAP, WORKSPACE, DEVICE.
+ */
+int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream);
+
+/*
+ * Inverse: the real rows whose bins 0 .. N/2 are `in`, scaled by 1/N, so that
+ * c2r(r2c(x)) = x.  The imaginary parts of in[b][0] and in[b][N/2] are
+ * ignored (a real row has real values there); bins N/2 + 1 .. N - 1 are
+ * taken as conj in[b][N - k].
+ *   in:  [batch][N/2 + 1] complex;  out: [batch][N] real.  Not modified: in.
+ *   Layout, alignment, overlap and workspace as fft_exec_r2c.
+ * Errors: as fft_exec_r2c.
+ */
+int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char* fft_status_string(int status);

@@ -108,11 +108,37 @@ def test_valid_plan_without_gpu_is_a_device_error():
         assert "hipGetDevice" in fm.fft_last_error()
 
 
+@pytest.mark.parametrize("n,prec,status", [
+    (0, 0, fm.FFT_ERR_INVALID_ARG),
+    (-8, 0, fm.FFT_ERR_INVALID_ARG),
+    (8, 2, fm.FFT_ERR_INVALID_ARG),
+    (6, 0, fm.FFT_ERR_NOT_POW2),
+    (1000, 1, fm.FFT_ERR_NOT_POW2),
+    (1 << 28, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (1 << 26, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+])
+def test_real_plan_create_rejects(n, prec, status):
+    h = ctypes.c_void_p(12345)
+    assert fm.lib().fft_plan_create_real(ctypes.byref(h), n, prec) == status
+    assert h.value is None
+    assert fm.lib().fft_plan_create_real(None, 8, 0) == fm.FFT_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
+def test_valid_real_plan_without_gpu_is_a_device_error():
+    for n, prec in ((1, 0), (2, 1), (16384, 0), (1 << 27, 0), (1 << 25, 1)):
+        h = ctypes.c_void_p(12345)
+        assert fm.lib().fft_plan_create_real(ctypes.byref(h), n, prec) == fm.FFT_ERR_DEVICE
+        assert h.value is None
+
+
 def test_exec_and_queries_with_null_plan():
     L = fm.lib()
     assert L.fft_exec_c2c(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_exec_2d(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_exec_3d(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_exec_r2c(None, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_exec_c2r(None, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_poly_mul(None, None, 1, None, 1, None, 1, None, None, None) == fm.FFT_ERR_INVALID_ARG
     sz = ctypes.c_size_t()
     assert L.fft_workspace_size(None, 1, ctypes.byref(sz)) == fm.FFT_ERR_INVALID_ARG

@@ -1,0 +1,151 @@
+"""Transforms of real rows (R2C / C2R) against the fp64 oracle's rfft / irfft
+(GPU).  N/2 within the one-kernel range runs the fused kernels; longer rows run
+the N/2-point multi-pass transform plus the bin-pair pass.
+
+Bar: per-row relative RMS <= 1e-6 log2 N (float32 rows) / 1e-14 log2 N
+(float64 rows), the bound of the complex transform of the same length."""
+import numpy as np
+import pytest
+import torch
+
+import fft_convolution_amd as fm
+import oracle
+from fft_convolution_amd import workloads as wl
+
+from conftest import fft_tol, rel_rms_rows
+
+pytestmark = pytest.mark.gpu
+
+F32_FUSED = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14]
+F64_FUSED = [0, 1, 2, 3, 4, 5, 8, 11, 12, 13]
+
+
+def _run(logn, batch, dtype, seed):
+    n = 1 << logn
+    print("case n=%d batch=%d %s" % (n, batch, np.dtype(dtype).name), flush=True)
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    plan = fm.RealPlan(n, tdt)
+    x_np = wl.real_normal(n, batch, seed=seed, dtype=dtype)
+    x = torch.from_numpy(x_np).cuda()
+    X = plan.rfft(x).cpu().numpy()
+    tol = fft_tol(n, dtype == np.float64)
+    ref = oracle.rfft(x_np)
+    assert X.shape == (batch, n // 2 + 1)
+    assert rel_rms_rows(X, ref).max() <= tol, rel_rms_rows(X, ref).max()
+    # the inverse of an arbitrary half spectrum (DC / Nyquist imaginary parts ignored)
+    cdt = np.complex64 if dtype == np.float32 else np.complex128
+    S_np = wl.real_spectrum(n, batch, seed=seed + 1, dtype=cdt)
+    y = plan.irfft(torch.from_numpy(S_np).cuda()).cpu().numpy()
+    yref = oracle.irfft(S_np, n)
+    assert y.shape == (batch, n)
+    assert rel_rms_rows(y, yref).max() <= tol, rel_rms_rows(y, yref).max()
+    # round trip
+    back = plan.irfft(plan.rfft(x)).cpu().numpy()
+    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+    return plan
+
+
+@pytest.mark.parametrize("logn", F32_FUSED)
+def test_real_fused_f32(dev, logn):
+    plan = _run(logn, 3 if logn > 10 else 67, np.float32, 100 + logn)
+    assert ("fused" in plan.describe()) == (logn >= 1)
+
+
+@pytest.mark.parametrize("logn", F64_FUSED)
+def test_real_fused_f64(dev, logn):
+    plan = _run(logn, 3 if logn > 10 else 33, np.float64, 200 + logn)
+    assert ("fused" in plan.describe()) == (logn >= 1)
+
+
+@pytest.mark.parametrize("logn,batch", [(15, 3), (16, 2), (18, 2), (21, 1), (24, 1)])
+def test_real_pairs_f32(dev, logn, batch):
+    plan = _run(logn, batch, np.float32, 300 + logn)
+    assert "pairs" in plan.describe()
+
+
+@pytest.mark.parametrize("logn,batch", [(14, 3), (15, 2), (17, 1), (20, 1)])
+def test_real_pairs_f64(dev, logn, batch):
+    plan = _run(logn, batch, np.float64, 400 + logn)
+    assert "pairs" in plan.describe()
+
+
+@pytest.mark.parametrize("n", [64, 1 << 13, 1 << 16])
+def test_real_closed_forms(dev, n):
+    """cos(2 pi f t / N) -> N/2 at bin f; sin -> -i N/2; an impulse back from w^{3k}."""
+    t = np.arange(n)
+    plan = fm.RealPlan(n, torch.float64)
+    for f in (0, 1, n // 4 + 3, n // 2):
+        X = plan.rfft(torch.from_numpy(np.cos(2 * np.pi * f * t / n)[None, :]).cuda()).cpu().numpy()[0]
+        want = np.zeros(n // 2 + 1, dtype=complex)
+        want[f] = n if f in (0, n // 2) else n / 2
+        assert np.abs(X - want).max() < 1e-9 * n
+    k = np.arange(n // 2 + 1)
+    imp = plan.irfft(torch.from_numpy(np.exp(-2j * np.pi * 3 * k / n)[None, :]).cuda()).cpu().numpy()[0]
+    want = np.zeros(n)
+    want[3] = 1.0
+    assert np.abs(imp - want).max() < 1e-13
+
+
+def test_real_sampled_bins_at_full_size(dev):
+    """The real-row workload's shape (8192-point rows): 256 rows checked in full,
+    then sampled bins of rows across the whole batch by the direct DFT."""
+    spec = wl.WORKLOADS["r2c_n8192_b16384"]
+    n, batch = spec["n"], spec["batch"]
+    x_np = wl.real_normal(n, batch, seed=spec["seed"])
+    x = torch.from_numpy(x_np).cuda()
+    plan = fm.RealPlan(n, torch.float32)
+    X = plan.rfft(x).cpu().numpy()
+    rows = np.random.default_rng(0).choice(batch, 256, replace=False)
+    assert rel_rms_rows(X[rows], oracle.rfft(x_np[rows])).max() <= fft_tol(n)
+    ks = np.array([0, 1, 2, n // 4, n // 2 - 1, n // 2])
+    tail = np.arange(batch - 4, batch)
+    ref = oracle.dft_sample(x_np[tail].astype(np.complex128), ks)
+    scale = np.sqrt(np.mean(np.abs(X[tail]) ** 2, axis=1, keepdims=True))
+    assert (np.abs(X[tail][:, ks] - ref) / scale).max() <= 10 * fft_tol(n)
+    back = plan.irfft(torch.from_numpy(X).cuda()).cpu().numpy()
+    assert rel_rms_rows(back[rows], x_np[rows]).max() <= 2 * fft_tol(n)
+
+
+def test_real_errors_and_kinds(dev):
+    n = 1 << 16
+    rp = fm.RealPlan(n, torch.float32)
+    x = torch.zeros(2, n, device=dev)
+    X = torch.zeros(2, n // 2 + 1, dtype=torch.complex64, device=dev)
+    ws = torch.empty(fm.fft_workspace_size(rp.handle, 2), dtype=torch.uint8, device=dev)
+    assert ws.numel() == 2 * (n // 2) * 8
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_r2c(rp.handle, x, X, 2, None)
+    assert e.value.status == fm.FFT_ERR_WORKSPACE
+    # out overlapping in
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_r2c(rp.handle, x, x.data_ptr() + 8, 1, ws)
+    assert e.value.status == fm.FFT_ERR_OVERLAP
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_r2c(rp.handle, x.data_ptr() + 4, X, 1, ws)
+    assert e.value.status == fm.FFT_ERR_ALIGN
+    # plan kinds
+    cp = fm.Plan(n, torch.complex64)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_r2c(cp.handle, x, X, 1, ws)
+    assert e.value.status == fm.FFT_ERR_RANK
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_c2c(rp.handle, fm.FFT_FORWARD, X, X, 1, ws)
+    assert e.value.status == fm.FFT_ERR_RANK
+    rp64 = fm.RealPlan(1024, torch.float64)
+    a = torch.ones(1, 8, dtype=torch.int64, device=dev)
+    c = torch.empty(1, 15, dtype=torch.int64, device=dev)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul(rp64.handle, a, 8, a, 8, c, 1)
+    assert e.value.status == fm.FFT_ERR_RANK
+    # batch 0 is a no-op; fused plans need no workspace
+    fm.fft_exec_r2c(rp.handle, x, X, 0, None)
+    assert fm.fft_workspace_size(fm.RealPlan(1 << 14, torch.float32).handle, 5) == 0
+    assert fm.fft_workspace_size(fm.RealPlan(1 << 14, torch.float64).handle, 5) == 5 * (1 << 13) * 16
+    # input untouched by both directions
+    xr = torch.randn(3, 4096, device=dev)
+    x0 = xr.clone()
+    Y = fm.RealPlan(4096).rfft(xr)
+    Y0 = Y.clone()
+    fm.RealPlan(4096).irfft(Y)
+    torch.cuda.synchronize()
+    assert torch.equal(xr, x0) and torch.equal(Y, Y0)
