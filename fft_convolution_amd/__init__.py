@@ -29,7 +29,7 @@ __all__ = [
     "lib", "lib_path", "EXPORTS",
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
-    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r",
+    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar", "fft_planar_workspace_size",
     "fft_status_string", "fft_last_error",
     "Plan", "RealPlan", "poly_mul",
 ]
@@ -59,7 +59,7 @@ lib_path = os.path.join(_HERE, "libfftmi.so")
 EXPORTS = (
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
-    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r",
+    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar", "fft_planar_workspace_size",
     "fft_status_string", "fft_last_error",
 )
 
@@ -102,6 +102,8 @@ def lib():
         L.fft_plan_create_real.argtypes = [ctypes.POINTER(vp), i64, c_int]
         L.fft_exec_r2c.argtypes = [vp, vp, vp, i64, vp, vp]
         L.fft_exec_c2r.argtypes = [vp, vp, vp, i64, vp, vp]
+        L.fft_exec_planar.argtypes = [vp, c_int, vp, vp, vp, vp, i64, vp, vp]
+        L.fft_planar_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_status_string.argtypes = [c_int]
         L.fft_status_string.restype = ctypes.c_char_p
         L.fft_last_error.argtypes = []
@@ -219,6 +221,18 @@ def fft_exec_c2r(plan, in_, out, batch: int, workspace=None, stream=None) -> Non
            "fft_exec_c2r")
 
 
+def fft_exec_planar(plan, dir: int, in_re, in_im, out_re, out_im, batch: int, workspace=None,
+                    stream=None) -> None:
+    _check(lib().fft_exec_planar(plan, int(dir), _ptr(in_re), _ptr(in_im), _ptr(out_re), _ptr(out_im),
+                                 int(batch), _ptr(workspace), _stream(stream)), "fft_exec_planar")
+
+
+def fft_planar_workspace_size(plan, batch: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().fft_planar_workspace_size(plan, int(batch), ctypes.byref(out)), "fft_planar_workspace_size")
+    return out.value
+
+
 # --------------------------------------------------------------------------
 # Conveniences over torch tensors (allocation and shape checks only)
 # --------------------------------------------------------------------------
@@ -309,6 +323,28 @@ class Plan:
         if self.rank != 3:
             raise ValueError("ifft3 needs a rank-3 plan")
         return self._exec(x, out, FFT_INVERSE, fft_exec_3d)
+
+    def planar(self, re, im, inverse=False, out=None):
+        """The transform of re + i im, real and imaginary parts in separate
+        float32/float64 tensors of shape [..., *dims]; returns (out_re, out_im)."""
+        import torch
+        rdt = torch.float32 if self.dtype == torch.complex64 else torch.float64
+        for t in (re, im):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != rdt or not t.is_contiguous():
+                raise TypeError("re and im must be contiguous %s device tensors" % rdt)
+        if re.shape != im.shape or tuple(re.shape[-self.rank:]) != self.dims:
+            raise ValueError("re/im shapes %s %s do not match the plan %s" % (tuple(re.shape), tuple(im.shape),
+                                                                              self.dims))
+        n = 1
+        for d in self.dims:
+            n *= d
+        batch = re.numel() // n
+        if out is None:
+            out = (torch.empty_like(re), torch.empty_like(im))
+        nb = fft_planar_workspace_size(self.handle, batch)
+        ws = torch.empty(nb, dtype=torch.uint8, device=re.device) if nb else None
+        fft_exec_planar(self.handle, FFT_INVERSE if inverse else FFT_FORWARD, re, im, out[0], out[1], batch, ws)
+        return out
 
     def poly_mul(self, a, b, out=None, residual=False):
         """Products of the rows of int64 device tensors a [batch, la], b [batch, lb]."""

@@ -614,35 +614,46 @@ int fft_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
     return FFT_OK;
 }
 
-int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
-                 void* stream)
+// Rank-1 execution on validated arguments.  io.in_im / io.out_im non-NULL:
+// planar arrays; the multi-pass path then runs its middle passes through the
+// workspace (two signal-sized buffers for three passes) instead of `out`.
+static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s,
+                  void* stream)
 {
-    bool noop = false;
-    const size_t ws = plan && batch > 0 ? c2c_workspace(plan, batch) : 0;
-    int st = check_exec(plan, dir, 1, in, out, batch, workspace, ws, &noop);
-    if (st != FFT_OK || noop) return st;
-    if ((st = check_device(plan)) != FFT_OK) return st;
-
-    hipStream_t s = (hipStream_t)stream;
-    const bool inv = dir == FFT_INVERSE;
+    const bool planar = io.in_im != nullptr;
     const double scale = 1.0 / (double)plan->n;
     hipError_t e = hipSuccess;
+    int st = FFT_OK;
     switch (plan->path) {
-        case PATH_COPY:
-            if (in != out) e = hipMemcpyAsync(out, in, (size_t)batch * plan->elem, hipMemcpyDeviceToDevice, s);
+        case PATH_COPY: {
+            const size_t bytes = (size_t)batch * plan->elem;
+            if (!planar) {
+                if (io.in != io.out) e = hipMemcpyAsync(io.out, io.in, bytes, hipMemcpyDeviceToDevice, s);
+            } else if (io.in != io.out || io.in_im != io.out_im) {
+                e = hipMemcpyAsync(io.out, io.in, bytes / 2, hipMemcpyDeviceToDevice, s);
+                if (e == hipSuccess) e = hipMemcpyAsync(io.out_im, io.in_im, bytes / 2, hipMemcpyDeviceToDevice, s);
+            }
             break;
+        }
         case PATH_ROWS:
-            e = launch_rows(plan->prec, plan->log_a, inv, inv, in, out, batch, plan->tw_a, scale, s);
+            e = launch_rows(plan->prec, plan->log_a, inv, inv, io.in, io.out, batch, plan->tw_a, scale, s, io.in_im,
+                            io.out_im);
             break;
         case PATH_MULTIPASS: {
-            // in -> ws -> out (two passes) or in -> ws -> out -> out (three, the last in place).
-            const void* src = in;
+            // Interleaved: in -> ws -> out (two passes) or in -> ws -> out -> out
+            // (three, the last in place).  Planar: in -> ws -> out, or
+            // in -> ws -> ws2 -> out.
+            const size_t sig = (size_t)batch * (size_t)plan->n * plan->elem;
+            void* ws2 = (char*)workspace + sig;
+            const void* src = io.in;
             for (int q = 0; q < plan->npass && e == hipSuccess; ++q) {
                 const PassPlan& pp = plan->passes[q];
-                void* dst = q == 0 ? workspace : out;
+                const bool last = q == plan->npass - 1;
+                void* dst = q == 0 ? workspace : (last || !planar) ? io.out : ws2;
                 const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, pp.logns + pp.logr};
                 e = launch_stock_pass(plan->prec, pp.logr, pp.kind, src, dst, plan->logn, pp.logns, batch, pp.tw, big,
-                                      inv && q == 0, inv && q == plan->npass - 1, scale, s);
+                                      inv && q == 0, inv && last, scale, s, q == 0 ? io.in_im : nullptr,
+                                      last ? io.out_im : nullptr);
                 src = dst;
             }
             break;
@@ -651,7 +662,7 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
             // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
             void* w = workspace;
             void* inner_ws = (char*)workspace + ((size_t)batch << plan->logm) * plan->elem;
-            e = launch_chirp_pre(plan->prec, in, w, plan->n, plan->logm, batch, plan->chirp, inv, s);
+            e = launch_chirp_pre(plan->prec, io.in, w, plan->n, plan->logm, batch, plan->chirp, inv, s, io.in_im);
             if (e != hipSuccess) break;
             st = fft_exec_c2c(plan->inner, FFT_FORWARD, w, w, batch, inner_ws, stream);
             if (st != FFT_OK) return st;
@@ -659,17 +670,95 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
             if (e != hipSuccess) break;
             st = fft_exec_c2c(plan->inner, FFT_INVERSE, w, w, batch, inner_ws, stream);
             if (st != FFT_OK) return st;
-            e = launch_chirp_post(plan->prec, w, out, plan->n, plan->logm, batch, plan->chirp, inv, scale, s);
+            e = launch_chirp_post(plan->prec, w, io.out, plan->n, plan->logm, batch, plan->chirp, inv, scale, s,
+                                  io.out_im);
             break;
         }
         default:
             return fail(FFT_ERR_RANK, "plan path is not rank 1");
     }
-    if (e != hipSuccess) return hip_fail(e, "fft_exec_c2c launch");
+    if (e != hipSuccess) return hip_fail(e, "rank-1 transform launch");
+    return FFT_OK;
+}
+
+static int sync_if_asked(hipStream_t s, const char* what)
+{
     if (getenv("FFTMI_SYNC")) {
-        e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return hip_fail(e, "fft_exec_c2c (FFTMI_SYNC)");
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, what);
     }
+    return FFT_OK;
+}
+
+int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
+                 void* stream)
+{
+    bool noop = false;
+    const size_t ws = plan && batch > 0 ? c2c_workspace(plan, batch) : 0;
+    int st = check_exec(plan, dir, 1, in, out, batch, workspace, ws, &noop);
+    if (st != FFT_OK || noop) return st;
+    if ((st = check_device(plan)) != FFT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const Io io{in, nullptr, out, nullptr};
+    st = run_1d(plan, dir == FFT_INVERSE, io, batch, workspace, s, stream);
+    if (st != FFT_OK) return st;
+    return sync_if_asked(s, "fft_exec_c2c (FFTMI_SYNC)");
+}
+
+// Rank-2/3 execution on validated arguments.  Interleaved: the intermediate
+// lives in `out` (in the workspace for an in-place folded call).  Planar: the
+// first pass reads the caller's planes into the workspace, later passes run
+// there, the last writes the caller's planes.
+static int run_nd(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s)
+{
+    const bool planar = io.in_im != nullptr;
+    const double scale = 1.0 / (double)plan->n;
+    const int k = plan->nd_k;
+    const BigTwiddle none{nullptr, nullptr, 0, 0};
+    hipError_t e = hipSuccess;
+    if (k == 0) {
+        const size_t bytes = (size_t)batch * plan->elem;
+        if (!planar) {
+            if (io.in != io.out) e = hipMemcpyAsync(io.out, io.in, bytes, hipMemcpyDeviceToDevice, s);
+        } else if (io.in != io.out || io.in_im != io.out_im) {
+            e = hipMemcpyAsync(io.out, io.in, bytes / 2, hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess) e = hipMemcpyAsync(io.out_im, io.in_im, bytes / 2, hipMemcpyDeviceToDevice, s);
+        }
+    } else if (k == 1) {
+        e = launch_rows(plan->prec, plan->log_a, inv, inv, io.in, io.out, batch, plan->tw_a, scale, s, io.in_im,
+                        io.out_im);
+    } else {
+        // innermost axis (rows) + next axis (columns of stride W); the first
+        // pass conjugates the input, the last conjugates and scales the output.
+        const int64_t w = int64_t(1) << plan->log_a;
+        const int logh = plan->log_b + plan->logf;
+        const int64_t nimg = batch * (plan->n >> (plan->log_a + logh));
+        const bool last2 = k == 2;
+        // where the column pass writes: the caller's array when it is the last
+        void* col_out = planar ? (last2 ? io.out : workspace) : io.out;
+        void* col_out_im = planar && last2 ? io.out_im : nullptr;
+        if (plan->logf == 0) {
+            void* mid = planar ? workspace : io.out;
+            e = launch_rows(plan->prec, plan->log_a, inv, false, io.in, mid, nimg << logh, plan->tw_a, 1.0, s,
+                            io.in_im, nullptr);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, mid, col_out, nimg, w, 0, plan->tw_b, none, inv && last2,
+                                  last2 ? scale : 1.0, s, col_out_im);
+        } else {
+            void* mid = planar || io.in == io.out ? workspace : io.out;
+            const BigTwiddle hb{plan->big_hi, plan->big_lo, plan->big_lbits, logh};
+            e = launch_rows2d_fold(plan->prec, plan->log_a, plan->logf, io.in, mid, nimg, plan->log_b, plan->tw_a, inv,
+                                   s, io.in_im);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, mid, col_out, nimg, w, plan->logf, plan->tw_b, hb,
+                                  inv && last2, last2 ? scale : 1.0, s, col_out_im);
+        }
+        // outer axis of three: columns of stride H W, in place (or into the planes)
+        if (e == hipSuccess && k == 3)
+            e = launch_cols2d(plan->prec, plan->eff_log[0], col_out, io.out, batch, w << logh, 0, plan->tw_c, none,
+                              inv, scale, s, io.out_im);
+    }
+    if (e != hipSuccess) return hip_fail(e, "multi-dimensional transform launch");
     return FFT_OK;
 }
 
@@ -681,49 +770,10 @@ static int exec_nd(const fft_plan* plan, int rank, const char* what, int dir, co
     int st = check_exec(plan, dir, rank, in, out, batch, workspace, ws, &noop);
     if (st != FFT_OK || noop) return st;
     if ((st = check_device(plan)) != FFT_OK) return st;
-
     hipStream_t s = (hipStream_t)stream;
-    const bool inv = dir == FFT_INVERSE;
-    const double scale = 1.0 / (double)plan->n;
-    const int k = plan->nd_k;
-    const BigTwiddle none{nullptr, nullptr, 0, 0};
-    hipError_t e = hipSuccess;
-    if (k == 0) {
-        if (in != out) e = hipMemcpyAsync(out, in, (size_t)batch * plan->elem, hipMemcpyDeviceToDevice, s);
-    } else if (k == 1) {
-        e = launch_rows(plan->prec, plan->log_a, inv, inv, in, out, batch, plan->tw_a, scale, s);
-    } else {
-        // innermost axis (rows) + next axis (columns of stride W); the first
-        // pass conjugates the input, the last conjugates and scales the output.
-        const int64_t w = int64_t(1) << plan->log_a;
-        const int logh = plan->log_b + plan->logf;
-        const int64_t nimg = batch * (plan->n >> (plan->log_a + logh));
-        const bool last2 = k == 2;
-        if (plan->logf == 0) {
-            e = launch_rows(plan->prec, plan->log_a, inv, false, in, out, nimg << logh, plan->tw_a, 1.0, s);
-            if (e == hipSuccess)
-                e = launch_cols2d(plan->prec, plan->log_b, out, out, nimg, w, 0, plan->tw_b, none, inv && last2,
-                                  last2 ? scale : 1.0, s);
-        } else {
-            void* mid = in == out ? workspace : out;
-            const BigTwiddle hb{plan->big_hi, plan->big_lo, plan->big_lbits, logh};
-            e = launch_rows2d_fold(plan->prec, plan->log_a, plan->logf, in, mid, nimg, plan->log_b, plan->tw_a, inv,
-                                   s);
-            if (e == hipSuccess)
-                e = launch_cols2d(plan->prec, plan->log_b, mid, out, nimg, w, plan->logf, plan->tw_b, hb,
-                                  inv && last2, last2 ? scale : 1.0, s);
-        }
-        // outer axis of three: columns of stride H W, in place
-        if (e == hipSuccess && k == 3)
-            e = launch_cols2d(plan->prec, plan->eff_log[0], out, out, batch, w << logh, 0, plan->tw_c, none, inv,
-                              scale, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, what);
-    if (getenv("FFTMI_SYNC")) {
-        e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return hip_fail(e, what);
-    }
-    return FFT_OK;
+    st = run_nd(plan, dir == FFT_INVERSE, Io{in, nullptr, out, nullptr}, batch, workspace, s);
+    if (st != FFT_OK) return st;
+    return sync_if_asked(s, what);
 }
 
 int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* workspace,
@@ -736,6 +786,68 @@ int fft_exec_3d(const fft_plan* plan, int dir, const void* in, void* out, int64_
                 void* stream)
 {
     return exec_nd(plan, 3, "fft_exec_3d", dir, in, out, batch, workspace, stream);
+}
+
+// Workspace of a planar call: the interleaved intermediates the multi-kernel
+// paths keep between their first (planar-reading) and last (planar-writing) pass.
+static size_t planar_workspace(const fft_plan* p, int64_t batch)
+{
+    const size_t sig = (size_t)batch * (size_t)p->n * p->elem;
+    switch (p->path) {
+        case PATH_MULTIPASS: return p->npass >= 3 ? 2 * sig : sig;
+        case PATH_BLUESTEIN: return c2c_workspace(p, batch);
+        case PATH_ND: return p->nd_k >= 2 ? sig : 0;
+        default: return 0;
+    }
+}
+
+int fft_planar_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
+{
+    if (!plan || !bytes) return fail(FFT_ERR_INVALID_ARG, "plan or bytes is NULL");
+    if (plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "plan is for real rows");
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
+    if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
+    *bytes = planar_workspace(plan, batch);
+    return FFT_OK;
+}
+
+int fft_exec_planar(const fft_plan* plan, int dir, const void* in_re, const void* in_im, void* out_re, void* out_im,
+                    int64_t batch, void* workspace, void* stream)
+{
+    if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "plan is for real rows: use fft_exec_r2c / fft_exec_c2r");
+    if (dir != FFT_FORWARD && dir != FFT_INVERSE) return fail(FFT_ERR_INVALID_ARG, "dir %d is not FFT_FORWARD/FFT_INVERSE", dir);
+    if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch %lld < 0", (long long)batch);
+    if (batch == 0) return FFT_OK;
+    if (!in_re || !in_im || !out_re || !out_im) return fail(FFT_ERR_INVALID_ARG, "a plane pointer is NULL");
+    if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem))
+        return fail(FFT_ERR_INVALID_ARG, "batch %lld overflows the buffer size", (long long)batch);
+    if (((uintptr_t)in_re | (uintptr_t)in_im | (uintptr_t)out_re | (uintptr_t)out_im) % 8)
+        return fail(FFT_ERR_ALIGN, "planes must be 8-byte aligned");
+    const size_t pb = (size_t)batch * (size_t)plan->n * (plan->elem / 2);  // bytes per plane
+    if (ranges_overlap(in_re, pb, in_im, pb) || ranges_overlap(out_re, pb, out_im, pb))
+        return fail(FFT_ERR_OVERLAP, "the re and im planes of one array overlap");
+    const bool in_place = in_re == out_re && in_im == out_im;
+    if (!in_place && (ranges_overlap(in_re, pb, out_re, pb) || ranges_overlap(in_re, pb, out_im, pb) ||
+                      ranges_overlap(in_im, pb, out_re, pb) || ranges_overlap(in_im, pb, out_im, pb)))
+        return fail(FFT_ERR_OVERLAP, "input and output planes overlap (only in_re == out_re and in_im == out_im "
+                                     "is allowed)");
+    const size_t ws = planar_workspace(plan, batch);
+    if (ws) {
+        if (!workspace) return fail(FFT_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
+        if ((uintptr_t)workspace % plan->elem) return fail(FFT_ERR_ALIGN, "workspace misaligned");
+        const void* planes[4] = {in_re, in_im, out_re, out_im};
+        for (const void* q : planes)
+            if (ranges_overlap(workspace, ws, q, pb)) return fail(FFT_ERR_WORKSPACE, "workspace overlaps a plane");
+    }
+    int st = check_device(plan);
+    if (st != FFT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const Io io{in_re, in_im, out_re, out_im};
+    const bool inv = dir == FFT_INVERSE;
+    st = plan->rank == 1 ? run_1d(plan, inv, io, batch, workspace, s, stream) : run_nd(plan, inv, io, batch, workspace, s);
+    if (st != FFT_OK) return st;
+    return sync_if_asked(s, "fft_exec_planar (FFTMI_SYNC)");
 }
 
 int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)

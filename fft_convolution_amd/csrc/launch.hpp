@@ -26,30 +26,49 @@ int tile_lines_2d(int prec, int logl);
 // Whether the folded 2D row pass exists for rows of 2^logw points and fold 2^logf.
 bool fold_supported(int prec, int logw, int logf);
 
+// The arrays of a launch: `in` / `out` are interleaved complex arrays, or,
+// with in_im / out_im non-NULL, the real-part planes of planar arrays whose
+// imaginary parts are at in_im / out_im (same indexing, one real per element).
+struct Io {
+    const void* in;
+    const void* in_im;
+    void* out;
+    void* out_im;
+};
+
 // Rows kernel: `nrows` contiguous rows of 2^logn points, in -> out (may alias).
 // conj_in conjugates on load; conj_out conjugates and multiplies by `scale` on store.
+// Planar in and out need conj_in == conj_out; planar in with interleaved out
+// needs conj_out false.
 hipError_t launch_rows(int prec, int logn, bool conj_in, bool conj_out, const void* in, void* out,
-                       int64_t nrows, const void* tw, double scale, hipStream_t stream);
+                       int64_t nrows, const void* tw, double scale, hipStream_t stream,
+                       const void* in_im = nullptr, void* out_im = nullptr);
 
 // 2D column pass over `nimg` images [H][w], H = 2^(logf + logl): lines are
 // (column, j'), j' < 2^logf, with points at rows j' + 2^logf r; when logf > 0
 // point r of line j' is first multiplied by w_H^{r j'} (htw: tables for H).
 // in -> out, may alias.  conj_out conjugates and multiplies by `scale`.
+// out_im non-NULL: planar output (see Io).
 hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t nimg, int64_t w, int logf,
-                         const void* tw, BigTwiddle htw, bool conj_out, double scale, hipStream_t stream);
+                         const void* tw, BigTwiddle htw, bool conj_out, double scale, hipStream_t stream,
+                         void* out_im = nullptr);
 
 // 2D row pass with the radix-2^logf column super-stage folded in: rows of
 // 2^logw points; image rows j + r Lc (r < 2^logf, Lc = 2^log_lc) are
 // transformed and combined into rows j 2^logf + r.  in -> out, must not alias.
+// in_im non-NULL: planar input (see Io).
 hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,
-                              const void* tw, bool conj_in, hipStream_t stream);
+                              const void* tw, bool conj_in, hipStream_t stream, const void* in_im = nullptr);
 
 // One super-stage pass of a multi-pass Stockham transform of `batch` signals
 // of 2^logn points: radix 2^logr, span 2^logns; kind 0 first, 1 middle, 2
 // last (in place allowed).  big: tables for w_M, M = 2^(logns + logr).
+// Planar (see Io): in_im only for kind 0 (conj_out false), out_im only for
+// kind 2 (conj_in false).
 hipError_t launch_stock_pass(int prec, int logr, int kind, const void* in, void* out, int logn, int logns,
                              int64_t batch, const void* tw, BigTwiddle big, bool conj_in, bool conj_out,
-                             double scale, hipStream_t stream);
+                             double scale, hipStream_t stream, const void* in_im = nullptr,
+                             void* out_im = nullptr);
 
 // Polynomial products, N = 2^logn <= LDS range: one fused kernel per row pair.
 hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int64_t* b, int64_t lb,
@@ -68,10 +87,11 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
 
 // Bluestein element-wise steps (bluestein.hip): rows of n points padded to 2^logm.
 hipError_t launch_chirp_pre(int prec, const void* in, void* w, int64_t n, int logm, int64_t batch, const void* chirp,
-                            bool conj_in, hipStream_t stream);
+                            bool conj_in, hipStream_t stream, const void* in_im = nullptr);
 hipError_t launch_cmul_table(int prec, void* w, int logm, int64_t batch, const void* tab, hipStream_t stream);
 hipError_t launch_chirp_post(int prec, const void* w, void* out, int64_t n, int logm, int64_t batch,
-                             const void* chirp, bool conj_out, double scale, hipStream_t stream);
+                             const void* chirp, bool conj_out, double scale, hipStream_t stream,
+                             void* out_im = nullptr);
 // complex128 -> complex64, `total` elements.
 hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t stream);
 

@@ -5,6 +5,7 @@
 // coalesced global write ("Stockham FFT Butterfly Algorithm in Parallel
 // GLSL", section "Performance and Pipeline Evaluation": stages batched in
 // on-chip memory instead of one global round trip per stage).
+#include "io.hpp"
 #include "launch.hpp"
 #include "stockham.hpp"
 
@@ -15,9 +16,9 @@ namespace fftmi {
 // the workgroups resident on a CU overlap.  (Measured on MI355X for 16384 rows
 // of 4096 points: this beats a persistent grid with a one-row register
 // prefetch, 174 us against 187-201 us per launch.)
-template <typename V, int LOGN, bool CONJ_IN, bool CONJ_OUT>
+template <typename V, int LOGN, bool CONJ_IN, bool CONJ_OUT, bool PIN, bool POUT>
 __global__ __launch_bounds__((Geom<V, LOGN>::T * rows_per_wg<V, LOGN>()))
-void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
+void rows_kernel(CIn<V, PIN> in, COut<V, POUT> out, int64_t nrows, const V* __restrict__ tw,
                  typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGN>;
@@ -34,60 +35,73 @@ void rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ tw,
     tb.load(tw, t);
 
     V v[G::E];
-    const V* src = in + row * G::N + t;
+    const int64_t base = row * G::N + t;
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
-        const V x = live ? ld_stream(src + i * G::T) : V{0, 0};
+        const V x = live ? in.ld(base + i * G::T) : V{0, 0};
         v[i] = CONJ_IN ? cconj(x) : x;
     }
     fft_regs<LOGN>(v, t, tb, LdsLines<V, 1>{lds + rloc * G::LDS, 0});
     if (live) {
-        V* dst = out + row * G::N + t;
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
             const V y = v[i];
-            st_stream(dst + i * G::T, CONJ_OUT ? V{y.x * scale, -y.y * scale} : y);
+            out.st(base + i * G::T, CONJ_OUT ? V{y.x * scale, -y.y * scale} : y);
         }
     }
 }
 
-template <typename V, int LOGN, bool CI, bool CO>
-static hipError_t launch_rows_t(const void* in, void* out, int64_t nrows, const void* tw, double scale,
-                                hipStream_t stream)
+template <typename V, int LOGN, bool CI, bool CO, bool PIN, bool POUT>
+static hipError_t launch_rows_t(const Io& io, int64_t nrows, const void* tw, double scale, hipStream_t stream)
 {
     constexpr int RPW = rows_per_wg<V, LOGN>();
     constexpr int BLOCK = Geom<V, LOGN>::T * RPW;
     const int64_t blocks = (nrows + RPW - 1) / RPW;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
-    hipLaunchKernelGGL((rows_kernel<V, LOGN, CI, CO>), dim3((unsigned)blocks), dim3(BLOCK), 0, stream,
-                       (const V*)in, (V*)out, nrows, (const V*)tw, (Rl)scale);
+    hipLaunchKernelGGL((rows_kernel<V, LOGN, CI, CO, PIN, POUT>), dim3((unsigned)blocks), dim3(BLOCK), 0, stream,
+                       make_in<V, PIN>(io.in, io.in_im), make_out<V, POUT>(io.out, io.out_im), nrows,
+                       (const V*)tw, (Rl)scale);
     return hipGetLastError();
 }
 
+// Interleaved in and out: every conjugation pattern.  Planar in and out: the
+// 1D transform (conj on both sides or neither).  Planar in, interleaved out:
+// the first pass of a multi-dimensional transform (no conj on the store).
 template <typename V, int LOGN>
-static hipError_t launch_rows_dir(bool ci, bool co, const void* in, void* out, int64_t nrows,
-                                  const void* tw, double scale, hipStream_t s)
+static hipError_t launch_rows_dir(bool ci, bool co, const Io& io, int64_t nrows, const void* tw, double scale,
+                                  hipStream_t s)
 {
-    if (!ci && !co) return launch_rows_t<V, LOGN, false, false>(in, out, nrows, tw, scale, s);
-    if (ci && co) return launch_rows_t<V, LOGN, true, true>(in, out, nrows, tw, scale, s);
-    if (ci) return launch_rows_t<V, LOGN, true, false>(in, out, nrows, tw, scale, s);
-    return launch_rows_t<V, LOGN, false, true>(in, out, nrows, tw, scale, s);
+    const bool pin = io.in_im != nullptr, pout = io.out_im != nullptr;
+    if (!pin && !pout) {
+        if (!ci && !co) return launch_rows_t<V, LOGN, false, false, false, false>(io, nrows, tw, scale, s);
+        if (ci && co) return launch_rows_t<V, LOGN, true, true, false, false>(io, nrows, tw, scale, s);
+        if (ci) return launch_rows_t<V, LOGN, true, false, false, false>(io, nrows, tw, scale, s);
+        return launch_rows_t<V, LOGN, false, true, false, false>(io, nrows, tw, scale, s);
+    }
+    if (pin && pout && ci == co)
+        return ci ? launch_rows_t<V, LOGN, true, true, true, true>(io, nrows, tw, scale, s)
+                  : launch_rows_t<V, LOGN, false, false, true, true>(io, nrows, tw, scale, s);
+    if (pin && !pout && !co)
+        return ci ? launch_rows_t<V, LOGN, true, false, true, false>(io, nrows, tw, scale, s)
+                  : launch_rows_t<V, LOGN, false, false, true, false>(io, nrows, tw, scale, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_rows(int prec, int logn, bool ci, bool co, const void* in, void* out, int64_t nrows,
-                       const void* tw, double scale, hipStream_t s)
+                       const void* tw, double scale, hipStream_t s, const void* in_im, void* out_im)
 {
+    const Io io{in, in_im, out, out_im};
 #define FFTMI_ROW_CASE(L) \
-    case L: return prec == 0 ? launch_rows_dir<float2, L>(ci, co, in, out, nrows, tw, scale, s) \
-                             : launch_rows_dir<double2, L>(ci, co, in, out, nrows, tw, scale, s);
+    case L: return prec == 0 ? launch_rows_dir<float2, L>(ci, co, io, nrows, tw, scale, s) \
+                             : launch_rows_dir<double2, L>(ci, co, io, nrows, tw, scale, s);
     if (prec == 1 && logn > 12) return hipErrorInvalidValue;
     switch (logn) {
         FFTMI_ROW_CASE(1) FFTMI_ROW_CASE(2) FFTMI_ROW_CASE(3) FFTMI_ROW_CASE(4)
         FFTMI_ROW_CASE(5) FFTMI_ROW_CASE(6) FFTMI_ROW_CASE(7) FFTMI_ROW_CASE(8)
         FFTMI_ROW_CASE(9) FFTMI_ROW_CASE(10) FFTMI_ROW_CASE(11) FFTMI_ROW_CASE(12)
         case 13:
-            if (prec == 0) return launch_rows_dir<float2, 13>(ci, co, in, out, nrows, tw, scale, s);
+            if (prec == 0) return launch_rows_dir<float2, 13>(ci, co, io, nrows, tw, scale, s);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }

@@ -24,6 +24,7 @@
 // super-stage writes the positions it reads (in place); the first writes each
 // butterfly's R outputs contiguously, so it hands the data from lanes-across-
 // lines to lanes-along-a-line inside its LDS exchange (fft_regs_remap).
+#include "io.hpp"
 #include "launch.hpp"
 #include "stockham.hpp"
 #include "tile_common.hpp"
@@ -34,9 +35,9 @@ namespace fftmi {
 // 2D column pass: lines (column, j') of [H][W] images, H = F Lc, line points
 // at rows j' + F r (r < Lc); in place allowed.
 // ---------------------------------------------------------------------------
-template <typename V, int LOGL, bool CONJ_OUT>
+template <typename V, int LOGL, bool CONJ_OUT, bool POUT>
 __global__ __launch_bounds__((Tile<V, LOGL>::THREADS))
-void cols2d_kernel(const V* in, V* out, int64_t w, int logf, int64_t col_tiles, const V* __restrict__ tw,
+void cols2d_kernel(const V* in, COut<V, POUT> out, int64_t w, int logf, int64_t col_tiles, const V* __restrict__ tw,
                    BigTw<V> htw, typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGL>;
@@ -85,7 +86,7 @@ void cols2d_kernel(const V* in, V* out, int64_t w, int logf, int64_t col_tiles, 
                 const V y = v[g][i];
                 q[g] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
             }
-            vstore(out + base + i * step, q);
+            out.stv(base + i * step, q);
         }
     }
 }
@@ -102,9 +103,9 @@ template <typename V, int LOGW, int LOGF> constexpr int fold_groups()
     return (Geom<V, LOGW>::T << LOGF) >= 256 ? 1 : 256 / (Geom<V, LOGW>::T << LOGF);
 }
 
-template <typename V, int LOGW, int LOGF, bool CONJ_IN>
+template <typename V, int LOGW, int LOGF, bool CONJ_IN, bool PIN>
 __global__ __launch_bounds__(((Geom<V, LOGW>::T << LOGF) * fold_groups<V, LOGW, LOGF>()))
-void rows2d_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* __restrict__ tw)
+void rows2d_fold_kernel(CIn<V, PIN> in, V* out, int64_t ngroups, int log_lc, const V* __restrict__ tw)
 {
     using G = Geom<V, LOGW>;
     constexpr int F = 1 << LOGF;
@@ -127,10 +128,10 @@ void rows2d_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const 
     TwBases<V, LOGW> tb;
     tb.load(tw, t);
     V v[G::E];
-    const V* src = in + ((img * h + j + rho * lc) << LOGW) + t;
+    const int64_t src = ((img * h + j + rho * lc) << LOGW) + t;
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
-        const V x = live ? ld_stream(src + i * G::T) : V{0, 0};
+        const V x = live ? in.ld(src + i * G::T) : V{0, 0};
         v[i] = CONJ_IN ? cconj(x) : x;
     }
     const LdsLines<V, 1> L{my + rho * SLOTS, 0};
@@ -161,10 +162,11 @@ void rows2d_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const 
 // Multi-pass Stockham super-stage (large 1D).  KIND 0: first (span 1, stored
 // along lines after a remap), 1: middle, 2: last (in place).
 // ---------------------------------------------------------------------------
-template <typename V, int LOGR, int KIND, bool CONJ_IN, bool CONJ_OUT>
+template <typename V, int LOGR, int KIND, bool CONJ_IN, bool CONJ_OUT, bool PL>
 __global__ __launch_bounds__((Tile<V, LOGR>::THREADS))
-void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_per_sig, const V* __restrict__ tw,
-                       BigTw<V> big, typename real_of<V>::type scale)
+void stock_pass_kernel(CIn<V, PL && KIND == 0> in, COut<V, PL && KIND == 2> out, int logn, int logns,
+                       int64_t tiles_per_sig, const V* __restrict__ tw, BigTw<V> big,
+                       typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGR>;
     using TL = Tile<V, LOGR>;
@@ -180,11 +182,11 @@ void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_p
 
     V v[TL::P][G::E];
     {
-        const V* src = in + sbase + j + t * stride;
+        const int64_t src = sbase + j + t * stride;
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
             V q[TL::P];
-            vload(src + i * G::T * stride, q);
+            in.ldv(src + i * G::T * stride, q);
 #pragma unroll
             for (int g = 0; g < TL::P; ++g) v[g][i] = CONJ_IN ? cconj(q[g]) : q[g];
         }
@@ -207,9 +209,9 @@ void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_p
         }
 #pragma unroll
         for (int g = 0; g < TL::P; ++g) {
-            V* dst = out + sbase + ((j0 + cb * TL::P + g) << LOGR) + tb_t;
+            const int64_t dst = sbase + ((j0 + cb * TL::P + g) << LOGR) + tb_t;
 #pragma unroll
-            for (int i = 0; i < G::E; ++i) dst[i * G::T] = v[g][i];
+            for (int i = 0; i < G::E; ++i) out.st_plain(dst + i * G::T, v[g][i]);
         }
     } else {
         TwBases<V, LOGR> tb;
@@ -220,7 +222,7 @@ void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_p
             fft_regs<LOGR>(v[g], t, tb, LdsLines<V, TL::CL>{lds, c0});
         }
         const int64_t ns = (int64_t)1 << logns;
-        V* dst = out + sbase + ((j >> logns) << (logns + LOGR)) + (j & ns_mask) + t * ns;
+        const int64_t dst = sbase + ((j >> logns) << (logns + LOGR)) + (j & ns_mask) + t * ns;
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
             V q[TL::P];
@@ -229,7 +231,7 @@ void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_p
                 const V y = v[g][i];
                 q[g] = CONJ_OUT ? V{y.x * scale, -y.y * scale} : y;
             }
-            vstore(dst + i * G::T * ns, q);
+            out.stv(dst + i * G::T * ns, q);
         }
     }
 }
@@ -240,8 +242,8 @@ void stock_pass_kernel(const V* in, V* out, int logn, int logns, int64_t tiles_p
 static inline dim3 grid_of(int64_t blocks) { return dim3((unsigned)blocks); }
 
 template <typename V, int LOGL>
-static hipError_t cols2d_t(const void* in, void* out, int64_t nimg, int64_t w, int logf, const void* tw,
-                           BigTwiddle htw, bool co, double scale, hipStream_t s)
+static hipError_t cols2d_t(const void* in, void* out, void* out_im, int64_t nimg, int64_t w, int logf,
+                           const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s)
 {
     using TL = Tile<V, LOGL>;
     if (TL::THREADS > 1024) return hipErrorInvalidValue;
@@ -250,12 +252,17 @@ static hipError_t cols2d_t(const void* in, void* out, int64_t nimg, int64_t w, i
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
     const BigTw<V> big{(const V*)htw.hi, (const V*)htw.lo, htw.lbits, htw.logn};
-    if (co)
-        hipLaunchKernelGGL((cols2d_kernel<V, LOGL, true>), grid_of(blocks), dim3(TL::THREADS), 0, s, (const V*)in,
-                           (V*)out, w, logf, col_tiles, (const V*)tw, big, (Rl)scale);
-    else
-        hipLaunchKernelGGL((cols2d_kernel<V, LOGL, false>), grid_of(blocks), dim3(TL::THREADS), 0, s, (const V*)in,
-                           (V*)out, w, logf, col_tiles, (const V*)tw, big, (Rl)scale);
+#define FFTMI_C2(CO, PO)                                                                                      \
+    hipLaunchKernelGGL((cols2d_kernel<V, LOGL, CO, PO>), grid_of(blocks), dim3(TL::THREADS), 0, s, (const V*)in, \
+                       make_out<V, PO>(out, out_im), w, logf, col_tiles, (const V*)tw, big, (Rl)scale)
+    if (out_im) {
+        if (co) FFTMI_C2(true, true);
+        else FFTMI_C2(false, true);
+    } else {
+        if (co) FFTMI_C2(true, false);
+        else FFTMI_C2(false, false);
+    }
+#undef FFTMI_C2
     return hipGetLastError();
 }
 
@@ -268,7 +275,8 @@ template <typename V, int LOGW, int LOGF> constexpr bool fold_ok()
 }
 
 template <typename V, int LOGW, int LOGF>
-static hipError_t fold_t(const void* in, void* out, int64_t nimg, int log_lc, const void* tw, bool ci, hipStream_t s)
+static hipError_t fold_t(const void* in, const void* in_im, void* out, int64_t nimg, int log_lc, const void* tw,
+                         bool ci, hipStream_t s)
 {
     if constexpr (!fold_ok<V, LOGW, LOGF>()) {
         return hipErrorInvalidValue;
@@ -278,19 +286,24 @@ static hipError_t fold_t(const void* in, void* out, int64_t nimg, int log_lc, co
         const int64_t blocks = (ngroups + GR - 1) / GR;
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
         const dim3 block((Geom<V, LOGW>::T << LOGF) * GR);
-        if (ci)
-            hipLaunchKernelGGL((rows2d_fold_kernel<V, LOGW, LOGF, true>), grid_of(blocks), block, 0, s, (const V*)in,
-                               (V*)out, ngroups, log_lc, (const V*)tw);
-        else
-            hipLaunchKernelGGL((rows2d_fold_kernel<V, LOGW, LOGF, false>), grid_of(blocks), block, 0, s, (const V*)in,
-                               (V*)out, ngroups, log_lc, (const V*)tw);
+#define FFTMI_FOLD(CI, PI)                                                                           \
+    hipLaunchKernelGGL((rows2d_fold_kernel<V, LOGW, LOGF, CI, PI>), grid_of(blocks), block, 0, s,       \
+                       make_in<V, PI>(in, in_im), (V*)out, ngroups, log_lc, (const V*)tw)
+        if (in_im) {
+            if (ci) FFTMI_FOLD(true, true);
+            else FFTMI_FOLD(false, true);
+        } else {
+            if (ci) FFTMI_FOLD(true, false);
+            else FFTMI_FOLD(false, false);
+        }
+#undef FFTMI_FOLD
         return hipGetLastError();
     }
 }
 
 template <typename V, int LOGR, int KIND>
-static hipError_t stock_t(const void* in, void* out, int logn, int logns, int64_t batch, const void* tw,
-                          BigTwiddle bt, bool ci, bool co, double scale, hipStream_t s)
+static hipError_t stock_t(const Io& io, int logn, int logns, int64_t batch, const void* tw, BigTwiddle bt, bool ci,
+                          bool co, double scale, hipStream_t s)
 {
     using TL = Tile<V, LOGR>;
     if (TL::THREADS > 1024) return hipErrorInvalidValue;
@@ -302,13 +315,29 @@ static hipError_t stock_t(const void* in, void* out, int logn, int logns, int64_
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
     const BigTw<V> big{(const V*)bt.hi, (const V*)bt.lo, bt.lbits, bt.logn};
-#define FFTMI_SP(CI, CO)                                                                                  \
-    hipLaunchKernelGGL((stock_pass_kernel<V, LOGR, KIND, CI, CO>), grid_of(blocks), dim3(TL::THREADS), 0, s, \
-                       (const V*)in, (V*)out, logn, logns, tps, (const V*)tw, big, (Rl)scale)
-    if (ci && co) FFTMI_SP(true, true);
-    else if (ci) FFTMI_SP(true, false);
-    else if (co) FFTMI_SP(false, true);
-    else FFTMI_SP(false, false);
+#define FFTMI_SP(CI, CO, PL)                                                                                  \
+    hipLaunchKernelGGL((stock_pass_kernel<V, LOGR, KIND, CI, CO, PL>), grid_of(blocks), dim3(TL::THREADS), 0, s, \
+                       make_in<V, PL && KIND == 0>(io.in, io.in_im), make_out<V, PL && KIND == 2>(io.out, io.out_im), \
+                       logn, logns, tps, (const V*)tw, big, (Rl)scale)
+    // Planar: the first pass reads the caller's planes (no conjugated store),
+    // the last writes them (no conjugated load).
+    const bool pl = io.in_im != nullptr || io.out_im != nullptr;
+    if (pl) {
+        if constexpr (KIND == 0) {
+            if (io.out_im || co) return hipErrorInvalidValue;
+            if (ci) FFTMI_SP(true, false, true);
+            else FFTMI_SP(false, false, true);
+        } else if constexpr (KIND == 2) {
+            if (io.in_im || ci) return hipErrorInvalidValue;
+            if (co) FFTMI_SP(false, true, true);
+            else FFTMI_SP(false, false, true);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (ci && co) FFTMI_SP(true, true, false);
+    else if (ci) FFTMI_SP(true, false, false);
+    else if (co) FFTMI_SP(false, true, false);
+    else FFTMI_SP(false, false, false);
 #undef FFTMI_SP
     return hipGetLastError();
 }
@@ -330,25 +359,25 @@ static hipError_t stock_t(const void* in, void* out, int logn, int logns, int64_
     }
 
 hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t nimg, int64_t w, int logf,
-                         const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s)
+                         const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s, void* out_im)
 {
-#define CF(L) cols2d_t<float2, L>(in, out, nimg, w, logf, tw, htw, co, scale, s)
-#define CD(L) cols2d_t<double2, L>(in, out, nimg, w, logf, tw, htw, co, scale, s)
+#define CF(L) cols2d_t<float2, L>(in, out, out_im, nimg, w, logf, tw, htw, co, scale, s)
+#define CD(L) cols2d_t<double2, L>(in, out, out_im, nimg, w, logf, tw, htw, co, scale, s)
     FFTMI_LOG_SWITCH(prec, logl, CF, CD)
 #undef CF
 #undef CD
 }
 
 hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,
-                              const void* tw, bool ci, hipStream_t s)
+                              const void* tw, bool ci, hipStream_t s, const void* in_im)
 {
-#define FOLD_F(LW) (logf == 1 ? fold_t<float2, LW, 1>(in, out, nimg, log_lc, tw, ci, s)   \
-                  : logf == 2 ? fold_t<float2, LW, 2>(in, out, nimg, log_lc, tw, ci, s) \
-                  : logf == 3 ? fold_t<float2, LW, 3>(in, out, nimg, log_lc, tw, ci, s) \
+#define FOLD_F(LW) (logf == 1 ? fold_t<float2, LW, 1>(in, in_im, out, nimg, log_lc, tw, ci, s)   \
+                  : logf == 2 ? fold_t<float2, LW, 2>(in, in_im, out, nimg, log_lc, tw, ci, s) \
+                  : logf == 3 ? fold_t<float2, LW, 3>(in, in_im, out, nimg, log_lc, tw, ci, s) \
                               : hipErrorInvalidValue)
-#define FOLD_D(LW) (logf == 1 ? fold_t<double2, LW, 1>(in, out, nimg, log_lc, tw, ci, s)   \
-                  : logf == 2 ? fold_t<double2, LW, 2>(in, out, nimg, log_lc, tw, ci, s) \
-                  : logf == 3 ? fold_t<double2, LW, 3>(in, out, nimg, log_lc, tw, ci, s) \
+#define FOLD_D(LW) (logf == 1 ? fold_t<double2, LW, 1>(in, in_im, out, nimg, log_lc, tw, ci, s)   \
+                  : logf == 2 ? fold_t<double2, LW, 2>(in, in_im, out, nimg, log_lc, tw, ci, s) \
+                  : logf == 3 ? fold_t<double2, LW, 3>(in, in_im, out, nimg, log_lc, tw, ci, s) \
                               : hipErrorInvalidValue)
     switch (logw) {
         case 1: return prec == 0 ? FOLD_F(1) : FOLD_D(1);
@@ -372,9 +401,10 @@ hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void
 
 hipError_t launch_stock_pass(int prec, int logr, int kind, const void* in, void* out, int logn, int logns,
                              int64_t batch, const void* tw, BigTwiddle big, bool ci, bool co, double scale,
-                             hipStream_t s)
+                             hipStream_t s, const void* in_im, void* out_im)
 {
-#define SK(L, K, V) stock_t<V, L, K>(in, out, logn, logns, batch, tw, big, ci, co, scale, s)
+    const Io io{in, in_im, out, out_im};
+#define SK(L, K, V) stock_t<V, L, K>(io, logn, logns, batch, tw, big, ci, co, scale, s)
 #define SF(L) (kind == 0 ? SK(L, 0, float2) : kind == 1 ? SK(L, 1, float2) : SK(L, 2, float2))
 #define SD(L) (kind == 0 ? SK(L, 0, double2) : kind == 1 ? SK(L, 1, double2) : SK(L, 2, double2))
     switch (logr) {

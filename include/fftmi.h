@@ -155,6 +155,33 @@ int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_
 int fft_exec_3d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
                 void* workspace, void* stream);
 
+/*
+ * The transform of any complex plan (rank 1, 2 or 3) on split arrays: the real
+ * parts in one plane and the imaginary parts in another ("The Butterfly: One
+ * Thread, One Output" holds its signal as a [2][N] array, plane 0 the real
+ * parts, plane 1 the imaginary parts).  Results equal those of the
+ * interleaved calls bit for bit: only the first kernel's loads and the last
+ * kernel's stores differ.
+ *   in_re, in_im, out_re, out_im: each [batch][dims...] float (FFT_C32) or
+ *              double (FFT_C64), the layout of the interleaved call with one
+ *              real per element; 8-byte aligned.  A [2][N] array p gives
+ *              re = p, im = p + N (batch 1); a [2][batch][N] array gives
+ *              im = p + batch N.  The two planes of one array must not overlap.
+ *              In place: in_re == out_re and in_im == out_im; any other
+ *              overlap of input and output planes is an error.
+ *   workspace: fft_planar_workspace_size(plan, batch) bytes (NULL when 0):
+ *              none for one-kernel rank-1 plans and rank-2/3 plans with one
+ *              axis longer than 1; one batch of signals for two-pass
+ *              multi-pass, rank-2/3 and Bluestein plans (these keep their
+ *              intermediate there); two for three-pass multi-pass plans.
+ * Errors: INVALID_ARG, RANK (real plan), ALIGN, OVERLAP, WORKSPACE, DEVICE.
+ */
+int fft_exec_planar(const fft_plan* plan, int dir, const void* in_re, const void* in_im, void* out_re,
+                    void* out_im, int64_t batch, void* workspace, void* stream);
+
+/* Bytes of device workspace fft_exec_planar needs for `batch` transforms. */
+int fft_planar_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes);
+
 /* Bytes of device workspace fft_poly_mul needs for `batch` pairs. */
 int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes);
 

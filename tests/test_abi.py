@@ -138,11 +138,13 @@ def test_exec_and_queries_with_null_plan():
     assert L.fft_exec_2d(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_exec_3d(None, 0, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_exec_r2c(None, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_exec_planar(None, 0, None, None, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_exec_c2r(None, None, None, 1, None, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_poly_mul(None, None, 1, None, 1, None, 1, None, None, None) == fm.FFT_ERR_INVALID_ARG
     sz = ctypes.c_size_t()
     assert L.fft_workspace_size(None, 1, ctypes.byref(sz)) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_poly_mul_workspace_size(None, 1, ctypes.byref(sz)) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_planar_workspace_size(None, 1, ctypes.byref(sz)) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_plan_describe(None, ctypes.create_string_buffer(8), 8) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_plan_destroy(None) == fm.FFT_OK
 
