@@ -92,6 +92,51 @@ void root_of_unity(int64_t m, int64_t M, double* re, double* im)
     *im = -s;
 }
 
+// e^{-2 pi i m / M} for any M >= 1: the angle, as p/q of a turn with q = 8M,
+// is folded into [0, 1/8] of a turn with integer arithmetic before libm.
+void root_of_unity_any(int64_t m, int64_t M, double* re, double* im)
+{
+    m %= M;
+    if (m < 0) m += M;
+    const int64_t q = 8 * M;
+    int64_t p = 8 * m;
+    double sin_sign = 1.0, cos_sign = 1.0;
+    bool swap = false;
+    if (2 * p > q) {  // theta in (pi, 2 pi): sin(2 pi - x) = -sin x
+        p = q - p;
+        sin_sign = -1.0;
+    }
+    if (4 * p > q) {  // theta in (pi/2, pi]: cos(pi - x) = -cos x
+        p = q / 2 - p;
+        cos_sign = -1.0;
+    }
+    if (8 * p > q) {  // theta in (pi/4, pi/2]: swap cos and sin
+        p = q / 4 - p;
+        swap = true;
+    }
+    const double th = 2.0 * M_PI * ((double)p / (double)q);
+    const double c = swap ? std::sin(th) : std::cos(th);
+    const double sn = swap ? std::cos(th) : std::sin(th);
+    *re = cos_sign * c;
+    *im = -sin_sign * sn;
+}
+
+// Radices of a mixed-radix plan: 8s, then 4, 2, then 3s, 5s, 7s; false if N
+// has another prime factor or needs more stages than the schedule holds.
+bool mixed_factor(int64_t n, MixedSchedule* ms)
+{
+    ms->nst = 0;
+    const int order[6] = {8, 4, 2, 3, 5, 7};
+    for (int r : order) {
+        while (n % r == 0) {
+            if (ms->nst == kMixedMaxStages) return false;
+            ms->radix[ms->nst++] = r;
+            n /= r;
+        }
+    }
+    return n == 1;
+}
+
 // Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
 // interleaved doubles: stage s >= 1 holds [l][k] = w_{Ns R}^{k 2^l}.
 std::vector<double> stage_table(int logn, int prec)
@@ -113,7 +158,15 @@ std::vector<double> stage_table(int logn, int prec)
 
 }  // namespace
 
-enum PlanPath { PATH_COPY = 0, PATH_ROWS = 1, PATH_MULTIPASS = 2, PATH_ND = 3, PATH_BLUESTEIN = 4, PATH_REAL = 5 };
+enum PlanPath {
+    PATH_COPY = 0,
+    PATH_ROWS = 1,
+    PATH_MULTIPASS = 2,
+    PATH_ND = 3,
+    PATH_BLUESTEIN = 4,
+    PATH_REAL = 5,
+    PATH_MIXED = 6
+};
 
 // One super-stage pass of a multi-pass plan.
 struct PassPlan {
@@ -151,6 +204,8 @@ struct fft_plan {
     // rank 1, any N (Bluestein): chirp c_j (N entries), B = F_M(b) (M entries),
     // the power-of-two plan of length M = 2^logm it runs on.
     int logm = 0;
+    // mixed radix: the stage radices; tw_a = w_N^m for m < N
+    MixedSchedule mixed{};
     // real rows of N = 2H points: inner = the complex plan of length H,
     // big_* = w_N, log_a = log2 H; real_fused: H within the rows kernel's range.
     bool real_fused = false;
@@ -303,8 +358,14 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
     if (rank == 1) {
         const int64_t n = dims[0];
         if (!is_pow2(n)) {
-            p->path = PATH_BLUESTEIN;
-            while ((int64_t(1) << p->logm) < 2 * n - 1) ++p->logm;
+            // lengths of 2, 3, 5 and 7 only, within one workgroup's LDS: mixed
+            // radix in one kernel; any other length: Bluestein
+            if (n <= mixed_max_n(prec) && mixed_factor(n, &p->mixed)) {
+                p->path = PATH_MIXED;
+            } else {
+                p->path = PATH_BLUESTEIN;
+                while ((int64_t(1) << p->logm) < 2 * n - 1) ++p->logm;
+            }
         } else if (n == 1) {
             p->path = PATH_COPY;
         } else if (n <= max_lds_n(prec)) {
@@ -455,6 +516,12 @@ int upload_tables(fft_plan* p)
         case PATH_BLUESTEIN:
             st = bluestein_tables(p);
             break;
+        case PATH_MIXED: {
+            std::vector<double> t(2 * (size_t)p->n);
+            for (int64_t m = 0; m < p->n; ++m) root_of_unity_any(m, p->n, &t[2 * m], &t[2 * m + 1]);
+            st = upload(t, prec, &p->tw_a);
+            break;
+        }
         case PATH_ROWS:
             st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
             break;
@@ -585,6 +652,12 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             snprintf(buf, len, "rank=1 n=%lld prec=%s path=bluestein m=%lld", (long long)p->n, prec,
                      1LL << p->logm);
             break;
+        case PATH_MIXED: {
+            int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=mixed radices=", (long long)p->n, prec);
+            for (int q = 0; q < p->mixed.nst && off > 0 && (size_t)off < len; ++q)
+                off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->mixed.radix[q]);
+            break;
+        }
         case PATH_REAL:
             snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
                      p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
@@ -658,6 +731,10 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
             }
             break;
         }
+        case PATH_MIXED:
+            e = launch_mixed_rows(plan->prec, (int)plan->n, plan->mixed, inv, inv, io.in, io.out, batch, plan->tw_a,
+                                  scale, s, io.in_im, io.out_im);
+            break;
         case PATH_BLUESTEIN: {
             // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
             void* w = workspace;
@@ -857,7 +934,8 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (plan->rank != 1 || plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "poly-mul needs a complex rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
-    if (plan->path == PATH_BLUESTEIN) return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
+    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED)
+        return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
     if (plan->logn > kPolyMaxLog) return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
     *bytes = plan->path == PATH_MULTIPASS ? (size_t)batch * (size_t)plan->n * plan->elem : 0;
     return FFT_OK;
@@ -871,7 +949,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
     if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
-    if (plan->path == PATH_BLUESTEIN)
+    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED)
         return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
     if (plan->logn > kPolyMaxLog)
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);

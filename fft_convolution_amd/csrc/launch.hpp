@@ -20,6 +20,21 @@ struct BigTwiddle {
     int logn;
 };
 
+// Stage radices of a mixed-radix row (each 2, 3, 4, 5, 7 or 8; product N).
+constexpr int kMixedMaxStages = 16;
+struct MixedSchedule {
+    int nst;
+    int radix[kMixedMaxStages];
+};
+
+// Mixed-radix rows (mixed.hip): `nrows` contiguous rows of n points,
+// n <= mixed_max_n(prec); tw = w_n^m for m < n.  Planar needs both in_im and
+// out_im.  in -> out, may alias.
+hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool conj_in, bool conj_out, const void* in,
+                             void* out, int64_t nrows, const void* tw, double scale, hipStream_t stream,
+                             const void* in_im = nullptr, void* out_im = nullptr);
+int mixed_max_n(int prec);
+
 // Lines per workgroup of the tile passes (tiles.hip) for lines of 2^logl points.
 int tile_lines_2d(int prec, int logl);
 

@@ -28,8 +28,9 @@ def _m(n):
     return m
 
 
-@pytest.mark.parametrize("n,batch", [(3, 4), (5, 1), (6, 3), (7, 2), (12, 5), (100, 3), (1000, 2), (4095, 2),
-                                     (4097, 1), (10007, 1), (3 * 1024, 2)])
+# lengths with a prime factor above 7, or beyond the mixed-radix range
+@pytest.mark.parametrize("n,batch", [(11, 4), (13, 1), (22, 3), (97, 2), (1001, 2), (4095, 2), (4097, 1),
+                                     (10007, 1), (3 * 4096, 2)])
 @pytest.mark.parametrize("dtype", [np.complex64, np.complex128])
 def test_bluestein_small_full(dev, n, batch, dtype):
     print("case n=%d batch=%d %s" % (n, batch, dtype.__name__), flush=True)

@@ -1,0 +1,91 @@
+"""Lengths N = 2^a 3^b 5^c 7^d that are not powers of two, within one
+workgroup's LDS (8192 points complex64, 4096 complex128): the mixed-radix
+Stockham kernel, against the fp64 oracle's direct DFT (GPU).
+
+Bar: per-row relative RMS <= 1e-6 log2 N (complex64) / 1e-14 log2 N
+(complex128), the bound of the power-of-two transforms."""
+import numpy as np
+import pytest
+import torch
+
+import fft_convolution_amd as fm
+import oracle
+from fft_convolution_amd import workloads as wl
+
+from conftest import fft_tol, rel_rms_rows
+
+pytestmark = pytest.mark.gpu
+
+F32 = [3, 5, 6, 7, 12, 15, 30, 49, 60, 100, 105, 210, 343, 360, 1000, 2187, 2401, 3125, 6000, 6144, 7168, 8000]
+F64 = [3, 12, 100, 105, 1000, 2187, 2401, 3000, 3072, 4000]
+
+
+def _radices(desc):
+    return [int(r) for r in desc.split("radices=")[1].split("x")]
+
+
+def _check(n, batch, dtype, seed):
+    print("case n=%d batch=%d %s" % (n, batch, dtype), flush=True)
+    npdt = np.complex64 if dtype == torch.complex64 else np.complex128
+    x_np = wl.batched_uniform(n, batch, seed=seed, dtype=npdt)
+    plan = fm.Plan(n, dtype)
+    desc = plan.describe()
+    assert "path=mixed" in desc
+    assert int(np.prod(_radices(desc))) == n
+    x = torch.from_numpy(x_np).cuda()
+    tol = fft_tol(n, dtype == torch.complex128)
+    y = plan.fft(x).cpu().numpy()
+    assert rel_rms_rows(y, oracle.dft(x_np)).max() <= tol
+    z = plan.ifft(x).cpu().numpy()
+    assert rel_rms_rows(z, oracle.dft(x_np, inverse=True)).max() <= tol
+    back = plan.ifft(plan.fft(x)).cpu().numpy()
+    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+
+
+@pytest.mark.parametrize("n", F32)
+def test_mixed_f32(dev, n):
+    _check(n, 67 if n <= 360 else 3, torch.complex64, n)
+
+
+@pytest.mark.parametrize("n", F64)
+def test_mixed_f64(dev, n):
+    _check(n, 33 if n <= 360 else 2, torch.complex128, n + 1)
+
+
+def test_mixed_closed_forms_and_in_place(dev):
+    """A single tone e^{2 pi i f t / N} gives N at bin f; an impulse at m gives
+    w^{mk}; in place equals out of place."""
+    n = 1260  # 4 * 3^2 * 5 * 7
+    t = np.arange(n)
+    plan = fm.Plan(n, torch.complex128)
+    for f in (0, 1, 419, n - 1):
+        # the phase from (f t) mod N, reduced in integers (exact input tone)
+        tone = np.exp(2j * np.pi * ((f * t) % n) / n)
+        y = plan.fft(torch.from_numpy(tone[None, :]).cuda()).cpu().numpy()[0]
+        want = np.zeros(n, dtype=complex)
+        want[f] = n
+        assert np.abs(y - want).max() < 1e-10
+    m = 5
+    imp = np.zeros((1, n), dtype=np.complex128)
+    imp[0, m] = 1
+    y = plan.fft(torch.from_numpy(imp).cuda()).cpu().numpy()[0]
+    assert np.abs(y - np.exp(-2j * np.pi * ((m * t) % n) / n)).max() < 1e-13
+    x = torch.from_numpy(wl.batched_normal(n, 9, seed=3, dtype=np.complex128)).cuda()
+    ref = plan.fft(x)
+    xx = x.clone()
+    plan.fft(xx, out=xx)
+    torch.cuda.synchronize()
+    assert torch.equal(xx, ref)
+
+
+def test_mixed_range_limits(dev):
+    # beyond one workgroup's LDS, or a prime factor above 7: Bluestein
+    assert "bluestein" in fm.Plan(3 * 4096, torch.complex64).describe()
+    assert "bluestein" in fm.Plan(3 * 2048, torch.complex128).describe()
+    assert "bluestein" in fm.Plan(11 * 64, torch.complex64).describe()
+    assert "mixed" in fm.Plan(3 * 2048, torch.complex64).describe()
+    # a large batch of short rows (many rows per workgroup, ragged last group)
+    n, batch = 12, 100003
+    x_np = wl.batched_uniform(n, batch, seed=8)
+    y = fm.Plan(n).fft(torch.from_numpy(x_np).cuda()).cpu().numpy()
+    assert rel_rms_rows(y, oracle.dft(x_np)).max() <= fft_tol(n)

@@ -3,7 +3,7 @@
 Only the first kernel's loads and the last kernel's stores differ from the
 interleaved calls, so every result must equal the interleaved call's bit for
 bit, on every path (one-kernel rows, two- and three-pass multi-pass,
-Bluestein, 2D with and without the folded column stage, 3D, axes of length
+Bluestein, mixed radix, 2D with and without the folded column stage, 3D, axes of length
 1); a few cases are also checked against the fp64 oracle directly, and the
 [2][N] layout of "The Butterfly: One Thread, One Output" is passed as one
 buffer."""
@@ -30,8 +30,10 @@ CASES = [
     ((1 << 20,), torch.complex64, 1),      # three passes
     ((1 << 13,), torch.complex128, 2),     # two passes, fp64
     ((1 << 19,), torch.complex128, 1),     # three passes, fp64
-    ((1000,), torch.complex64, 3),         # Bluestein
+    ((1001,), torch.complex64, 3),         # Bluestein
     ((4097,), torch.complex128, 2),
+    ((60,), torch.complex64, 7),           # mixed radix
+    ((2401,), torch.complex128, 2),
     ((64, 128), torch.complex64, 3),
     ((2048, 256), torch.complex64, 1),     # folded column stage
     ((1024, 64), torch.complex128, 2),     # folded, fp64
@@ -78,7 +80,8 @@ def test_planar_equals_interleaved(dev, dims, dtype, batch):
 
 
 @pytest.mark.parametrize("dims,dtype", [((4096,), torch.complex64), ((1 << 18,), torch.complex128),
-                                        ((999,), torch.complex64), ((128, 256), torch.complex64)])
+                                        ((999,), torch.complex64), ((1001,), torch.complex64),
+                                        ((128, 256), torch.complex64)])
 def test_planar_against_oracle(dev, dims, dtype):
     n = int(np.prod(dims))
     npdt = np.complex64 if dtype == torch.complex64 else np.complex128
