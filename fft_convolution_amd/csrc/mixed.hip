@@ -9,10 +9,10 @@
 // R-point DFT, and the outputs at y[(j / Ns) Ns R + (j mod Ns) + r Ns]; after
 // the last stage the row is in natural order.
 //
-// Unlike the power-of-two engine (compile-time geometry, data in registers
-// between LDS exchanges), the schedule here is a runtime list: a group of TR
-// threads owns a row, the row ping-pongs between two LDS buffers, one stage
-// per barrier.  The row still crosses HBM once each way.  Twiddles come from a
+// Unlike the power-of-two engine (compile-time geometry), the schedule here is
+// a runtime list: a group of TR >= N/8 threads owns a row held in LDS; each
+// stage reads its butterflies into registers, and writes them back in place
+// after a barrier.  The row crosses HBM once each way.  Twiddles come from a
 // table of w_N^m (m < N) in the plan precision; the roots of unity of the odd
 // radices are read from the same table (w_R^m = w_N^{m N / R}).
 #include "io.hpp"
@@ -60,14 +60,36 @@ __device__ __forceinline__ void dft_odd(V (&u)[R], const typename real_of<V>::ty
     for (int k = 0; k < R; ++k) u[k] = y[k];
 }
 
-// One stage of radix R over the rows' LDS buffers: group thread tl of tr.
+// q = j / d and r = j mod d for 0 <= j < 2^15, 1 <= d < 2^15, from a float
+// reciprocal (the quotient estimate is off by at most one) and an exact fix.
+__device__ __forceinline__ void divmod_small(int j, int d, float inv_d, int& q, int& r)
+{
+    q = (int)((float)j * inv_d);
+    r = j - q * d;
+    if (r < 0) {
+        --q;
+        r += d;
+    } else if (r >= d) {
+        ++q;
+        r -= d;
+    }
+}
+
+// Butterflies per thread and stage: a row of N points has at least N/8
+// threads, so a radix-R stage (N/R butterflies) gives each at most ceil(8/R).
+template <int R> constexpr int mixed_bmax() { return (8 + R - 1) / R; }
+
+// One stage of radix R on a row held in LDS (`row`), thread tl of tr.  All
+// butterflies are read and computed into registers, then (after a barrier
+// across the workgroup) written back in place.
 template <int R, typename V>
-__device__ __forceinline__ void mixed_stage(const V* src, V* dst, int n, int ns, int tl, int tr,
-                                            const V* __restrict__ tw)
+__device__ __forceinline__ void mixed_stage(V* row, int n, int ns, int tl, int tr, const V* __restrict__ tw)
 {
     using Rl = typename real_of<V>::type;
+    constexpr int B = mixed_bmax<R>();
     const int stride = n / R;             // input spacing N/R
     const int tstep = n / (ns * R);       // w_{Ns R}^x = w_N^{x tstep}
+    const float inv_ns = 1.0f / (float)ns;
     Rl c[R], sn[R];
     if constexpr (R == 3 || R == 5 || R == 7) {
 #pragma unroll
@@ -77,84 +99,106 @@ __device__ __forceinline__ void mixed_stage(const V* src, V* dst, int n, int ns,
             sn[m] = -w.y;
         }
     }
-    for (int j = tl; j < stride; j += tr) {
-        const int k = j % ns;
-        V u[R];
+    V u[B][R];
+    int dst[B];
 #pragma unroll
-        for (int r = 0; r < R; ++r) u[r] = src[j + r * stride];
-        if (ns > 1) {
+    for (int b = 0; b < B; ++b) {
+        const int j = tl + b * tr;
+        dst[b] = -1;
+        if (j < stride) {
+            int g, k;
+            divmod_small(j, ns, inv_ns, g, k);
 #pragma unroll
-            for (int r = 1; r < R; ++r) u[r] = cmul(u[r], tw[r * k * tstep]);
+            for (int r = 0; r < R; ++r) u[b][r] = row[j + r * stride];
+            if (ns > 1) {
+                // w^r = w_{Ns R}^{r k} as powers of one table value
+                const V w = tw[k * tstep];
+                V wr = w;
+#pragma unroll
+                for (int r = 1; r < R; ++r) {
+                    u[b][r] = cmul(u[b][r], wr);
+                    if (r + 1 < R) wr = cmul(wr, w);
+                }
+            }
+            if constexpr (R == 3 || R == 5 || R == 7)
+                dft_odd<R>(u[b], c, sn);
+            else
+                Dft<R>::run(u[b]);
+            dst[b] = g * ns * R + k;
         }
-        if constexpr (R == 3 || R == 5 || R == 7)
-            dft_odd<R>(u, c, sn);
-        else
-            Dft<R>::run(u);
-        const int base = (j / ns) * ns * R + k;
-#pragma unroll
-        for (int r = 0; r < R; ++r) dst[base + r * ns] = u[r];
     }
-}
-
-// rpw rows per workgroup, tr threads per row (blockDim = rpw tr); each row
-// uses 2N slots of LDS.  CAP: LDS slots of the workgroup.
-template <typename V, int CAP, bool PL>
-__global__ __launch_bounds__(256) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n, int tr,
-                                                         int rpw, MixedSchedule ms, const V* __restrict__ tw,
-                                                         int conj_in, int conj_out, typename real_of<V>::type scale)
-{
-    __shared__ V lds[CAP];
-    const int rl = threadIdx.x / tr, tl = threadIdx.x % tr;
-    const int64_t row = (int64_t)blockIdx.x * rpw + rl;
-    const bool live = row < nrows;
-    V* a = lds + rl * 2 * n;
-    V* b = a + n;
-    const int64_t base = row * n;
-    for (int p = tl; p < n; p += tr) {
-        V x = live ? in.ld(base + p) : V{0, 0};
-        a[p] = conj_in ? cconj(x) : x;
+    __syncthreads();  // every read of this stage is done before any write
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        if (dst[b] >= 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) row[dst[b] + r * ns] = u[b][r];
+        }
     }
     __syncthreads();
+}
+
+// rpw rows per workgroup, tr threads per row (blockDim = rpw tr), rows
+// contiguous in LDS as in memory (row rl at rl N), so the workgroup's rows are
+// loaded and stored as one contiguous, coalesced segment.  CAP: LDS slots.
+// Threads per workgroup at most: N/8 for the longest row of each precision.
+template <typename V> constexpr int mixed_max_threads() { return sizeof(V) == 8 ? 1024 : 512; }
+
+template <typename V, int CAP, bool PL>
+__global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n, int tr,
+                                                          int rpw, MixedSchedule ms, const V* __restrict__ tw,
+                                                          int conj_in, int conj_out, typename real_of<V>::type scale)
+{
+    __shared__ V lds[CAP];
+    const int threads = tr * rpw;
+    const int rl = threadIdx.x / tr, tl = threadIdx.x % tr;
+    const int64_t row0 = (int64_t)blockIdx.x * rpw;
+    const int rows = (int)(nrows - row0 < rpw ? nrows - row0 : rpw);
+    const int count = rows * n;
+    const int64_t base = row0 * n;
+    for (int i = threadIdx.x; i < rpw * n; i += threads) {
+        V x = i < count ? in.ld(base + i) : V{0, 0};
+        lds[i] = conj_in ? cconj(x) : x;
+    }
+    __syncthreads();
+    V* row = lds + rl * n;
     int ns = 1;
     for (int s = 0; s < ms.nst; ++s) {
         const int R = ms.radix[s];
         switch (R) {
-            case 2: mixed_stage<2>(a, b, n, ns, tl, tr, tw); break;
-            case 3: mixed_stage<3>(a, b, n, ns, tl, tr, tw); break;
-            case 4: mixed_stage<4>(a, b, n, ns, tl, tr, tw); break;
-            case 5: mixed_stage<5>(a, b, n, ns, tl, tr, tw); break;
-            case 7: mixed_stage<7>(a, b, n, ns, tl, tr, tw); break;
-            default: mixed_stage<8>(a, b, n, ns, tl, tr, tw); break;
+            case 2: mixed_stage<2>(row, n, ns, tl, tr, tw); break;
+            case 3: mixed_stage<3>(row, n, ns, tl, tr, tw); break;
+            case 4: mixed_stage<4>(row, n, ns, tl, tr, tw); break;
+            case 5: mixed_stage<5>(row, n, ns, tl, tr, tw); break;
+            case 7: mixed_stage<7>(row, n, ns, tl, tr, tw); break;
+            default: mixed_stage<8>(row, n, ns, tl, tr, tw); break;
         }
-        __syncthreads();
-        V* t = a;
-        a = b;
-        b = t;
         ns *= R;
     }
-    if (!live) return;
-    for (int p = tl; p < n; p += tr) {
-        const V y = a[p];
-        out.st(base + p, conj_out ? V{y.x * scale, -y.y * scale} : y);
+    for (int i = threadIdx.x; i < count; i += threads) {
+        const V y = lds[i];
+        out.st(base + i, conj_out ? V{y.x * scale, -y.y * scale} : y);
     }
 }
 
-// LDS classes (slots): small for short rows, large (128 KiB) for long ones.
-template <typename V> constexpr int mixed_cap_small() { return 4096 * 8 / (int)sizeof(V); }
-template <typename V> constexpr int mixed_cap_large() { return 16384 * 8 / (int)sizeof(V); }
+// LDS classes (slots): rows of up to 2048 points (several rows per workgroup
+// for short ones), and one row of up to 8192 / 4096 points (64 KiB).
+template <typename V> constexpr int mixed_cap_small() { return 2048; }
+template <typename V> constexpr int mixed_cap_large() { return 8192 * 8 / (int)sizeof(V); }
 
 template <typename V, bool PL>
 static hipError_t mixed_t(const Io& io, int64_t nrows, int n, MixedSchedule ms, const void* tw, bool ci, bool co,
                           double scale, hipStream_t s)
 {
-    // threads per row: a power of two near N/8, at most 256
+    // threads per row: the power of two >= N/8 (so no thread has more than
+    // ceil(8/R) butterflies in a stage), at most 1024; 256 threads or more
+    // per workgroup
     int tr = 1;
-    while (tr < 256 && tr * 8 < n) tr *= 2;
-    int rpw = 256 / tr;
-    const bool small = 2 * n <= mixed_cap_small<V>();
-    if (!small && 2 * n > mixed_cap_large<V>()) return hipErrorInvalidValue;
-    const int cap = small ? mixed_cap_small<V>() : mixed_cap_large<V>();
-    while (rpw > 1 && 2 * n * rpw > cap) rpw /= 2;
+    while (tr * 8 < n) tr *= 2;
+    if (tr > mixed_max_threads<V>()) return hipErrorInvalidValue;
+    const int rpw = tr >= 256 ? 1 : 256 / tr;
+    const bool small = rpw * n <= mixed_cap_small<V>();
+    if (!small && rpw * n > mixed_cap_large<V>()) return hipErrorInvalidValue;
     const int64_t blocks = (nrows + rpw - 1) / rpw;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
@@ -182,6 +226,6 @@ hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool ci, 
               : mixed_t<double2, false>(io, nrows, n, ms, tw, ci, co, scale, s);
 }
 
-int mixed_max_n(int prec) { return prec == 0 ? mixed_cap_large<float2>() / 2 : mixed_cap_large<double2>() / 2; }
+int mixed_max_n(int prec) { return prec == 0 ? mixed_cap_large<float2>() : mixed_cap_large<double2>(); }
 
 }  // namespace fftmi
