@@ -336,8 +336,10 @@ int check_device(const fft_plan* plan)
 // signal-sized buffer; the folded 2D transform needs one only in place.
 size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
-    if (p->path == PATH_BLUESTEIN)
-        return ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
+    if (p->path == PATH_BLUESTEIN)  // none when M is within one workgroup (one kernel)
+        return (int64_t(1) << p->logm) <= max_lds_n(p->prec)
+                   ? 0
+                   : ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
     if (p->path == PATH_REAL)  // the H-point spectrum of every row, beyond the one-kernel range
         return p->real_fused || p->n == 1 ? 0 : (size_t)batch * (size_t)(p->n / 2) * p->elem;
     const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_ND && p->logf > 0);
@@ -649,8 +651,8 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                      plan_nstages(p->log_a, plan_lem(p->prec)));
             break;
         case PATH_BLUESTEIN:
-            snprintf(buf, len, "rank=1 n=%lld prec=%s path=bluestein m=%lld", (long long)p->n, prec,
-                     1LL << p->logm);
+            snprintf(buf, len, "rank=1 n=%lld prec=%s path=bluestein m=%lld %s", (long long)p->n, prec,
+                     1LL << p->logm, (int64_t(1) << p->logm) <= max_lds_n(p->prec) ? "fused" : "passes");
             break;
         case PATH_MIXED: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=mixed radices=", (long long)p->n, prec);
@@ -737,6 +739,12 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
             break;
         case PATH_BLUESTEIN: {
             // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
+            if ((int64_t(1) << plan->logm) <= max_lds_n(plan->prec)) {  // one kernel
+                e = launch_bluestein_rows(plan->prec, plan->logm, (int)plan->n, io.in, io.out, batch,
+                                          plan->inner->tw_a, plan->chirp, plan->bspec, inv, inv, scale, s, io.in_im,
+                                          io.out_im);
+                break;
+            }
             void* w = workspace;
             void* inner_ws = (char*)workspace + ((size_t)batch << plan->logm) * plan->elem;
             e = launch_chirp_pre(plan->prec, io.in, w, plan->n, plan->logm, batch, plan->chirp, inv, s, io.in_im);

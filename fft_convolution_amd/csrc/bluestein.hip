@@ -124,6 +124,108 @@ hipError_t launch_chirp_post(int prec, const void* w, void* out, int64_t n, int 
     return hipGetLastError();
 }
 
+// The whole chirp-z transform of a row in one kernel, for M = 2^LOGM within
+// the row kernel's range: the row is loaded once (times the chirp, zero
+// padded to M in registers), transformed, multiplied by B, transformed back
+// (conj F conj / M) and stored once (times the chirp) -- the same arithmetic
+// as the five-pass route, without its four HBM round trips over M points.
+// tw: stage table for M; conj_in / conj_out and scale as the five passes.
+template <typename V, int LOGM, bool PL>
+__global__ __launch_bounds__((Geom<V, LOGM>::T * rows_per_wg<V, LOGM>()))
+void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n, const V* __restrict__ tw,
+                           const V* __restrict__ chirp, const V* __restrict__ bspec, int conj_in, int conj_out,
+                           typename real_of<V>::type scale)
+{
+    using G = Geom<V, LOGM>;
+    using Rl = typename real_of<V>::type;
+    constexpr int RPW = rows_per_wg<V, LOGM>();
+    __shared__ V lds[G::LDS > 0 ? G::LDS * RPW : 1];
+
+    const int tid = threadIdx.x;
+    const int rloc = tid / G::T;
+    const int t = tid % G::T;
+    const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
+    const bool live = row < nrows;
+    const LdsLines<V, 1> L{lds + rloc * G::LDS, 0};
+
+    TwBases<V, LOGM> tb;
+    tb.load(tw, t);
+    V v[G::E];
+    const int64_t base = row * n;
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) {
+        const int p = t + i * G::T;
+        V x{0, 0};
+        if (live && p < n) {
+            x = in.ld(base + p);
+            if (conj_in) x = cconj(x);
+            x = cmul(x, chirp[p]);
+        }
+        v[i] = x;
+    }
+    fft_regs<LOGM>(v, t, tb, L);
+    // W B, conjugated for the inverse transform
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) v[i] = cconj(cmul(v[i], bspec[t + i * G::T]));
+    __syncthreads();  // the forward transform's last exchange is read by now
+    fft_regs<LOGM>(v, t, tb, L);
+    if (!live) return;
+    const Rl inv_m = (Rl)1 / (Rl)(1 << LOGM);
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) {
+        const int p = t + i * G::T;
+        if (p < n) {
+            const V y = cmul(V{v[i].x * inv_m, -v[i].y * inv_m}, chirp[p]);
+            out.st(base + p, conj_out ? V{y.x * scale, -y.y * scale} : y);
+        }
+    }
+}
+
+template <typename V, int LOGM, bool PL>
+static hipError_t bluestein_rows_t(const Io& io, int64_t nrows, int n, const void* tw, const void* chirp,
+                                   const void* bspec, bool ci, bool co, double scale, hipStream_t s)
+{
+    constexpr int RPW = rows_per_wg<V, LOGM>();
+    constexpr int BLOCK = Geom<V, LOGM>::T * RPW;
+    const int64_t blocks = (nrows + RPW - 1) / RPW;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    using Rl = typename real_of<V>::type;
+    hipLaunchKernelGGL((bluestein_rows_kernel<V, LOGM, PL>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
+                       make_in<V, PL>(io.in, io.in_im), make_out<V, PL>(io.out, io.out_im), nrows, n, (const V*)tw,
+                       (const V*)chirp, (const V*)bspec, (int)ci, (int)co, (Rl)scale);
+    return hipGetLastError();
+}
+
+template <typename V, int LOGM>
+static hipError_t bluestein_rows_pl(const Io& io, int64_t nrows, int n, const void* tw, const void* chirp,
+                                    const void* bspec, bool ci, bool co, double scale, hipStream_t s)
+{
+    if (io.in_im) return bluestein_rows_t<V, LOGM, true>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+    return bluestein_rows_t<V, LOGM, false>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+}
+
+hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void* out, int64_t nrows, const void* tw,
+                                 const void* chirp, const void* bspec, bool ci, bool co, double scale, hipStream_t s,
+                                 const void* in_im, void* out_im)
+{
+    const Io io{in, in_im, out, out_im};
+    if ((in_im != nullptr) != (out_im != nullptr)) return hipErrorInvalidValue;
+#define FFTMI_BL(L)                                                                                          \
+    case L:                                                                                                  \
+        return prec == 0 ? bluestein_rows_pl<float2, L>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s)   \
+                         : bluestein_rows_pl<double2, L>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+    if (prec == 1 && logm > 12) return hipErrorInvalidValue;
+    switch (logm) {
+        FFTMI_BL(2) FFTMI_BL(3) FFTMI_BL(4) FFTMI_BL(5) FFTMI_BL(6) FFTMI_BL(7) FFTMI_BL(8) FFTMI_BL(9)
+        FFTMI_BL(10) FFTMI_BL(11) FFTMI_BL(12)
+        case 13:
+            if (prec == 0) return bluestein_rows_pl<float2, 13>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+#undef FFTMI_BL
+}
+
 hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t s)
 {
     hipLaunchKernelGGL(narrow_kernel, ew_grid(total), dim3(256), 0, s, (const double2*)in, (float2*)out, total);

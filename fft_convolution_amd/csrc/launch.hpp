@@ -107,6 +107,12 @@ hipError_t launch_cmul_table(int prec, void* w, int logm, int64_t batch, const v
 hipError_t launch_chirp_post(int prec, const void* w, void* out, int64_t n, int logm, int64_t batch,
                              const void* chirp, bool conj_out, double scale, hipStream_t stream,
                              void* out_im = nullptr);
+// The whole Bluestein transform of each row in one kernel, M = 2^logm within
+// the row kernel's range (logm <= 13 complex64, 12 complex128); tw: stage
+// table for M.  Planar needs both in_im and out_im.  in -> out, may alias.
+hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void* out, int64_t nrows, const void* tw,
+                                 const void* chirp, const void* bspec, bool conj_in, bool conj_out, double scale,
+                                 hipStream_t stream, const void* in_im = nullptr, void* out_im = nullptr);
 // complex128 -> complex64, `total` elements.
 hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t stream);
 
