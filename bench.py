@@ -14,6 +14,12 @@ Prints ONE JSON line with:
              (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), read
              from profiles/ and null once the kernel sources have changed
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows
+  step_us    mean / median / min / max of the per-step event durations
+  copy_ceiling  a device-to-device copy of the same byte count (at least
+             512 MiB each way), timed alike, and the step's algorithmic rate
+             as a fraction of the copy's (the practical ceiling)
+  rotated    the same steps cycling over --rotate buffer sets (default 3), so
+             that no step finds its input in the 256 MB MALL
 
 Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
@@ -39,15 +45,25 @@ WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_204
              "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384")
 
 
-def kernel_sources_digest() -> str:
-    """sha256 over the HIP sources, to tell whether stored counters still apply."""
+# The sources each single-kernel workload's kernel is built from: a stored
+# counter record applies while these files are unchanged.
+KERNEL_SOURCES = {
+    "c2c_n4096_b16384": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
+    "c2c_n1024_b64": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
+    "r2c_n8192_b16384": ("real.hip", "stockham.hpp", "radix_plan.hpp", "tile_common.hpp"),
+}
+
+
+def kernel_sources_digest(workload: str = WORKLOADS[0]) -> str:
+    """sha256 over the HIP sources of the workload's kernel (all of csrc/ for
+    multi-kernel workloads), to tell whether stored counters still apply."""
     csrc = os.path.join(ROOT, "fft_convolution_amd", "csrc")
+    names = KERNEL_SOURCES.get(workload) or [n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp", ".cpp"))]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in sorted(names):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -57,7 +73,7 @@ def stored_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sources_sha256") != kernel_sources_digest():
+    if rec.get("kernel_sources_sha256") != kernel_sources_digest(workload):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -71,94 +87,92 @@ def ensure_built():
     return fm
 
 
-def setup_workload(name, dev, fm, torch):
-    """Returns (step_fn, info) with inputs resident on the device."""
+def setup_workload(name, dev, fm, torch, sets=1):
+    """Returns (step_fn, info): step(k) runs the hot path once on buffer set
+    k mod `sets` (each set: its own input, output and workspace, all resident
+    in HBM; set 0 holds the seeded workload input, the others copies)."""
     from fft_convolution_amd import workloads as wl
     spec = dict(wl.WORKLOADS[name])
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def ws_of(nbytes):
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
     if name.startswith("c2c_n"):
         n, batch = spec["n"], spec["batch"]
-        x = torch.from_numpy(wl.workload_input(name)).to(dev)
-        y = torch.empty_like(x)
+        x_np = wl.workload_input(name)
         plan = fm.Plan(n, torch.complex64)
         wsb = fm.fft_workspace_size(plan.handle, batch)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-        stream = torch.cuda.current_stream().cuda_stream
+        x0 = torch.from_numpy(x_np).to(dev)
+        bufs = [(x0 if k == 0 else x0.clone(), torch.empty_like(x0), ws_of(wsb)) for k in range(sets)]
 
-        def step():
+        def step(k=0):
+            x, y, ws = bufs[k % sets]
             fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, y, batch, ws, stream)
-        flops = batch * 5.0 * n * math.log2(n)
-        info = dict(n=n, batch=batch, dtype="f32", flops=flops, bytes=2 * x.numel() * 8,
-                    plan=plan.describe(), kernels=1 if wsb == 0 else 2,
-                    sample_rows=lambda rows: x[:rows].cpu().numpy(),
-                    oracle_unit=5.0 * n * math.log2(n), keep=(plan, x, y, ws))
+        desc = plan.describe()
+        kernels = len(desc.split("radices=")[1].split("x")) if "radices=" in desc else 1
+        info = dict(n=n, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=2 * x0.numel() * 8,
+                    plan=desc, kernels=kernels, sample_rows=lambda rows: x_np[:rows],
+                    oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))
         return step, info
-    if name.startswith("c2c2d"):
-        h, w, batch = spec["h"], spec["w"], spec["batch"]
-        x = torch.from_numpy(wl.workload_input(name)).to(dev)
-        y = torch.empty_like(x)
-        plan = fm.Plan((h, w), torch.complex64)
-        stream = torch.cuda.current_stream().cuda_stream
+    if name.startswith("c2c2d") or name.startswith("c2c3d"):
+        three = name.startswith("c2c3d")
+        dims = (spec["d"], spec["h"], spec["w"]) if three else (spec["h"], spec["w"])
+        batch = spec["batch"]
+        x_np = wl.workload_input(name)
+        plan = fm.Plan(dims, torch.complex64)
+        x0 = torch.from_numpy(x_np).to(dev)
+        bufs = [(x0 if k == 0 else x0.clone(), torch.empty_like(x0)) for k in range(sets)]
+        fn = fm.fft_exec_3d if three else fm.fft_exec_2d
 
-        def step():
-            fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, x, y, batch, None, stream)
-        flops = batch * 5.0 * h * w * math.log2(h * w)
-        info = dict(h=h, w=w, batch=batch, dtype="f32", flops=flops, bytes=2 * x.numel() * 8,
-                    plan=plan.describe(), kernels=2, keep=(plan, x, y),
-                    sample_rows=lambda rows: x[:rows].cpu().numpy(),
-                    oracle_unit=5.0 * h * w * math.log2(h * w))
-        return step, info
-    if name.startswith("c2c3d"):
-        d, h, w, batch = spec["d"], spec["h"], spec["w"], spec["batch"]
-        x = torch.from_numpy(wl.workload_input(name)).to(dev)
-        y = torch.empty_like(x)
-        plan = fm.Plan((d, h, w), torch.complex64)
-        stream = torch.cuda.current_stream().cuda_stream
-
-        def step():
-            fm.fft_exec_3d(plan.handle, fm.FFT_FORWARD, x, y, batch, None, stream)
-        n = d * h * w
-        info = dict(d=d, h=h, w=w, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n),
-                    bytes=2 * x.numel() * 8, plan=plan.describe(), kernels=3, keep=(plan, x, y),
-                    sample_rows=lambda rows: x[:rows].cpu().numpy(), oracle_unit=5.0 * n * math.log2(n))
+        def step(k=0):
+            x, y = bufs[k % sets]
+            fn(plan.handle, fm.FFT_FORWARD, x, y, batch, None, stream)
+        n = int(math.prod(dims))
+        info = dict(batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=2 * x0.numel() * 8,
+                    plan=plan.describe(), kernels=3 if three else 2, keep=(plan, bufs),
+                    sample_rows=lambda rows: x_np[:rows], oracle_unit=5.0 * n * math.log2(n),
+                    oracle_fn="fft3" if three else "fft2",
+                    **dict(zip(("d", "h", "w") if three else ("h", "w"), dims)))
         return step, info
     if name.startswith("r2c"):
         n, batch = spec["n"], spec["batch"]
         x_np = wl.workload_input(name)
-        x = torch.from_numpy(x_np).to(dev)
-        y = torch.empty(batch, n // 2 + 1, dtype=torch.complex64, device=dev)
         plan = fm.RealPlan(n, torch.float32)
         wsb = fm.fft_workspace_size(plan.handle, batch)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-        stream = torch.cuda.current_stream().cuda_stream
+        x0 = torch.from_numpy(x_np).to(dev)
+        bufs = [(x0 if k == 0 else x0.clone(),
+                 torch.empty(batch, n // 2 + 1, dtype=torch.complex64, device=dev), ws_of(wsb)) for k in range(sets)]
 
-        def step():
+        def step(k=0):
+            x, y, ws = bufs[k % sets]
             fm.fft_exec_r2c(plan.handle, x, y, batch, ws, stream)
         info = dict(n=n, batch=batch, dtype="f32", flops=batch * 2.5 * n * math.log2(n),
-                    bytes=x.numel() * 4 + y.numel() * 8, plan=plan.describe(), kernels=1 if wsb == 0 else 2,
-                    sample_rows=lambda rows: x_np[:rows], oracle_unit=2.5 * n * math.log2(n),
-                    oracle_fn="rfft", keep=(plan, x, y, ws))
+                    bytes=x0.numel() * 4 + bufs[0][1].numel() * 8, plan=plan.describe(),
+                    kernels=1 if wsb == 0 else 2, sample_rows=lambda rows: x_np[:rows],
+                    oracle_unit=2.5 * n * math.log2(n), oracle_fn="rfft", keep=(plan, bufs))
         return step, info
     if name.startswith("polymul"):
         length, batch = spec["length"], spec["batch"]
         a_np, b_np = wl.workload_input(name)
-        a = torch.from_numpy(a_np).to(dev)
-        b = torch.from_numpy(b_np).to(dev)
         n = 1
         while n < 2 * length - 1:
             n *= 2
         plan = fm.Plan(n, torch.complex128)
-        c = torch.empty(batch, 2 * length - 1, dtype=torch.int64, device=dev)
-        ws = torch.empty(fm.fft_poly_mul_workspace_size(plan.handle, batch), dtype=torch.uint8, device=dev)
-        resid = torch.empty(1, dtype=torch.float64, device=dev)
-        stream = torch.cuda.current_stream().cuda_stream
+        wsb = fm.fft_poly_mul_workspace_size(plan.handle, batch)
+        a0 = torch.from_numpy(a_np).to(dev)
+        b0 = torch.from_numpy(b_np).to(dev)
+        bufs = [(a0 if k == 0 else a0.clone(), b0 if k == 0 else b0.clone(),
+                 torch.empty(batch, 2 * length - 1, dtype=torch.int64, device=dev), ws_of(wsb),
+                 torch.empty(1, dtype=torch.float64, device=dev)) for k in range(sets)]
 
-        def step():
+        def step(k=0):
+            a, b, c, ws, resid = bufs[k % sets]
             fm.fft_poly_mul(plan.handle, a, length, b, length, c, batch, ws, resid, stream)
-        flops = batch * 3 * 5.0 * n * math.log2(n)
-        info = dict(n=n, length=length, batch=batch, dtype="f64", flops=flops,
-                    bytes=(a.numel() + b.numel() + c.numel()) * 8, plan=plan.describe(), kernels=4,
-                    keep=(plan, a, b, c, ws, resid),
-                    sample_pairs=lambda p: (a_np[:p], b_np[:p]), oracle_unit=3 * 5.0 * n * math.log2(n))
+        info = dict(n=n, length=length, batch=batch, dtype="f64", flops=batch * 3 * 5.0 * n * math.log2(n),
+                    bytes=(a0.numel() + b0.numel() + bufs[0][2].numel()) * 8, plan=plan.describe(), kernels=4,
+                    keep=(plan, bufs), sample_pairs=lambda p: (a_np[:p], b_np[:p]),
+                    oracle_unit=3 * 5.0 * n * math.log2(n))
         return step, info
     raise SystemExit("unknown workload %s" % name)
 
@@ -185,7 +199,7 @@ def cpu_baseline(name, info, budget_s):
         imgs = 1
         x = info["sample_rows"](imgs)
         t0 = time.perf_counter()
-        (oracle.fft3 if name.startswith("c2c3d") else oracle.fft2)(x)
+        getattr(oracle, info["oracle_fn"])(x)
         dt = time.perf_counter() - t0
         units, sample = imgs, "first %d of %d images" % (imgs, info["batch"])
     else:
@@ -220,6 +234,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOADS[0], choices=WORKLOADS)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="buffer sets for the extra rotated-buffer timing (1 = none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a device-to-device copy of the input's size (for counter scaling)")
     args = ap.parse_args()
@@ -237,27 +253,59 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    step, info = setup_workload(args.workload, dev, fm, torch)
-    for _ in range(args.warmup):
-        step()
+    sets = max(1, args.rotate)
+    step, info = setup_workload(args.workload, dev, fm, torch, sets=sets)
+    for k in range(max(args.warmup, sets)):
+        step(k)
     torch.cuda.synchronize()
 
-    # Timed region: K steps back to back on the launch stream, each bracketed
-    # by its own pair of HIP events, so that the per-launch kernel duration is
-    # measured the same way a kernel trace measures it.
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    start, end = ev(), ev()
-    marks = [(ev(), ev()) for _ in range(args.steps)]
+    def timed(k0, stride):
+        """K steps back to back on the launch stream (set k0 + i stride), each
+        bracketed by its own pair of HIP events, so that the per-launch
+        duration is measured the way a kernel trace measures it.  Returns
+        (ms per step over the whole region, per-step event durations in ms)."""
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        start, end = ev(), ev()
+        marks = [(ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        start.record()
+        for i, (a, b) in enumerate(marks):
+            a.record()
+            step(k0 + i * stride)
+            b.record()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps, [a.elapsed_time(b) for a, b in marks]
+
+    # Timed region: the same buffers every step (the figure `value` is from).
+    ms, per = timed(0, 0)
+    launch_ms = sum(per) / len(per)
+    per_sorted = sorted(per)
+    # Rotated: consecutive steps on different buffer sets, so that nothing a
+    # step reads is still in the 256 MB MALL from the step before.
+    rotated = None
+    if sets > 1:
+        ms_rot, per_rot = timed(0, 1)
+        rotated = {"sets": sets, "ms_per_step": round(ms_rot, 5),
+                   "step_us_median": round(sorted(per_rot)[len(per_rot) // 2] * 1e3, 2)}
+
+    # The practical ceiling: a device-to-device copy of the same byte count
+    # (half the algorithmic bytes each way), at least 512 MiB each way so that
+    # it streams from HBM rather than the 256 MB MALL.
+    copy_bytes = max(info["bytes"] // 2, 512 << 20)
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
     torch.cuda.synchronize()
-    start.record()
-    for a, b in marks:
-        a.record()
-        step()
-        b.record()
-    end.record()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(20):
+        dst.copy_(src)
+    c1.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    launch_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    copy_ms = c0.elapsed_time(c1) / 20
+    del src, dst
 
     if args.copy_calibration:
         # A plain elementwise kernel that reads and writes known byte counts
@@ -286,6 +334,12 @@ def main():
         "config": {"workload": args.workload, "plan": info["plan"],
                    **{k: info[k] for k in ("n", "d", "h", "w", "batch", "length") if k in info}},
         "hbm_tb_s": round(tbs, 3),
+        "step_us": {"mean": round(launch_ms * 1e3, 2), "median": round(per_sorted[len(per) // 2] * 1e3, 2),
+                    "min": round(per_sorted[0] * 1e3, 2), "max": round(per_sorted[-1] * 1e3, 2)},
+        "copy_ceiling": {"what": "device-to-device copy of the same bytes (half each way)",
+                         "gb_s": round(2 * copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                         "frac_of_copy": round((info["bytes"] / ms) / (2 * copy_bytes / copy_ms), 4)},
+        "rotated": rotated,
         "gpu": torch.cuda.get_device_name(dev),
     }
     if info["kernels"] == 1:

@@ -123,7 +123,7 @@ def cmd_traffic(args):
         "traffic_bytes_per_launch": fetch_b + write_b,
         "algorithmic_bytes_per_launch": args.algorithmic_bytes,
         "commands": args.cmd,
-        "kernel_sources_sha256": kernel_sources_digest(),
+        "kernel_sources_sha256": kernel_sources_digest(args.workload),
     }
     with open(args.out, "w") as f:
         json.dump(rec, f, indent=1)
