@@ -137,8 +137,8 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
  * every row, then column transforms of length H over every column.
  *   in, out:   [batch][H][W] complex, images contiguous.  in == out allowed.
  *   workspace: used only by an in-place call (in == out) on a plan that folds
- *              part of the column transform into the row pass (H > 1024 for
- *              FFT_C32, H > 512 for FFT_C64; fft_plan_describe shows fold > 1);
+ *              part of the column transform into the row pass (H > 512;
+ *              fft_plan_describe shows fold > 1);
  *              it then needs fft_workspace_size(plan, batch) bytes.  Otherwise
  *              it may be NULL.
  * Errors: as fft_exec_c2c.

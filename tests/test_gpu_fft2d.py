@@ -87,12 +87,12 @@ def test_fft2_round_trip_and_in_place(dev):
 
 
 def test_fft2_folded_in_place_needs_workspace(dev):
-    # 2048 rows fold a radix-2 column super-stage into the row pass; in place
+    # 2048 rows fold a radix-4 column super-stage into the row pass; in place
     # that pass cannot write its output over rows other groups still read, so
     # an in-place call takes a workspace (and is rejected without one).
     h, w = 2048, 64
     plan = fm.Plan((h, w), torch.complex64)
-    assert "fold=2" in plan.describe()
+    assert "fold=4" in plan.describe()
     x_np = wl.batched_normal(h * w, 2, seed=11).reshape(2, h, w)
     x = torch.from_numpy(x_np).to(dev)
     ws_bytes = fm.fft_workspace_size(plan.handle, 2)
