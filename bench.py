@@ -24,7 +24,8 @@ Prints ONE JSON line with:
 Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
 transform the same way, and the R2C transform of 16384 real rows of 8192
-points (value = batch * 2.5 N log2 N / t, half the complex count).
+points (value = batch * 2.5 N log2 N / t, half the complex count), and rows
+of 1000 (mixed radix) and 1001 (Bluestein) points.
 """
 from __future__ import annotations
 
@@ -42,7 +43,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
-             "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384")
+             "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384", "c2c_n1000_b65536",
+             "c2c_n1001_b65536")
 
 
 # The sources each single-kernel workload's kernel is built from: a stored
@@ -51,6 +53,8 @@ KERNEL_SOURCES = {
     "c2c_n4096_b16384": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
     "c2c_n1024_b64": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
     "r2c_n8192_b16384": ("real.hip", "stockham.hpp", "radix_plan.hpp", "tile_common.hpp"),
+    "c2c_n1000_b65536": ("mixed.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
+    "c2c_n1001_b65536": ("bluestein.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
 }
 
 
@@ -110,7 +114,8 @@ def setup_workload(name, dev, fm, torch, sets=1):
             x, y, ws = bufs[k % sets]
             fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, y, batch, ws, stream)
         desc = plan.describe()
-        kernels = len(desc.split("radices=")[1].split("x")) if "radices=" in desc else 1
+        kernels = len(desc.split("radices=")[1].split("x")) if "path=multipass" in desc else \
+            (5 if "passes" in desc else 1)
         info = dict(n=n, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=2 * x0.numel() * 8,
                     plan=desc, kernels=kernels, sample_rows=lambda rows: x_np[:rows],
                     oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))

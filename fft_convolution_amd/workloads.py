@@ -21,6 +21,8 @@ stated):
 * a 256^3 volume, re and im uniform [-1, 1) (seed 6), for the 3D transform.
 * ``real_normal`` -- real rows of N points, i.i.d. standard normal: the real
   operands of the R2C / C2R transforms.  N = 8192 x 16384 rows (seed 7).
+* rows of 1000 and 1001 points x 65536, ``batched_normal`` (seeds 8, 9): the
+  mixed-radix and Bluestein paths.
 """
 from __future__ import annotations
 
@@ -37,6 +39,10 @@ WORKLOADS = {
     "c2c3d_256x256x256_b1": dict(kind="uniform3d", d=256, h=256, w=256, batch=1, seed=6),
     # real rows, the R2C transform (512 MiB of float32 in)
     "r2c_n8192_b16384": dict(kind="real_normal", n=8192, batch=16384, seed=7),
+    # lengths that are not powers of two (~500 MiB in): 1000 = 8 * 5^3 (mixed
+    # radix), 1001 = 7 * 11 * 13 (Bluestein, M = 2048)
+    "c2c_n1000_b65536": dict(kind="normal", n=1000, batch=65536, seed=8),
+    "c2c_n1001_b65536": dict(kind="normal", n=1001, batch=65536, seed=9),
 }
 
 
