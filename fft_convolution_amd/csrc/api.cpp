@@ -201,6 +201,9 @@ struct fft_plan {
     int eff_log[3] = {0, 0, 0};
     void* tw_c = nullptr;
     int logf = 0;  // log2 of the column super-stage folded into the row pass
+    // the radix-2^logf column super-stage runs as a pass of its own (rows too
+    // wide for F of them in LDS): rows, column stage, column pass
+    bool col_split = false;
     // rank 1, any N (Bluestein): chirp c_j (N entries), B = F_M(b) (M entries),
     // the power-of-two plan of length M = 2^logm it runs on.
     int logm = 0;
@@ -346,6 +349,13 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
     return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
 
+// Workspace a rank-2/3 interleaved call needs: the folded layout only in
+// place, the split layout always.
+size_t nd_workspace(const fft_plan* p, int64_t batch, bool in_place)
+{
+    return p->col_split || in_place ? c2c_workspace(p, batch) : 0;
+}
+
 // Largest radix per super-stage pass, and the preferred / largest column
 // length of the 2D column pass (LDS: lines of 128 bytes x length must fit).
 // Columns of 512 points, the rest of the column transform folded into the
@@ -421,6 +431,13 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
             p->logf = lf;
         }
         p->log_b = logh - p->logf;
+        if (p->log_b > col_cap_log(prec)) {
+            // the fold cannot shorten the columns enough: the column
+            // super-stage of radix up to 16 as a separate pass
+            p->col_split = true;
+            p->logf = std::min(4, logh - col_pref_log(prec));
+            p->log_b = logh - p->logf;
+        }
         if (p->log_b > col_cap_log(prec))
             return fail(FFT_ERR_UNSUPPORTED_SIZE, "no layout for a %lld-point axis over %lld-point rows",
                         1LL << logh, 1LL << p->log_a);
@@ -674,10 +691,10 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             break;
         }
         default:
-            snprintf(buf, len, "rank=%d dims=%lldx%lldx%lld prec=%s path=nd axes=%d fold=%d col_len=%lld",
+            snprintf(buf, len, "rank=%d dims=%lldx%lldx%lld prec=%s path=nd axes=%d %s=%d col_len=%lld",
                      p->rank, (long long)p->dims[0], (long long)(p->rank > 1 ? p->dims[1] : 1),
-                     (long long)(p->rank > 2 ? p->dims[2] : 1), prec, p->nd_k, 1 << p->logf,
-                     p->nd_k >= 2 ? 1LL << p->log_b : 0LL);
+                     (long long)(p->rank > 2 ? p->dims[2] : 1), prec, p->nd_k, p->col_split ? "split" : "fold",
+                     1 << p->logf, p->nd_k >= 2 ? 1LL << p->log_b : 0LL);
             break;
     }
     return FFT_OK;
@@ -825,7 +842,20 @@ static int run_nd(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
         // where the column pass writes: the caller's array when it is the last
         void* col_out = planar ? (last2 ? io.out : workspace) : io.out;
         void* col_out_im = planar && last2 ? io.out_im : nullptr;
-        if (plan->logf == 0) {
+        if (plan->col_split) {
+            // rows (in -> ws), column super-stage (ws -> out, or a second
+            // workspace for planar arrays), column pass (-> col_out)
+            const size_t sig = (size_t)batch * (size_t)plan->n * plan->elem;
+            void* mid = planar ? (char*)workspace + sig : io.out;
+            const BigTwiddle hb{plan->big_hi, plan->big_lo, plan->big_lbits, logh};
+            e = launch_rows(plan->prec, plan->log_a, inv, false, io.in, workspace, nimg << logh, plan->tw_a, 1.0, s,
+                            io.in_im, nullptr);
+            if (e == hipSuccess)
+                e = launch_colstage(plan->prec, plan->logf, workspace, mid, nimg, w, plan->log_b, s);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, mid, col_out, nimg, w, plan->logf, plan->tw_b, hb,
+                                  inv && last2, last2 ? scale : 1.0, s, col_out_im);
+        } else if (plan->logf == 0) {
             void* mid = planar ? workspace : io.out;
             e = launch_rows(plan->prec, plan->log_a, inv, false, io.in, mid, nimg << logh, plan->tw_a, 1.0, s,
                             io.in_im, nullptr);
@@ -854,7 +884,7 @@ static int exec_nd(const fft_plan* plan, int rank, const char* what, int dir, co
                    int64_t batch, void* workspace, void* stream)
 {
     bool noop = false;
-    const size_t ws = plan && batch > 0 && in == out ? c2c_workspace(plan, batch) : 0;
+    const size_t ws = plan && batch > 0 && plan->path == PATH_ND ? nd_workspace(plan, batch, in == out) : 0;
     int st = check_exec(plan, dir, rank, in, out, batch, workspace, ws, &noop);
     if (st != FFT_OK || noop) return st;
     if ((st = check_device(plan)) != FFT_OK) return st;
@@ -884,7 +914,7 @@ static size_t planar_workspace(const fft_plan* p, int64_t batch)
     switch (p->path) {
         case PATH_MULTIPASS: return p->npass >= 3 ? 2 * sig : sig;
         case PATH_BLUESTEIN: return c2c_workspace(p, batch);
-        case PATH_ND: return p->nd_k >= 2 ? sig : 0;
+        case PATH_ND: return p->nd_k >= 2 ? (p->col_split ? 2 * sig : sig) : 0;
         default: return 0;
     }
 }

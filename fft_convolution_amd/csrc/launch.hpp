@@ -75,6 +75,12 @@ hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t 
 hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,
                               const void* tw, bool conj_in, hipStream_t stream, const void* in_im = nullptr);
 
+// 2D column super-stage of radix 2^logf (1..4) as a pass of its own: image
+// rows j + r Lc (r < 2^logf, Lc = 2^log_lc) -> rows j 2^logf + r, for
+// [nimg][2^logf Lc][w] images (w a multiple of 16 bytes / element).  Must not alias.
+hipError_t launch_colstage(int prec, int logf, const void* in, void* out, int64_t nimg, int64_t w, int log_lc,
+                           hipStream_t stream);
+
 // One super-stage pass of a multi-pass Stockham transform of `batch` signals
 // of 2^logn points: radix 2^logr, span 2^logns; kind 0 first, 1 middle, 2
 // last (in place allowed).  big: tables for w_M, M = 2^(logns + logr).

@@ -92,6 +92,45 @@ void cols2d_kernel(const V* in, COut<V, POUT> out, int64_t w, int logf, int64_t 
 }
 
 // ---------------------------------------------------------------------------
+// 2D column super-stage of radix F on its own (for rows too wide to fold F of
+// them into LDS): rows j + r Lc (r < F) of an image are combined, position by
+// position, by an F-point DFT into rows j F + r.  No LDS: each thread takes P
+// adjacent columns (one 16-byte vector per row) of one (image, j); lanes run
+// along the row, so every row access of a wave is contiguous.  Out of place.
+// ---------------------------------------------------------------------------
+template <typename V, int LOGF>
+__global__ __launch_bounds__(256) void colstage_kernel(const V* __restrict__ in, V* __restrict__ out, int64_t w,
+                                                       int log_lc, int64_t total)
+{
+    constexpr int F = 1 << LOGF;
+    constexpr int P = 16 / (int)sizeof(V);
+    const int64_t wp = w / P;  // column vectors per row
+    const int64_t lc = (int64_t)1 << log_lc;
+    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t cv = g % wp, rest = g / wp;
+        const int64_t j = rest & (lc - 1), img = rest >> log_lc;
+        const int64_t base = (img << (log_lc + LOGF)) * w + cv * P;
+        V u[P][F];
+#pragma unroll
+        for (int r = 0; r < F; ++r) {
+            V q[P];
+            vload(in + base + (j + ((int64_t)r << log_lc)) * w, q);
+#pragma unroll
+            for (int e = 0; e < P; ++e) u[e][r] = q[e];
+        }
+#pragma unroll
+        for (int e = 0; e < P; ++e) Dft<F>::run(u[e]);
+#pragma unroll
+        for (int r = 0; r < F; ++r) {
+            V q[P];
+#pragma unroll
+            for (int e = 0; e < P; ++e) q[e] = u[e][r];
+            vstore(out + base + ((j << LOGF) + r) * w, q);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 2D row pass with the column super-stage of radix F folded in: a group of F
 // threads-rows takes rows j + r Lc (r < F) of one image, transforms each row
 // (length W), exchanges through LDS so that every thread holds all F rows at
@@ -366,6 +405,34 @@ hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t 
     FFTMI_LOG_SWITCH(prec, logl, CF, CD)
 #undef CF
 #undef CD
+}
+
+template <typename V, int LOGF>
+static hipError_t colstage_t(const void* in, void* out, int64_t nimg, int64_t w, int log_lc, hipStream_t s)
+{
+    constexpr int P = 16 / (int)sizeof(V);
+    if (w % P) return hipErrorInvalidValue;
+    const int64_t total = (nimg << log_lc) * (w / P);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
+    hipLaunchKernelGGL((colstage_kernel<V, LOGF>), dim3((unsigned)blocks), dim3(256), 0, s, (const V*)in, (V*)out, w,
+                       log_lc, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_colstage(int prec, int logf, const void* in, void* out, int64_t nimg, int64_t w, int log_lc,
+                           hipStream_t s)
+{
+#define CS(F) (prec == 0 ? colstage_t<float2, F>(in, out, nimg, w, log_lc, s) \
+                         : colstage_t<double2, F>(in, out, nimg, w, log_lc, s))
+    switch (logf) {
+        case 1: return CS(1);
+        case 2: return CS(2);
+        case 3: return CS(3);
+        case 4: return CS(4);
+        default: return hipErrorInvalidValue;
+    }
+#undef CS
 }
 
 hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,

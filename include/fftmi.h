@@ -92,10 +92,12 @@ enum fft_status {
  *           batch * M elements plus that of the M-point plan.
  *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
  *           Parallel GLSL", section "Multi-Dimensional Transforms and
- *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*,
- *           except very tall, narrow shapes whose column transform cannot be
- *           split between the two passes (e.g. H = 8192 with W = 2, FFT_C32),
- *           which give FFT_ERR_UNSUPPORTED_SIZE.
+ *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*.
+ *           Columns longer than 512 points are split H = F * Lc: the radix-F
+ *           column stage is folded into the row pass, or, where F rows of
+ *           W points do not fit one workgroup's LDS (e.g. 8192 x 8192
+ *           FFT_C32), runs as a pass of its own (fft_plan_describe shows
+ *           split=F).
  *   rank 3: dims = {D, H, W}, row-major: the 2D transform of every [H][W]
  *           slice, then the D-point transform along the depth axis of every
  *           (y, x) (the same separability, one axis after another); each
@@ -136,11 +138,11 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
  * Batched 2D transform with a rank-2 plan: row transforms of length W over
  * every row, then column transforms of length H over every column.
  *   in, out:   [batch][H][W] complex, images contiguous.  in == out allowed.
- *   workspace: used only by an in-place call (in == out) on a plan that folds
- *              part of the column transform into the row pass (H > 512;
- *              fft_plan_describe shows fold > 1);
- *              it then needs fft_workspace_size(plan, batch) bytes.  Otherwise
- *              it may be NULL.
+ *   workspace: fft_workspace_size(plan, batch) bytes for an in-place call
+ *              (in == out) on a plan that folds part of the column transform
+ *              into the row pass (H > 512; fft_plan_describe shows fold > 1),
+ *              and for every call on a split plan (split=F); otherwise it may
+ *              be NULL.
  * Errors: as fft_exec_c2c.
  */
 int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,

@@ -79,7 +79,6 @@ def _create_status(rank, dims, prec):
     (1, [1 << 25], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (2, [8192, 2], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # column axis cannot be split over 2-point rows
     (3, [8, 6, 8], 0, fm.FFT_ERR_NOT_POW2),
     (3, [0, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
     (3, [4096, 8, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # depth beyond the column-pass range
@@ -102,7 +101,9 @@ def test_plan_create_null_out_pointer():
 def test_valid_plan_without_gpu_is_a_device_error():
     for rank, dims, prec in ((1, [1024], 0), (1, [1 << 24], 0), (2, [64, 32], 1), (1, [1], 0),
                              (3, [16, 8, 32], 0), (3, [4096, 1, 1], 0), (2, [8192, 8], 0),
-                             (1, [1000], 0), (1, [12], 1), (1, [1 << 23], 0)):
+                             (1, [1000], 0), (1, [12], 1), (1, [1 << 23], 0),
+                             (2, [8192, 8192], 0), (2, [4096, 4096], 1), (2, [8192, 2], 0),
+                             (3, [2048, 8192, 8192], 0)):
         st, h = _create_status(rank, dims, prec)
         assert st == fm.FFT_ERR_DEVICE and h is None
         assert "hipGetDevice" in fm.fft_last_error()

@@ -107,3 +107,32 @@ def test_fft2_folded_in_place_needs_workspace(dev):
     torch.cuda.synchronize()
     assert torch.equal(y, z)
     assert rel_rms_rows(_flat(y.cpu().numpy()), _flat(oracle.fft2(x_np))).max() <= fft_tol(h * w)
+
+
+@pytest.mark.parametrize("h,w,dtype,batch", [(8192, 2, torch.complex64, 3), (4096, 2, torch.complex128, 3),
+                                             (4096, 4096, torch.complex128, 1), (8192, 8192, torch.complex64, 1)])
+def test_fft2_split_column_stage(dev, h, w, dtype, batch):
+    """Rows too narrow (fewer points per thread than F) or too wide (F rows
+    over the LDS) to fold the column stage: rows, a separate radix-F column
+    stage, then the column pass -- against the oracle, both directions, in
+    place; these plans need a workspace on every call."""
+    print("case %dx%d %s batch=%d" % (h, w, dtype, batch), flush=True)
+    npdt = np.complex64 if dtype == torch.complex64 else np.complex128
+    x_np = wl.batched_uniform(h * w, batch, seed=h + w, dtype=npdt).reshape(batch, h, w)
+    plan = fm.Plan((h, w), dtype)
+    assert "split=" in plan.describe()
+    x = torch.from_numpy(x_np).to(dev)
+    tol = fft_tol(h * w, dtype == torch.complex128)
+    X = plan.fft2(x)
+    assert rel_rms_rows(_flat(X.cpu().numpy()), _flat(oracle.fft2(x_np))).max() <= tol
+    back = plan.ifft2(X).cpu().numpy()
+    assert rel_rms_rows(_flat(back), _flat(x_np)).max() <= 2 * tol
+    z = x.clone()
+    plan.fft2(z, out=z)
+    torch.cuda.synchronize()
+    assert torch.equal(z, X)
+    # a workspace is required even out of place
+    out = torch.empty_like(x)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, x, out, batch, None)
+    assert e.value.status == fm.FFT_ERR_WORKSPACE

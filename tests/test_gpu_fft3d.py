@@ -71,3 +71,16 @@ def test_fft3_plane_wave_closed_form(dev):
     ref = np.zeros((d, h, w), complex)
     ref[7, 50, 3] = d * h * w
     assert np.max(np.abs(X - ref)) < 1e-5 * d * h * w
+
+
+@pytest.mark.parametrize("d,h,w,dtype", [(4, 8192, 2, torch.complex64), (2, 4096, 4096, torch.complex128)])
+def test_fft3_split_column_stage(dev, d, h, w, dtype):
+    print("case %dx%dx%d %s" % (d, h, w, dtype), flush=True)
+    npdt = np.complex64 if dtype == torch.complex64 else np.complex128
+    x_np = wl.batched_uniform(d * h * w, 1, seed=d + h, dtype=npdt).reshape(1, d, h, w)
+    plan = fm.Plan((d, h, w), dtype)
+    assert "split=" in plan.describe()
+    x = torch.from_numpy(x_np).to(dev)
+    X = plan.fft3(x).cpu().numpy().reshape(1, -1)
+    ref = oracle.fft3(x_np).reshape(1, -1)
+    assert rel_rms_rows(X, ref).max() <= fft_tol(d * h * w, dtype == torch.complex128)

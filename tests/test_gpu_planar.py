@@ -37,6 +37,9 @@ CASES = [
     ((64, 128), torch.complex64, 3),
     ((2048, 256), torch.complex64, 1),     # folded column stage
     ((1024, 64), torch.complex128, 2),     # folded, fp64
+    ((8192, 2), torch.complex64, 3),       # column stage as a pass of its own
+    ((4096, 2), torch.complex128, 2),
+    ((4, 8192, 2), torch.complex64, 1),
     ((1, 1024), torch.complex64, 3),       # one axis longer than 1
     ((1, 1), torch.complex128, 4),
     ((16, 32, 64), torch.complex64, 2),    # 3D
