@@ -1,4 +1,4 @@
-"""Python binding of ``libfftmi.so``, the MI355X (gfx950) power-of-two FFT library.
+"""Python binding of ``libfftmi.so``, the MI355X (gfx950) Stockham FFT library.
 
 The functions below carry the names of the C ABI in ``include/fftmi.h`` and do
 argument marshalling only: device pointers come from PyTorch tensors (or plain
@@ -9,9 +9,11 @@ call fails, the error propagates.
 
 Thin conveniences built on those calls:
 
-* :class:`Plan` -- owns a plan handle; ``fft``/``ifft`` (rank 1), ``fft2``/``ifft2``
-  (rank 2), ``fft3``/``ifft3`` (rank 3) and ``poly_mul`` (rank 1, complex128) on
-  contiguous device tensors.
+* :class:`Plan` -- owns a plan handle; ``fft``/``ifft`` (rank 1, any length up
+  to the limits: power-of-two, mixed-radix 2/3/5/7 or Bluestein), ``fft2``/``ifft2``
+  (rank 2), ``fft3``/``ifft3`` (rank 3), ``planar`` (split re / im tensors, any
+  rank) and ``poly_mul`` (rank 1, complex128) on contiguous device tensors.
+* :class:`RealPlan` -- ``rfft``/``irfft`` of real rows.
 * :func:`poly_mul` -- one-shot integer polynomial products.
 """
 from __future__ import annotations
@@ -150,7 +152,7 @@ def fft_last_error() -> str:
 
 
 def fft_plan_create(rank: int, dims, prec: int = FFT_C32) -> int:
-    """Create a plan (rank 1: dims = [N]; rank 2: dims = [H, W]); returns its handle."""
+    """Create a plan (rank 1: dims = [N]; rank 2: [H, W]; rank 3: [D, H, W]); returns its handle."""
     dims = [int(d) for d in dims]
     arr = (ctypes.c_int64 * max(len(dims), 1))(*dims)
     h = ctypes.c_void_p()
@@ -238,7 +240,7 @@ def fft_planar_workspace_size(plan, batch: int) -> int:
 # --------------------------------------------------------------------------
 
 class Plan:
-    """A plan handle.  ``Plan(n)`` or ``Plan((h, w))``; dtype torch.complex64/128."""
+    """A plan handle.  ``Plan(n)``, ``Plan((h, w))`` or ``Plan((d, h, w))``; dtype torch.complex64/128."""
 
     def __init__(self, dims, dtype=None):
         import torch

@@ -1,5 +1,5 @@
 /*
- * fftmi.h -- C ABI of a power-of-two complex FFT library for one AMD Instinct
+ * fftmi.h -- C ABI of a complex (and real-row) FFT library for one AMD Instinct
  * MI355X (gfx950).
  *
  * The transform computed is the discrete Fourier transform of the page "FFT on
@@ -12,11 +12,14 @@
  * Butterfly: One Thread, One Output") in the out-of-place Stockham autosort
  * form of "Stockham FFT Butterfly Algorithm in Parallel GLSL" (section "The
  * Bit-Reversal Bottleneck and the Stockham Advantage"): no bit-reversal pass,
- * output in natural order.
+ * output in natural order.  Rank-1 lengths that are not powers of two run as
+ * mixed-radix Stockham stages (radices 2, 3, 4, 5, 7, 8) or by Bluestein's
+ * chirp-z convolution on the power-of-two path (fft_plan_create).
  *
  * Conventions shared by every entry point
  *  - Complex data are interleaved (re, im): FFT_C32 = two floats (8 B per
- *    element), FFT_C64 = two doubles (16 B per element).
+ *    element), FFT_C64 = two doubles (16 B per element); fft_exec_planar takes
+ *    split re / im planes instead.
  *  - Every data pointer (in, out, a, b, c, workspace, d_max_residual) is a
  *    DEVICE pointer on the device that was current when the plan was created.
  *    The caller owns all of them; the library never frees or retains them.
@@ -82,14 +85,19 @@ enum fft_status {
  *           rows; larger N runs as two or three Stockham super-stage passes
  *           (radix <= 512 each) through HBM and needs a workspace of one
  *           batch of signals.
- *           N not a power of two (N <= FFT_MAX_BLUESTEIN_N): the chirp-z
- *           (Bluestein) route that "FFT on GPU" (section "Algorithm per
- *           signal Length") names for such lengths: X_k = c_k (x.c * conj c)_k
- *           with c_j = e^{-i pi j^2/N}, the convolution done cyclically at the
- *           power-of-two M >= 2N - 1 by the library's own transforms.  Plan
- *           creation then also runs one fp64 M-point transform on the device
- *           (the spectrum of the chirp), and execution needs a workspace of
- *           batch * M elements plus that of the M-point plan.
+ *           N not a power of two (N <= FFT_MAX_BLUESTEIN_N), the two routes
+ *           "FFT on GPU" (section "Algorithm per signal Length") names for
+ *           such lengths:
+ *           - N = 2^a 3^b 5^c 7^d up to 8192 (C32) / 4096 (C64): mixed-radix
+ *             Stockham stages (radices 8, 4, 2, 3, 5, 7) in one kernel, no
+ *             workspace;
+ *           - any other N: chirp-z (Bluestein), X_k = c_k (x.c * conj c)_k
+ *             with c_j = e^{-i pi j^2/N}, the convolution done cyclically at
+ *             the power-of-two M >= 2N - 1 by the library's own transforms.
+ *             Plan creation then also runs one fp64 M-point transform on the
+ *             device (the spectrum of the chirp).  M <= FFT_MAX_LDS_N_*: one
+ *             kernel, no workspace; larger M: five passes and a workspace of
+ *             batch * M elements plus that of the M-point plan.
  *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
  *           Parallel GLSL", section "Multi-Dimensional Transforms and
  *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*.
