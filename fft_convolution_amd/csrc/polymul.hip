@@ -97,6 +97,12 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
     resid_max(worst, d_resid);
 }
 
+// Tiles of the column passes A and A2: they also move int64 values (8 bytes
+// per lane), so 16 lanes per row segment make those 128-byte segments too
+// (measured on MI355X, 32 x 2^18 products: 329 -> 322 us); 1024-point columns
+// keep 8 (16 would need 2048 threads).
+template <int LOGN2> using PolyTile = Tile<double2, LOGN2, (LOGN2 <= 9 ? 16 : 8)>;
+
 // ---------------------------------------------------------------------------
 // N > 4096: the two real operands travel as one complex signal z = a + i b
 // (both have real coefficients), N = N1 N2 split as n = n1 + N1 n2,
@@ -107,12 +113,12 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
 // w_N^{n1 k2}; written as rows k2 (Y[k2][n1]).
 // ---------------------------------------------------------------------------
 template <int LOGN2>
-__global__ __launch_bounds__((Tile<double2, LOGN2>::THREADS))
+__global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
                        double2* __restrict__ ws, int logn1, const double2* __restrict__ tw, BigTw<double2> big)
 {
     using G = Geom<double2, LOGN2>;
-    using TL = Tile<double2, LOGN2>;
+    using TL = PolyTile<LOGN2>;
     __shared__ double2 lds[TL::LDS];
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -216,12 +222,12 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
 // Pass A2: columns again (k2 -> n2), Re / N, rint, int64 store.
 // ---------------------------------------------------------------------------
 template <int LOGN2>
-__global__ __launch_bounds__((Tile<double2, LOGN2>::THREADS))
+__global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
                         const double2* __restrict__ tw, double* __restrict__ d_resid)
 {
     using G = Geom<double2, LOGN2>;
-    using TL = Tile<double2, LOGN2>;
+    using TL = PolyTile<LOGN2>;
     __shared__ double2 lds[TL::LDS];
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -289,7 +295,7 @@ template <int LOGN2>
 static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* ws,
                                int64_t batch, const void* tw_col, BigTw<double2> big, hipStream_t s)
 {
-    using TL = Tile<double2, LOGN2>;
+    using TL = PolyTile<LOGN2>;
     const int64_t n1 = (int64_t)1 << logn1;
     if (n1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
     const int64_t blocks = batch * (n1 / TL::C);
@@ -316,7 +322,7 @@ template <int LOGN2>
 static hipError_t polypack_a2_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
                                 const void* tw_col, double* d_resid, hipStream_t s)
 {
-    using TL = Tile<double2, LOGN2>;
+    using TL = PolyTile<LOGN2>;
     const int64_t n1 = (int64_t)1 << logn1;
     if (n1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
     const int64_t blocks = batch * (n1 / TL::C);

@@ -11,11 +11,14 @@ namespace fftmi {
 // per position; CL threads side by side cover a 128-byte row segment (the
 // unit the memory system moves without waste); a workgroup owns C = CL P
 // lines and runs the P sets of CL lines through LDS one after another.
-template <typename V, int LOGL> struct Tile {
+// CLMIN: the fewest lanes per row segment (8: 128-byte segments of 16-byte
+// vectors; 16 for passes that also move 8-byte values per lane, so that those
+// come in 128-byte segments too).
+template <typename V, int LOGL, int CLMIN = 8> struct Tile {
     using G = Geom<V, LOGL>;
     static constexpr int P = 16 / (int)sizeof(V);      // complex64: 2, complex128: 1
     static constexpr int CL0 = 256 / G::T;
-    static constexpr int CL = CL0 < 8 ? 8 : (CL0 > 64 ? 64 : CL0);
+    static constexpr int CL = CL0 < CLMIN ? CLMIN : (CL0 > 64 ? 64 : CL0);
     static constexpr int C = CL * P;
     static constexpr int THREADS = CL * G::T;
     static constexpr int LDS = G::S > 1 ? lds_padded(CL * G::N) : 1;
