@@ -29,7 +29,7 @@ __all__ = [
     "FFT_ERR_WORKSPACE", "FFT_ERR_DEVICE",
     "FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64", "FFT_MAX_N_C32", "FFT_MAX_N_C64", "FFT_MAX_BLUESTEIN_N",
     "lib", "lib_path", "EXPORTS",
-    "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
+    "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
     "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar", "fft_planar_workspace_size",
     "fft_status_string", "fft_last_error",
@@ -59,7 +59,7 @@ lib_path = os.path.join(_HERE, "libfftmi.so")
 
 # Every symbol include/fftmi.h declares.
 EXPORTS = (
-    "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_workspace_size",
+    "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
     "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar", "fft_planar_workspace_size",
     "fft_status_string", "fft_last_error",
@@ -95,6 +95,7 @@ def lib():
         L.fft_plan_create.argtypes = [ctypes.POINTER(vp), c_int, ctypes.POINTER(i64), c_int]
         L.fft_plan_destroy.argtypes = [vp]
         L.fft_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
+        L.fft_plan_query.argtypes = [c_int, ctypes.POINTER(i64), c_int, ctypes.c_char_p, sz]
         L.fft_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_exec_c2c.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
         L.fft_exec_2d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
@@ -168,6 +169,15 @@ def fft_plan_destroy(plan) -> None:
 def fft_plan_describe(plan) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib().fft_plan_describe(plan, buf, 256), "fft_plan_describe")
+    return buf.value.decode()
+
+
+def fft_plan_query(rank: int, dims, prec: int = FFT_C32) -> str:
+    """Description of the plan fft_plan_create would make (host only, no device)."""
+    dims = [int(d) for d in dims]
+    arr = (ctypes.c_int64 * max(len(dims), 1))(*dims)
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fft_plan_query(int(rank), arr if dims else None, int(prec), buf, 256), "fft_plan_query")
     return buf.value.decode()
 
 

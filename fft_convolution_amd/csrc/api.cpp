@@ -596,10 +596,10 @@ const char* fft_status_string(int status)
 
 const char* fft_last_error(void) { return g_last_error.c_str(); }
 
-int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec)
+// Validation and layout of a complex plan, on the host only: every size check
+// happens here, before any HIP call.
+static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
 {
-    if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
-    *out_plan = nullptr;
     if (rank < 1 || rank > 3) return fail(FFT_ERR_INVALID_ARG, "rank %d not supported (1, 2 or 3)", rank);
     if (!dims) return fail(FFT_ERR_INVALID_ARG, "dims is NULL");
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
@@ -618,9 +618,6 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
             return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", d, (long long)dims[d],
                         (long long)lim);
     }
-
-    fft_plan* p = new (std::nothrow) fft_plan;
-    if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
     p->rank = rank;
     p->prec = prec;
     p->elem = elem_bytes(prec);
@@ -630,9 +627,17 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
         p->n *= dims[d];
     }
     p->logn = ilog2(p->n);
+    return plan_layout(p, rank, dims, prec);
+}
 
-    // 1. Layout, on the host only: every size check happens before any HIP call.
-    int st = plan_layout(p, rank, dims, prec);
+int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec)
+{
+    if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
+    *out_plan = nullptr;
+    fft_plan* p = new (std::nothrow) fft_plan;
+    if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
+    // 1. Layout, on the host only.
+    int st = plan_prepare(p, rank, dims, prec);
     if (st != FFT_OK) {
         delete p;
         return st;
@@ -650,6 +655,15 @@ int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec
     }
     *out_plan = p;
     return FFT_OK;
+}
+
+int fft_plan_query(int rank, const int64_t* dims, int prec, char* buf, size_t len)
+{
+    if (!buf || len == 0) return fail(FFT_ERR_INVALID_ARG, "buf is NULL");
+    fft_plan p;
+    const int st = plan_prepare(&p, rank, dims, prec);
+    if (st != FFT_OK) return st;
+    return fft_plan_describe(&p, buf, len);
 }
 
 int fft_plan_destroy(fft_plan* plan)

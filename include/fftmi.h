@@ -126,6 +126,12 @@ int fft_plan_destroy(fft_plan* plan);
  * NUL-terminated string of at most len bytes.  Host-only. */
 int fft_plan_describe(const fft_plan* plan, char* buf, size_t len);
 
+/* The description fft_plan_describe would give for the plan that
+ * fft_plan_create(rank, dims, prec) would make, without making it: host-only
+ * (no HIP call, no device needed), the same validation and status codes.
+ * Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE. */
+int fft_plan_query(int rank, const int64_t* dims, int prec, char* buf, size_t len);
+
 /* Bytes of device workspace fft_exec_c2c / fft_exec_2d need for `batch`
  * transforms with this plan (0 when none is needed).  Host-only. */
 int fft_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes);

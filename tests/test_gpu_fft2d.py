@@ -22,6 +22,7 @@ def _flat(a):
     (1, 1, 2), (1, 64, 3), (64, 1, 3), (2, 2, 1), (2, 4096, 1), (4096, 2, 1), (16, 16, 5),
     (32, 64, 3), (64, 32, 2), (8, 8192, 1), (8192, 8, 1), (128, 256, 2), (512, 512, 1),
     (1024, 64, 1), (2048, 2048, 1),
+    (8192, 4, 1), (4096, 8192, 1),   # 2048-point column passes (the cap)
 ])
 def test_fft2_c64(dev, h, w, batch):
     print("case h=%d w=%d batch=%d" % (h, w, batch), flush=True)
@@ -37,7 +38,8 @@ def test_fft2_c64(dev, h, w, batch):
 
 
 @pytest.mark.parametrize("h,w,batch", [(1, 8, 2), (8, 1, 2), (16, 32, 3), (256, 128, 2), (4096, 16, 1),
-                                       (16, 4096, 1), (1024, 1024, 1)])
+                                       (16, 4096, 1), (1024, 1024, 1),
+                                       (2048, 2, 2), (4096, 4, 1), (4096, 2048, 1)])  # 1024-point columns
 def test_fft2_c128(dev, h, w, batch):
     x_np = wl.batched_uniform(h * w, batch, seed=h * 17 + w, dtype=np.complex128).reshape(batch, h, w)
     plan = fm.Plan((h, w), torch.complex128)

@@ -1,0 +1,115 @@
+"""The planner on the CPU (fft_plan_query: the plan fft_plan_create would
+make, without a device): which path each size takes and the sizes the
+kernels are given, checked against the rules the kernels rely on."""
+import math
+
+import pytest
+
+import fft_convolution_amd as fm
+
+LDS_MAX = {0: 8192, 1: 4096}
+MIXED_MAX = {0: 8192, 1: 4096}
+
+
+def _q(rank, dims, prec):
+    return fm.fft_plan_query(rank, dims, prec)
+
+
+def _field(desc, key):
+    for tok in desc.split():
+        if tok.startswith(key + "="):
+            return tok.split("=", 1)[1]
+    return None
+
+
+def _smooth(n):
+    for p in (2, 3, 5, 7):
+        while n % p == 0:
+            n //= p
+    return n == 1
+
+
+@pytest.mark.parametrize("prec", [0, 1])
+def test_power_of_two_paths(prec):
+    top = 26 if prec == 0 else 24
+    for logn in range(0, top + 1):
+        n = 1 << logn
+        d = _q(1, [n], prec)
+        if n == 1:
+            assert "path=copy" in d
+        elif n <= LDS_MAX[prec]:
+            assert "path=rows" in d
+        else:
+            assert "path=multipass" in d
+            r = [int(x) for x in _field(d, "radices").split("x")]
+            # super-stages of at most 512 points, as few as possible, as even as possible, larger first
+            assert math.prod(r) == n and max(r) <= 512
+            assert len(r) == math.ceil(logn / 9)
+            assert r == sorted(r, reverse=True) and r[0] <= 2 * r[-1]
+
+
+@pytest.mark.parametrize("prec", [0, 1])
+def test_every_length_up_to_20000(prec):
+    for n in range(2, 20001):
+        d = _q(1, [n], prec)
+        if n & (n - 1) == 0:
+            continue
+        if _smooth(n) and n <= MIXED_MAX[prec]:
+            assert "path=mixed" in d, (n, d)
+            r = [int(x) for x in _field(d, "radices").split("x")]
+            assert math.prod(r) == n and set(r) <= {2, 3, 4, 5, 7, 8}, (n, d)
+            assert len(r) <= 16
+        else:
+            assert "path=bluestein" in d, (n, d)
+            m = int(_field(d, "m"))
+            assert m & (m - 1) == 0 and m >= 2 * n - 1 and m < 4 * n - 2, (n, d)
+            assert d.endswith("fused") == (m <= LDS_MAX[prec]), (n, d)
+
+
+@pytest.mark.parametrize("prec", [0, 1])
+def test_every_2d_shape_has_a_layout(prec):
+    top = 13 if prec == 0 else 12
+    cap = 2048 if prec == 0 else 1024
+    for lh in range(0, top + 1):
+        for lw in range(0, top + 1):
+            h, w = 1 << lh, 1 << lw
+            d = _q(2, [h, w], prec)
+            assert "path=nd" in d, (h, w, d)
+            axes = int(_field(d, "axes"))
+            assert axes == (h > 1) + (w > 1)
+            if axes < 2:
+                continue
+            f = int(_field(d, "fold") or _field(d, "split"))
+            lc = int(_field(d, "col_len"))
+            # the column transform of H points is split H = F * Lc
+            assert f * lc == h and lc <= cap and f <= 16, (h, w, d)
+            if h <= 512:
+                assert f == 1 and "fold=" in d, (h, w, d)
+            if "split=" in d:
+                # only where F rows cannot be folded into the row pass
+                assert w == 2 or w * (1 if prec == 0 else 2) >= 8192 or lc > 512, (h, w, d)
+
+
+def test_3d_layouts():
+    assert "axes=3" in _q(3, [256, 256, 256], 0)
+    assert "axes=2" in _q(3, [1, 64, 128], 0)
+    assert "axes=1" in _q(3, [1, 1, 4096], 1)
+    assert "split=" in _q(3, [4, 8192, 2], 0)
+    with pytest.raises(fm.FFTError) as e:
+        _q(3, [4096, 8, 8], 0)
+    assert e.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE
+
+
+@pytest.mark.parametrize("rank,dims,prec,status", [
+    (0, [8], 0, fm.FFT_ERR_INVALID_ARG),
+    (1, [0], 0, fm.FFT_ERR_INVALID_ARG),
+    (1, [8], 5, fm.FFT_ERR_INVALID_ARG),
+    (2, [12, 8], 0, fm.FFT_ERR_NOT_POW2),
+    (1, [(1 << 23) + 1], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+])
+def test_query_rejects_as_create_does(rank, dims, prec, status):
+    with pytest.raises(fm.FFTError) as e:
+        _q(rank, dims, prec)
+    assert e.value.status == status
