@@ -726,13 +726,11 @@ int fft_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
 // Rank-1 execution on validated arguments.  io.in_im / io.out_im non-NULL:
 // planar arrays; the multi-pass path then runs its middle passes through the
 // workspace (two signal-sized buffers for three passes) instead of `out`.
-static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s,
-                  void* stream)
+static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s)
 {
     const bool planar = io.in_im != nullptr;
     const double scale = 1.0 / (double)plan->n;
     hipError_t e = hipSuccess;
-    int st = FFT_OK;
     switch (plan->path) {
         case PATH_COPY: {
             const size_t bytes = (size_t)batch * plan->elem;
@@ -779,18 +777,47 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
                                           io.out_im);
                 break;
             }
-            void* w = workspace;
-            void* inner_ws = (char*)workspace + ((size_t)batch << plan->logm) * plan->elem;
-            e = launch_chirp_pre(plan->prec, io.in, w, plan->n, plan->logm, batch, plan->chirp, inv, s, io.in_im);
-            if (e != hipSuccess) break;
-            st = fft_exec_c2c(plan->inner, FFT_FORWARD, w, w, batch, inner_ws, stream);
-            if (st != FFT_OK) return st;
-            e = launch_cmul_table(plan->prec, w, plan->logm, batch, plan->bspec, s);
-            if (e != hipSuccess) break;
-            st = fft_exec_c2c(plan->inner, FFT_INVERSE, w, w, batch, inner_ws, stream);
-            if (st != FFT_OK) return st;
-            e = launch_chirp_post(plan->prec, w, io.out, plan->n, plan->logm, batch, plan->chirp, inv, scale, s,
-                                  io.out_im);
+            // M beyond one workgroup: the M-point multi-pass transforms, the
+            // chirp products and the product with B riding on their first and
+            // last passes; buffers A, B of batch x M in the workspace.
+            // forward:  x c -> A (-> B) -> conj(W B) in B
+            // inverse:  B -> A (-> B) -> c conj(.) / M -> out
+            const fft_plan* mp = plan->inner;
+            const int np = mp->npass;
+            void* A = workspace;
+            void* B = (char*)workspace + ((size_t)batch << plan->logm) * plan->elem;
+            const ChirpArgs c{io.in, io.in_im, io.out, io.out_im, plan->chirp, plan->bspec, plan->n, inv, inv, scale};
+            const void* src = nullptr;
+            for (int q = 0; q < np && e == hipSuccess; ++q) {
+                const PassPlan& pp = mp->passes[q];
+                const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, pp.logns + pp.logr};
+                if (q == 0) {
+                    e = launch_bluestein_pass(plan->prec, pp.logr, 0, nullptr, A, plan->logm, pp.logns, batch, pp.tw,
+                                              big, c, s);
+                    src = A;
+                } else if (q == np - 1) {
+                    e = launch_bluestein_pass(plan->prec, pp.logr, 2, src, B, plan->logm, pp.logns, batch, pp.tw, big,
+                                              c, s);
+                } else {
+                    e = launch_stock_pass(plan->prec, pp.logr, pp.kind, src, B, plan->logm, pp.logns, batch, pp.tw,
+                                          big, false, false, 1.0, s);
+                    src = B;
+                }
+            }
+            src = B;
+            for (int q = 0; q < np && e == hipSuccess; ++q) {
+                const PassPlan& pp = mp->passes[q];
+                const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, pp.logns + pp.logr};
+                if (q == np - 1) {
+                    e = launch_bluestein_pass(plan->prec, pp.logr, 4, src, nullptr, plan->logm, pp.logns, batch,
+                                              pp.tw, big, c, s);
+                } else {
+                    void* dst = q == 0 ? A : B;
+                    e = launch_stock_pass(plan->prec, pp.logr, pp.kind, src, dst, plan->logm, pp.logns, batch, pp.tw,
+                                          big, false, false, 1.0, s);
+                    src = dst;
+                }
+            }
             break;
         }
         default:
@@ -819,7 +846,7 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
     if ((st = check_device(plan)) != FFT_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     const Io io{in, nullptr, out, nullptr};
-    st = run_1d(plan, dir == FFT_INVERSE, io, batch, workspace, s, stream);
+    st = run_1d(plan, dir == FFT_INVERSE, io, batch, workspace, s);
     if (st != FFT_OK) return st;
     return sync_if_asked(s, "fft_exec_c2c (FFTMI_SYNC)");
 }
@@ -977,7 +1004,7 @@ int fft_exec_planar(const fft_plan* plan, int dir, const void* in_re, const void
     hipStream_t s = (hipStream_t)stream;
     const Io io{in_re, in_im, out_re, out_im};
     const bool inv = dir == FFT_INVERSE;
-    st = plan->rank == 1 ? run_1d(plan, inv, io, batch, workspace, s, stream) : run_nd(plan, inv, io, batch, workspace, s);
+    st = plan->rank == 1 ? run_1d(plan, inv, io, batch, workspace, s) : run_nd(plan, inv, io, batch, workspace, s);
     if (st != FFT_OK) return st;
     return sync_if_asked(s, "fft_exec_planar (FFTMI_SYNC)");
 }

@@ -106,19 +106,37 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
                                    void* ws, const void* tw_row, const void* tw_col, BigTwiddle big,
                                    double* d_resid, hipStream_t stream);
 
-// Bluestein element-wise steps (bluestein.hip): rows of n points padded to 2^logm.
-hipError_t launch_chirp_pre(int prec, const void* in, void* w, int64_t n, int logm, int64_t batch, const void* chirp,
-                            bool conj_in, hipStream_t stream, const void* in_im = nullptr);
-hipError_t launch_cmul_table(int prec, void* w, int logm, int64_t batch, const void* tab, hipStream_t stream);
-hipError_t launch_chirp_post(int prec, const void* w, void* out, int64_t n, int logm, int64_t batch,
-                             const void* chirp, bool conj_out, double scale, hipStream_t stream,
-                             void* out_im = nullptr);
 // The whole Bluestein transform of each row in one kernel, M = 2^logm within
 // the row kernel's range (logm <= 13 complex64, 12 complex128); tw: stage
 // table for M.  Planar needs both in_im and out_im.  in -> out, may alias.
 hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void* out, int64_t nrows, const void* tw,
                                  const void* chirp, const void* bspec, bool conj_in, bool conj_out, double scale,
                                  hipStream_t stream, const void* in_im = nullptr, void* out_im = nullptr);
+// Bluestein beyond the row kernel's range: the chirp products and the
+// product with B carried by the first / last passes of the M-point
+// multi-pass transforms (chirp_io.hpp).  x / y: the caller's rows of n points
+// (x_im / y_im non-NULL: planar); conj_in / conj_out and scale (1/n) for an
+// inverse transform.
+struct ChirpArgs {
+    const void* x;
+    const void* x_im;
+    void* y;
+    void* y_im;
+    const void* chirp;
+    const void* bspec;
+    int64_t n;
+    bool conj_in;
+    bool conj_out;
+    double scale;
+};
+// One pass of radix 2^logr of a transform of 2^logm points over [batch][M]:
+// mode 0 = first forward pass (reads x times the chirp, zero padded; out:
+// interleaved), 2 = last forward pass (stores conj(W B) to out), 4 = last
+// inverse pass (stores the chirp times the convolution to y).  Middle passes
+// and the inverse's first pass are plain launch_stock_pass calls.
+hipError_t launch_bluestein_pass(int prec, int logr, int mode, const void* in, void* out, int logm, int logns,
+                                 int64_t batch, const void* tw, BigTwiddle big, const ChirpArgs& c,
+                                 hipStream_t stream);
 // complex128 -> complex64, `total` elements.
 hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t stream);
 

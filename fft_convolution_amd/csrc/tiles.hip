@@ -24,6 +24,7 @@
 // super-stage writes the positions it reads (in place); the first writes each
 // butterfly's R outputs contiguously, so it hands the data from lanes-across-
 // lines to lanes-along-a-line inside its LDS exchange (fft_regs_remap).
+#include "chirp_io.hpp"
 #include "io.hpp"
 #include "launch.hpp"
 #include "stockham.hpp"
@@ -201,11 +202,12 @@ void rows2d_fold_kernel(CIn<V, PIN> in, V* out, int64_t ngroups, int log_lc, con
 // Multi-pass Stockham super-stage (large 1D).  KIND 0: first (span 1, stored
 // along lines after a remap), 1: middle, 2: last (in place).
 // ---------------------------------------------------------------------------
-template <typename V, int LOGR, int KIND, bool CONJ_IN, bool CONJ_OUT, bool PL>
+// IN: ldv(index, P values); OUT: st_plain (KIND 0) or stv (KIND 1, 2) -- the
+// caller's arrays (io.hpp), or the chirp-z steps of chirp_io.hpp.
+template <typename V, int LOGR, int KIND, bool CONJ_IN, bool CONJ_OUT, typename IN, typename OUT>
 __global__ __launch_bounds__((Tile<V, LOGR>::THREADS))
-void stock_pass_kernel(CIn<V, PL && KIND == 0> in, COut<V, PL && KIND == 2> out, int logn, int logns,
-                       int64_t tiles_per_sig, const V* __restrict__ tw, BigTw<V> big,
-                       typename real_of<V>::type scale)
+void stock_pass_kernel(IN in, OUT out, int logn, int logns, int64_t tiles_per_sig, const V* __restrict__ tw,
+                       BigTw<V> big, typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGR>;
     using TL = Tile<V, LOGR>;
@@ -340,9 +342,9 @@ static hipError_t fold_t(const void* in, const void* in_im, void* out, int64_t n
     }
 }
 
-template <typename V, int LOGR, int KIND>
-static hipError_t stock_t(const Io& io, int logn, int logns, int64_t batch, const void* tw, BigTwiddle bt, bool ci,
-                          bool co, double scale, hipStream_t s)
+template <typename V, int LOGR, int KIND, bool CI, bool CO, typename IN, typename OUT>
+static hipError_t stock_launch(IN in, OUT out, int logn, int logns, int64_t batch, const void* tw, BigTwiddle bt,
+                               double scale, hipStream_t s)
 {
     using TL = Tile<V, LOGR>;
     if (TL::THREADS > 1024) return hipErrorInvalidValue;
@@ -354,10 +356,19 @@ static hipError_t stock_t(const Io& io, int logn, int logns, int64_t batch, cons
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
     const BigTw<V> big{(const V*)bt.hi, (const V*)bt.lo, bt.lbits, bt.logn};
-#define FFTMI_SP(CI, CO, PL)                                                                                  \
-    hipLaunchKernelGGL((stock_pass_kernel<V, LOGR, KIND, CI, CO, PL>), grid_of(blocks), dim3(TL::THREADS), 0, s, \
-                       make_in<V, PL && KIND == 0>(io.in, io.in_im), make_out<V, PL && KIND == 2>(io.out, io.out_im), \
-                       logn, logns, tps, (const V*)tw, big, (Rl)scale)
+    hipLaunchKernelGGL((stock_pass_kernel<V, LOGR, KIND, CI, CO, IN, OUT>), grid_of(blocks), dim3(TL::THREADS), 0, s,
+                       in, out, logn, logns, tps, (const V*)tw, big, (Rl)scale);
+    return hipGetLastError();
+}
+
+template <typename V, int LOGR, int KIND>
+static hipError_t stock_t(const Io& io, int logn, int logns, int64_t batch, const void* tw, BigTwiddle bt, bool ci,
+                          bool co, double scale, hipStream_t s)
+{
+#define FFTMI_SP(CI, CO, PL)                                                                                 \
+    return stock_launch<V, LOGR, KIND, CI, CO>(make_in<V, PL && KIND == 0>(io.in, io.in_im),                \
+                                               make_out<V, PL && KIND == 2>(io.out, io.out_im), logn, logns, \
+                                               batch, tw, bt, scale, s)
     // Planar: the first pass reads the caller's planes (no conjugated store),
     // the last writes them (no conjugated load).
     const bool pl = io.in_im != nullptr || io.out_im != nullptr;
@@ -378,7 +389,54 @@ static hipError_t stock_t(const Io& io, int logn, int logns, int64_t batch, cons
     else if (co) FFTMI_SP(false, true, false);
     else FFTMI_SP(false, false, false);
 #undef FFTMI_SP
-    return hipGetLastError();
+}
+
+// Bluestein's passes (chirp_io.hpp): mode 0 = first forward pass (chirp in),
+// 2 = last forward pass (x B, conjugated), 4 = last inverse pass (chirp out).
+template <typename V, int LOGR, bool PL>
+static hipError_t bluestein_pass_t(int mode, const void* in, void* out, int logm, int logns, int64_t batch,
+                                   const void* tw, BigTwiddle bt, const ChirpArgs& c, hipStream_t s)
+{
+    using Rl = typename real_of<V>::type;
+    if (mode == 0) {
+        const ChirpIn<V, PL> ci{make_in<V, PL>(c.x, c.x_im), (const V*)c.chirp, c.n, logm, (int)c.conj_in};
+        return stock_launch<V, LOGR, 0, false, false>(ci, make_out<V, false>(out, nullptr), logm, logns, batch, tw,
+                                                       bt, 1.0, s);
+    }
+    if constexpr (!PL) {
+        if (mode == 2) {
+            const MulConjOut<V> mo{(V*)out, (const V*)c.bspec, logm};
+            return stock_launch<V, LOGR, 2, false, false>(make_in<V, false>(in, nullptr), mo, logm, logns, batch, tw,
+                                                           bt, 1.0, s);
+        }
+    }
+    if (mode == 4) {
+        const ChirpOut<V, PL> co{make_out<V, PL>(c.y, c.y_im), (const V*)c.chirp, c.n, logm, (int)c.conj_out,
+                                 (Rl)c.scale, (Rl)(1.0 / (double)((int64_t)1 << logm))};
+        return stock_launch<V, LOGR, 2, false, false>(make_in<V, false>(in, nullptr), co, logm, logns, batch, tw, bt,
+                                                       1.0, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bluestein_pass(int prec, int logr, int mode, const void* in, void* out, int logm, int logns,
+                                 int64_t batch, const void* tw, BigTwiddle big, const ChirpArgs& c, hipStream_t s)
+{
+    // planar only where the pass touches the caller's arrays
+    const bool pl = mode == 0 ? c.x_im != nullptr : mode == 4 ? c.y_im != nullptr : false;
+#define BP(L) (prec == 0 ? (pl ? bluestein_pass_t<float2, L, true>(mode, in, out, logm, logns, batch, tw, big, c, s)   \
+                               : bluestein_pass_t<float2, L, false>(mode, in, out, logm, logns, batch, tw, big, c, s)) \
+                         : (pl ? bluestein_pass_t<double2, L, true>(mode, in, out, logm, logns, batch, tw, big, c, s)  \
+                               : bluestein_pass_t<double2, L, false>(mode, in, out, logm, logns, batch, tw, big, c, s)))
+    switch (logr) {
+        case 5: return BP(5);
+        case 6: return BP(6);
+        case 7: return BP(7);
+        case 8: return BP(8);
+        case 9: return BP(9);
+        default: return hipErrorInvalidValue;
+    }
+#undef BP
 }
 
 #define FFTMI_LOG_SWITCH(PREC, L, CALL_F, CALL_D)                                     \
