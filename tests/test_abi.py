@@ -155,3 +155,15 @@ def test_binding_raises_fft_error():
         fm.fft_plan_create(2, [6, 8], fm.FFT_C32)
     assert ei.value.status == fm.FFT_ERR_NOT_POW2
     assert "not a power of two" in str(ei.value)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(fm, "_lib", None)
+    monkeypatch.setattr(fm, "lib_path", str(tmp_path / "libfftmi.so"))
+    with pytest.raises(ImportError):
+        fm.lib()
+    with pytest.raises(ImportError):
+        fm.fft_plan_query(1, [1024], fm.FFT_C32)
+    with pytest.raises(ImportError):
+        fm.fft_status_string(0)
