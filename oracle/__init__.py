@@ -24,6 +24,9 @@ What it computes, and the passage each part follows:
   ``ifft`` of the Hermitian extension of N/2 + 1 values, the imaginary parts
   of X_0 and X_{N/2} taken as zero.  The operands of polynomial multiplication
   are real ("FFT on GPU", polynomial-multiplication section).
+  ``rfft2`` / ``irfft2`` -- the same for real [H][W] images: columns 0 .. W/2
+  of ``fft2``; back, the inverse column transforms (complex), then ``irfft``
+  of every row.
 * ``polymul_fft`` -- forward both zero-padded operands, pointwise product,
   inverse, rint ("FFT on GPU", polynomial-multiplication and whole-process
   sections); ``schoolbook`` / ``schoolbook_sample`` -- the exact convolution
@@ -198,6 +201,29 @@ def irfft(X, n: int) -> np.ndarray:
         full[..., h] = full[..., h].real
         full[..., h + 1:] = np.conj(X[..., 1:h][..., ::-1])
     return ifft(full).real
+
+
+def rfft2(x) -> np.ndarray:
+    """Columns 0 .. W/2 of the 2D transform of real [..., H, W] images:
+    [..., H, W // 2 + 1] complex128."""
+    x = np.asarray(x)
+    if np.iscomplexobj(x):
+        raise TypeError("rfft2 takes real images")
+    w = x.shape[-1]
+    return fft2(x.astype(np.float64))[..., : w // 2 + 1]
+
+
+def irfft2(X, shape) -> np.ndarray:
+    """Real [..., H, W] images from columns 0 .. W/2 of their 2D transform:
+    the inverse transform along the columns (complex, 1/H), then
+    :func:`irfft` of every row (1/W; the imaginary parts of columns 0 and W/2
+    of that intermediate are dropped, as a real row's are real there)."""
+    h, w = shape
+    X = _as_c128(X)
+    if X.shape[-2:] != (h, w // 2 + 1):
+        raise ValueError("irfft2 of %dx%d takes %dx%d values" % (h, w, h, w // 2 + 1))
+    cols = np.swapaxes(ifft(np.ascontiguousarray(np.swapaxes(X, -1, -2))), -1, -2)
+    return irfft(np.ascontiguousarray(cols), w)
 
 
 def fft2(x, inverse: bool = False) -> np.ndarray:

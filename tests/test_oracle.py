@@ -409,6 +409,36 @@ def test_rfft_closed_forms_and_hermitian_half():
     assert np.abs(imp - want).max() < 1e-13
 
 
+@pytest.mark.parametrize("h,w", [(1, 2), (2, 1 << 1), (4, 8), (16, 64), (64, 2), (128, 256)])
+def test_rfft2_irfft2_match_numpy(h, w):
+    rng = np.random.default_rng(h * 1000 + w)
+    x = rng.standard_normal((2, h, w))
+    X = oracle.rfft2(x)
+    assert X.shape == (2, h, w // 2 + 1)
+    ref = np.fft.rfft2(x)
+    assert np.abs(X - ref).max() <= 1e-12 * np.abs(ref).max()
+    assert np.abs(oracle.irfft2(X, (h, w)) - x).max() <= 1e-12
+    # any half spectrum, as numpy's irfft2 takes it
+    Y = rng.standard_normal((2, h, w // 2 + 1)) + 1j * rng.standard_normal((2, h, w // 2 + 1))
+    assert np.abs(oracle.irfft2(Y, (h, w)) - np.fft.irfft2(Y, s=(h, w))).max() <= 1e-12
+
+
+def test_rfft2_closed_form():
+    """cos(2 pi (fy y / H + fx x / W)) -> H W / 2 at (fy, fx) (and its mirror
+    (-fy, -fx), which lands in the stored half only for fx = 0 or W/2)."""
+    h, w = 32, 64
+    y = np.arange(h)[:, None]
+    xx = np.arange(w)[None, :]
+    for fy, fx in ((3, 5), (0, 7), (5, 0), (0, 0), (7, w // 2)):
+        img = np.cos(2 * np.pi * (((fy * y) % h) / h + ((fx * xx) % w) / w))
+        X = oracle.rfft2(img[None])[0]
+        want = np.zeros((h, w // 2 + 1), dtype=complex)
+        want[fy, fx] += h * w / 2
+        if fx in (0, w // 2):
+            want[(-fy) % h, fx] += h * w / 2
+        assert np.abs(X - want).max() < 1e-9
+
+
 def test_polymul_worked_example():
     rows = {r[0]: [int(v) for v in r[1:]] for r in _golden_rows("polymul_worked.txt")}
     a, b, c = rows["a"], rows["b"], rows["c"]
