@@ -31,8 +31,8 @@ __all__ = [
     "lib", "lib_path", "EXPORTS",
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
-    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar", "fft_planar_workspace_size",
-    "fft_status_string", "fft_last_error",
+    "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar",
+    "fft_planar_workspace_size", "fft_status_string", "fft_last_error",
     "Plan", "RealPlan", "poly_mul",
 ]
 
@@ -61,8 +61,8 @@ lib_path = os.path.join(_HERE, "libfftmi.so")
 EXPORTS = (
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
-    "fft_plan_create_real", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar", "fft_planar_workspace_size",
-    "fft_status_string", "fft_last_error",
+    "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar",
+    "fft_planar_workspace_size", "fft_status_string", "fft_last_error",
 )
 
 _lock = threading.Lock()
@@ -103,6 +103,7 @@ def lib():
         L.fft_poly_mul_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_poly_mul.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, vp, vp]
         L.fft_plan_create_real.argtypes = [ctypes.POINTER(vp), i64, c_int]
+        L.fft_plan_create_real_2d.argtypes = [ctypes.POINTER(vp), i64, i64, c_int]
         L.fft_exec_r2c.argtypes = [vp, vp, vp, i64, vp, vp]
         L.fft_exec_c2r.argtypes = [vp, vp, vp, i64, vp, vp]
         L.fft_exec_planar.argtypes = [vp, c_int, vp, vp, vp, vp, i64, vp, vp]
@@ -221,6 +222,13 @@ def fft_plan_create_real(n: int, prec: int = FFT_C32) -> int:
     h = ctypes.c_void_p()
     _check(lib().fft_plan_create_real(ctypes.byref(h), int(n), int(prec)), "fft_plan_create_real")
     return h.value
+
+
+def fft_plan_create_real_2d(h: int, w: int, prec: int = FFT_C32) -> int:
+    """Create a plan for real [h][w] images; returns its handle."""
+    hd = ctypes.c_void_p()
+    _check(lib().fft_plan_create_real_2d(ctypes.byref(hd), int(h), int(w), int(prec)), "fft_plan_create_real_2d")
+    return hd.value
 
 
 def fft_exec_r2c(plan, in_, out, batch: int, workspace=None, stream=None) -> None:
@@ -383,10 +391,12 @@ class Plan:
 
 
 class RealPlan:
-    """A plan for real rows of n points: ``rfft`` [..., n] float32/64 ->
-    [..., n // 2 + 1] complex64/128, ``irfft`` the reverse."""
+    """A plan for real rows of n points (``RealPlan(n)``) or real [h][w]
+    images (``RealPlan((h, w))``): ``rfft`` [..., n] / [..., h, w] float32/64
+    -> [..., n // 2 + 1] / [..., h, w // 2 + 1] complex64/128, ``irfft`` the
+    reverse."""
 
-    def __init__(self, n: int, dtype=None):
+    def __init__(self, dims, dtype=None):
         import torch
         if dtype is None:
             dtype = torch.float32
@@ -395,8 +405,15 @@ class RealPlan:
         self.dtype = dtype
         self.cdtype = torch.complex64 if dtype == torch.float32 else torch.complex128
         self.prec = FFT_C32 if dtype == torch.float32 else FFT_C64
-        self.n = int(n)
-        self.handle = fft_plan_create_real(self.n, self.prec)
+        self.dims = (int(dims),) if isinstance(dims, int) else tuple(int(d) for d in dims)
+        self.n = self.dims[-1]
+        self.rows = self.dims[0] if len(self.dims) == 2 else 1
+        if len(self.dims) == 1:
+            self.handle = fft_plan_create_real(self.n, self.prec)
+        elif len(self.dims) == 2:
+            self.handle = fft_plan_create_real_2d(self.dims[0], self.dims[1], self.prec)
+        else:
+            raise ValueError("real plans have one or two dims")
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -410,8 +427,9 @@ class RealPlan:
     def describe(self) -> str:
         return fft_plan_describe(self.handle)
 
-    @staticmethod
-    def _check(x, dtype, last):
+    def _check(self, x, dtype, last):
+        """Validates a tensor ending in [rows][last] (rows = h for images);
+        returns the number of transforms."""
         import torch
         if not isinstance(x, torch.Tensor) or not x.is_cuda:
             raise TypeError("expected a device tensor")
@@ -419,9 +437,9 @@ class RealPlan:
             raise TypeError("expected %s, got %s" % (dtype, x.dtype))
         if not x.is_contiguous():
             raise ValueError("tensor must be contiguous")
-        if x.shape[-1] != last:
-            raise ValueError("last dim %d, expected %d" % (x.shape[-1], last))
-        return x.numel() // last
+        if x.shape[-1] != last or (len(self.dims) == 2 and (x.dim() < 2 or x.shape[-2] != self.rows)):
+            raise ValueError("trailing dims %s do not fit the plan %s" % (tuple(x.shape), self.dims))
+        return x.numel() // (last * self.rows)
 
     def _ws(self, batch, device):
         import torch

@@ -212,6 +212,12 @@ struct fft_plan {
     // real rows of N = 2H points: inner = the complex plan of length H,
     // big_* = w_N, log_a = log2 H; real_fused: H within the rows kernel's range.
     bool real_fused = false;
+    // real images [H][W] (rank 2): the W-point rows as above, then the H-point
+    // columns over W/2 + 1 columns: tw_b = stage table for 2^log_b, logf > 0:
+    // a radix-2^logf column stage first, col_* = tables for w_H.
+    void* col_hi = nullptr;
+    void* col_lo = nullptr;
+    int col_lbits = 0;
     void* chirp = nullptr;
     void* bspec = nullptr;
     fft_plan* inner = nullptr;
@@ -259,7 +265,7 @@ int upload(const std::vector<double>& host, int prec, void** dev)
 void free_plan(fft_plan* p)
 {
     if (!p) return;
-    void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo, p->chirp, p->bspec};
+    void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo, p->chirp, p->bspec, p->col_hi, p->col_lo};
     for (void* q : ptrs)
         if (q) hipFree(q);
     for (int i = 0; i < 4; ++i) {
@@ -343,6 +349,8 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
         return (int64_t(1) << p->logm) <= max_lds_n(p->prec)
                    ? 0
                    : ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
+    if (p->path == PATH_REAL && p->rank == 2)  // the half spectrum of every image (C2R; R2C with a column stage)
+        return p->dims[0] > 1 ? (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem : 0;
     if (p->path == PATH_REAL)  // the H-point spectrum of every row, beyond the one-kernel range
         return p->real_fused || p->n == 1 ? 0 : (size_t)batch * (size_t)(p->n / 2) * p->elem;
     const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_ND && p->logf > 0);
@@ -695,8 +703,13 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             break;
         }
         case PATH_REAL:
-            snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
-                     p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
+            if (p->rank == 2)
+                snprintf(buf, len, "real dims=%lldx%lld prec=%s path=real2d col_stage=%d col_len=%lld",
+                         (long long)p->dims[0], (long long)p->dims[1], prec, 1 << p->logf,
+                         p->dims[0] > 1 ? 1LL << p->log_b : 0LL);
+            else
+                snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
+                         p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
             break;
         case PATH_MULTIPASS: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
@@ -1128,9 +1141,57 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     return FFT_OK;
 }
 
+int fft_plan_create_real_2d(fft_plan** out_plan, int64_t h, int64_t w, int prec)
+{
+    if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
+    *out_plan = nullptr;
+    if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
+    if (h < 1 || w < 1) return fail(FFT_ERR_INVALID_ARG, "dims %lld x %lld < 1", (long long)h, (long long)w);
+    if (!is_pow2(h) || !is_pow2(w))
+        return fail(FFT_ERR_NOT_POW2, "dims %lld x %lld are not powers of two", (long long)h, (long long)w);
+    if (h > max_lds_n(prec) || w > 2 * max_lds_n(prec))
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims %lld x %lld exceed %lld x %lld", (long long)h, (long long)w,
+                    (long long)max_lds_n(prec), (long long)(2 * max_lds_n(prec)));
+    fft_plan* p = new (std::nothrow) fft_plan;
+    if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
+    p->rank = 2;
+    p->path = PATH_REAL;
+    p->prec = prec;
+    p->elem = elem_bytes(prec);
+    p->dims[0] = h;
+    p->dims[1] = w;
+    p->n = h * w;
+    p->logn = ilog2(w);  // the row length; the row tables are for w_W
+    p->log_a = p->logn > 0 ? p->logn - 1 : 0;
+    p->real_fused = w >= 2;
+    const int logh = ilog2(h);
+    if (logh > col_pref_log(prec)) p->logf = std::min(4, logh - col_pref_log(prec));
+    p->log_b = logh - p->logf;
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "hipGetDevice");
+    }
+    int st = FFT_OK;
+    if (w >= 2) {
+        const int64_t half = w / 2;
+        st = fft_plan_create(&p->inner, 1, &half, prec);
+        const int want = p->log_a - plan_loge(p->log_a, plan_lem(prec));
+        if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits, want);
+    }
+    if (st == FFT_OK && h > 1) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
+    if (st == FFT_OK && p->logf > 0) st = upload_big(logh, prec, &p->col_hi, &p->col_lo, &p->col_lbits);
+    if (st != FFT_OK) {
+        free_plan(p);
+        return st;
+    }
+    *out_plan = p;
+    return FFT_OK;
+}
+
 // Checks of fft_exec_r2c / fft_exec_c2r: `in_bytes` / `out_bytes` per row.
 static int check_real_exec(const fft_plan* plan, const void* in, size_t in_row, const void* out, size_t out_row,
-                           int64_t batch, void* workspace, bool* noop)
+                           int64_t batch, void* workspace, bool need_ws, bool* noop)
 {
     *noop = false;
     if (!plan) return fail(FFT_ERR_INVALID_ARG, "plan is NULL");
@@ -1141,13 +1202,13 @@ static int check_real_exec(const fft_plan* plan, const void* in, size_t in_row, 
         return FFT_OK;
     }
     if (!in || !out) return fail(FFT_ERR_INVALID_ARG, "in or out is NULL");
-    if (batch > INT64_MAX / (int64_t)((plan->n + 2) * plan->elem))
+    if (batch > INT64_MAX / (int64_t)((plan->n + 2 * plan->dims[0] + 2) * plan->elem))
         return fail(FFT_ERR_INVALID_ARG, "batch %lld overflows the buffer size", (long long)batch);
     if (((uintptr_t)in | (uintptr_t)out) % plan->elem)
         return fail(FFT_ERR_ALIGN, "in/out must be aligned to %zu bytes", plan->elem);
     const size_t bi = (size_t)batch * in_row, bo = (size_t)batch * out_row;
     if (ranges_overlap(in, bi, out, bo)) return fail(FFT_ERR_OVERLAP, "in and out overlap");
-    const size_t ws = c2c_workspace(plan, batch);
+    const size_t ws = need_ws ? c2c_workspace(plan, batch) : 0;
     if (ws) {
         if (!workspace) return fail(FFT_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
         if ((uintptr_t)workspace % plan->elem) return fail(FFT_ERR_ALIGN, "workspace misaligned");
@@ -1167,14 +1228,73 @@ static int real_done(hipError_t e, const char* what, hipStream_t s)
     return FFT_OK;
 }
 
+// Real images [batch][H][W] <-> [batch][H][W/2 + 1]: the rows (real-row
+// kernels), then the columns of the half spectrum (one column per lane).
+static int exec_real_2d(const fft_plan* plan, bool c2r, const void* in, void* out, int64_t batch, void* workspace,
+                        hipStream_t s)
+{
+    const int64_t h = plan->dims[0], w = plan->dims[1], wc = w / 2 + 1;
+    const int64_t rows = batch * h;
+    const BigTwiddle none{nullptr, nullptr, 0, 0};
+    const BigTwiddle hb{plan->col_hi, plan->col_lo, plan->col_lbits, plan->log_b + plan->logf};
+    hipError_t e = hipSuccess;
+    auto row_pass = [&](const void* src, void* dst) {
+        return w == 1 ? launch_real_n1(plan->prec, c2r, src, dst, rows, s)
+                      : launch_real_rows(plan->prec, plan->log_a, c2r, src, dst, rows, plan->inner->tw_a,
+                                         plan->big_hi, plan->big_lo, s);
+    };
+    if (h == 1) return real_done(row_pass(in, out), c2r ? "fft_exec_c2r" : "fft_exec_r2c", s);
+    if (!c2r) {
+        // rows -> out (or the workspace ahead of a column stage), columns in place on out
+        if (plan->logf == 0) {
+            e = row_pass(in, out);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, wc, 0, plan->tw_b, none, false, 1.0, s,
+                                  nullptr, true, false);
+        } else {
+            e = row_pass(in, workspace);
+            if (e == hipSuccess)
+                e = launch_colstage(plan->prec, plan->logf, workspace, out, batch, wc, plan->log_b, s, true, false);
+            if (e == hipSuccess)
+                e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, wc, plan->logf, plan->tw_b, hb, false, 1.0,
+                                  s, nullptr, true, false);
+        }
+        return real_done(e, "fft_exec_r2c", s);
+    }
+    // inverse columns as conj(F(conj X)) / H into the workspace, then the rows
+    const double inv_h = 1.0 / (double)h;
+    if (plan->logf == 0) {
+        e = launch_cols2d(plan->prec, plan->log_b, in, workspace, batch, wc, 0, plan->tw_b, none, true, inv_h, s,
+                          nullptr, true, true);
+    } else {
+        e = launch_colstage(plan->prec, plan->logf, in, workspace, batch, wc, plan->log_b, s, true, true);
+        if (e == hipSuccess)
+            e = launch_cols2d(plan->prec, plan->log_b, workspace, workspace, batch, wc, plan->logf, plan->tw_b, hb,
+                              true, inv_h, s, nullptr, true, false);
+    }
+    if (e == hipSuccess) e = row_pass(workspace, out);
+    return real_done(e, "fft_exec_c2r", s);
+}
+
+// Bytes of one transform's real array and of its half spectrum.
+static void real_sizes(const fft_plan* p, size_t* real_bytes, size_t* half_bytes)
+{
+    const size_t rows = p->rank == 2 ? (size_t)p->dims[0] : 1;
+    const size_t w = p->rank == 2 ? (size_t)p->dims[1] : (size_t)p->n;
+    *real_bytes = rows * w * (p->elem / 2);
+    *half_bytes = rows * (w / 2 + 1) * p->elem;
+}
+
 int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream)
 {
     bool noop = false;
-    const size_t rb = plan ? plan->elem / 2 : 0;  // bytes of one real value
-    int st = check_real_exec(plan, in, plan ? plan->n * rb : 0, out, plan ? (plan->n / 2 + 1) * plan->elem : 0,
-                             batch, workspace, &noop);
+    size_t rbytes = 0, hbytes = 0;
+    if (plan) real_sizes(plan, &rbytes, &hbytes);
+    const bool need_ws = plan && (plan->rank == 1 || plan->logf > 0);
+    int st = check_real_exec(plan, in, rbytes, out, hbytes, batch, workspace, need_ws, &noop);
     if (st != FFT_OK || noop) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (plan->rank == 2) return exec_real_2d(plan, false, in, out, batch, workspace, s);
     hipError_t e;
     if (plan->n == 1) {
         e = launch_real_n1(plan->prec, false, in, out, batch, s);
@@ -1196,11 +1316,12 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
 int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream)
 {
     bool noop = false;
-    const size_t rb = plan ? plan->elem / 2 : 0;
-    int st = check_real_exec(plan, in, plan ? (plan->n / 2 + 1) * plan->elem : 0, out, plan ? plan->n * rb : 0,
-                             batch, workspace, &noop);
+    size_t rbytes = 0, hbytes = 0;
+    if (plan) real_sizes(plan, &rbytes, &hbytes);
+    int st = check_real_exec(plan, in, hbytes, out, rbytes, batch, workspace, true, &noop);
     if (st != FFT_OK || noop) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (plan->rank == 2) return exec_real_2d(plan, true, in, out, batch, workspace, s);
     hipError_t e;
     if (plan->n == 1) {
         e = launch_real_n1(plan->prec, true, in, out, batch, s);

@@ -63,10 +63,12 @@ hipError_t launch_rows(int prec, int logn, bool conj_in, bool conj_out, const vo
 // (column, j'), j' < 2^logf, with points at rows j' + 2^logf r; when logf > 0
 // point r of line j' is first multiplied by w_H^{r j'} (htw: tables for H).
 // in -> out, may alias.  conj_out conjugates and multiplies by `scale`.
-// out_im non-NULL: planar output (see Io).
+// out_im non-NULL: planar output (see Io).  one_col: one column per lane, for
+// rows of any length w (the W/2 + 1 columns of a real image's spectrum);
+// conj_in (one_col only) conjugates on load.
 hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t nimg, int64_t w, int logf,
                          const void* tw, BigTwiddle htw, bool conj_out, double scale, hipStream_t stream,
-                         void* out_im = nullptr);
+                         void* out_im = nullptr, bool one_col = false, bool conj_in = false);
 
 // 2D row pass with the radix-2^logf column super-stage folded in: rows of
 // 2^logw points; image rows j + r Lc (r < 2^logf, Lc = 2^log_lc) are
@@ -78,8 +80,9 @@ hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void
 // 2D column super-stage of radix 2^logf (1..4) as a pass of its own: image
 // rows j + r Lc (r < 2^logf, Lc = 2^log_lc) -> rows j 2^logf + r, for
 // [nimg][2^logf Lc][w] images (w a multiple of 16 bytes / element).  Must not alias.
+// one_col: one element per thread (rows of any length); conj_in conjugates on load.
 hipError_t launch_colstage(int prec, int logf, const void* in, void* out, int64_t nimg, int64_t w, int log_lc,
-                           hipStream_t stream);
+                           hipStream_t stream, bool one_col = false, bool conj_in = false);
 
 // One super-stage pass of a multi-pass Stockham transform of `batch` signals
 // of 2^logn points: radix 2^logr, span 2^logns; kind 0 first, 1 middle, 2

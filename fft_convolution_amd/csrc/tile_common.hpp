@@ -14,9 +14,11 @@ namespace fftmi {
 // CLMIN: the fewest lanes per row segment (8: 128-byte segments of 16-byte
 // vectors; 16 for passes that also move 8-byte values per lane, so that those
 // come in 128-byte segments too).
-template <typename V, int LOGL, int CLMIN = 8> struct Tile {
+// PV: adjacent lines per thread (16 bytes by default; 1 for arrays whose rows
+// are not a multiple of 16 bytes long).
+template <typename V, int LOGL, int CLMIN = 8, int PV = 16 / (int)sizeof(V)> struct Tile {
     using G = Geom<V, LOGL>;
-    static constexpr int P = 16 / (int)sizeof(V);      // complex64: 2, complex128: 1
+    static constexpr int P = PV;                        // complex64: 2, complex128: 1
     static constexpr int CL0 = 256 / G::T;
     static constexpr int CL = CL0 < CLMIN ? CLMIN : (CL0 > 64 ? 64 : CL0);
     static constexpr int C = CL * P;
@@ -34,12 +36,14 @@ __device__ __forceinline__ void vload(const float2* p, float2 (&d)[2])
     d[1] = float2{q.z, q.w};
 }
 __device__ __forceinline__ void vload(const double2* p, double2 (&d)[1]) { d[0] = *p; }
+__device__ __forceinline__ void vload(const float2* p, float2 (&d)[1]) { d[0] = *p; }
 __device__ __forceinline__ void vstore(float2* p, const float2 (&s)[2])
 {
     const vio_f4 q = {s[0].x, s[0].y, s[1].x, s[1].y};
     *reinterpret_cast<vio_f4*>(p) = q;
 }
 __device__ __forceinline__ void vstore(double2* p, const double2 (&s)[1]) { *p = s[0]; }
+__device__ __forceinline__ void vstore(float2* p, const float2 (&s)[1]) { *p = s[0]; }
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
 // b mod 8).  Give each XCD a contiguous range of tiles instead, so that

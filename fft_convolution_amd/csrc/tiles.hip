@@ -37,13 +37,18 @@ namespace fftmi {
 // 2D column pass: lines (column, j') of [H][W] images, H = F Lc, line points
 // at rows j' + F r (r < Lc); in place allowed.
 // ---------------------------------------------------------------------------
-template <typename V, int LOGL, bool CONJ_OUT, bool POUT>
-__global__ __launch_bounds__((Tile<V, LOGL>::THREADS))
+// ONE: one column per lane (rows of any length, e.g. the W/2 + 1 columns of
+// a real image's half spectrum), 16 lanes per 128-byte segment for complex64.
+template <typename V, int LOGL, bool ONE>
+using ColTile = Tile<V, LOGL, (ONE && sizeof(V) == 8) ? 16 : 8, ONE ? 1 : 16 / (int)sizeof(V)>;
+
+template <typename V, int LOGL, bool CONJ_OUT, bool POUT, bool ONE = false, bool CONJ_IN = false>
+__global__ __launch_bounds__((ColTile<V, LOGL, ONE>::THREADS))
 void cols2d_kernel(const V* in, COut<V, POUT> out, int64_t w, int logf, int64_t col_tiles, const V* __restrict__ tw,
                    BigTw<V> htw, typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGL>;
-    using TL = Tile<V, LOGL>;
+    using TL = ColTile<V, LOGL, ONE>;
     __shared__ V lds[TL::LDS];
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -66,7 +71,7 @@ void cols2d_kernel(const V* in, COut<V, POUT> out, int64_t w, int logf, int64_t 
 #pragma unroll
             for (int g = 0; g < TL::P; ++g) q[g] = V{0, 0};
 #pragma unroll
-        for (int g = 0; g < TL::P; ++g) v[g][i] = q[g];
+        for (int g = 0; g < TL::P; ++g) v[g][i] = CONJ_IN ? cconj(q[g]) : q[g];
     }
     TwBases<V, LOGL> tb;
     tb.load(tw, t);
@@ -100,12 +105,12 @@ void cols2d_kernel(const V* in, COut<V, POUT> out, int64_t w, int logf, int64_t 
 // adjacent columns (one 16-byte vector per row) of one (image, j); lanes run
 // along the row, so every row access of a wave is contiguous.  Out of place.
 // ---------------------------------------------------------------------------
-template <typename V, int LOGF>
+template <typename V, int LOGF, bool ONE>
 __global__ __launch_bounds__(256) void colstage_kernel(const V* __restrict__ in, V* __restrict__ out, int64_t w,
-                                                       int log_lc, int64_t total)
+                                                       int log_lc, int64_t total, int conj_in)
 {
     constexpr int F = 1 << LOGF;
-    constexpr int P = 16 / (int)sizeof(V);
+    constexpr int P = ONE ? 1 : 16 / (int)sizeof(V);
     const int64_t wp = w / P;  // column vectors per row
     const int64_t lc = (int64_t)1 << log_lc;
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (int64_t)gridDim.x * blockDim.x) {
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(256) void colstage_kernel(const V* __restrict__ in,
             V q[P];
             vload(in + base + (j + ((int64_t)r << log_lc)) * w, q);
 #pragma unroll
-            for (int e = 0; e < P; ++e) u[e][r] = q[e];
+            for (int e = 0; e < P; ++e) u[e][r] = conj_in ? cconj(q[e]) : q[e];
         }
 #pragma unroll
         for (int e = 0; e < P; ++e) Dft<F>::run(u[e]);
@@ -285,29 +290,43 @@ void stock_pass_kernel(IN in, OUT out, int logn, int logns, int64_t tiles_per_si
 // ---------------------------------------------------------------------------
 static inline dim3 grid_of(int64_t blocks) { return dim3((unsigned)blocks); }
 
-template <typename V, int LOGL>
+template <typename V, int LOGL, bool ONE>
 static hipError_t cols2d_t(const void* in, void* out, void* out_im, int64_t nimg, int64_t w, int logf,
-                           const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s)
+                           const void* tw, BigTwiddle htw, bool ci, bool co, double scale, hipStream_t s)
 {
-    using TL = Tile<V, LOGL>;
-    if (TL::THREADS > 1024) return hipErrorInvalidValue;
-    const int64_t col_tiles = (w + TL::C - 1) / TL::C;
-    const int64_t blocks = (col_tiles << logf) * nimg;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    using Rl = typename real_of<V>::type;
-    const BigTw<V> big{(const V*)htw.hi, (const V*)htw.lo, htw.lbits, htw.logn};
-#define FFTMI_C2(CO, PO)                                                                                      \
-    hipLaunchKernelGGL((cols2d_kernel<V, LOGL, CO, PO>), grid_of(blocks), dim3(TL::THREADS), 0, s, (const V*)in, \
-                       make_out<V, PO>(out, out_im), w, logf, col_tiles, (const V*)tw, big, (Rl)scale)
-    if (out_im) {
-        if (co) FFTMI_C2(true, true);
-        else FFTMI_C2(false, true);
+    using TL = ColTile<V, LOGL, ONE>;
+    if constexpr (TL::THREADS > 1024) {
+        return hipErrorInvalidValue;
     } else {
-        if (co) FFTMI_C2(true, false);
-        else FFTMI_C2(false, false);
-    }
+        const int64_t col_tiles = (w + TL::C - 1) / TL::C;
+        const int64_t blocks = (col_tiles << logf) * nimg;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        if (w % TL::P) return hipErrorInvalidValue;
+        using Rl = typename real_of<V>::type;
+        const BigTw<V> big{(const V*)htw.hi, (const V*)htw.lo, htw.lbits, htw.logn};
+#define FFTMI_C2(CI, CO, PO)                                                                                      \
+    hipLaunchKernelGGL((cols2d_kernel<V, LOGL, CO, PO, ONE, CI>), grid_of(blocks), dim3(TL::THREADS), 0, s,         \
+                       (const V*)in, make_out<V, PO>(out, out_im), w, logf, col_tiles, (const V*)tw, big, (Rl)scale)
+        if constexpr (ONE) {
+            // the real-image column passes: forward (no conj), inverse (conj on
+            // both sides, or only on the store after a conjugating column stage)
+            if (out_im || (ci && !co)) return hipErrorInvalidValue;
+            if (ci) FFTMI_C2(true, true, false);
+            else if (co) FFTMI_C2(false, true, false);
+            else FFTMI_C2(false, false, false);
+        } else {
+            if (ci) return hipErrorInvalidValue;
+            if (out_im) {
+                if (co) FFTMI_C2(false, true, true);
+                else FFTMI_C2(false, false, true);
+            } else {
+                if (co) FFTMI_C2(false, true, false);
+                else FFTMI_C2(false, false, false);
+            }
+        }
 #undef FFTMI_C2
-    return hipGetLastError();
+        return hipGetLastError();
+    }
 }
 
 template <typename V, int LOGW, int LOGF> constexpr bool fold_ok()
@@ -459,33 +478,37 @@ hipError_t launch_bluestein_pass(int prec, int logr, int mode, const void* in, v
     }
 
 hipError_t launch_cols2d(int prec, int logl, const void* in, void* out, int64_t nimg, int64_t w, int logf,
-                         const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s, void* out_im)
+                         const void* tw, BigTwiddle htw, bool co, double scale, hipStream_t s, void* out_im,
+                         bool one_col, bool ci)
 {
-#define CF(L) cols2d_t<float2, L>(in, out, out_im, nimg, w, logf, tw, htw, co, scale, s)
-#define CD(L) cols2d_t<double2, L>(in, out, out_im, nimg, w, logf, tw, htw, co, scale, s)
+#define CF(L) (one_col ? cols2d_t<float2, L, true>(in, out, out_im, nimg, w, logf, tw, htw, ci, co, scale, s) \
+                       : cols2d_t<float2, L, false>(in, out, out_im, nimg, w, logf, tw, htw, ci, co, scale, s))
+#define CD(L) (one_col ? cols2d_t<double2, L, true>(in, out, out_im, nimg, w, logf, tw, htw, ci, co, scale, s) \
+                       : cols2d_t<double2, L, false>(in, out, out_im, nimg, w, logf, tw, htw, ci, co, scale, s))
     FFTMI_LOG_SWITCH(prec, logl, CF, CD)
 #undef CF
 #undef CD
 }
 
-template <typename V, int LOGF>
-static hipError_t colstage_t(const void* in, void* out, int64_t nimg, int64_t w, int log_lc, hipStream_t s)
+template <typename V, int LOGF, bool ONE>
+static hipError_t colstage_t(const void* in, void* out, int64_t nimg, int64_t w, int log_lc, bool ci, hipStream_t s)
 {
-    constexpr int P = 16 / (int)sizeof(V);
+    constexpr int P = ONE ? 1 : 16 / (int)sizeof(V);
     if (w % P) return hipErrorInvalidValue;
     const int64_t total = (nimg << log_lc) * (w / P);
     int64_t blocks = (total + 255) / 256;
     if (blocks > (1 << 20)) blocks = 1 << 20;
-    hipLaunchKernelGGL((colstage_kernel<V, LOGF>), dim3((unsigned)blocks), dim3(256), 0, s, (const V*)in, (V*)out, w,
-                       log_lc, total);
+    hipLaunchKernelGGL((colstage_kernel<V, LOGF, ONE>), dim3((unsigned)blocks), dim3(256), 0, s, (const V*)in,
+                       (V*)out, w, log_lc, total, (int)ci);
     return hipGetLastError();
 }
 
 hipError_t launch_colstage(int prec, int logf, const void* in, void* out, int64_t nimg, int64_t w, int log_lc,
-                           hipStream_t s)
+                           hipStream_t s, bool one_col, bool ci)
 {
-#define CS(F) (prec == 0 ? colstage_t<float2, F>(in, out, nimg, w, log_lc, s) \
-                         : colstage_t<double2, F>(in, out, nimg, w, log_lc, s))
+#define CS1(F, ONE) (prec == 0 ? colstage_t<float2, F, ONE>(in, out, nimg, w, log_lc, ci, s) \
+                               : colstage_t<double2, F, ONE>(in, out, nimg, w, log_lc, ci, s))
+#define CS(F) (one_col ? CS1(F, true) : CS1(F, false))
     switch (logf) {
         case 1: return CS(1);
         case 2: return CS(2);
@@ -494,6 +517,7 @@ hipError_t launch_colstage(int prec, int logf, const void* in, void* out, int64_
         default: return hipErrorInvalidValue;
     }
 #undef CS
+#undef CS1
 }
 
 hipError_t launch_rows2d_fold(int prec, int logw, int logf, const void* in, void* out, int64_t nimg, int log_lc,

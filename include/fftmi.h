@@ -240,6 +240,18 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
 int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
 
 /*
+ * Plan for real images [H][W] (H, W powers of two, 1 <= H <= FFT_MAX_LDS_N_*,
+ * 1 <= W <= 2 FFT_MAX_LDS_N_*): the 2D transform's columns 0 .. W/2, the rest
+ * following from X[u][v] = conj X[-u][-v].  The rows go through the real-row
+ * kernels, then the H-point column transforms run over the W/2 + 1 columns of
+ * the half spectrum (one column per lane; for H > 512 a radix-F column stage
+ * first, as for complex plans).  The same fft_exec_r2c / fft_exec_c2r calls
+ * take it; fft_plan_describe shows path=real2d.
+ * Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE, DEVICE.
+ */
+int fft_plan_create_real_2d(fft_plan** plan, int64_t h, int64_t w, int prec);
+
+/*
  * Forward transform of real rows: out[b][k] = sum_n in[b][n] e^{-2 pi i k n / N},
  * k = 0 .. N/2.
  *   in:        [batch][N] real (float for C32, double for C64), rows contiguous.
@@ -248,6 +260,9 @@ int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
  *              size (8 bytes C32, 16 bytes C64).
  *   workspace: fft_workspace_size(plan, batch) bytes: none for N/2 <=
  *              FFT_MAX_LDS_N_* (one kernel), batch * N/2 complex values beyond.
+ *   Images (fft_plan_create_real_2d): in [batch][H][W] real, out
+ *              [batch][H][W/2 + 1] complex; the workspace (batch H (W/2 + 1)
+ *              complex values) is needed for H > 512 only.
  * Errors: INVALID_ARG, RANK, ALIGN, OVERLAP, WORKSPACE, DEVICE.
  */
 int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream);
@@ -258,6 +273,10 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
  * ignored (a real row has real values there); bins N/2 + 1 .. N - 1 are
  * taken as conj in[b][N - k].
  *   in:  [batch][N/2 + 1] complex;  out: [batch][N] real.  Not modified: in.
+ *   Images: in [batch][H][W/2 + 1], out [batch][H][W], scaled 1/(H W): the
+ *   inverse column transforms, then the rows as above (the imaginary parts of
+ *   columns 0 and W/2 of that intermediate are ignored).  The workspace is
+ *   needed for every H > 1.
  *   Layout, alignment, overlap and workspace as fft_exec_r2c.
  * Errors: as fft_exec_r2c.
  */

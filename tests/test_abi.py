@@ -167,3 +167,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         fm.fft_plan_query(1, [1024], fm.FFT_C32)
     with pytest.raises(ImportError):
         fm.fft_status_string(0)
+
+
+@pytest.mark.parametrize("h,w,prec,status", [
+    (0, 8, 0, fm.FFT_ERR_INVALID_ARG),
+    (8, 0, 0, fm.FFT_ERR_INVALID_ARG),
+    (8, 8, 3, fm.FFT_ERR_INVALID_ARG),
+    (6, 8, 0, fm.FFT_ERR_NOT_POW2),
+    (8, 12, 1, fm.FFT_ERR_NOT_POW2),
+    (16384, 8, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (8, 32768, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (8192, 8, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (8, 16384, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+])
+def test_real_2d_plan_create_rejects(h, w, prec, status):
+    hd = ctypes.c_void_p(12345)
+    assert fm.lib().fft_plan_create_real_2d(ctypes.byref(hd), h, w, prec) == status
+    assert hd.value is None
+
+
+@pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
+def test_valid_real_2d_plan_without_gpu_is_a_device_error():
+    for h, w, prec in ((1, 1, 0), (8192, 16384, 0), (4096, 8192, 1), (64, 2, 0)):
+        hd = ctypes.c_void_p(12345)
+        assert fm.lib().fft_plan_create_real_2d(ctypes.byref(hd), h, w, prec) == fm.FFT_ERR_DEVICE
+        assert hd.value is None

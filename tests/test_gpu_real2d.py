@@ -1,0 +1,82 @@
+"""2D transforms of real images (R2C / C2R) against the fp64 oracle's
+rfft2 / irfft2 (GPU): the row kernels of real rows, then the column passes
+over the W/2 + 1 columns of the half spectrum (one column per lane), with a
+separate radix-F column stage for H > 512.
+
+Bar: per-image relative RMS <= 1e-6 log2(H W) (float32) / 1e-14 log2(H W)
+(float64)."""
+import numpy as np
+import pytest
+import torch
+
+import fft_convolution_amd as fm
+import oracle
+from fft_convolution_amd import workloads as wl
+
+from conftest import fft_tol, rel_rms_rows
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # h, w, dtype, batch
+    (1, 8, torch.float32, 3), (8, 1, torch.float32, 2), (2, 2, torch.float32, 5), (16, 32, torch.float32, 3),
+    (64, 2, torch.float32, 2), (512, 1024, torch.float32, 1), (1024, 512, torch.float32, 2),
+    (2048, 2048, torch.float32, 1), (8192, 64, torch.float32, 1), (64, 16384, torch.float32, 1),
+    (4, 8, torch.float64, 3), (256, 128, torch.float64, 2), (1024, 64, torch.float64, 1),
+    (4096, 2, torch.float64, 2), (2048, 8192, torch.float64, 1),
+]
+
+
+def _flat(a):
+    return a.reshape(a.shape[0], -1)
+
+
+@pytest.mark.parametrize("h,w,dtype,batch", CASES, ids=lambda v: str(v))
+def test_real_2d(dev, h, w, dtype, batch):
+    print("case %dx%d %s batch=%d" % (h, w, dtype, batch), flush=True)
+    npdt = np.float32 if dtype == torch.float32 else np.float64
+    cdt = np.complex64 if dtype == torch.float32 else np.complex128
+    x_np = wl.real_normal(h * w, batch, seed=h + 3 * w, dtype=npdt).reshape(batch, h, w)
+    plan = fm.RealPlan((h, w), dtype)
+    assert "path=real2d" in plan.describe()
+    x = torch.from_numpy(x_np).to(dev)
+    tol = fft_tol(h * w, dtype == torch.float64)
+    X = plan.rfft(x)
+    assert X.shape == (batch, h, w // 2 + 1)
+    assert rel_rms_rows(_flat(X.cpu().numpy()), _flat(oracle.rfft2(x_np))).max() <= tol
+    # an arbitrary half spectrum back (numpy's irfft2 reading)
+    S = wl.batched_normal(h * (w // 2 + 1), batch, seed=h + w, dtype=cdt).reshape(batch, h, w // 2 + 1)
+    y = plan.irfft(torch.from_numpy(S).to(dev)).cpu().numpy()
+    assert rel_rms_rows(_flat(y), _flat(oracle.irfft2(S, (h, w)))).max() <= tol
+    back = plan.irfft(X).cpu().numpy()
+    assert rel_rms_rows(_flat(back), _flat(x_np)).max() <= 2 * tol
+
+
+def test_real_2d_closed_form_and_errors(dev):
+    h, w = 1024, 256
+    yy = np.arange(h)[:, None]
+    xx = np.arange(w)[None, :]
+    fy, fx = 37, 19
+    img = np.cos(2 * np.pi * (((fy * yy) % h) / h + ((fx * xx) % w) / w))[None]
+    plan = fm.RealPlan((h, w), torch.float64)
+    X = plan.rfft(torch.from_numpy(img).to(dev)).cpu().numpy()[0]
+    want = np.zeros((h, w // 2 + 1), dtype=complex)
+    want[fy, fx] = h * w / 2
+    assert np.abs(X - want).max() < 1e-8
+    # C2R needs a workspace for H > 1; R2C only with a column stage (H > 512)
+    Xd = torch.from_numpy(X[None]).to(dev)
+    out = torch.empty(1, h, w, dtype=torch.float64, device=dev)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_c2r(plan.handle, Xd, out, 1, None)
+    assert e.value.status == fm.FFT_ERR_WORKSPACE
+    small = fm.RealPlan((256, 256))
+    xs = torch.randn(2, 256, 256, device=dev)
+    Ys = torch.empty(2, 256, 129, dtype=torch.complex64, device=dev)
+    fm.fft_exec_r2c(small.handle, xs, Ys, 2, None)    # no column stage: no workspace
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_r2c(plan.handle, torch.from_numpy(img).to(dev), Xd, 1, None)
+    assert e.value.status == fm.FFT_ERR_WORKSPACE
+    # 1D real plans and complex calls stay apart
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_2d(plan.handle, 0, Xd, Xd, 1, None)
+    assert e.value.status == fm.FFT_ERR_RANK
