@@ -25,7 +25,8 @@ Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
 transform the same way, and the R2C transform of 16384 real rows of 8192
 points (value = batch * 2.5 N log2 N / t, half the complex count), and rows
-of 1000 (mixed radix) and 1001 (Bluestein) points.
+of 1000 (mixed radix) and 1001 (Bluestein) points, and the 2D R2C transform
+of eight real 2048 x 2048 images.
 """
 from __future__ import annotations
 
@@ -44,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
              "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384", "c2c_n1000_b65536",
-             "c2c_n1001_b65536")
+             "c2c_n1001_b65536", "r2c2d_2048x2048_b8")
 
 
 # The sources each single-kernel workload's kernel is built from: a stored
@@ -140,6 +141,23 @@ def setup_workload(name, dev, fm, torch, sets=1):
                     oracle_fn="fft3" if three else "fft2",
                     **dict(zip(("d", "h", "w") if three else ("h", "w"), dims)))
         return step, info
+    if name.startswith("r2c2d"):
+        h, w, batch = spec["h"], spec["w"], spec["batch"]
+        x_np = wl.workload_input(name)
+        plan = fm.RealPlan((h, w), torch.float32)
+        wsb = fm.fft_workspace_size(plan.handle, batch)
+        x0 = torch.from_numpy(x_np).to(dev)
+        bufs = [(x0 if k == 0 else x0.clone(), torch.empty(batch, h, w // 2 + 1, dtype=torch.complex64, device=dev),
+                 ws_of(wsb)) for k in range(sets)]
+
+        def step(k=0):
+            x, y, ws = bufs[k % sets]
+            fm.fft_exec_r2c(plan.handle, x, y, batch, ws, stream)
+        info = dict(h=h, w=w, batch=batch, dtype="f32", flops=batch * 2.5 * h * w * math.log2(h * w),
+                    bytes=x0.numel() * 4 + bufs[0][1].numel() * 8, plan=plan.describe(), kernels=3,
+                    sample_rows=lambda rows: x_np[:rows], oracle_unit=2.5 * h * w * math.log2(h * w),
+                    oracle_fn="rfft2", keep=(plan, bufs))
+        return step, info
     if name.startswith("r2c"):
         n, batch = spec["n"], spec["batch"]
         x_np = wl.workload_input(name)
@@ -200,13 +218,24 @@ def cpu_baseline(name, info, budget_s):
         oracle.polymul_fft(a, b, n=info["n"])
         dt = time.perf_counter() - t0
         units, sample = pairs, "first %d of %d pairs" % (pairs, total)
-    elif name.startswith("c2c2d") or name.startswith("c2c3d"):
-        imgs = 1
-        x = info["sample_rows"](imgs)
+    elif name.startswith("c2c2d") or name.startswith("c2c3d") or name.startswith("r2c2d"):
+        # The first image, then as many of the batch as fit the budget, the
+        # whole set transformed again until the budget is used.
+        fn = getattr(oracle, info["oracle_fn"])
+        x = info["sample_rows"](1)
         t0 = time.perf_counter()
-        getattr(oracle, info["oracle_fn"])(x)
-        dt = time.perf_counter() - t0
-        units, sample = imgs, "first %d of %d images" % (imgs, info["batch"])
+        fn(x)
+        per = time.perf_counter() - t0
+        imgs = int(max(1, min(info["batch"], budget_s / max(per, 1e-9))))
+        x = info["sample_rows"](imgs)
+        reps, dt = 0, 0.0
+        while reps == 0 or dt < budget_s:
+            t0 = time.perf_counter()
+            fn(x)
+            dt += time.perf_counter() - t0
+            reps += 1
+        units = imgs * reps
+        sample = "first %d of %d images, transformed %d time(s)" % (imgs, info["batch"], reps)
     else:
         # The first rows of the batch, as many as fit the budget; if the whole
         # batch takes less, it is transformed repeatedly until the budget is used.

@@ -23,6 +23,7 @@ stated):
   operands of the R2C / C2R transforms.  N = 8192 x 16384 rows (seed 7).
 * rows of 1000 and 1001 points x 65536, ``batched_normal`` (seeds 8, 9): the
   mixed-radix and Bluestein paths.
+* real 2048 x 2048 images x 8, ``real_normal`` (seed 10): the 2D R2C path.
 """
 from __future__ import annotations
 
@@ -43,6 +44,8 @@ WORKLOADS = {
     # radix), 1001 = 7 * 11 * 13 (Bluestein, M = 2048)
     "c2c_n1000_b65536": dict(kind="normal", n=1000, batch=65536, seed=8),
     "c2c_n1001_b65536": dict(kind="normal", n=1001, batch=65536, seed=9),
+    # real 2048 x 2048 images, the 2D R2C transform
+    "r2c2d_2048x2048_b8": dict(kind="real_images", h=2048, w=2048, batch=8, seed=10),
 }
 
 
@@ -162,6 +165,9 @@ def workload_input(name: str, **overrides):
         return random_polys(spec["length"], spec["batch"], spec["seed"])
     if kind == "real_normal":
         return real_normal(spec["n"], spec["batch"], spec["seed"])
+    if kind == "real_images":
+        return real_normal(spec["h"] * spec["w"], spec["batch"], spec["seed"]).reshape(
+            spec["batch"], spec["h"], spec["w"])
     if kind == "uniform3d":
         d, h, w = spec["d"], spec["h"], spec["w"]
         return batched_uniform(d * h * w, spec["batch"], spec["seed"]).reshape(spec["batch"], d, h, w)
