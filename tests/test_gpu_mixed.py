@@ -89,3 +89,42 @@ def test_mixed_range_limits(dev):
     x_np = wl.batched_uniform(n, batch, seed=8)
     y = fm.Plan(n).fft(torch.from_numpy(x_np).cuda()).cpu().numpy()
     assert rel_rms_rows(y, oracle.dft(x_np)).max() <= fft_tol(n)
+
+
+def _seven_smooth(limit):
+    out = []
+    for n in range(3, limit + 1):
+        m = n
+        for p in (2, 3, 5, 7):
+            while m % p == 0:
+                m //= p
+        if m == 1 and n & (n - 1):
+            out.append(n)
+    return out
+
+
+@pytest.mark.parametrize("dtype,limit", [(torch.complex64, 8192), (torch.complex128, 4096)])
+def test_mixed_every_smooth_length(dev, dtype, limit):
+    """Every length 2^a 3^b 5^c 7^d (not a power of two) in the mixed-radix
+    range: two rows, forward and inverse, against the direct DFT (all bins up
+    to 2048 points, 48 bins spread over the spectrum beyond)."""
+    npdt = np.complex64 if dtype == torch.complex64 else np.complex128
+    oracle.set_threads(8)
+    bad = []
+    for n in _seven_smooth(limit):
+        plan = fm.Plan(n, dtype)
+        assert "path=mixed" in plan.describe(), n
+        x_np = wl.batched_uniform(n, 2, seed=7000 + n, dtype=npdt)
+        x = torch.from_numpy(x_np).cuda()
+        ks = None if n <= 2048 else np.unique(np.linspace(0, n - 1, 48).astype(np.int64))
+        tol = fft_tol(n, dtype == torch.complex128)
+        for inverse in (False, True):
+            y = (plan.ifft(x) if inverse else plan.fft(x)).cpu().numpy()
+            if ks is None:
+                ref = oracle.dft(x_np, inverse=inverse)
+            else:
+                y, ref = y[:, ks], oracle.dft_sample(x_np, ks, inverse=inverse)
+            err = rel_rms_rows(y, ref).max()
+            if not err <= tol:
+                bad.append((n, inverse, float(err)))
+    assert not bad, bad
