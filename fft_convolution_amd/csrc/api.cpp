@@ -121,20 +121,41 @@ void root_of_unity_any(int64_t m, int64_t M, double* re, double* im)
     *im = -sin_sign * sn;
 }
 
-// Radices of a mixed-radix plan: 8s, then 4, 2, then 3s, 5s, 7s; false if N
+// Radices of a mixed-radix plan: 8s, then 4, 2, then 3s, 5s, 7s, and the
+// per-stage span, stride, quotient magic and twiddle-table offset; false if N
 // has another prime factor or needs more stages than the schedule holds.
 bool mixed_factor(int64_t n, MixedSchedule* ms)
 {
     ms->nst = 0;
+    int64_t rest = n;
     const int order[6] = {8, 4, 2, 3, 5, 7};
     for (int r : order) {
-        while (n % r == 0) {
+        while (rest % r == 0) {
             if (ms->nst == kMixedMaxStages) return false;
             ms->radix[ms->nst++] = r;
-            n /= r;
+            rest /= r;
         }
     }
-    return n == 1;
+    if (rest != 1) return false;
+    int64_t ns = 1, off = 0;
+    for (int q = 0; q < ms->nst; ++q) {
+        const int r = ms->radix[q];
+        ms->ns[q] = (int)ns;
+        ms->stride[q] = (int)(n / r);
+        ms->magic[q] = ns > 1 ? (unsigned)(((uint64_t(1) << 32) + ns - 1) / ns) : 0u;
+        ms->twoff[q] = (int)off;
+        if (q > 0) off += ns * mixed_tw_slots(r);
+        ns *= r;
+    }
+    return true;
+}
+
+// Entries of a mixed-radix twiddle table (see MixedSchedule).
+int64_t mixed_table_entries(const MixedSchedule& ms)
+{
+    int64_t e = 0;
+    for (int q = 1; q < ms.nst; ++q) e += (int64_t)ms.ns[q] * mixed_tw_slots(ms.radix[q]);
+    return e;
 }
 
 // Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
@@ -207,7 +228,7 @@ struct fft_plan {
     // rank 1, any N (Bluestein): chirp c_j (N entries), B = F_M(b) (M entries),
     // the power-of-two plan of length M = 2^logm it runs on.
     int logm = 0;
-    // mixed radix: the stage radices; tw_a = w_N^m for m < N
+    // mixed radix: the stage schedule; tw_a = its twiddle table
     MixedSchedule mixed{};
     // real rows of N = 2H points: inner = the complex plan of length H,
     // big_* = w_N, log_a = log2 H; real_fused: H within the rows kernel's range.
@@ -547,8 +568,19 @@ int upload_tables(fft_plan* p)
             st = bluestein_tables(p);
             break;
         case PATH_MIXED: {
-            std::vector<double> t(2 * (size_t)p->n);
-            for (int64_t m = 0; m < p->n; ++m) root_of_unity_any(m, p->n, &t[2 * m], &t[2 * m + 1]);
+            // rows w_{ns R}^{r k}, r = 1 .. R-1, for k < ns, per stage s >= 1;
+            // pad entries 0 (N = R alone has no table: one entry, unused)
+            const MixedSchedule& ms = p->mixed;
+            std::vector<double> t(2 * (size_t)std::max<int64_t>(1, mixed_table_entries(ms)), 0.0);
+            for (int q = 1; q < ms.nst; ++q) {
+                const int r = ms.radix[q];
+                const int64_t ns = ms.ns[q];
+                for (int64_t k = 0; k < ns; ++k)
+                    for (int j = 1; j < r; ++j) {
+                        const size_t e = (size_t)(ms.twoff[q] + k * mixed_tw_slots(r) + (j - 1));
+                        root_of_unity_any(j * k, ns * r, &t[2 * e], &t[2 * e + 1]);
+                    }
+            }
             st = upload(t, prec, &p->tw_a);
             break;
         }
@@ -779,7 +811,7 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
             break;
         }
         case PATH_MIXED:
-            e = launch_mixed_rows(plan->prec, (int)plan->n, plan->mixed, inv, inv, io.in, io.out, batch, plan->tw_a,
+            e = launch_mixed_rows(plan->prec, (int)plan->n, plan->mixed, inv, io.in, io.out, batch, plan->tw_a,
                                   scale, s, io.in_im, io.out_im);
             break;
         case PATH_BLUESTEIN: {

@@ -20,18 +20,29 @@ struct BigTwiddle {
     int logn;
 };
 
-// Stage radices of a mixed-radix row (each 2, 3, 4, 5, 7 or 8; product N).
+// Stages of a mixed-radix row of N points: radix R_s (each 2, 3, 4, 5, 7 or
+// 8; product N), span ns_s = R_0 ... R_{s-1}, stride N / R_s, magic_s =
+// ceil(2^32 / ns_s) (so j / ns_s = mulhi(j, magic_s) for j ns_s < 2^32), and
+// twoff_s: where stage s >= 1 starts in the twiddle table, which holds, for
+// every k < ns_s, the row w_{ns_s R_s}^{r k}, r = 1 .. R_s - 1, padded to
+// mixed_tw_slots(R_s) entries (stage 0 has none: its twiddles are all 1).
 constexpr int kMixedMaxStages = 16;
 struct MixedSchedule {
     int nst;
     int radix[kMixedMaxStages];
+    int ns[kMixedMaxStages];
+    int stride[kMixedMaxStages];
+    unsigned magic[kMixedMaxStages];
+    int twoff[kMixedMaxStages];
 };
+constexpr int mixed_tw_slots(int r) { return r & ~1; }
 
 // Mixed-radix rows (mixed.hip): `nrows` contiguous rows of n points,
-// n <= mixed_max_n(prec); tw = w_n^m for m < n.  Planar needs both in_im and
-// out_im.  in -> out, may alias.
-hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool conj_in, bool conj_out, const void* in,
-                             void* out, int64_t nrows, const void* tw, double scale, hipStream_t stream,
+// n <= mixed_max_n(prec); tw = the schedule's twiddle table.  Inverse:
+// conjugate in, conjugate and scale out.  Planar needs both in_im and out_im.
+// in -> out, may alias.
+hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool inverse, const void* in, void* out,
+                             int64_t nrows, const void* tw, double scale, hipStream_t stream,
                              const void* in_im = nullptr, void* out_im = nullptr);
 int mixed_max_n(int prec);
 

@@ -12,21 +12,37 @@
 // Unlike the power-of-two engine (compile-time geometry), the schedule here is
 // a runtime list: a group of TR >= N/8 threads owns a row held in LDS; each
 // stage reads its butterflies into registers, and writes them back in place
-// after a barrier.  The row crosses HBM once each way.  Twiddles come from a
-// table of w_N^m (m < N) in the plan precision; the roots of unity of the odd
-// radices are read from the same table (w_R^m = w_N^{m N / R}).
+// after a barrier.  The row crosses HBM once each way.  Each stage s >= 1 reads
+// its twiddles w_{Ns R}^{r k}, r = 1 .. R-1, as one row of a per-stage table
+// (16-byte loads, no products of table values), and splits j into (j / Ns,
+// j mod Ns) with a multiply-high by a precomputed reciprocal.
 #include "io.hpp"
 #include "launch.hpp"
 #include "stockham.hpp"
 
 namespace fftmi {
 
+// cos(2 pi m / R) and sin(2 pi m / R), 1 <= m <= (R - 1) / 2, for R = 3, 5, 7
+// (correctly rounded doubles; the float kernels round them once more).
+__host__ __device__ constexpr double odd_cos(int r, int m)
+{
+    return r == 3 ? -0.5
+         : r == 5 ? (m == 1 ? 0.3090169943749474241023 : -0.8090169943749474241023)
+                  : (m == 1 ? 0.6234898018587335305251 : m == 2 ? -0.2225209339563144042890 : -0.9009688679024191262361);
+}
+__host__ __device__ constexpr double odd_sin(int r, int m)
+{
+    return r == 3 ? 0.8660254037844386467637
+         : r == 5 ? (m == 1 ? 0.9510565162951535721164 : 0.5877852522924731291687)
+                  : (m == 1 ? 0.7818314824680298087084 : m == 2 ? 0.9749279121818236070181 : 0.4338837391175581204758);
+}
+
 // Odd-radix DFT (R = 3, 5, 7) in registers, natural order in and out, by the
 // pairing of x_n with x_{R-n}:
 //   y_0 = x_0 + sum_n a_n,   y_k, y_{R-k} = x_0 + sum_n a_n c_{nk} -/+ i sum_n b_n s_{nk},
-// a_n = x_n + x_{R-n}, b_n = x_n - x_{R-n}, c_m = cos(2 pi m / R), s_m = sin(2 pi m / R).
-template <int R, typename V>
-__device__ __forceinline__ void dft_odd(V (&u)[R], const typename real_of<V>::type (&c)[R], const typename real_of<V>::type (&sn)[R])
+// a_n = x_n + x_{R-n}, b_n = x_n - x_{R-n}, c_m = cos(2 pi m / R), s_m = sin(2 pi m / R)
+// (c_{R-m} = c_m, s_{R-m} = -s_m).
+template <int R, typename V> __device__ __forceinline__ void dft_odd(V (&u)[R])
 {
     using Rl = typename real_of<V>::type;
     constexpr int H = (R - 1) / 2;
@@ -46,9 +62,9 @@ __device__ __forceinline__ void dft_odd(V (&u)[R], const typename real_of<V>::ty
         V B{0, 0};
 #pragma unroll
         for (int n = 1; n <= H; ++n) {
-            const int m = (n * k) % R;  // c_m = c_{R-m}, s_{R-m} = -s_m
-            const Rl cm = c[m];
-            const Rl sm = sn[m];
+            const int m = (n * k) % R;
+            const Rl cm = (Rl)odd_cos(R, m <= H ? m : R - m);
+            const Rl sm = m <= H ? (Rl)odd_sin(R, m) : -(Rl)odd_sin(R, R - m);
             A = V{A.x + a[n].x * cm, A.y + a[n].y * cm};
             B = V{B.x + b[n].x * sm, B.y + b[n].y * sm};
         }
@@ -60,45 +76,32 @@ __device__ __forceinline__ void dft_odd(V (&u)[R], const typename real_of<V>::ty
     for (int k = 0; k < R; ++k) u[k] = y[k];
 }
 
-// q = j / d and r = j mod d for 0 <= j < 2^15, 1 <= d < 2^15, from a float
-// reciprocal (the quotient estimate is off by at most one) and an exact fix.
-__device__ __forceinline__ void divmod_small(int j, int d, float inv_d, int& q, int& r)
+template <int R, typename V> __device__ __forceinline__ void dft_any(V (&u)[R])
 {
-    q = (int)((float)j * inv_d);
-    r = j - q * d;
-    if (r < 0) {
-        --q;
-        r += d;
-    } else if (r >= d) {
-        ++q;
-        r -= d;
-    }
+    if constexpr (R == 3 || R == 5 || R == 7)
+        dft_odd<R>(u);
+    else
+        Dft<R>::run(u);
 }
 
 // Butterflies per thread and stage: a row of N points has at least N/8
 // threads, so a radix-R stage (N/R butterflies) gives each at most ceil(8/R).
 template <int R> constexpr int mixed_bmax() { return (8 + R - 1) / R; }
 
-// One stage of radix R on a row held in LDS (`row`), thread tl of tr.  All
-// butterflies are read and computed into registers, then (after a barrier
-// across the workgroup) written back in place.
-template <int R, typename V>
-__device__ __forceinline__ void mixed_stage(V* row, int n, int ns, int tl, int tr, const V* __restrict__ tw)
+// One stage of radix R on a row held in LDS (`row`), thread tl of tr: for
+// every butterfly j < N/R, inputs row[j + r N/R], twiddles w_{Ns R}^{r k}
+// from the table row k = j mod Ns (none in the first stage, Ns = 1), the
+// R-point DFT, outputs at g Ns R + k + r Ns, g = j / Ns.  All butterflies are
+// read and computed into registers, then (after a barrier across the
+// workgroup) written back in place.
+template <int R, bool FIRST, typename V>
+__device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, int ns, unsigned magic,
+                                            const V* __restrict__ tw)
 {
-    using Rl = typename real_of<V>::type;
     constexpr int B = mixed_bmax<R>();
-    const int stride = n / R;             // input spacing N/R
-    const int tstep = n / (ns * R);       // w_{Ns R}^x = w_N^{x tstep}
-    const float inv_ns = 1.0f / (float)ns;
-    Rl c[R], sn[R];
-    if constexpr (R == 3 || R == 5 || R == 7) {
-#pragma unroll
-        for (int m = 0; m < R; ++m) {
-            const V w = tw[m * stride];   // w_R^m = cos - i sin
-            c[m] = w.x;
-            sn[m] = -w.y;
-        }
-    }
+    constexpr int S = mixed_tw_slots(R);
+    constexpr int P = 16 / (int)sizeof(V);           // table entries per 16-byte load
+    constexpr int NL = ((R - 1 + P - 1) / P) * P;    // entries loaded per row (<= S)
     V u[B][R];
     int dst[B];
 #pragma unroll
@@ -106,25 +109,25 @@ __device__ __forceinline__ void mixed_stage(V* row, int n, int ns, int tl, int t
         const int j = tl + b * tr;
         dst[b] = -1;
         if (j < stride) {
-            int g, k;
-            divmod_small(j, ns, inv_ns, g, k);
 #pragma unroll
             for (int r = 0; r < R; ++r) u[b][r] = row[j + r * stride];
-            if (ns > 1) {
-                // w^r = w_{Ns R}^{r k} as powers of one table value
-                const V w = tw[k * tstep];
-                V wr = w;
+            int g = j;
+            if constexpr (!FIRST) {
+                g = (int)__umulhi((unsigned)j, magic);
+                const V* t = tw + (j - g * ns) * S;
+                V w[NL];
 #pragma unroll
-                for (int r = 1; r < R; ++r) {
-                    u[b][r] = cmul(u[b][r], wr);
-                    if (r + 1 < R) wr = cmul(wr, w);
+                for (int q = 0; q < NL; q += P) {
+                    V d[P];
+                    vload(t + q, d);
+#pragma unroll
+                    for (int e = 0; e < P; ++e) w[q + e] = d[e];
                 }
+#pragma unroll
+                for (int r = 1; r < R; ++r) u[b][r] = cmul(u[b][r], w[r - 1]);
             }
-            if constexpr (R == 3 || R == 5 || R == 7)
-                dft_odd<R>(u[b], c, sn);
-            else
-                Dft<R>::run(u[b]);
-            dst[b] = g * ns * R + k;
+            dft_any<R>(u[b]);
+            dst[b] = j + g * (ns * (R - 1));  // g Ns R + k
         }
     }
     __syncthreads();  // every read of this stage is done before any write
@@ -138,16 +141,33 @@ __device__ __forceinline__ void mixed_stage(V* row, int n, int ns, int tl, int t
     __syncthreads();
 }
 
+template <bool FIRST, typename V>
+__device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, int stride, int ns, unsigned magic,
+                                                const V* __restrict__ tw)
+{
+    switch (r) {
+        case 2: mixed_stage<2, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        case 3: mixed_stage<3, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        case 4: mixed_stage<4, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        case 5: mixed_stage<5, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        case 7: mixed_stage<7, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        default: mixed_stage<8, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+    }
+}
+
 // rpw rows per workgroup, tr threads per row (blockDim = rpw tr), rows
 // contiguous in LDS as in memory (row rl at rl N), so the workgroup's rows are
 // loaded and stored as one contiguous, coalesced segment.  CAP: LDS slots.
 // Threads per workgroup at most: N/8 for the longest row of each precision.
+// INV: conjugate in, conjugate and scale out.
 template <typename V> constexpr int mixed_max_threads() { return sizeof(V) == 8 ? 1024 : 512; }
 
-template <typename V, int CAP, bool PL>
-__global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n, int tr,
-                                                          int rpw, MixedSchedule ms, const V* __restrict__ tw,
-                                                          int conj_in, int conj_out, typename real_of<V>::type scale)
+template <typename V, int CAP, bool PL, bool INV>
+__global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out,
+                                                                            int64_t nrows, int n, int tr, int rpw,
+                                                                            MixedSchedule ms,
+                                                                            const V* __restrict__ tw,
+                                                                            typename real_of<V>::type scale)
 {
     __shared__ V lds[CAP];
     const int threads = tr * rpw;
@@ -156,28 +176,20 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
     const int rows = (int)(nrows - row0 < rpw ? nrows - row0 : rpw);
     const int count = rows * n;
     const int64_t base = row0 * n;
-    for (int i = threadIdx.x; i < rpw * n; i += threads) {
-        V x = i < count ? in.ld(base + i) : V{0, 0};
-        lds[i] = conj_in ? cconj(x) : x;
+    // rows past the end of the batch (last workgroup only) are computed on
+    // whatever LDS holds and never stored
+    for (int i = threadIdx.x; i < count; i += threads) {
+        const V x = in.ld(base + i);
+        lds[i] = INV ? cconj(x) : x;
     }
     __syncthreads();
     V* row = lds + rl * n;
-    int ns = 1;
-    for (int s = 0; s < ms.nst; ++s) {
-        const int R = ms.radix[s];
-        switch (R) {
-            case 2: mixed_stage<2>(row, n, ns, tl, tr, tw); break;
-            case 3: mixed_stage<3>(row, n, ns, tl, tr, tw); break;
-            case 4: mixed_stage<4>(row, n, ns, tl, tr, tw); break;
-            case 5: mixed_stage<5>(row, n, ns, tl, tr, tw); break;
-            case 7: mixed_stage<7>(row, n, ns, tl, tr, tw); break;
-            default: mixed_stage<8>(row, n, ns, tl, tr, tw); break;
-        }
-        ns *= R;
-    }
+    mixed_stage_any<true>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw);
+    for (int s = 1; s < ms.nst; ++s)
+        mixed_stage_any<false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s], tw + ms.twoff[s]);
     for (int i = threadIdx.x; i < count; i += threads) {
         const V y = lds[i];
-        out.st(base + i, conj_out ? V{y.x * scale, -y.y * scale} : y);
+        out.st(base + i, INV ? V{y.x * scale, -y.y * scale} : y);
     }
 }
 
@@ -186,9 +198,9 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
 template <typename V> constexpr int mixed_cap_small() { return 2048; }
 template <typename V> constexpr int mixed_cap_large() { return 8192 * 8 / (int)sizeof(V); }
 
-template <typename V, bool PL>
-static hipError_t mixed_t(const Io& io, int64_t nrows, int n, MixedSchedule ms, const void* tw, bool ci, bool co,
-                          double scale, hipStream_t s)
+template <typename V, bool PL, bool INV>
+static hipError_t mixed_t(const Io& io, int64_t nrows, int n, const MixedSchedule& ms, const void* tw, double scale,
+                          hipStream_t s)
 {
     // threads per row: the power of two >= N/8 (so no thread has more than
     // ceil(8/R) butterflies in a stage), at most 1024; 256 threads or more
@@ -205,25 +217,33 @@ static hipError_t mixed_t(const Io& io, int64_t nrows, int n, MixedSchedule ms, 
     const auto in = make_in<V, PL>(io.in, io.in_im);
     const auto out = make_out<V, PL>(io.out, io.out_im);
     if (small)
-        hipLaunchKernelGGL((mixed_rows_kernel<V, mixed_cap_small<V>(), PL>), dim3((unsigned)blocks), dim3(tr * rpw), 0,
-                           s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (int)ci, (int)co, (Rl)scale);
+        hipLaunchKernelGGL((mixed_rows_kernel<V, mixed_cap_small<V>(), PL, INV>), dim3((unsigned)blocks),
+                           dim3(tr * rpw), 0, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
     else
-        hipLaunchKernelGGL((mixed_rows_kernel<V, mixed_cap_large<V>(), PL>), dim3((unsigned)blocks), dim3(tr * rpw), 0,
-                           s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (int)ci, (int)co, (Rl)scale);
+        hipLaunchKernelGGL((mixed_rows_kernel<V, mixed_cap_large<V>(), PL, INV>), dim3((unsigned)blocks),
+                           dim3(tr * rpw), 0, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
     return hipGetLastError();
 }
 
-hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool ci, bool co, const void* in, void* out,
+template <typename V, bool PL>
+static hipError_t mixed_dir(const Io& io, int64_t nrows, int n, const MixedSchedule& ms, bool inv, const void* tw,
+                            double scale, hipStream_t s)
+{
+    return inv ? mixed_t<V, PL, true>(io, nrows, n, ms, tw, scale, s)
+               : mixed_t<V, PL, false>(io, nrows, n, ms, tw, scale, s);
+}
+
+hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool inverse, const void* in, void* out,
                              int64_t nrows, const void* tw, double scale, hipStream_t s, const void* in_im,
                              void* out_im)
 {
     const Io io{in, in_im, out, out_im};
     const bool pl = in_im != nullptr;
     if (pl != (out_im != nullptr)) return hipErrorInvalidValue;
-    if (prec == 0) return pl ? mixed_t<float2, true>(io, nrows, n, ms, tw, ci, co, scale, s)
-                             : mixed_t<float2, false>(io, nrows, n, ms, tw, ci, co, scale, s);
-    return pl ? mixed_t<double2, true>(io, nrows, n, ms, tw, ci, co, scale, s)
-              : mixed_t<double2, false>(io, nrows, n, ms, tw, ci, co, scale, s);
+    if (prec == 0) return pl ? mixed_dir<float2, true>(io, nrows, n, ms, inverse, tw, scale, s)
+                             : mixed_dir<float2, false>(io, nrows, n, ms, inverse, tw, scale, s);
+    return pl ? mixed_dir<double2, true>(io, nrows, n, ms, inverse, tw, scale, s)
+              : mixed_dir<double2, false>(io, nrows, n, ms, inverse, tw, scale, s);
 }
 
 int mixed_max_n(int prec) { return prec == 0 ? mixed_cap_large<float2>() : mixed_cap_large<double2>(); }
