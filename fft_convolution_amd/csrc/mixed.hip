@@ -84,6 +84,76 @@ template <int R, typename V> __device__ __forceinline__ void dft_any(V (&u)[R])
         Dft<R>::run(u);
 }
 
+// p advanced by a 32-bit byte offset: lets the compiler address a uniform base
+// plus a per-lane 32-bit offset, with no 64-bit arithmetic per access.
+template <typename T> __device__ __forceinline__ T* at_bytes(T* p, unsigned off)
+{
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + off);
+}
+template <typename T> __device__ __forceinline__ const T* at_bytes(const T* p, unsigned off)
+{
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
+}
+
+typedef float mx_f4 __attribute__((ext_vector_type(4)));
+
+// The workgroup's segment [base, base + count) of the input into lds[0, count),
+// conjugated for the inverse.  Interleaved complex64 segments that start on
+// 16 bytes move two elements per streaming access.
+template <bool INV, typename V, bool PL>
+__device__ __forceinline__ void seg_load(const CIn<V, PL>& in, int64_t base, int count, V* lds, int threads)
+{
+    if constexpr (!PL && sizeof(V) == 8) {
+        if ((base & 1) == 0) {
+            const mx_f4* src = reinterpret_cast<const mx_f4*>(in.p + base);
+            const int pairs = count >> 1;
+            for (int i = threadIdx.x; i < pairs; i += threads) {
+                const mx_f4 q = __builtin_nontemporal_load(at_bytes(src, (unsigned)i * 16u));
+                lds[2 * i] = INV ? V{q.x, -q.y} : V{q.x, q.y};
+                lds[2 * i + 1] = INV ? V{q.z, -q.w} : V{q.z, q.w};
+            }
+            if ((count & 1) && threadIdx.x == 0) {
+                const V x = in.ld(base + count - 1);
+                lds[count - 1] = INV ? cconj(x) : x;
+            }
+            return;
+        }
+    }
+    for (int i = threadIdx.x; i < count; i += threads) {
+        const V x = in.ld(base + i);
+        lds[i] = INV ? cconj(x) : x;
+    }
+}
+
+// lds[0, count) to the output segment [base, base + count); the inverse
+// conjugates and scales.
+template <bool INV, typename V, bool PL>
+__device__ __forceinline__ void seg_store(const COut<V, PL>& out, int64_t base, int count, const V* lds, int threads,
+                                          typename real_of<V>::type scale)
+{
+    if constexpr (!PL && sizeof(V) == 8) {
+        if ((base & 1) == 0) {
+            mx_f4* dst = reinterpret_cast<mx_f4*>(out.p + base);
+            const int pairs = count >> 1;
+            for (int i = threadIdx.x; i < pairs; i += threads) {
+                const V a = lds[2 * i], b = lds[2 * i + 1];
+                const mx_f4 q = INV ? mx_f4{a.x * scale, -a.y * scale, b.x * scale, -b.y * scale}
+                                    : mx_f4{a.x, a.y, b.x, b.y};
+                __builtin_nontemporal_store(q, at_bytes(dst, (unsigned)i * 16u));
+            }
+            if ((count & 1) && threadIdx.x == 0) {
+                const V y = lds[count - 1];
+                out.st(base + count - 1, INV ? V{y.x * scale, -y.y * scale} : y);
+            }
+            return;
+        }
+    }
+    for (int i = threadIdx.x; i < count; i += threads) {
+        const V y = lds[i];
+        out.st(base + i, INV ? V{y.x * scale, -y.y * scale} : y);
+    }
+}
+
 // Butterflies per thread and stage: a row of N points has at least N/8
 // threads, so a radix-R stage (N/R butterflies) gives each at most ceil(8/R).
 template <int R> constexpr int mixed_bmax() { return (8 + R - 1) / R; }
@@ -114,7 +184,7 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
             int g = j;
             if constexpr (!FIRST) {
                 g = (int)__umulhi((unsigned)j, magic);
-                const V* t = tw + (j - g * ns) * S;
+                const V* t = at_bytes(tw, (unsigned)((j - g * ns) * S * (int)sizeof(V)));
                 V w[NL];
 #pragma unroll
                 for (int q = 0; q < NL; q += P) {
@@ -178,19 +248,13 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
     const int64_t base = row0 * n;
     // rows past the end of the batch (last workgroup only) are computed on
     // whatever LDS holds and never stored
-    for (int i = threadIdx.x; i < count; i += threads) {
-        const V x = in.ld(base + i);
-        lds[i] = INV ? cconj(x) : x;
-    }
+    seg_load<INV>(in, base, count, lds, threads);
     __syncthreads();
     V* row = lds + rl * n;
     mixed_stage_any<true>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw);
     for (int s = 1; s < ms.nst; ++s)
         mixed_stage_any<false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s], tw + ms.twoff[s]);
-    for (int i = threadIdx.x; i < count; i += threads) {
-        const V y = lds[i];
-        out.st(base + i, INV ? V{y.x * scale, -y.y * scale} : y);
-    }
+    seg_store<INV>(out, base, count, lds, threads, scale);
 }
 
 // LDS classes (slots): rows of up to 2048 points (several rows per workgroup
