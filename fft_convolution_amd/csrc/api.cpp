@@ -121,14 +121,14 @@ void root_of_unity_any(int64_t m, int64_t M, double* re, double* im)
     *im = -sin_sign * sn;
 }
 
-// Radices of a mixed-radix plan: 8s, then 4, 2, then 3s, 5s, 7s, and the
+// Radices of a mixed-radix plan: 8s, then 4, 2, then 9s, 3, 5s, 7s, and the
 // per-stage span, stride, quotient magic and twiddle-table offset; false if N
 // has another prime factor or needs more stages than the schedule holds.
 bool mixed_factor(int64_t n, MixedSchedule* ms)
 {
     ms->nst = 0;
     int64_t rest = n;
-    const int order[6] = {8, 4, 2, 3, 5, 7};
+    const int order[7] = {8, 4, 2, 9, 3, 5, 7};
     for (int r : order) {
         while (rest % r == 0) {
             if (ms->nst == kMixedMaxStages) return false;

@@ -1,5 +1,5 @@
 // mixed.hip -- rows whose length N = 2^a 3^b 5^c 7^d is not a power of two,
-// up to the one-kernel range: the Stockham stages with radices 8, 4, 2, 3, 5
+// up to the one-kernel range: the Stockham stages with radices 8, 4, 2, 9, 3, 5
 // and 7 ("FFT on GPU", section "Algorithm per signal Length", names mixed
 // radix for such lengths, with 12 = 3 x 4 as its example).
 //
@@ -22,22 +22,29 @@
 
 namespace fftmi {
 
-// cos(2 pi m / R) and sin(2 pi m / R), 1 <= m <= (R - 1) / 2, for R = 3, 5, 7
-// (correctly rounded doubles; the float kernels round them once more).
+// cos(2 pi m / R) and sin(2 pi m / R), 0 <= m <= (R - 1) / 2, for R = 3, 5, 7, 9
+// (correctly rounded doubles; the float kernels round them once more).  m = 0
+// arises for R = 9, where n k = 9 in the DFT below.
 __host__ __device__ constexpr double odd_cos(int r, int m)
 {
-    return r == 3 ? -0.5
+    return m == 0 ? 1.0
+         : r == 3 ? -0.5
          : r == 5 ? (m == 1 ? 0.3090169943749474241023 : -0.8090169943749474241023)
-                  : (m == 1 ? 0.6234898018587335305251 : m == 2 ? -0.2225209339563144042890 : -0.9009688679024191262361);
+         : r == 7 ? (m == 1 ? 0.6234898018587335305251 : m == 2 ? -0.2225209339563144042890 : -0.9009688679024191262361)
+                  : (m == 1 ? 0.7660444431189780352024 : m == 2 ? 0.1736481776669303488517
+                     : m == 3 ? -0.5 : -0.9396926207859083840541);
 }
 __host__ __device__ constexpr double odd_sin(int r, int m)
 {
-    return r == 3 ? 0.8660254037844386467637
+    return m == 0 ? 0.0
+         : r == 3 ? 0.8660254037844386467637
          : r == 5 ? (m == 1 ? 0.9510565162951535721164 : 0.5877852522924731291687)
-                  : (m == 1 ? 0.7818314824680298087084 : m == 2 ? 0.9749279121818236070181 : 0.4338837391175581204758);
+         : r == 7 ? (m == 1 ? 0.7818314824680298087084 : m == 2 ? 0.9749279121818236070181 : 0.4338837391175581204758)
+                  : (m == 1 ? 0.6427876096865393263226 : m == 2 ? 0.9848077530122080593667
+                     : m == 3 ? 0.8660254037844386467637 : 0.3420201433256687330441);
 }
 
-// Odd-radix DFT (R = 3, 5, 7) in registers, natural order in and out, by the
+// Odd-radix DFT (R = 3, 5, 7, 9) in registers, natural order in and out, by the
 // pairing of x_n with x_{R-n}:
 //   y_0 = x_0 + sum_n a_n,   y_k, y_{R-k} = x_0 + sum_n a_n c_{nk} -/+ i sum_n b_n s_{nk},
 // a_n = x_n + x_{R-n}, b_n = x_n - x_{R-n}, c_m = cos(2 pi m / R), s_m = sin(2 pi m / R)
@@ -78,7 +85,7 @@ template <int R, typename V> __device__ __forceinline__ void dft_odd(V (&u)[R])
 
 template <int R, typename V> __device__ __forceinline__ void dft_any(V (&u)[R])
 {
-    if constexpr (R == 3 || R == 5 || R == 7)
+    if constexpr (R % 2 == 1)
         dft_odd<R>(u);
     else
         Dft<R>::run(u);
@@ -154,9 +161,10 @@ __device__ __forceinline__ void seg_store(const COut<V, PL>& out, int64_t base, 
     }
 }
 
-// Butterflies per thread and stage: a row of N points has at least N/8
-// threads, so a radix-R stage (N/R butterflies) gives each at most ceil(8/R).
-template <int R> constexpr int mixed_bmax() { return (8 + R - 1) / R; }
+// Butterflies per thread and stage at most (about 8 elements a thread); the
+// launcher gives a row enough threads for every stage of its schedule.
+__host__ __device__ constexpr int mixed_bmax_of(int r) { return (8 + r - 1) / r; }
+template <int R> constexpr int mixed_bmax() { return mixed_bmax_of(R); }
 
 // One stage of radix R on a row held in LDS (`row`), thread tl of tr: for
 // every butterfly j < N/R, inputs row[j + r N/R], twiddles w_{Ns R}^{r k}
@@ -221,25 +229,29 @@ __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, i
         case 4: mixed_stage<4, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
         case 5: mixed_stage<5, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
         case 7: mixed_stage<7, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        case 9: mixed_stage<9, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
         default: mixed_stage<8, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
     }
 }
 
 // rpw rows per workgroup, tr threads per row (blockDim = rpw tr), rows
 // contiguous in LDS as in memory (row rl at rl N), so the workgroup's rows are
-// loaded and stored as one contiguous, coalesced segment.  CAP: LDS slots.
-// Threads per workgroup at most: N/8 for the longest row of each precision.
+// loaded and stored as one contiguous, coalesced segment.  LDS: exactly the
+// rpw N elements (dynamic, set at launch), so short and odd-sized rows do not
+// hold LDS they do not use.  Threads per workgroup at most: N/8 for the
+// longest row of each precision.
 // INV: conjugate in, conjugate and scale out.
 template <typename V> constexpr int mixed_max_threads() { return sizeof(V) == 8 ? 1024 : 512; }
 
-template <typename V, int CAP, bool PL, bool INV>
+template <typename V, bool PL, bool INV>
 __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out,
                                                                             int64_t nrows, int n, int tr, int rpw,
                                                                             MixedSchedule ms,
                                                                             const V* __restrict__ tw,
                                                                             typename real_of<V>::type scale)
 {
-    __shared__ V lds[CAP];
+    extern __shared__ __align__(16) unsigned char mixed_lds[];
+    V* lds = reinterpret_cast<V*>(mixed_lds);
     const int threads = tr * rpw;
     const int rl = threadIdx.x / tr, tl = threadIdx.x % tr;
     const int64_t row0 = (int64_t)blockIdx.x * rpw;
@@ -257,35 +269,29 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
     seg_store<INV>(out, base, count, lds, threads, scale);
 }
 
-// LDS classes (slots): rows of up to 2048 points (several rows per workgroup
-// for short ones), and one row of up to 8192 / 4096 points (64 KiB).
-template <typename V> constexpr int mixed_cap_small() { return 2048; }
-template <typename V> constexpr int mixed_cap_large() { return 8192 * 8 / (int)sizeof(V); }
+// Longest row: 64 KiB of LDS (8192 complex64 / 4096 complex128 points).
+template <typename V> constexpr int mixed_max_points() { return 65536 / (int)sizeof(V); }
 
 template <typename V, bool PL, bool INV>
 static hipError_t mixed_t(const Io& io, int64_t nrows, int n, const MixedSchedule& ms, const void* tw, double scale,
                           hipStream_t s)
 {
-    // threads per row: the power of two >= N/8 (so no thread has more than
-    // ceil(8/R) butterflies in a stage), at most 1024; 256 threads or more
-    // per workgroup
+    // threads per row: the least power of two that covers every stage's N/R
+    // butterflies at mixed_bmax(R) each; 256 threads or more per workgroup
     int tr = 1;
-    while (tr * 8 < n) tr *= 2;
+    for (int q = 0; q < ms.nst; ++q)
+        while ((int64_t)tr * mixed_bmax_of(ms.radix[q]) < n / ms.radix[q]) tr *= 2;
     if (tr > mixed_max_threads<V>()) return hipErrorInvalidValue;
     const int rpw = tr >= 256 ? 1 : 256 / tr;
-    const bool small = rpw * n <= mixed_cap_small<V>();
-    if (!small && rpw * n > mixed_cap_large<V>()) return hipErrorInvalidValue;
+    const int64_t lds_bytes = (int64_t)rpw * n * (int64_t)sizeof(V);
+    if (lds_bytes > 65536) return hipErrorInvalidValue;
     const int64_t blocks = (nrows + rpw - 1) / rpw;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
     const auto in = make_in<V, PL>(io.in, io.in_im);
     const auto out = make_out<V, PL>(io.out, io.out_im);
-    if (small)
-        hipLaunchKernelGGL((mixed_rows_kernel<V, mixed_cap_small<V>(), PL, INV>), dim3((unsigned)blocks),
-                           dim3(tr * rpw), 0, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
-    else
-        hipLaunchKernelGGL((mixed_rows_kernel<V, mixed_cap_large<V>(), PL, INV>), dim3((unsigned)blocks),
-                           dim3(tr * rpw), 0, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
+    hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV>), dim3((unsigned)blocks), dim3(tr * rpw), (unsigned)lds_bytes, s,
+                       in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
     return hipGetLastError();
 }
 
@@ -310,6 +316,6 @@ hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool inve
               : mixed_dir<double2, false>(io, nrows, n, ms, inverse, tw, scale, s);
 }
 
-int mixed_max_n(int prec) { return prec == 0 ? mixed_cap_large<float2>() : mixed_cap_large<double2>(); }
+int mixed_max_n(int prec) { return prec == 0 ? mixed_max_points<float2>() : mixed_max_points<double2>(); }
 
 }  // namespace fftmi

@@ -89,7 +89,7 @@ enum fft_status {
  *           "FFT on GPU" (section "Algorithm per signal Length") names for
  *           such lengths:
  *           - N = 2^a 3^b 5^c 7^d up to 8192 (C32) / 4096 (C64): mixed-radix
- *             Stockham stages (radices 8, 4, 2, 3, 5, 7) in one kernel, no
+ *             Stockham stages (radices 8, 4, 2, 9, 3, 5, 7) in one kernel, no
  *             workspace;
  *           - any other N: chirp-z (Bluestein), X_k = c_k (x.c * conj c)_k
  *             with c_j = e^{-i pi j^2/N}, the convolution done cyclically at
