@@ -15,6 +15,17 @@
 
 namespace fftmi {
 
+// p advanced by a 32-bit byte offset: lets the compiler address a uniform base
+// plus a per-lane 32-bit offset, with no 64-bit arithmetic per access.
+template <typename T> __device__ __forceinline__ T* at_bytes(T* p, unsigned off)
+{
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + off);
+}
+template <typename T> __device__ __forceinline__ const T* at_bytes(const T* p, unsigned off)
+{
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
+}
+
 template <typename Rl> __device__ __forceinline__ Rl ld_nt(const Rl* p) { return __builtin_nontemporal_load(p); }
 template <typename Rl> __device__ __forceinline__ void st_nt(Rl* p, Rl x) { __builtin_nontemporal_store(x, p); }
 
@@ -27,6 +38,9 @@ template <typename V> struct CIn<V, false> {
     __device__ __forceinline__ V ld(int64_t i) const { return ld_stream(p + i); }
     __device__ __forceinline__ V ld_plain(int64_t i) const { return p[i]; }
     template <int P> __device__ __forceinline__ void ldv(int64_t i, V (&d)[P]) const { vload(p + i, d); }
+    // the array from element `base` on, then element e < 2^32 / sizeof(V) of it
+    __device__ __forceinline__ CIn at(int64_t base) const { return CIn{p + base, nullptr}; }
+    __device__ __forceinline__ V ld32(unsigned e) const { return ld_stream(at_bytes(p, e * (unsigned)sizeof(V))); }
 };
 
 template <typename V> struct CIn<V, true> {
@@ -45,6 +59,12 @@ template <typename V> struct CIn<V, true> {
         d[1] = float2{a.y, b.y};
     }
     __device__ __forceinline__ void ldv(int64_t i, double2 (&d)[1]) const { d[0] = double2{re[i], im[i]}; }
+    __device__ __forceinline__ CIn at(int64_t base) const { return CIn{re + base, im + base}; }
+    __device__ __forceinline__ V ld32(unsigned e) const
+    {
+        const unsigned o = e * (unsigned)sizeof(Rl);
+        return V{ld_nt(at_bytes(re, o)), ld_nt(at_bytes(im, o))};
+    }
 };
 
 template <typename V> struct COut<V, false> {
@@ -53,6 +73,8 @@ template <typename V> struct COut<V, false> {
     __device__ __forceinline__ void st(int64_t i, V y) const { st_stream(p + i, y); }
     __device__ __forceinline__ void st_plain(int64_t i, V y) const { p[i] = y; }
     template <int P> __device__ __forceinline__ void stv(int64_t i, const V (&s)[P]) const { vstore(p + i, s); }
+    __device__ __forceinline__ COut at(int64_t base) const { return COut{p + base, nullptr}; }
+    __device__ __forceinline__ void st32(unsigned e, V y) const { st_stream(at_bytes(p, e * (unsigned)sizeof(V)), y); }
 };
 
 template <typename V> struct COut<V, true> {
@@ -78,6 +100,13 @@ template <typename V> struct COut<V, true> {
     {
         re[i] = s[0].x;
         im[i] = s[0].y;
+    }
+    __device__ __forceinline__ COut at(int64_t base) const { return COut{re + base, im + base}; }
+    __device__ __forceinline__ void st32(unsigned e, V y) const
+    {
+        const unsigned o = e * (unsigned)sizeof(Rl);
+        st_nt(at_bytes(re, o), y.x);
+        st_nt(at_bytes(im, o), y.y);
     }
 };
 

@@ -10,9 +10,11 @@
 // the last stage the row is in natural order.
 //
 // Unlike the power-of-two engine (compile-time geometry), the schedule here is
-// a runtime list: a group of TR >= N/8 threads owns a row held in LDS; each
-// stage reads its butterflies into registers, and writes them back in place
-// after a barrier.  The row crosses HBM once each way.  Each stage s >= 1 reads
+// a runtime list: a group of TR threads owns a row.  The first stage reads its
+// butterflies from the input rows and writes the row into LDS; each later
+// stage reads its butterflies from LDS into registers and writes them back in
+// place after a barrier, except the last, which writes to the output rows.
+// The row crosses HBM once each way.  Each stage s >= 1 reads
 // its twiddles w_{Ns R}^{r k}, r = 1 .. R-1, as one row of a per-stage table
 // (16-byte loads, no products of table values), and splits j into (j / Ns,
 // j mod Ns) with a multiply-high by a precomputed reciprocal.
@@ -91,17 +93,6 @@ template <int R, typename V> __device__ __forceinline__ void dft_any(V (&u)[R])
         Dft<R>::run(u);
 }
 
-// p advanced by a 32-bit byte offset: lets the compiler address a uniform base
-// plus a per-lane 32-bit offset, with no 64-bit arithmetic per access.
-template <typename T> __device__ __forceinline__ T* at_bytes(T* p, unsigned off)
-{
-    return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + off);
-}
-template <typename T> __device__ __forceinline__ const T* at_bytes(const T* p, unsigned off)
-{
-    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
-}
-
 typedef float mx_f4 __attribute__((ext_vector_type(4)));
 
 // The workgroup's segment [base, base + count) of the input into lds[0, count),
@@ -166,15 +157,35 @@ __device__ __forceinline__ void seg_store(const COut<V, PL>& out, int64_t base, 
 __host__ __device__ constexpr int mixed_bmax_of(int r) { return (8 + r - 1) / r; }
 template <int R> constexpr int mixed_bmax() { return mixed_bmax_of(R); }
 
-// One stage of radix R on a row held in LDS (`row`), thread tl of tr: for
-// every butterfly j < N/R, inputs row[j + r N/R], twiddles w_{Ns R}^{r k}
-// from the table row k = j mod Ns (none in the first stage, Ns = 1), the
-// R-point DFT, outputs at g Ns R + k + r Ns, g = j / Ns.  All butterflies are
-// read and computed into registers, then (after a barrier across the
-// workgroup) written back in place.
-template <int R, bool FIRST, typename V>
+// Where a stage reads and writes.  Rows of 64 threads or more (a wave within
+// one row): the first stage reads its butterflies straight from the input rows
+// (for each r the lanes' inputs j + r N/R are contiguous) and the last writes
+// straight to the output rows (its butterflies j < N/R = Ns all have g = 0, so
+// the outputs k + r Ns are contiguous too); a row of one stage (N = R) goes
+// from input to output.  Shorter rows, where a wave spans several rows, are
+// copied into LDS and back as contiguous 16-byte segments instead, and every
+// stage works in LDS.
+// The rows of one workgroup: input and output from its first element, the
+// offset of this thread's row in them, whether that row exists (the last
+// workgroup may have fewer), and the inverse's output scale.
+template <typename V, bool PL> struct MixedRows {
+    CIn<V, PL> in;
+    COut<V, PL> out;
+    unsigned rbase;
+    bool live;
+    typename real_of<V>::type scale;
+};
+
+// One stage of radix R, thread tl of tr: for every butterfly j < N/R, inputs
+// x[j + r N/R], twiddles w_{Ns R}^{r k} from the table row k = j mod Ns (none
+// in the first stage, Ns = 1), the R-point DFT, outputs at g Ns R + k + r Ns,
+// g = j / Ns.  A stage within LDS reads all its butterflies into registers
+// before a barrier across the workgroup and writes them back in place after
+// it.  INV: the first stage conjugates its inputs, the last conjugates and
+// scales its outputs.
+template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, typename V, bool PL>
 __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, int ns, unsigned magic,
-                                            const V* __restrict__ tw)
+                                            const V* __restrict__ tw, const MixedRows<V, PL>& io)
 {
     constexpr int B = mixed_bmax<R>();
     constexpr int S = mixed_tw_slots(R);
@@ -187,8 +198,18 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
         const int j = tl + b * tr;
         dst[b] = -1;
         if (j < stride) {
+            if constexpr (FROM_IN) {
+                if (io.live) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) u[b][r] = row[j + r * stride];
+                    for (int r = 0; r < R; ++r) {
+                        const V x = io.in.ld32(io.rbase + (unsigned)(j + r * stride));
+                        u[b][r] = INV ? cconj(x) : x;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) u[b][r] = row[j + r * stride];
+            }
             int g = j;
             if constexpr (!FIRST) {
                 g = (int)__umulhi((unsigned)j, magic);
@@ -208,42 +229,58 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
             dst[b] = j + g * (ns * (R - 1));  // g Ns R + k
         }
     }
-    __syncthreads();  // every read of this stage is done before any write
+    if constexpr (TO_OUT) {
+        if (!io.live) return;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        if (dst[b] >= 0) {
+        for (int b = 0; b < B; ++b) {
+            if (dst[b] >= 0) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) row[dst[b] + r * ns] = u[b][r];
+                for (int r = 0; r < R; ++r) {
+                    const V y = u[b][r];
+                    io.out.st32(io.rbase + (unsigned)(dst[b] + r * ns),
+                                INV ? V{y.x * io.scale, -y.y * io.scale} : y);
+                }
+            }
         }
+    } else {
+        if constexpr (!FROM_IN) __syncthreads();  // every read of this stage is done before any write
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (dst[b] >= 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) row[dst[b] + r * ns] = u[b][r];
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 }
 
-template <bool FIRST, typename V>
+template <bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, typename V, bool PL>
 __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, int stride, int ns, unsigned magic,
-                                                const V* __restrict__ tw)
+                                                const V* __restrict__ tw, const MixedRows<V, PL>& io)
 {
+#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, INV>(row, tl, tr, stride, ns, magic, tw, io)
     switch (r) {
-        case 2: mixed_stage<2, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
-        case 3: mixed_stage<3, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
-        case 4: mixed_stage<4, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
-        case 5: mixed_stage<5, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
-        case 7: mixed_stage<7, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
-        case 9: mixed_stage<9, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
-        default: mixed_stage<8, FIRST>(row, tl, tr, stride, ns, magic, tw); break;
+        case 2: MX_STAGE(2); break;
+        case 3: MX_STAGE(3); break;
+        case 4: MX_STAGE(4); break;
+        case 5: MX_STAGE(5); break;
+        case 7: MX_STAGE(7); break;
+        case 9: MX_STAGE(9); break;
+        default: MX_STAGE(8); break;
     }
+#undef MX_STAGE
 }
 
 // rpw rows per workgroup, tr threads per row (blockDim = rpw tr), rows
-// contiguous in LDS as in memory (row rl at rl N), so the workgroup's rows are
-// loaded and stored as one contiguous, coalesced segment.  LDS: exactly the
+// contiguous in LDS as in memory (row rl at rl N).  LDS: exactly the
 // rpw N elements (dynamic, set at launch), so short and odd-sized rows do not
 // hold LDS they do not use.  Threads per workgroup at most: N/8 for the
 // longest row of each precision.
 // INV: conjugate in, conjugate and scale out.
 template <typename V> constexpr int mixed_max_threads() { return sizeof(V) == 8 ? 1024 : 512; }
 
-template <typename V, bool PL, bool INV>
+template <typename V, bool PL, bool INV, bool DIRECT>
 __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out,
                                                                             int64_t nrows, int n, int tr, int rpw,
                                                                             MixedSchedule ms,
@@ -252,21 +289,36 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
 {
     extern __shared__ __align__(16) unsigned char mixed_lds[];
     V* lds = reinterpret_cast<V*>(mixed_lds);
-    const int threads = tr * rpw;
     const int rl = threadIdx.x / tr, tl = threadIdx.x % tr;
     const int64_t row0 = (int64_t)blockIdx.x * rpw;
-    const int rows = (int)(nrows - row0 < rpw ? nrows - row0 : rpw);
-    const int count = rows * n;
     const int64_t base = row0 * n;
-    // rows past the end of the batch (last workgroup only) are computed on
-    // whatever LDS holds and never stored
-    seg_load<INV>(in, base, count, lds, threads);
-    __syncthreads();
+    const MixedRows<V, PL> io{in.at(base), out.at(base), (unsigned)(rl * n), row0 + rl < nrows, scale};
     V* row = lds + rl * n;
-    mixed_stage_any<true>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw);
-    for (int s = 1; s < ms.nst; ++s)
-        mixed_stage_any<false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s], tw + ms.twoff[s]);
-    seg_store<INV>(out, base, count, lds, threads, scale);
+    const int last = ms.nst - 1;
+    if constexpr (DIRECT) {
+        if (last == 0) {
+            mixed_stage_any<true, true, true, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+            return;
+        }
+        mixed_stage_any<true, true, false, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+        for (int s = 1; s < last; ++s)
+            mixed_stage_any<false, false, false, INV>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s],
+                                                      tw + ms.twoff[s], io);
+        mixed_stage_any<false, false, true, INV>(ms.radix[last], row, tl, tr, ms.stride[last], ms.ns[last],
+                                                 ms.magic[last], tw + ms.twoff[last], io);
+    } else {
+        // rows past the end of the batch (last workgroup only) are computed
+        // on whatever LDS holds and never stored
+        const int threads = tr * rpw;
+        const int rows = (int)(nrows - row0 < rpw ? nrows - row0 : rpw);
+        seg_load<INV>(in, base, rows * n, lds, threads);
+        __syncthreads();
+        mixed_stage_any<true, false, false, false>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+        for (int s = 1; s <= last; ++s)
+            mixed_stage_any<false, false, false, false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s],
+                                                        ms.magic[s], tw + ms.twoff[s], io);
+        seg_store<INV>(out, base, rows * n, lds, threads, scale);
+    }
 }
 
 // Longest row: 64 KiB of LDS (8192 complex64 / 4096 complex128 points).
@@ -290,8 +342,12 @@ static hipError_t mixed_t(const Io& io, int64_t nrows, int n, const MixedSchedul
     using Rl = typename real_of<V>::type;
     const auto in = make_in<V, PL>(io.in, io.in_im);
     const auto out = make_out<V, PL>(io.out, io.out_im);
-    hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV>), dim3((unsigned)blocks), dim3(tr * rpw), (unsigned)lds_bytes, s,
-                       in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
+    if (tr >= 64)
+        hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV, true>), dim3((unsigned)blocks), dim3(tr * rpw),
+                           (unsigned)lds_bytes, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
+    else
+        hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV, false>), dim3((unsigned)blocks), dim3(tr * rpw),
+                           (unsigned)lds_bytes, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
     return hipGetLastError();
 }
 
