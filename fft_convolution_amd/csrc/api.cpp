@@ -818,7 +818,7 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
             // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
             if ((int64_t(1) << plan->logm) <= max_lds_n(plan->prec)) {  // one kernel
                 e = launch_bluestein_rows(plan->prec, plan->logm, (int)plan->n, io.in, io.out, batch,
-                                          plan->inner->tw_a, plan->chirp, plan->bspec, inv, inv, scale, s, io.in_im,
+                                          plan->inner->tw_a, plan->chirp, plan->bspec, inv, scale, s, io.in_im,
                                           io.out_im);
                 break;
             }

@@ -33,17 +33,31 @@ __global__ void narrow_kernel(const double2* __restrict__ in, float2* __restrict
         out[e] = float2{(float)in[e].x, (float)in[e].y};
 }
 
+// a w with the rounding pinned: each part is one product rounded, then a fused
+// multiply-add.  The chirp and spectrum products sit next to the loads and
+// stores, whose form differs between interleaved and planar rows; with the
+// fusion left to the compiler the two could round differently.
+__device__ __forceinline__ float fma_r(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_r(double a, double b, double c) { return __builtin_fma(a, b, c); }
+template <typename V> __device__ __forceinline__ V cmul_pinned(V a, V w)
+{
+    const auto p = a.y * w.y;
+    const auto q = a.y * w.x;
+    return V{fma_r(a.x, w.x, -p), fma_r(a.x, w.y, q)};
+}
+
 // The whole chirp-z transform of a row in one kernel, for M = 2^LOGM within
 // the row kernel's range: the row is loaded once (times the chirp, zero
 // padded to M in registers), transformed, multiplied by B, transformed back
 // (conj F conj / M) and stored once (times the chirp) -- the same arithmetic
 // as the five-pass route, without its four HBM round trips over M points.
-// tw: stage table for M; conj_in / conj_out and scale as the five passes.
-template <typename V, int LOGM, bool PL>
+// tw: stage table for M.  INV: the inverse transform (conj in, conj and scale
+// out).  The twiddle bases are loaded again for the second transform rather
+// than held in registers across the first.
+template <typename V, int LOGM, bool PL, bool INV>
 __global__ __launch_bounds__((Geom<V, LOGM>::T * rows_per_wg<V, LOGM>()))
 void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n, const V* __restrict__ tw,
-                           const V* __restrict__ chirp, const V* __restrict__ bspec, int conj_in, int conj_out,
-                           typename real_of<V>::type scale)
+                           const V* __restrict__ chirp, const V* __restrict__ bspec, typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGM>;
     using Rl = typename real_of<V>::type;
@@ -57,78 +71,87 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
     const bool live = row < nrows;
     const LdsLines<V, 1> L{lds + rloc * G::LDS, 0};
 
-    TwBases<V, LOGM> tb;
-    tb.load(tw, t);
     V v[G::E];
     const int64_t base = row * n;
+    {
+        TwBases<V, LOGM> tb;
+        tb.load(tw, t);
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) {
-        const int p = t + i * G::T;
-        V x{0, 0};
-        if (live && p < n) {
-            x = in.ld(base + p);
-            if (conj_in) x = cconj(x);
-            x = cmul(x, chirp[p]);
+        for (int i = 0; i < G::E; ++i) {
+            const int p = t + i * G::T;
+            V x{0, 0};
+            if (live && p < n) {
+                x = in.ld(base + p);
+                if (INV) x = cconj(x);
+                x = cmul_pinned(x, chirp[p]);
+            }
+            v[i] = x;
         }
-        v[i] = x;
+        fft_regs<LOGM>(v, t, tb, L);
     }
-    fft_regs<LOGM>(v, t, tb, L);
     // W B, conjugated for the inverse transform
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) v[i] = cconj(cmul(v[i], bspec[t + i * G::T]));
+    for (int i = 0; i < G::E; ++i) v[i] = cconj(cmul_pinned(v[i], bspec[t + i * G::T]));
     __syncthreads();  // the forward transform's last exchange is read by now
-    fft_regs<LOGM>(v, t, tb, L);
+    {
+        TwBases<V, LOGM> tb;
+        tb.load(tw, t);
+        fft_regs<LOGM>(v, t, tb, L);
+    }
     if (!live) return;
     const Rl inv_m = (Rl)1 / (Rl)(1 << LOGM);
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
         const int p = t + i * G::T;
         if (p < n) {
-            const V y = cmul(V{v[i].x * inv_m, -v[i].y * inv_m}, chirp[p]);
-            out.st(base + p, conj_out ? V{y.x * scale, -y.y * scale} : y);
+            const V y = cmul_pinned(V{v[i].x * inv_m, -v[i].y * inv_m}, chirp[p]);
+            out.st(base + p, INV ? V{y.x * scale, -y.y * scale} : y);
         }
     }
 }
 
-template <typename V, int LOGM, bool PL>
+template <typename V, int LOGM, bool PL, bool INV>
 static hipError_t bluestein_rows_t(const Io& io, int64_t nrows, int n, const void* tw, const void* chirp,
-                                   const void* bspec, bool ci, bool co, double scale, hipStream_t s)
+                                   const void* bspec, double scale, hipStream_t s)
 {
     constexpr int RPW = rows_per_wg<V, LOGM>();
     constexpr int BLOCK = Geom<V, LOGM>::T * RPW;
     const int64_t blocks = (nrows + RPW - 1) / RPW;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     using Rl = typename real_of<V>::type;
-    hipLaunchKernelGGL((bluestein_rows_kernel<V, LOGM, PL>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
+    hipLaunchKernelGGL((bluestein_rows_kernel<V, LOGM, PL, INV>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
                        make_in<V, PL>(io.in, io.in_im), make_out<V, PL>(io.out, io.out_im), nrows, n, (const V*)tw,
-                       (const V*)chirp, (const V*)bspec, (int)ci, (int)co, (Rl)scale);
+                       (const V*)chirp, (const V*)bspec, (Rl)scale);
     return hipGetLastError();
 }
 
 template <typename V, int LOGM>
 static hipError_t bluestein_rows_pl(const Io& io, int64_t nrows, int n, const void* tw, const void* chirp,
-                                    const void* bspec, bool ci, bool co, double scale, hipStream_t s)
+                                    const void* bspec, bool inv, double scale, hipStream_t s)
 {
-    if (io.in_im) return bluestein_rows_t<V, LOGM, true>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
-    return bluestein_rows_t<V, LOGM, false>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+    if (io.in_im)
+        return inv ? bluestein_rows_t<V, LOGM, true, true>(io, nrows, n, tw, chirp, bspec, scale, s)
+                   : bluestein_rows_t<V, LOGM, true, false>(io, nrows, n, tw, chirp, bspec, scale, s);
+    return inv ? bluestein_rows_t<V, LOGM, false, true>(io, nrows, n, tw, chirp, bspec, scale, s)
+               : bluestein_rows_t<V, LOGM, false, false>(io, nrows, n, tw, chirp, bspec, scale, s);
 }
 
 hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void* out, int64_t nrows, const void* tw,
-                                 const void* chirp, const void* bspec, bool ci, bool co, double scale, hipStream_t s,
+                                 const void* chirp, const void* bspec, bool inverse, double scale, hipStream_t s,
                                  const void* in_im, void* out_im)
 {
     const Io io{in, in_im, out, out_im};
     if ((in_im != nullptr) != (out_im != nullptr)) return hipErrorInvalidValue;
 #define FFTMI_BL(L)                                                                                          \
     case L:                                                                                                  \
-        return prec == 0 ? bluestein_rows_pl<float2, L>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s)   \
-                         : bluestein_rows_pl<double2, L>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+        return prec == 0 ? bluestein_rows_pl<float2, L>(io, nrows, n, tw, chirp, bspec, inverse, scale, s)   \
+                         : bluestein_rows_pl<double2, L>(io, nrows, n, tw, chirp, bspec, inverse, scale, s);
     if (prec == 1 && logm > 12) return hipErrorInvalidValue;
     switch (logm) {
         FFTMI_BL(2) FFTMI_BL(3) FFTMI_BL(4) FFTMI_BL(5) FFTMI_BL(6) FFTMI_BL(7) FFTMI_BL(8) FFTMI_BL(9)
         FFTMI_BL(10) FFTMI_BL(11) FFTMI_BL(12)
         case 13:
-            if (prec == 0) return bluestein_rows_pl<float2, 13>(io, nrows, n, tw, chirp, bspec, ci, co, scale, s);
+            if (prec == 0) return bluestein_rows_pl<float2, 13>(io, nrows, n, tw, chirp, bspec, inverse, scale, s);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }

@@ -122,9 +122,10 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
 
 // The whole Bluestein transform of each row in one kernel, M = 2^logm within
 // the row kernel's range (logm <= 13 complex64, 12 complex128); tw: stage
-// table for M.  Planar needs both in_im and out_im.  in -> out, may alias.
+// table for M.  Inverse: conjugate in, conjugate and scale out.  Planar needs
+// both in_im and out_im.  in -> out, may alias.
 hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void* out, int64_t nrows, const void* tw,
-                                 const void* chirp, const void* bspec, bool conj_in, bool conj_out, double scale,
+                                 const void* chirp, const void* bspec, bool inverse, double scale,
                                  hipStream_t stream, const void* in_im = nullptr, void* out_im = nullptr);
 // Bluestein beyond the row kernel's range: the chirp products and the
 // product with B carried by the first / last passes of the M-point
