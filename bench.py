@@ -25,7 +25,7 @@ Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
 transform the same way, and the R2C transform of 16384 real rows of 8192
 points (value = batch * 2.5 N log2 N / t, half the complex count), and rows
-of 1000 (mixed radix) and 1001 (Bluestein) points, and the 2D R2C transform
+of 1000 (mixed radix) and 1009 (Bluestein) points, and the 2D R2C transform
 of eight real 2048 x 2048 images.
 """
 from __future__ import annotations
@@ -45,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
              "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384", "c2c_n1000_b65536",
-             "c2c_n1001_b65536", "r2c2d_2048x2048_b8")
+             "c2c_n1009_b65536", "r2c2d_2048x2048_b8")
 
 
 # The sources each single-kernel workload's kernel is built from: a stored
@@ -55,7 +55,7 @@ KERNEL_SOURCES = {
     "c2c_n1024_b64": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
     "r2c_n8192_b16384": ("real.hip", "stockham.hpp", "radix_plan.hpp", "tile_common.hpp"),
     "c2c_n1000_b65536": ("mixed.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
-    "c2c_n1001_b65536": ("bluestein.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
+    "c2c_n1009_b65536": ("bluestein.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
 }
 
 

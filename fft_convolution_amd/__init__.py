@@ -10,7 +10,7 @@ call fails, the error propagates.
 Thin conveniences built on those calls:
 
 * :class:`Plan` -- owns a plan handle; ``fft``/``ifft`` (rank 1, any length up
-  to the limits: power-of-two, mixed-radix 2/3/5/7 or Bluestein), ``fft2``/``ifft2``
+  to the limits: power-of-two, mixed-radix 2/3/5/7/11/13 or Bluestein), ``fft2``/``ifft2``
   (rank 2), ``fft3``/``ifft3`` (rank 3), ``planar`` (split re / im tensors, any
   rank) and ``poly_mul`` (rank 1, complex128) on contiguous device tensors.
 * :class:`RealPlan` -- ``rfft``/``irfft`` of real rows.

@@ -121,14 +121,14 @@ void root_of_unity_any(int64_t m, int64_t M, double* re, double* im)
     *im = -sin_sign * sn;
 }
 
-// Radices of a mixed-radix plan: 8s, then 4, 2, then 9s, 3, 5s, 7s, and the
+// Radices of a mixed-radix plan: 8s, then 4, 2, then 9s, 3, 5s, 7s, 11s, 13s, and the
 // per-stage span, stride, quotient magic and twiddle-table offset; false if N
 // has another prime factor or needs more stages than the schedule holds.
 bool mixed_factor(int64_t n, MixedSchedule* ms)
 {
     ms->nst = 0;
     int64_t rest = n;
-    const int order[7] = {8, 4, 2, 9, 3, 5, 7};
+    const int order[9] = {8, 4, 2, 9, 3, 5, 7, 11, 13};
     for (int r : order) {
         while (rest % r == 0) {
             if (ms->nst == kMixedMaxStages) return false;
@@ -402,7 +402,7 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
     if (rank == 1) {
         const int64_t n = dims[0];
         if (!is_pow2(n)) {
-            // lengths of 2, 3, 5 and 7 only, within one workgroup's LDS: mixed
+            // lengths of 2, 3, 5, 7, 11 and 13 only, within one workgroup's LDS: mixed
             // radix in one kernel; any other length: Bluestein
             if (n <= mixed_max_n(prec) && mixed_factor(n, &p->mixed)) {
                 p->path = PATH_MIXED;

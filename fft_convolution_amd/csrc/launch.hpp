@@ -20,8 +20,8 @@ struct BigTwiddle {
     int logn;
 };
 
-// Stages of a mixed-radix row of N points: radix R_s (each 2, 3, 4, 5, 7, 8 or
-// 9; product N), span ns_s = R_0 ... R_{s-1}, stride N / R_s, magic_s =
+// Stages of a mixed-radix row of N points: radix R_s (each 2, 3, 4, 5, 7, 8,
+// 9, 11 or 13; product N), span ns_s = R_0 ... R_{s-1}, stride N / R_s, magic_s =
 // ceil(2^32 / ns_s) (so j / ns_s = mulhi(j, magic_s) for j ns_s < 2^32), and
 // twoff_s: where stage s >= 1 starts in the twiddle table, which holds, for
 // every k < ns_s, the row w_{ns_s R_s}^{r k}, r = 1 .. R_s - 1, padded to

@@ -1,6 +1,6 @@
-// mixed.hip -- rows whose length N = 2^a 3^b 5^c 7^d is not a power of two,
-// up to the one-kernel range: the Stockham stages with radices 8, 4, 2, 9, 3, 5
-// and 7 ("FFT on GPU", section "Algorithm per signal Length", names mixed
+// mixed.hip -- rows whose length N = 2^a 3^b 5^c 7^d 11^e 13^f is not a power of two,
+// up to the one-kernel range: the Stockham stages with radices 8, 4, 2, 9, 3, 5,
+// 7, 11 and 13 ("FFT on GPU", section "Algorithm per signal Length", names mixed
 // radix for such lengths, with 12 = 3 x 4 as its example).
 //
 // The stage is the one of radix_plan.hpp with a radix that varies from stage
@@ -24,29 +24,67 @@
 
 namespace fftmi {
 
-// cos(2 pi m / R) and sin(2 pi m / R), 0 <= m <= (R - 1) / 2, for R = 3, 5, 7, 9
-// (correctly rounded doubles; the float kernels round them once more).  m = 0
-// arises for R = 9, where n k = 9 in the DFT below.
+// cos(2 pi m / R) and sin(2 pi m / R), 0 <= m <= (R - 1) / 2, for R = 3, 5, 7,
+// 9, 11, 13 (correctly rounded doubles; the float kernels round them once
+// more).  m = 0 arises for R = 9, where n k = 9 in the DFT below.
 __host__ __device__ constexpr double odd_cos(int r, int m)
 {
-    return m == 0 ? 1.0
-         : r == 3 ? -0.5
-         : r == 5 ? (m == 1 ? 0.3090169943749474241023 : -0.8090169943749474241023)
-         : r == 7 ? (m == 1 ? 0.6234898018587335305251 : m == 2 ? -0.2225209339563144042890 : -0.9009688679024191262361)
-                  : (m == 1 ? 0.7660444431189780352024 : m == 2 ? 0.1736481776669303488517
-                     : m == 3 ? -0.5 : -0.9396926207859083840541);
+    if (m == 0) return 1.0;
+    switch (r * 16 + m) {
+        case 3 * 16 + 1: return -0.5;
+        case 5 * 16 + 1: return 0.3090169943749474241023;
+        case 5 * 16 + 2: return -0.8090169943749474241023;
+        case 7 * 16 + 1: return 0.6234898018587335305251;
+        case 7 * 16 + 2: return -0.2225209339563144042890;
+        case 7 * 16 + 3: return -0.9009688679024191262361;
+        case 9 * 16 + 1: return 0.7660444431189780352024;
+        case 9 * 16 + 2: return 0.1736481776669303488517;
+        case 9 * 16 + 3: return -0.5;
+        case 9 * 16 + 4: return -0.9396926207859083840541;
+        case 11 * 16 + 1: return 0.8412535328311811688618;
+        case 11 * 16 + 2: return 0.4154150130018864255293;
+        case 11 * 16 + 3: return -0.1423148382732851404438;
+        case 11 * 16 + 4: return -0.6548607339452850640569;
+        case 11 * 16 + 5: return -0.9594929736144973898904;
+        case 13 * 16 + 1: return 0.8854560256532098959004;
+        case 13 * 16 + 2: return 0.5680647467311558025118;
+        case 13 * 16 + 3: return 0.1205366802553230533491;
+        case 13 * 16 + 4: return -0.3546048870425356259696;
+        case 13 * 16 + 5: return -0.7485107481711010986346;
+        case 13 * 16 + 6: return -0.9709418174260520271570;
+        default: return 0.0;
+    }
 }
 __host__ __device__ constexpr double odd_sin(int r, int m)
 {
-    return m == 0 ? 0.0
-         : r == 3 ? 0.8660254037844386467637
-         : r == 5 ? (m == 1 ? 0.9510565162951535721164 : 0.5877852522924731291687)
-         : r == 7 ? (m == 1 ? 0.7818314824680298087084 : m == 2 ? 0.9749279121818236070181 : 0.4338837391175581204758)
-                  : (m == 1 ? 0.6427876096865393263226 : m == 2 ? 0.9848077530122080593667
-                     : m == 3 ? 0.8660254037844386467637 : 0.3420201433256687330441);
+    if (m == 0) return 0.0;
+    switch (r * 16 + m) {
+        case 3 * 16 + 1: return 0.8660254037844386467637;
+        case 5 * 16 + 1: return 0.9510565162951535721164;
+        case 5 * 16 + 2: return 0.5877852522924731291687;
+        case 7 * 16 + 1: return 0.7818314824680298087084;
+        case 7 * 16 + 2: return 0.9749279121818236070181;
+        case 7 * 16 + 3: return 0.4338837391175581204758;
+        case 9 * 16 + 1: return 0.6427876096865393263226;
+        case 9 * 16 + 2: return 0.9848077530122080593667;
+        case 9 * 16 + 3: return 0.8660254037844386467637;
+        case 9 * 16 + 4: return 0.3420201433256687330441;
+        case 11 * 16 + 1: return 0.5406408174555975821076;
+        case 11 * 16 + 2: return 0.9096319953545183714117;
+        case 11 * 16 + 3: return 0.9898214418809327323761;
+        case 11 * 16 + 4: return 0.7557495743542582837740;
+        case 11 * 16 + 5: return 0.2817325568414296977114;
+        case 13 * 16 + 1: return 0.4647231720437685456560;
+        case 13 * 16 + 2: return 0.8229838658936563945796;
+        case 13 * 16 + 3: return 0.9927088740980539928007;
+        case 13 * 16 + 4: return 0.9350162426854148234398;
+        case 13 * 16 + 5: return 0.6631226582407952023768;
+        case 13 * 16 + 6: return 0.2393156642875577671488;
+        default: return 0.0;
+    }
 }
 
-// Odd-radix DFT (R = 3, 5, 7, 9) in registers, natural order in and out, by the
+// Odd-radix DFT (R = 3, 5, 7, 9, 11, 13) in registers, natural order in and out, by the
 // pairing of x_n with x_{R-n}:
 //   y_0 = x_0 + sum_n a_n,   y_k, y_{R-k} = x_0 + sum_n a_n c_{nk} -/+ i sum_n b_n s_{nk},
 // a_n = x_n + x_{R-n}, b_n = x_n - x_{R-n}, c_m = cos(2 pi m / R), s_m = sin(2 pi m / R)
@@ -255,11 +293,24 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
     }
 }
 
-template <bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, typename V, bool PL>
+// WIDE: the schedule may hold radices 11 and 13, whose DFTs keep more values
+// live; kernels for the other schedules are compiled without them so that
+// they keep their lower register count.
+template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, typename V, bool PL>
 __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, int stride, int ns, unsigned magic,
                                                 const V* __restrict__ tw, const MixedRows<V, PL>& io)
 {
 #define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, INV>(row, tl, tr, stride, ns, magic, tw, io)
+    if constexpr (WIDE) {
+        if (r == 11) {
+            MX_STAGE(11);
+            return;
+        }
+        if (r == 13) {
+            MX_STAGE(13);
+            return;
+        }
+    }
     switch (r) {
         case 2: MX_STAGE(2); break;
         case 3: MX_STAGE(3); break;
@@ -280,7 +331,7 @@ __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, i
 // INV: conjugate in, conjugate and scale out.
 template <typename V> constexpr int mixed_max_threads() { return sizeof(V) == 8 ? 1024 : 512; }
 
-template <typename V, bool PL, bool INV, bool DIRECT>
+template <typename V, bool PL, bool INV, bool DIRECT, bool WIDE>
 __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<V, PL> in, COut<V, PL> out,
                                                                             int64_t nrows, int n, int tr, int rpw,
                                                                             MixedSchedule ms,
@@ -297,14 +348,14 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
     const int last = ms.nst - 1;
     if constexpr (DIRECT) {
         if (last == 0) {
-            mixed_stage_any<true, true, true, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+            mixed_stage_any<WIDE, true, true, true, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
             return;
         }
-        mixed_stage_any<true, true, false, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+        mixed_stage_any<WIDE, true, true, false, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
         for (int s = 1; s < last; ++s)
-            mixed_stage_any<false, false, false, INV>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s],
+            mixed_stage_any<WIDE, false, false, false, INV>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s],
                                                       tw + ms.twoff[s], io);
-        mixed_stage_any<false, false, true, INV>(ms.radix[last], row, tl, tr, ms.stride[last], ms.ns[last],
+        mixed_stage_any<WIDE, false, false, true, INV>(ms.radix[last], row, tl, tr, ms.stride[last], ms.ns[last],
                                                  ms.magic[last], tw + ms.twoff[last], io);
     } else {
         // rows past the end of the batch (last workgroup only) are computed
@@ -313,9 +364,9 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
         const int rows = (int)(nrows - row0 < rpw ? nrows - row0 : rpw);
         seg_load<INV>(in, base, rows * n, lds, threads);
         __syncthreads();
-        mixed_stage_any<true, false, false, false>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+        mixed_stage_any<WIDE, true, false, false, false>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
         for (int s = 1; s <= last; ++s)
-            mixed_stage_any<false, false, false, false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s],
+            mixed_stage_any<WIDE, false, false, false, false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s],
                                                         ms.magic[s], tw + ms.twoff[s], io);
         seg_store<INV>(out, base, rows * n, lds, threads, scale);
     }
@@ -342,12 +393,20 @@ static hipError_t mixed_t(const Io& io, int64_t nrows, int n, const MixedSchedul
     using Rl = typename real_of<V>::type;
     const auto in = make_in<V, PL>(io.in, io.in_im);
     const auto out = make_out<V, PL>(io.out, io.out_im);
-    if (tr >= 64)
-        hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV, true>), dim3((unsigned)blocks), dim3(tr * rpw),
-                           (unsigned)lds_bytes, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
-    else
-        hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV, false>), dim3((unsigned)blocks), dim3(tr * rpw),
-                           (unsigned)lds_bytes, s, in, out, nrows, n, tr, rpw, ms, (const V*)tw, (Rl)scale);
+    bool wide = false;
+    for (int q = 0; q < ms.nst; ++q) wide = wide || ms.radix[q] > 9;
+    const dim3 grid((unsigned)blocks), block(tr * rpw);
+#define MX_LAUNCH(D, W)                                                                                        \
+    hipLaunchKernelGGL((mixed_rows_kernel<V, PL, INV, D, W>), grid, block, (unsigned)lds_bytes, s, in, out, nrows, n, \
+                       tr, rpw, ms, (const V*)tw, (Rl)scale)
+    if (tr >= 64) {
+        if (wide) MX_LAUNCH(true, true);
+        else MX_LAUNCH(true, false);
+    } else {
+        if (wide) MX_LAUNCH(false, true);
+        else MX_LAUNCH(false, false);
+    }
+#undef MX_LAUNCH
     return hipGetLastError();
 }
 

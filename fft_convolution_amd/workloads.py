@@ -21,7 +21,7 @@ stated):
 * a 256^3 volume, re and im uniform [-1, 1) (seed 6), for the 3D transform.
 * ``real_normal`` -- real rows of N points, i.i.d. standard normal: the real
   operands of the R2C / C2R transforms.  N = 8192 x 16384 rows (seed 7).
-* rows of 1000 and 1001 points x 65536, ``batched_normal`` (seeds 8, 9): the
+* rows of 1000 and 1009 points x 65536, ``batched_normal`` (seeds 8, 9): the
   mixed-radix and Bluestein paths.
 * real 2048 x 2048 images x 8, ``real_normal`` (seed 10): the 2D R2C path.
 """
@@ -41,9 +41,9 @@ WORKLOADS = {
     # real rows, the R2C transform (512 MiB of float32 in)
     "r2c_n8192_b16384": dict(kind="real_normal", n=8192, batch=16384, seed=7),
     # lengths that are not powers of two (~500 MiB in): 1000 = 8 * 5^3 (mixed
-    # radix), 1001 = 7 * 11 * 13 (Bluestein, M = 2048)
+    # radix), 1009 prime (Bluestein, M = 2048)
     "c2c_n1000_b65536": dict(kind="normal", n=1000, batch=65536, seed=8),
-    "c2c_n1001_b65536": dict(kind="normal", n=1001, batch=65536, seed=9),
+    "c2c_n1009_b65536": dict(kind="normal", n=1009, batch=65536, seed=9),
     # real 2048 x 2048 images, the 2D R2C transform
     "r2c2d_2048x2048_b8": dict(kind="real_images", h=2048, w=2048, batch=8, seed=10),
 }

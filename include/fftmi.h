@@ -88,9 +88,9 @@ enum fft_status {
  *           N not a power of two (N <= FFT_MAX_BLUESTEIN_N), the two routes
  *           "FFT on GPU" (section "Algorithm per signal Length") names for
  *           such lengths:
- *           - N = 2^a 3^b 5^c 7^d up to 8192 (C32) / 4096 (C64): mixed-radix
- *             Stockham stages (radices 8, 4, 2, 9, 3, 5, 7) in one kernel, no
- *             workspace;
+ *           - N = 2^a 3^b 5^c 7^d 11^e 13^f up to 8192 (C32) / 4096 (C64):
+ *             mixed-radix Stockham stages (radices 8, 4, 2, 9, 3, 5, 7, 11,
+ *             13) in one kernel, no workspace;
  *           - any other N: chirp-z (Bluestein), X_k = c_k (x.c * conj c)_k
  *             with c_j = e^{-i pi j^2/N}, the convolution done cyclically at
  *             the power-of-two M >= 2N - 1 by the library's own transforms.

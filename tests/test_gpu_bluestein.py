@@ -28,8 +28,8 @@ def _m(n):
     return m
 
 
-# lengths with a prime factor above 7, or beyond the mixed-radix range
-@pytest.mark.parametrize("n,batch", [(11, 4), (13, 1), (22, 3), (97, 2), (1001, 2), (4095, 2), (4097, 1),
+# lengths with a prime factor above 13, or beyond the mixed-radix range
+@pytest.mark.parametrize("n,batch", [(17, 4), (19, 1), (34, 3), (97, 2), (1009, 2), (4093, 2), (4097, 1),
                                      (10007, 1), (3 * 4096, 2)])
 @pytest.mark.parametrize("dtype", [np.complex64, np.complex128])
 def test_bluestein_small_full(dev, n, batch, dtype):

@@ -16,8 +16,9 @@ from conftest import fft_tol, rel_rms_rows
 
 pytestmark = pytest.mark.gpu
 
-F32 = [3, 5, 6, 7, 12, 15, 30, 49, 60, 100, 105, 210, 343, 360, 1000, 2187, 2401, 3125, 6000, 6144, 7168, 8000]
-F64 = [3, 12, 100, 105, 1000, 2187, 2401, 3000, 3072, 4000]
+F32 = [3, 5, 6, 7, 11, 12, 13, 15, 30, 49, 60, 100, 105, 143, 210, 343, 360, 1000, 1001, 1331, 2187, 2197, 2401,
+       3125, 6000, 6144, 7168, 8000, 8008]
+F64 = [3, 11, 12, 13, 100, 105, 1000, 1001, 2187, 2401, 3000, 3072, 4000, 4095]
 
 
 def _radices(desc):
@@ -79,10 +80,11 @@ def test_mixed_closed_forms_and_in_place(dev):
 
 
 def test_mixed_range_limits(dev):
-    # beyond one workgroup's LDS, or a prime factor above 7: Bluestein
+    # beyond one workgroup's LDS, or a prime factor above 13: Bluestein
     assert "bluestein" in fm.Plan(3 * 4096, torch.complex64).describe()
     assert "bluestein" in fm.Plan(3 * 2048, torch.complex128).describe()
-    assert "bluestein" in fm.Plan(11 * 64, torch.complex64).describe()
+    assert "bluestein" in fm.Plan(17 * 64, torch.complex64).describe()
+    assert "mixed" in fm.Plan(11 * 13 * 32, torch.complex64).describe()
     assert "mixed" in fm.Plan(3 * 2048, torch.complex64).describe()
     # a large batch of short rows (many rows per workgroup, ragged last group)
     n, batch = 12, 100003
@@ -91,11 +93,11 @@ def test_mixed_range_limits(dev):
     assert rel_rms_rows(y, oracle.dft(x_np)).max() <= fft_tol(n)
 
 
-def _seven_smooth(limit):
+def _smooth13(limit):
     out = []
     for n in range(3, limit + 1):
         m = n
-        for p in (2, 3, 5, 7):
+        for p in (2, 3, 5, 7, 11, 13):
             while m % p == 0:
                 m //= p
         if m == 1 and n & (n - 1):
@@ -105,13 +107,13 @@ def _seven_smooth(limit):
 
 @pytest.mark.parametrize("dtype,limit", [(torch.complex64, 8192), (torch.complex128, 4096)])
 def test_mixed_every_smooth_length(dev, dtype, limit):
-    """Every length 2^a 3^b 5^c 7^d (not a power of two) in the mixed-radix
-    range: two rows, forward and inverse, against the direct DFT (all bins up
-    to 2048 points, 48 bins spread over the spectrum beyond)."""
+    """Every length 2^a 3^b 5^c 7^d 11^e 13^f (not a power of two) in the
+    mixed-radix range: two rows, forward and inverse, against the direct DFT
+    (all bins up to 2048 points, 48 bins spread over the spectrum beyond)."""
     npdt = np.complex64 if dtype == torch.complex64 else np.complex128
     oracle.set_threads(8)
     bad = []
-    for n in _seven_smooth(limit):
+    for n in _smooth13(limit):
         plan = fm.Plan(n, dtype)
         assert "path=mixed" in plan.describe(), n
         x_np = wl.batched_uniform(n, 2, seed=7000 + n, dtype=npdt)

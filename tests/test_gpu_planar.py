@@ -30,7 +30,8 @@ CASES = [
     ((1 << 20,), torch.complex64, 1),      # three passes
     ((1 << 13,), torch.complex128, 2),     # two passes, fp64
     ((1 << 19,), torch.complex128, 1),     # three passes, fp64
-    ((1001,), torch.complex64, 3),         # Bluestein
+    ((1009,), torch.complex64, 3),         # Bluestein
+    ((1001,), torch.complex64, 3),         # mixed radix with 11 and 13
     ((4097,), torch.complex128, 2),
     ((60,), torch.complex64, 7),           # mixed radix
     ((2401,), torch.complex128, 2),

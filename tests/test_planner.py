@@ -23,7 +23,7 @@ def _field(desc, key):
 
 
 def _smooth(n):
-    for p in (2, 3, 5, 7):
+    for p in (2, 3, 5, 7, 11, 13):
         while n % p == 0:
             n //= p
     return n == 1
@@ -57,7 +57,7 @@ def test_every_length_up_to_20000(prec):
         if _smooth(n) and n <= MIXED_MAX[prec]:
             assert "path=mixed" in d, (n, d)
             r = [int(x) for x in _field(d, "radices").split("x")]
-            assert math.prod(r) == n and set(r) <= {2, 3, 4, 5, 7, 8, 9}, (n, d)
+            assert math.prod(r) == n and set(r) <= {2, 3, 4, 5, 7, 8, 9, 11, 13}, (n, d)
             assert len(r) <= 16
         else:
             assert "path=bluestein" in d, (n, d)
