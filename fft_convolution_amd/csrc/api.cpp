@@ -158,6 +158,67 @@ int64_t mixed_table_entries(const MixedSchedule& ms)
     return e;
 }
 
+// A mixed-radix twiddle table (see MixedSchedule), interleaved fp64: rows
+// w_{ns R}^{r k}, r = 1 .. R-1, for k < ns, per stage s >= 1; pad entries 0
+// (N = R alone has no table: one entry, unused).
+std::vector<double> mixed_table(const MixedSchedule& ms)
+{
+    std::vector<double> t(2 * (size_t)std::max<int64_t>(1, mixed_table_entries(ms)), 0.0);
+    for (int q = 1; q < ms.nst; ++q) {
+        const int r = ms.radix[q];
+        const int64_t ns = ms.ns[q];
+        for (int64_t k = 0; k < ns; ++k)
+            for (int j = 1; j < r; ++j) {
+                const size_t e = (size_t)(ms.twoff[q] + k * mixed_tw_slots(r) + (j - 1));
+                root_of_unity_any(j * k, ns * r, &t[2 * e], &t[2 * e + 1]);
+            }
+    }
+    return t;
+}
+
+// Radices of a multi-pass mixed-radix plan: N = r[0] r[1] (r[2]), each at
+// most kMixPassMax, as few passes as possible, then as even as possible (the
+// largest smallest factor), larger first.  Returns the pass count, 0 if none.
+constexpr int kMixPassMax = 512;
+int mixed_split(int64_t n, int* r)
+{
+    std::vector<int64_t> divs;
+    for (int64_t d = 2; d <= kMixPassMax && d < n; ++d)
+        if (n % d == 0) divs.push_back(d);
+    for (int np = 2; np <= 3; ++np) {
+        int64_t best[3] = {0, 0, 0}, best_min = 0;
+        for (int64_t a : divs) {
+            if (np == 2) {
+                const int64_t b = n / a;
+                if (b >= 2 && b <= kMixPassMax && std::min(a, b) > best_min) {
+                    best_min = std::min(a, b);
+                    best[0] = a;
+                    best[1] = b;
+                }
+                continue;
+            }
+            for (int64_t b : divs) {
+                if ((n / a) % b) continue;
+                const int64_t c = n / a / b;
+                if (c < 2 || c > kMixPassMax) continue;
+                const int64_t m = std::min(a, std::min(b, c));
+                if (m > best_min) {
+                    best_min = m;
+                    best[0] = a;
+                    best[1] = b;
+                    best[2] = c;
+                }
+            }
+        }
+        if (best_min > 0) {
+            std::sort(best, best + np, [](int64_t x, int64_t y) { return x > y; });
+            for (int q = 0; q < np; ++q) r[q] = (int)best[q];
+            return np;
+        }
+    }
+    return 0;
+}
+
 // Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
 // interleaved doubles: stage s >= 1 holds [l][k] = w_{Ns R}^{k 2^l}.
 std::vector<double> stage_table(int logn, int prec)
@@ -186,12 +247,16 @@ enum PlanPath {
     PATH_ND = 3,
     PATH_BLUESTEIN = 4,
     PATH_REAL = 5,
-    PATH_MIXED = 6
+    PATH_MIXED = 6,
+    PATH_MIXPASS = 7
 };
 
 // One super-stage pass of a multi-pass plan.
 struct PassPlan {
     int logr = 0, logns = 0, kind = 0;
+    // mixed-radix passes: radix r (its stage schedule ms), span ns
+    int r = 0, ns = 0;
+    MixedSchedule ms{};
     const void* tw = nullptr;  // stage table for 2^logr (owned by the plan's table list)
     void* big_hi = nullptr;    // tables for w_M, M = 2^(logns + logr) (owned)
     void* big_lo = nullptr;
@@ -313,6 +378,22 @@ int upload_big(int logm, int prec, void** hi_dev, void** lo_dev, int* lbits, int
     return st;
 }
 
+// Two-level table for w_M^m, any M: lo[q] = w_M^q (q < 2^lbits), hi[q] =
+// w_M^{q 2^lbits} (q < ceil(M / 2^lbits)).
+int upload_big_any(int64_t m, int prec, void** hi_dev, void** lo_dev, int* lbits)
+{
+    int lm = 0;
+    while ((int64_t(1) << lm) < m) ++lm;
+    *lbits = (lm + 1) / 2;
+    const int64_t nlo = int64_t(1) << *lbits, nhi = (m + nlo - 1) / nlo;
+    std::vector<double> lo(2 * nlo), hi(2 * nhi);
+    for (int64_t q = 0; q < nlo; ++q) root_of_unity_any(q, m, &lo[2 * q], &lo[2 * q + 1]);
+    for (int64_t q = 0; q < nhi; ++q) root_of_unity_any(q * nlo, m, &hi[2 * q], &hi[2 * q + 1]);
+    int st = upload(lo, prec, lo_dev);
+    if (st == FFT_OK) st = upload(hi, prec, hi_dev);
+    return st;
+}
+
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -374,7 +455,7 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
         return p->dims[0] > 1 ? (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem : 0;
     if (p->path == PATH_REAL)  // the H-point spectrum of every row, beyond the one-kernel range
         return p->real_fused || p->n == 1 ? 0 : (size_t)batch * (size_t)(p->n / 2) * p->elem;
-    const bool need = p->path == PATH_MULTIPASS || (p->path == PATH_ND && p->logf > 0);
+    const bool need = p->path == PATH_MULTIPASS || p->path == PATH_MIXPASS || (p->path == PATH_ND && p->logf > 0);
     return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
 
@@ -402,10 +483,25 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
     if (rank == 1) {
         const int64_t n = dims[0];
         if (!is_pow2(n)) {
-            // lengths of 2, 3, 5, 7, 11 and 13 only, within one workgroup's LDS: mixed
-            // radix in one kernel; any other length: Bluestein
+            // lengths of 2, 3, 5, 7, 11 and 13 only: mixed radix, in one kernel
+            // within one workgroup's LDS, else in 2-3 super-stage passes; any
+            // other length: Bluestein
+            int rs[3];
+            int np = 0;
             if (n <= mixed_max_n(prec) && mixed_factor(n, &p->mixed)) {
                 p->path = PATH_MIXED;
+            } else if (n > mixed_max_n(prec) && mixed_factor(n, &p->mixed) && (np = mixed_split(n, rs)) > 0) {
+                p->path = PATH_MIXPASS;
+                p->npass = np;
+                int64_t ns = 1;
+                for (int q = 0; q < np; ++q) {
+                    PassPlan& pp = p->passes[q];
+                    pp.r = rs[q];
+                    pp.ns = (int)ns;
+                    if (!mixed_factor(pp.r, &pp.ms))
+                        return fail(FFT_ERR_UNSUPPORTED_SIZE, "no pass schedule for n = %lld", (long long)n);
+                    ns *= rs[q];
+                }
             } else {
                 p->path = PATH_BLUESTEIN;
                 while ((int64_t(1) << p->logm) < 2 * n - 1) ++p->logm;
@@ -567,23 +663,18 @@ int upload_tables(fft_plan* p)
         case PATH_BLUESTEIN:
             st = bluestein_tables(p);
             break;
-        case PATH_MIXED: {
-            // rows w_{ns R}^{r k}, r = 1 .. R-1, for k < ns, per stage s >= 1;
-            // pad entries 0 (N = R alone has no table: one entry, unused)
-            const MixedSchedule& ms = p->mixed;
-            std::vector<double> t(2 * (size_t)std::max<int64_t>(1, mixed_table_entries(ms)), 0.0);
-            for (int q = 1; q < ms.nst; ++q) {
-                const int r = ms.radix[q];
-                const int64_t ns = ms.ns[q];
-                for (int64_t k = 0; k < ns; ++k)
-                    for (int j = 1; j < r; ++j) {
-                        const size_t e = (size_t)(ms.twoff[q] + k * mixed_tw_slots(r) + (j - 1));
-                        root_of_unity_any(j * k, ns * r, &t[2 * e], &t[2 * e + 1]);
-                    }
-            }
-            st = upload(t, prec, &p->tw_a);
+        case PATH_MIXED:
+            st = upload(mixed_table(p->mixed), prec, &p->tw_a);
             break;
-        }
+        case PATH_MIXPASS:
+            for (int q = 0; q < p->npass && st == FFT_OK; ++q) {
+                PassPlan& pp = p->passes[q];
+                st = upload(mixed_table(pp.ms), prec, &p->pass_tw[q]);
+                pp.tw = p->pass_tw[q];
+                if (st == FFT_OK && q > 0)
+                    st = upload_big_any((int64_t)pp.ns * pp.r, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
+            }
+            break;
         case PATH_ROWS:
             st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
             break;
@@ -743,6 +834,12 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                 snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
                          p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
             break;
+        case PATH_MIXPASS: {
+            int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=mixpass radices=", (long long)p->n, prec);
+            for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
+                off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->passes[q].r);
+            break;
+        }
         case PATH_MULTIPASS: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
             for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
@@ -814,6 +911,34 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
             e = launch_mixed_rows(plan->prec, (int)plan->n, plan->mixed, inv, io.in, io.out, batch, plan->tw_a,
                                   scale, s, io.in_im, io.out_im);
             break;
+        case PATH_MIXPASS: {
+            // the buffers of the power-of-two multi-pass path: in -> ws -> out
+            // (-> out, the last pass in place), planar in -> ws (-> ws2) -> out
+            const size_t sig = (size_t)batch * (size_t)plan->n * plan->elem;
+            void* ws2 = (char*)workspace + sig;
+            const void* src = io.in;
+            const int lines = mixed_pass_lines(plan->prec);
+            for (int q = 0; q < plan->npass && e == hipSuccess; ++q) {
+                const PassPlan& pp = plan->passes[q];
+                const bool last = q == plan->npass - 1;
+                void* dst = q == 0 ? workspace : (last || !planar) ? io.out : ws2;
+                MixedPassArgs a{};
+                a.n = (int)plan->n;
+                a.r = pp.r;
+                a.ns = pp.ns;
+                a.stride = (int)(plan->n / pp.r);
+                a.tiles = (a.stride + lines - 1) / lines;
+                a.tr = mixed_pass_threads(pp.ms, pp.r);
+                a.rmagic = (unsigned)(((uint64_t(1) << 32) + pp.r - 1) / pp.r);
+                a.conj_in = inv && q == 0;
+                a.conj_out = inv && last;
+                const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, 0};
+                e = launch_mixed_pass(plan->prec, a, pp.ms, src, dst, batch, pp.tw, big, scale, s,
+                                      q == 0 ? io.in_im : nullptr, last ? io.out_im : nullptr);
+                src = dst;
+            }
+            break;
+        }
         case PATH_BLUESTEIN: {
             // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
             if ((int64_t(1) << plan->logm) <= max_lds_n(plan->prec)) {  // one kernel
@@ -998,7 +1123,8 @@ static size_t planar_workspace(const fft_plan* p, int64_t batch)
 {
     const size_t sig = (size_t)batch * (size_t)p->n * p->elem;
     switch (p->path) {
-        case PATH_MULTIPASS: return p->npass >= 3 ? 2 * sig : sig;
+        case PATH_MULTIPASS:
+        case PATH_MIXPASS: return p->npass >= 3 ? 2 * sig : sig;
         case PATH_BLUESTEIN: return c2c_workspace(p, batch);
         case PATH_ND: return p->nd_k >= 2 ? (p->col_split ? 2 * sig : sig) : 0;
         default: return 0;
@@ -1061,7 +1187,7 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (plan->rank != 1 || plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "poly-mul needs a complex rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
-    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED)
+    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED || plan->path == PATH_MIXPASS)
         return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
     if (plan->logn > kPolyMaxLog) return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
     *bytes = plan->path == PATH_MULTIPASS ? (size_t)batch * (size_t)plan->n * plan->elem : 0;
@@ -1076,7 +1202,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
     if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
-    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED)
+    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED || plan->path == PATH_MIXPASS)
         return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
     if (plan->logn > kPolyMaxLog)
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);

@@ -46,6 +46,24 @@ hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool inve
                              const void* in_im = nullptr, void* out_im = nullptr);
 int mixed_max_n(int prec);
 
+// One mixed-radix super-stage pass (mixed.hip) over `batch` signals of n
+// points: radix r (<= 512, its stage schedule `ms`, twiddle table `tw` of
+// that schedule), span ns, stride n / r, tiles = ceil(stride / lines) per
+// signal, tr threads per line (mixed_pass_threads), rmagic = ceil(2^32 / r);
+// big: w_{ns r}^m (unused for ns = 1).  conj_in / conj_out + scale: the
+// inverse's first / last pass.  Planar: in_im on a first pass, or out_im on a
+// last pass, not both.  in -> out; in place only for the last pass (ns r = n).
+struct MixedPassArgs {
+    int n, r, ns, stride, tiles, tr;
+    unsigned rmagic;
+    int conj_in, conj_out;
+};
+int mixed_pass_threads(const MixedSchedule& ms, int r);
+int mixed_pass_lines(int prec);
+hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedule& ms, const void* in, void* out,
+                             int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t stream,
+                             const void* in_im = nullptr, void* out_im = nullptr);
+
 // Lines per workgroup of the tile passes (tiles.hip) for lines of 2^logl points.
 int tile_lines_2d(int prec, int logl);
 

@@ -220,8 +220,9 @@ template <typename V, bool PL> struct MixedRows {
 // g = j / Ns.  A stage within LDS reads all its butterflies into registers
 // before a barrier across the workgroup and writes them back in place after
 // it.  INV: the first stage conjugates its inputs, the last conjugates and
-// scales its outputs.
-template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, typename V, bool PL>
+// scales its outputs.  ES: LDS slots between consecutive elements of a row
+// (1 for a row of its own; the tile width where rows are interleaved).
+template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, int ES = 1, typename V, bool PL>
 __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, int ns, unsigned magic,
                                             const V* __restrict__ tw, const MixedRows<V, PL>& io)
 {
@@ -246,7 +247,7 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
                 }
             } else {
 #pragma unroll
-                for (int r = 0; r < R; ++r) u[b][r] = row[j + r * stride];
+                for (int r = 0; r < R; ++r) u[b][r] = row[(j + r * stride) * ES];
             }
             int g = j;
             if constexpr (!FIRST) {
@@ -286,7 +287,7 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
         for (int b = 0; b < B; ++b) {
             if (dst[b] >= 0) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) row[dst[b] + r * ns] = u[b][r];
+                for (int r = 0; r < R; ++r) row[(dst[b] + r * ns) * ES] = u[b][r];
             }
         }
         __syncthreads();
@@ -296,11 +297,11 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
 // WIDE: the schedule may hold radices 11 and 13, whose DFTs keep more values
 // live; kernels for the other schedules are compiled without them so that
 // they keep their lower register count.
-template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, typename V, bool PL>
+template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, int ES = 1, typename V, bool PL>
 __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, int stride, int ns, unsigned magic,
                                                 const V* __restrict__ tw, const MixedRows<V, PL>& io)
 {
-#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, INV>(row, tl, tr, stride, ns, magic, tw, io)
+#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, INV, ES>(row, tl, tr, stride, ns, magic, tw, io)
     if constexpr (WIDE) {
         if (r == 11) {
             MX_STAGE(11);
@@ -432,5 +433,148 @@ hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool inve
 }
 
 int mixed_max_n(int prec) { return prec == 0 ? mixed_max_points<float2>() : mixed_max_points<double2>(); }
+
+// ---------------------------------------------------------------------------
+// Rows beyond one workgroup: N = R_0 R_1 ... as Stockham super-stages, one
+// pass each (radix R <= 512, span Ns = R_0 ... R_{p-1}): for every butterfly
+// j < N/R, inputs x[j + q N/R] times w_{Ns R}^{q k} (k = j mod Ns), the
+// R-point DFT (the mixed-radix stages above, on a line of the tile), outputs at
+// g Ns R + k + q Ns (g = j / Ns).
+//
+// A workgroup takes LINES consecutive butterflies (a 128-byte segment of
+// elements for each q) into LDS, element q of line c at q (LINES + 1) + c (the
+// extra slot per element row keeps both store orders free of bank
+// conflicts).  The first pass (Ns = 1) writes each line's outputs j R + q, so
+// the tile's lines together are one contiguous block; later passes write, for
+// each q, the lines' outputs side by side.
+// ---------------------------------------------------------------------------
+
+// w_M^m for any M (m < M < 2^31) from two tables: hi[q] = w_M^{q 2^lbits},
+// lo[q] = w_M^q.
+template <typename V> struct AnyTw {
+    const V* __restrict__ hi;
+    const V* __restrict__ lo;
+    int lbits;
+    __device__ __forceinline__ V operator()(int m) const
+    {
+        return cmul(hi[m >> lbits], lo[m & ((1 << lbits) - 1)]);
+    }
+};
+
+template <typename V> constexpr int mp_lines() { return 128 / (int)sizeof(V); }
+
+template <typename V, bool WIDE, int RCAP, typename IN, typename OUT>
+__global__ __launch_bounds__(1024) void mixed_pass_kernel(IN in, OUT out, MixedPassArgs a, MixedSchedule ms,
+                                                          const V* __restrict__ tw, AnyTw<V> big,
+                                                          typename real_of<V>::type scale)
+{
+    constexpr int LINES = mp_lines<V>();
+    constexpr int P = LINES + 1;
+    __shared__ V lds[P * RCAP];
+    const int c = threadIdx.x % LINES, tl = threadIdx.x / LINES;
+    const int64_t sig = (int64_t)blockIdx.x / a.tiles;
+    const int j0 = (int)((int64_t)blockIdx.x - sig * a.tiles) * LINES;
+    const int j = j0 + c;
+    const bool live = j < a.stride;
+    const int g = j / a.ns, k = j - g * a.ns;
+    const int64_t sbase = sig * (int64_t)a.n;
+    for (int q = tl; q < a.r; q += a.tr) {
+        V x{0, 0};
+        if (live) {
+            x = in.ld(sbase + j + (int64_t)q * a.stride);
+            if (a.conj_in) x = cconj(x);
+            if (a.ns > 1) x = cmul(x, big(q * k));
+        }
+        lds[q * P + c] = x;
+    }
+    __syncthreads();
+    const MixedRows<V, false> none{};
+    V* row = lds + c;
+    mixed_stage_any<WIDE, true, false, false, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, none);
+    for (int s = 1; s < ms.nst; ++s)
+        mixed_stage_any<WIDE, false, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
+                                                             ms.magic[s], tw + ms.twoff[s], none);
+    if (a.ns == 1) {
+        const int lines = a.stride - j0 < LINES ? a.stride - j0 : LINES;
+        const int count = lines * a.r;
+        const int64_t obase = sbase + (int64_t)j0 * a.r;
+        for (int e = threadIdx.x; e < count; e += blockDim.x) {
+            const int cl = (int)__umulhi((unsigned)e, a.rmagic);
+            const V y = lds[(e - cl * a.r) * P + cl];
+            out.st(obase + e, a.conj_out ? V{y.x * scale, -y.y * scale} : y);
+        }
+    } else if (live) {
+        const int64_t obase = sbase + (int64_t)g * a.ns * a.r + k;
+        for (int q = tl; q < a.r; q += a.tr) {
+            const V y = lds[q * P + c];
+            out.st(obase + (int64_t)q * a.ns, a.conj_out ? V{y.x * scale, -y.y * scale} : y);
+        }
+    }
+}
+
+// LDS classes: radix <= 128 and <= 512.
+template <typename V, bool WIDE, typename IN, typename OUT>
+static hipError_t mixed_pass_t(IN in, OUT out, int64_t batch, const MixedPassArgs& a, const MixedSchedule& ms,
+                               const void* tw, const BigTwiddle& bt, double scale, hipStream_t s)
+{
+    using Rl = typename real_of<V>::type;
+    const int64_t blocks = (int64_t)a.tiles * batch;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const AnyTw<V> big{(const V*)bt.hi, (const V*)bt.lo, bt.lbits};
+    const dim3 grid((unsigned)blocks), block(mp_lines<V>() * a.tr);
+    if (a.r <= 128)
+        hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 128, IN, OUT>), grid, block, 0, s, in, out, a, ms,
+                           (const V*)tw, big, (Rl)scale);
+    else
+        hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 512, IN, OUT>), grid, block, 0, s, in, out, a, ms,
+                           (const V*)tw, big, (Rl)scale);
+    return hipGetLastError();
+}
+
+template <typename V, typename IN, typename OUT>
+static hipError_t mixed_pass_w(IN in, OUT out, int64_t batch, const MixedPassArgs& a, const MixedSchedule& ms,
+                               const void* tw, const BigTwiddle& bt, double scale, hipStream_t s)
+{
+    bool wide = false;
+    for (int q = 0; q < ms.nst; ++q) wide = wide || ms.radix[q] > 9;
+    return wide ? mixed_pass_t<V, true>(in, out, batch, a, ms, tw, bt, scale, s)
+                : mixed_pass_t<V, false>(in, out, batch, a, ms, tw, bt, scale, s);
+}
+
+template <typename V>
+static hipError_t mixed_pass_v(const Io& io, int64_t batch, const MixedPassArgs& a, const MixedSchedule& ms,
+                               const void* tw, const BigTwiddle& bt, double scale, hipStream_t s)
+{
+    if (io.in_im) return mixed_pass_w<V>(make_in<V, true>(io.in, io.in_im), make_out<V, false>(io.out, nullptr), batch,
+                                         a, ms, tw, bt, scale, s);
+    if (io.out_im) return mixed_pass_w<V>(make_in<V, false>(io.in, nullptr), make_out<V, true>(io.out, io.out_im),
+                                          batch, a, ms, tw, bt, scale, s);
+    return mixed_pass_w<V>(make_in<V, false>(io.in, nullptr), make_out<V, false>(io.out, nullptr), batch, a, ms, tw,
+                           bt, scale, s);
+}
+
+int mixed_pass_threads(const MixedSchedule& ms, int r)
+{
+    int tr = 1;
+    for (int q = 0; q < ms.nst; ++q)
+        while ((int64_t)tr * mixed_bmax_of(ms.radix[q]) < r / ms.radix[q]) tr *= 2;
+    return tr;
+}
+
+int mixed_pass_lines(int prec) { return prec == 0 ? mp_lines<float2>() : mp_lines<double2>(); }
+
+hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedule& ms, const void* in, void* out,
+                             int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t s,
+                             const void* in_im, void* out_im)
+{
+    if (in_im && out_im) return hipErrorInvalidValue;  // planar only at the first or the last pass
+    if (a.r > 512 || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr * mixed_pass_lines(prec) > 1024 ||
+        a.ns < 1 || (int64_t)a.stride * a.r != a.n || a.tiles * (int64_t)mixed_pass_lines(prec) < a.stride ||
+        a.rmagic != (unsigned)(((uint64_t(1) << 32) + a.r - 1) / a.r))
+        return hipErrorInvalidValue;
+    const Io io{in, in_im, out, out_im};
+    return prec == 0 ? mixed_pass_v<float2>(io, batch, a, ms, tw, big, scale, s)
+                     : mixed_pass_v<double2>(io, batch, a, ms, tw, big, scale, s);
+}
 
 }  // namespace fftmi

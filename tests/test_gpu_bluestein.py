@@ -28,9 +28,9 @@ def _m(n):
     return m
 
 
-# lengths with a prime factor above 13, or beyond the mixed-radix range
+# lengths with a prime factor above 13
 @pytest.mark.parametrize("n,batch", [(17, 4), (19, 1), (34, 3), (97, 2), (1009, 2), (4093, 2), (4097, 1),
-                                     (10007, 1), (3 * 4096, 2)])
+                                     (10007, 1), (17 * 1024, 2)])
 @pytest.mark.parametrize("dtype", [np.complex64, np.complex128])
 def test_bluestein_small_full(dev, n, batch, dtype):
     print("case n=%d batch=%d %s" % (n, batch, dtype.__name__), flush=True)
@@ -45,7 +45,7 @@ def test_bluestein_small_full(dev, n, batch, dtype):
         assert rel_rms_rows(y, ref).max() <= tol, (inverse, rel_rms_rows(y, ref).max())
 
 
-@pytest.mark.parametrize("n", [100003, (1 << 20) + 1, 3 << 18])
+@pytest.mark.parametrize("n", [100003, (1 << 20) + 1, 17 << 16])
 def test_bluestein_large_sampled(dev, n):
     print("case n=%d" % n, flush=True)
     x_np = wl.batched_normal(n, 1, seed=n % 1000)

@@ -80,9 +80,10 @@ def test_mixed_closed_forms_and_in_place(dev):
 
 
 def test_mixed_range_limits(dev):
-    # beyond one workgroup's LDS, or a prime factor above 13: Bluestein
-    assert "bluestein" in fm.Plan(3 * 4096, torch.complex64).describe()
-    assert "bluestein" in fm.Plan(3 * 2048, torch.complex128).describe()
+    # beyond one workgroup's LDS: super-stage passes; a prime factor above
+    # 13: Bluestein
+    assert "mixpass" in fm.Plan(3 * 4096, torch.complex64).describe()
+    assert "mixpass" in fm.Plan(3 * 2048, torch.complex128).describe()
     assert "bluestein" in fm.Plan(17 * 64, torch.complex64).describe()
     assert "mixed" in fm.Plan(11 * 13 * 32, torch.complex64).describe()
     assert "mixed" in fm.Plan(3 * 2048, torch.complex64).describe()
@@ -130,3 +131,57 @@ def test_mixed_every_smooth_length(dev, dtype, limit):
             if not err <= tol:
                 bad.append((n, inverse, float(err)))
     assert not bad, bad
+
+
+# Beyond one kernel: 2-3 mixed-radix super-stage passes (radix <= 512 each).
+MIXPASS = [(9000, torch.complex64, 3), (10000, torch.complex64, 2), (12288, torch.complex64, 2),
+           (30030, torch.complex64, 2), (3 * 65536, torch.complex64, 1), (10 ** 6, torch.complex64, 1),
+           (3 << 20, torch.complex64, 1), (6000, torch.complex128, 3), (10000, torch.complex128, 2),
+           (5 ** 9, torch.complex128, 1), (8 * 10 ** 6, torch.complex64, 1)]
+
+
+@pytest.mark.parametrize("n,dtype,batch", MIXPASS)
+def test_mixpass(dev, n, dtype, batch):
+    """Forward and inverse against the direct DFT (every bin up to 20000
+    points, 64 bins beyond, relative to the spectrum's RMS), the round trip,
+    and in place equal to out of place."""
+    print("case n=%d %s batch=%d" % (n, dtype, batch), flush=True)
+    npdt = np.complex64 if dtype == torch.complex64 else np.complex128
+    plan = fm.Plan(n, dtype)
+    assert "path=mixpass" in plan.describe()
+    x_np = wl.batched_normal(n, batch, seed=n % 1009, dtype=npdt)
+    x = torch.from_numpy(x_np).to(dev)
+    tol = fft_tol(n, dtype == torch.complex128)
+    oracle.set_threads(8)
+    ks = None if n <= 20000 else np.unique(np.concatenate(
+        [[0, 1, n // 2, n - 1], np.random.default_rng(n).integers(0, n, 60)]))
+    for inverse in (False, True):
+        y = (plan.ifft(x) if inverse else plan.fft(x)).cpu().numpy()
+        if ks is None:
+            err = rel_rms_rows(y, oracle.dft(x_np, inverse=inverse)).max()
+        else:
+            ref = oracle.dft_sample(x_np, ks, inverse=inverse)
+            err = (np.sqrt(np.mean(np.abs(y[:, ks] - ref) ** 2, axis=1)) /
+                   np.sqrt(np.mean(np.abs(y) ** 2, axis=1))).max()
+        assert err <= tol, (inverse, err)
+    back = plan.ifft(plan.fft(x)).cpu().numpy()
+    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+    z = x.clone()
+    plan.fft(z, out=z)
+    ref = plan.fft(x)
+    torch.cuda.synchronize()
+    assert torch.equal(z, ref)
+
+
+def test_mixpass_needs_workspace_and_rejects_poly_mul(dev):
+    n, batch = 10000, 2
+    plan = fm.Plan(n, torch.complex64)
+    assert fm.fft_workspace_size(plan.handle, batch) == batch * n * 8
+    x = torch.zeros(batch, n, dtype=torch.complex64, device=dev)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, torch.empty_like(x), batch, None)
+    assert e.value.status == fm.FFT_ERR_WORKSPACE
+    p64 = fm.Plan(n, torch.complex128)
+    with pytest.raises(fm.FFTError) as e:
+        fm.fft_poly_mul_workspace_size(p64.handle, 1)
+    assert e.value.status == fm.FFT_ERR_NOT_POW2

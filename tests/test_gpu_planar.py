@@ -32,6 +32,9 @@ CASES = [
     ((1 << 19,), torch.complex128, 1),     # three passes, fp64
     ((1009,), torch.complex64, 3),         # Bluestein
     ((1001,), torch.complex64, 3),         # mixed radix with 11 and 13
+    ((10000,), torch.complex64, 2),        # mixed-radix passes (two)
+    ((10 ** 6,), torch.complex64, 1),      # mixed-radix passes (three)
+    ((6000,), torch.complex128, 2),
     ((4097,), torch.complex128, 2),
     ((60,), torch.complex64, 7),           # mixed radix
     ((2401,), torch.complex128, 2),

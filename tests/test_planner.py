@@ -59,6 +59,15 @@ def test_every_length_up_to_20000(prec):
             r = [int(x) for x in _field(d, "radices").split("x")]
             assert math.prod(r) == n and set(r) <= {2, 3, 4, 5, 7, 8, 9, 11, 13}, (n, d)
             assert len(r) <= 16
+        elif _smooth(n):
+            # beyond one kernel: two super-stage passes of radix <= 512 (three
+            # only past 512^2), as even as possible, larger first
+            assert "path=mixpass" in d, (n, d)
+            r = [int(x) for x in _field(d, "radices").split("x")]
+            assert math.prod(r) == n and max(r) <= 512 and len(r) == 2, (n, d)
+            assert r == sorted(r, reverse=True), (n, d)
+            best = max(min(a, n // a) for a in range(2, 513) if n % a == 0 and n // a <= 512)
+            assert r[1] == best, (n, d)
         else:
             assert "path=bluestein" in d, (n, d)
             m = int(_field(d, "m"))
@@ -113,3 +122,18 @@ def test_query_rejects_as_create_does(rank, dims, prec, status):
     with pytest.raises(fm.FFTError) as e:
         _q(rank, dims, prec)
     assert e.value.status == status
+
+
+def test_mixpass_splits():
+    """Large 13-smooth lengths: the fewest passes of radix <= 512, the most even
+    split (largest smallest radix), larger radices first."""
+    cases = {10 ** 6: [100, 100, 100], 3 << 20: [192, 128, 128], 5 ** 9: [125, 125, 125],
+             12288: [128, 96], 30030: [182, 165], 3 * 65536: [512, 384], 7 << 20: [448, 128, 128]}
+    for n, want in cases.items():
+        for prec in (0, 1):
+            d = _q(1, [n], prec)
+            assert "path=mixpass" in d and _field(d, "radices") == "x".join(map(str, want)), (n, d)
+    # between the one-kernel limits of the two precisions: complex128 only
+    assert "path=mixpass" in _q(1, [6000], 1) and "path=mixed" in _q(1, [6000], 0)
+    # a prime factor above 13, or beyond 2^23: Bluestein or rejected
+    assert "path=bluestein" in _q(1, [1000003], 0)
