@@ -463,8 +463,15 @@ template <typename V> struct AnyTw {
 
 template <typename V> constexpr int mp_lines() { return 128 / (int)sizeof(V); }
 
+// Elements of a line per thread at most: the sub-schedule gives a line R / tr
+// <= 14 elements per thread (tr covers every stage at <= ceil(8/r) butterflies
+// of radix r); the block store needs as many per thread too (LINES R over a
+// workgroup of LINES tr threads).  They are moved MP_CHUNK at a time.
+constexpr int MP_QMAX = 16;
+constexpr int MP_CHUNK = 8;
+
 template <typename V, bool WIDE, int RCAP, typename IN, typename OUT>
-__global__ __launch_bounds__(1024) void mixed_pass_kernel(IN in, OUT out, MixedPassArgs a, MixedSchedule ms,
+__global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, OUT out, MixedPassArgs a, MixedSchedule ms,
                                                           const V* __restrict__ tw, AnyTw<V> big,
                                                           typename real_of<V>::type scale)
 {
@@ -478,14 +485,43 @@ __global__ __launch_bounds__(1024) void mixed_pass_kernel(IN in, OUT out, MixedP
     const bool live = j < a.stride;
     const int g = j / a.ns, k = j - g * a.ns;
     const int64_t sbase = sig * (int64_t)a.n;
-    for (int q = tl; q < a.r; q += a.tr) {
-        V x{0, 0};
-        if (live) {
-            x = in.ld(sbase + j + (int64_t)q * a.stride);
-            if (a.conj_in) x = cconj(x);
-            if (a.ns > 1) x = cmul(x, big(q * k));
+    // element q = tl + i tr of line c, i < nq <= MP_QMAX, in chunks of
+    // MP_CHUNK: the chunk's loads and table reads are all issued before the
+    // first is used
+    // Twiddle of element q = tl + (i0 + i) tr: w^{k (tl + i0 tr)} (one table
+    // read per chunk) times w^{k tr 2^b} over the set bits b of i (read once
+    // per thread; tr 2^b < R keeps every exponent below Ns R).  At most
+    // LC + 1 rounded factors per twiddle, and far fewer table reads than
+    // one lookup per element.
+    const int nq = (a.r - tl + a.tr - 1) / a.tr;
+    static_assert(MP_CHUNK == 4 || MP_CHUNK == 8, "chunk of 2^LC elements");
+    constexpr int LC = MP_CHUNK == 4 ? 2 : 3;
+    V gstep[LC];
+    if (a.ns > 1 && live) {
+#pragma unroll
+        for (int b = 0; b < LC; ++b) gstep[b] = big((a.tr << b) * k);
+    }
+    for (int i0 = 0; i0 < nq; i0 += MP_CHUNK) {
+        V x[MP_CHUNK];
+#pragma unroll
+        for (int i = 0; i < MP_CHUNK; ++i) {
+            x[i] = V{0, 0};
+            if (i0 + i < nq && live) x[i] = in.ld(sbase + j + (int64_t)(tl + (i0 + i) * a.tr) * a.stride);
         }
-        lds[q * P + c] = x;
+        if (a.ns > 1 && live) {
+            const V wc = big((tl + i0 * a.tr) * k);
+#pragma unroll
+            for (int i = 0; i < MP_CHUNK; ++i) {
+                V w = wc;
+#pragma unroll
+                for (int b = 0; b < LC; ++b)
+                    if (i & (1 << b)) w = cmul(w, gstep[b]);
+                if (i0 + i < nq) x[i] = cmul(x[i], w);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MP_CHUNK; ++i)
+            if (i0 + i < nq) lds[(tl + (i0 + i) * a.tr) * P + c] = a.conj_in ? cconj(x[i]) : x[i];
     }
     __syncthreads();
     const MixedRows<V, false> none{};
@@ -495,19 +531,38 @@ __global__ __launch_bounds__(1024) void mixed_pass_kernel(IN in, OUT out, MixedP
         mixed_stage_any<WIDE, false, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
                                                              ms.magic[s], tw + ms.twoff[s], none);
     if (a.ns == 1) {
+        // the tile's outputs are one block: element e = tid + i blockDim
         const int lines = a.stride - j0 < LINES ? a.stride - j0 : LINES;
         const int count = lines * a.r;
         const int64_t obase = sbase + (int64_t)j0 * a.r;
-        for (int e = threadIdx.x; e < count; e += blockDim.x) {
-            const int cl = (int)__umulhi((unsigned)e, a.rmagic);
-            const V y = lds[(e - cl * a.r) * P + cl];
-            out.st(obase + e, a.conj_out ? V{y.x * scale, -y.y * scale} : y);
+        for (int e0 = threadIdx.x; e0 < count; e0 += MP_CHUNK * blockDim.x) {
+            V y[MP_CHUNK];
+#pragma unroll
+            for (int i = 0; i < MP_CHUNK; ++i) {
+                const int e = e0 + i * blockDim.x;
+                if (e < count) {
+                    const int cl = (int)__umulhi((unsigned)e, a.rmagic);
+                    y[i] = lds[(e - cl * a.r) * P + cl];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MP_CHUNK; ++i) {
+                const int e = e0 + i * blockDim.x;
+                if (e < count) out.st(obase + e, a.conj_out ? V{y[i].x * scale, -y[i].y * scale} : y[i]);
+            }
         }
     } else if (live) {
         const int64_t obase = sbase + (int64_t)g * a.ns * a.r + k;
-        for (int q = tl; q < a.r; q += a.tr) {
-            const V y = lds[q * P + c];
-            out.st(obase + (int64_t)q * a.ns, a.conj_out ? V{y.x * scale, -y.y * scale} : y);
+        for (int i0 = 0; i0 < nq; i0 += MP_CHUNK) {
+            V y[MP_CHUNK];
+#pragma unroll
+            for (int i = 0; i < MP_CHUNK; ++i)
+                if (i0 + i < nq) y[i] = lds[(tl + (i0 + i) * a.tr) * P + c];
+#pragma unroll
+            for (int i = 0; i < MP_CHUNK; ++i)
+                if (i0 + i < nq)
+                    out.st(obase + (int64_t)(tl + (i0 + i) * a.tr) * a.ns,
+                           a.conj_out ? V{y[i].x * scale, -y[i].y * scale} : y[i]);
         }
     }
 }
@@ -568,7 +623,8 @@ hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedu
                              const void* in_im, void* out_im)
 {
     if (in_im && out_im) return hipErrorInvalidValue;  // planar only at the first or the last pass
-    if (a.r > 512 || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr * mixed_pass_lines(prec) > 1024 ||
+    if (a.r > 512 || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr > 64 ||
+        (a.r + a.tr - 1) / a.tr > MP_QMAX ||
         a.ns < 1 || (int64_t)a.stride * a.r != a.n || a.tiles * (int64_t)mixed_pass_lines(prec) < a.stride ||
         a.rmagic != (unsigned)(((uint64_t(1) << 32) + a.r - 1) / a.r))
         return hipErrorInvalidValue;
