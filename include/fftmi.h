@@ -91,6 +91,10 @@ enum fft_status {
  *           - N = 2^a 3^b 5^c 7^d 11^e 13^f up to 8192 (C32) / 4096 (C64):
  *             mixed-radix Stockham stages (radices 8, 4, 2, 9, 3, 5, 7, 11,
  *             13) in one kernel, no workspace;
+ *           - such N beyond that: N = R0 R1 (R2), each R <= 512, as two or
+ *             three super-stage passes whose R-point transforms run those
+ *             mixed-radix stages; a workspace of one batch of signals, like
+ *             the power-of-two passes (fft_plan_describe: path=mixpass);
  *           - any other N: chirp-z (Bluestein), X_k = c_k (x.c * conj c)_k
  *             with c_j = e^{-i pi j^2/N}, the convolution done cyclically at
  *             the power-of-two M >= 2N - 1 by the library's own transforms.
