@@ -25,8 +25,9 @@ Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
 transform the same way, and the R2C transform of 16384 real rows of 8192
 points (value = batch * 2.5 N log2 N / t, half the complex count), and rows
-of 1000 (mixed radix) and 1009 (Bluestein) points, and the 2D R2C transform
-of eight real 2048 x 2048 images.
+of 1000 (mixed radix) and 1009 (Bluestein) points, the 2D R2C transform of
+eight real 2048 x 2048 images, and 64 rows of 10^6 points (mixed-radix
+super-stage passes, 100 x 100 x 100).
 """
 from __future__ import annotations
 
@@ -45,7 +46,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
              "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384", "c2c_n1000_b65536",
-             "c2c_n1009_b65536", "r2c2d_2048x2048_b8")
+             "c2c_n1009_b65536", "r2c2d_2048x2048_b8", "c2c_n1000000_b64")
 
 
 # The sources each single-kernel workload's kernel is built from: a stored
@@ -115,10 +116,15 @@ def setup_workload(name, dev, fm, torch, sets=1):
             x, y, ws = bufs[k % sets]
             fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, y, batch, ws, stream)
         desc = plan.describe()
-        kernels = len(desc.split("radices=")[1].split("x")) if "path=multipass" in desc else \
-            (5 if "passes" in desc else 1)
+        kernels = len(desc.split("radices=")[1].split("x")) if ("path=multipass" in desc or "path=mixpass" in desc) \
+            else (5 if "passes" in desc else 1)
+        # the oracle's route for the length: the radix-2 FFT, the direct DFT,
+        # or (rows too long for an O(N^2) pass in the time budget) a bounded
+        # set of bins of the direct DFT, scaled to whole rows
+        pow2 = n & (n - 1) == 0
         info = dict(n=n, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=2 * x0.numel() * 8,
                     plan=desc, kernels=kernels, sample_rows=lambda rows: x_np[:rows],
+                    oracle_fn="fft" if pow2 else ("dft" if n <= 16384 else "dft_bins"),
                     oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))
         return step, info
     if name.startswith("c2c2d") or name.startswith("c2c3d"):
@@ -236,6 +242,20 @@ def cpu_baseline(name, info, budget_s):
             reps += 1
         units = imgs * reps
         sample = "first %d of %d images, transformed %d time(s)" % (imgs, info["batch"], reps)
+    elif info.get("oracle_fn") == "dft_bins":
+        # One row of N points: bins 0, 1, ... of its direct DFT (O(N) each),
+        # as many as fit the budget, scaled to whole rows (N bins a row).
+        n = info["n"]
+        x = info["sample_rows"](1)
+        t0 = time.perf_counter()
+        oracle.dft_sample(x, np.arange(16))
+        per_bin = (time.perf_counter() - t0) / 16
+        bins = int(max(16, min(n, budget_s / max(per_bin, 1e-12))))
+        t0 = time.perf_counter()
+        oracle.dft_sample(x, np.arange(bins))
+        dt = time.perf_counter() - t0
+        units = bins / n
+        sample = "bins 0..%d of row 0 (direct DFT, %d of %d bins), scaled to whole rows" % (bins - 1, bins, n)
     else:
         # The first rows of the batch, as many as fit the budget; if the whole
         # batch takes less, it is transformed repeatedly until the budget is used.

@@ -24,6 +24,8 @@ stated):
 * rows of 1000 and 1009 points x 65536, ``batched_normal`` (seeds 8, 9): the
   mixed-radix and Bluestein paths.
 * real 2048 x 2048 images x 8, ``real_normal`` (seed 10): the 2D R2C path.
+* rows of 10^6 points x 64, ``batched_normal`` (seed 11): the mixed-radix
+  super-stage passes.
 """
 from __future__ import annotations
 
@@ -46,6 +48,8 @@ WORKLOADS = {
     "c2c_n1009_b65536": dict(kind="normal", n=1009, batch=65536, seed=9),
     # real 2048 x 2048 images, the 2D R2C transform
     "r2c2d_2048x2048_b8": dict(kind="real_images", h=2048, w=2048, batch=8, seed=10),
+    # 10^6 = 100 x 100 x 100: three mixed-radix super-stage passes (~500 MiB in)
+    "c2c_n1000000_b64": dict(kind="normal", n=10 ** 6, batch=64, seed=11),
 }
 
 
