@@ -205,13 +205,33 @@ template <int R> constexpr int mixed_bmax() { return mixed_bmax_of(R); }
 // stage works in LDS.
 // The rows of one workgroup: input and output from its first element, the
 // offset of this thread's row in them, whether that row exists (the last
-// workgroup may have fewer), and the inverse's output scale.
-template <typename V, bool PL> struct MixedRows {
+// workgroup may have fewer), and the inverse's output scale.  load / store:
+// the R elements j + r stride of the row (conjugated for the inverse), and
+// the R outputs dst + r ns (conjugated and scaled for the inverse).
+template <typename V, bool PL, bool INV> struct MixedRows {
     CIn<V, PL> in;
     COut<V, PL> out;
     unsigned rbase;
     bool live;
     typename real_of<V>::type scale;
+    template <int R> __device__ __forceinline__ void load(int j, int stride, V (&u)[R]) const
+    {
+        if (!live) return;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const V x = in.ld32(rbase + (unsigned)(j + r * stride));
+            u[r] = INV ? cconj(x) : x;
+        }
+    }
+    template <int R> __device__ __forceinline__ void store(int dst, int ns, const V (&u)[R]) const
+    {
+        if (!live) return;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const V y = u[r];
+            out.st32(rbase + (unsigned)(dst + r * ns), INV ? V{y.x * scale, -y.y * scale} : y);
+        }
+    }
 };
 
 // One stage of radix R, thread tl of tr: for every butterfly j < N/R, inputs
@@ -219,12 +239,13 @@ template <typename V, bool PL> struct MixedRows {
 // in the first stage, Ns = 1), the R-point DFT, outputs at g Ns R + k + r Ns,
 // g = j / Ns.  A stage within LDS reads all its butterflies into registers
 // before a barrier across the workgroup and writes them back in place after
-// it.  INV: the first stage conjugates its inputs, the last conjugates and
-// scales its outputs.  ES: LDS slots between consecutive elements of a row
-// (1 for a row of its own; the tile width where rows are interleaved).
-template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, int ES = 1, typename V, bool PL>
+// it.  FROM_IN / TO_OUT: the stage reads its inputs through io.load, or
+// writes its outputs through io.store, instead of the LDS row.  ES: LDS slots
+// between consecutive elements of a row (1 for a row of its own; the tile
+// width where rows are interleaved).
+template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, int ES = 1, typename V, typename IO>
 __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, int ns, unsigned magic,
-                                            const V* __restrict__ tw, const MixedRows<V, PL>& io)
+                                            const V* __restrict__ tw, const IO& io)
 {
     constexpr int B = mixed_bmax<R>();
     constexpr int S = mixed_tw_slots(R);
@@ -238,13 +259,7 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
         dst[b] = -1;
         if (j < stride) {
             if constexpr (FROM_IN) {
-                if (io.live) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const V x = io.in.ld32(io.rbase + (unsigned)(j + r * stride));
-                        u[b][r] = INV ? cconj(x) : x;
-                    }
-                }
+                io.template load<R>(j, stride, u[b]);
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) u[b][r] = row[(j + r * stride) * ES];
@@ -269,18 +284,9 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
         }
     }
     if constexpr (TO_OUT) {
-        if (!io.live) return;
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            if (dst[b] >= 0) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const V y = u[b][r];
-                    io.out.st32(io.rbase + (unsigned)(dst[b] + r * ns),
-                                INV ? V{y.x * io.scale, -y.y * io.scale} : y);
-                }
-            }
-        }
+        for (int b = 0; b < B; ++b)
+            if (dst[b] >= 0) io.template store<R>(dst[b], ns, u[b]);
     } else {
         if constexpr (!FROM_IN) __syncthreads();  // every read of this stage is done before any write
 #pragma unroll
@@ -297,11 +303,11 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
 // WIDE: the schedule may hold radices 11 and 13, whose DFTs keep more values
 // live; kernels for the other schedules are compiled without them so that
 // they keep their lower register count.
-template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, bool INV, int ES = 1, typename V, bool PL>
+template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, int ES = 1, typename V, typename IO>
 __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, int stride, int ns, unsigned magic,
-                                                const V* __restrict__ tw, const MixedRows<V, PL>& io)
+                                                const V* __restrict__ tw, const IO& io)
 {
-#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, INV, ES>(row, tl, tr, stride, ns, magic, tw, io)
+#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, ES>(row, tl, tr, stride, ns, magic, tw, io)
     if constexpr (WIDE) {
         if (r == 11) {
             MX_STAGE(11);
@@ -344,19 +350,19 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
     const int rl = threadIdx.x / tr, tl = threadIdx.x % tr;
     const int64_t row0 = (int64_t)blockIdx.x * rpw;
     const int64_t base = row0 * n;
-    const MixedRows<V, PL> io{in.at(base), out.at(base), (unsigned)(rl * n), row0 + rl < nrows, scale};
+    const MixedRows<V, PL, INV> io{in.at(base), out.at(base), (unsigned)(rl * n), row0 + rl < nrows, scale};
     V* row = lds + rl * n;
     const int last = ms.nst - 1;
     if constexpr (DIRECT) {
         if (last == 0) {
-            mixed_stage_any<WIDE, true, true, true, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+            mixed_stage_any<WIDE, true, true, true>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
             return;
         }
-        mixed_stage_any<WIDE, true, true, false, INV>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+        mixed_stage_any<WIDE, true, true, false>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
         for (int s = 1; s < last; ++s)
-            mixed_stage_any<WIDE, false, false, false, INV>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s],
+            mixed_stage_any<WIDE, false, false, false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s], ms.magic[s],
                                                       tw + ms.twoff[s], io);
-        mixed_stage_any<WIDE, false, false, true, INV>(ms.radix[last], row, tl, tr, ms.stride[last], ms.ns[last],
+        mixed_stage_any<WIDE, false, false, true>(ms.radix[last], row, tl, tr, ms.stride[last], ms.ns[last],
                                                  ms.magic[last], tw + ms.twoff[last], io);
     } else {
         // rows past the end of the batch (last workgroup only) are computed
@@ -365,9 +371,9 @@ __global__ __launch_bounds__(mixed_max_threads<V>()) void mixed_rows_kernel(CIn<
         const int rows = (int)(nrows - row0 < rpw ? nrows - row0 : rpw);
         seg_load<INV>(in, base, rows * n, lds, threads);
         __syncthreads();
-        mixed_stage_any<WIDE, true, false, false, false>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
+        mixed_stage_any<WIDE, true, false, false>(ms.radix[0], row, tl, tr, ms.stride[0], 1, 0u, tw, io);
         for (int s = 1; s <= last; ++s)
-            mixed_stage_any<WIDE, false, false, false, false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s],
+            mixed_stage_any<WIDE, false, false, false>(ms.radix[s], row, tl, tr, ms.stride[s], ms.ns[s],
                                                         ms.magic[s], tw + ms.twoff[s], io);
         seg_store<INV>(out, base, rows * n, lds, threads, scale);
     }
@@ -441,12 +447,14 @@ int mixed_max_n(int prec) { return prec == 0 ? mixed_max_points<float2>() : mixe
 // R-point DFT (the mixed-radix stages above, on a line of the tile), outputs at
 // g Ns R + k + q Ns (g = j / Ns).
 //
-// A workgroup takes LINES consecutive butterflies (a 128-byte segment of
-// elements for each q) into LDS, element q of line c at q (LINES + 1) + c (the
-// extra slot per element row keeps both store orders free of bank
-// conflicts).  The first pass (Ns = 1) writes each line's outputs j R + q, so
-// the tile's lines together are one contiguous block; later passes write, for
-// each q, the lines' outputs side by side.
+// A workgroup takes LINES consecutive butterflies j (a 128-byte segment of
+// elements for each q); element q of line c lives in LDS at q (LINES + 1) + c
+// (the extra slot per element row keeps both store orders free of bank
+// conflicts).  The first stage of the R-point transform reads its inputs from
+// HBM; the first pass (Ns = 1) writes each line's outputs j R + q, so the
+// tile's lines together are one contiguous block, stored from LDS; later
+// passes write the last stage's outputs straight to HBM (for each q, the
+// lines' outputs side by side).
 // ---------------------------------------------------------------------------
 
 // w_M^m for any M (m < M < 2^31) from two tables: hi[q] = w_M^{q 2^lbits},
@@ -461,12 +469,59 @@ template <typename V> struct AnyTw {
     }
 };
 
+// The global side of a pass's line: input element q at ibase + q istride,
+// times w^{q k} when twiddled (conjugated first for the inverse's first
+// pass); output element q at obase + q ostride (conjugated and scaled for the
+// inverse's last pass).  load: the R elements j + r stride of a butterfly,
+// the twiddles as w^{k j} times powers of w^{k stride} (R - 1 products,
+// exponents below Ns R).
+template <typename V, typename IN, typename OUT> struct PassIO {
+    IN in;
+    OUT out;
+    int64_t ibase;
+    int istride;
+    int64_t obase;
+    int ostride;
+    AnyTw<V> big;
+    int k;
+    bool twiddle, conj_in, conj_out, live;
+    typename real_of<V>::type scale;
+    template <int R> __device__ __forceinline__ void load(int j, int stride, V (&u)[R]) const
+    {
+        if (!live) return;
+        V w{1, 0}, step{1, 0};
+        if (twiddle) {
+            w = big(k * j);
+            step = big(k * stride);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            V x = in.ld(ibase + (int64_t)(j + r * stride) * istride);
+            if (conj_in) x = cconj(x);
+            if (twiddle) {
+                x = cmul(x, w);
+                if (r + 1 < R) w = cmul(w, step);
+            }
+            u[r] = x;
+        }
+    }
+    template <int R> __device__ __forceinline__ void store(int dst, int ns, const V (&u)[R]) const
+    {
+        if (!live) return;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const V y = u[r];
+            out.st(obase + (int64_t)(dst + r * ns) * ostride, conj_out ? V{y.x * scale, -y.y * scale} : y);
+        }
+    }
+};
+
 template <typename V> constexpr int mp_lines() { return 128 / (int)sizeof(V); }
 
 // Elements of a line per thread at most: the sub-schedule gives a line R / tr
 // <= 14 elements per thread (tr covers every stage at <= ceil(8/r) butterflies
-// of radix r); the block store needs as many per thread too (LINES R over a
-// workgroup of LINES tr threads).  They are moved MP_CHUNK at a time.
+// of radix r); the block store of the first pass moves as many per thread
+// (LINES R over a workgroup of LINES tr threads), MP_CHUNK at a time.
 constexpr int MP_QMAX = 16;
 constexpr int MP_CHUNK = 8;
 
@@ -485,84 +540,50 @@ __global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, O
     const bool live = j < a.stride;
     const int g = j / a.ns, k = j - g * a.ns;
     const int64_t sbase = sig * (int64_t)a.n;
-    // element q = tl + i tr of line c, i < nq <= MP_QMAX, in chunks of
-    // MP_CHUNK: the chunk's loads and table reads are all issued before the
-    // first is used
-    // Twiddle of element q = tl + (i0 + i) tr: w^{k (tl + i0 tr)} (one table
-    // read per chunk) times w^{k tr 2^b} over the set bits b of i (read once
-    // per thread; tr 2^b < R keeps every exponent below Ns R).  At most
-    // LC + 1 rounded factors per twiddle, and far fewer table reads than
-    // one lookup per element.
-    const int nq = (a.r - tl + a.tr - 1) / a.tr;
-    static_assert(MP_CHUNK == 4 || MP_CHUNK == 8, "chunk of 2^LC elements");
-    constexpr int LC = MP_CHUNK == 4 ? 2 : 3;
-    V gstep[LC];
-    if (a.ns > 1 && live) {
-#pragma unroll
-        for (int b = 0; b < LC; ++b) gstep[b] = big((a.tr << b) * k);
+    // The first stage of the line's transform reads its butterflies straight
+    // from the input (element q of line j at j + q N/R, times w^{q k}); for
+    // Ns > 1 the last writes straight to the output (element q at
+    // g Ns R + k + q Ns); the stages between go through LDS.
+    const PassIO<V, IN, OUT> io{in, out, sbase + j, a.stride, sbase + (int64_t)g * a.ns * a.r + k, a.ns, big, k,
+                                a.ns > 1, a.conj_in != 0, a.conj_out != 0, live, scale};
+    V* row = lds + c;
+    const int last = ms.nst - 1;
+    if (a.ns > 1) {
+        if (last == 0) {
+            mixed_stage_any<WIDE, true, true, true, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+            return;
+        }
+        mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+        for (int s = 1; s < last; ++s)
+            mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
+                                                          ms.magic[s], tw + ms.twoff[s], io);
+        mixed_stage_any<WIDE, false, false, true, P>(ms.radix[last], row, tl, a.tr, ms.stride[last], ms.ns[last],
+                                                     ms.magic[last], tw + ms.twoff[last], io);
+        return;
     }
-    for (int i0 = 0; i0 < nq; i0 += MP_CHUNK) {
-        V x[MP_CHUNK];
+    mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+    for (int s = 1; s <= last; ++s)
+        mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s], ms.magic[s],
+                                                      tw + ms.twoff[s], io);
+    // Ns = 1: line j's outputs are j R + q, so the tile's lines are one
+    // contiguous block: element e = tid + i blockDim of it, in chunks
+    const int lines = a.stride - j0 < LINES ? a.stride - j0 : LINES;
+    const int count = lines * a.r;
+    const int64_t obase = sbase + (int64_t)j0 * a.r;
+    for (int e0 = threadIdx.x; e0 < count; e0 += MP_CHUNK * blockDim.x) {
+        V y[MP_CHUNK];
 #pragma unroll
         for (int i = 0; i < MP_CHUNK; ++i) {
-            x[i] = V{0, 0};
-            if (i0 + i < nq && live) x[i] = in.ld(sbase + j + (int64_t)(tl + (i0 + i) * a.tr) * a.stride);
-        }
-        if (a.ns > 1 && live) {
-            const V wc = big((tl + i0 * a.tr) * k);
-#pragma unroll
-            for (int i = 0; i < MP_CHUNK; ++i) {
-                V w = wc;
-#pragma unroll
-                for (int b = 0; b < LC; ++b)
-                    if (i & (1 << b)) w = cmul(w, gstep[b]);
-                if (i0 + i < nq) x[i] = cmul(x[i], w);
+            const int e = e0 + i * blockDim.x;
+            if (e < count) {
+                const int cl = (int)__umulhi((unsigned)e, a.rmagic);
+                y[i] = lds[(e - cl * a.r) * P + cl];
             }
         }
 #pragma unroll
-        for (int i = 0; i < MP_CHUNK; ++i)
-            if (i0 + i < nq) lds[(tl + (i0 + i) * a.tr) * P + c] = a.conj_in ? cconj(x[i]) : x[i];
-    }
-    __syncthreads();
-    const MixedRows<V, false> none{};
-    V* row = lds + c;
-    mixed_stage_any<WIDE, true, false, false, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, none);
-    for (int s = 1; s < ms.nst; ++s)
-        mixed_stage_any<WIDE, false, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
-                                                             ms.magic[s], tw + ms.twoff[s], none);
-    if (a.ns == 1) {
-        // the tile's outputs are one block: element e = tid + i blockDim
-        const int lines = a.stride - j0 < LINES ? a.stride - j0 : LINES;
-        const int count = lines * a.r;
-        const int64_t obase = sbase + (int64_t)j0 * a.r;
-        for (int e0 = threadIdx.x; e0 < count; e0 += MP_CHUNK * blockDim.x) {
-            V y[MP_CHUNK];
-#pragma unroll
-            for (int i = 0; i < MP_CHUNK; ++i) {
-                const int e = e0 + i * blockDim.x;
-                if (e < count) {
-                    const int cl = (int)__umulhi((unsigned)e, a.rmagic);
-                    y[i] = lds[(e - cl * a.r) * P + cl];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < MP_CHUNK; ++i) {
-                const int e = e0 + i * blockDim.x;
-                if (e < count) out.st(obase + e, a.conj_out ? V{y[i].x * scale, -y[i].y * scale} : y[i]);
-            }
-        }
-    } else if (live) {
-        const int64_t obase = sbase + (int64_t)g * a.ns * a.r + k;
-        for (int i0 = 0; i0 < nq; i0 += MP_CHUNK) {
-            V y[MP_CHUNK];
-#pragma unroll
-            for (int i = 0; i < MP_CHUNK; ++i)
-                if (i0 + i < nq) y[i] = lds[(tl + (i0 + i) * a.tr) * P + c];
-#pragma unroll
-            for (int i = 0; i < MP_CHUNK; ++i)
-                if (i0 + i < nq)
-                    out.st(obase + (int64_t)(tl + (i0 + i) * a.tr) * a.ns,
-                           a.conj_out ? V{y[i].x * scale, -y[i].y * scale} : y[i]);
+        for (int i = 0; i < MP_CHUNK; ++i) {
+            const int e = e0 + i * blockDim.x;
+            if (e < count) out.st(obase + e, a.conj_out ? V{y[i].x * scale, -y[i].y * scale} : y[i]);
         }
     }
 }
