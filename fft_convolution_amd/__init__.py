@@ -307,9 +307,10 @@ class Plan:
         else:
             self._check_tensor(out)
         ws_bytes = fft_workspace_size(self.handle, batch)
-        # A rank-2/3 plan uses its workspace only for an in-place call, unless
-        # its column stage runs as a pass of its own ("split" plans).
-        if self.rank >= 2 and out.data_ptr() != x.data_ptr() and "split=" not in self.describe():
+        # A power-of-two rank-2/3 plan uses its workspace only for an in-place
+        # call, unless its column stage runs as a pass of its own ("split").
+        desc = self.describe()
+        if self.rank >= 2 and out.data_ptr() != x.data_ptr() and "path=nd " in desc and "split=" not in desc:
             ws_bytes = 0
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
         fn(self.handle, direction, x, out, batch, ws)

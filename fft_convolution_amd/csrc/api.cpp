@@ -248,7 +248,8 @@ enum PlanPath {
     PATH_BLUESTEIN = 4,
     PATH_REAL = 5,
     PATH_MIXED = 6,
-    PATH_MIXPASS = 7
+    PATH_MIXPASS = 7,
+    PATH_NDX = 8
 };
 
 // One super-stage pass of a multi-pass plan.
@@ -308,8 +309,16 @@ struct fft_plan {
     void* bspec = nullptr;
     fft_plan* inner = nullptr;
     int npass = 0;
-    PassPlan passes[4];
-    void* pass_tw[4] = {nullptr, nullptr, nullptr, nullptr};
+    PassPlan passes[8];
+    void* pass_tw[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    // rank 2 / 3 with a dimension that is not a power of two: inner = the
+    // rank-1 plan of the innermost axis (any length); then the other axes
+    // longer than 1, inner to outer (nx_k of them): axis a of length nx_len[a]
+    // and stride nx_stride[a] runs nx_np[a] super-stage passes,
+    // passes[3a .. 3a + nx_np[a]) (span = stride x the axis's own span).
+    int nx_k = 0;
+    int64_t nx_len[2] = {1, 1}, nx_stride[2] = {1, 1};
+    int nx_np[2] = {0, 0};
     size_t elem = 8;
 };
 
@@ -354,7 +363,7 @@ void free_plan(fft_plan* p)
     void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo, p->chirp, p->bspec, p->col_hi, p->col_lo};
     for (void* q : ptrs)
         if (q) hipFree(q);
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
         if (p->pass_tw[i]) hipFree(p->pass_tw[i]);
         if (p->passes[i].big_hi) hipFree(p->passes[i].big_hi);
         if (p->passes[i].big_lo) hipFree(p->passes[i].big_lo);
@@ -445,8 +454,29 @@ int check_device(const fft_plan* plan)
 
 // Workspace of an exec call: the multi-pass transform ping-pongs through one
 // signal-sized buffer; the folded 2D transform needs one only in place.
+size_t c2c_workspace(const fft_plan* p, int64_t batch);
+size_t planar_ws(const fft_plan* p, int64_t batch);
+
+// Rank 2 / 3, some dimension not a power of two: buffers for the axis passes
+// (one signal-sized buffer when an axis takes two or more passes; planar
+// calls a second one when it takes three), then the rows' own workspace.
+size_t ndx_axis_buffers(const fft_plan* p, bool planar)
+{
+    int most = 0;
+    for (int a = 0; a < p->nx_k; ++a) most = std::max(most, p->nx_np[a]);
+    return most >= 3 && planar ? 2 : most >= 2 ? 1 : 0;
+}
+size_t ndx_workspace(const fft_plan* p, int64_t batch, bool planar)
+{
+    const size_t sig = (size_t)batch * (size_t)p->n * p->elem;
+    const int64_t rows = batch * (p->n / p->dims[p->rank - 1]);
+    const size_t rws = p->dims[p->rank - 1] == 1 ? 0 : planar ? planar_ws(p->inner, rows) : c2c_workspace(p->inner, rows);
+    return ndx_axis_buffers(p, planar) * sig + rws;
+}
+
 size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
+    if (p->path == PATH_NDX) return ndx_workspace(p, batch, false);
     if (p->path == PATH_BLUESTEIN)  // none when M is within one workgroup (one kernel)
         return (int64_t(1) << p->logm) <= max_lds_n(p->prec)
                    ? 0
@@ -477,9 +507,47 @@ constexpr int64_t kBluesteinMax = FFT_MAX_BLUESTEIN_N;  // largest length that i
 int col_pref_log(int) { return 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
 
+// Rank 2 / 3 with a dimension that is not a power of two: the innermost axis
+// as rank-1 rows, every other axis longer than 1 as super-stage passes over
+// signals of (its length x its stride) points.
+int ndx_layout(fft_plan* p, int rank, const int64_t* dims)
+{
+    p->path = PATH_NDX;
+    p->nx_k = 0;
+    int64_t stride = dims[rank - 1];
+    for (int d = rank - 2; d >= 0; --d) {
+        const int64_t len = dims[d];
+        if (len > 1) {
+            const int a = p->nx_k++;
+            p->nx_len[a] = len;
+            p->nx_stride[a] = stride;
+            int rs[3] = {(int)len, 0, 0};
+            const int np = len <= kMixPassMax ? 1 : mixed_split(len, rs);
+            if (np == 0) return fail(FFT_ERR_UNSUPPORTED_SIZE, "no passes for an axis of %lld points", (long long)len);
+            p->nx_np[a] = np;
+            int64_t ns = 1;
+            for (int q = 0; q < np; ++q) {
+                PassPlan& pp = p->passes[3 * a + q];
+                pp.r = rs[q];
+                pp.ns = (int)(ns * stride);
+                if (!mixed_factor(pp.r, &pp.ms))
+                    return fail(FFT_ERR_UNSUPPORTED_SIZE, "no schedule for radix %d", pp.r);
+                ns *= rs[q];
+            }
+        }
+        stride *= len;
+    }
+    return FFT_OK;
+}
+
 // Chooses the kernel path and its sizes; host only.
 int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
 {
+    if (rank > 1) {
+        bool all_pow2 = true;
+        for (int d = 0; d < rank; ++d) all_pow2 = all_pow2 && is_pow2(dims[d]);
+        if (!all_pow2) return ndx_layout(p, rank, dims);
+    }
     if (rank == 1) {
         const int64_t n = dims[0];
         if (!is_pow2(n)) {
@@ -675,6 +743,22 @@ int upload_tables(fft_plan* p)
                     st = upload_big_any((int64_t)pp.ns * pp.r, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
             }
             break;
+        case PATH_NDX: {
+            // the rows' plan, then each axis pass's tables: w_M with M = the
+            // axis's own span x radix (the span over the stride)
+            const int64_t w = p->dims[p->rank - 1];
+            if (w > 1) st = fft_plan_create(&p->inner, 1, &w, prec);
+            for (int a = 0; a < p->nx_k && st == FFT_OK; ++a)
+                for (int q = 0; q < p->nx_np[a] && st == FFT_OK; ++q) {
+                    PassPlan& pp = p->passes[3 * a + q];
+                    st = upload(mixed_table(pp.ms), prec, &p->pass_tw[3 * a + q]);
+                    pp.tw = p->pass_tw[3 * a + q];
+                    if (st == FFT_OK && q > 0)
+                        st = upload_big_any(pp.ns / p->nx_stride[a] * pp.r, prec, &pp.big_hi, &pp.big_lo,
+                                            &pp.big_lbits);
+                }
+            break;
+        }
         case PATH_ROWS:
             st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
             break;
@@ -734,17 +818,44 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
     if (rank < 1 || rank > 3) return fail(FFT_ERR_INVALID_ARG, "rank %d not supported (1, 2 or 3)", rank);
     if (!dims) return fail(FFT_ERR_INVALID_ARG, "dims is NULL");
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
+    bool all_pow2 = true;
     for (int d = 0; d < rank; ++d) {
         if (dims[d] < 1) return fail(FFT_ERR_INVALID_ARG, "dims[%d] = %lld < 1", d, (long long)dims[d]);
+        all_pow2 = all_pow2 && is_pow2(dims[d]);
+    }
+    if (rank > 1 && !all_pow2) {
+        // the innermost axis: any length a rank-1 plan takes; the others:
+        // 2^a 3^b 5^c 7^d 11^e 13^f, as at most three passes of radix <= 512
+        int64_t total = 1;
+        for (int d = 0; d < rank; ++d) {
+            total *= dims[d];
+            if (total > max_n(prec))
+                return fail(FFT_ERR_UNSUPPORTED_SIZE, "%lld points per transform exceed %lld", (long long)total,
+                            (long long)max_n(prec));
+        }
+        const int64_t w = dims[rank - 1];
+        if (!is_pow2(w) && w > kBluesteinMax)
+            return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", rank - 1, (long long)w,
+                        (long long)kBluesteinMax);
+        for (int d = 0; d < rank - 1; ++d) {
+            if (dims[d] == 1) continue;
+            MixedSchedule ms;
+            int rs[3];
+            if (!mixed_factor(dims[d], &ms) || (dims[d] > kMixPassMax && mixed_split(dims[d], rs) == 0))
+                return fail(FFT_ERR_UNSUPPORTED_SIZE,
+                            "dims[%d] = %lld: axes other than the innermost take 2^a 3^b 5^c 7^d 11^e 13^f points",
+                            d, (long long)dims[d]);
+        }
+    }
+    for (int d = 0; d < rank; ++d) {
         if (!is_pow2(dims[d])) {
-            if (rank > 1)
-                return fail(FFT_ERR_NOT_POW2, "dims[%d] = %lld is not a power of two", d, (long long)dims[d]);
+            if (rank > 1) continue;
             if (dims[d] > kBluesteinMax)
                 return fail(FFT_ERR_UNSUPPORTED_SIZE, "length %lld (not a power of two) exceeds %lld",
                             (long long)dims[d], (long long)kBluesteinMax);
             continue;
         }
-        const int64_t lim = rank == 1 ? max_n(prec) : max_lds_n(prec);
+        const int64_t lim = rank == 1 || !all_pow2 ? max_n(prec) : max_lds_n(prec);
         if (dims[d] > lim)
             return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", d, (long long)dims[d],
                         (long long)lim);
@@ -834,6 +945,26 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                 snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
                          p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
             break;
+        case PATH_NDX: {
+            // the rows' route, then each axis's radices
+            fft_plan rows;
+            const int64_t w = p->dims[p->rank - 1];
+            char rb[160] = "copy";
+            if (w > 1 && plan_prepare(&rows, 1, &w, p->prec) == FFT_OK) {
+                fft_plan_describe(&rows, rb, sizeof rb);
+                const char* at = strstr(rb, "path=");
+                if (at) memmove(rb, at + 5, strlen(at + 5) + 1);
+            }
+            int off = snprintf(buf, len, "rank=%d dims=%lldx%lldx%lld prec=%s path=ndmixed rows=[%s]", p->rank,
+                               (long long)p->dims[0], (long long)(p->rank > 1 ? p->dims[1] : 1),
+                               (long long)(p->rank > 2 ? p->dims[2] : 1), prec, rb);
+            for (int a = 0; a < p->nx_k && off > 0 && (size_t)off < len; ++a) {
+                off += snprintf(buf + off, len - off, " axis%d=", a + 1);
+                for (int q = 0; q < p->nx_np[a] && off > 0 && (size_t)off < len; ++q)
+                    off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->passes[3 * a + q].r);
+            }
+            break;
+        }
         case PATH_MIXPASS: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=mixpass radices=", (long long)p->n, prec);
             for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
@@ -932,6 +1063,8 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
                 a.rmagic = (unsigned)(((uint64_t(1) << 32) + pp.r - 1) / pp.r);
                 a.conj_in = inv && q == 0;
                 a.conj_out = inv && last;
+                a.tdiv = 1;
+                a.twiddle = q > 0;
                 const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, 0};
                 e = launch_mixed_pass(plan->prec, a, pp.ms, src, dst, batch, pp.tw, big, scale, s,
                                       q == 0 ? io.in_im : nullptr, last ? io.out_im : nullptr);
@@ -1025,8 +1158,71 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
 // lives in `out` (in the workspace for an in-place folded call).  Planar: the
 // first pass reads the caller's planes into the workspace, later passes run
 // there, the last writes the caller's planes.
+// Rank 2 / 3 with a dimension that is not a power of two: the innermost axis
+// as rank-1 rows (in -> out), then each other axis in passes over `out`: one
+// pass in place; two: out -> Y -> out; three: out -> Y -> out -> out, the last
+// in place (planar: out -> Y -> Y2 -> out, the planar arrays read by an axis's
+// first pass and written by its last).  Workspace: [Y][Y2][the rows' own].
+static int run_ndx(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s)
+{
+    const bool planar = io.in_im != nullptr;
+    const size_t sig = (size_t)batch * (size_t)plan->n * plan->elem;
+    const size_t nbuf = ndx_axis_buffers(plan, planar);
+    char* y = (char*)workspace;
+    char* y2 = y + sig;
+    void* rows_ws = nbuf ? (void*)(y + nbuf * sig) : workspace;
+    const int64_t w = plan->dims[plan->rank - 1];
+    const int lines = mixed_pass_lines(plan->prec);
+    int st = FFT_OK;
+    if (w > 1) {
+        st = run_1d(plan->inner, inv, io, batch * (plan->n / w), rows_ws, s);
+        if (st != FFT_OK) return st;
+    }
+    // where the data is before the first axis pass
+    const void* cur = w > 1 ? (const void*)io.out : io.in;
+    const void* cur_im = w > 1 ? (const void*)io.out_im : io.in_im;
+    hipError_t e = hipSuccess;
+    for (int a = 0; a < plan->nx_k && e == hipSuccess; ++a) {
+        const int np = plan->nx_np[a];
+        const int64_t sig_pts = plan->nx_len[a] * plan->nx_stride[a];  // one signal of this axis
+        const int64_t nsig = batch * (plan->n / sig_pts);
+        for (int q = 0; q < np && e == hipSuccess; ++q) {
+            const PassPlan& pp = plan->passes[3 * a + q];
+            const bool first = q == 0, last = q == np - 1;
+            void* dst;
+            void* dst_im = nullptr;
+            if (last) {
+                dst = io.out;
+                dst_im = io.out_im;
+            } else {
+                dst = q == 0 ? (void*)y : (planar ? (void*)y2 : io.out);
+            }
+            MixedPassArgs ar{};
+            ar.n = (int)sig_pts;
+            ar.r = pp.r;
+            ar.ns = pp.ns;
+            ar.stride = (int)(sig_pts / pp.r);
+            ar.tiles = (ar.stride + lines - 1) / lines;
+            ar.tr = mixed_pass_threads(pp.ms, pp.r);
+            ar.rmagic = (unsigned)(((uint64_t(1) << 32) + pp.r - 1) / pp.r);
+            ar.conj_in = inv && first;
+            ar.conj_out = inv && last;
+            ar.tdiv = (int)plan->nx_stride[a];
+            ar.twiddle = q > 0;
+            const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, 0};
+            e = launch_mixed_pass(plan->prec, ar, pp.ms, cur, dst, nsig, pp.tw, big, 1.0 / (double)plan->nx_len[a], s,
+                                  first ? cur_im : nullptr, dst_im);
+            cur = dst;
+            cur_im = dst_im;
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "rank-2/3 transform launch");
+    return FFT_OK;
+}
+
 static int run_nd(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s)
 {
+    if (plan->path == PATH_NDX) return run_ndx(plan, inv, io, batch, workspace, s);
     const bool planar = io.in_im != nullptr;
     const double scale = 1.0 / (double)plan->n;
     const int k = plan->nd_k;
@@ -1095,7 +1291,9 @@ static int exec_nd(const fft_plan* plan, int rank, const char* what, int dir, co
                    int64_t batch, void* workspace, void* stream)
 {
     bool noop = false;
-    const size_t ws = plan && batch > 0 && plan->path == PATH_ND ? nd_workspace(plan, batch, in == out) : 0;
+    const size_t ws = !plan || batch <= 0 ? 0
+                      : plan->path == PATH_ND ? nd_workspace(plan, batch, in == out)
+                      : plan->path == PATH_NDX ? c2c_workspace(plan, batch) : 0;
     int st = check_exec(plan, dir, rank, in, out, batch, workspace, ws, &noop);
     if (st != FFT_OK || noop) return st;
     if ((st = check_device(plan)) != FFT_OK) return st;
@@ -1127,9 +1325,14 @@ static size_t planar_workspace(const fft_plan* p, int64_t batch)
         case PATH_MIXPASS: return p->npass >= 3 ? 2 * sig : sig;
         case PATH_BLUESTEIN: return c2c_workspace(p, batch);
         case PATH_ND: return p->nd_k >= 2 ? (p->col_split ? 2 * sig : sig) : 0;
+        case PATH_NDX: return ndx_workspace(p, batch, true);
         default: return 0;
     }
 }
+
+namespace {
+size_t planar_ws(const fft_plan* p, int64_t batch) { return planar_workspace(p, batch); }
+}  // namespace
 
 int fft_planar_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
 {

@@ -49,14 +49,19 @@ int mixed_max_n(int prec);
 // One mixed-radix super-stage pass (mixed.hip) over `batch` signals of n
 // points: radix r (<= 512, its stage schedule `ms`, twiddle table `tw` of
 // that schedule), span ns, stride n / r, tiles = ceil(stride / lines) per
-// signal, tr threads per line (mixed_pass_threads), rmagic = ceil(2^32 / r);
-// big: w_{ns r}^m (unused for ns = 1).  conj_in / conj_out + scale: the
-// inverse's first / last pass.  Planar: in_im on a first pass, or out_im on a
-// last pass, not both.  in -> out; in place only for the last pass (ns r = n).
+// signal, tr threads per line (mixed_pass_threads), rmagic = ceil(2^32 / r).
+// Twiddles (twiddle != 0): w_M^{q (k / tdiv)} from `big`, k = j mod ns, M =
+// r ns / tdiv; tdiv = 1 for a 1D transform, the axis stride for a pass of
+// one axis of an image or volume (ns = tdiv ns_axis: the pass runs the
+// axis's own super-stage on every column).  conj_in / conj_out + scale: the
+// inverse's first / last pass.  Planar: in_im on a first pass, out_im on a
+// last pass (both on a pass that is both).  in -> out; in place only for the
+// last pass (ns r = n).
 struct MixedPassArgs {
     int n, r, ns, stride, tiles, tr;
     unsigned rmagic;
     int conj_in, conj_out;
+    int tdiv, twiddle;
 };
 int mixed_pass_threads(const MixedSchedule& ms, int r);
 int mixed_pass_lines(int prec);

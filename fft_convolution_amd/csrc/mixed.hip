@@ -544,8 +544,8 @@ __global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, O
     // from the input (element q of line j at j + q N/R, times w^{q k}); for
     // Ns > 1 the last writes straight to the output (element q at
     // g Ns R + k + q Ns); the stages between go through LDS.
-    const PassIO<V, IN, OUT> io{in, out, sbase + j, a.stride, sbase + (int64_t)g * a.ns * a.r + k, a.ns, big, k,
-                                a.ns > 1, a.conj_in != 0, a.conj_out != 0, live, scale};
+    const PassIO<V, IN, OUT> io{in, out, sbase + j, a.stride, sbase + (int64_t)g * a.ns * a.r + k, a.ns, big,
+                                k / a.tdiv, a.twiddle != 0, a.conj_in != 0, a.conj_out != 0, live, scale};
     V* row = lds + c;
     const int last = ms.nst - 1;
     if (a.ns > 1) {
@@ -621,6 +621,9 @@ template <typename V>
 static hipError_t mixed_pass_v(const Io& io, int64_t batch, const MixedPassArgs& a, const MixedSchedule& ms,
                                const void* tw, const BigTwiddle& bt, double scale, hipStream_t s)
 {
+    if (io.in_im && io.out_im)
+        return mixed_pass_w<V>(make_in<V, true>(io.in, io.in_im), make_out<V, true>(io.out, io.out_im), batch, a, ms,
+                               tw, bt, scale, s);
     if (io.in_im) return mixed_pass_w<V>(make_in<V, true>(io.in, io.in_im), make_out<V, false>(io.out, nullptr), batch,
                                          a, ms, tw, bt, scale, s);
     if (io.out_im) return mixed_pass_w<V>(make_in<V, false>(io.in, nullptr), make_out<V, true>(io.out, io.out_im),
@@ -643,10 +646,10 @@ hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedu
                              int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t s,
                              const void* in_im, void* out_im)
 {
-    if (in_im && out_im) return hipErrorInvalidValue;  // planar only at the first or the last pass
     if (a.r > 512 || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr > 64 ||
         (a.r + a.tr - 1) / a.tr > MP_QMAX ||
-        a.ns < 1 || (int64_t)a.stride * a.r != a.n || a.tiles * (int64_t)mixed_pass_lines(prec) < a.stride ||
+        a.ns < 1 || a.tdiv < 1 || a.ns % a.tdiv || (int64_t)a.stride * a.r != a.n ||
+        a.tiles * (int64_t)mixed_pass_lines(prec) < a.stride ||
         a.rmagic != (unsigned)(((uint64_t(1) << 32) + a.r - 1) / a.r))
         return hipErrorInvalidValue;
     const Io io{in, in_im, out, out_im};

@@ -18,6 +18,8 @@ What it computes, and the passage each part follows:
 * ``fft2`` / ``ifft2`` -- rows then columns ("Stockham FFT Butterfly Algorithm in
   Parallel GLSL", section "Multi-Dimensional Transforms and Separability");
   ``fft3`` / ``ifft3`` -- the same, one axis after another, for 3D data.
+  ``dftn`` -- that separable evaluation with ``dft`` along each of the last
+  k axes, for any lengths (shapes that are not powers of two).
 * ``rfft`` / ``irfft`` -- transforms of real rows: the first N/2 + 1 outputs of
   ``fft`` of the row widened to complex (the other half follows from
   X_{N-k} = conj X_k, since the inputs are real), and back: the real part of
@@ -252,6 +254,17 @@ def fft3(x, inverse: bool = False) -> np.ndarray:
 
 def ifft3(X) -> np.ndarray:
     return fft3(X, inverse=True)
+
+
+def dftn(x, k: int, inverse: bool = False) -> np.ndarray:
+    """The k-dimensional transform over the last k axes, any lengths: ``dft``
+    along the last axis, then along each axis before it (the sums over the
+    k indices evaluated one index at a time)."""
+    y = _as_c128(x)
+    for ax in range(1, k + 1):
+        moved = np.ascontiguousarray(np.moveaxis(y, -ax, -1))
+        y = np.ascontiguousarray(np.moveaxis(dft(moved, inverse=inverse), -1, -ax))
+    return y
 
 
 def _as_i64(a) -> np.ndarray:

@@ -73,13 +73,18 @@ def _create_status(rank, dims, prec):
     (1, [-4], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [(1 << 23) + 1], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # beyond the Bluestein range
     (1, [3 << 22], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (2, [8, 6], 0, fm.FFT_ERR_NOT_POW2),
-    (2, [12, 8], 1, fm.FFT_ERR_NOT_POW2),
+    # not powers of two: axes other than the innermost must be 13-smooth, and
+    # the transform at most 2^26 / 2^24 points
+    (2, [97, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [17 * 3, 12], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [10000, 10000], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [1200, 16000], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [2, (1 << 23) + 1], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 25], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (3, [8, 6, 8], 0, fm.FFT_ERR_NOT_POW2),
+    (3, [8, 19, 6], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (3, [0, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
     (3, [4096, 8, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # depth beyond the column-pass range
     (3, [2048, 8, 8], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -152,9 +157,9 @@ def test_exec_and_queries_with_null_plan():
 
 def test_binding_raises_fft_error():
     with pytest.raises(fm.FFTError) as ei:
-        fm.fft_plan_create(2, [6, 8], fm.FFT_C32)
-    assert ei.value.status == fm.FFT_ERR_NOT_POW2
-    assert "not a power of two" in str(ei.value)
+        fm.fft_plan_create(2, [97, 8], fm.FFT_C32)
+    assert ei.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE
+    assert "innermost" in str(ei.value)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

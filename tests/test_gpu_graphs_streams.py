@@ -23,7 +23,7 @@ def test_graph_replays_equal_eager(dev):
     cases = []
     # one-kernel rows, multi-pass, 2D fold, Bluestein, mixed radix (11 x 13 too), N = 1 copy
     for dims, dtype in (((4096,), torch.complex64), ((1 << 20,), torch.complex64), ((2048, 256), torch.complex64),
-                        ((1009,), torch.complex64), ((1001,), torch.complex64), ((10 ** 6,), torch.complex64), ((360,), torch.complex128), ((1,), torch.complex64)):
+                        ((1009,), torch.complex64), ((1001,), torch.complex64), ((10 ** 6,), torch.complex64), ((1000, 60), torch.complex64), ((360,), torch.complex128), ((1,), torch.complex64)):
         n = int(np.prod(dims))
         batch = max(1, (1 << 20) // n)
         npdt = np.complex64 if dtype == torch.complex64 else np.complex128

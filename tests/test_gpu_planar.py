@@ -35,6 +35,9 @@ CASES = [
     ((10000,), torch.complex64, 2),        # mixed-radix passes (two)
     ((10 ** 6,), torch.complex64, 1),      # mixed-radix passes (three)
     ((6000,), torch.complex128, 2),
+    ((100, 7), torch.complex64, 2),        # non-power-of-two images: rows, one column pass
+    ((1000, 60), torch.complex64, 1),      # two column passes
+    ((12, 30, 50), torch.complex128, 1),
     ((4097,), torch.complex128, 2),
     ((60,), torch.complex64, 7),           # mixed radix
     ((2401,), torch.complex128, 2),

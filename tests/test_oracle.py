@@ -338,6 +338,41 @@ def test_fft2_plane_waves_closed_form():
         assert top == set((fy[b] * w + fx[b]).tolist())
 
 
+def test_dftn_brute_force_closed_forms_and_pow2_agreement():
+    """dftn (any lengths) against the multi-dimensional definition summed
+    directly over all indices on tiny shapes, plane waves of non-power-of-two
+    shapes, numpy's fftn, and the radix-2 fft2 / fft3 on power-of-two shapes."""
+    rng = np.random.default_rng(21)
+    for shape in ((3, 5), (1, 7), (6, 1), (2, 3, 4), (5, 1, 3)):
+        x = crand(rng, *shape)
+        k = len(shape)
+        idx = [np.arange(n) for n in shape]
+        ref = np.zeros(shape, complex)
+        for out in np.ndindex(*shape):
+            # sum over every input index of x[n] prod_d e^{-2 pi i n_d k_d / N_d}
+            ph = np.zeros(shape)
+            for d in range(k):
+                sh = [1] * k
+                sh[d] = shape[d]
+                ph = ph + ((idx[d] * out[d]) % shape[d]).reshape(sh) / shape[d]
+            ref[out] = np.sum(x * np.exp(-2j * np.pi * ph))
+        assert rel_rms(oracle.dftn(x, k), ref) < 1e-14, shape
+        assert rel_rms(oracle.dftn(oracle.dftn(x, k), k, inverse=True), x) < 1e-14
+    for shape in ((12, 20), (7, 100), (3, 10, 6)):
+        x = crand(rng, 2, *shape)
+        assert rel_rms(oracle.dftn(x, len(shape)), np.fft.fftn(x, axes=tuple(range(1, len(shape) + 1)))) < 1e-13
+    # a plane wave of a 30 x 14 image: H W at (fy, fx)
+    h, w, fy, fx = 30, 14, 7, 9
+    yy, xx = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
+    wave = np.exp(2j * np.pi * (((fy * yy) % h) / h + ((fx * xx) % w) / w))
+    ref = np.zeros((h, w), complex)
+    ref[fy, fx] = h * w
+    assert np.max(np.abs(oracle.dftn(wave, 2) - ref)) < 1e-10 * h * w
+    x2, x3 = crand(rng, 2, 16, 32), crand(rng, 8, 4, 16)
+    assert rel_rms(oracle.dftn(x2, 2), oracle.fft2(x2)) < 1e-14
+    assert rel_rms(oracle.dftn(x3, 3), oracle.fft3(x3)) < 1e-14
+
+
 def test_fft3_matches_numpy_separability_and_closed_form():
     rng = np.random.default_rng(13)
     for d, h, w in ((1, 4, 8), (4, 1, 8), (8, 4, 1), (2, 2, 2), (8, 16, 4), (16, 8, 32)):

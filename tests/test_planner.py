@@ -113,7 +113,7 @@ def test_3d_layouts():
     (0, [8], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [0], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [8], 5, fm.FFT_ERR_INVALID_ARG),
-    (2, [12, 8], 0, fm.FFT_ERR_NOT_POW2),
+    (2, [17, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [(1 << 23) + 1], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -137,3 +137,20 @@ def test_mixpass_splits():
     assert "path=mixpass" in _q(1, [6000], 1) and "path=mixed" in _q(1, [6000], 0)
     # a prime factor above 13, or beyond 2^23: Bluestein or rejected
     assert "path=bluestein" in _q(1, [1000003], 0)
+
+
+def test_ndmixed_layouts():
+    """Rank 2 / 3 with a dimension that is not a power of two: the innermost
+    axis by its rank-1 route, every other axis longer than 1 as passes of
+    radix <= 512 (one up to 512 points)."""
+    d = _q(2, [1000, 1000], 0)
+    assert "path=ndmixed" in d and "rows=[mixed radices=8x5x5x5]" in d and d.endswith("axis1=40x25")
+    d = _q(2, [64, 97], 1)
+    assert "rows=[bluestein" in d and d.endswith("axis1=64")
+    d = _q(3, [12, 30, 50], 0)
+    assert d.endswith("axis1=30 axis2=12")
+    d = _q(2, [1000, 1], 0)
+    assert "rows=[copy]" in d and d.endswith("axis1=40x25")
+    assert "axis" not in _q(2, [1, 1000], 0)
+    # the power-of-two shapes keep their own path
+    assert "path=nd " in _q(2, [64, 32], 0)
