@@ -472,10 +472,11 @@ template <typename V> struct AnyTw {
 // The global side of a pass's line: input element q at ibase + q istride,
 // times w^{q k} when twiddled (conjugated first for the inverse's first
 // pass); output element q at obase + q ostride (conjugated and scaled for the
-// inverse's last pass).  load: the R elements j + r stride of a butterfly,
+// inverse's last pass).  TW: the twiddles are on (a compile-time switch, so
+// that each stage's code is built with or without them).  load: the R elements j + r stride of a butterfly,
 // the twiddles as w^{k j} times powers of w^{k stride} (R - 1 products,
 // exponents below Ns R).
-template <typename V, typename IN, typename OUT> struct PassIO {
+template <typename V, typename IN, typename OUT, bool TW> struct PassIO {
     IN in;
     OUT out;
     int64_t ibase;
@@ -484,13 +485,13 @@ template <typename V, typename IN, typename OUT> struct PassIO {
     int ostride;
     AnyTw<V> big;
     int k;
-    bool twiddle, conj_in, conj_out, live;
+    bool conj_in, conj_out, live;
     typename real_of<V>::type scale;
     template <int R> __device__ __forceinline__ void load(int j, int stride, V (&u)[R]) const
     {
         if (!live) return;
         V w{1, 0}, step{1, 0};
-        if (twiddle) {
+        if constexpr (TW) {
             w = big(k * j);
             step = big(k * stride);
         }
@@ -498,7 +499,7 @@ template <typename V, typename IN, typename OUT> struct PassIO {
         for (int r = 0; r < R; ++r) {
             V x = in.ld(ibase + (int64_t)(j + r * stride) * istride);
             if (conj_in) x = cconj(x);
-            if (twiddle) {
+            if constexpr (TW) {
                 x = cmul(x, w);
                 if (r + 1 < R) w = cmul(w, step);
             }
@@ -532,7 +533,11 @@ __global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, O
 {
     constexpr int LINES = mp_lines<V>();
     constexpr int P = LINES + 1;
-    __shared__ V lds[P * RCAP];
+    // RCAP 0: LDS sized at launch to the radix (short lines leave room for
+    // many workgroups per CU); otherwise a static class
+    __shared__ V lds_static[RCAP > 0 ? P * RCAP : 1];
+    extern __shared__ __align__(16) unsigned char mp_lds_dyn[];
+    V* const lds = RCAP > 0 ? lds_static : reinterpret_cast<V*>(mp_lds_dyn);
     const int c = threadIdx.x % LINES, tl = threadIdx.x / LINES;
     const int64_t sig = (int64_t)blockIdx.x / a.tiles;
     const int j0 = (int)((int64_t)blockIdx.x - sig * a.tiles) * LINES;
@@ -544,27 +549,38 @@ __global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, O
     // from the input (element q of line j at j + q N/R, times w^{q k}); for
     // Ns > 1 the last writes straight to the output (element q at
     // g Ns R + k + q Ns); the stages between go through LDS.
-    const PassIO<V, IN, OUT> io{in, out, sbase + j, a.stride, sbase + (int64_t)g * a.ns * a.r + k, a.ns, big,
-                                k / a.tdiv, a.twiddle != 0, a.conj_in != 0, a.conj_out != 0, live, scale};
     V* row = lds + c;
     const int last = ms.nst - 1;
-    if (a.ns > 1) {
-        if (last == 0) {
-            mixed_stage_any<WIDE, true, true, true, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+    auto stages = [&](const auto& io) {
+        if (a.ns > 1) {
+            if (last == 0) {
+                mixed_stage_any<WIDE, true, true, true, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+                return;
+            }
+            mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+            for (int s = 1; s < last; ++s)
+                mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
+                                                              ms.magic[s], tw + ms.twoff[s], io);
+            mixed_stage_any<WIDE, false, false, true, P>(ms.radix[last], row, tl, a.tr, ms.stride[last],
+                                                         ms.ns[last], ms.magic[last], tw + ms.twoff[last], io);
             return;
         }
         mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
-        for (int s = 1; s < last; ++s)
+        for (int s = 1; s <= last; ++s)
             mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
                                                           ms.magic[s], tw + ms.twoff[s], io);
-        mixed_stage_any<WIDE, false, false, true, P>(ms.radix[last], row, tl, a.tr, ms.stride[last], ms.ns[last],
-                                                     ms.magic[last], tw + ms.twoff[last], io);
-        return;
+    };
+    const int64_t ibase = sbase + j, obase_l = sbase + (int64_t)g * a.ns * a.r + k;
+    if (a.twiddle) {
+        const PassIO<V, IN, OUT, true> io{in, out, ibase, a.stride, obase_l, a.ns, big, a.tdiv == 1 ? k : k / a.tdiv,
+                                          a.conj_in != 0, a.conj_out != 0, live, scale};
+        stages(io);
+    } else {
+        const PassIO<V, IN, OUT, false> io{in, out, ibase, a.stride, obase_l, a.ns, big, 0,
+                                           a.conj_in != 0, a.conj_out != 0, live, scale};
+        stages(io);
     }
-    mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
-    for (int s = 1; s <= last; ++s)
-        mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s], ms.magic[s],
-                                                      tw + ms.twoff[s], io);
+    if (a.ns > 1) return;
     // Ns = 1: line j's outputs are j R + q, so the tile's lines are one
     // contiguous block: element e = tid + i blockDim of it, in chunks
     const int lines = a.stride - j0 < LINES ? a.stride - j0 : LINES;
@@ -588,7 +604,8 @@ __global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, O
     }
 }
 
-// LDS classes: radix <= 128 and <= 512.
+// LDS: exactly (lines + 1) r elements up to radix 128 (set at launch), a
+// static class of radix 512 beyond.
 template <typename V, bool WIDE, typename IN, typename OUT>
 static hipError_t mixed_pass_t(IN in, OUT out, int64_t batch, const MixedPassArgs& a, const MixedSchedule& ms,
                                const void* tw, const BigTwiddle& bt, double scale, hipStream_t s)
@@ -599,8 +616,9 @@ static hipError_t mixed_pass_t(IN in, OUT out, int64_t batch, const MixedPassArg
     const AnyTw<V> big{(const V*)bt.hi, (const V*)bt.lo, bt.lbits};
     const dim3 grid((unsigned)blocks), block(mp_lines<V>() * a.tr);
     if (a.r <= 128)
-        hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 128, IN, OUT>), grid, block, 0, s, in, out, a, ms,
-                           (const V*)tw, big, (Rl)scale);
+        hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 0, IN, OUT>), grid, block,
+                           (unsigned)((mp_lines<V>() + 1) * a.r * (int)sizeof(V)), s, in, out, a, ms, (const V*)tw,
+                           big, (Rl)scale);
     else
         hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 512, IN, OUT>), grid, block, 0, s, in, out, a, ms,
                            (const V*)tw, big, (Rl)scale);
