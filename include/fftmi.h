@@ -58,8 +58,8 @@ enum fft_direction { FFT_FORWARD = 0, FFT_INVERSE = 1 };
 enum fft_status {
     FFT_OK = 0,
     FFT_ERR_INVALID_ARG = -1,      /* NULL pointer, batch < 0, bad rank/dir/prec value */
-    FFT_ERR_NOT_POW2 = -2,         /* a dimension of a rank-2/3 plan, or the length of a
-                                      poly-mul plan, is not a power of two */
+    FFT_ERR_NOT_POW2 = -2,         /* the length of a poly-mul or real-input plan is not a
+                                      power of two */
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
@@ -115,11 +115,19 @@ enum fft_status {
  *           (y, x) (the same separability, one axis after another); each
  *           dimension as for rank 2, and the depth D <= 2048 (C32) / 1024 (C64)
  *           unless H = W = 1.
+ *   rank 2 / 3 with a dimension that is not a power of two: the innermost
+ *           axis W may have any length a rank-1 plan takes (it runs as the
+ *           rank-1 plan over every row); every other axis longer than 1 must
+ *           be 2^a 3^b 5^c 7^d 11^e 13^f and runs as one super-stage pass up
+ *           to 512 points, two or three beyond; at most FFT_MAX_N_* points
+ *           per transform (fft_plan_describe: path=ndmixed).  Workspace:
+ *           fft_workspace_size, out of place too (a signal-sized buffer for
+ *           an axis of two or more passes, plus what the rows need).
  *   prec:   FFT_C32 or FFT_C64.
  * Builds the twiddle tables in fp64 on the host, rounds them to the plan
  * precision and uploads them (the only synchronous device work of the
  * library).  On success *plan receives the new plan; on failure *plan is set
- * to NULL.  Errors: INVALID_ARG, NOT_POW2 (rank 2/3), UNSUPPORTED_SIZE, DEVICE.
+ * to NULL.  Errors: INVALID_ARG, UNSUPPORTED_SIZE, DEVICE.
  */
 int fft_plan_create(fft_plan** plan, int rank, const int64_t* dims, int prec);
 
@@ -133,7 +141,7 @@ int fft_plan_describe(const fft_plan* plan, char* buf, size_t len);
 /* The description fft_plan_describe would give for the plan that
  * fft_plan_create(rank, dims, prec) would make, without making it: host-only
  * (no HIP call, no device needed), the same validation and status codes.
- * Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE. */
+ * Errors: INVALID_ARG, UNSUPPORTED_SIZE. */
 int fft_plan_query(int rank, const int64_t* dims, int prec, char* buf, size_t len);
 
 /* Bytes of device workspace fft_exec_c2c / fft_exec_2d need for `batch`
@@ -159,8 +167,9 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
  *   workspace: fft_workspace_size(plan, batch) bytes for an in-place call
  *              (in == out) on a plan that folds part of the column transform
  *              into the row pass (H > 512; fft_plan_describe shows fold > 1),
- *              and for every call on a split plan (split=F); otherwise it may
- *              be NULL.
+ *              and for every call on a split plan (split=F) or a plan with a
+ *              dimension that is not a power of two (path=ndmixed) whose
+ *              fft_workspace_size is not 0; otherwise it may be NULL.
  * Errors: as fft_exec_c2c.
  */
 int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
@@ -169,7 +178,8 @@ int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_
 /*
  * Batched 3D transform with a rank-3 plan.
  *   in, out:   [batch][D][H][W] complex, volumes contiguous.  in == out allowed.
- *   workspace: as fft_exec_2d (needed only in place when the plan folds).
+ *   workspace: as fft_exec_2d (power-of-two plans: only in place when the
+ *              plan folds).
  * Errors: as fft_exec_c2c.
  */
 int fft_exec_3d(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch,
