@@ -483,8 +483,12 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
                    : ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
     if (p->path == PATH_REAL && p->rank == 2)  // the half spectrum of every image (C2R; R2C with a column stage)
         return p->dims[0] > 1 ? (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem : 0;
-    if (p->path == PATH_REAL)  // the H-point spectrum of every row, beyond the one-kernel range
-        return p->real_fused || p->n == 1 ? 0 : (size_t)batch * (size_t)(p->n / 2) * p->elem;
+    if (p->path == PATH_REAL) {  // the H-point spectrum of every row, beyond the one-kernel range
+        if (p->real_fused || p->n == 1) return 0;
+        const size_t z = (size_t)batch * (size_t)(p->n / 2) * p->elem;
+        // lengths that are not powers of two: the H-point plan's own workspace after it
+        return is_pow2(p->n) ? z : z + c2c_workspace(p->inner, batch);
+    }
     const bool need = p->path == PATH_MULTIPASS || p->path == PATH_MIXPASS || (p->path == PATH_ND && p->logf > 0);
     return need ? (size_t)batch * (size_t)p->n * p->elem : 0;
 }
@@ -1467,9 +1471,11 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     *out_plan = nullptr;
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
     if (n < 1) return fail(FFT_ERR_INVALID_ARG, "n = %lld < 1", (long long)n);
-    if (!is_pow2(n)) return fail(FFT_ERR_NOT_POW2, "n = %lld is not a power of two", (long long)n);
-    if (n > 2 * max_n(prec))
-        return fail(FFT_ERR_UNSUPPORTED_SIZE, "n = %lld exceeds %lld", (long long)n, (long long)(2 * max_n(prec)));
+    // any even length: the complex plan of N/2 points (any route) and the
+    // bin-pair pass; powers of two within one workgroup also fuse the two
+    if (n > 1 && n % 2) return fail(FFT_ERR_NOT_POW2, "n = %lld is odd (real rows take an even length)", (long long)n);
+    const int64_t lim = is_pow2(n) ? 2 * max_n(prec) : 2 * kBluesteinMax;
+    if (n > lim) return fail(FFT_ERR_UNSUPPORTED_SIZE, "n = %lld exceeds %lld", (long long)n, (long long)lim);
     fft_plan* p = new (std::nothrow) fft_plan;
     if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
     p->rank = 1;
@@ -1477,9 +1483,9 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     p->prec = prec;
     p->elem = elem_bytes(prec);
     p->dims[0] = p->n = n;
-    p->logn = ilog2(n);
-    p->log_a = p->logn > 0 ? p->logn - 1 : 0;
-    p->real_fused = n >= 2 && (n / 2) <= max_lds_n(prec);
+    p->logn = is_pow2(n) ? ilog2(n) : 31;  // 31: w_N lookups of any N take no index mask (k < N)
+    p->log_a = is_pow2(n) && p->logn > 0 ? p->logn - 1 : 0;
+    p->real_fused = is_pow2(n) && n >= 2 && (n / 2) <= max_lds_n(prec);
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) {
         delete p;
@@ -1492,7 +1498,9 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
         // w_N^{t + i T} = hi[i] lo[t] for the fused kernels (T threads per row)
         const int lem = plan_lem(prec);
         const int want = p->real_fused ? p->log_a - plan_loge(p->log_a, lem) : -1;
-        if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits, want);
+        if (st == FFT_OK)
+            st = is_pow2(n) ? upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits, want)
+                            : upload_big_any(n, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
     }
     if (st != FFT_OK) {
         free_plan(p);
@@ -1666,7 +1674,8 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
         // Z = F_H(rows read as complex) into the workspace (the out buffer, which
         // holds batch (H + 1) >= batch H values, is the H-point plan's scratch),
         // then the split, two bins per thread.
-        st = fft_exec_c2c(plan->inner, FFT_FORWARD, in, workspace, batch, out, stream);
+        void* inner_ws = is_pow2(plan->n) ? out : (char*)workspace + (size_t)batch * (size_t)(plan->n / 2) * plan->elem;
+        st = fft_exec_c2c(plan->inner, FFT_FORWARD, in, workspace, batch, inner_ws, stream);
         if (st != FFT_OK) return st;
         const BigTwiddle wn{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
         e = launch_real_pairs(plan->prec, false, workspace, out, plan->n / 2, batch, wn, s);

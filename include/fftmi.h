@@ -58,8 +58,8 @@ enum fft_direction { FFT_FORWARD = 0, FFT_INVERSE = 1 };
 enum fft_status {
     FFT_OK = 0,
     FFT_ERR_INVALID_ARG = -1,      /* NULL pointer, batch < 0, bad rank/dir/prec value */
-    FFT_ERR_NOT_POW2 = -2,         /* the length of a poly-mul or real-input plan is not a
-                                      power of two */
+    FFT_ERR_NOT_POW2 = -2,         /* the length of a poly-mul plan or of real images is not
+                                      a power of two, or real rows are of odd length */
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
@@ -239,8 +239,10 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
                  double* d_max_residual, void* stream);
 
 /*
- * Plan for transforms of real rows of N points (N a power of two,
- * 1 <= N <= 2 * FFT_MAX_N_C32 (C32) / 2 * FFT_MAX_N_C64 (C64)).  The
+ * Plan for transforms of real rows of N points: N = 1 or even, up to
+ * 2 * FFT_MAX_N_C32 (C32) / 2 * FFT_MAX_N_C64 (C64) for powers of two and
+ * 2 * FFT_MAX_BLUESTEIN_N otherwise (the N/2-point complex plan then takes
+ * whichever route its length has; odd N > 1 gives FFT_ERR_NOT_POW2).  The
  * operands of polynomial multiplication are real ("FFT on GPU",
  * polynomial-multiplication section); a real row's transform is fixed by
  * its bins X_0 .. X_{N/2}, since X_{N-k} = conj X_k.  The row is read as N/2
@@ -249,7 +251,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
  * bins) or FFT_C64 (double rows, complex128 bins).  The plan serves only
  * fft_exec_r2c / fft_exec_c2r (other calls give FFT_ERR_RANK);
  * fft_workspace_size and fft_plan_describe accept it.
- * Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE, DEVICE.
+ * Errors: INVALID_ARG, NOT_POW2 (odd N), UNSUPPORTED_SIZE, DEVICE.
  */
 int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
 

@@ -178,13 +178,14 @@ def ifft(X) -> np.ndarray:
 
 
 def rfft(x) -> np.ndarray:
-    """X_0 .. X_{N/2} of the transform of each real row (N a power of two):
-    [..., N] real -> [..., N // 2 + 1] complex128."""
+    """X_0 .. X_{N/2} of the transform of each real row: [..., N] real ->
+    [..., N // 2 + 1] complex128 (``fft`` for a power-of-two N, else ``dft``)."""
     x = np.asarray(x)
     if np.iscomplexobj(x):
         raise TypeError("rfft takes real rows")
     n = x.shape[-1]
-    return fft(x.astype(np.float64))[..., : n // 2 + 1]
+    full = fft(x.astype(np.float64)) if n & (n - 1) == 0 else dft(x.astype(np.float64))
+    return full[..., : n // 2 + 1]
 
 
 def irfft(X, n: int) -> np.ndarray:
@@ -196,13 +197,15 @@ def irfft(X, n: int) -> np.ndarray:
     h = n // 2
     if X.shape[-1] != h + 1:
         raise ValueError("irfft of length %d takes %d values per row" % (n, h + 1))
+    if n > 1 and n % 2:
+        raise ValueError("irfft takes an even length")
     full = np.empty(X.shape[:-1] + (n,), dtype=np.complex128)
     full[..., : h + 1] = X[..., : h + 1] if n > 1 else X[..., :1]
     full[..., 0] = full[..., 0].real
     if n > 1:
         full[..., h] = full[..., h].real
         full[..., h + 1:] = np.conj(X[..., 1:h][..., ::-1])
-    return ifft(full).real
+    return (ifft(full) if n & (n - 1) == 0 else dft(full, inverse=True)).real
 
 
 def rfft2(x) -> np.ndarray:

@@ -118,8 +118,9 @@ def test_valid_plan_without_gpu_is_a_device_error():
     (0, 0, fm.FFT_ERR_INVALID_ARG),
     (-8, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 2, fm.FFT_ERR_INVALID_ARG),
-    (6, 0, fm.FFT_ERR_NOT_POW2),
-    (1000, 1, fm.FFT_ERR_NOT_POW2),
+    (7, 0, fm.FFT_ERR_NOT_POW2),            # odd: real rows take an even length
+    (1001, 1, fm.FFT_ERR_NOT_POW2),
+    (2 * ((1 << 23) + 1), 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1 << 28, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1 << 26, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
 ])

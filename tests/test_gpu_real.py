@@ -149,3 +149,38 @@ def test_real_errors_and_kinds(dev):
     fm.RealPlan(4096).irfft(Y)
     torch.cuda.synchronize()
     assert torch.equal(xr, x0) and torch.equal(Y, Y0)
+
+
+# Even lengths that are not powers of two: the N/2-point complex plan by its
+# route (mixed radix, 11 x 13, Bluestein fused and in passes, mixed-radix
+# passes) plus the bin-pair pass.
+@pytest.mark.parametrize("n,dtype,batch", [
+    (6, np.float32, 5), (10, np.float32, 3), (12, np.float64, 4), (100, np.float32, 3), (1000, np.float32, 2),
+    (2002, np.float32, 2), (2 * 1009, np.float32, 2), (20000, np.float32, 2), (2 * 10007, np.float32, 1),
+    (1000, np.float64, 2), (2 * 1009, np.float64, 2), (20000, np.float64, 1)])
+def test_real_even_lengths(dev, n, dtype, batch):
+    print("case n=%d %s batch=%d" % (n, np.dtype(dtype).name, batch), flush=True)
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    cdt = np.complex64 if dtype == np.float32 else np.complex128
+    plan = fm.RealPlan(n, tdt)
+    assert "pairs" in plan.describe()
+    h = n // 2
+    route = fm.fft_plan_query(1, [h], 0 if dtype == np.float32 else 1)
+    size = n
+    if "bluestein" in route:  # the tolerance of the convolution length
+        m = 1
+        while m < 2 * h - 1:
+            m *= 2
+        size = 2 * m
+    tol = fft_tol(size, dtype == np.float64)
+    oracle.set_threads(8)
+    x_np = wl.real_normal(n, batch, seed=n % 997, dtype=dtype)
+    x = torch.from_numpy(x_np).cuda()
+    X = plan.rfft(x).cpu().numpy()
+    assert X.shape == (batch, h + 1)
+    assert rel_rms_rows(X, oracle.rfft(x_np)).max() <= tol
+    S_np = wl.real_spectrum(n, batch, seed=n % 991, dtype=cdt)
+    y = plan.irfft(torch.from_numpy(S_np).cuda()).cpu().numpy()
+    assert rel_rms_rows(y, oracle.irfft(S_np, n)).max() <= tol
+    back = plan.irfft(plan.rfft(x)).cpu().numpy()
+    assert rel_rms_rows(back, x_np).max() <= 2 * tol

@@ -398,7 +398,7 @@ def test_fft3_matches_numpy_separability_and_closed_form():
 # Polynomial multiplication
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n", [1, 2, 4, 8, 64, 4096, 1 << 17])
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 64, 4096, 1 << 17, 6, 10, 100, 1000, 2002])
 def test_rfft_irfft_match_numpy(n):
     rng = np.random.default_rng(n)
     x = rng.standard_normal((3, n))
@@ -412,6 +412,20 @@ def test_rfft_irfft_match_numpy(n):
     # also takes the DC and Nyquist bins as real
     Y = rng.standard_normal((2, n // 2 + 1)) + 1j * rng.standard_normal((2, n // 2 + 1))
     assert np.abs(oracle.irfft(Y, n) - np.fft.irfft(Y, n)).max() <= 1e-13 * max(1.0, math.log2(n))
+
+
+def test_rfft_even_lengths_closed_form_and_odd_rejected():
+    # a cosine of frequency f in a 1000-point row: N/2 at bin f (f < N/2)
+    n = 1000
+    t = np.arange(n)
+    for f in (0, 3, 499, 500):
+        x = np.cos(2 * np.pi * ((f * t) % n) / n)
+        X = oracle.rfft(x[None, :])[0]
+        want = np.zeros(n // 2 + 1, complex)
+        want[f] = n if f in (0, n // 2) else n / 2
+        assert np.abs(X - want).max() < 1e-9
+    with pytest.raises(ValueError):
+        oracle.irfft(np.zeros((1, 3), complex), 5)
 
 
 def test_rfft_closed_forms_and_hermitian_half():
