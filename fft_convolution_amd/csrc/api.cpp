@@ -319,6 +319,10 @@ struct fft_plan {
     int nx_k = 0;
     int64_t nx_len[2] = {1, 1}, nx_stride[2] = {1, 1};
     int nx_np[2] = {0, 0};
+    // real images outside the power-of-two route: inner = the real-row plan
+    // of length W, then the column axis as above over the W/2 + 1 columns of
+    // the half spectrum (nx_stride[0] = W/2 + 1)
+    bool real_nd = false;
     size_t elem = 8;
 };
 
@@ -481,6 +485,12 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
         return (int64_t(1) << p->logm) <= max_lds_n(p->prec)
                    ? 0
                    : ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
+    if (p->path == PATH_REAL && p->rank == 2 && p->real_nd) {
+        // [Z: the half spectrum (C2R)][Y: an axis of two or more passes][the rows' own]
+        const size_t half = (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem;
+        const size_t zy = p->nx_k ? half * (p->nx_np[0] >= 2 ? 2 : 1) : 0;
+        return zy + c2c_workspace(p->inner, batch * p->dims[0]);
+    }
     if (p->path == PATH_REAL && p->rank == 2)  // the half spectrum of every image (C2R; R2C with a column stage)
         return p->dims[0] > 1 ? (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem : 0;
     if (p->path == PATH_REAL) {  // the H-point spectrum of every row, beyond the one-kernel range
@@ -941,7 +951,16 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             break;
         }
         case PATH_REAL:
-            if (p->rank == 2)
+            if (p->real_nd) {
+                int off = snprintf(buf, len, "real dims=%lldx%lld prec=%s path=real2dmixed rows=real %s",
+                                   (long long)p->dims[0], (long long)p->dims[1], prec,
+                                   !p->inner || p->inner->n == 1 ? "copy" : p->inner->real_fused ? "fused" : "pairs");
+                if (p->nx_k && off > 0 && (size_t)off < len) {
+                    off += snprintf(buf + off, len - off, " axis1=");
+                    for (int q = 0; q < p->nx_np[0] && off > 0 && (size_t)off < len; ++q)
+                        off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->passes[q].r);
+                }
+            } else if (p->rank == 2)
                 snprintf(buf, len, "real dims=%lldx%lld prec=%s path=real2d col_stage=%d col_len=%lld",
                          (long long)p->dims[0], (long long)p->dims[1], prec, 1 << p->logf,
                          p->dims[0] > 1 ? 1LL << p->log_b : 0LL);
@@ -1162,63 +1181,70 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
 // lives in `out` (in the workspace for an in-place folded call).  Planar: the
 // first pass reads the caller's planes into the workspace, later passes run
 // there, the last writes the caller's planes.
+// The passes of axis a of a plan with nx_* axes (signals of length x stride
+// points, batch x n / that of them): src -> dst, one pass directly (in place
+// when src == dst), two through y, three through y then y2 (planar) or dst
+// (the last in place).  src_im / dst_im: planar arrays read by the first
+// pass / written by the last.  scale 1/length on the inverse's last pass.
+static hipError_t axis_passes(const fft_plan* plan, int a, bool inv, const void* src, const void* src_im, void* dst,
+                              void* dst_im, void* y, void* y2, int64_t batch, hipStream_t s)
+{
+    const int np = plan->nx_np[a];
+    const int64_t sig_pts = plan->nx_len[a] * plan->nx_stride[a];
+    const int64_t nsig = batch * (plan->n / sig_pts);
+    const int lines = mixed_pass_lines(plan->prec);
+    const void* cur = src;
+    const void* cur_im = src_im;
+    hipError_t e = hipSuccess;
+    for (int q = 0; q < np && e == hipSuccess; ++q) {
+        const PassPlan& pp = plan->passes[3 * a + q];
+        const bool first = q == 0, last = q == np - 1;
+        void* d = last ? dst : q == 0 ? y : (y2 ? y2 : dst);
+        void* d_im = last ? dst_im : nullptr;
+        MixedPassArgs ar{};
+        ar.n = (int)sig_pts;
+        ar.r = pp.r;
+        ar.ns = pp.ns;
+        ar.stride = (int)(sig_pts / pp.r);
+        ar.tiles = (ar.stride + lines - 1) / lines;
+        ar.tr = mixed_pass_threads(pp.ms, pp.r);
+        ar.rmagic = (unsigned)(((uint64_t(1) << 32) + pp.r - 1) / pp.r);
+        ar.conj_in = inv && first;
+        ar.conj_out = inv && last;
+        ar.tdiv = (int)plan->nx_stride[a];
+        ar.twiddle = q > 0;
+        const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, 0};
+        e = launch_mixed_pass(plan->prec, ar, pp.ms, cur, d, nsig, pp.tw, big, 1.0 / (double)plan->nx_len[a], s,
+                              first ? cur_im : nullptr, d_im);
+        cur = d;
+        cur_im = d_im;
+    }
+    return e;
+}
+
 // Rank 2 / 3 with a dimension that is not a power of two: the innermost axis
-// as rank-1 rows (in -> out), then each other axis in passes over `out`: one
-// pass in place; two: out -> Y -> out; three: out -> Y -> out -> out, the last
-// in place (planar: out -> Y -> Y2 -> out, the planar arrays read by an axis's
-// first pass and written by its last).  Workspace: [Y][Y2][the rows' own].
+// as rank-1 rows (in -> out), then each other axis in passes over `out` (the
+// first axis reads `in` when the rows are one point long).  Planar: the rows
+// planar -> planar into out, the axes' first / last passes read / write the
+// planes.  Workspace: [Y][Y2][the rows' own].
 static int run_ndx(const fft_plan* plan, bool inv, const Io& io, int64_t batch, void* workspace, hipStream_t s)
 {
     const bool planar = io.in_im != nullptr;
     const size_t sig = (size_t)batch * (size_t)plan->n * plan->elem;
     const size_t nbuf = ndx_axis_buffers(plan, planar);
     char* y = (char*)workspace;
-    char* y2 = y + sig;
+    char* y2 = planar && nbuf >= 2 ? y + sig : nullptr;
     void* rows_ws = nbuf ? (void*)(y + nbuf * sig) : workspace;
     const int64_t w = plan->dims[plan->rank - 1];
-    const int lines = mixed_pass_lines(plan->prec);
-    int st = FFT_OK;
     if (w > 1) {
-        st = run_1d(plan->inner, inv, io, batch * (plan->n / w), rows_ws, s);
+        const int st = run_1d(plan->inner, inv, io, batch * (plan->n / w), rows_ws, s);
         if (st != FFT_OK) return st;
     }
-    // where the data is before the first axis pass
-    const void* cur = w > 1 ? (const void*)io.out : io.in;
-    const void* cur_im = w > 1 ? (const void*)io.out_im : io.in_im;
     hipError_t e = hipSuccess;
     for (int a = 0; a < plan->nx_k && e == hipSuccess; ++a) {
-        const int np = plan->nx_np[a];
-        const int64_t sig_pts = plan->nx_len[a] * plan->nx_stride[a];  // one signal of this axis
-        const int64_t nsig = batch * (plan->n / sig_pts);
-        for (int q = 0; q < np && e == hipSuccess; ++q) {
-            const PassPlan& pp = plan->passes[3 * a + q];
-            const bool first = q == 0, last = q == np - 1;
-            void* dst;
-            void* dst_im = nullptr;
-            if (last) {
-                dst = io.out;
-                dst_im = io.out_im;
-            } else {
-                dst = q == 0 ? (void*)y : (planar ? (void*)y2 : io.out);
-            }
-            MixedPassArgs ar{};
-            ar.n = (int)sig_pts;
-            ar.r = pp.r;
-            ar.ns = pp.ns;
-            ar.stride = (int)(sig_pts / pp.r);
-            ar.tiles = (ar.stride + lines - 1) / lines;
-            ar.tr = mixed_pass_threads(pp.ms, pp.r);
-            ar.rmagic = (unsigned)(((uint64_t(1) << 32) + pp.r - 1) / pp.r);
-            ar.conj_in = inv && first;
-            ar.conj_out = inv && last;
-            ar.tdiv = (int)plan->nx_stride[a];
-            ar.twiddle = q > 0;
-            const BigTwiddle big{pp.big_hi, pp.big_lo, pp.big_lbits, 0};
-            e = launch_mixed_pass(plan->prec, ar, pp.ms, cur, dst, nsig, pp.tw, big, 1.0 / (double)plan->nx_len[a], s,
-                                  first ? cur_im : nullptr, dst_im);
-            cur = dst;
-            cur_im = dst_im;
-        }
+        const bool from_in = a == 0 && w == 1;
+        e = axis_passes(plan, a, inv, from_in ? io.in : io.out, from_in ? io.in_im : io.out_im, io.out, io.out_im, y,
+                        y2, batch, s);
     }
     if (e != hipSuccess) return hip_fail(e, "rank-2/3 transform launch");
     return FFT_OK;
@@ -1510,17 +1536,76 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     return FFT_OK;
 }
 
+// Real images outside the power-of-two route: rows by the real-row plan of
+// length W (W even or 1), then the H-point column axis (2^a 3^b 5^c 7^d 11^e
+// 13^f) as mixed-radix passes over the W/2 + 1 columns of the half spectrum.
+static int real_2d_any(fft_plan** out_plan, int64_t h, int64_t w, int prec)
+{
+    if (w > 1 && w % 2)
+        return fail(FFT_ERR_NOT_POW2, "image width %lld is odd (real rows take an even length)", (long long)w);
+    const int64_t wc = w / 2 + 1;
+    if (h * wc > max_n(prec))
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "%lld x %lld half-spectrum points exceed %lld", (long long)h,
+                    (long long)wc, (long long)max_n(prec));
+    MixedSchedule chk;
+    int rs[3] = {(int)h, 0, 0};
+    const int np = h == 1 ? 0 : h <= kMixPassMax ? 1 : mixed_split(h, rs);
+    if (h > 1 && (!mixed_factor(h, &chk) || np == 0))
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "image height %lld: columns take 2^a 3^b 5^c 7^d 11^e 13^f points",
+                    (long long)h);
+    fft_plan* p = new (std::nothrow) fft_plan;
+    if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
+    p->rank = 2;
+    p->path = PATH_REAL;
+    p->real_nd = true;
+    p->prec = prec;
+    p->elem = elem_bytes(prec);
+    p->dims[0] = h;
+    p->dims[1] = w;
+    p->n = h * wc;  // points of the half spectrum: the column passes' signal
+    if (h > 1) {
+        p->nx_k = 1;
+        p->nx_len[0] = h;
+        p->nx_stride[0] = wc;
+        p->nx_np[0] = np;
+        int64_t ns = 1;
+        for (int q = 0; q < np; ++q) {
+            PassPlan& pp = p->passes[q];
+            pp.r = rs[q];
+            pp.ns = (int)(ns * wc);
+            mixed_factor(pp.r, &pp.ms);
+            ns *= rs[q];
+        }
+    }
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "hipGetDevice");
+    }
+    int st = fft_plan_create_real(&p->inner, w, prec);
+    for (int q = 0; q < p->nx_np[0] && st == FFT_OK; ++q) {
+        PassPlan& pp = p->passes[q];
+        st = upload(mixed_table(pp.ms), prec, &p->pass_tw[q]);
+        pp.tw = p->pass_tw[q];
+        if (st == FFT_OK && q > 0)
+            st = upload_big_any(pp.ns / wc * pp.r, prec, &pp.big_hi, &pp.big_lo, &pp.big_lbits);
+    }
+    if (st != FFT_OK) {
+        free_plan(p);
+        return st;
+    }
+    *out_plan = p;
+    return FFT_OK;
+}
+
 int fft_plan_create_real_2d(fft_plan** out_plan, int64_t h, int64_t w, int prec)
 {
     if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
     *out_plan = nullptr;
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
     if (h < 1 || w < 1) return fail(FFT_ERR_INVALID_ARG, "dims %lld x %lld < 1", (long long)h, (long long)w);
-    if (!is_pow2(h) || !is_pow2(w))
-        return fail(FFT_ERR_NOT_POW2, "dims %lld x %lld are not powers of two", (long long)h, (long long)w);
-    if (h > max_lds_n(prec) || w > 2 * max_lds_n(prec))
-        return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims %lld x %lld exceed %lld x %lld", (long long)h, (long long)w,
-                    (long long)max_lds_n(prec), (long long)(2 * max_lds_n(prec)));
+    if (!(is_pow2(h) && is_pow2(w) && h <= max_lds_n(prec) && w <= 2 * max_lds_n(prec)))
+        return real_2d_any(out_plan, h, w, prec);
     fft_plan* p = new (std::nothrow) fft_plan;
     if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
     p->rank = 2;
@@ -1597,6 +1682,33 @@ static int real_done(hipError_t e, const char* what, hipStream_t s)
     return FFT_OK;
 }
 
+// Real images outside the power-of-two route.  R2C: the real rows into out,
+// then the column passes over out.  C2R: the inverse column passes from in
+// into the workspace's Z, then the real rows from Z.  Workspace: [Z][Y][the
+// rows' own].
+static int exec_real_2d_any(const fft_plan* plan, bool c2r, const void* in, void* out, int64_t batch,
+                            void* workspace, hipStream_t s)
+{
+    const int64_t h = plan->dims[0];
+    const size_t half = (size_t)batch * (size_t)plan->n * plan->elem;
+    const bool cols = plan->nx_k > 0;
+    char* z = (char*)workspace;
+    char* y = cols && plan->nx_np[0] >= 2 ? z + half : nullptr;
+    void* rows_ws = cols ? (void*)(z + half * (y ? 2 : 1)) : workspace;
+    const char* what = c2r ? "fft_exec_c2r" : "fft_exec_r2c";
+    hipError_t e = hipSuccess;
+    if (!c2r) {
+        int st = fft_exec_r2c(plan->inner, in, out, batch * h, rows_ws, s);
+        if (st != FFT_OK) return st;
+        if (cols) e = axis_passes(plan, 0, false, out, nullptr, out, nullptr, y, nullptr, batch, s);
+        return real_done(e, what, s);
+    }
+    if (!cols) return fft_exec_c2r(plan->inner, in, out, batch * h, rows_ws, s);
+    e = axis_passes(plan, 0, true, in, nullptr, z, nullptr, y, nullptr, batch, s);
+    if (e != hipSuccess) return hip_fail(e, what);
+    return fft_exec_c2r(plan->inner, z, out, batch * h, rows_ws, s);
+}
+
 // Real images [batch][H][W] <-> [batch][H][W/2 + 1]: the rows (real-row
 // kernels), then the columns of the half spectrum (one column per lane).
 static int exec_real_2d(const fft_plan* plan, bool c2r, const void* in, void* out, int64_t batch, void* workspace,
@@ -1659,10 +1771,11 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
     bool noop = false;
     size_t rbytes = 0, hbytes = 0;
     if (plan) real_sizes(plan, &rbytes, &hbytes);
-    const bool need_ws = plan && (plan->rank == 1 || plan->logf > 0);
+    const bool need_ws = plan && (plan->rank == 1 || plan->logf > 0 || plan->real_nd);
     int st = check_real_exec(plan, in, rbytes, out, hbytes, batch, workspace, need_ws, &noop);
     if (st != FFT_OK || noop) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (plan->real_nd) return exec_real_2d_any(plan, false, in, out, batch, workspace, s);
     if (plan->rank == 2) return exec_real_2d(plan, false, in, out, batch, workspace, s);
     hipError_t e;
     if (plan->n == 1) {
@@ -1691,6 +1804,7 @@ int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch,
     int st = check_real_exec(plan, in, hbytes, out, rbytes, batch, workspace, true, &noop);
     if (st != FFT_OK || noop) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (plan->real_nd) return exec_real_2d_any(plan, true, in, out, batch, workspace, s);
     if (plan->rank == 2) return exec_real_2d(plan, true, in, out, batch, workspace, s);
     hipError_t e;
     if (plan->n == 1) {

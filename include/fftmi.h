@@ -256,14 +256,20 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
 int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
 
 /*
- * Plan for real images [H][W] (H, W powers of two, 1 <= H <= FFT_MAX_LDS_N_*,
- * 1 <= W <= 2 FFT_MAX_LDS_N_*): the 2D transform's columns 0 .. W/2, the rest
+ * Plan for real images [H][W] -- H, W powers of two, 1 <= H <= FFT_MAX_LDS_N_*,
+ * 1 <= W <= 2 FFT_MAX_LDS_N_*: the 2D transform's columns 0 .. W/2, the rest
  * following from X[u][v] = conj X[-u][-v].  The rows go through the real-row
  * kernels, then the H-point column transforms run over the W/2 + 1 columns of
  * the half spectrum (one column per lane; for H > 512 a radix-F column stage
  * first, as for complex plans).  The same fft_exec_r2c / fft_exec_c2r calls
  * take it; fft_plan_describe shows path=real2d.
- * Errors: INVALID_ARG, NOT_POW2, UNSUPPORTED_SIZE, DEVICE.
+ * Other shapes: W even (or 1), H = 2^a 3^b 5^c 7^d 11^e 13^f, at most
+ * FFT_MAX_N_* points in the half spectrum: the rows by the real-row plan of
+ * length W (fft_plan_create_real), then the column axis as mixed-radix
+ * super-stage passes over the half spectrum (path=real2dmixed); a workspace of
+ * fft_workspace_size bytes on every call (C2R runs the columns into it and
+ * leaves its input as it was).
+ * Errors: INVALID_ARG, NOT_POW2 (odd W), UNSUPPORTED_SIZE, DEVICE.
  */
 int fft_plan_create_real_2d(fft_plan** plan, int64_t h, int64_t w, int prec);
 

@@ -210,12 +210,15 @@ def irfft(X, n: int) -> np.ndarray:
 
 def rfft2(x) -> np.ndarray:
     """Columns 0 .. W/2 of the 2D transform of real [..., H, W] images:
-    [..., H, W // 2 + 1] complex128."""
+    [..., H, W // 2 + 1] complex128 (``fft2`` for power-of-two shapes, else
+    ``dftn``)."""
     x = np.asarray(x)
     if np.iscomplexobj(x):
         raise TypeError("rfft2 takes real images")
-    w = x.shape[-1]
-    return fft2(x.astype(np.float64))[..., : w // 2 + 1]
+    h, w = x.shape[-2], x.shape[-1]
+    pow2 = h & (h - 1) == 0 and w & (w - 1) == 0
+    full = fft2(x.astype(np.float64)) if pow2 else dftn(x.astype(np.float64), 2)
+    return full[..., : w // 2 + 1]
 
 
 def irfft2(X, shape) -> np.ndarray:
@@ -227,7 +230,8 @@ def irfft2(X, shape) -> np.ndarray:
     X = _as_c128(X)
     if X.shape[-2:] != (h, w // 2 + 1):
         raise ValueError("irfft2 of %dx%d takes %dx%d values" % (h, w, h, w // 2 + 1))
-    cols = np.swapaxes(ifft(np.ascontiguousarray(np.swapaxes(X, -1, -2))), -1, -2)
+    col_t = np.ascontiguousarray(np.swapaxes(X, -1, -2))
+    cols = np.swapaxes(ifft(col_t) if h & (h - 1) == 0 else dft(col_t, inverse=True), -1, -2)
     return irfft(np.ascontiguousarray(cols), w)
 
 

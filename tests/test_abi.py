@@ -179,12 +179,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     (0, 8, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 0, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 8, 3, fm.FFT_ERR_INVALID_ARG),
-    (6, 8, 0, fm.FFT_ERR_NOT_POW2),
-    (8, 12, 1, fm.FFT_ERR_NOT_POW2),
-    (16384, 8, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (8, 32768, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (8192, 8, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (8, 16384, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (8, 7, 0, fm.FFT_ERR_NOT_POW2),          # odd width: real rows take an even length
+    (6, 15, 1, fm.FFT_ERR_NOT_POW2),
+    (97, 8, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),    # height with a prime factor above 13
+    (51, 16, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (65536, 2048, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # half spectrum beyond 2^26 points
+    (16384, 2048, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),  # beyond 2^24 points
 ])
 def test_real_2d_plan_create_rejects(h, w, prec, status):
     hd = ctypes.c_void_p(12345)

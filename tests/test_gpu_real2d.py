@@ -52,6 +52,46 @@ def test_real_2d(dev, h, w, dtype, batch):
     assert rel_rms_rows(_flat(back), _flat(x_np)).max() <= 2 * tol
 
 
+# Shapes outside the power-of-two route: the real rows of any even width by
+# their route, the H-point column axis as mixed-radix passes over the half
+# spectrum.
+CASES_ANY = [
+    (100, 8, torch.float32, 2), (7, 100, torch.float32, 2), (12, 30, torch.float32, 3), (1, 100, torch.float32, 2),
+    (100, 1, torch.float32, 2), (30, 194, torch.float32, 2), (1000, 600, torch.float32, 1),
+    (360, 640, torch.float32, 1), (16384, 8, torch.float32, 1), (100, 10, torch.float64, 2),
+    (60, 1000, torch.float64, 1),
+]
+
+
+@pytest.mark.parametrize("h,w,dtype,batch", CASES_ANY, ids=lambda v: str(v))
+def test_real_2d_any_shape(dev, h, w, dtype, batch):
+    print("case %dx%d %s batch=%d" % (h, w, dtype, batch), flush=True)
+    npdt = np.float32 if dtype == torch.float32 else np.float64
+    cdt = np.complex64 if dtype == torch.float32 else np.complex128
+    x_np = wl.real_normal(h * w, batch, seed=h + 5 * w, dtype=npdt).reshape(batch, h, w)
+    plan = fm.RealPlan((h, w), dtype)
+    assert "path=real2dmixed" in plan.describe()
+    x = torch.from_numpy(x_np).to(dev)
+    weff = w
+    if w > 1 and "bluestein" in fm.fft_plan_query(1, [w // 2], 0 if dtype == torch.float32 else 1):
+        m = 1
+        while m < w - 1:
+            m *= 2
+        weff = 2 * m
+    tol = fft_tol(h * weff, dtype == torch.float64)
+    oracle.set_threads(8)
+    X = plan.rfft(x)
+    assert X.shape == (batch, h, w // 2 + 1)
+    assert rel_rms_rows(_flat(X.cpu().numpy()), _flat(oracle.rfft2(x_np))).max() <= tol
+    S = wl.batched_normal(h * (w // 2 + 1), batch, seed=h + w + 1, dtype=cdt).reshape(batch, h, w // 2 + 1)
+    S_dev = torch.from_numpy(S).to(dev)
+    y = plan.irfft(S_dev).cpu().numpy()
+    assert rel_rms_rows(_flat(y), _flat(oracle.irfft2(S, (h, w)))).max() <= tol
+    assert torch.equal(S_dev.cpu(), torch.from_numpy(S))  # the C2R input is left as it was
+    back = plan.irfft(X).cpu().numpy()
+    assert rel_rms_rows(_flat(back), _flat(x_np)).max() <= 2 * tol
+
+
 def test_real_2d_closed_form_and_errors(dev):
     h, w = 1024, 256
     yy = np.arange(h)[:, None]

@@ -458,7 +458,8 @@ def test_rfft_closed_forms_and_hermitian_half():
     assert np.abs(imp - want).max() < 1e-13
 
 
-@pytest.mark.parametrize("h,w", [(1, 2), (2, 1 << 1), (4, 8), (16, 64), (64, 2), (128, 256)])
+@pytest.mark.parametrize("h,w", [(1, 2), (2, 1 << 1), (4, 8), (16, 64), (64, 2), (128, 256),
+                                 (3, 10), (12, 30), (100, 8), (7, 100), (1, 6)])
 def test_rfft2_irfft2_match_numpy(h, w):
     rng = np.random.default_rng(h * 1000 + w)
     x = rng.standard_normal((2, h, w))
