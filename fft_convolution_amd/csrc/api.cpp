@@ -1071,9 +1071,9 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
             const size_t sig = (size_t)batch * (size_t)plan->n * plan->elem;
             void* ws2 = (char*)workspace + sig;
             const void* src = io.in;
-            const int lines = mixed_pass_lines(plan->prec);
             for (int q = 0; q < plan->npass && e == hipSuccess; ++q) {
                 const PassPlan& pp = plan->passes[q];
+                const int lines = mixed_pass_lines(plan->prec, pp.r);
                 const bool last = q == plan->npass - 1;
                 void* dst = q == 0 ? workspace : (last || !planar) ? io.out : ws2;
                 MixedPassArgs a{};
@@ -1192,12 +1192,12 @@ static hipError_t axis_passes(const fft_plan* plan, int a, bool inv, const void*
     const int np = plan->nx_np[a];
     const int64_t sig_pts = plan->nx_len[a] * plan->nx_stride[a];
     const int64_t nsig = batch * (plan->n / sig_pts);
-    const int lines = mixed_pass_lines(plan->prec);
     const void* cur = src;
     const void* cur_im = src_im;
     hipError_t e = hipSuccess;
     for (int q = 0; q < np && e == hipSuccess; ++q) {
         const PassPlan& pp = plan->passes[3 * a + q];
+        const int lines = mixed_pass_lines(plan->prec, pp.r);
         const bool first = q == 0, last = q == np - 1;
         void* d = last ? dst : q == 0 ? y : (y2 ? y2 : dst);
         void* d_im = last ? dst_im : nullptr;

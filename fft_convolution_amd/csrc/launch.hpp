@@ -49,7 +49,8 @@ int mixed_max_n(int prec);
 // One mixed-radix super-stage pass (mixed.hip) over `batch` signals of n
 // points: radix r (<= 512, its stage schedule `ms`, twiddle table `tw` of
 // that schedule), span ns, stride n / r, tiles = ceil(stride / lines) per
-// signal, tr threads per line (mixed_pass_threads), rmagic = ceil(2^32 / r).
+// signal (lines = mixed_pass_lines(prec, r)), tr threads per line
+// (mixed_pass_threads), rmagic = ceil(2^32 / r).
 // Twiddles (twiddle != 0): w_M^{q (k / tdiv)} from `big`, k = j mod ns, M =
 // r ns / tdiv; tdiv = 1 for a 1D transform, the axis stride for a pass of
 // one axis of an image or volume (ns = tdiv ns_axis: the pass runs the
@@ -64,7 +65,7 @@ struct MixedPassArgs {
     int tdiv, twiddle;
 };
 int mixed_pass_threads(const MixedSchedule& ms, int r);
-int mixed_pass_lines(int prec);
+int mixed_pass_lines(int prec, int r);  // butterflies per tile of a radix-r pass
 hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedule& ms, const void* in, void* out,
                              int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t stream,
                              const void* in_im = nullptr, void* out_im = nullptr);

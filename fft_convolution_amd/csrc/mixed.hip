@@ -447,8 +447,8 @@ int mixed_max_n(int prec) { return prec == 0 ? mixed_max_points<float2>() : mixe
 // R-point DFT (the mixed-radix stages above, on a line of the tile), outputs at
 // g Ns R + k + q Ns (g = j / Ns).
 //
-// A workgroup takes LINES consecutive butterflies j (a 128-byte segment of
-// elements for each q); element q of line c lives in LDS at q (LINES + 1) + c
+// A workgroup takes LINES consecutive butterflies j (a 128-, 256- or 512-byte
+// segment of elements for each q, by radix); element q of line c lives in LDS at q (LINES + 1) + c
 // (the extra slot per element row keeps both store orders free of bank
 // conflicts).  The first stage of the R-point transform reads its inputs from
 // HBM; the first pass (Ns = 1) writes each line's outputs j R + q, so the
@@ -525,13 +525,18 @@ template <typename V> constexpr int mp_lines() { return 128 / (int)sizeof(V); }
 // (LINES R over a workgroup of LINES tr threads), MP_CHUNK at a time.
 constexpr int MP_QMAX = 16;
 constexpr int MP_CHUNK = 8;
+// Tile widths: 512 bytes of elements per q up to radix MP_R4, 256 bytes up to
+// MP_R2, 128 bytes beyond (LDS (lines + 1) r elements: sized at launch up to
+// MP_R2, a static radix-512 class beyond).
+constexpr int MP_R4 = 64;
+constexpr int MP_R2 = 256;
 
-template <typename V, bool WIDE, int RCAP, typename IN, typename OUT>
-__global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, OUT out, MixedPassArgs a, MixedSchedule ms,
+template <typename V, int LN, bool WIDE, int RCAP, typename IN, typename OUT>
+__global__ __launch_bounds__(LN * 64 < 1024 ? LN * 64 : 1024) void mixed_pass_kernel(IN in, OUT out, MixedPassArgs a, MixedSchedule ms,
                                                           const V* __restrict__ tw, AnyTw<V> big,
                                                           typename real_of<V>::type scale)
 {
-    constexpr int LINES = mp_lines<V>();
+    constexpr int LINES = LN;
     constexpr int P = LINES + 1;
     // RCAP 0: LDS sized at launch to the radix (short lines leave room for
     // many workgroups per CU); otherwise a static class
@@ -604,8 +609,7 @@ __global__ __launch_bounds__(mp_lines<V>() * 64) void mixed_pass_kernel(IN in, O
     }
 }
 
-// LDS: exactly (lines + 1) r elements up to radix 128 (set at launch), a
-// static class of radix 512 beyond.
+// One launch of a pass: the tile width (and LDS sizing) class of its radix.
 template <typename V, bool WIDE, typename IN, typename OUT>
 static hipError_t mixed_pass_t(IN in, OUT out, int64_t batch, const MixedPassArgs& a, const MixedSchedule& ms,
                                const void* tw, const BigTwiddle& bt, double scale, hipStream_t s)
@@ -614,14 +618,19 @@ static hipError_t mixed_pass_t(IN in, OUT out, int64_t batch, const MixedPassArg
     const int64_t blocks = (int64_t)a.tiles * batch;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const AnyTw<V> big{(const V*)bt.hi, (const V*)bt.lo, bt.lbits};
-    const dim3 grid((unsigned)blocks), block(mp_lines<V>() * a.tr);
-    if (a.r <= 128)
-        hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 0, IN, OUT>), grid, block,
-                           (unsigned)((mp_lines<V>() + 1) * a.r * (int)sizeof(V)), s, in, out, a, ms, (const V*)tw,
-                           big, (Rl)scale);
+    constexpr int L1 = mp_lines<V>(), L2 = 2 * L1, L4 = 4 * L1;
+    const dim3 grid((unsigned)blocks);
+    if (a.r <= MP_R4)
+        hipLaunchKernelGGL((mixed_pass_kernel<V, L4, WIDE, 0, IN, OUT>), grid, dim3(L4 * a.tr),
+                           (unsigned)((L4 + 1) * a.r * (int)sizeof(V)), s, in, out, a, ms, (const V*)tw, big,
+                           (Rl)scale);
+    else if (a.r <= MP_R2)
+        hipLaunchKernelGGL((mixed_pass_kernel<V, L2, WIDE, 0, IN, OUT>), grid, dim3(L2 * a.tr),
+                           (unsigned)((L2 + 1) * a.r * (int)sizeof(V)), s, in, out, a, ms, (const V*)tw, big,
+                           (Rl)scale);
     else
-        hipLaunchKernelGGL((mixed_pass_kernel<V, WIDE, 512, IN, OUT>), grid, block, 0, s, in, out, a, ms,
-                           (const V*)tw, big, (Rl)scale);
+        hipLaunchKernelGGL((mixed_pass_kernel<V, L1, WIDE, 512, IN, OUT>), grid, dim3(L1 * a.tr), 0, s, in, out, a,
+                           ms, (const V*)tw, big, (Rl)scale);
     return hipGetLastError();
 }
 
@@ -658,7 +667,11 @@ int mixed_pass_threads(const MixedSchedule& ms, int r)
     return tr;
 }
 
-int mixed_pass_lines(int prec) { return prec == 0 ? mp_lines<float2>() : mp_lines<double2>(); }
+int mixed_pass_lines(int prec, int r)
+{
+    const int base = prec == 0 ? mp_lines<float2>() : mp_lines<double2>();
+    return r <= MP_R4 ? 4 * base : r <= MP_R2 ? 2 * base : base;
+}
 
 hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedule& ms, const void* in, void* out,
                              int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t s,
@@ -667,7 +680,7 @@ hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedu
     if (a.r > 512 || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr > 64 ||
         (a.r + a.tr - 1) / a.tr > MP_QMAX ||
         a.ns < 1 || a.tdiv < 1 || a.ns % a.tdiv || (int64_t)a.stride * a.r != a.n ||
-        a.tiles * (int64_t)mixed_pass_lines(prec) < a.stride ||
+        a.tiles * (int64_t)mixed_pass_lines(prec, a.r) < a.stride || a.tr * mixed_pass_lines(prec, a.r) > 1024 ||
         a.rmagic != (unsigned)(((uint64_t(1) << 32) + a.r - 1) / a.r))
         return hipErrorInvalidValue;
     const Io io{in, in_im, out, out_im};

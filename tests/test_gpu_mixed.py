@@ -133,11 +133,15 @@ def test_mixed_every_smooth_length(dev, dtype, limit):
     assert not bad, bad
 
 
-# Beyond one kernel: 2-3 mixed-radix super-stage passes (radix <= 512 each).
+# Beyond one kernel: 2-3 mixed-radix super-stage passes (radix <= 512 each),
+# radices from 50 to 512 in both precisions (each tile width of the pass
+# kernel: radix <= 64, <= 256, beyond).
 MIXPASS = [(9000, torch.complex64, 3), (10000, torch.complex64, 2), (12288, torch.complex64, 2),
-           (30030, torch.complex64, 2), (3 * 65536, torch.complex64, 1), (10 ** 6, torch.complex64, 1),
-           (3 << 20, torch.complex64, 1), (6000, torch.complex128, 3), (10000, torch.complex128, 2),
-           (5 ** 9, torch.complex128, 1), (8 * 10 ** 6, torch.complex64, 1)]
+           (30030, torch.complex64, 2), (60060, torch.complex64, 1), (3 * 65536, torch.complex64, 1),
+           (10 ** 6, torch.complex64, 1), (3 << 20, torch.complex64, 1), (6000, torch.complex128, 3),
+           (4608, torch.complex128, 3), (5000, torch.complex128, 2), (10000, torch.complex128, 2),
+           (30030, torch.complex128, 1), (3 * 65536, torch.complex128, 1), (5 ** 9, torch.complex128, 1),
+           (8 * 10 ** 6, torch.complex64, 1)]
 
 
 @pytest.mark.parametrize("n,dtype,batch", MIXPASS)
