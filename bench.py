@@ -20,6 +20,8 @@ Prints ONE JSON line with:
              as a fraction of the copy's (the practical ceiling)
   rotated    the same steps cycling over --rotate buffer sets (default 3), so
              that no step finds its input in the 256 MB MALL
+  torch_fft  (--compare-torch) the same transform by torch.fft on the same
+             input (mean of per-call event durations) and its ratio to step_us mean
 
 Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
@@ -206,6 +208,47 @@ def setup_workload(name, dev, fm, torch, sets=1):
     raise SystemExit("unknown workload %s" % name)
 
 
+def torch_fft_time(name, info, torch, reps):
+    """The same transform by torch.fft (the ROCm vendor FFT behind it) on the
+    same resident input, timed like the steps: a point of comparison only,
+    never a path of this library.  Poly-mul: forward transforms of a and b
+    (fp64, length N), their product, the inverse, rounded to int64."""
+    bufs = info["keep"][1]
+    if name.startswith("polymul"):
+        a, b = bufs[0][0], bufs[0][1]
+        n, m = info["n"], 2 * info["length"] - 1
+
+        def fn():
+            fa = torch.fft.fft(a.to(torch.float64), n=n)
+            fb = torch.fft.fft(b.to(torch.float64), n=n)
+            return torch.fft.ifft(fa * fb).real[..., :m].round().to(torch.int64)
+        what = "torch.fft: fft(a), fft(b), product, ifft, round to int64"
+    else:
+        x = bufs[0][0]
+        if name.startswith("c2c3d"):
+            fn, what = (lambda: torch.fft.fftn(x, dim=(-3, -2, -1))), "torch.fft.fftn over the last 3 dims"
+        elif name.startswith("c2c2d"):
+            fn, what = (lambda: torch.fft.fft2(x)), "torch.fft.fft2"
+        elif name.startswith("r2c2d"):
+            fn, what = (lambda: torch.fft.rfft2(x)), "torch.fft.rfft2"
+        elif name.startswith("r2c"):
+            fn, what = (lambda: torch.fft.rfft(x)), "torch.fft.rfft"
+        else:
+            fn, what = (lambda: torch.fft.fft(x)), "torch.fft.fft"
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    # each call bracketed by its own pair of events, as the steps are
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in marks:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    mean = sum(e0.elapsed_time(e1) for e0, e1 in marks) / reps
+    return {"what": what, "call_us_mean": round(mean * 1e3, 2), "calls": reps}
+
+
 def cpu_baseline(name, info, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -292,6 +335,8 @@ def main():
                     help="buffer sets for the extra rotated-buffer timing (1 = none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a device-to-device copy of the input's size (for counter scaling)")
+    ap.add_argument("--compare-torch", action="store_true",
+                    help="also time torch.fft on the same input (a comparison point, not part of the step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -408,6 +453,10 @@ def main():
         out["roofline"] = None
         out["roofline_note"] = ("%d kernels per step; per-kernel durations are in the rocprofv3 "
                                 "summaries under profiles/" % info["kernels"])
+    if args.compare_torch:
+        tf = torch_fft_time(args.workload, info, torch, reps=args.steps)
+        tf["speedup"] = round(tf["call_us_mean"] / (launch_ms * 1e3), 3)  # against step_us mean
+        out["torch_fft"] = tf
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, info, args.cpu_budget)
     print(json.dumps(out), flush=True)
