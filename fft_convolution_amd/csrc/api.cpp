@@ -176,21 +176,29 @@ std::vector<double> mixed_table(const MixedSchedule& ms)
     return t;
 }
 
-// Radices of a multi-pass mixed-radix plan: N = r[0] r[1] (r[2]), each at
-// most kMixPassMax, as few passes as possible, then as even as possible (the
-// largest smallest factor), larger first.  Returns the pass count, 0 if none.
+// Radices of a multi-pass mixed-radix plan: N = r[0] r[1] (r[2]), as few
+// passes as possible, then as even as possible (the largest smallest factor),
+// larger first; each radix at most kMixPassMax, or up to kMixPassWide where
+// that saves a pass (two passes instead of three; one pass for an axis) and
+// the radix has no factor 11 or 13 (whose wide-pass kernels would spill).
+// Returns the pass count, 0 if none.
 constexpr int kMixPassMax = 512;
-int mixed_split(int64_t n, int* r)
+constexpr int kMixPassWide = 1024;
+static bool pass_radix_ok(int64_t r, int cap)
+{
+    return r <= kMixPassMax || (r <= cap && r % 11 != 0 && r % 13 != 0);
+}
+static int mixed_split_cap(int64_t n, int cap, int np_max, int* r)
 {
     std::vector<int64_t> divs;
-    for (int64_t d = 2; d <= kMixPassMax && d < n; ++d)
-        if (n % d == 0) divs.push_back(d);
-    for (int np = 2; np <= 3; ++np) {
+    for (int64_t d = 2; d <= cap && d < n; ++d)
+        if (n % d == 0 && pass_radix_ok(d, cap)) divs.push_back(d);
+    for (int np = 2; np <= np_max; ++np) {
         int64_t best[3] = {0, 0, 0}, best_min = 0;
         for (int64_t a : divs) {
             if (np == 2) {
                 const int64_t b = n / a;
-                if (b >= 2 && b <= kMixPassMax && std::min(a, b) > best_min) {
+                if (b >= 2 && pass_radix_ok(b, cap) && std::min(a, b) > best_min) {
                     best_min = std::min(a, b);
                     best[0] = a;
                     best[1] = b;
@@ -200,7 +208,7 @@ int mixed_split(int64_t n, int* r)
             for (int64_t b : divs) {
                 if ((n / a) % b) continue;
                 const int64_t c = n / a / b;
-                if (c < 2 || c > kMixPassMax) continue;
+                if (c < 2 || !pass_radix_ok(c, cap)) continue;
                 const int64_t m = std::min(a, std::min(b, c));
                 if (m > best_min) {
                     best_min = m;
@@ -217,6 +225,23 @@ int mixed_split(int64_t n, int* r)
         }
     }
     return 0;
+}
+
+int mixed_split(int64_t n, int* r)
+{
+    if (mixed_split_cap(n, kMixPassMax, 2, r)) return 2;
+    if (mixed_split_cap(n, kMixPassWide, 2, r)) return 2;
+    return mixed_split_cap(n, kMixPassMax, 3, r);
+}
+
+// Passes of an axis of len points (len > 1): one up to kMixPassWide.
+static int axis_split(int64_t len, int* r)
+{
+    if (pass_radix_ok(len, kMixPassWide)) {
+        r[0] = (int)len;
+        return 1;
+    }
+    return mixed_split(len, r);
 }
 
 // Host copy of the stage tables of radix_plan.hpp for N = 2^logn, as
@@ -536,7 +561,7 @@ int ndx_layout(fft_plan* p, int rank, const int64_t* dims)
             p->nx_len[a] = len;
             p->nx_stride[a] = stride;
             int rs[3] = {(int)len, 0, 0};
-            const int np = len <= kMixPassMax ? 1 : mixed_split(len, rs);
+            const int np = axis_split(len, rs);
             if (np == 0) return fail(FFT_ERR_UNSUPPORTED_SIZE, "no passes for an axis of %lld points", (long long)len);
             p->nx_np[a] = np;
             int64_t ns = 1;
@@ -855,7 +880,7 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
             if (dims[d] == 1) continue;
             MixedSchedule ms;
             int rs[3];
-            if (!mixed_factor(dims[d], &ms) || (dims[d] > kMixPassMax && mixed_split(dims[d], rs) == 0))
+            if (!mixed_factor(dims[d], &ms) || axis_split(dims[d], rs) == 0)
                 return fail(FFT_ERR_UNSUPPORTED_SIZE,
                             "dims[%d] = %lld: axes other than the innermost take 2^a 3^b 5^c 7^d 11^e 13^f points",
                             d, (long long)dims[d]);
@@ -1549,7 +1574,7 @@ static int real_2d_any(fft_plan** out_plan, int64_t h, int64_t w, int prec)
                     (long long)wc, (long long)max_n(prec));
     MixedSchedule chk;
     int rs[3] = {(int)h, 0, 0};
-    const int np = h == 1 ? 0 : h <= kMixPassMax ? 1 : mixed_split(h, rs);
+    const int np = h == 1 ? 0 : axis_split(h, rs);
     if (h > 1 && (!mixed_factor(h, &chk) || np == 0))
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "image height %lld: columns take 2^a 3^b 5^c 7^d 11^e 13^f points",
                     (long long)h);

@@ -47,7 +47,8 @@ hipError_t launch_mixed_rows(int prec, int n, const MixedSchedule& ms, bool inve
 int mixed_max_n(int prec);
 
 // One mixed-radix super-stage pass (mixed.hip) over `batch` signals of n
-// points: radix r (<= 512, its stage schedule `ms`, twiddle table `tw` of
+// points: radix r (<= 1024, above 512 without a radix-11 or -13 stage; its
+// stage schedule `ms`, twiddle table `tw` of
 // that schedule), span ns, stride n / r, tiles = ceil(stride / lines) per
 // signal (lines = mixed_pass_lines(prec, r)), tr threads per line
 // (mixed_pass_threads), rmagic = ceil(2^32 / r).

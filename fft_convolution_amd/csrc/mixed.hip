@@ -192,8 +192,8 @@ __device__ __forceinline__ void seg_store(const COut<V, PL>& out, int64_t base, 
 
 // Butterflies per thread and stage at most (about 8 elements a thread); the
 // launcher gives a row enough threads for every stage of its schedule.
-__host__ __device__ constexpr int mixed_bmax_of(int r) { return (8 + r - 1) / r; }
-template <int R> constexpr int mixed_bmax() { return mixed_bmax_of(R); }
+__host__ __device__ constexpr int mixed_bmax_of(int r, int bm = 8) { return (bm + r - 1) / r; }
+template <int R, int BM = 8> constexpr int mixed_bmax() { return mixed_bmax_of(R, BM); }
 
 // Where a stage reads and writes.  Rows of 64 threads or more (a wave within
 // one row): the first stage reads its butterflies straight from the input rows
@@ -243,11 +243,11 @@ template <typename V, bool PL, bool INV> struct MixedRows {
 // writes its outputs through io.store, instead of the LDS row.  ES: LDS slots
 // between consecutive elements of a row (1 for a row of its own; the tile
 // width where rows are interleaved).
-template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, int ES = 1, typename V, typename IO>
+template <int R, bool FIRST, bool FROM_IN, bool TO_OUT, int ES = 1, int BM = 8, typename V, typename IO>
 __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, int ns, unsigned magic,
                                             const V* __restrict__ tw, const IO& io)
 {
-    constexpr int B = mixed_bmax<R>();
+    constexpr int B = mixed_bmax<R, BM>();
     constexpr int S = mixed_tw_slots(R);
     constexpr int P = 16 / (int)sizeof(V);           // table entries per 16-byte load
     constexpr int NL = ((R - 1 + P - 1) / P) * P;    // entries loaded per row (<= S)
@@ -303,11 +303,11 @@ __device__ __forceinline__ void mixed_stage(V* row, int tl, int tr, int stride, 
 // WIDE: the schedule may hold radices 11 and 13, whose DFTs keep more values
 // live; kernels for the other schedules are compiled without them so that
 // they keep their lower register count.
-template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, int ES = 1, typename V, typename IO>
+template <bool WIDE, bool FIRST, bool FROM_IN, bool TO_OUT, int ES = 1, int BM = 8, typename V, typename IO>
 __device__ __forceinline__ void mixed_stage_any(int r, V* row, int tl, int tr, int stride, int ns, unsigned magic,
                                                 const V* __restrict__ tw, const IO& io)
 {
-#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, ES>(row, tl, tr, stride, ns, magic, tw, io)
+#define MX_STAGE(R) mixed_stage<R, FIRST, FROM_IN, TO_OUT, ES, BM>(row, tl, tr, stride, ns, magic, tw, io)
     if constexpr (WIDE) {
         if (r == 11) {
             MX_STAGE(11);
@@ -442,7 +442,7 @@ int mixed_max_n(int prec) { return prec == 0 ? mixed_max_points<float2>() : mixe
 
 // ---------------------------------------------------------------------------
 // Rows beyond one workgroup: N = R_0 R_1 ... as Stockham super-stages, one
-// pass each (radix R <= 512, span Ns = R_0 ... R_{p-1}): for every butterfly
+// pass each (radix R <= 1024, span Ns = R_0 ... R_{p-1}): for every butterfly
 // j < N/R, inputs x[j + q N/R] times w_{Ns R}^{q k} (k = j mod Ns), the
 // R-point DFT (the mixed-radix stages above, on a line of the tile), outputs at
 // g Ns R + k + q Ns (g = j / Ns).
@@ -527,9 +527,12 @@ constexpr int MP_QMAX = 16;
 constexpr int MP_CHUNK = 8;
 // Tile widths: 512 bytes of elements per q up to radix MP_R4, 256 bytes up to
 // MP_R2, 128 bytes beyond (LDS (lines + 1) r elements: sized at launch up to
-// MP_R2, a static radix-512 class beyond).
+// MP_R2, static classes of radix 512 and MP_RMAX beyond).  Threads per line:
+// up to 64, with up to twice the butterflies per thread in the widest class,
+// which takes no radix-11 or -13 stage (their registers would spill).
 constexpr int MP_R4 = 64;
 constexpr int MP_R2 = 256;
+constexpr int MP_RMAX = 1024;
 
 template <typename V, int LN, bool WIDE, int RCAP, typename IN, typename OUT>
 __global__ __launch_bounds__(LN * 64 < 1024 ? LN * 64 : 1024) void mixed_pass_kernel(IN in, OUT out, MixedPassArgs a, MixedSchedule ms,
@@ -556,23 +559,24 @@ __global__ __launch_bounds__(LN * 64 < 1024 ? LN * 64 : 1024) void mixed_pass_ke
     // g Ns R + k + q Ns); the stages between go through LDS.
     V* row = lds + c;
     const int last = ms.nst - 1;
+    constexpr int BM = RCAP > 512 ? 16 : 8;  // butterfly budget per thread and stage (x R elements)
     auto stages = [&](const auto& io) {
         if (a.ns > 1) {
             if (last == 0) {
-                mixed_stage_any<WIDE, true, true, true, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+                mixed_stage_any<WIDE, true, true, true, P, BM>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
                 return;
             }
-            mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+            mixed_stage_any<WIDE, true, true, false, P, BM>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
             for (int s = 1; s < last; ++s)
-                mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
+                mixed_stage_any<WIDE, false, false, false, P, BM>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
                                                               ms.magic[s], tw + ms.twoff[s], io);
-            mixed_stage_any<WIDE, false, false, true, P>(ms.radix[last], row, tl, a.tr, ms.stride[last],
+            mixed_stage_any<WIDE, false, false, true, P, BM>(ms.radix[last], row, tl, a.tr, ms.stride[last],
                                                          ms.ns[last], ms.magic[last], tw + ms.twoff[last], io);
             return;
         }
-        mixed_stage_any<WIDE, true, true, false, P>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
+        mixed_stage_any<WIDE, true, true, false, P, BM>(ms.radix[0], row, tl, a.tr, ms.stride[0], 1, 0u, tw, io);
         for (int s = 1; s <= last; ++s)
-            mixed_stage_any<WIDE, false, false, false, P>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
+            mixed_stage_any<WIDE, false, false, false, P, BM>(ms.radix[s], row, tl, a.tr, ms.stride[s], ms.ns[s],
                                                           ms.magic[s], tw + ms.twoff[s], io);
     };
     const int64_t ibase = sbase + j, obase_l = sbase + (int64_t)g * a.ns * a.r + k;
@@ -628,9 +632,14 @@ static hipError_t mixed_pass_t(IN in, OUT out, int64_t batch, const MixedPassArg
         hipLaunchKernelGGL((mixed_pass_kernel<V, L2, WIDE, 0, IN, OUT>), grid, dim3(L2 * a.tr),
                            (unsigned)((L2 + 1) * a.r * (int)sizeof(V)), s, in, out, a, ms, (const V*)tw, big,
                            (Rl)scale);
-    else
+    else if (a.r <= 512)
         hipLaunchKernelGGL((mixed_pass_kernel<V, L1, WIDE, 512, IN, OUT>), grid, dim3(L1 * a.tr), 0, s, in, out, a,
                            ms, (const V*)tw, big, (Rl)scale);
+    else if constexpr (!WIDE)
+        hipLaunchKernelGGL((mixed_pass_kernel<V, L1, false, MP_RMAX, IN, OUT>), grid, dim3(L1 * a.tr), 0, s, in,
+                           out, a, ms, (const V*)tw, big, (Rl)scale);
+    else
+        return hipErrorInvalidValue;  // radices 11, 13 stay within 512 (the launcher checks)
     return hipGetLastError();
 }
 
@@ -663,7 +672,8 @@ int mixed_pass_threads(const MixedSchedule& ms, int r)
 {
     int tr = 1;
     for (int q = 0; q < ms.nst; ++q)
-        while ((int64_t)tr * mixed_bmax_of(ms.radix[q]) < r / ms.radix[q]) tr *= 2;
+        while ((int64_t)tr * mixed_bmax_of(ms.radix[q], r > 512 ? 16 : 8) < r / ms.radix[q]) tr *= 2;
+    while (tr * MP_QMAX < r) tr *= 2;
     return tr;
 }
 
@@ -677,7 +687,9 @@ hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedu
                              int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t s,
                              const void* in_im, void* out_im)
 {
-    if (a.r > 512 || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr > 64 ||
+    bool wide_radix = false;  // an 11- or 13-point stage
+    for (int q = 0; q < ms.nst; ++q) wide_radix |= ms.radix[q] == 11 || ms.radix[q] == 13;
+    if (a.r > MP_RMAX || (a.r > 512 && wide_radix) || a.r < 2 || a.tr < mixed_pass_threads(ms, a.r) || a.tr > 64 ||
         (a.r + a.tr - 1) / a.tr > MP_QMAX ||
         a.ns < 1 || a.tdiv < 1 || a.ns % a.tdiv || (int64_t)a.stride * a.r != a.n ||
         a.tiles * (int64_t)mixed_pass_lines(prec, a.r) < a.stride || a.tr * mixed_pass_lines(prec, a.r) > 1024 ||

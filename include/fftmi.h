@@ -91,8 +91,10 @@ enum fft_status {
  *           - N = 2^a 3^b 5^c 7^d 11^e 13^f up to 8192 (C32) / 4096 (C64):
  *             mixed-radix Stockham stages (radices 8, 4, 2, 9, 3, 5, 7, 11,
  *             13) in one kernel, no workspace;
- *           - such N beyond that: N = R0 R1 (R2), each R <= 512, as two or
- *             three super-stage passes whose R-point transforms run those
+ *           - such N beyond that: N = R0 R1 (R2), each R <= 512 (<= 1024
+ *             where that makes two passes of three, for R without a factor
+ *             11 or 13), as two or three super-stage passes whose R-point
+ *             transforms run those
  *             mixed-radix stages; a workspace of one batch of signals, like
  *             the power-of-two passes (fft_plan_describe: path=mixpass);
  *           - any other N: chirp-z (Bluestein), X_k = c_k (x.c * conj c)_k
@@ -119,7 +121,8 @@ enum fft_status {
  *           axis W may have any length a rank-1 plan takes (it runs as the
  *           rank-1 plan over every row); every other axis longer than 1 must
  *           be 2^a 3^b 5^c 7^d 11^e 13^f and runs as one super-stage pass up
- *           to 512 points, two or three beyond; at most FFT_MAX_N_* points
+ *           to 1024 points (512 with a factor 11 or 13), two or three beyond;
+ *           at most FFT_MAX_N_* points
  *           per transform (fft_plan_describe: path=ndmixed).  Workspace:
  *           fft_workspace_size, out of place too (a signal-sized buffer for
  *           an axis of two or more passes, plus what the rows need).

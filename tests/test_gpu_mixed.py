@@ -133,15 +133,18 @@ def test_mixed_every_smooth_length(dev, dtype, limit):
     assert not bad, bad
 
 
-# Beyond one kernel: 2-3 mixed-radix super-stage passes (radix <= 512 each),
-# radices from 50 to 512 in both precisions (each tile width of the pass
-# kernel: radix <= 64, <= 256, beyond).
+# Beyond one kernel: 2-3 mixed-radix super-stage passes, radices from 50 to
+# 1024 in both precisions (each tile width and LDS class of the pass kernel:
+# radix <= 64, <= 256, <= 512, and the wide class up to 1024 where it saves a
+# pass: 10^6 = 1000 1000, 3 2^18 = 1024 768; 1001000 = 7 11 13 ... keeps its
+# radices within 512 and takes three).
 MIXPASS = [(9000, torch.complex64, 3), (10000, torch.complex64, 2), (12288, torch.complex64, 2),
            (30030, torch.complex64, 2), (60060, torch.complex64, 1), (3 * 65536, torch.complex64, 1),
            (10 ** 6, torch.complex64, 1), (3 << 20, torch.complex64, 1), (6000, torch.complex128, 3),
            (4608, torch.complex128, 3), (5000, torch.complex128, 2), (10000, torch.complex128, 2),
            (30030, torch.complex128, 1), (3 * 65536, torch.complex128, 1), (5 ** 9, torch.complex128, 1),
-           (8 * 10 ** 6, torch.complex64, 1)]
+           (8 * 10 ** 6, torch.complex64, 1), (3 << 18, torch.complex64, 1), (3 << 18, torch.complex128, 1),
+           (10 ** 6, torch.complex128, 1), (1001000, torch.complex64, 1)]
 
 
 @pytest.mark.parametrize("n,dtype,batch", MIXPASS)

@@ -38,17 +38,22 @@ CASES = [
     ((12, 20), torch.complex64, 3),
     ((100, 7), torch.complex64, 2),      # 7-point rows, one 100-point column pass
     ((7, 100), torch.complex64, 2),
-    ((1000, 1), torch.complex64, 2),     # a column of 1000: two passes, no rows
+    ((1000, 1), torch.complex64, 2),     # a column of 1000: one pass, no rows
+    ((3000, 1), torch.complex64, 1),     # a column of 3000: two passes, no rows
     ((1, 1000), torch.complex64, 2),     # rows only
     ((64, 97), torch.complex64, 2),      # Bluestein rows
-    ((1000, 600), torch.complex64, 1),   # 1000-point columns: two passes
-    ((1024, 100), torch.complex64, 1),   # power-of-two columns, passes 32 x 32
+    ((1000, 600), torch.complex64, 1),   # 1000-point columns: one pass of radix 1000
+    ((2000, 60), torch.complex64, 1),    # 2000-point columns: two passes
+    ((1024, 100), torch.complex64, 1),   # power-of-two columns: one pass of radix 1024
+    ((1001, 12), torch.complex64, 1),    # 7 11 13: two passes (radices 11, 13 stay within 512)
+    ((845, 6), torch.complex128, 1),     # 5 13 13: two passes
     ((720, 1280), torch.complex64, 1),
     ((12, 30, 50), torch.complex64, 2),
     ((3, 5, 7), torch.complex64, 3),
     ((10, 100, 10), torch.complex64, 1),
     ((100, 7), torch.complex128, 2),
     ((1000, 60), torch.complex128, 1),
+    ((729, 40), torch.complex128, 1),    # radix 729 = 9^3, the widest pass class in complex128
     ((12, 30, 50), torch.complex128, 1),
 ]
 
@@ -82,10 +87,10 @@ def test_ndmixed(dev, dims, dtype, batch):
 
 
 def test_ndmixed_three_pass_axis(dev):
-    """A column axis of 331776 = 2^12 3^4 points (three passes) over two-point
-    rows, on sampled bins: with W = 2 the image transform at (k1, k2) is the
-    column transform of x[:, 0] + (-1)^k2 x[:, 1]."""
-    h, w = 331776, 2
+    """A column axis of 1161216 = 2^11 3^4 7 points (three passes: beyond
+    1024^2) over two-point rows, on sampled bins: with W = 2 the image
+    transform at (k1, k2) is the column transform of x[:, 0] + (-1)^k2 x[:, 1]."""
+    h, w = 1161216, 2
     plan = fm.Plan((h, w), torch.complex64)
     d = plan.describe()
     assert "axis1=" in d and d.split("axis1=")[1].count("x") == 2, d
@@ -101,13 +106,15 @@ def test_ndmixed_three_pass_axis(dev):
 
 
 def test_ndmixed_workspace_rules(dev):
-    # two-pass columns need a signal-sized buffer, out of place too
-    plan = fm.Plan((1000, 600), torch.complex64)
+    # two-pass columns (beyond 1024 points) need a signal-sized buffer, out
+    # of place too
+    plan = fm.Plan((2000, 600), torch.complex64)
     need = fm.fft_workspace_size(plan.handle, 1)
-    assert need >= 1000 * 600 * 8
-    x = torch.zeros(1, 1000, 600, dtype=torch.complex64, device=dev)
+    assert need >= 2000 * 600 * 8
+    x = torch.zeros(1, 2000, 600, dtype=torch.complex64, device=dev)
     with pytest.raises(fm.FFTError) as e:
         fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, x, torch.empty_like(x), 1, None)
     assert e.value.status == fm.FFT_ERR_WORKSPACE
-    # one-pass columns over mixed-radix rows: none
+    # one-pass columns (up to 1024 points) over mixed-radix rows: none
     assert fm.fft_workspace_size(fm.Plan((100, 7), torch.complex64).handle, 5) == 0
+    assert fm.fft_workspace_size(fm.Plan((1000, 600), torch.complex64).handle, 2) == 0

@@ -125,10 +125,13 @@ def test_query_rejects_as_create_does(rank, dims, prec, status):
 
 
 def test_mixpass_splits():
-    """Large 13-smooth lengths: the fewest passes of radix <= 512, the most even
-    split (largest smallest radix), larger radices first."""
-    cases = {10 ** 6: [100, 100, 100], 3 << 20: [192, 128, 128], 5 ** 9: [125, 125, 125],
-             12288: [128, 96], 30030: [182, 165], 3 * 65536: [512, 384], 7 << 20: [448, 128, 128]}
+    """Large 13-smooth lengths: the fewest passes, the most even split
+    (largest smallest radix), larger radices first; radices up to 512, or up
+    to 1024 where two passes then do instead of three (radices above 512 take
+    no factor 11 or 13)."""
+    cases = {10 ** 6: [1000, 1000], 3 << 18: [1024, 768], 1001000: [110, 100, 91], 3 << 20: [192, 128, 128],
+             5 ** 9: [125, 125, 125], 12288: [128, 96], 30030: [182, 165], 3 * 65536: [512, 384],
+             7 << 20: [448, 128, 128]}
     for n, want in cases.items():
         for prec in (0, 1):
             d = _q(1, [n], prec)
@@ -141,16 +144,21 @@ def test_mixpass_splits():
 
 def test_ndmixed_layouts():
     """Rank 2 / 3 with a dimension that is not a power of two: the innermost
-    axis by its rank-1 route, every other axis longer than 1 as passes of
-    radix <= 512 (one up to 512 points)."""
+    axis by its rank-1 route, every other axis longer than 1 as passes (one
+    up to 1024 points when the length has no factor 11 or 13, else up to
+    512)."""
     d = _q(2, [1000, 1000], 0)
-    assert "path=ndmixed" in d and "rows=[mixed radices=8x5x5x5]" in d and d.endswith("axis1=40x25")
+    assert "path=ndmixed" in d and "rows=[mixed radices=8x5x5x5]" in d and d.endswith("axis1=1000")
+    assert _q(2, [1024, 1000], 0).endswith("axis1=1024")
+    assert _q(2, [2000, 8], 0).endswith("axis1=50x40")
+    assert _q(2, [1001, 8], 1).endswith("axis1=77x13")
+    assert _q(2, [845, 6], 0).endswith("axis1=65x13")
     d = _q(2, [64, 97], 1)
     assert "rows=[bluestein" in d and d.endswith("axis1=64")
     d = _q(3, [12, 30, 50], 0)
     assert d.endswith("axis1=30 axis2=12")
     d = _q(2, [1000, 1], 0)
-    assert "rows=[copy]" in d and d.endswith("axis1=40x25")
+    assert "rows=[copy]" in d and d.endswith("axis1=1000")
     assert "axis" not in _q(2, [1, 1000], 0)
     # the power-of-two shapes keep their own path
     assert "path=nd " in _q(2, [64, 32], 0)
