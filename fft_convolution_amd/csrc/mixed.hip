@@ -547,8 +547,15 @@ __global__ __launch_bounds__(LN * 64 < 1024 ? LN * 64 : 1024) void mixed_pass_ke
     extern __shared__ __align__(16) unsigned char mp_lds_dyn[];
     V* const lds = RCAP > 0 ? lds_static : reinterpret_cast<V*>(mp_lds_dyn);
     const int c = threadIdx.x % LINES, tl = threadIdx.x / LINES;
-    const int64_t sig = (int64_t)blockIdx.x / a.tiles;
-    const int j0 = (int)((int64_t)blockIdx.x - sig * a.tiles) * LINES;
+    // Where the element rows of a tile (N/R elements apart) are not a whole
+    // number of 128-byte lines apart, a tile's segments straddle lines that
+    // the neighbouring tile reads too: each XCD then takes a contiguous range
+    // of tiles, so that both go through the same L2.  Otherwise launch order
+    // (measured faster there).
+    const bool straddle = ((a.stride * (int)sizeof(V)) & 127) != 0;
+    const int64_t tile = straddle ? xcd_tile(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+    const int64_t sig = tile / a.tiles;
+    const int j0 = (int)(tile - sig * a.tiles) * LINES;
     const int j = j0 + c;
     const bool live = j < a.stride;
     const int g = j / a.ns, k = j - g * a.ns;
