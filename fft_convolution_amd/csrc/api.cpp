@@ -864,7 +864,7 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
     }
     if (rank > 1 && !all_pow2) {
         // the innermost axis: any length a rank-1 plan takes; the others:
-        // 2^a 3^b 5^c 7^d 11^e 13^f, as at most three passes of radix <= 512
+        // 2^a 3^b 5^c 7^d 11^e 13^f, as at most three passes (axis_split)
         int64_t total = 1;
         for (int d = 0; d < rank; ++d) {
             total *= dims[d];
