@@ -1758,9 +1758,16 @@ static int exec_real_2d(const fft_plan* plan, bool c2r, const void* in, void* ou
                 e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, wc, 0, plan->tw_b, none, false, 1.0, s,
                                   nullptr, true, false);
         } else {
-            e = row_pass(in, workspace);
-            if (e == hipSuccess)
-                e = launch_colstage(plan->prec, plan->logf, workspace, out, batch, wc, plan->log_b, s, true, false);
+            if (r2c_fold_supported(plan->prec, plan->log_a, plan->logf)) {
+                // the radix-F column stage folded into the row pass
+                e = launch_r2c_fold(plan->prec, plan->log_a, plan->logf, in, out, batch, plan->log_b,
+                                    plan->inner->tw_a, plan->big_hi, plan->big_lo, s);
+            } else {
+                e = row_pass(in, workspace);
+                if (e == hipSuccess)
+                    e = launch_colstage(plan->prec, plan->logf, workspace, out, batch, wc, plan->log_b, s, true,
+                                        false);
+            }
             if (e == hipSuccess)
                 e = launch_cols2d(plan->prec, plan->log_b, out, out, batch, wc, plan->logf, plan->tw_b, hb, false, 1.0,
                                   s, nullptr, true, false);

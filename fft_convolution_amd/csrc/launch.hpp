@@ -186,6 +186,15 @@ hipError_t launch_narrow(const void* in, void* out, int64_t total, hipStream_t s
 // tables split at T (threads per row).  in and out must not alias.
 hipError_t launch_real_rows(int prec, int logh, bool c2r, const void* in, void* out, int64_t nrows, const void* tw,
                             const void* whi, const void* wlo, hipStream_t stream);
+// R2C rows of nimg real images [F Lc][2H] (H = 2^logh) with the radix-F
+// column super-stage (F = 2^logf) folded in: half-spectrum rows j F + r' of
+// out [nimg][F Lc][H + 1] get the F-point DFT over r of the half spectra of
+// real rows j + r Lc; tw, whi, wlo as for launch_real_rows.  in and out must
+// not alias.  r2c_fold_supported: whether a kernel exists for the sizes
+// (launch_r2c_fold returns hipErrorInvalidValue otherwise).
+bool r2c_fold_supported(int prec, int logh, int logf);
+hipError_t launch_r2c_fold(int prec, int logh, int logf, const void* in, void* out, int64_t nimg, int log_lc,
+                           const void* tw, const void* whi, const void* wlo, hipStream_t stream);
 // Longer rows, around the H-point complex transform: R2C z [batch][H] -> out
 // [batch][H + 1]; C2R x [batch][H + 1] -> z [batch][H].  wn: tables for w_N.
 hipError_t launch_real_pairs(int prec, bool c2r, const void* in, void* out, int64_t h, int64_t batch,

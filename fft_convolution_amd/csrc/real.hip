@@ -238,6 +238,166 @@ hipError_t launch_real_rows(int prec, int logh, bool c2r, const void* in, void* 
 #undef FFTMI_REAL_CASE
 }
 
+// ---------------------------------------------------------------------------
+// R2C rows of [H'][2H] real images with the radix-F column super-stage folded
+// in (the real counterpart of rows2d_fold_kernel): a group of F row-groups
+// takes real rows j + r Lc (r < F) of one image, makes each row's half
+// spectrum (the H-point transform and the even/odd split, as r2c_rows_kernel),
+// exchanges through LDS so that every thread holds all F rows at E/F bins,
+// does the F-point DFT across the rows and writes half-spectrum rows j F + r'
+// ([H'][H + 1]); bin H of the F rows goes to thread 0 of the group.  The
+// values the DFT reads are the split's, rounded to V in LDS as they were in
+// memory when the column stage ran on its own.  Out of place.
+// ---------------------------------------------------------------------------
+template <typename V, int LOGH, int LOGF> constexpr int r2c_fold_groups()
+{
+    return (Geom<V, LOGH>::T << LOGF) >= 256 ? 1 : 256 / (Geom<V, LOGH>::T << LOGF);
+}
+
+template <typename V, int LOGH, int LOGF> constexpr bool r2c_fold_ok()
+{
+    using G = Geom<V, LOGH>;
+    constexpr long threads = (long)(G::T << LOGF) * r2c_fold_groups<V, LOGH, LOGF>();
+    constexpr long lds = (long)real_slots<LOGH>() * (1 << LOGF) * r2c_fold_groups<V, LOGH, LOGF>() * (long)sizeof(V);
+    return LOGH >= 1 && G::E >= (1 << LOGF) && threads <= 1024 && lds <= 160 * 1024;
+}
+
+template <typename V, int LOGH, int LOGF>
+__global__ __launch_bounds__(((Geom<V, LOGH>::T << LOGF) * r2c_fold_groups<V, LOGH, LOGF>()))
+void r2c_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* __restrict__ tw,
+                     const V* __restrict__ whi, const V* __restrict__ wlo)
+{
+    using G = Geom<V, LOGH>;
+    constexpr int H = G::N, T = G::T, E = G::E, F = 1 << LOGF, EF = E / F;
+    constexpr int GR = r2c_fold_groups<V, LOGH, LOGF>();
+    constexpr int SLOTS = real_slots<LOGH>();
+    __shared__ V lds[SLOTS * F * GR];
+    const int tid = threadIdx.x;
+    const int gl = tid / (F * T);
+    const int rho = (tid / T) % F;
+    const int t = tid % T;
+    const int64_t grp = (int64_t)blockIdx.x * GR + gl;
+    const bool live = grp < ngroups;
+    const int64_t lc = (int64_t)1 << log_lc;
+    const int64_t img = grp >> log_lc, j = grp & (lc - 1);
+    const int64_t hh = lc << LOGF;  // rows per image
+    V* my = lds + (gl * F) * SLOTS;
+    const LdsLines<V, 1> L{my + rho * SLOTS, 0};
+
+    TwBases<V, LOGH> tb;
+    tb.load(tw, t);
+    V v[E];
+    const V* src = in + (img * hh + j + rho * lc) * H + t;
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = live ? ld_stream(src + i * T) : V{0, 0};
+    fft_regs<LOGH>(v, t, tb, L);
+    __syncthreads();  // the transform's last exchange is read by now
+#pragma unroll
+    for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
+    __syncthreads();
+    const V w0 = wlo[t];
+    V y[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int k = t + i * T;
+        y[i] = real_split(v[i], *L.ptr((H - k) & (H - 1)), cmul(whi[i], w0));
+    }
+    const V yh{v[0].x - v[0].y, 0};  // bin H, from Z_0 (thread 0)
+    __syncthreads();  // every partner read is done
+#pragma unroll
+    for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = y[i];
+    if (t == 0) *L.ptr(H) = yh;
+    __syncthreads();
+    V* dst = out + (img * hh + j * F) * (H + 1);
+#pragma unroll
+    for (int k = 0; k < EF; ++k) {
+        const int p = t + (rho * EF + k) * T;
+        V u[F];
+#pragma unroll
+        for (int r = 0; r < F; ++r) u[r] = *LdsLines<V, 1>{my + r * SLOTS, 0}.ptr(p);
+        Dft<F>::run(u);
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < F; ++r) st_stream(dst + r * (H + 1) + p, u[r]);
+        }
+    }
+    if (rho == 0 && t == 0) {
+        V u[F];
+#pragma unroll
+        for (int r = 0; r < F; ++r) u[r] = *LdsLines<V, 1>{my + r * SLOTS, 0}.ptr(H);
+        Dft<F>::run(u);
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < F; ++r) st_stream(dst + r * (H + 1) + H, u[r]);
+        }
+    }
+}
+
+template <typename V, int LOGH, int LOGF>
+static hipError_t r2c_fold_t(const void* in, void* out, int64_t nimg, int log_lc, const void* tw, const void* whi,
+                             const void* wlo, hipStream_t s)
+{
+    if constexpr (!r2c_fold_ok<V, LOGH, LOGF>()) {
+        return hipErrorInvalidValue;
+    } else {
+        constexpr int GR = r2c_fold_groups<V, LOGH, LOGF>();
+        const int64_t ngroups = nimg << log_lc;
+        const int64_t blocks = (ngroups + GR - 1) / GR;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((r2c_fold_kernel<V, LOGH, LOGF>), dim3((unsigned)blocks),
+                           dim3((Geom<V, LOGH>::T << LOGF) * GR), 0, s, (const V*)in, (V*)out, ngroups, log_lc,
+                           (const V*)tw, (const V*)whi, (const V*)wlo);
+        return hipGetLastError();
+    }
+}
+
+template <typename V, int LOGH>
+static hipError_t r2c_fold_f(int logf, const void* in, void* out, int64_t nimg, int log_lc, const void* tw,
+                             const void* whi, const void* wlo, hipStream_t s)
+{
+    switch (logf) {
+        case 1: return r2c_fold_t<V, LOGH, 1>(in, out, nimg, log_lc, tw, whi, wlo, s);
+        case 2: return r2c_fold_t<V, LOGH, 2>(in, out, nimg, log_lc, tw, whi, wlo, s);
+        case 3: return r2c_fold_t<V, LOGH, 3>(in, out, nimg, log_lc, tw, whi, wlo, s);
+        case 4: return r2c_fold_t<V, LOGH, 4>(in, out, nimg, log_lc, tw, whi, wlo, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool r2c_fold_supported(int prec, int logh, int logf)
+{
+#define FFTMI_FOLD_OK(V, L) \
+    (logf == 1 ? r2c_fold_ok<V, L, 1>() : logf == 2 ? r2c_fold_ok<V, L, 2>() \
+     : logf == 3 ? r2c_fold_ok<V, L, 3>() : logf == 4 ? r2c_fold_ok<V, L, 4>() : false)
+#define FFTMI_FOLD_CASE(L) \
+    case L: return prec == 0 ? FFTMI_FOLD_OK(float2, L) : FFTMI_FOLD_OK(double2, L);
+    switch (logh) {
+        FFTMI_FOLD_CASE(1) FFTMI_FOLD_CASE(2) FFTMI_FOLD_CASE(3) FFTMI_FOLD_CASE(4) FFTMI_FOLD_CASE(5)
+        FFTMI_FOLD_CASE(6) FFTMI_FOLD_CASE(7) FFTMI_FOLD_CASE(8) FFTMI_FOLD_CASE(9) FFTMI_FOLD_CASE(10)
+        FFTMI_FOLD_CASE(11) FFTMI_FOLD_CASE(12)
+        default: return false;
+    }
+#undef FFTMI_FOLD_CASE
+#undef FFTMI_FOLD_OK
+}
+
+hipError_t launch_r2c_fold(int prec, int logh, int logf, const void* in, void* out, int64_t nimg, int log_lc,
+                           const void* tw, const void* whi, const void* wlo, hipStream_t s)
+{
+    if (!r2c_fold_supported(prec, logh, logf) || nimg < 1 || log_lc < 0) return hipErrorInvalidValue;
+#define FFTMI_FOLD_CASE(L)                                                                      \
+    case L:                                                                                     \
+        return prec == 0 ? r2c_fold_f<float2, L>(logf, in, out, nimg, log_lc, tw, whi, wlo, s) \
+                         : r2c_fold_f<double2, L>(logf, in, out, nimg, log_lc, tw, whi, wlo, s);
+    switch (logh) {
+        FFTMI_FOLD_CASE(1) FFTMI_FOLD_CASE(2) FFTMI_FOLD_CASE(3) FFTMI_FOLD_CASE(4) FFTMI_FOLD_CASE(5)
+        FFTMI_FOLD_CASE(6) FFTMI_FOLD_CASE(7) FFTMI_FOLD_CASE(8) FFTMI_FOLD_CASE(9) FFTMI_FOLD_CASE(10)
+        FFTMI_FOLD_CASE(11) FFTMI_FOLD_CASE(12)
+        default: return hipErrorInvalidValue;
+    }
+#undef FFTMI_FOLD_CASE
+}
+
 template <typename V>
 static hipError_t launch_real_pairs_t(bool c2r, const void* in, void* out, int64_t h, int64_t batch, BigTwiddle wn,
                                       hipStream_t s)

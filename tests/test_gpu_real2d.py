@@ -24,6 +24,8 @@ CASES = [
     (2048, 2048, torch.float32, 1), (8192, 64, torch.float32, 1), (64, 16384, torch.float32, 1),
     (4, 8, torch.float64, 3), (256, 128, torch.float64, 2), (1024, 64, torch.float64, 1),
     (4096, 2, torch.float64, 2), (2048, 8192, torch.float64, 1),
+    # column stages of radix 8 and 16 folded into the real row pass, complex128 too
+    (4096, 256, torch.float32, 2), (8192, 1024, torch.float32, 1), (2048, 256, torch.float64, 2),
 ]
 
 
