@@ -27,6 +27,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
+# Per-file additions.  The chirp-z kernel's forward transform reads a row
+# whose upper half is zero (M >= 2N - 1): without signed zeros the compiler
+# may drop the x + 0 terms of its first stage and the unused half of the
+# inverse's last (17 % fewer instructions in the kernel's code, 1-2 % less
+# time: 1009-point rows 534 -> 529 us); results differ at most in the sign
+# of a zero.
+FILE_FLAGS = {"bluestein.hip": ["-fno-signed-zeros"]}
 
 
 def _hipcc() -> str:
@@ -38,7 +45,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

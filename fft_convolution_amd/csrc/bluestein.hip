@@ -60,6 +60,7 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
                            const V* __restrict__ chirp, const V* __restrict__ bspec, typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGM>;
+    static_assert(G::E >= 2, "positions t + i T with i >= E/2 are the upper half");
     using Rl = typename real_of<V>::type;
     constexpr int RPW = rows_per_wg<V, LOGM>();
     __shared__ V lds[G::LDS > 0 ? G::LDS * RPW : 1];
@@ -80,7 +81,9 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
         for (int i = 0; i < G::E; ++i) {
             const int p = t + i * G::T;
             V x{0, 0};
-            if (live && p < n) {
+            // positions from M/2 on are zero padding (n <= M/2): a
+            // compile-time zero, so the first stage's x + 0 terms can go
+            if (i < G::E / 2 && live && p < n) {
                 x = in.ld(base + p);
                 if (INV) x = cconj(x);
                 x = cmul_pinned(x, chirp[p]);
@@ -103,7 +106,7 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
         const int p = t + i * G::T;
-        if (p < n) {
+        if (i < G::E / 2 && p < n) {  // outputs from M/2 on are never stored
             const V y = cmul_pinned(V{v[i].x * inv_m, -v[i].y * inv_m}, chirp[p]);
             out.st(base + p, INV ? V{y.x * scale, -y.y * scale} : y);
         }
@@ -142,6 +145,8 @@ hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void
 {
     const Io io{in, in_im, out, out_im};
     if ((in_im != nullptr) != (out_im != nullptr)) return hipErrorInvalidValue;
+    // the kernel takes every position from M/2 on as zero padding
+    if (n < 1 || logm < 1 || logm > 13 || 2 * (int64_t)n - 1 > (int64_t(1) << logm)) return hipErrorInvalidValue;
 #define FFTMI_BL(L)                                                                                          \
     case L:                                                                                                  \
         return prec == 0 ? bluestein_rows_pl<float2, L>(io, nrows, n, tw, chirp, bspec, inverse, scale, s)   \
