@@ -7,21 +7,25 @@ LDS-resident path.  One step = one fft_exec_c2c call over the whole batch with
 the input already resident in HBM.
 
 Prints ONE JSON line with:
-  value      GFLOP/s = batch * 5 N log2 N / t  (pseudo-flops, 10 per radix-2 butterfly)
-  roofline   achieved HBM GB/s of the kernel (input + output bytes / average
-             kernel time from HIP events on the launch stream) against 8000 GB/s,
-             plus `traffic`: HBM bytes per launch measured with rocprofv3 counters
-             (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), read
-             from profiles/ and null once the kernel sources have changed
-  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows
-  step_us    mean / median / min / max of the per-step event durations
-  copy_ceiling  a device-to-device copy of the same byte count (at least
-             512 MiB each way), timed alike, and the step's algorithmic rate
-             as a fraction of the copy's (the practical ceiling)
+  value      GFLOP/s = batch * 5 N log2 N / t, t = ms_per_step: K steps launched
+             back to back between ONE pair of HIP events on the launch stream
+             (pseudo-flops, 10 per radix-2 butterfly)
+  roofline   achieved HBM GB/s of the step's one kernel (input + output bytes /
+             the same t: a step is one launch, so t is that kernel's average
+             launch duration) against 8000 GB/s, plus `traffic`: HBM bytes per
+             launch measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE
+             scaled by a copy kernel of known size), read from profiles/ and
+             null once the kernel sources have changed
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows, with
+             the thread count and the host CPU model
+  launch_us  a separate pass with a pair of events around every launch: mean /
+             median / min / max of the per-launch durations
+  copy_ceiling  the library's streaming copy (fft_stream_copy: every byte read
+             once and written once, nontemporal 16-byte lanes) of the same byte
+             count, timed like the steps, and the step's algorithmic rate as a
+             fraction of the copy's (the practical ceiling of the access pattern)
   rotated    the same steps cycling over --rotate buffer sets (default 3), so
              that no step finds its input in the 256 MB MALL
-  torch_fft  (--compare-torch) the same transform by torch.fft on the same
-             input (mean of per-call event durations) and its ratio to step_us mean
 
 Other workloads (--workload) time the 2^24-point multi-pass transform, the
 2048x2048x8 2D transform, the 32 x 2^18 polynomial products and a 256^3 3D
@@ -208,47 +212,6 @@ def setup_workload(name, dev, fm, torch, sets=1):
     raise SystemExit("unknown workload %s" % name)
 
 
-def torch_fft_time(name, info, torch, reps):
-    """The same transform by torch.fft (the ROCm vendor FFT behind it) on the
-    same resident input, timed like the steps: a point of comparison only,
-    never a path of this library.  Poly-mul: forward transforms of a and b
-    (fp64, length N), their product, the inverse, rounded to int64."""
-    bufs = info["keep"][1]
-    if name.startswith("polymul"):
-        a, b = bufs[0][0], bufs[0][1]
-        n, m = info["n"], 2 * info["length"] - 1
-
-        def fn():
-            fa = torch.fft.fft(a.to(torch.float64), n=n)
-            fb = torch.fft.fft(b.to(torch.float64), n=n)
-            return torch.fft.ifft(fa * fb).real[..., :m].round().to(torch.int64)
-        what = "torch.fft: fft(a), fft(b), product, ifft, round to int64"
-    else:
-        x = bufs[0][0]
-        if name.startswith("c2c3d"):
-            fn, what = (lambda: torch.fft.fftn(x, dim=(-3, -2, -1))), "torch.fft.fftn over the last 3 dims"
-        elif name.startswith("c2c2d"):
-            fn, what = (lambda: torch.fft.fft2(x)), "torch.fft.fft2"
-        elif name.startswith("r2c2d"):
-            fn, what = (lambda: torch.fft.rfft2(x)), "torch.fft.rfft2"
-        elif name.startswith("r2c"):
-            fn, what = (lambda: torch.fft.rfft(x)), "torch.fft.rfft"
-        else:
-            fn, what = (lambda: torch.fft.fft(x)), "torch.fft.fft"
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
-    # each call bracketed by its own pair of events, as the steps are
-    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in marks:
-        e0.record()
-        fn()
-        e1.record()
-    torch.cuda.synchronize()
-    mean = sum(e0.elapsed_time(e1) for e0, e1 in marks) / reps
-    return {"what": what, "call_us_mean": round(mean * 1e3, 2), "calls": reps}
-
-
 def cpu_baseline(name, info, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -320,7 +283,19 @@ def cpu_baseline(name, info, budget_s):
         units = rows * reps
         sample = "first %d of %d rows, transformed %d time(s)" % (rows, total, reps)
     return {"value": units * info["oracle_unit"] / dt / 1e9, "unit": "GFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3), "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -335,8 +310,6 @@ def main():
                     help="buffer sets for the extra rotated-buffer timing (1 = none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a device-to-device copy of the input's size (for counter scaling)")
-    ap.add_argument("--compare-torch", action="store_true",
-                    help="also time torch.fft on the same input (a comparison point, not part of the step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -354,57 +327,66 @@ def main():
 
     sets = max(1, args.rotate)
     step, info = setup_workload(args.workload, dev, fm, torch, sets=sets)
-    for k in range(max(args.warmup, sets)):
-        step(k)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # The practical ceiling, measured first: the library's streaming copy of
+    # the same byte count (half the algorithmic bytes each way), at least
+    # 512 MiB each way so that it streams from HBM rather than the 256 MB MALL.
+    copy_bytes = max(info["bytes"] // 2, 512 << 20)
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        fm.fft_stream_copy(src, dst, copy_bytes, stream.cuda_stream)
+    torch.cuda.synchronize()
+    c0, c1 = ev(), ev()
+    c0.record()
+    for _ in range(args.steps):
+        fm.fft_stream_copy(src, dst, copy_bytes, stream.cuda_stream)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / args.steps
+    del src, dst
+
+    for _ in range(args.warmup):
+        step(0)
     torch.cuda.synchronize()
 
-    def timed(k0, stride):
-        """K steps back to back on the launch stream (set k0 + i stride), each
-        bracketed by its own pair of HIP events, so that the per-launch
-        duration is measured the way a kernel trace measures it.  Returns
-        (ms per step over the whole region, per-step event durations in ms)."""
-        ev = lambda: torch.cuda.Event(enable_timing=True)
+    def region(stride):
+        """K steps launched back to back between one pair of events on the
+        launch stream (step i on buffer set i * stride mod sets); ms per step."""
         start, end = ev(), ev()
-        marks = [(ev(), ev()) for _ in range(args.steps)]
         torch.cuda.synchronize()
         start.record()
-        for i, (a, b) in enumerate(marks):
-            a.record()
-            step(k0 + i * stride)
-            b.record()
+        for i in range(args.steps):
+            step(i * stride)
         end.record()
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / args.steps, [a.elapsed_time(b) for a, b in marks]
+        return start.elapsed_time(end) / args.steps
 
     # Timed region: the same buffers every step (the figure `value` is from).
-    ms, per = timed(0, 0)
-    launch_ms = sum(per) / len(per)
-    per_sorted = sorted(per)
+    ms = region(0)
+
+    # Separate pass, not part of `value`: each launch between its own pair of
+    # events, for the spread of single-launch durations.
+    marks = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in marks:
+        a.record()
+        step(0)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in marks)
+
     # Rotated: consecutive steps on different buffer sets, so that nothing a
     # step reads is still in the 256 MB MALL from the step before.
     rotated = None
     if sets > 1:
-        ms_rot, per_rot = timed(0, 1)
-        rotated = {"sets": sets, "ms_per_step": round(ms_rot, 5),
-                   "step_us_median": round(sorted(per_rot)[len(per_rot) // 2] * 1e3, 2)}
-
-    # The practical ceiling: a device-to-device copy of the same byte count
-    # (half the algorithmic bytes each way), at least 512 MiB each way so that
-    # it streams from HBM rather than the 256 MB MALL.
-    copy_bytes = max(info["bytes"] // 2, 512 << 20)
-    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(20):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / 20
-    del src, dst
+        for k in range(sets):
+            step(k)
+        rotated = {"sets": sets, "ms_per_step": round(region(1), 5)}
 
     if args.copy_calibration:
         # A plain elementwise kernel that reads and writes known byte counts
@@ -433,9 +415,9 @@ def main():
         "config": {"workload": args.workload, "plan": info["plan"],
                    **{k: info[k] for k in ("n", "d", "h", "w", "batch", "length") if k in info}},
         "hbm_tb_s": round(tbs, 3),
-        "step_us": {"mean": round(launch_ms * 1e3, 2), "median": round(per_sorted[len(per) // 2] * 1e3, 2),
-                    "min": round(per_sorted[0] * 1e3, 2), "max": round(per_sorted[-1] * 1e3, 2)},
-        "copy_ceiling": {"what": "device-to-device copy of the same bytes (half each way)",
+        "launch_us": {"mean": round(sum(per) / len(per) * 1e3, 2), "median": round(per[len(per) // 2] * 1e3, 2),
+                      "min": round(per[0] * 1e3, 2), "max": round(per[-1] * 1e3, 2)},
+        "copy_ceiling": {"what": "fft_stream_copy of the same bytes (half each way), launched back to back",
                          "gb_s": round(2 * copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
                          "frac_of_copy": round((info["bytes"] / ms) / (2 * copy_bytes / copy_ms), 4)},
         "rotated": rotated,
@@ -443,20 +425,17 @@ def main():
     }
     if info["kernels"] == 1:
         # One kernel per step: algorithmic bytes (input read once + output
-        # written once) over that kernel's average launch duration.
-        achieved = info["bytes"] / (launch_ms * 1e-3) / 1e9
+        # written once) over that kernel's average launch duration, which is
+        # the timed region's ms per step (the same figure as `value`).
+        achieved = info["bytes"] / (ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": stored_traffic(args.workload),
-                           "kernel_avg_us": round(launch_ms * 1e3, 2)}
+                           "kernel_avg_us": round(ms * 1e3, 2)}
     else:
         out["roofline"] = None
         out["roofline_note"] = ("%d kernels per step; per-kernel durations are in the rocprofv3 "
                                 "summaries under profiles/" % info["kernels"])
-    if args.compare_torch:
-        tf = torch_fft_time(args.workload, info, torch, reps=args.steps)
-        tf["speedup"] = round(tf["call_us_mean"] / (launch_ms * 1e3), 3)  # against step_us mean
-        out["torch_fft"] = tf
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, info, args.cpu_budget)
     print(json.dumps(out), flush=True)

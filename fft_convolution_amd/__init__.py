@@ -32,7 +32,7 @@ __all__ = [
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
     "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar",
-    "fft_planar_workspace_size", "fft_status_string", "fft_last_error",
+    "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
     "Plan", "RealPlan", "poly_mul",
 ]
 
@@ -62,7 +62,7 @@ EXPORTS = (
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
     "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
     "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar",
-    "fft_planar_workspace_size", "fft_status_string", "fft_last_error",
+    "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
 )
 
 _lock = threading.Lock()
@@ -108,6 +108,7 @@ def lib():
         L.fft_exec_c2r.argtypes = [vp, vp, vp, i64, vp, vp]
         L.fft_exec_planar.argtypes = [vp, c_int, vp, vp, vp, vp, i64, vp, vp]
         L.fft_planar_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
+        L.fft_stream_copy.argtypes = [vp, vp, sz, vp]
         L.fft_status_string.argtypes = [c_int]
         L.fft_status_string.restype = ctypes.c_char_p
         L.fft_last_error.argtypes = []
@@ -251,6 +252,10 @@ def fft_planar_workspace_size(plan, batch: int) -> int:
     out = ctypes.c_size_t()
     _check(lib().fft_planar_workspace_size(plan, int(batch), ctypes.byref(out)), "fft_planar_workspace_size")
     return out.value
+
+
+def fft_stream_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check(lib().fft_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "fft_stream_copy")
 
 
 # --------------------------------------------------------------------------

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfftmi.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "rows.hip", "tiles.hip", "polymul.hip", "bluestein.hip", "real.hip", "mixed.hip"]
+SOURCES = ["api.cpp", "rows.hip", "tiles.hip", "polymul.hip", "bluestein.hip", "real.hip", "mixed.hip", "copy.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

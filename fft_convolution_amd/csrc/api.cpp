@@ -986,9 +986,10 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                         off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->passes[q].r);
                 }
             } else if (p->rank == 2)
-                snprintf(buf, len, "real dims=%lldx%lld prec=%s path=real2d col_stage=%d col_len=%lld",
+                snprintf(buf, len, "real dims=%lldx%lld prec=%s path=real2d col_stage=%d col_len=%lld folded=%d",
                          (long long)p->dims[0], (long long)p->dims[1], prec, 1 << p->logf,
-                         p->dims[0] > 1 ? 1LL << p->log_b : 0LL);
+                         p->dims[0] > 1 ? 1LL << p->log_b : 0LL,
+                         p->logf > 0 && r2c_fold_supported(p->prec, p->log_a, p->logf) ? 1 : 0);
             else
                 snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
                          p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
@@ -1803,7 +1804,10 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
     bool noop = false;
     size_t rbytes = 0, hbytes = 0;
     if (plan) real_sizes(plan, &rbytes, &hbytes);
-    const bool need_ws = plan && (plan->rank == 1 || plan->logf > 0 || plan->real_nd);
+    // Real images: a workspace only where the column stage runs as a pass
+    // of its own (the folded row pass writes the caller's output directly).
+    const bool need_ws = plan && (plan->rank == 1 || plan->real_nd ||
+                                  (plan->logf > 0 && !r2c_fold_supported(plan->prec, plan->log_a, plan->logf)));
     int st = check_real_exec(plan, in, rbytes, out, hbytes, batch, workspace, need_ws, &noop);
     if (st != FFT_OK || noop) return st;
     hipStream_t s = (hipStream_t)stream;
@@ -1855,6 +1859,18 @@ int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch,
         e = hipSuccess;
     }
     return real_done(e, "fft_exec_c2r", s);
+}
+
+int fft_stream_copy(const void* src, void* dst, size_t bytes, void* stream)
+{
+    if (bytes == 0) return FFT_OK;
+    if (!src || !dst) return fail(FFT_ERR_INVALID_ARG, "src or dst is NULL");
+    if (((uintptr_t)src | (uintptr_t)dst | bytes) & 15)
+        return fail(FFT_ERR_ALIGN, "src, dst and bytes must be multiples of 16");
+    if (ranges_overlap(src, bytes, dst, bytes)) return fail(FFT_ERR_OVERLAP, "src and dst overlap");
+    const hipError_t e = launch_stream_copy(src, dst, (int64_t)(bytes / 16), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fft_stream_copy");
+    return FFT_OK;
 }
 
 }  // extern "C"

@@ -205,4 +205,8 @@ hipError_t launch_real_n1(int prec, bool c2r, const void* in, void* out, int64_t
 // d_resid[0] = 0 (a kernel, not a memset, so the call is safe to capture).
 hipError_t launch_zero_resid(double* d_resid, hipStream_t stream);
 
+// Streaming copy of nvec 16-byte vectors (copy.hip): src and dst 16-byte
+// aligned, not overlapping.  A measurement aid, not part of any transform.
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t nvec, hipStream_t stream);
+
 }  // namespace fftmi

@@ -44,6 +44,23 @@ __device__ __forceinline__ void resid_max(double r, double* d_resid)
 
 __global__ void zero_resid_kernel(double* d) { *d = 0.0; }
 
+// The residual of one output value val (= Re(y) / N) rounded to r = rint(val):
+// |val - r|, or +infinity where that cannot vouch for the result -- |val| >=
+// 2^53, where every double is an integer and a rounding error no longer shows
+// as a fraction, or val not finite (NaN fails the comparison too).
+__device__ __forceinline__ double out_residual(double val, double r)
+{
+    return fabs(val) < 0x1p53 ? fabs(val - r) : __builtin_inf();
+}
+
+// r as int64 where it is in range; INT64_MIN (a value no exact product of
+// this size can take) where it is beyond the int64 range or not finite, so
+// that the conversion is always defined.
+__device__ __forceinline__ int64_t to_int64(double r)
+{
+    return fabs(r) < 0x1p63 ? (int64_t)r : INT64_MIN;
+}
+
 template <int LOGN> constexpr int poly_rows_per_wg() { return Geom<double2, LOGN>::T >= 256 ? 1 : 256 / Geom<double2, LOGN>::T; }
 
 // ---------------------------------------------------------------------------
@@ -90,8 +107,8 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
         if (live && n < lc) {
             const double val = va[i].x * inv_n;
             const double r = rint(val);
-            c[pair * lc + n] = (int64_t)r;
-            worst = fmax(worst, fabs(val - r));
+            c[pair * lc + n] = to_int64(r);
+            worst = fmax(worst, out_residual(val, r));
         }
     }
     resid_max(worst, d_resid);
@@ -252,8 +269,8 @@ void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_
         if (n < lc) {
             const double val = v[i].x * inv_n;
             const double r = rint(val);
-            dst[n] = (int64_t)r;
-            worst = fmax(worst, fabs(val - r));
+            dst[n] = to_int64(r);
+            worst = fmax(worst, out_residual(val, r));
         }
     }
     resid_max(worst, d_resid);

@@ -232,8 +232,12 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
  *   workspace: fft_poly_mul_workspace_size(plan, batch) bytes.
  *   d_max_residual: NULL, or a device double that receives
  *          max |Re(y)/N - rint(Re(y)/N)| over all outputs (overwritten, not
- *          accumulated).  The result is exact when this stays well below 0.5;
- *          callers with coefficients near the fp64 limit should check it.
+ *          accumulated), or +infinity if any output has |Re(y)/N| >= 2^53 or
+ *          is not finite: past 2^53 every double is an integer, so a rounding
+ *          error no longer shows as a fraction and exactness cannot be
+ *          vouched for.  The result is exact when this stays well below 0.5;
+ *          callers with large coefficients should check it.  Outputs beyond
+ *          the int64 range (or not finite) are stored as INT64_MIN.
  * Errors: INVALID_ARG, RANK, PRECISION, NOT_POW2, UNSUPPORTED_SIZE, ALIGN,
  *         OVERLAP, WORKSPACE, DEVICE.
  */
@@ -287,7 +291,10 @@ int fft_plan_create_real_2d(fft_plan** plan, int64_t h, int64_t w, int prec);
  *              FFT_MAX_LDS_N_* (one kernel), batch * N/2 complex values beyond.
  *   Images (fft_plan_create_real_2d): in [batch][H][W] real, out
  *              [batch][H][W/2 + 1] complex; the workspace (batch H (W/2 + 1)
- *              complex values) is needed for H > 512 only.
+ *              complex values, the size fft_workspace_size reports, which
+ *              covers fft_exec_c2r too) is needed only for H > 512 on plans
+ *              whose radix-F column stage is not folded into the row pass
+ *              (fft_plan_describe: folded=0); with folded=1 it may be NULL.
  * Errors: INVALID_ARG, RANK, ALIGN, OVERLAP, WORKSPACE, DEVICE.
  */
 int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream);
@@ -306,6 +313,19 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
  * Errors: as fft_exec_r2c.
  */
 int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream);
+
+/*
+ * Measurement aid, not part of any transform: copy `bytes` bytes from src to
+ * dst (device memory) with a streaming kernel that reads every byte once and
+ * writes it once, as the row kernels stream their rows ("Stockham FFT
+ * Butterfly Algorithm in Parallel GLSL", section "Performance and Pipeline
+ * Evaluation": the transform is bound by memory throughput, so a plain copy
+ * of the same bytes is its practical ceiling).  Enqueued on `stream`.
+ *   src, dst: 16-byte aligned, not overlapping; bytes a multiple of 16
+ *             (0 is a no-op).
+ * Errors: INVALID_ARG (NULL), ALIGN, OVERLAP, DEVICE.
+ */
+int fft_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char* fft_status_string(int status);

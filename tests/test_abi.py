@@ -198,3 +198,13 @@ def test_valid_real_2d_plan_without_gpu_is_a_device_error():
         hd = ctypes.c_void_p(12345)
         assert fm.lib().fft_plan_create_real_2d(ctypes.byref(hd), h, w, prec) == fm.FFT_ERR_DEVICE
         assert hd.value is None
+
+
+def test_stream_copy_rejects_before_any_hip_call():
+    L = fm.lib()
+    assert L.fft_stream_copy(None, None, 0, None) == fm.FFT_OK  # nothing to copy
+    assert L.fft_stream_copy(None, 4096, 64, None) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_stream_copy(4096, None, 64, None) == fm.FFT_ERR_INVALID_ARG
+    assert L.fft_stream_copy(4096 + 8, 1 << 20, 64, None) == fm.FFT_ERR_ALIGN
+    assert L.fft_stream_copy(4096, 1 << 20, 63, None) == fm.FFT_ERR_ALIGN
+    assert L.fft_stream_copy(4096, 4096 + 32, 64, None) == fm.FFT_ERR_OVERLAP

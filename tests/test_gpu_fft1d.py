@@ -91,20 +91,23 @@ def test_workload_n1024_b64_forward_and_round_trip(dev):
     assert rel_rms_rows(back.cpu().numpy(), x_np).max() <= fft_tol(1024)
 
 
-def test_workload_n4096_b16384_sampled_rows(dev):
-    # The full 16384 x 4096 batch in the launch the benchmark times; the oracle
-    # checks 64 sampled rows (first, last and 62 random), and every row must
-    # satisfy Parseval.
+def test_workload_n4096_b16384_every_row(dev):
+    # The full 16384 x 4096 batch in the launch the benchmark times; every row
+    # against the oracle (in chunks of 2048 rows to bound host memory), and
+    # every row must also satisfy Parseval.
     x_np = wl.workload_input("c2c_n4096_b16384")
     plan = fm.Plan(4096, torch.complex64)
     x = torch.from_numpy(x_np).to(dev)
     y = torch.empty_like(x)
     fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, y, 16384, None)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 16383], rng.integers(0, 16384, 62)]))
-    yr = y[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    assert rel_rms_rows(yr, oracle.fft(x_np[rows])).max() <= fft_tol(4096)
+    y_np = y.cpu().numpy()
+    worst = 0.0
+    for r0 in range(0, 16384, 2048):
+        err = rel_rms_rows(y_np[r0:r0 + 2048], oracle.fft(x_np[r0:r0 + 2048]))
+        assert err.shape == (2048,)
+        worst = max(worst, float(err.max()))
+    assert worst <= fft_tol(4096), worst
     ex = (x.abs() ** 2).sum(dim=1).double()
     ey = (y.abs() ** 2).sum(dim=1).double() / 4096
     assert float(((ey - ex).abs() / ex).max()) < 1e-5

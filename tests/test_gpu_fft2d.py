@@ -53,8 +53,8 @@ def test_fft2_c128(dev, h, w, batch):
 
 def test_workload_2048x2048_b8(dev):
     # The full 8-image plane-wave workload in the launch the benchmark times.
-    # Two images (first and last) against the oracle; on all 8 images the 16
-    # largest bins are exactly the planted frequencies, with value ~H W e^{i phi}.
+    # Every image against the oracle; on every image the 16 largest bins are
+    # also exactly the planted frequencies, with value ~H W e^{i phi}.
     h = w = 2048
     x_np, (fy, fx, phi) = wl.plane_waves_2d(h, w, 8, seed=4, with_params=True)
     plan = fm.Plan((h, w), torch.complex64)
@@ -62,7 +62,7 @@ def test_workload_2048x2048_b8(dev):
     y = torch.empty_like(x)
     fm.fft_exec_2d(plan.handle, fm.FFT_FORWARD, x, y, 8, None)
     torch.cuda.synchronize()
-    for b in (0, 7):
+    for b in range(8):
         ref = oracle.fft2(x_np[b])
         err = rel_rms_rows(y[b].cpu().numpy().reshape(1, -1), ref.reshape(1, -1))
         assert err.max() <= fft_tol(h * w)
@@ -128,7 +128,7 @@ def test_fft2_split_column_stage(dev, h, w, dtype, batch):
     X = plan.fft2(x)
     assert rel_rms_rows(_flat(X.cpu().numpy()), _flat(oracle.fft2(x_np))).max() <= tol
     back = plan.ifft2(X).cpu().numpy()
-    assert rel_rms_rows(_flat(back), _flat(x_np)).max() <= 2 * tol
+    assert rel_rms_rows(_flat(back), _flat(x_np)).max() <= tol
     z = x.clone()
     plan.fft2(z, out=z)
     torch.cuda.synchronize()

@@ -27,7 +27,7 @@ def test_max_power_of_two(dev, logn, dtype):
     X = plan.fft(x)
     tol = fft_tol(n, dtype == torch.complex128)
     assert rel_rms_rows(X.cpu().numpy(), oracle.fft(x_np)).max() <= tol
-    assert rel_rms_rows(plan.ifft(X).cpu().numpy(), x_np).max() <= 2 * tol
+    assert rel_rms_rows(plan.ifft(X).cpu().numpy(), x_np).max() <= tol
     with pytest.raises(fm.FFTError) as e:
         fm.Plan(2 * n, dtype)
     assert e.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE
@@ -46,10 +46,10 @@ def test_max_bluestein(dev, dtype):
     Xn = X.cpu().numpy()
     ks = np.unique(np.concatenate([[0, 1, n // 2, n - 1], np.random.default_rng(5).integers(0, n, 20)]))
     ref = oracle.dft_sample(x_np, ks)
-    m = 1 << 24
-    err = np.sqrt(np.mean(np.abs(Xn[:, ks] - ref) ** 2)) / np.sqrt(np.mean(np.abs(Xn) ** 2))
-    assert err <= fft_tol(m, dtype == torch.complex128)
-    assert rel_rms_rows(plan.ifft(X).cpu().numpy(), x_np).max() <= 2 * fft_tol(m, dtype == torch.complex128)
+    # relative RMS over the sampled bins, against the reference's own RMS there
+    err = np.sqrt(np.mean(np.abs(Xn[:, ks] - ref) ** 2)) / np.sqrt(np.mean(np.abs(ref) ** 2))
+    assert err <= fft_tol(n, dtype == torch.complex128)
+    assert rel_rms_rows(plan.ifft(X).cpu().numpy(), x_np).max() <= fft_tol(n, dtype == torch.complex128)
     with pytest.raises(fm.FFTError) as e:
         fm.Plan((1 << 23) + 1, dtype)
     assert e.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE
@@ -67,7 +67,7 @@ def test_max_real(dev, logn, dtype):
     X = plan.rfft(x)
     tol = fft_tol(n, dtype == torch.float64)
     assert rel_rms_rows(X.cpu().numpy(), oracle.rfft(x_np)).max() <= tol
-    assert rel_rms_rows(plan.irfft(X).cpu().numpy(), x_np).max() <= 2 * tol
+    assert rel_rms_rows(plan.irfft(X).cpu().numpy(), x_np).max() <= tol
     with pytest.raises(fm.FFTError) as e:
         fm.RealPlan(2 * n, dtype)
     assert e.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE

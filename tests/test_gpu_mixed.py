@@ -40,7 +40,7 @@ def _check(n, batch, dtype, seed):
     z = plan.ifft(x).cpu().numpy()
     assert rel_rms_rows(z, oracle.dft(x_np, inverse=True)).max() <= tol
     back = plan.ifft(plan.fft(x)).cpu().numpy()
-    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+    assert rel_rms_rows(back, x_np).max() <= tol
 
 
 @pytest.mark.parametrize("n", F32)
@@ -169,10 +169,10 @@ def test_mixpass(dev, n, dtype, batch):
         else:
             ref = oracle.dft_sample(x_np, ks, inverse=inverse)
             err = (np.sqrt(np.mean(np.abs(y[:, ks] - ref) ** 2, axis=1)) /
-                   np.sqrt(np.mean(np.abs(y) ** 2, axis=1))).max()
+                   np.sqrt(np.mean(np.abs(ref) ** 2, axis=1))).max()
         assert err <= tol, (inverse, err)
     back = plan.ifft(plan.fft(x)).cpu().numpy()
-    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+    assert rel_rms_rows(back, x_np).max() <= tol
     z = x.clone()
     plan.fft(z, out=z)
     ref = plan.fft(x)

@@ -15,6 +15,11 @@ from fft_convolution_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
+def _ws(plan, batch, dev):
+    nbytes = fm.fft_poly_mul_workspace_size(plan.handle, batch)
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+
 def _gpu_mul(a_np, b_np, n, dev):
     a = torch.from_numpy(np.ascontiguousarray(a_np)).to(dev)
     b = torch.from_numpy(np.ascontiguousarray(b_np)).to(dev)
@@ -110,3 +115,35 @@ def test_validation_on_device(dev):
         fm.fft_poly_mul(plan.handle, a, 20, b, 30, a, 2)   # c overlaps a
     assert e.value.status == fm.FFT_ERR_OVERLAP
     fm.fft_poly_mul(plan.handle, a, 20, b, 30, c, 0)        # batch 0: no-op
+
+
+@pytest.mark.parametrize("n", [64, 8192])
+def test_residual_flags_results_past_2p53(dev, n):
+    """Products of at least 2^53 cannot be vouched for by the rounding
+    residual (every double there is an integer): the residual must then read
+    +inf, and values beyond int64 come back as INT64_MIN.  Both the one-kernel
+    route (N = 64) and the split route (N = 8192)."""
+    print("case residual flag n=%d" % n, flush=True)
+    plan = fm.Plan(n, torch.complex128)
+    resid = torch.full((1,), -1.0, dtype=torch.float64, device=dev)
+    # exact: small coefficients, residual finite and small
+    a = torch.tensor([[3, 1, 4, 1, 5]], dtype=torch.int64, device=dev)
+    b = torch.tensor([[2, 7, 1]], dtype=torch.int64, device=dev)
+    c = torch.empty(1, 7, dtype=torch.int64, device=dev)
+    fm.fft_poly_mul(plan.handle, a, 5, b, 3, c, 1, _ws(plan, 1, dev), resid)
+    torch.cuda.synchronize()
+    assert c.cpu().numpy().tolist() == oracle.schoolbook(a.cpu().numpy(), b.cpu().numpy()).tolist()
+    assert 0.0 <= float(resid) < 0.1
+    # (2^27 + 2^27 z)^2 = 2^54 + 2^55 z + 2^54 z^2: every coefficient >= 2^53
+    big = torch.full((1, 2), 1 << 27, dtype=torch.int64, device=dev)
+    c2 = torch.empty(1, 3, dtype=torch.int64, device=dev)
+    fm.fft_poly_mul(plan.handle, big, 2, big, 2, c2, 1, _ws(plan, 1, dev), resid)
+    torch.cuda.synchronize()
+    assert math.isinf(float(resid)) and float(resid) > 0
+    # (2^40)^2 = 2^80, beyond int64: stored as INT64_MIN, residual +inf
+    huge = torch.full((1, 1), 1 << 40, dtype=torch.int64, device=dev)
+    c3 = torch.empty(1, 1, dtype=torch.int64, device=dev)
+    fm.fft_poly_mul(plan.handle, huge, 1, huge, 1, c3, 1, _ws(plan, 1, dev), resid)
+    torch.cuda.synchronize()
+    assert int(c3[0, 0]) == -(1 << 63)
+    assert math.isinf(float(resid))

@@ -41,7 +41,7 @@ def _run(logn, batch, dtype, seed):
     assert rel_rms_rows(y, yref).max() <= tol, rel_rms_rows(y, yref).max()
     # round trip
     back = plan.irfft(plan.rfft(x)).cpu().numpy()
-    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+    assert rel_rms_rows(back, x_np).max() <= tol
     return plan
 
 
@@ -86,24 +86,22 @@ def test_real_closed_forms(dev, n):
     assert np.abs(imp - want).max() < 1e-13
 
 
-def test_real_sampled_bins_at_full_size(dev):
-    """The real-row workload's shape (8192-point rows): 256 rows checked in full,
-    then sampled bins of rows across the whole batch by the direct DFT."""
+def test_real_every_row_at_full_size(dev):
+    """The real-row workload (16384 rows of 8192 points) in the launch the
+    benchmark times: every row against the oracle (in chunks of 2048 rows to
+    bound host memory), then every row back through C2R."""
     spec = wl.WORKLOADS["r2c_n8192_b16384"]
     n, batch = spec["n"], spec["batch"]
     x_np = wl.real_normal(n, batch, seed=spec["seed"])
     x = torch.from_numpy(x_np).cuda()
     plan = fm.RealPlan(n, torch.float32)
-    X = plan.rfft(x).cpu().numpy()
-    rows = np.random.default_rng(0).choice(batch, 256, replace=False)
-    assert rel_rms_rows(X[rows], oracle.rfft(x_np[rows])).max() <= fft_tol(n)
-    ks = np.array([0, 1, 2, n // 4, n // 2 - 1, n // 2])
-    tail = np.arange(batch - 4, batch)
-    ref = oracle.dft_sample(x_np[tail].astype(np.complex128), ks)
-    scale = np.sqrt(np.mean(np.abs(X[tail]) ** 2, axis=1, keepdims=True))
-    assert (np.abs(X[tail][:, ks] - ref) / scale).max() <= 10 * fft_tol(n)
-    back = plan.irfft(torch.from_numpy(X).cuda()).cpu().numpy()
-    assert rel_rms_rows(back[rows], x_np[rows]).max() <= 2 * fft_tol(n)
+    Xt = plan.rfft(x)
+    X = Xt.cpu().numpy()
+    back = plan.irfft(Xt).cpu().numpy()
+    for r0 in range(0, batch, 2048):
+        sl = slice(r0, r0 + 2048)
+        assert rel_rms_rows(X[sl], oracle.rfft(x_np[sl])).max() <= fft_tol(n)
+        assert rel_rms_rows(back[sl], x_np[sl]).max() <= fft_tol(n)
 
 
 def test_real_errors_and_kinds(dev):
@@ -183,4 +181,4 @@ def test_real_even_lengths(dev, n, dtype, batch):
     y = plan.irfft(torch.from_numpy(S_np).cuda()).cpu().numpy()
     assert rel_rms_rows(y, oracle.irfft(S_np, n)).max() <= tol
     back = plan.irfft(plan.rfft(x)).cpu().numpy()
-    assert rel_rms_rows(back, x_np).max() <= 2 * tol
+    assert rel_rms_rows(back, x_np).max() <= tol

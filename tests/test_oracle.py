@@ -616,3 +616,63 @@ def test_planted_mistakes_are_caught(tmp_path):
                   "ORACLE_PLANT_TWIDDLE_STEP", "ORACLE_PLANT_CONJ_PRODUCT",
                   "ORACLE_PLANT_POLY_SHIFT"):
         assert not _pins_hold(_build_mutant(tmp_path, macro)), macro
+
+
+def _poly_eval_pins_hold(fn):
+    """Hand-worked values of sum_k c_k z^k mod p (p = 2^61 - 1), coefficient
+    k the factor of z^k as in the product c_k = sum_i a_i b_{k-i} ("FFT on
+    GPU", polynomial multiplication section).  Returns whether all hold."""
+    p = oracle.MOD_P
+    checks = [
+        (([1, 2, 3], 10), 321),             # 1 + 2*10 + 3*100, not 123 (order of coefficients)
+        (([7], 12345), 7),                  # a constant
+        (([0, 1], 5), 5),                   # z itself
+        (([5, 0, 1], 1 << 31), 7),          # 5 + 2^62, and 2^62 = 2 (2^61 - 1) + 2: wraps once
+        (([0, 0, 0, 1], 1 << 21), 4),       # 2^63 = 4 (2^61 - 1) + 4
+        (([7, 3, 9], p), 7),                # z = p = 0 (mod p): only c_0 survives
+        (([4, 5, 6], 1), 15),               # z = 1: the sum
+        (([4, 5, 6], p - 1), 5),            # z = -1: 4 - 5 + 6
+        (([p - 1, 2], 3), 5),               # -1 + 2*3, the coefficient reduced
+        (([], 9), 0),                       # the empty polynomial
+    ]
+    return all(fn(c, z) == want for (c, z), want in checks)
+
+
+def test_poly_eval_mod_hand_values():
+    assert _poly_eval_pins_hold(oracle.poly_eval_mod)
+
+
+def test_poly_eval_mod_pins_reject_planted_mistakes():
+    # Plausible mistakes in a Horner evaluation, each planted in a copy on the
+    # CPU: every one must fail at least one hand value.
+    p = oracle.MOD_P
+
+    def constant(c, z):
+        return 0
+
+    def reversed_order(c, z):
+        acc = 0
+        for v in [int(x) for x in c]:  # highest power taken from c_0
+            acc = (acc * z + v) % p
+        return acc
+
+    def no_reduction(c, z):
+        acc = 0
+        for v in reversed([int(x) for x in c]):
+            acc = acc * z + v
+        return acc
+
+    def dropped_constant(c, z):
+        acc = 0
+        for v in reversed([int(x) for x in c][1:]):
+            acc = (acc * z + v) % p
+        return acc * z % p
+
+    def other_modulus(c, z):
+        acc = 0
+        for v in reversed([int(x) for x in c]):
+            acc = (acc * z + v) % (p + 2)
+        return acc
+
+    for bad in (constant, reversed_order, no_reduction, dropped_constant, other_modulus):
+        assert not _poly_eval_pins_hold(bad), bad.__name__
