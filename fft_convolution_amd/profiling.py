@@ -19,6 +19,15 @@ Three subcommands, all reading the CSV output of ``rocprofv3 --output-format csv
                python -m fft_convolution_amd.profiling traffic --fetch DIR1 --write DIR2 \\
                    --kernel rows_kernel --copy-bytes B --workload W --out profiles/traffic_W.json
 
+``sq``      -- instruction-level counters per kernel from one ``--pmc`` run of
+               SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT
+               SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES GRBM_GUI_ACTIVE:
+               per wave, VALU and LDS instructions and LDS bank-conflict cycles;
+               the conflict rate (conflict cycles / LDS active cycles) and VALU
+               busy (100 * SQ_ACTIVE_INST_VALU * 4 / SIMDs / GRBM_GUI_ACTIVE, the
+               usual definition, 1024 SIMDs on MI355X):
+               python -m fft_convolution_amd.profiling sq DIR --stats DIR2 --out profiles/sq_W.md --cmd "..."
+
 The traffic record carries a digest of the kernel sources; ``bench.py``
 reports it only while the sources are unchanged.
 """
@@ -171,6 +180,44 @@ def cmd_counters(args):
     print(text)
 
 
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+               "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+MI355X_SIMDS = 256 * 4
+
+
+def cmd_sq(args):
+    vals = {c: counter_values(args.dir, c) for c in SQ_COUNTERS}
+    durations = {r["name"]: r["avg_ns"] for r in kernel_stats(args.stats)} if args.stats else {}
+    med = lambda c, k: statistics.median(vals[c][k]) if vals[c].get(k) else float("nan")
+    lines = ["# LDS and VALU counters per kernel: %s" % args.title, "",
+             "Commands (R = repository root):", "", "```"] + list(args.cmd) + ["```", "",
+             "Per wave: instructions and LDS bank-conflict cycles (SQ_LDS_BANK_CONFLICT / SQ_WAVES). "
+             "Conflict %% = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS. VALU busy %% = 100 * "
+             "SQ_ACTIVE_INST_VALU * 4 / %d SIMDs / GRBM_GUI_ACTIVE. Medians over dispatches." % MI355X_SIMDS, "",
+             "| kernel | dispatches | avg us | waves | VALU inst / wave | LDS inst / wave | "
+             "conflict cycles / wave | conflict % | VALU busy % |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(vals["SQ_WAVES"], key=lambda k: -med("SQ_WAVES", k)):
+        if "copyBuffer" in k or "elementwise" in k:
+            continue
+        waves = med("SQ_WAVES", k)
+        if not waves:
+            continue
+        lds_act = med("SQ_ACTIVE_INST_LDS", k)
+        conf = med("SQ_LDS_BANK_CONFLICT", k)
+        gui = med("GRBM_GUI_ACTIVE", k)
+        busy = 100.0 * med("SQ_ACTIVE_INST_VALU", k) * 4 / MI355X_SIMDS / gui if gui else float("nan")
+        us = next((v for n, v in durations.items() if n == k), 0.0) / 1e3
+        lines.append("| `%s` | %d | %.1f | %d | %.0f | %.1f | %.1f | %.1f | %.1f |" % (
+            _short(k), len(vals["SQ_WAVES"][k]), us, waves, med("SQ_INSTS_VALU", k) / waves,
+            med("SQ_INSTS_LDS", k) / waves, conf / waves, 100.0 * conf / lds_act if lds_act else 0.0, busy))
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -201,6 +248,13 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", nargs="*", default=[])
     t.set_defaults(fn=cmd_traffic)
+    q = sub.add_parser("sq")
+    q.add_argument("dir")
+    q.add_argument("--stats")
+    q.add_argument("--title", default="")
+    q.add_argument("--out")
+    q.add_argument("--cmd", nargs="*", default=[])
+    q.set_defaults(fn=cmd_sq)
     args = ap.parse_args(argv)
     args.fn(args)
 
