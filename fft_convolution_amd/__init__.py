@@ -30,10 +30,10 @@ __all__ = [
     "FFT_MAX_LDS_N_C32", "FFT_MAX_LDS_N_C64", "FFT_MAX_N_C32", "FFT_MAX_N_C64", "FFT_MAX_BLUESTEIN_N",
     "lib", "lib_path", "EXPORTS",
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
-    "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
-    "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar",
-    "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
-    "Plan", "RealPlan", "poly_mul",
+    "fft_exec_c2c", "fft_exec_c2c_noalloc", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size",
+    "fft_poly_mul", "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r",
+    "fft_exec_planar", "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
+    "FFT_NOALLOC_SCRATCH_BYTES", "Plan", "RealPlan", "poly_mul",
 ]
 
 FFT_C32, FFT_C64 = 0, 1
@@ -53,6 +53,7 @@ FFT_MAX_LDS_N_C64 = 4096
 FFT_MAX_N_C32 = 1 << 26
 FFT_MAX_N_C64 = 1 << 24
 FFT_MAX_BLUESTEIN_N = 1 << 23
+FFT_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfftmi.so")
@@ -60,9 +61,9 @@ lib_path = os.path.join(_HERE, "libfftmi.so")
 # Every symbol include/fftmi.h declares.
 EXPORTS = (
     "fft_plan_create", "fft_plan_destroy", "fft_plan_describe", "fft_plan_query", "fft_workspace_size",
-    "fft_exec_c2c", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size", "fft_poly_mul",
-    "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r", "fft_exec_planar",
-    "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
+    "fft_exec_c2c", "fft_exec_c2c_noalloc", "fft_exec_2d", "fft_exec_3d", "fft_poly_mul_workspace_size",
+    "fft_poly_mul", "fft_plan_create_real", "fft_plan_create_real_2d", "fft_exec_r2c", "fft_exec_c2r",
+    "fft_exec_planar", "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
 )
 
 _lock = threading.Lock()
@@ -98,6 +99,7 @@ def lib():
         L.fft_plan_query.argtypes = [c_int, ctypes.POINTER(i64), c_int, ctypes.c_char_p, sz]
         L.fft_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         L.fft_exec_c2c.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
+        L.fft_exec_c2c_noalloc.argtypes = [vp, c_int, vp, vp, i64, vp]
         L.fft_exec_2d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
         L.fft_exec_3d.argtypes = [vp, c_int, vp, vp, i64, vp, vp]
         L.fft_poly_mul_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
@@ -192,6 +194,11 @@ def fft_workspace_size(plan, batch: int) -> int:
 def fft_exec_c2c(plan, dir: int, in_, out, batch: int, workspace=None, stream=None) -> None:
     _check(lib().fft_exec_c2c(plan, int(dir), _ptr(in_), _ptr(out), int(batch), _ptr(workspace),
                               _stream(stream)), "fft_exec_c2c")
+
+
+def fft_exec_c2c_noalloc(plan, dir: int, in_, out, batch: int, stream=None) -> None:
+    _check(lib().fft_exec_c2c_noalloc(plan, int(dir), _ptr(in_), _ptr(out), int(batch), _stream(stream)),
+           "fft_exec_c2c_noalloc")
 
 
 def fft_exec_2d(plan, dir: int, in_, out, batch: int, workspace=None, stream=None) -> None:

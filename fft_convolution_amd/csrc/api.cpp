@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1859,6 +1860,60 @@ int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch,
         e = hipSuccess;
     }
     return real_done(e, "fft_exec_c2r", s);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch for fft_exec_c2c_noalloc: a file-scope device array, one copy per
+// GPU (each holds it from the first use until the process ends).  Host code
+// never passes `scratch` itself to a kernel: its device address on the current
+// device comes from hipGetSymbolAddress, taken once per device and kept.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[FFT_NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on device `dev` (current), looked up on the
+// first call for that device.
+static int scratch_address(int dev, void** ptr)
+{
+    if (dev < 0 || dev >= kScratchDevices) return fail(FFT_ERR_DEVICE, "device %d beyond the scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(FFT_ERR_DEVICE, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return FFT_OK;
+}
+
+extern "C" {
+
+int fft_exec_c2c_noalloc(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* stream)
+{
+    // every argument but the workspace, before any HIP call
+    bool noop = false;
+    int st = check_exec(plan, dir, 1, in, out, batch, nullptr, 0, &noop);
+    if (st != FFT_OK || noop) return st;
+    const size_t need = c2c_workspace(plan, batch);
+    if (need > (size_t)FFT_NOALLOC_SCRATCH_BYTES)
+        return fail(FFT_ERR_WORKSPACE, "%zu bytes of workspace needed, more than the %zu bytes of scratch the "
+                    "no-allocation entry point holds (use fft_exec_c2c with a workspace)", need,
+                    (size_t)FFT_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need) {
+        if ((st = check_device(plan)) != FFT_OK) return st;
+        if ((st = scratch_address(plan->device, &ws)) != FFT_OK) return st;
+    }
+    return fft_exec_c2c(plan, dir, in, out, batch, ws, stream);
 }
 
 int fft_stream_copy(const void* src, void* dst, size_t bytes, void* stream)

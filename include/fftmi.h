@@ -164,6 +164,29 @@ int fft_exec_c2c(const fft_plan* plan, int dir, const void* in, void* out, int64
                  void* workspace, void* stream);
 
 /*
+ * fft_exec_c2c without any allocation, for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it).  The same transform, kernels and results as fft_exec_c2c,
+ * but plans that need a workspace take it from a scratch array the library
+ * holds in device memory: FFT_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU,
+ * reserved on each GPU from its first call there until the process ends
+ * (enough for one 2^24-point complex64 transform, or batch x N <= 2^24
+ * complex64 / 2^23 complex128 elements on the multi-pass path).
+ *   in, out, batch, dir, stream: as fft_exec_c2c.
+ *   The scratch is shared by every call on a GPU and keeps the last call's
+ *   contents; no part of it needs to start at zero (every kernel writes what
+ *   it later reads).  Calls on one GPU whose executions overlap (different
+ *   streams, or host threads racing) use the same scratch and RACE: order
+ *   them on one stream or synchronise between them.
+ * Calls no hipMalloc, hipFree or other allocating routine; the first call on
+ * a device looks up the scratch's device address (hipGetSymbolAddress).
+ * Errors: as fft_exec_c2c, plus WORKSPACE when fft_workspace_size(plan,
+ * batch) exceeds FFT_NOALLOC_SCRATCH_BYTES (checked before any HIP call).
+ */
+#define FFT_NOALLOC_SCRATCH_BYTES (128LL << 20)
+int fft_exec_c2c_noalloc(const fft_plan* plan, int dir, const void* in, void* out, int64_t batch, void* stream);
+
+/*
  * Batched 2D transform with a rank-2 plan: row transforms of length W over
  * every row, then column transforms of length H over every column.
  *   in, out:   [batch][H][W] complex, images contiguous.  in == out allowed.
