@@ -189,22 +189,23 @@ def rfft(x) -> np.ndarray:
 
 
 def irfft(X, n: int) -> np.ndarray:
-    """The real rows of length n whose transform has X_0 .. X_{n/2} equal to
-    the rows of X ([..., n // 2 + 1]): every bin k > n/2 is set to
-    conj X_{n-k}, the imaginary parts of X_0 and X_{n/2} are dropped (a real
-    row has real values there), then the real part of :func:`ifft`."""
+    """The real rows of length n whose transform has X_0 .. X_{floor(n/2)}
+    equal to the rows of X ([..., n // 2 + 1]): every bin k > n/2 is set to
+    conj X_{n-k}, the imaginary part of X_0 is dropped, and for even n that
+    of X_{n/2} too (a real row has real values there; an odd n has no such
+    middle bin), then the real part of :func:`ifft`."""
     X = _as_c128(X)
     h = n // 2
     if X.shape[-1] != h + 1:
         raise ValueError("irfft of length %d takes %d values per row" % (n, h + 1))
-    if n > 1 and n % 2:
-        raise ValueError("irfft takes an even length")
     full = np.empty(X.shape[:-1] + (n,), dtype=np.complex128)
     full[..., : h + 1] = X[..., : h + 1] if n > 1 else X[..., :1]
     full[..., 0] = full[..., 0].real
-    if n > 1:
+    if n > 1 and n % 2 == 0:
         full[..., h] = full[..., h].real
         full[..., h + 1:] = np.conj(X[..., 1:h][..., ::-1])
+    elif n > 1:
+        full[..., h + 1:] = np.conj(X[..., 1:h + 1][..., ::-1])
     return (ifft(full) if n & (n - 1) == 0 else dft(full, inverse=True)).real
 
 

@@ -398,7 +398,8 @@ def test_fft3_matches_numpy_separability_and_closed_form():
 # Polynomial multiplication
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n", [1, 2, 4, 8, 64, 4096, 1 << 17, 6, 10, 100, 1000, 2002])
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 64, 4096, 1 << 17, 6, 10, 100, 1000, 2002,
+                               3, 5, 7, 9, 15, 27, 101, 999, 1001])
 def test_rfft_irfft_match_numpy(n):
     rng = np.random.default_rng(n)
     x = rng.standard_normal((3, n))
@@ -409,23 +410,37 @@ def test_rfft_irfft_match_numpy(n):
     back = oracle.irfft(X, n)
     assert np.abs(back - x).max() <= 1e-13 * max(1.0, math.log2(n))
     # a spectrum that is not the half of a real row's: numpy's pocketfft c2r
-    # also takes the DC and Nyquist bins as real
+    # also takes the DC and (even n) Nyquist bins as real
     Y = rng.standard_normal((2, n // 2 + 1)) + 1j * rng.standard_normal((2, n // 2 + 1))
     assert np.abs(oracle.irfft(Y, n) - np.fft.irfft(Y, n)).max() <= 1e-13 * max(1.0, math.log2(n))
 
 
-def test_rfft_even_lengths_closed_form_and_odd_rejected():
-    # a cosine of frequency f in a 1000-point row: N/2 at bin f (f < N/2)
-    n = 1000
-    t = np.arange(n)
-    for f in (0, 3, 499, 500):
-        x = np.cos(2 * np.pi * ((f * t) % n) / n)
-        X = oracle.rfft(x[None, :])[0]
-        want = np.zeros(n // 2 + 1, complex)
-        want[f] = n if f in (0, n // 2) else n / 2
-        assert np.abs(X - want).max() < 1e-9
+def test_rfft_closed_forms_even_and_odd_lengths():
+    # a cosine of frequency f in an N-point row: N/2 at bin f (0 < f < N/2),
+    # N at f = 0 and, for even N, at f = N/2 (the two halves of the cosine
+    # meet there); an odd N has no middle bin
+    for n in (1000, 999, 15):
+        t = np.arange(n)
+        for f in sorted({0, 3 % n, n // 2 - 1, n // 2}):
+            x = np.cos(2 * np.pi * ((f * t) % n) / n)
+            X = oracle.rfft(x[None, :])[0]
+            want = np.zeros(n // 2 + 1, complex)
+            want[f] = n if (f == 0 or 2 * f == n) else n / 2
+            assert np.abs(X - want).max() < 1e-9, (n, f)
+            # and back: irfft of that half gives the cosine again
+            assert np.abs(oracle.irfft(X[None, :], n)[0] - x).max() < 1e-12, (n, f)
+    # odd N: the half spectrum of a unit impulse at 4 is w^{4k}, k <= (N-1)/2,
+    # and irfft brings the impulse back; an imaginary part at X_0 is dropped
+    n = 9
+    k = np.arange(n // 2 + 1)
+    half = np.exp(-2j * np.pi * 4 * k / n)
+    half[0] += 5j
+    imp = oracle.irfft(half[None, :], n)[0]
+    want = np.zeros(n)
+    want[4] = 1.0
+    assert np.abs(imp - want).max() < 1e-13
     with pytest.raises(ValueError):
-        oracle.irfft(np.zeros((1, 3), complex), 5)
+        oracle.irfft(np.zeros((1, 4), complex), 5)  # 5 points take 3 bins
 
 
 def test_rfft_closed_forms_and_hermitian_half():
@@ -459,7 +474,8 @@ def test_rfft_closed_forms_and_hermitian_half():
 
 
 @pytest.mark.parametrize("h,w", [(1, 2), (2, 1 << 1), (4, 8), (16, 64), (64, 2), (128, 256),
-                                 (3, 10), (12, 30), (100, 8), (7, 100), (1, 6)])
+                                 (3, 10), (12, 30), (100, 8), (7, 100), (1, 6),
+                                 (3, 7), (5, 9), (4, 15), (1, 5), (8, 1)])
 def test_rfft2_irfft2_match_numpy(h, w):
     rng = np.random.default_rng(h * 1000 + w)
     x = rng.standard_normal((2, h, w))
