@@ -21,7 +21,8 @@ Prints ONE JSON line with:
   launch_us  a separate pass with a pair of events around every launch: mean /
              median / min / max of the per-launch durations
   copy_ceiling  the library's streaming copy (fft_stream_copy: every byte read
-             once and written once, nontemporal 16-byte lanes) of the same byte
+             once and written once, nontemporal 8-byte lanes as in the row
+             kernels, the fastest copy measured) of the same byte
              count, timed like the steps, and the step's algorithmic rate as a
              fraction of the copy's (the practical ceiling of the access pattern)
   rotated    the same steps cycling over --rotate buffer sets (default 3), so

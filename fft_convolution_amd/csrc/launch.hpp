@@ -71,6 +71,11 @@ hipError_t launch_mixed_pass(int prec, const MixedPassArgs& a, const MixedSchedu
                              int64_t batch, const void* tw, const BigTwiddle& big, double scale, hipStream_t stream,
                              const void* in_im = nullptr, void* out_im = nullptr);
 
+// nmat matrices [rows][cols] -> [cols][rows] (tiles.hip); in_im / out_im
+// non-NULL: that side planar.  in and out must not alias.
+hipError_t launch_transpose(int prec, const void* in, const void* in_im, void* out, void* out_im, int64_t rows,
+                            int64_t cols, int64_t nmat, hipStream_t stream);
+
 // Lines per workgroup of the tile passes (tiles.hip) for lines of 2^logl points.
 int tile_lines_2d(int prec, int logl);
 
@@ -199,13 +204,19 @@ hipError_t launch_r2c_fold(int prec, int logh, int logf, const void* in, void* o
 // [batch][H + 1]; C2R x [batch][H + 1] -> z [batch][H].  wn: tables for w_N.
 hipError_t launch_real_pairs(int prec, bool c2r, const void* in, void* out, int64_t h, int64_t batch,
                              BigTwiddle wn, hipStream_t stream);
+// Real rows of odd length n around the n-point complex transform (real.hip),
+// mode: 0 widen (real rows -> complex z), 1 take (z -> bins 0 .. (n-1)/2),
+// 2 extend (bins 0 .. (n-1)/2 -> the full Hermitian z), 3 real parts
+// (z -> real rows); rows rows each.  in and out must not alias.
+hipError_t launch_real_odd(int prec, int mode, const void* in, void* out, int64_t n, int64_t rows,
+                           hipStream_t stream);
 // N = 1: out = in, real <-> complex.
 hipError_t launch_real_n1(int prec, bool c2r, const void* in, void* out, int64_t batch, hipStream_t stream);
 
 // d_resid[0] = 0 (a kernel, not a memset, so the call is safe to capture).
 hipError_t launch_zero_resid(double* d_resid, hipStream_t stream);
 
-// Streaming copy of nvec 16-byte vectors (copy.hip): src and dst 16-byte
+// Streaming copy of nvec 8-byte elements (copy.hip): src and dst 8-byte
 // aligned, not overlapping.  A measurement aid, not part of any transform.
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t nvec, hipStream_t stream);
 

@@ -75,7 +75,10 @@ constexpr int plan_lem(int prec) { return prec == 0 ? 4 : 3; }
 // f0 plus a delta that is a multiple of a power of two g with f0 mod 16 < g,
 // or of 16) the slot of f0 + d is slot(f0) + lds_off(d), a compile-time
 // constant, so the per-element LDS addresses cost no instructions.
-constexpr int lds_padded(int n) { return n + (n >> 4); }
-constexpr int lds_off(int d) { return d + (d >> 4); }
+//
+// The row kernels may take one pad slot per 32 instead (ps = 5): the same
+// argument holds with 32 in place of 16 for the accesses they make.
+constexpr int lds_padded(int n, int ps = 4) { return n + (n >> ps); }
+constexpr int lds_off(int d, int ps = 4) { return d + (d >> ps); }
 
 }  // namespace fftmi

@@ -11,6 +11,28 @@
 
 namespace fftmi {
 
+// LDS layout of a row: one pad slot per 16 elements, per 32 for 8192-point
+// complex64 rows.  Measured on MI355X (SQ_LDS_BANK_CONFLICT per wave, same-box
+// A/B): one per 16 leaves 0 conflict cycles for rows of 256 - 2048 points, 64
+// at 4096 (no padding tried -- one per 8, 32, 64, or two levels 16 + 128 /
+// 256 / 512, 32 + 128 / 256 / 512 -- went below 64, and none changed the
+// time) and 192 at 8192, where one per 32 gives 0 and ran 2-3 % faster
+// (209 against 214.7 us for 8192 rows); one per 32 costs 64 at 256 - 2048.
+template <typename V, int LOGN> constexpr int row_pad_shift()
+{
+    return sizeof(V) == 8 && LOGN == 13 ? 5 : 4;
+}
+// A row's threads share a wavefront (rows of up to 1024 complex64 / 512
+// complex128 points): the exchanges need no workgroup barrier (64 rows of
+// 1024 points: 4.45 -> 4.22 us per call, same-box A/B).
+template <typename V, int LOGN> constexpr bool row_in_wave() { return Geom<V, LOGN>::T <= 64; }
+template <typename V, int LOGN> constexpr int row_lds_slots()
+{
+    return Geom<V, LOGN>::S > 1 ? lds_padded(Geom<V, LOGN>::N, row_pad_shift<V, LOGN>()) : 0;
+}
+template <typename V, int LOGN>
+using RowLds = LdsLines<V, 1, row_pad_shift<V, LOGN>(), row_in_wave<V, LOGN>()>;
+
 // One workgroup per group of RPW rows; the hardware dispatcher starts a new
 // workgroup as soon as one retires, so the load, compute and store phases of
 // the workgroups resident on a CU overlap.  (Measured on MI355X for 16384 rows
@@ -23,7 +45,8 @@ void rows_kernel(CIn<V, PIN> in, COut<V, POUT> out, int64_t nrows, const V* __re
 {
     using G = Geom<V, LOGN>;
     constexpr int RPW = rows_per_wg<V, LOGN>();
-    __shared__ V lds[G::LDS > 0 ? G::LDS * RPW : 1];
+    constexpr int SLOTS = row_lds_slots<V, LOGN>();
+    __shared__ V lds[SLOTS > 0 ? SLOTS * RPW : 1];
 
     const int tid = threadIdx.x;
     const int rloc = tid / G::T;
@@ -41,7 +64,7 @@ void rows_kernel(CIn<V, PIN> in, COut<V, POUT> out, int64_t nrows, const V* __re
         const V x = live ? in.ld(base + i * G::T) : V{0, 0};
         v[i] = CONJ_IN ? cconj(x) : x;
     }
-    fft_regs<LOGN>(v, t, tb, LdsLines<V, 1>{lds + rloc * G::LDS, 0});
+    fft_regs<LOGN>(v, t, tb, RowLds<V, LOGN>{lds + rloc * SLOTS, 0});
     if (live) {
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {

@@ -263,16 +263,34 @@ template <typename V, int LOGN, int STAGE> struct TwBases<V, LOGN, STAGE, true> 
 };
 
 // LDS layout of C interleaved transforms (line c of C): element `pos` of line
-// c sits at f = pos C + c, slot f + floor(f / 16).  C = 1 is one transform.
-template <typename V, int C> struct LdsLines {
+// c sits at f = pos C + c, slot f + floor(f / 2^PS) (one pad slot per 16 by
+// default).  C = 1 is one transform.
+//
+// sync() orders the exchange: every thread's LDS writes of one stage before
+// any read of the next, and every read before the next stage's writes.  With
+// WAVE the threads sharing this region all sit in one wavefront (a row of at
+// most 64 threads, rows never straddling waves), whose LDS instructions
+// execute in issue order: a wavefront-scope fence keeps the compiler from
+// moving LDS accesses across it and no workgroup barrier is needed.
+template <typename V, int C, int PS = 4, bool WAVE = false> struct LdsLines {
     V* base;
     int c;
     __device__ __forceinline__ V* ptr(int pos) const
     {
         const int f = pos * C + c;
-        return base + f + (f >> 4);
+        return base + f + (f >> PS);
     }
-    static constexpr int off(int dpos) { return lds_off(dpos * C); }
+    static constexpr int off(int dpos) { return lds_off(dpos * C, PS); }
+    __device__ __forceinline__ static void sync()
+    {
+        if constexpr (WAVE) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else {
+            __syncthreads();
+        }
+    }
 };
 
 // u[r] *= w^r for r = 1 .. R-1, w^r built from the bases w^{2^l} (wb[l]).
@@ -328,11 +346,11 @@ __device__ __forceinline__ void fft_stages_from(V (&v)[E], int t, const TB& tb, 
     using G = Geom<V, LOGN>;
     if constexpr (STAGE < G::S) {
         if constexpr (STAGE > 0) {
-            __syncthreads();  // the previous stage's LDS writes are visible
+            L::sync();  // the previous stage's LDS writes are visible
             const V* rp = lds.ptr(t);
 #pragma unroll
             for (int i = 0; i < G::E; ++i) v[i] = rp[L::off(i * G::T)];
-            if constexpr (STAGE < G::S - 1) __syncthreads();  // all reads done before rewriting
+            if constexpr (STAGE < G::S - 1) L::sync();  // all reads done before rewriting
         }
         fft_stage<LOGN, STAGE>(v, t, tb, lds);
         fft_stages_from<LOGN, STAGE + 1>(v, t, tb, lds);

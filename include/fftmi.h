@@ -58,8 +58,7 @@ enum fft_direction { FFT_FORWARD = 0, FFT_INVERSE = 1 };
 enum fft_status {
     FFT_OK = 0,
     FFT_ERR_INVALID_ARG = -1,      /* NULL pointer, batch < 0, bad rank/dir/prec value */
-    FFT_ERR_NOT_POW2 = -2,         /* the length of a poly-mul plan or of real images is not
-                                      a power of two, or real rows are of odd length */
+    FFT_ERR_NOT_POW2 = -2,         /* the length of a poly-mul plan is not a power of two */
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
@@ -119,13 +118,18 @@ enum fft_status {
  *           unless H = W = 1.
  *   rank 2 / 3 with a dimension that is not a power of two: the innermost
  *           axis W may have any length a rank-1 plan takes (it runs as the
- *           rank-1 plan over every row); every other axis longer than 1 must
- *           be 2^a 3^b 5^c 7^d 11^e 13^f and runs as one super-stage pass up
+ *           rank-1 plan over every row); every other axis longer than 1 of
+ *           2^a 3^b 5^c 7^d 11^e 13^f points runs as one super-stage pass up
  *           to 1024 points (512 with a factor 11 or 13), two or three beyond;
- *           at most FFT_MAX_N_* points
- *           per transform (fft_plan_describe: path=ndmixed).  Workspace:
- *           fft_workspace_size, out of place too (a signal-sized buffer for
- *           an axis of two or more passes, plus what the rows need).
+ *           an axis of any other length up to FFT_MAX_BLUESTEIN_N is
+ *           transposed to be innermost, transformed as rows by the rank-1
+ *           plan of its length (chirp-z), and transposed back
+ *           (fft_plan_describe: axisK=transposed[...]); at most FFT_MAX_N_*
+ *           points per transform (fft_plan_describe: path=ndmixed).
+ *           Workspace: fft_workspace_size, out of place too (a signal-sized
+ *           buffer for an axis of two or more passes, plus what the rows
+ *           need, plus a signal-sized buffer and the axis plan's workspace
+ *           for a transposed axis).
  *   prec:   FFT_C32 or FFT_C64.
  * Builds the twiddle tables in fp64 on the host, rounds them to the plan
  * precision and uploads them (the only synchronous device work of the
@@ -269,19 +273,21 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
                  double* d_max_residual, void* stream);
 
 /*
- * Plan for transforms of real rows of N points: N = 1 or even, up to
- * 2 * FFT_MAX_N_C32 (C32) / 2 * FFT_MAX_N_C64 (C64) for powers of two and
- * 2 * FFT_MAX_BLUESTEIN_N otherwise (the N/2-point complex plan then takes
- * whichever route its length has; odd N > 1 gives FFT_ERR_NOT_POW2).  The
- * operands of polynomial multiplication are real ("FFT on GPU",
+ * Plan for transforms of real rows of N points: any N >= 1, up to
+ * 2 * FFT_MAX_N_C32 (C32) / 2 * FFT_MAX_N_C64 (C64) for powers of two,
+ * 2 * FFT_MAX_BLUESTEIN_N for other even N and FFT_MAX_BLUESTEIN_N for odd N.
+ * The operands of polynomial multiplication are real ("FFT on GPU",
  * polynomial-multiplication section); a real row's transform is fixed by
- * its bins X_0 .. X_{N/2}, since X_{N-k} = conj X_k.  The row is read as N/2
- * complex values and goes through the N/2-point complex transform, then one
- * split step (and the reverse for C2R).  prec: FFT_C32 (float rows, complex64
- * bins) or FFT_C64 (double rows, complex128 bins).  The plan serves only
- * fft_exec_r2c / fft_exec_c2r (other calls give FFT_ERR_RANK);
+ * its bins X_0 .. X_{floor(N/2)}, since X_{N-k} = conj X_k.  Even N: the row
+ * is read as N/2 complex values and goes through the N/2-point complex
+ * transform (whichever route that length has), then one split step (and the
+ * reverse for C2R).  Odd N: the row goes through the N-point complex
+ * transform of the row itself (mixed radix or chirp-z), widened to complex
+ * in the workspace (fft_plan_describe: "odd").  prec: FFT_C32 (float rows,
+ * complex64 bins) or FFT_C64 (double rows, complex128 bins).  The plan
+ * serves only fft_exec_r2c / fft_exec_c2r (other calls give FFT_ERR_RANK);
  * fft_workspace_size and fft_plan_describe accept it.
- * Errors: INVALID_ARG, NOT_POW2 (odd N), UNSUPPORTED_SIZE, DEVICE.
+ * Errors: INVALID_ARG, UNSUPPORTED_SIZE, DEVICE.
  */
 int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
 
@@ -293,25 +299,28 @@ int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
  * the half spectrum (one column per lane; for H > 512 a radix-F column stage
  * first, as for complex plans).  The same fft_exec_r2c / fft_exec_c2r calls
  * take it; fft_plan_describe shows path=real2d.
- * Other shapes: W even (or 1), H = 2^a 3^b 5^c 7^d 11^e 13^f, at most
+ * Other shapes: any W, H = 2^a 3^b 5^c 7^d 11^e 13^f, at most
  * FFT_MAX_N_* points in the half spectrum: the rows by the real-row plan of
  * length W (fft_plan_create_real), then the column axis as mixed-radix
  * super-stage passes over the half spectrum (path=real2dmixed); a workspace of
  * fft_workspace_size bytes on every call (C2R runs the columns into it and
  * leaves its input as it was).
- * Errors: INVALID_ARG, NOT_POW2 (odd W), UNSUPPORTED_SIZE, DEVICE.
+ * Errors: INVALID_ARG, UNSUPPORTED_SIZE, DEVICE.
  */
 int fft_plan_create_real_2d(fft_plan** plan, int64_t h, int64_t w, int prec);
 
 /*
  * Forward transform of real rows: out[b][k] = sum_n in[b][n] e^{-2 pi i k n / N},
- * k = 0 .. N/2.
+ * k = 0 .. floor(N/2).
  *   in:        [batch][N] real (float for C32, double for C64), rows contiguous.
- *   out:       [batch][N/2 + 1] complex, rows contiguous.  in and out must not
- *              overlap (FFT_ERR_OVERLAP); both aligned to the complex element
- *              size (8 bytes C32, 16 bytes C64).
- *   workspace: fft_workspace_size(plan, batch) bytes: none for N/2 <=
- *              FFT_MAX_LDS_N_* (one kernel), batch * N/2 complex values beyond.
+ *   out:       [batch][floor(N/2) + 1] complex, rows contiguous.  in and out
+ *              must not overlap (FFT_ERR_OVERLAP); both aligned to the complex
+ *              element size (8 bytes C32, 16 bytes C64).
+ *   workspace: fft_workspace_size(plan, batch) bytes: none for powers of two
+ *              with N/2 <= FFT_MAX_LDS_N_* (one kernel); batch * N/2 complex
+ *              values beyond (even N; plus the N/2-point plan's own workspace
+ *              where N/2 is not a power of two); batch * N complex values
+ *              plus the N-point plan's workspace for odd N.
  *   Images (fft_plan_create_real_2d): in [batch][H][W] real, out
  *              [batch][H][W/2 + 1] complex; the workspace (batch H (W/2 + 1)
  *              complex values, the size fft_workspace_size reports, which
@@ -323,11 +332,12 @@ int fft_plan_create_real_2d(fft_plan** plan, int64_t h, int64_t w, int prec);
 int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch, void* workspace, void* stream);
 
 /*
- * Inverse: the real rows whose bins 0 .. N/2 are `in`, scaled by 1/N, so that
- * c2r(r2c(x)) = x.  The imaginary parts of in[b][0] and in[b][N/2] are
- * ignored (a real row has real values there); bins N/2 + 1 .. N - 1 are
- * taken as conj in[b][N - k].
- *   in:  [batch][N/2 + 1] complex;  out: [batch][N] real.  Not modified: in.
+ * Inverse: the real rows whose bins 0 .. floor(N/2) are `in`, scaled by 1/N,
+ * so that c2r(r2c(x)) = x.  The imaginary parts of in[b][0] and, for even N,
+ * in[b][N/2] are ignored (a real row has real values there); bins above
+ * N/2 are taken as conj in[b][N - k].
+ *   in:  [batch][floor(N/2) + 1] complex;  out: [batch][N] real.  Not
+ *   modified: in.
  *   Images: in [batch][H][W/2 + 1], out [batch][H][W], scaled 1/(H W): the
  *   inverse column transforms, then the rows as above (the imaginary parts of
  *   columns 0 and W/2 of that intermediate are ignored).  The workspace is
@@ -344,7 +354,7 @@ int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch,
  * Butterfly Algorithm in Parallel GLSL", section "Performance and Pipeline
  * Evaluation": the transform is bound by memory throughput, so a plain copy
  * of the same bytes is its practical ceiling).  Enqueued on `stream`.
- *   src, dst: 16-byte aligned, not overlapping; bytes a multiple of 16
+ *   src, dst: 8-byte aligned, not overlapping; bytes a multiple of 8
  *             (0 is a no-op).
  * Errors: INVALID_ARG (NULL), ALIGN, OVERLAP, DEVICE.
  */

@@ -73,10 +73,10 @@ def _create_status(rank, dims, prec):
     (1, [-4], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [(1 << 23) + 1], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # beyond the Bluestein range
     (1, [3 << 22], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    # not powers of two: axes other than the innermost must be 13-smooth, and
+    # not powers of two: every axis at most 2^23 points unless 13-smooth, and
     # the transform at most 2^26 / 2^24 points
-    (2, [97, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (2, [17 * 3, 12], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [(1 << 23) + 1, 2], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (3, [2, (1 << 23) + 1, 1], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [10000, 10000], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [1200, 16000], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [2, (1 << 23) + 1], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -84,7 +84,6 @@ def _create_status(rank, dims, prec):
     (1, [1 << 25], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (3, [8, 19, 6], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (3, [0, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
     (3, [4096, 8, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # depth beyond the column-pass range
     (3, [2048, 8, 8], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -108,7 +107,8 @@ def test_valid_plan_without_gpu_is_a_device_error():
                              (3, [16, 8, 32], 0), (3, [4096, 1, 1], 0), (2, [8192, 8], 0),
                              (1, [1000], 0), (1, [12], 1), (1, [1 << 23], 0),
                              (2, [8192, 8192], 0), (2, [4096, 4096], 1), (2, [8192, 2], 0),
-                             (3, [2048, 8192, 8192], 0)):
+                             (3, [2048, 8192, 8192], 0), (2, [97, 8], 0), (2, [51, 12], 1),
+                             (3, [8, 19, 6], 0)):
         st, h = _create_status(rank, dims, prec)
         assert st == fm.FFT_ERR_DEVICE and h is None
         assert "hipGetDevice" in fm.fft_last_error()
@@ -118,8 +118,7 @@ def test_valid_plan_without_gpu_is_a_device_error():
     (0, 0, fm.FFT_ERR_INVALID_ARG),
     (-8, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 2, fm.FFT_ERR_INVALID_ARG),
-    (7, 0, fm.FFT_ERR_NOT_POW2),            # odd: real rows take an even length
-    (1001, 1, fm.FFT_ERR_NOT_POW2),
+    ((1 << 23) + 1, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # odd: the N-point complex plan's limit
     (2 * ((1 << 23) + 1), 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1 << 28, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1 << 26, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -133,7 +132,7 @@ def test_real_plan_create_rejects(n, prec, status):
 
 @pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
 def test_valid_real_plan_without_gpu_is_a_device_error():
-    for n, prec in ((1, 0), (2, 1), (16384, 0), (1 << 27, 0), (1 << 25, 1)):
+    for n, prec in ((1, 0), (2, 1), (16384, 0), (1 << 27, 0), (1 << 25, 1), (7, 0), (1001, 1), ((1 << 23) - 1, 0)):
         h = ctypes.c_void_p(12345)
         assert fm.lib().fft_plan_create_real(ctypes.byref(h), n, prec) == fm.FFT_ERR_DEVICE
         assert h.value is None
@@ -158,9 +157,9 @@ def test_exec_and_queries_with_null_plan():
 
 def test_binding_raises_fft_error():
     with pytest.raises(fm.FFTError) as ei:
-        fm.fft_plan_create(2, [97, 8], fm.FFT_C32)
+        fm.fft_plan_create(2, [(1 << 23) + 1, 2], fm.FFT_C32)
     assert ei.value.status == fm.FFT_ERR_UNSUPPORTED_SIZE
-    assert "innermost" in str(ei.value)
+    assert "exceeds" in str(ei.value)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -179,8 +178,6 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     (0, 8, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 0, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 8, 3, fm.FFT_ERR_INVALID_ARG),
-    (8, 7, 0, fm.FFT_ERR_NOT_POW2),          # odd width: real rows take an even length
-    (6, 15, 1, fm.FFT_ERR_NOT_POW2),
     (97, 8, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),    # height with a prime factor above 13
     (51, 16, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (65536, 2048, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # half spectrum beyond 2^26 points
@@ -194,7 +191,7 @@ def test_real_2d_plan_create_rejects(h, w, prec, status):
 
 @pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
 def test_valid_real_2d_plan_without_gpu_is_a_device_error():
-    for h, w, prec in ((1, 1, 0), (8192, 16384, 0), (4096, 8192, 1), (64, 2, 0)):
+    for h, w, prec in ((1, 1, 0), (8192, 16384, 0), (4096, 8192, 1), (64, 2, 0), (8, 7, 0), (6, 15, 1)):
         hd = ctypes.c_void_p(12345)
         assert fm.lib().fft_plan_create_real_2d(ctypes.byref(hd), h, w, prec) == fm.FFT_ERR_DEVICE
         assert hd.value is None
@@ -205,6 +202,6 @@ def test_stream_copy_rejects_before_any_hip_call():
     assert L.fft_stream_copy(None, None, 0, None) == fm.FFT_OK  # nothing to copy
     assert L.fft_stream_copy(None, 4096, 64, None) == fm.FFT_ERR_INVALID_ARG
     assert L.fft_stream_copy(4096, None, 64, None) == fm.FFT_ERR_INVALID_ARG
-    assert L.fft_stream_copy(4096 + 8, 1 << 20, 64, None) == fm.FFT_ERR_ALIGN
-    assert L.fft_stream_copy(4096, 1 << 20, 63, None) == fm.FFT_ERR_ALIGN
+    assert L.fft_stream_copy(4096 + 4, 1 << 20, 64, None) == fm.FFT_ERR_ALIGN
+    assert L.fft_stream_copy(4096, 1 << 20, 60, None) == fm.FFT_ERR_ALIGN
     assert L.fft_stream_copy(4096, 4096 + 32, 64, None) == fm.FFT_ERR_OVERLAP
