@@ -325,6 +325,11 @@ struct fft_plan {
     // real rows of N = 2H points: inner = the complex plan of length H,
     // big_* = w_N, log_a = log2 H; real_fused: H within the rows kernel's range.
     bool real_fused = false;
+    // real rows of odd N: inner = the complex plan of length N (any route);
+    // rows are widened to complex in the workspace, transformed in place there
+    // and the bins 0 .. (N - 1) / 2 copied out (C2R: the Hermitian extension,
+    // the inverse, the real parts).
+    bool real_odd = false;
     // real images [H][W] (rank 2): the W-point rows as above, then the H-point
     // columns over W/2 + 1 columns: tw_b = stage table for 2^log_b, logf > 0:
     // a radix-2^logf column stage first, col_* = tables for w_H.
@@ -345,6 +350,10 @@ struct fft_plan {
     int nx_k = 0;
     int64_t nx_len[2] = {1, 1}, nx_stride[2] = {1, 1};
     int nx_np[2] = {0, 0};
+    // an axis whose length has a prime factor above 13 (nx_np = 0): brought
+    // innermost by a transpose, transformed as rows by the rank-1 plan of its
+    // length (chirp-z or any other route), and transposed back
+    fft_plan* nx_plan[2] = {nullptr, nullptr};
     // real images outside the power-of-two route: inner = the real-row plan
     // of length W, then the column axis as above over the W/2 + 1 columns of
     // the half spectrum (nx_stride[0] = W/2 + 1)
@@ -399,6 +408,8 @@ void free_plan(fft_plan* p)
         if (p->passes[i].big_lo) hipFree(p->passes[i].big_lo);
     }
     if (p->inner) free_plan(p->inner);
+    for (fft_plan* q : p->nx_plan)
+        if (q) free_plan(q);
     delete p;
 }
 
@@ -496,12 +507,27 @@ size_t ndx_axis_buffers(const fft_plan* p, bool planar)
     for (int a = 0; a < p->nx_k; ++a) most = std::max(most, p->nx_np[a]);
     return most >= 3 && planar ? 2 : most >= 2 ? 1 : 0;
 }
+// Workspace of the axes transformed as rank-1 rows: the transposed signal,
+// then the largest such axis plan's own workspace.
+size_t ndx_transposed_ws(const fft_plan* p, int64_t batch)
+{
+    size_t most = 0;
+    bool any = false;
+    for (int a = 0; a < p->nx_k; ++a)
+        if (p->nx_np[a] == 0 && p->nx_plan[a]) {
+            any = true;
+            most = std::max(most, c2c_workspace(p->nx_plan[a], batch * (p->n / p->nx_len[a])));
+        }
+    return any ? (size_t)batch * (size_t)p->n * p->elem + most : 0;
+}
+
+// [axis pass buffers][rows' workspace][transposed axes' workspace]
 size_t ndx_workspace(const fft_plan* p, int64_t batch, bool planar)
 {
     const size_t sig = (size_t)batch * (size_t)p->n * p->elem;
     const int64_t rows = batch * (p->n / p->dims[p->rank - 1]);
     const size_t rws = p->dims[p->rank - 1] == 1 ? 0 : planar ? planar_ws(p->inner, rows) : c2c_workspace(p->inner, rows);
-    return ndx_axis_buffers(p, planar) * sig + rws;
+    return ndx_axis_buffers(p, planar) * sig + rws + ndx_transposed_ws(p, batch);
 }
 
 size_t c2c_workspace(const fft_plan* p, int64_t batch)
@@ -521,6 +547,8 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
         return p->dims[0] > 1 ? (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem : 0;
     if (p->path == PATH_REAL) {  // the H-point spectrum of every row, beyond the one-kernel range
         if (p->real_fused || p->n == 1) return 0;
+        if (p->real_odd)  // the rows as complex signals, then the N-point plan's own workspace
+            return (size_t)batch * (size_t)p->n * p->elem + c2c_workspace(p->inner, batch);
         const size_t z = (size_t)batch * (size_t)(p->n / 2) * p->elem;
         // lengths that are not powers of two: the H-point plan's own workspace after it
         return is_pow2(p->n) ? z : z + c2c_workspace(p->inner, batch);
@@ -562,9 +590,9 @@ int ndx_layout(fft_plan* p, int rank, const int64_t* dims)
             p->nx_len[a] = len;
             p->nx_stride[a] = stride;
             int rs[3] = {(int)len, 0, 0};
-            const int np = axis_split(len, rs);
-            if (np == 0) return fail(FFT_ERR_UNSUPPORTED_SIZE, "no passes for an axis of %lld points", (long long)len);
-            p->nx_np[a] = np;
+            MixedSchedule chk;
+            const int np = mixed_factor(len, &chk) ? axis_split(len, rs) : 0;
+            p->nx_np[a] = np;  // 0: transposed, the rank-1 plan of its length
             int64_t ns = 1;
             for (int q = 0; q < np; ++q) {
                 PassPlan& pp = p->passes[3 * a + q];
@@ -789,6 +817,8 @@ int upload_tables(fft_plan* p)
             const int64_t w = p->dims[p->rank - 1];
             if (w > 1) st = fft_plan_create(&p->inner, 1, &w, prec);
             for (int a = 0; a < p->nx_k && st == FFT_OK; ++a)
+                if (p->nx_np[a] == 0) st = fft_plan_create(&p->nx_plan[a], 1, &p->nx_len[a], prec);
+            for (int a = 0; a < p->nx_k && st == FFT_OK; ++a)
                 for (int q = 0; q < p->nx_np[a] && st == FFT_OK; ++q) {
                     PassPlan& pp = p->passes[3 * a + q];
                     st = upload(mixed_table(pp.ms), prec, &p->pass_tw[3 * a + q]);
@@ -881,10 +911,11 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
             if (dims[d] == 1) continue;
             MixedSchedule ms;
             int rs[3];
-            if (!mixed_factor(dims[d], &ms) || axis_split(dims[d], rs) == 0)
-                return fail(FFT_ERR_UNSUPPORTED_SIZE,
-                            "dims[%d] = %lld: axes other than the innermost take 2^a 3^b 5^c 7^d 11^e 13^f points",
-                            d, (long long)dims[d]);
+            // 13-smooth: super-stage passes; otherwise the rank-1 plan of the
+            // length over the transposed axis
+            if (!(mixed_factor(dims[d], &ms) && axis_split(dims[d], rs) > 0) && dims[d] > kBluesteinMax)
+                return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", d, (long long)dims[d],
+                            (long long)kBluesteinMax);
         }
     }
     for (int d = 0; d < rank; ++d) {
@@ -980,7 +1011,8 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             if (p->real_nd) {
                 int off = snprintf(buf, len, "real dims=%lldx%lld prec=%s path=real2dmixed rows=real %s",
                                    (long long)p->dims[0], (long long)p->dims[1], prec,
-                                   !p->inner || p->inner->n == 1 ? "copy" : p->inner->real_fused ? "fused" : "pairs");
+                                   !p->inner || p->inner->n == 1 ? "copy"
+                                   : p->inner->real_odd ? "odd" : p->inner->real_fused ? "fused" : "pairs");
                 if (p->nx_k && off > 0 && (size_t)off < len) {
                     off += snprintf(buf + off, len - off, " axis1=");
                     for (int q = 0; q < p->nx_np[0] && off > 0 && (size_t)off < len; ++q)
@@ -993,7 +1025,7 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                          p->logf > 0 && r2c_fold_supported(p->prec, p->log_a, p->logf) ? 1 : 0);
             else
                 snprintf(buf, len, "real n=%lld prec=%s path=real %s", (long long)p->n, prec,
-                         p->n == 1 ? "copy" : p->real_fused ? "fused" : "pairs");
+                         p->n == 1 ? "copy" : p->real_odd ? "odd" : p->real_fused ? "fused" : "pairs");
             break;
         case PATH_NDX: {
             // the rows' route, then each axis's radices
@@ -1010,6 +1042,16 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                                (long long)(p->rank > 2 ? p->dims[2] : 1), prec, rb);
             for (int a = 0; a < p->nx_k && off > 0 && (size_t)off < len; ++a) {
                 off += snprintf(buf + off, len - off, " axis%d=", a + 1);
+                if (p->nx_np[a] == 0) {  // transposed: the route of the rank-1 plan of its length
+                    fft_plan ax;
+                    char ab[160] = "?";
+                    if (plan_prepare(&ax, 1, &p->nx_len[a], p->prec) == FFT_OK) {
+                        fft_plan_describe(&ax, ab, sizeof ab);
+                        const char* at = strstr(ab, "path=");
+                        if (at) memmove(ab, at + 5, strlen(at + 5) + 1);
+                    }
+                    off += snprintf(buf + off, len - off, "transposed[%s]", ab);
+                }
                 for (int q = 0; q < p->nx_np[a] && off > 0 && (size_t)off < len; ++q)
                     off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->passes[3 * a + q].r);
             }
@@ -1267,11 +1309,27 @@ static int run_ndx(const fft_plan* plan, bool inv, const Io& io, int64_t batch, 
         const int st = run_1d(plan->inner, inv, io, batch * (plan->n / w), rows_ws, s);
         if (st != FFT_OK) return st;
     }
+    const int64_t rows = batch * (plan->n / w);
+    char* tbuf = (char*)rows_ws + (w == 1 ? 0 : planar ? planar_ws(plan->inner, rows) : c2c_workspace(plan->inner, rows));
+    void* tws = tbuf + sig;
     hipError_t e = hipSuccess;
     for (int a = 0; a < plan->nx_k && e == hipSuccess; ++a) {
         const bool from_in = a == 0 && w == 1;
-        e = axis_passes(plan, a, inv, from_in ? io.in : io.out, from_in ? io.in_im : io.out_im, io.out, io.out_im, y,
-                        y2, batch, s);
+        const void* src = from_in ? io.in : io.out;
+        const void* src_im = from_in ? io.in_im : io.out_im;
+        if (plan->nx_np[a] == 0) {
+            // [m][L][S] -> [m][S][L], the L-point rows, and back
+            const int64_t len = plan->nx_len[a], str = plan->nx_stride[a];
+            const int64_t nmat = batch * (plan->n / (len * str));
+            e = launch_transpose(plan->prec, src, src_im, tbuf, nullptr, len, str, nmat, s);
+            if (e != hipSuccess) break;
+            const Io tio{tbuf, nullptr, tbuf, nullptr};
+            const int st = run_1d(plan->nx_plan[a], inv, tio, nmat * str, tws, s);
+            if (st != FFT_OK) return st;
+            e = launch_transpose(plan->prec, tbuf, nullptr, io.out, io.out_im, str, len, nmat, s);
+            continue;
+        }
+        e = axis_passes(plan, a, inv, src, src_im, io.out, io.out_im, y, y2, batch, s);
     }
     if (e != hipSuccess) return hip_fail(e, "rank-2/3 transform launch");
     return FFT_OK;
@@ -1525,9 +1583,10 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
     if (n < 1) return fail(FFT_ERR_INVALID_ARG, "n = %lld < 1", (long long)n);
     // any even length: the complex plan of N/2 points (any route) and the
-    // bin-pair pass; powers of two within one workgroup also fuse the two
-    if (n > 1 && n % 2) return fail(FFT_ERR_NOT_POW2, "n = %lld is odd (real rows take an even length)", (long long)n);
-    const int64_t lim = is_pow2(n) ? 2 * max_n(prec) : 2 * kBluesteinMax;
+    // bin-pair pass; powers of two within one workgroup also fuse the two.
+    // Odd lengths: the complex plan of N points itself.
+    const bool odd = n > 1 && n % 2;
+    const int64_t lim = is_pow2(n) ? 2 * max_n(prec) : odd ? kBluesteinMax : 2 * kBluesteinMax;
     if (n > lim) return fail(FFT_ERR_UNSUPPORTED_SIZE, "n = %lld exceeds %lld", (long long)n, (long long)lim);
     fft_plan* p = new (std::nothrow) fft_plan;
     if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
@@ -1539,13 +1598,16 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     p->logn = is_pow2(n) ? ilog2(n) : 31;  // 31: w_N lookups of any N take no index mask (k < N)
     p->log_a = is_pow2(n) && p->logn > 0 ? p->logn - 1 : 0;
     p->real_fused = is_pow2(n) && n >= 2 && (n / 2) <= max_lds_n(prec);
+    p->real_odd = odd;
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) {
         delete p;
         return hip_fail(e, "hipGetDevice");
     }
     int st = FFT_OK;
-    if (n >= 2) {
+    if (odd) {
+        st = fft_plan_create(&p->inner, 1, &n, prec);
+    } else if (n >= 2) {
         const int64_t h = n / 2;
         st = fft_plan_create(&p->inner, 1, &h, prec);
         // w_N^{t + i T} = hi[i] lo[t] for the fused kernels (T threads per row)
@@ -1568,8 +1630,6 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
 // 13^f) as mixed-radix passes over the W/2 + 1 columns of the half spectrum.
 static int real_2d_any(fft_plan** out_plan, int64_t h, int64_t w, int prec)
 {
-    if (w > 1 && w % 2)
-        return fail(FFT_ERR_NOT_POW2, "image width %lld is odd (real rows take an even length)", (long long)w);
     const int64_t wc = w / 2 + 1;
     if (h * wc > max_n(prec))
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "%lld x %lld half-spectrum points exceed %lld", (long long)h,
@@ -1817,6 +1877,15 @@ int fft_exec_r2c(const fft_plan* plan, const void* in, void* out, int64_t batch,
     hipError_t e;
     if (plan->n == 1) {
         e = launch_real_n1(plan->prec, false, in, out, batch, s);
+    } else if (plan->real_odd) {
+        // widen into the workspace, the N-point transform in place there, bins out
+        void* z = workspace;
+        void* inner_ws = (char*)workspace + (size_t)batch * (size_t)plan->n * plan->elem;
+        e = launch_real_odd(plan->prec, 0, in, z, plan->n, batch, s);
+        if (e != hipSuccess) return hip_fail(e, "fft_exec_r2c");
+        st = fft_exec_c2c(plan->inner, FFT_FORWARD, z, z, batch, inner_ws, stream);
+        if (st != FFT_OK) return st;
+        e = launch_real_odd(plan->prec, 1, z, out, plan->n, batch, s);
     } else if (plan->real_fused) {
         e = launch_real_rows(plan->prec, plan->log_a, false, in, out, batch, plan->inner->tw_a, plan->big_hi,
                              plan->big_lo, s);
@@ -1846,6 +1915,15 @@ int fft_exec_c2r(const fft_plan* plan, const void* in, void* out, int64_t batch,
     hipError_t e;
     if (plan->n == 1) {
         e = launch_real_n1(plan->prec, true, in, out, batch, s);
+    } else if (plan->real_odd) {
+        // the Hermitian extension into the workspace, the inverse in place, real parts out
+        void* z = workspace;
+        void* inner_ws = (char*)workspace + (size_t)batch * (size_t)plan->n * plan->elem;
+        e = launch_real_odd(plan->prec, 2, in, z, plan->n, batch, s);
+        if (e != hipSuccess) return hip_fail(e, "fft_exec_c2r");
+        st = fft_exec_c2c(plan->inner, FFT_INVERSE, z, z, batch, inner_ws, stream);
+        if (st != FFT_OK) return st;
+        e = launch_real_odd(plan->prec, 3, z, out, plan->n, batch, s);
     } else if (plan->real_fused) {
         e = launch_real_rows(plan->prec, plan->log_a, true, in, out, batch, plan->inner->tw_a, plan->big_hi,
                              plan->big_lo, s);
@@ -1920,10 +1998,10 @@ int fft_stream_copy(const void* src, void* dst, size_t bytes, void* stream)
 {
     if (bytes == 0) return FFT_OK;
     if (!src || !dst) return fail(FFT_ERR_INVALID_ARG, "src or dst is NULL");
-    if (((uintptr_t)src | (uintptr_t)dst | bytes) & 15)
-        return fail(FFT_ERR_ALIGN, "src, dst and bytes must be multiples of 16");
+    if (((uintptr_t)src | (uintptr_t)dst | bytes) & 7)
+        return fail(FFT_ERR_ALIGN, "src, dst and bytes must be multiples of 8");
     if (ranges_overlap(src, bytes, dst, bytes)) return fail(FFT_ERR_OVERLAP, "src and dst overlap");
-    const hipError_t e = launch_stream_copy(src, dst, (int64_t)(bytes / 16), (hipStream_t)stream);
+    const hipError_t e = launch_stream_copy(src, dst, (int64_t)(bytes / 8), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "fft_stream_copy");
     return FFT_OK;
 }

@@ -18,7 +18,9 @@
 // H-point transform in registers and LDS and does the split (or, backwards,
 // the merge) through one more LDS exchange, so a row crosses HBM once each
 // way.  Longer rows: the H-point multi-pass transform plus one pass that
-// handles the bins k and H - k together.
+// handles the bins k and H - k together.  Rows of odd length have no half
+// length: they go through the N-point complex transform of the row itself
+// (real_odd_kernel, at the end).
 #include "launch.hpp"
 #include "stockham.hpp"
 #include "tile_common.hpp"
@@ -433,6 +435,71 @@ hipError_t launch_real_n1(int prec, bool c2r, const void* in, void* out, int64_t
     else
         hipLaunchKernelGGL(real_n1_kernel<double2>, dim3((unsigned)blocks), dim3(256), 0, s, in, out, batch, (int)c2r);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Real rows of odd length N, around the N-point complex transform of the row
+// itself (its route: mixed radix or chirp-z): the bin pairs of the even
+// case need N/2 points, which an odd N has not.  Row r of a [rows][len]
+// array is handled by blocks (x, r) for r < gridDim.y, (x, r + gridDim.y), ...
+//   ODD_WIDEN   z[r][n] = (x[r][n], 0),                    n < N
+//   ODD_TAKE    X[r][k] = z[r][k],                          k <= (N - 1) / 2
+//   ODD_EXTEND  z[r][k] = X[r][k] (k <= (N - 1) / 2; X_0 with its imaginary
+//               part dropped), conj X[r][N - k] beyond
+//   ODD_REAL    x[r][n] = Re z[r][n]
+// ---------------------------------------------------------------------------
+enum { ODD_WIDEN = 0, ODD_TAKE = 1, ODD_EXTEND = 2, ODD_REAL = 3 };
+
+template <typename V, int MODE>
+__global__ __launch_bounds__(256) void real_odd_kernel(const void* __restrict__ in, void* __restrict__ out, int64_t n,
+                                                       int64_t rows)
+{
+    using Rl = typename real_of<V>::type;
+    const int64_t h1 = (n + 1) / 2;  // bins 0 .. (N - 1) / 2
+    const int64_t len = MODE == ODD_TAKE ? h1 : n;  // elements written per row
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= len) return;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        if constexpr (MODE == ODD_WIDEN) {
+            ((V*)out)[r * n + j] = V{((const Rl*)in)[r * n + j], (Rl)0};
+        } else if constexpr (MODE == ODD_TAKE) {
+            ((V*)out)[r * h1 + j] = ((const V*)in)[r * n + j];
+        } else if constexpr (MODE == ODD_EXTEND) {
+            const V* X = (const V*)in + r * h1;
+            V z;
+            if (j == 0) z = V{X[0].x, (Rl)0};
+            else if (j < h1) z = X[j];
+            else z = cconj(X[n - j]);
+            ((V*)out)[r * n + j] = z;
+        } else {
+            ((Rl*)out)[r * n + j] = ((const V*)in)[r * n + j].x;
+        }
+    }
+}
+
+template <typename V>
+static hipError_t launch_real_odd_t(int mode, const void* in, void* out, int64_t n, int64_t rows, hipStream_t s)
+{
+    const int64_t len = mode == ODD_TAKE ? (n + 1) / 2 : n;
+    const int64_t bx = (len + 255) / 256;
+    const int64_t by = rows < 65535 ? rows : 65535;
+    if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (bx == 0 || by == 0) return hipSuccess;
+    const dim3 grid((unsigned)bx, (unsigned)by);
+    switch (mode) {
+        case ODD_WIDEN: hipLaunchKernelGGL((real_odd_kernel<V, ODD_WIDEN>), grid, dim3(256), 0, s, in, out, n, rows); break;
+        case ODD_TAKE: hipLaunchKernelGGL((real_odd_kernel<V, ODD_TAKE>), grid, dim3(256), 0, s, in, out, n, rows); break;
+        case ODD_EXTEND: hipLaunchKernelGGL((real_odd_kernel<V, ODD_EXTEND>), grid, dim3(256), 0, s, in, out, n, rows); break;
+        case ODD_REAL: hipLaunchKernelGGL((real_odd_kernel<V, ODD_REAL>), grid, dim3(256), 0, s, in, out, n, rows); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_real_odd(int prec, int mode, const void* in, void* out, int64_t n, int64_t rows, hipStream_t s)
+{
+    return prec == 0 ? launch_real_odd_t<float2>(mode, in, out, n, rows, s)
+                     : launch_real_odd_t<double2>(mode, in, out, n, rows, s);
 }
 
 }  // namespace fftmi

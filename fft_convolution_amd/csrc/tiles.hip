@@ -609,4 +609,68 @@ int tile_lines_2d(int prec, int logl)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Transpose of nmat matrices [rows][cols] -> [cols][rows] (complex elements),
+// through 32 x 32 tiles in LDS (one pad slot per tile row), for axes whose
+// transform runs as rank-1 rows: the axis is brought innermost, transformed,
+// and brought back.  Both sides read and write 32 consecutive elements per
+// tile row.  Planar input and / or output as for the other first and last
+// passes.
+// ---------------------------------------------------------------------------
+template <typename V, bool PIN, bool POUT>
+__global__ __launch_bounds__(256) void transpose_kernel(CIn<V, PIN> in, COut<V, POUT> out, int64_t rows,
+                                                        int64_t cols, int64_t nmat)
+{
+    __shared__ V tile[32][33];
+    const int64_t tx = (cols + 31) / 32, ty = (rows + 31) / 32;
+    const int64_t per = tx * ty;
+    const int lx = threadIdx.x & 31, ly = threadIdx.x >> 5;  // 32 x 8 threads
+    for (int64_t b = blockIdx.x; b < per * nmat; b += gridDim.x) {
+        const int64_t m = b / per, q = b % per;
+        const int64_t r0 = (q / tx) * 32, c0 = (q % tx) * 32;
+        const int64_t base = m * rows * cols;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t r = r0 + ly + 8 * k, c = c0 + lx;
+            if (r < rows && c < cols) tile[ly + 8 * k][lx] = in.ld_plain(base + r * cols + c);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t c = c0 + ly + 8 * k, r = r0 + lx;  // output row c, column r
+            if (r < rows && c < cols) out.st_plain(base + c * rows + r, tile[lx][ly + 8 * k]);
+        }
+        __syncthreads();  // the tile is read before the next one overwrites it
+    }
+}
+
+template <typename V, bool PIN, bool POUT>
+static hipError_t launch_transpose_t(const void* in, const void* in_im, void* out, void* out_im, int64_t rows,
+                                     int64_t cols, int64_t nmat, hipStream_t s)
+{
+    const int64_t tiles = ((cols + 31) / 32) * ((rows + 31) / 32) * nmat;
+    const int64_t blocks = tiles < (1 << 20) ? tiles : (1 << 20);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((transpose_kernel<V, PIN, POUT>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       make_in<V, PIN>(in, in_im), make_out<V, POUT>(out, out_im), rows, cols, nmat);
+    return hipGetLastError();
+}
+
+template <typename V>
+static hipError_t launch_transpose_v(const void* in, const void* in_im, void* out, void* out_im, int64_t rows,
+                                     int64_t cols, int64_t nmat, hipStream_t s)
+{
+    if (in_im && out_im) return launch_transpose_t<V, true, true>(in, in_im, out, out_im, rows, cols, nmat, s);
+    if (in_im) return launch_transpose_t<V, true, false>(in, in_im, out, out_im, rows, cols, nmat, s);
+    if (out_im) return launch_transpose_t<V, false, true>(in, in_im, out, out_im, rows, cols, nmat, s);
+    return launch_transpose_t<V, false, false>(in, in_im, out, out_im, rows, cols, nmat, s);
+}
+
+hipError_t launch_transpose(int prec, const void* in, const void* in_im, void* out, void* out_im, int64_t rows,
+                            int64_t cols, int64_t nmat, hipStream_t s)
+{
+    return prec == 0 ? launch_transpose_v<float2>(in, in_im, out, out_im, rows, cols, nmat, s)
+                     : launch_transpose_v<double2>(in, in_im, out, out_im, rows, cols, nmat, s);
+}
+
 }  // namespace fftmi

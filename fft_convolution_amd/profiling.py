@@ -24,8 +24,9 @@ Three subcommands, all reading the CSV output of ``rocprofv3 --output-format csv
                SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES GRBM_GUI_ACTIVE:
                per wave, VALU and LDS instructions and LDS bank-conflict cycles;
                the conflict rate (conflict cycles / LDS active cycles) and VALU
-               busy (100 * SQ_ACTIVE_INST_VALU * 4 / SIMDs / GRBM_GUI_ACTIVE, the
-               usual definition, 1024 SIMDs on MI355X):
+               busy (100 * SQ_ACTIVE_INST_VALU * 4 / SIMDs / (GRBM_GUI_ACTIVE / XCDs):
+               1024 SIMDs on MI355X, and GRBM_GUI_ACTIVE reads the sum over its 8
+               XCDs -- 3.06e6 cycles for a 176-us kernel, 8 x 382e3 at ~2.2 GHz):
                python -m fft_convolution_amd.profiling sq DIR --stats DIR2 --out profiles/sq_W.md --cmd "..."
 
 The traffic record carries a digest of the kernel sources; ``bench.py``
@@ -183,6 +184,7 @@ def cmd_counters(args):
 SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
                "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
 MI355X_SIMDS = 256 * 4
+MI355X_XCDS = 8
 
 
 def cmd_sq(args):
@@ -206,7 +208,7 @@ def cmd_sq(args):
         lds_act = med("SQ_ACTIVE_INST_LDS", k)
         conf = med("SQ_LDS_BANK_CONFLICT", k)
         gui = med("GRBM_GUI_ACTIVE", k)
-        busy = 100.0 * med("SQ_ACTIVE_INST_VALU", k) * 4 / MI355X_SIMDS / gui if gui else float("nan")
+        busy = 100.0 * med("SQ_ACTIVE_INST_VALU", k) * 4 / MI355X_SIMDS / (gui / MI355X_XCDS) if gui else float("nan")
         us = next((v for n, v in durations.items() if n == k), 0.0) / 1e3
         lines.append("| `%s` | %d | %.1f | %d | %.0f | %.1f | %.1f | %.1f | %.1f |" % (
             _short(k), len(vals["SQ_WAVES"][k]), us, waves, med("SQ_INSTS_VALU", k) / waves,

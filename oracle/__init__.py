@@ -194,6 +194,13 @@ def irfft(X, n: int) -> np.ndarray:
     conj X_{n-k}, the imaginary part of X_0 is dropped, and for even n that
     of X_{n/2} too (a real row has real values there; an odd n has no such
     middle bin), then the real part of :func:`ifft`."""
+    full = _hermitian_full(X, n)
+    return (ifft(full) if n & (n - 1) == 0 else dft(full, inverse=True)).real
+
+
+def _hermitian_full(X, n: int) -> np.ndarray:
+    """The n bins of a real row's transform from its X_0 .. X_{floor(n/2)}
+    (the reading of :func:`irfft`)."""
     X = _as_c128(X)
     h = n // 2
     if X.shape[-1] != h + 1:
@@ -206,7 +213,14 @@ def irfft(X, n: int) -> np.ndarray:
         full[..., h + 1:] = np.conj(X[..., 1:h][..., ::-1])
     elif n > 1:
         full[..., h + 1:] = np.conj(X[..., 1:h + 1][..., ::-1])
-    return (ifft(full) if n & (n - 1) == 0 else dft(full, inverse=True)).real
+    return full
+
+
+def irfft_sample(X, n: int, ks) -> np.ndarray:
+    """Selected samples x_j, j in ks, of :func:`irfft` (X, n), each computed
+    from the inverse DFT's definition in O(n) (:func:`dft_sample`)."""
+    full = _hermitian_full(X, n)
+    return dft_sample(full.reshape(-1, n), ks, inverse=True).real
 
 
 def rfft2(x) -> np.ndarray:

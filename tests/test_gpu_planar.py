@@ -52,6 +52,8 @@ CASES = [
     ((16, 32, 64), torch.complex64, 2),    # 3D
     ((8, 2048, 16), torch.complex64, 1),   # 3D, folded
     ((4, 1, 128), torch.complex128, 2),
+    ((17, 8), torch.complex64, 2),         # a transposed axis (chirp-z columns)
+    ((29, 31, 1), torch.complex128, 1),    # two transposed axes, no rows
 ]
 
 

@@ -182,3 +182,72 @@ def test_real_even_lengths(dev, n, dtype, batch):
     assert rel_rms_rows(y, oracle.irfft(S_np, n)).max() <= tol
     back = plan.irfft(plan.rfft(x)).cpu().numpy()
     assert rel_rms_rows(back, x_np).max() <= tol
+
+
+def _run_any(n, batch, dtype, seed):
+    """Real rows of any length n against the oracle: forward, the inverse of
+    an arbitrary half spectrum, and the round trip."""
+    print("case real n=%d batch=%d %s" % (n, batch, np.dtype(dtype).name), flush=True)
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    plan = fm.RealPlan(n, tdt)
+    x_np = wl.real_normal(n, batch, seed=seed, dtype=dtype)
+    x = torch.from_numpy(x_np).cuda()
+    X = plan.rfft(x).cpu().numpy()
+    tol = fft_tol(n, dtype == np.float64)
+    assert X.shape == (batch, n // 2 + 1)
+    cdt = np.complex64 if dtype == np.float32 else np.complex128
+    S_np = wl.real_spectrum(n, batch, seed=seed + 1, dtype=cdt)
+    S = torch.from_numpy(S_np).cuda()
+    y = plan.irfft(S).cpu().numpy()
+    if n <= 20000 or n & (n - 1) == 0:  # every output
+        assert rel_rms_rows(X, oracle.rfft(x_np)).max() <= tol, rel_rms_rows(X, oracle.rfft(x_np)).max()
+        yref = oracle.irfft(S_np, n)
+        assert rel_rms_rows(y, yref).max() <= tol, rel_rms_rows(y, yref).max()
+    else:  # the direct DFT is O(N^2): 64 outputs, each from the definition
+        oracle.set_threads(8)
+        rng = np.random.default_rng(n)
+        ks = np.unique(np.concatenate([[0, 1, n // 2], rng.integers(0, n // 2 + 1, 61)]))
+        ref = oracle.dft_sample(x_np.astype(np.float64), ks)
+        err = np.sqrt(np.mean(np.abs(X[:, ks] - ref) ** 2, axis=1)) / np.sqrt(np.mean(np.abs(ref) ** 2, axis=1))
+        assert err.max() <= tol, err.max()
+        js = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 62)]))
+        yref = oracle.irfft_sample(S_np, n, js)
+        err = np.sqrt(np.mean((y[:, js] - yref) ** 2, axis=1)) / np.sqrt(np.mean(yref ** 2, axis=1))
+        assert err.max() <= tol, err.max()
+    assert torch.equal(S.cpu(), torch.from_numpy(S_np))  # the C2R input is left as it was
+    back = plan.irfft(plan.rfft(x)).cpu().numpy()
+    assert rel_rms_rows(back, x_np).max() <= tol
+    return plan
+
+
+# odd lengths through each route of the N-point complex plan: mixed radix in
+# one kernel (15, 105, 1001 = 7 11 13, 2187 = 3^7), mixed-radix passes
+# (19683 = 3^9, 78125 = 5^7), chirp-z in one kernel (17, 97, 1009, 4097) and
+# in passes (100003)
+ODD = [(3, 5), (15, 7), (105, 3), (1001, 2), (2187, 2), (19683, 2), (78125, 1), (17, 9), (97, 4), (1009, 3),
+       (4097, 2), (100003, 1)]
+
+
+@pytest.mark.parametrize("n,batch", ODD)
+def test_real_odd_lengths_f32(dev, n, batch):
+    plan = _run_any(n, batch, np.float32, 300 + n % 97)
+    assert "odd" in plan.describe()
+
+
+@pytest.mark.parametrize("n,batch", [(3, 4), (45, 3), (1001, 2), (97, 3), (19683, 1)])
+def test_real_odd_lengths_f64(dev, n, batch):
+    _run_any(n, batch, np.float64, 400 + n % 89)
+
+
+def test_real_odd_closed_form(dev):
+    """A cosine of frequency 4 in a 15-point row: 15/2 at bin 4 and nothing
+    else; and back."""
+    n = 15
+    t = np.arange(n)
+    x = np.cos(2 * np.pi * ((4 * t) % n) / n)[None, :]
+    plan = fm.RealPlan(n, torch.float64)
+    X = plan.rfft(torch.from_numpy(x).cuda())
+    want = np.zeros(n // 2 + 1, complex)
+    want[4] = n / 2
+    assert np.abs(X.cpu().numpy()[0] - want).max() < 1e-12
+    assert np.abs(plan.irfft(X).cpu().numpy() - x).max() < 1e-13

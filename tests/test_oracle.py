@@ -692,3 +692,13 @@ def test_poly_eval_mod_pins_reject_planted_mistakes():
 
     for bad in (constant, reversed_order, no_reduction, dropped_constant, other_modulus):
         assert not _poly_eval_pins_hold(bad), bad.__name__
+
+
+@pytest.mark.parametrize("n", [2, 7, 16, 99, 1000])
+def test_irfft_sample_matches_irfft(n):
+    # the sampled route of the inverse equals the full one at the samples
+    rng = np.random.default_rng(n)
+    X = rng.standard_normal((2, n // 2 + 1)) + 1j * rng.standard_normal((2, n // 2 + 1))
+    ks = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 5)]))
+    full = oracle.irfft(X, n)
+    assert np.abs(oracle.irfft_sample(X, n, ks) - full[:, ks]).max() <= 1e-13 * max(1.0, math.log2(n))

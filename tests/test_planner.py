@@ -113,7 +113,7 @@ def test_3d_layouts():
     (0, [8], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [0], 0, fm.FFT_ERR_INVALID_ARG),
     (1, [8], 5, fm.FFT_ERR_INVALID_ARG),
-    (2, [17, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [(1 << 23) + 1, 2], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [(1 << 23) + 1], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
@@ -162,3 +162,16 @@ def test_ndmixed_layouts():
     assert "axis" not in _q(2, [1, 1000], 0)
     # the power-of-two shapes keep their own path
     assert "path=nd " in _q(2, [64, 32], 0)
+
+
+def test_transposed_axes_planned():
+    """Axes other than the innermost whose length has a prime factor above 13
+    are planned as the rank-1 route of their length over the transposed axis;
+    13-smooth axes keep their passes."""
+    d = _q(2, [17, 8], 0)
+    assert "axis1=transposed[bluestein" in d, d
+    d = _q(3, [19, 5, 8], 0)
+    assert "axis1=5 " in d and "axis2=transposed[bluestein" in d, d
+    d = _q(2, [4099, 3], 1)
+    assert "axis1=transposed[bluestein m=16384" in d, d
+    assert "transposed" not in _q(2, [1001, 12], 0)
