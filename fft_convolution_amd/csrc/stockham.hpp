@@ -281,6 +281,9 @@ template <typename V, int C, int PS = 4, bool WAVE = false> struct LdsLines {
         return base + f + (f >> PS);
     }
     static constexpr int off(int dpos) { return lds_off(dpos * C, PS); }
+    static constexpr int LINES = C;
+    // LDS slots of C interleaved transforms of n points
+    static constexpr int slots(int n) { return lds_padded(n * C, PS); }
     __device__ __forceinline__ static void sync()
     {
         if constexpr (WAVE) {
@@ -357,6 +360,29 @@ __device__ __forceinline__ void fft_stages_from(V (&v)[E], int t, const TB& tb, 
     }
 }
 
+// Race and index check, compiled in with -DFFTMI_LDS_POISON (the same
+// kernels, not a second path): before the first stage every slot of the LDS
+// region the transform's threads share is set to NaN, so that a read of a
+// slot the previous stage did not write -- a wrong index, or a missing
+// barrier -- turns the output into NaN instead of a stale value.
+template <int LOGN, typename V, typename L>
+__device__ __forceinline__ void lds_poison(const L& lds, int t)
+{
+#ifdef FFTMI_LDS_POISON
+    using G = Geom<V, LOGN>;
+    using Rl = typename real_of<V>::type;
+    if constexpr (G::S > 1) {
+        constexpr int threads = G::T * L::LINES;
+        const Rl nan = __builtin_nan("");
+        for (int k = t * L::LINES + lds.c; k < L::slots(G::N); k += threads) lds.base[k] = V{nan, nan};
+        L::sync();
+    }
+#else
+    (void)lds;
+    (void)t;
+#endif
+}
+
 // Forward transform of N = 2^LOGN points held as v[i] = x[t + i T]; on return
 // v[i] = X[t + i T].  Every thread of the workgroup must call it (barriers).
 // If the caller reuses the LDS afterwards it must put a barrier first.
@@ -364,6 +390,7 @@ template <int LOGN, typename V, int E, typename TB, typename L>
 __device__ __forceinline__ void fft_regs(V (&v)[E], int t, const TB& tb, const L& lds)
 {
     static_assert(E == kE<V, LOGN>, "register array size");
+    lds_poison<LOGN, V>(lds, t);
     fft_stages_from<LOGN, 0>(v, t, tb, lds);
 }
 
@@ -381,6 +408,7 @@ __device__ __forceinline__ void fft_regs_remap(V (&v)[E], int ta, const LA& la, 
 {
     static_assert(E == kE<V, LOGN>, "register array size");
     static_assert(Geom<V, LOGN>::S > 1, "a remap needs at least one exchange");
+    lds_poison<LOGN, V>(la, ta);
     fft_stage<LOGN, 0>(v, ta, tb, la);
     fft_stages_from<LOGN, 1>(v, tb_t, tb, lb);
 }
