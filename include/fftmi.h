@@ -156,7 +156,14 @@ int fft_plan_query(int rank, const int64_t* dims, int prec, char* buf, size_t le
 int fft_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes);
 
 /*
- * Batched 1D transform with a rank-1 plan.
+ * Batched 1D transform with a rank-1 plan: for each row, X_k = sum_n x_n
+ * e^{-2 pi i k n / N} (forward) or x_n = (1/N) sum_k X_k e^{+2 pi i k n / N}
+ * (inverse) -- "FFT on GPU", sections "Discrete Fourier Transform" and the
+ * one on why roots of unity are used (w -> w^{-1}, factor 1/N) -- computed
+ * as the Stockham passes of "Stockham FFT Butterfly Algorithm in Parallel
+ * GLSL", section "Execution via GLSL Compute Shaders and Textures", fused
+ * into on-chip stages as its section "Performance and Pipeline Evaluation"
+ * recommends.
  *   in, out:   [batch][N] complex of the plan's precision, rows contiguous.
  *              in == out (in place) is allowed; any other overlap is an error.
  *              in is not modified unless in == out.
@@ -192,7 +199,11 @@ int fft_exec_c2c_noalloc(const fft_plan* plan, int dir, const void* in, void* ou
 
 /*
  * Batched 2D transform with a rank-2 plan: row transforms of length W over
- * every row, then column transforms of length H over every column.
+ * every row, then column transforms of length H over every column
+ * ("Stockham FFT Butterfly Algorithm in Parallel GLSL", section
+ * "Multi-Dimensional Transforms and Separability": the 2D transform is the 1D
+ * transform along one axis, then along the other); the inverse scales by
+ * 1/(H W).
  *   in, out:   [batch][H][W] complex, images contiguous.  in == out allowed.
  *   workspace: fft_workspace_size(plan, batch) bytes for an in-place call
  *              (in == out) on a plan that folds part of the column transform
@@ -206,7 +217,10 @@ int fft_exec_2d(const fft_plan* plan, int dir, const void* in, void* out, int64_
                 void* workspace, void* stream);
 
 /*
- * Batched 3D transform with a rank-3 plan.
+ * Batched 3D transform with a rank-3 plan: the same separability one axis
+ * after another ("Stockham FFT Butterfly Algorithm in Parallel GLSL", section
+ * "Multi-Dimensional Transforms and Separability", which names 2D and 3D
+ * data); the inverse scales by 1/(D H W).
  *   in, out:   [batch][D][H][W] complex, volumes contiguous.  in == out allowed.
  *   workspace: as fft_exec_2d (power-of-two plans: only in place when the
  *              plan folds).
