@@ -88,6 +88,10 @@ void r2c_rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ t
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         const int k = t + i * T;
+        // rows of H + 1 bins start anywhere in a 128-byte line: nontemporal
+        // stores write some lines partially twice (16384 x 8192 real rows:
+        // 527 MiB written against 512.5 with plain stores), but plain stores
+        // measured slower (186.5 -> 193.6 us, same-box A/B)
         st_stream(dst + k, real_split(v[i], *L.ptr((H - k) & (H - 1)), cmul(whi[i], w0)));
     }
     if (t == 0) st_stream(dst + H, V{v[0].x - v[0].y, 0});
@@ -310,6 +314,12 @@ void r2c_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* 
     for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = y[i];
     if (t == 0) *L.ptr(H) = yh;
     __syncthreads();
+    // Rows of H + 1 bins start anywhere in a 128-byte line, so most store
+    // instructions begin and end in a line another one also writes: plain
+    // stores let L2 merge those halves, nontemporal ones reached HBM as
+    // partial lines (2048^2 x 8 real images: writes 142.6 -> 128.1 MiB, the
+    // algorithmic bytes; 116.3 -> 108.9 us for rows and columns, same-box A/B;
+    // staging the F rows in LDS and storing 128-byte-aligned windows: 110.4).
     V* dst = out + (img * hh + j * F) * (H + 1);
 #pragma unroll
     for (int k = 0; k < EF; ++k) {
@@ -320,7 +330,7 @@ void r2c_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* 
         Dft<F>::run(u);
         if (live) {
 #pragma unroll
-            for (int r = 0; r < F; ++r) st_stream(dst + r * (H + 1) + p, u[r]);
+            for (int r = 0; r < F; ++r) dst[r * (H + 1) + p] = u[r];
         }
     }
     if (rho == 0 && t == 0) {
@@ -330,7 +340,7 @@ void r2c_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* 
         Dft<F>::run(u);
         if (live) {
 #pragma unroll
-            for (int r = 0; r < F; ++r) st_stream(dst + r * (H + 1) + H, u[r]);
+            for (int r = 0; r < F; ++r) dst[r * (H + 1) + H] = u[r];
         }
     }
 }
