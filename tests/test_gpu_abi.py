@@ -49,3 +49,17 @@ def test_exec_validation(dev):
     assert _status(fm.fft_exec_3d, p2.handle, 0, x, y, 1) == fm.FFT_ERR_RANK
     assert _status(fm.fft_exec_2d, p3.handle, 0, x, y, 1) == fm.FFT_ERR_RANK
     assert _status(fm.fft_exec_3d, p3.handle, 0, x, y, 2) == fm.FFT_OK
+
+
+@pytest.mark.parametrize("nbytes", [8, 4096, 32768, 32768 + 8, 5 * 32768 + 1000, 1 << 26])
+def test_stream_copy_copies_every_byte(dev, nbytes):
+    """fft_stream_copy (the benchmark's ceiling) copies exactly `nbytes`:
+    full 32 KiB blocks, a partial last block, and leaves the bytes after the
+    range untouched."""
+    g = torch.Generator(device="cpu").manual_seed(nbytes % 1000)
+    src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, generator=g).to(dev)
+    dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device=dev)
+    fm.fft_stream_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src[:nbytes])
+    assert int(dst[nbytes:].count_nonzero()) == 0
