@@ -12,15 +12,19 @@
 namespace fftmi {
 
 // LDS layout of a row: one pad slot per 16 elements, per 32 for 8192-point
-// complex64 rows.  Measured on MI355X (SQ_LDS_BANK_CONFLICT per wave, same-box
-// A/B): one per 16 leaves 0 conflict cycles for rows of 256 - 2048 points, 64
-// at 4096 (no padding tried -- one per 8, 32, 64, or two levels 16 + 128 /
-// 256 / 512, 32 + 128 / 256 / 512 -- went below 64, and none changed the
-// time) and 192 at 8192, where one per 32 gives 0 and ran 2-3 % faster
-// (209 against 214.7 us for 8192 rows); one per 32 costs 64 at 256 - 2048.
+// complex64 rows, per 8 for complex128 rows.  Measured on MI355X
+// (SQ_LDS_BANK_CONFLICT per wave, same-box A/B): complex64, one per 16 leaves
+// 0 conflict cycles for rows of 256 - 2048 points, 64 at 4096 (no padding
+// tried -- one per 8, 32, 64, or two levels 16 + 128 / 256 / 512, 32 + 128 /
+// 256 / 512 -- went below 64, and none changed the time) and 192 at 8192,
+// where one per 32 gives 0 and ran 2-3 % faster (209 against 214.7 us for
+// 8192 rows); one per 32 costs 64 at 256 - 2048.  Complex128 (16-byte
+// elements), one per 8: 0 / 64 / 96 cycles for rows of 64 / 256 - 512 /
+// 1024 - 4096 points, against 96 / 128 / 160 with one per 16 (one per 4:
+// 96 - 384, per 32: 192 - 256, per 64: 448 - 512), times equal within noise.
 template <typename V, int LOGN> constexpr int row_pad_shift()
 {
-    return sizeof(V) == 8 && LOGN == 13 ? 5 : 4;
+    return sizeof(V) == 8 ? (LOGN == 13 ? 5 : 4) : 3;
 }
 // A row's threads share a wavefront (rows of up to 1024 complex64 / 512
 // complex128 points): the exchanges need no workgroup barrier (64 rows of
