@@ -16,6 +16,11 @@
 //       from the pair, conj, F, times w_N^{n1 k2} -- the forward's last pass
 //       and the inverse's first pass are one kernel
 //   A2: columns (length N2) again, Re / N, rint, int64 store.
+// Pass A has a pipelined form for columns of 512 points or more (one
+// workgroup per CU, the next tile's loads in flight during a transform).
+#include <atomic>
+
+#include "io.hpp"
 #include "launch.hpp"
 #include "stockham.hpp"
 #include "tile_common.hpp"
@@ -158,6 +163,90 @@ void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t*
     double2* dst = ws + (pair << (logn1 + LOGN2)) + col;
 #pragma unroll
     for (int i = 0; i < G::E; ++i) dst[(int64_t)(t + i * G::T) << logn1] = v[i];
+}
+
+// Pass A when both operands fit in the lower half of every column (la, lb <=
+// N/2, so positions n2 >= N2/2 are zero padding, a compile-time fact here).
+// Pass A holds one workgroup per CU (its tile's LDS), so a grid of one tile
+// per workgroup leaves each CU idle while a tile's loads are in flight.
+// Instead a grid of one workgroup per CU walks the tiles of the plain grid's
+// order (virtual block j * grid + b, so every workgroup stays on its XCD's
+// tile range) and loads tile j + 1's int64 values -- E/2 per operand and lane
+// -- while tile j is transformed and stored.
+template <int LOGN2>
+__global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
+void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
+                            double2* __restrict__ ws, int logn1, unsigned ntiles, const double2* __restrict__ tw,
+                            BigTw<double2> big)
+{
+    using G = Geom<double2, LOGN2>;
+    using TL = PolyTile<LOGN2>;
+    constexpr int H = G::E / 2;
+    constexpr int LC = __builtin_ctz(TL::C);
+    __shared__ double2 lds[TL::LDS];
+    const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
+    const LdsLines<double2, TL::CL> L{lds, c0};
+    const int lt = logn1 - LC;  // log2 of the tiles per pair
+    // Offsets within a pair's signal (< N <= 2^22 elements, so byte offsets
+    // fit 32 bits): the lane's first element, and the step between its
+    // elements (T rows of N1).
+    const unsigned lane = (unsigned)c0 + ((unsigned)t << logn1);
+    const unsigned step = (unsigned)G::T << logn1;
+    int64_t ra[H], rb[H];
+    // Every lane loads (an index past the operand is clamped to its last
+    // coefficient and the value dropped in value()), so that the loads are not
+    // branched around and the waits for later loads can count them.  With
+    // `real` false (the prefetch after a workgroup's last tile) every lane
+    // reads coefficient 0: one line, no tile's worth of HBM reads.
+    auto load = [&](unsigned vb, bool real) {
+        const unsigned tile = (unsigned)xcd_tile(vb, ntiles);
+        const unsigned n0 = real ? ((tile & ((1u << lt) - 1)) << LC) + lane : 0u;
+        const unsigned st = real ? step : 0u;
+        const int64_t* pa = a + (int64_t)(tile >> lt) * la;
+        const int64_t* pb = b + (int64_t)(tile >> lt) * lb;
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+            const unsigned n = n0 + i * st;
+            ra[i] = *at_bytes(pa, (unsigned)min((int64_t)n, la - 1) * 8u);
+            rb[i] = *at_bytes(pb, (unsigned)min((int64_t)n, lb - 1) * 8u);
+        }
+    };
+    auto value = [&](int i, unsigned n0) {
+        const int64_t n = (int64_t)(n0 + i * step);
+        return double2{n < la ? (double)ra[i] : 0.0, n < lb ? (double)rb[i] : 0.0};
+    };
+    if (blockIdx.x >= ntiles) return;  // the whole workgroup
+    // a loop body of one basic block (no early exit), so that the compiler
+    // cannot sink the next tile's loads towards their use
+    const unsigned iters = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    unsigned vb = blockIdx.x;
+    load(vb, true);
+    for (unsigned k = 0; k < iters; ++k) {
+        const unsigned tile = (unsigned)xcd_tile(vb, ntiles);
+        const unsigned col = ((tile & ((1u << lt) - 1)) << LC) + c0;  // n1
+        double2* dst = ws + ((int64_t)(tile >> lt) << (logn1 + LOGN2));
+        double2 v[G::E];
+#pragma unroll
+        for (int i = 0; i < G::E; ++i) v[i] = i < H ? value(i, col - c0 + lane) : double2{0.0, 0.0};
+        // The stage twiddle bases are loaded per tile, not held across the
+        // loop (the empty asm hides that their offset is loop-invariant), and
+        // before the next tile's loads: loads complete in issue order, so a
+        // wait for them then leaves the next tile's loads in flight.
+        unsigned zero = 0;
+        asm volatile("" : "+s"(zero));
+        TwBases<double2, LOGN2> tb;
+        tb.load(tw + zero, t);
+        __builtin_amdgcn_sched_barrier(0);
+        vb += gridDim.x;
+        const bool more = k + 1 < iters;  // uniform over the workgroup
+        load(more ? vb : vb - gridDim.x, more);
+        __builtin_amdgcn_sched_barrier(0);
+        fft_regs<LOGN2>(v, t, tb, L);
+        apply_big_twiddle<LOGN2>(v, (int64_t)col, t, big);
+#pragma unroll
+        for (int i = 0; i < G::E; ++i) *at_bytes(dst, (col + ((unsigned)t << logn1) + i * step) * 16u) = v[i];
+        __syncthreads();  // this tile's last exchange is read before the next one's first write
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -311,6 +400,21 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
     }
 }
 
+// Workgroups of the pipelined pass A: one per CU of the current device (a
+// multiple of 8, so that a workgroup keeps its XCD from tile to tile).
+static int64_t pipe_grid()
+{
+    static std::atomic<int> cus_of[64];  // per device, 0 until queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int cus = cus_of[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        cus_of[dev].store(cus, std::memory_order_relaxed);
+    }
+    return (int64_t)(cus & ~7);
+}
+
 template <int LOGN2>
 static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* ws,
                                int64_t batch, const void* tw_col, BigTw<double2> big, hipStream_t s)
@@ -320,6 +424,18 @@ static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const in
     if (n1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
     const int64_t blocks = batch * (n1 / TL::C);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // columns of 512 or more points: the tile's LDS holds a CU to one
+    // workgroup, the case the pipelined kernel is for (32 x 2^18 products:
+    // pass A 120.1 -> 91.7 us, product 315 -> 288 us)
+    if constexpr (TL::LDS * sizeof(double2) > 80 * 1024) {
+        const int64_t half = (int64_t)1 << (logn1 + LOGN2 - 1);
+        if (la <= half && lb <= half) {
+            const int64_t grid = std::min<int64_t>(blocks, pipe_grid());
+            hipLaunchKernelGGL((polypack_a_pipe_kernel<LOGN2>), dim3((unsigned)grid), dim3(TL::THREADS), 0, s, a, la,
+                               b, lb, (double2*)ws, logn1, (unsigned)blocks, (const double2*)tw_col, big);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((polypack_a_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s, a, la, b, lb,
                        (double2*)ws, logn1, (const double2*)tw_col, big);
     return hipGetLastError();

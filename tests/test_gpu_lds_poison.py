@@ -9,7 +9,7 @@ correct kernel reads) and free of NaN, and the 1D rows also match the oracle.
 Covered: the row kernels (every power of two, both precisions, wave-scope and
 workgroup exchanges), the multi-pass super-stages, the 2D fold and column
 passes and the split column stage, 3D, poly-mul in one kernel and in the
-four-step passes, real rows (fused and paired) and real images, chirp-z rows
+four-step passes (512-point columns: the pipelined pass A), real rows (fused and paired) and real images, chirp-z rows
 in one kernel and in passes."""
 import os
 
@@ -40,6 +40,7 @@ def _cases():
           ("c2c", (1024, 1024), torch.complex64, 1), ("c2c", (1024, 64), torch.complex128, 1),
           ("c2c", (16, 32, 64), torch.complex64, 1),
           ("poly", (1000,), torch.complex128, 2), ("poly", (3000,), torch.complex128, 2),
+          ("poly", (40000,), torch.complex128, 2),
           ("real", (1024,), torch.float32, 4), ("real", (1 << 15,), torch.float32, 2),
           ("real", (1024, 512), torch.float32, 1), ("real", (64, 64), torch.float64, 2)]
     return c

@@ -50,6 +50,11 @@ def test_small_exact(dev, la, lb, batch):
     (5000, 3000, 16384, 3),    # four-step, ragged lengths
     (1 << 15, 1 << 15, 1 << 16, 2),
     (10, 20, 1 << 16, 1),      # mostly zero padding
+    # 512-point columns, operands in the lower half: the pipelined pass A
+    (40000, 50001, 1 << 17, 3),    # 48 tiles: one per workgroup, grid not a multiple of 8
+    (1 << 19, 3, 1 << 20, 1),      # mostly zero padding in b
+    (1 << 21, 1 << 21, 1 << 22, 1),  # 1024-point columns, two tiles per workgroup
+    (70000, 10, 1 << 17, 2),       # a longer than N/2: the plain pass A
 ])
 def test_larger_against_oracle(dev, la, lb, n, batch):
     print("case la=%d lb=%d n=%d batch=%d" % (la, lb, n, batch), flush=True)
