@@ -299,7 +299,8 @@ struct fft_plan {
     int64_t n = 1;          // points per transform (H*W for 2D)
     int logn = 0;
     // rank 1, rows:      tw_a = stage table for N
-    // rank 1, multipass: passes[], poly-mul four-step: tw_a = rows (N1), tw_b = columns (N2), big_* = w_N
+    // rank 1, multipass: passes[], poly-mul four-step: tw_a = rows (N1), tw_b = columns (N2), big_* = w_N,
+    //                    tw_c = rows of N1/2 (the half-length inverse, N1 <= 1024)
     // rank 2:            tw_a = rows (W), tw_b = columns (Lc = H / F), big_* = w_H (F > 1)
     int log_a = 0, log_b = 0;
     void* tw_a = nullptr;
@@ -843,6 +844,9 @@ int upload_tables(fft_plan* p)
                 st = upload(stage_table(p->log_a, prec), prec, &p->tw_a);
                 if (st == FFT_OK) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
                 if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
+                // rows of N1/2 points: the half-length inverse of the real product
+                if (st == FFT_OK && p->log_a >= 5 && p->log_a <= 10)
+                    st = upload(stage_table(p->log_a - 1, prec), prec, &p->tw_c);
             }
             break;
         default:
@@ -1559,7 +1563,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
         if (plan->path == PATH_MULTIPASS) {
             const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
             e = launch_polymul_fourstep(plan->log_a, plan->log_b, a, la, b, lb, c, batch, workspace, plan->tw_a,
-                                        plan->tw_b, big, d_max_residual, s);
+                                        plan->tw_b, plan->tw_c, big, d_max_residual, s);
         } else if (plan->path == PATH_ROWS) {
             e = launch_polymul_rows(plan->log_a, a, la, b, lb, c, batch, plan->tw_a, d_max_residual, s);
         } else {

@@ -17,7 +17,9 @@
 //       and the inverse's first pass are one kernel
 //   A2: columns (length N2) again, Re / N, rint, int64 store.
 // Pass A has a pipelined form for columns of 512 points or more (one
-// workgroup per CU, the next tile's loads in flight during a transform).
+// workgroup per CU, the next tile's loads in flight during a transform), and
+// for rows of N1 <= 1024 the inverse runs at half length (B's HALF form and
+// A2h: even and odd coefficients of the real product as one complex value).
 #include <atomic>
 
 #include "io.hpp"
@@ -258,16 +260,28 @@ void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int
 // spectrum is C_k = A_k B_k = (Z_k^2 - conj(Z_{-k})^2) / (4i).  The inverse
 // starts right here: conj(C), the N1-point row transform again, times
 // w_N^{n1 k2}, written back over the row.
+//
+// HALF (rows of N1 <= 1024): the product c is real, so its inverse transform
+// runs at half length.  With d_m = c_{2m} + i c_{2m+1} (m < N/2),
+//     d = F_{N/2}^{-1}(D) / 2,  D_j = (C_j + C_{j+N/2}) + i (C_j - C_{j+N/2}) w_N^{-j}
+// (the even and odd samples of c have the spectra (C_j + C_{j+N/2}) / 2 and
+// (C_j - C_{j+N/2}) w_N^{-j} / 2).  j + N/2 is position k1 + N1/2 of the same
+// row, held by the same thread, so each row forms conj(D) for k1 < N1/2 and
+// runs the inverse's first step on N1/2 points: the transform over k1 (its
+// first T/2 threads, one wavefront at most), times w_{N/2}^{k2 m1} =
+// w_N^{2 k2 m1}, written over the first half of the row.  Pass A2 then reads
+// N1/2 columns and stores two coefficients per element: half the bytes of
+// this pass's writes and of A2's reads.
 // ---------------------------------------------------------------------------
 template <int LOGN1> constexpr int pack_groups()
 {
     return 2 * Geom<double2, LOGN1>::T >= 256 ? 1 : 256 / (2 * Geom<double2, LOGN1>::T);
 }
 
-template <int LOGN1>
+template <int LOGN1, bool HALF>
 __global__ __launch_bounds__((2 * Geom<double2, LOGN1>::T * pack_groups<LOGN1>()))
 void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, const double2* __restrict__ tw,
-                       BigTw<double2> big)
+                       const double2* __restrict__ tw_half, BigTw<double2> big)
 {
     using G = Geom<double2, LOGN1>;
     constexpr int GR = pack_groups<LOGN1>();
@@ -319,11 +333,48 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
         v[i] = double2{0.25 * sy, 0.25 * sx};
     }
     __syncthreads();  // partner reads done before the LDS is reused
-    fft_regs<LOGN1>(v, t, tb, L);
-    apply_big_twiddle<LOGN1>(v, row, t, big);
-    if (live) {
+    if constexpr (!HALF) {
+        fft_regs<LOGN1>(v, t, tb, L);
+        apply_big_twiddle<LOGN1>(v, row, t, big);
+        if (live) {
 #pragma unroll
-        for (int i = 0; i < G::E; ++i) rp[i * G::T] = v[i];
+            for (int i = 0; i < G::E; ++i) rp[i * G::T] = v[i];
+        }
+    } else {
+        using GH = Geom<double2, LOGN1 - 1>;
+        static_assert(GH::E == G::E && 2 * GH::T == G::T && GH::T <= 64, "half rows: the first T/2 threads, one wave");
+        using LH = LdsLines<double2, 1, PS, true>;
+        // conj(D_j) = (v_a + v_b) - i (v_a - v_b) w_N^j, v = conj(C) at k1 and
+        // k1 + N1/2 (registers i and i + E/2), j = k2 + N2 k1, staged in LDS
+        // at position k1 (slot k1 + k1 / 2^PS, the layout of LH)
+        double2 w = big(row + ((int64_t)t << logn2));
+        const double2 g = big((int64_t)G::T << logn2);
+#pragma unroll
+        for (int i = 0; i < G::E / 2; ++i) {
+            const double2 va = v[i], vb = v[i + G::E / 2];
+            const double2 u = cmul(double2{va.x - vb.x, va.y - vb.y}, w);
+            const int k1 = t + i * G::T;
+            mine[k1 + (k1 >> PS)] = double2{va.x + vb.x + u.y, va.y + vb.y - u.x};
+            if (i + 1 < G::E / 2) w = cmul(w, g);
+        }
+        __syncthreads();
+        if (t < GH::T) {
+            double2 y[GH::E];
+#pragma unroll
+            for (int i = 0; i < GH::E; ++i) {
+                const int k1 = t + i * GH::T;
+                y[i] = mine[k1 + (k1 >> PS)];
+            }
+            TwBases<double2, LOGN1 - 1> th;
+            th.load(tw_half, t);
+            fft_regs<LOGN1 - 1>(y, t, th, LH{mine, 0});
+            apply_big_twiddle<LOGN1 - 1>(y, 2 * row, t, big);
+            if (live) {
+                double2* hp = ws + (sig << (logn2 + LOGN1)) + (row << LOGN1) + t;
+#pragma unroll
+                for (int i = 0; i < GH::E; ++i) hp[i * GH::T] = y[i];
+            }
+        }
     }
 }
 
@@ -363,6 +414,51 @@ void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_
             const double r = rint(val);
             dst[n] = to_int64(r);
             worst = fmax(worst, out_residual(val, r));
+        }
+    }
+    resid_max(worst, d_resid);
+}
+
+// Pass A2 after a HALF pass B: columns m1 < N1/2 of the half-length rows
+// (k2 -> m2), r = F(conj D) at m = m1 + (N1/2) m2 is N conj(d_m), so
+// c_{2m} = Re(r) / N and c_{2m+1} = -Im(r) / N, rint, int64 store.
+template <int LOGN2>
+__global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
+void polypack_a2h_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
+                         const double2* __restrict__ tw, double* __restrict__ d_resid)
+{
+    using G = Geom<double2, LOGN2>;
+    using TL = PolyTile<LOGN2>;
+    __shared__ double2 lds[TL::LDS];
+    const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t tps = ((int64_t)1 << (logn1 - 1)) / TL::C;
+    const int64_t pair = tile / tps;
+    const int64_t col = (tile % tps) * TL::C + c0;  // m1
+    const double2* src = ws + (pair << (logn1 + LOGN2)) + col;
+
+    double2 v[G::E];
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) v[i] = src[(int64_t)(t + i * G::T) << logn1];
+    TwBases<double2, LOGN2> tb;
+    tb.load(tw, t);
+    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, TL::CL>{lds, c0});
+
+    const double inv_n = 1.0 / (double)((int64_t)1 << (logn1 + LOGN2));
+    double worst = 0.0;
+    int64_t* dst = c_out + pair * lc;
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) {
+        const int64_t n = 2 * (col + ((int64_t)(t + i * G::T) << (logn1 - 1)));
+        const double ve = v[i].x * inv_n, vo = -v[i].y * inv_n;
+        const double re = rint(ve), ro = rint(vo);
+        if (n < lc) {
+            dst[n] = to_int64(re);
+            worst = fmax(worst, out_residual(ve, re));
+        }
+        if (n + 1 < lc) {
+            dst[n + 1] = to_int64(ro);
+            worst = fmax(worst, out_residual(vo, ro));
         }
     }
     resid_max(worst, d_resid);
@@ -441,16 +537,16 @@ static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const in
     return hipGetLastError();
 }
 
-template <int LOGN1>
-static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* tw_row, BigTw<double2> big,
-                               hipStream_t s)
+template <int LOGN1, bool HALF>
+static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* tw_row, const void* tw_half,
+                               BigTw<double2> big, hipStream_t s)
 {
     constexpr int GR = pack_groups<LOGN1>();
     const int64_t ngroups = batch << (logn2 - 1);
     const int64_t blocks = (ngroups + GR - 1) / GR;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polypack_b_kernel<LOGN1>), dim3((unsigned)blocks), dim3(2 * Geom<double2, LOGN1>::T * GR), 0, s,
-                       (double2*)ws, ngroups, logn2, (const double2*)tw_row, big);
+    hipLaunchKernelGGL((polypack_b_kernel<LOGN1, HALF>), dim3((unsigned)blocks), dim3(2 * Geom<double2, LOGN1>::T * GR),
+                       0, s, (double2*)ws, ngroups, logn2, (const double2*)tw_row, (const double2*)tw_half, big);
     return hipGetLastError();
 }
 
@@ -468,11 +564,35 @@ static hipError_t polypack_a2_t(int logn1, const void* ws, int64_t* c, int64_t l
     return hipGetLastError();
 }
 
+template <int LOGN2>
+static hipError_t polypack_a2h_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
+                                 const void* tw_col, double* d_resid, hipStream_t s)
+{
+    using TL = PolyTile<LOGN2>;
+    const int64_t h1 = (int64_t)1 << (logn1 - 1);
+    if (h1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
+    const int64_t blocks = batch * (h1 / TL::C);
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((polypack_a2h_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s,
+                       (const double2*)ws, c, lc, logn1, (const double2*)tw_col, d_resid);
+    return hipGetLastError();
+}
+
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la, const int64_t* b, int64_t lb,
                                    int64_t* c, int64_t batch, void* ws, const void* tw_row, const void* tw_col,
-                                   BigTwiddle bigt, double* d_resid, hipStream_t s)
+                                   const void* tw_half, BigTwiddle bigt, double* d_resid, hipStream_t s)
 {
     const BigTw<double2> big{(const double2*)bigt.hi, (const double2*)bigt.lo, bigt.lbits, bigt.logn};
+    // the half-length inverse: rows of N1 <= 1024 (their halves fit one
+    // wavefront) whose first N1/2 columns split into whole column tiles
+    int tile_cols = 0;
+    switch (logn2) {
+#define TC(L) case L: tile_cols = PolyTile<L>::C; break;
+        TC(5) TC(6) TC(7) TC(8) TC(9) TC(10)
+#undef TC
+        default: return hipErrorInvalidValue;
+    }
+    const bool half = tw_half != nullptr && logn1 >= 5 && logn1 <= 10 && ((1 << (logn1 - 1)) % tile_cols) == 0;
     hipError_t e = hipErrorInvalidValue;
     switch (logn2) {
 #define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, s); break;
@@ -482,15 +602,19 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     }
     if (e != hipSuccess) return e;
     switch (logn1) {
-#define PB(L) case L: e = polypack_b_t<L>(logn2, ws, batch, tw_row, big, s); break;
-        PB(5) PB(6) PB(7) PB(8) PB(9) PB(10) PB(11) PB(12)
+#define PB(L) case L: e = half ? polypack_b_t<L, true>(logn2, ws, batch, tw_row, tw_half, big, s) \
+                             : polypack_b_t<L, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
+        PB(5) PB(6) PB(7) PB(8) PB(9) PB(10)
 #undef PB
+        case 11: e = polypack_b_t<11, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
+        case 12: e = polypack_b_t<12, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     const int64_t lc = la + lb - 1;
     switch (logn2) {
-#define PA2(L) case L: e = polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
+#define PA2(L) case L: e = half ? polypack_a2h_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s) \
+                              : polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
         PA2(5) PA2(6) PA2(7) PA2(8) PA2(9) PA2(10)
 #undef PA2
         default: return hipErrorInvalidValue;
