@@ -123,7 +123,7 @@ def setup_workload(name, dev, fm, torch, sets=1):
             x, y, ws = bufs[k % sets]
             fm.fft_exec_c2c(plan.handle, fm.FFT_FORWARD, x, y, batch, ws, stream)
         desc = plan.describe()
-        kernels = len(desc.split("radices=")[1].split("x")) if ("path=multipass" in desc or "path=mixpass" in desc) \
+        kernels = len(desc.split("radices=")[1].split()[0].split("x")) if ("path=multipass" in desc or "path=mixpass" in desc) \
             else (5 if "passes" in desc else 1)
         # the oracle's route for the length: the radix-2 FFT, the direct DFT,
         # or (rows too long for an O(N^2) pass in the time budget) a bounded

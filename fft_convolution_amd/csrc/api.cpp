@@ -789,6 +789,10 @@ int bluestein_tables(fft_plan* p)
     return st;
 }
 
+// Poly-mul products run their inverse at half length where the N1/2-point
+// halves of pass B's rows fit one wavefront (N1 <= 1024).
+bool poly_half_inverse(const fft_plan* p) { return p->log_a >= 5 && p->log_a <= 10; }
+
 // Builds and uploads the twiddle tables the layout needs.
 int upload_tables(fft_plan* p)
 {
@@ -845,8 +849,7 @@ int upload_tables(fft_plan* p)
                 if (st == FFT_OK) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
                 if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
                 // rows of N1/2 points: the half-length inverse of the real product
-                if (st == FFT_OK && p->log_a >= 5 && p->log_a <= 10)
-                    st = upload(stage_table(p->log_a - 1, prec), prec, &p->tw_c);
+                if (st == FFT_OK && poly_half_inverse(p)) st = upload(stage_table(p->log_a - 1, prec), prec, &p->tw_c);
             }
             break;
         default:
@@ -1071,6 +1074,10 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
             for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
                 off += snprintf(buf + off, len - off, q ? "x%lld" : "%lld", 1LL << p->passes[q].logr);
+            // the poly-mul split: rows N1 x columns N2, inverse at half length
+            if (p->log_a > 0 && off > 0 && (size_t)off < len)
+                snprintf(buf + off, len - off, " poly=%lldx%lld%s", 1LL << p->log_a, 1LL << p->log_b,
+                         poly_half_inverse(p) ? " inverse=half" : "");
             break;
         }
         default:

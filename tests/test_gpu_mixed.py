@@ -22,7 +22,7 @@ F64 = [3, 11, 12, 13, 100, 105, 1000, 1001, 2187, 2401, 3000, 3072, 4000, 4095]
 
 
 def _radices(desc):
-    return [int(r) for r in desc.split("radices=")[1].split("x")]
+    return [int(r) for r in desc.split("radices=")[1].split()[0].split("x")]
 
 
 def _check(n, batch, dtype, seed):
