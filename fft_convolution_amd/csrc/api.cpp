@@ -390,7 +390,7 @@ int upload(const std::vector<double>& host, int prec, void** dev)
     }
     e = hipMemcpy(*dev, src, bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-        hipFree(*dev);
+        (void)hipFree(*dev);
         *dev = nullptr;
         return hip_fail(e, "hipMemcpy(twiddles)");
     }
@@ -402,11 +402,11 @@ void free_plan(fft_plan* p)
     if (!p) return;
     void* ptrs[] = {p->tw_a, p->tw_b, p->tw_c, p->big_hi, p->big_lo, p->chirp, p->bspec, p->col_hi, p->col_lo};
     for (void* q : ptrs)
-        if (q) hipFree(q);
+        if (q) (void)hipFree(q);  // teardown: nothing to report a failure to
     for (int i = 0; i < 8; ++i) {
-        if (p->pass_tw[i]) hipFree(p->pass_tw[i]);
-        if (p->passes[i].big_hi) hipFree(p->passes[i].big_hi);
-        if (p->passes[i].big_lo) hipFree(p->passes[i].big_lo);
+        if (p->pass_tw[i]) (void)hipFree(p->pass_tw[i]);
+        if (p->passes[i].big_hi) (void)hipFree(p->passes[i].big_hi);
+        if (p->passes[i].big_lo) (void)hipFree(p->passes[i].big_lo);
     }
     if (p->inner) free_plan(p->inner);
     for (fft_plan* q : p->nx_plan)
@@ -782,8 +782,8 @@ int bluestein_tables(fft_plan* p)
         hipError_t e = hipStreamSynchronize(nullptr);
         if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize(plan)");
     }
-    if (ws) hipFree(ws);
-    if (bdev) hipFree(bdev);
+    if (ws) (void)hipFree(ws);
+    if (bdev) (void)hipFree(bdev);
     if (sub) fft_plan_destroy(sub);
     if (st == FFT_OK) st = fft_plan_create(&p->inner, 1, &mdim, p->prec);
     return st;
