@@ -300,7 +300,7 @@ struct fft_plan {
     int logn = 0;
     // rank 1, rows:      tw_a = stage table for N
     // rank 1, multipass: passes[], poly-mul four-step: tw_a = rows (N1), tw_b = columns (N2), big_* = w_N,
-    //                    tw_c = rows of N1/2 (the half-length inverse, N1 <= 1024)
+    //                    tw_c = rows of N1/2 (the half-length inverse)
     // rank 2:            tw_a = rows (W), tw_b = columns (Lc = H / F), big_* = w_H (F > 1)
     int log_a = 0, log_b = 0;
     void* tw_a = nullptr;
@@ -789,9 +789,9 @@ int bluestein_tables(fft_plan* p)
     return st;
 }
 
-// Poly-mul products run their inverse at half length where the N1/2-point
-// halves of pass B's rows fit one wavefront (N1 <= 1024).
-bool poly_half_inverse(const fft_plan* p) { return p->log_a >= 5 && p->log_a <= 10; }
+// Poly-mul products run their inverse at half length (N1/2-point rows in
+// pass B), for every row length of the four-step split.
+bool poly_half_inverse(const fft_plan* p) { return p->log_a >= 5 && p->log_a <= 12; }
 
 // Builds and uploads the twiddle tables the layout needs.
 int upload_tables(fft_plan* p)

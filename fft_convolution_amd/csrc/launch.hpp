@@ -145,8 +145,7 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
 //  A : z = a + i b -> column FFTs (length 2^logn2) + w_N^{n1 k2}    -> ws
 //  B : rows k2, N2 - k2: FFT, product spectrum, conj, FFT, w_N^{n1 k2} -> ws
 //  A2: column FFTs, real part / N, rint                            -> c
-// tw_half (stage table for N1/2, or NULL): for N1 <= 1024 the inverse runs at
-// half length (B: N1/2-point rows of the packed spectrum of the real product,
+// tw_half (stage table for N1/2, or NULL): the inverse runs at half length (B: N1/2-point rows of the packed spectrum of the real product,
 // A2: N1/2 columns, two coefficients per element).
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la,
                                    const int64_t* b, int64_t lb, int64_t* c, int64_t batch,

@@ -18,8 +18,8 @@
 //   A2: columns (length N2) again, Re / N, rint, int64 store.
 // Pass A has a pipelined form for columns of 512 points or more (one
 // workgroup per CU, the next tile's loads in flight during a transform), and
-// for rows of N1 <= 1024 the inverse runs at half length (B's HALF form and
-// A2h: even and odd coefficients of the real product as one complex value).
+// the inverse runs at half length (B's HALF form and A2h: even and odd
+// coefficients of the real product as one complex value).
 #include <atomic>
 
 #include "io.hpp"
@@ -261,14 +261,14 @@ void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int
 // starts right here: conj(C), the N1-point row transform again, times
 // w_N^{n1 k2}, written back over the row.
 //
-// HALF (rows of N1 <= 1024): the product c is real, so its inverse transform
+// HALF: the product c is real, so its inverse transform
 // runs at half length.  With d_m = c_{2m} + i c_{2m+1} (m < N/2),
 //     d = F_{N/2}^{-1}(D) / 2,  D_j = (C_j + C_{j+N/2}) + i (C_j - C_{j+N/2}) w_N^{-j}
 // (the even and odd samples of c have the spectra (C_j + C_{j+N/2}) / 2 and
 // (C_j - C_{j+N/2}) w_N^{-j} / 2).  j + N/2 is position k1 + N1/2 of the same
 // row, held by the same thread, so each row forms conj(D) for k1 < N1/2 and
 // runs the inverse's first step on N1/2 points: the transform over k1 (its
-// first T/2 threads, one wavefront at most), times w_{N/2}^{k2 m1} =
+// first T/2 threads), times w_{N/2}^{k2 m1} =
 // w_N^{2 k2 m1}, written over the first half of the row.  Pass A2 then reads
 // N1/2 columns and stores two coefficients per element: half the bytes of
 // this pass's writes and of A2's reads.
@@ -342,11 +342,10 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
         }
     } else {
         using GH = Geom<double2, LOGN1 - 1>;
-        static_assert(GH::E == G::E && 2 * GH::T == G::T && GH::T <= 64, "half rows: the first T/2 threads, one wave");
-        using LH = LdsLines<double2, 1, PS, true>;
+        static_assert(GH::E == G::E && 2 * GH::T == G::T, "half rows: the first T/2 threads of the row");
         // conj(D_j) = (v_a + v_b) - i (v_a - v_b) w_N^j, v = conj(C) at k1 and
         // k1 + N1/2 (registers i and i + E/2), j = k2 + N2 k1, staged in LDS
-        // at position k1 (slot k1 + k1 / 2^PS, the layout of LH)
+        // at position k1 (slot k1 + k1 / 2^PS, the layout of LdsLines)
         double2 w = big(row + ((int64_t)t << logn2));
         const double2 g = big((int64_t)G::T << logn2);
 #pragma unroll
@@ -358,19 +357,51 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
             if (i + 1 < G::E / 2) w = cmul(w, g);
         }
         __syncthreads();
-        if (t < GH::T) {
+        if constexpr (GH::T <= 64) {
+            // one wavefront: its exchanges need no workgroup barrier, and the
+            // row's other threads are done
+            if (t < GH::T) {
+                double2 y[GH::E];
+#pragma unroll
+                for (int i = 0; i < GH::E; ++i) {
+                    const int k1 = t + i * GH::T;
+                    y[i] = mine[k1 + (k1 >> PS)];
+                }
+                TwBases<double2, LOGN1 - 1> th;
+                th.load(tw_half, t);
+                fft_regs<LOGN1 - 1>(y, t, th, LdsLines<double2, 1, PS, true>{mine, 0});
+                apply_big_twiddle<LOGN1 - 1>(y, 2 * row, t, big);
+                if (live) {
+                    double2* hp = ws + (sig << (logn2 + LOGN1)) + (row << LOGN1) + t;
+#pragma unroll
+                    for (int i = 0; i < GH::E; ++i) hp[i * GH::T] = y[i];
+                }
+            }
+        } else {
+            // several wavefronts: the exchanges take workgroup barriers, which
+            // every thread must meet, so the row's other T/2 threads run the
+            // same transform on the second half of the row's LDS (whatever it
+            // holds: slots(N1) = 2 slots(N1/2) for PS = 3) and drop the result
+            constexpr int HS = lds_padded(GH::N, PS);
+            static_assert(2 * HS <= SLOTS, "a second half-row region in the row's LDS");
+            const bool kept = t < GH::T;
+            const int th_t = kept ? t : t - GH::T;
+            double2* reg = kept ? mine : mine + HS;
             double2 y[GH::E];
 #pragma unroll
             for (int i = 0; i < GH::E; ++i) {
-                const int k1 = t + i * GH::T;
-                y[i] = mine[k1 + (k1 >> PS)];
+                const int k1 = th_t + i * GH::T;
+                y[i] = reg[k1 + (k1 >> PS)];
             }
+            // the transform's first stage writes this region straight from
+            // registers: every wavefront's staged reads are done by then
+            __syncthreads();
             TwBases<double2, LOGN1 - 1> th;
-            th.load(tw_half, t);
-            fft_regs<LOGN1 - 1>(y, t, th, LH{mine, 0});
-            apply_big_twiddle<LOGN1 - 1>(y, 2 * row, t, big);
-            if (live) {
-                double2* hp = ws + (sig << (logn2 + LOGN1)) + (row << LOGN1) + t;
+            th.load(tw_half, th_t);
+            fft_regs<LOGN1 - 1>(y, th_t, th, LdsLines<double2, 1, PS>{reg, 0});
+            apply_big_twiddle<LOGN1 - 1>(y, 2 * row, th_t, big);
+            if (kept && live) {
+                double2* hp = ws + (sig << (logn2 + LOGN1)) + (row << LOGN1) + th_t;
 #pragma unroll
                 for (int i = 0; i < GH::E; ++i) hp[i * GH::T] = y[i];
             }
@@ -583,8 +614,8 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
                                    const void* tw_half, BigTwiddle bigt, double* d_resid, hipStream_t s)
 {
     const BigTw<double2> big{(const double2*)bigt.hi, (const double2*)bigt.lo, bigt.lbits, bigt.logn};
-    // the half-length inverse: rows of N1 <= 1024 (their halves fit one
-    // wavefront) whose first N1/2 columns split into whole column tiles
+    // the half-length inverse, where the first N1/2 columns split into whole
+    // column tiles
     int tile_cols = 0;
     switch (logn2) {
 #define TC(L) case L: tile_cols = PolyTile<L>::C; break;
@@ -592,7 +623,7 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
 #undef TC
         default: return hipErrorInvalidValue;
     }
-    const bool half = tw_half != nullptr && logn1 >= 5 && logn1 <= 10 && ((1 << (logn1 - 1)) % tile_cols) == 0;
+    const bool half = tw_half != nullptr && logn1 >= 5 && logn1 <= 12 && ((1 << (logn1 - 1)) % tile_cols) == 0;
     hipError_t e = hipErrorInvalidValue;
     switch (logn2) {
 #define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, s); break;
@@ -604,10 +635,8 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     switch (logn1) {
 #define PB(L) case L: e = half ? polypack_b_t<L, true>(logn2, ws, batch, tw_row, tw_half, big, s) \
                              : polypack_b_t<L, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
-        PB(5) PB(6) PB(7) PB(8) PB(9) PB(10)
+        PB(5) PB(6) PB(7) PB(8) PB(9) PB(10) PB(11) PB(12)
 #undef PB
-        case 11: e = polypack_b_t<11, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
-        case 12: e = polypack_b_t<12, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

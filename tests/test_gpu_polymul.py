@@ -53,6 +53,9 @@ def test_small_exact(dev, la, lb, batch):
     # 512-point columns, operands in the lower half: the pipelined pass A
     (40000, 50001, 1 << 17, 3),    # 48 tiles: one per workgroup, grid not a multiple of 8
     (1 << 19, 3, 1 << 20, 1),      # mostly zero padding in b
+    # rows of 2048 / 4096: half-length inverse rows spanning several wavefronts
+    (1 << 19, 1 << 19, 1 << 20, 2),
+    (1 << 20, (1 << 20) - 7, 1 << 21, 1),
     (1 << 21, 1 << 21, 1 << 22, 1),  # 1024-point columns, two tiles per workgroup
     (70000, 10, 1 << 17, 2),       # a longer than N/2: the plain pass A
 ])
