@@ -789,10 +789,6 @@ int bluestein_tables(fft_plan* p)
     return st;
 }
 
-// Poly-mul products run their inverse at half length (N1/2-point rows in
-// pass B), for every row length of the four-step split.
-bool poly_half_inverse(const fft_plan* p) { return p->log_a >= 5 && p->log_a <= 12; }
-
 // Builds and uploads the twiddle tables the layout needs.
 int upload_tables(fft_plan* p)
 {
@@ -849,7 +845,7 @@ int upload_tables(fft_plan* p)
                 if (st == FFT_OK) st = upload(stage_table(p->log_b, prec), prec, &p->tw_b);
                 if (st == FFT_OK) st = upload_big(p->logn, prec, &p->big_hi, &p->big_lo, &p->big_lbits);
                 // rows of N1/2 points: the half-length inverse of the real product
-                if (st == FFT_OK && poly_half_inverse(p)) st = upload(stage_table(p->log_a - 1, prec), prec, &p->tw_c);
+                if (st == FFT_OK) st = upload(stage_table(p->log_a - 1, prec), prec, &p->tw_c);
             }
             break;
         default:
@@ -1074,10 +1070,9 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=multipass radices=", (long long)p->n, prec);
             for (int q = 0; q < p->npass && off > 0 && (size_t)off < len; ++q)
                 off += snprintf(buf + off, len - off, q ? "x%lld" : "%lld", 1LL << p->passes[q].logr);
-            // the poly-mul split: rows N1 x columns N2, inverse at half length
+            // the poly-mul split: rows N1 x columns N2
             if (p->log_a > 0 && off > 0 && (size_t)off < len)
-                snprintf(buf + off, len - off, " poly=%lldx%lld%s", 1LL << p->log_a, 1LL << p->log_b,
-                         poly_half_inverse(p) ? " inverse=half" : "");
+                snprintf(buf + off, len - off, " poly=%lldx%lld", 1LL << p->log_a, 1LL << p->log_b);
             break;
         }
         default:

@@ -143,10 +143,10 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
 // Polynomial products, N = 2^(logn1 + logn2) beyond the LDS range (fp64),
 // ws = batch x N complex128:
 //  A : z = a + i b -> column FFTs (length 2^logn2) + w_N^{n1 k2}    -> ws
-//  B : rows k2, N2 - k2: FFT, product spectrum, conj, FFT, w_N^{n1 k2} -> ws
-//  A2: column FFTs, real part / N, rint                            -> c
-// tw_half (stage table for N1/2, or NULL): the inverse runs at half length (B: N1/2-point rows of the packed spectrum of the real product,
-// A2: N1/2 columns, two coefficients per element).
+//  B : rows k2, N2 - k2: FFT, product spectrum, the packed spectrum of the
+//      real product's even / odd coefficients, N1/2-point FFT, twiddle -> ws
+//  A2: the N1/2 column FFTs, two coefficients per element, rint      -> c
+// tw_half: the stage table for N1/2 points (the inverse runs at half length).
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la,
                                    const int64_t* b, int64_t lb, int64_t* c, int64_t batch,
                                    void* ws, const void* tw_row, const void* tw_col, const void* tw_half,

@@ -15,11 +15,12 @@
 //   B : rows k2 and N2 - k2 (length N1): F of both, the product spectrum
 //       from the pair, conj, F, times w_N^{n1 k2} -- the forward's last pass
 //       and the inverse's first pass are one kernel
-//   A2: columns (length N2) again, Re / N, rint, int64 store.
-// Pass A has a pipelined form for columns of 512 points or more (one
-// workgroup per CU, the next tile's loads in flight during a transform), and
-// the inverse runs at half length (B's HALF form and A2h: even and odd
-// coefficients of the real product as one complex value).
+//   A2: columns (length N2) again, then the real product, rint, int64 store.
+// The inverse runs at half length (even and odd coefficients of the real
+// product as one complex value: B's second transform has N1/2 points, A2
+// reads N1/2 columns).  Pass A has a pipelined form for columns of 512 points
+// or more (one workgroup per CU, the next tile's loads in flight during a
+// transform).
 #include <atomic>
 
 #include "io.hpp"
@@ -258,11 +259,10 @@ void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int
 // N1 - 1 - k1; row 0: position -k1 mod N1).  With A = (Z_k + conj Z_{-k})/2
 // and B = (Z_k - conj Z_{-k})/(2i) the spectra of a and b, the product
 // spectrum is C_k = A_k B_k = (Z_k^2 - conj(Z_{-k})^2) / (4i).  The inverse
-// starts right here: conj(C), the N1-point row transform again, times
-// w_N^{n1 k2}, written back over the row.
+// starts right here.
 //
-// HALF: the product c is real, so its inverse transform
-// runs at half length.  With d_m = c_{2m} + i c_{2m+1} (m < N/2),
+// The product c is real, so its inverse transform runs at half length.  With
+// d_m = c_{2m} + i c_{2m+1} (m < N/2),
 //     d = F_{N/2}^{-1}(D) / 2,  D_j = (C_j + C_{j+N/2}) + i (C_j - C_{j+N/2}) w_N^{-j}
 // (the even and odd samples of c have the spectra (C_j + C_{j+N/2}) / 2 and
 // (C_j - C_{j+N/2}) w_N^{-j} / 2).  j + N/2 is position k1 + N1/2 of the same
@@ -278,7 +278,7 @@ template <int LOGN1> constexpr int pack_groups()
     return 2 * Geom<double2, LOGN1>::T >= 256 ? 1 : 256 / (2 * Geom<double2, LOGN1>::T);
 }
 
-template <int LOGN1, bool HALF>
+template <int LOGN1>
 __global__ __launch_bounds__((2 * Geom<double2, LOGN1>::T * pack_groups<LOGN1>()))
 void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, const double2* __restrict__ tw,
                        const double2* __restrict__ tw_half, BigTw<double2> big)
@@ -333,14 +333,7 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
         v[i] = double2{0.25 * sy, 0.25 * sx};
     }
     __syncthreads();  // partner reads done before the LDS is reused
-    if constexpr (!HALF) {
-        fft_regs<LOGN1>(v, t, tb, L);
-        apply_big_twiddle<LOGN1>(v, row, t, big);
-        if (live) {
-#pragma unroll
-            for (int i = 0; i < G::E; ++i) rp[i * G::T] = v[i];
-        }
-    } else {
+    {
         using GH = Geom<double2, LOGN1 - 1>;
         static_assert(GH::E == G::E && 2 * GH::T == G::T, "half rows: the first T/2 threads of the row");
         // conj(D_j) = (v_a + v_b) - i (v_a - v_b) w_N^j, v = conj(C) at k1 and
@@ -410,52 +403,13 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
 }
 
 // ---------------------------------------------------------------------------
-// Pass A2: columns again (k2 -> n2), Re / N, rint, int64 store.
+// Pass A2: columns m1 < N1/2 of pass B's half-length rows (k2 -> m2);
+// r = F(conj D) at m = m1 + (N1/2) m2 is N conj(d_m), so c_{2m} = Re(r) / N
+// and c_{2m+1} = -Im(r) / N, rint, int64 store.
 // ---------------------------------------------------------------------------
 template <int LOGN2>
 __global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
-                        const double2* __restrict__ tw, double* __restrict__ d_resid)
-{
-    using G = Geom<double2, LOGN2>;
-    using TL = PolyTile<LOGN2>;
-    __shared__ double2 lds[TL::LDS];
-    const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t tps = ((int64_t)1 << logn1) / TL::C;
-    const int64_t pair = tile / tps;
-    const int64_t col = (tile % tps) * TL::C + c0;  // n1
-    const double2* src = ws + (pair << (logn1 + LOGN2)) + col;
-
-    double2 v[G::E];
-#pragma unroll
-    for (int i = 0; i < G::E; ++i) v[i] = src[(int64_t)(t + i * G::T) << logn1];
-    TwBases<double2, LOGN2> tb;
-    tb.load(tw, t);
-    fft_regs<LOGN2>(v, t, tb, LdsLines<double2, TL::CL>{lds, c0});
-
-    const double inv_n = 1.0 / (double)((int64_t)1 << (logn1 + LOGN2));
-    double worst = 0.0;
-    int64_t* dst = c_out + pair * lc;
-#pragma unroll
-    for (int i = 0; i < G::E; ++i) {
-        const int64_t n = col + ((int64_t)(t + i * G::T) << logn1);
-        if (n < lc) {
-            const double val = v[i].x * inv_n;
-            const double r = rint(val);
-            dst[n] = to_int64(r);
-            worst = fmax(worst, out_residual(val, r));
-        }
-    }
-    resid_max(worst, d_resid);
-}
-
-// Pass A2 after a HALF pass B: columns m1 < N1/2 of the half-length rows
-// (k2 -> m2), r = F(conj D) at m = m1 + (N1/2) m2 is N conj(d_m), so
-// c_{2m} = Re(r) / N and c_{2m+1} = -Im(r) / N, rint, int64 store.
-template <int LOGN2>
-__global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
-void polypack_a2h_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
                          const double2* __restrict__ tw, double* __restrict__ d_resid)
 {
     using G = Geom<double2, LOGN2>;
@@ -568,7 +522,7 @@ static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const in
     return hipGetLastError();
 }
 
-template <int LOGN1, bool HALF>
+template <int LOGN1>
 static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* tw_row, const void* tw_half,
                                BigTw<double2> big, hipStream_t s)
 {
@@ -576,27 +530,13 @@ static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* t
     const int64_t ngroups = batch << (logn2 - 1);
     const int64_t blocks = (ngroups + GR - 1) / GR;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polypack_b_kernel<LOGN1, HALF>), dim3((unsigned)blocks), dim3(2 * Geom<double2, LOGN1>::T * GR),
+    hipLaunchKernelGGL((polypack_b_kernel<LOGN1>), dim3((unsigned)blocks), dim3(2 * Geom<double2, LOGN1>::T * GR),
                        0, s, (double2*)ws, ngroups, logn2, (const double2*)tw_row, (const double2*)tw_half, big);
     return hipGetLastError();
 }
 
 template <int LOGN2>
 static hipError_t polypack_a2_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
-                                const void* tw_col, double* d_resid, hipStream_t s)
-{
-    using TL = PolyTile<LOGN2>;
-    const int64_t n1 = (int64_t)1 << logn1;
-    if (n1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
-    const int64_t blocks = batch * (n1 / TL::C);
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polypack_a2_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s,
-                       (const double2*)ws, c, lc, logn1, (const double2*)tw_col, d_resid);
-    return hipGetLastError();
-}
-
-template <int LOGN2>
-static hipError_t polypack_a2h_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
                                  const void* tw_col, double* d_resid, hipStream_t s)
 {
     using TL = PolyTile<LOGN2>;
@@ -604,7 +544,7 @@ static hipError_t polypack_a2h_t(int logn1, const void* ws, int64_t* c, int64_t 
     if (h1 % TL::C || TL::THREADS > 1024) return hipErrorInvalidValue;
     const int64_t blocks = batch * (h1 / TL::C);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((polypack_a2h_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s,
+    hipLaunchKernelGGL((polypack_a2_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s,
                        (const double2*)ws, c, lc, logn1, (const double2*)tw_col, d_resid);
     return hipGetLastError();
 }
@@ -614,8 +554,8 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
                                    const void* tw_half, BigTwiddle bigt, double* d_resid, hipStream_t s)
 {
     const BigTw<double2> big{(const double2*)bigt.hi, (const double2*)bigt.lo, bigt.lbits, bigt.logn};
-    // the half-length inverse, where the first N1/2 columns split into whole
-    // column tiles
+    // the half-length inverse: rows of N1/2 points in B, whose N1/2 columns
+    // split into whole column tiles in A2
     int tile_cols = 0;
     switch (logn2) {
 #define TC(L) case L: tile_cols = PolyTile<L>::C; break;
@@ -623,7 +563,8 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
 #undef TC
         default: return hipErrorInvalidValue;
     }
-    const bool half = tw_half != nullptr && logn1 >= 5 && logn1 <= 12 && ((1 << (logn1 - 1)) % tile_cols) == 0;
+    if (tw_half == nullptr || logn1 < 5 || logn1 > 12 || ((1 << (logn1 - 1)) % tile_cols) != 0)
+        return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     switch (logn2) {
 #define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, s); break;
@@ -633,8 +574,7 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     }
     if (e != hipSuccess) return e;
     switch (logn1) {
-#define PB(L) case L: e = half ? polypack_b_t<L, true>(logn2, ws, batch, tw_row, tw_half, big, s) \
-                             : polypack_b_t<L, false>(logn2, ws, batch, tw_row, nullptr, big, s); break;
+#define PB(L) case L: e = polypack_b_t<L>(logn2, ws, batch, tw_row, tw_half, big, s); break;
         PB(5) PB(6) PB(7) PB(8) PB(9) PB(10) PB(11) PB(12)
 #undef PB
         default: return hipErrorInvalidValue;
@@ -642,8 +582,7 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     if (e != hipSuccess) return e;
     const int64_t lc = la + lb - 1;
     switch (logn2) {
-#define PA2(L) case L: e = half ? polypack_a2h_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s) \
-                              : polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
+#define PA2(L) case L: e = polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
         PA2(5) PA2(6) PA2(7) PA2(8) PA2(9) PA2(10)
 #undef PA2
         default: return hipErrorInvalidValue;
