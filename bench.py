@@ -53,7 +53,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "C2C FFT GFLOP/s (5N·log2N/t) + achieved HBM TB/s, fp32 N=4096 batch 16384"
 WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_2048x2048_b8",
              "polymul_l262144_b32", "c2c3d_256x256x256_b1", "r2c_n8192_b16384", "c2c_n1000_b65536",
-             "c2c_n1009_b65536", "r2c2d_2048x2048_b8", "c2c_n1000000_b64")
+             "c2c_n1009_b65536", "r2c2d_2048x2048_b8", "c2c_n1000000_b64", "c2cpl_n4096_b16384")
 
 
 # The sources each single-kernel workload's kernel is built from: a stored
@@ -61,6 +61,7 @@ WORKLOADS = ("c2c_n4096_b16384", "c2c_n1024_b64", "c2c_n16777216_b1", "c2c2d_204
 KERNEL_SOURCES = {
     "c2c_n4096_b16384": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
     "c2c_n1024_b64": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
+    "c2cpl_n4096_b16384": ("rows.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
     "r2c_n8192_b16384": ("real.hip", "stockham.hpp", "radix_plan.hpp", "tile_common.hpp"),
     "c2c_n1000_b65536": ("mixed.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
     "c2c_n1009_b65536": ("bluestein.hip", "stockham.hpp", "radix_plan.hpp", "io.hpp", "tile_common.hpp"),
@@ -133,6 +134,25 @@ def setup_workload(name, dev, fm, torch, sets=1):
                     plan=desc, kernels=kernels, sample_rows=lambda rows: x_np[:rows],
                     oracle_fn="fft" if pow2 else ("dft" if n <= 16384 else "dft_bins"),
                     oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))
+        return step, info
+    if name.startswith("c2cpl_n"):
+        # split planes: re and im of the same seeded complex rows
+        import numpy as np
+        n, batch = spec["n"], spec["batch"]
+        x_np = wl.workload_input(name)
+        plan = fm.Plan(n, torch.complex64)
+        wsb = fm.fft_planar_workspace_size(plan.handle, batch)
+        re0 = torch.from_numpy(np.ascontiguousarray(x_np.real)).to(dev)
+        im0 = torch.from_numpy(np.ascontiguousarray(x_np.imag)).to(dev)
+        bufs = [((re0, im0) if k == 0 else (re0.clone(), im0.clone())) + (torch.empty_like(re0), torch.empty_like(im0),
+                                                                         ws_of(wsb)) for k in range(sets)]
+
+        def step(k=0):
+            xr, xi, yr, yi, ws = bufs[k % sets]
+            fm.fft_exec_planar(plan.handle, fm.FFT_FORWARD, xr, xi, yr, yi, batch, ws, stream)
+        info = dict(n=n, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=4 * re0.numel() * 4,
+                    plan=plan.describe() + " layout=planar", kernels=1, sample_rows=lambda rows: x_np[:rows],
+                    oracle_fn="fft", oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))
         return step, info
     if name.startswith("c2c2d") or name.startswith("c2c3d"):
         three = name.startswith("c2c3d")
