@@ -3,24 +3,25 @@
 // N, forward FFT of both, pointwise product, inverse FFT scaled by 1/N, round
 // the real part to the nearest integer.  fp64 throughout.
 //
-// The inverse is evaluated as conj(F(conj(P))) / N with the forward engine,
-// and only the real part is kept, which conj does not change.
+// Inverse transforms are evaluated as conj(F(conj(P))) / N with the forward
+// engine.
 //
 // N <= 4096: one fused kernel per pair (int64 load with implicit zero
-// padding, two forward transforms, product, third transform, rint, int64
-// store) -- the whole product never leaves the chip.
+// padding, two forward transforms, product, third transform, the real part,
+// rint, int64 store) -- the whole product never leaves the chip.
 // N > 4096: z = a + i b as one complex signal, split N = N1 N2, with the
-// pointwise product fused between the forward and the inverse row transforms:
+// pointwise product fused between the forward and the inverse row transforms,
+// and the inverse at half length (the real product's even and odd
+// coefficients as one complex value, N/2 points):
 //   A : columns (length N2) of z, times w_N^{n1 k2}
 //   B : rows k2 and N2 - k2 (length N1): F of both, the product spectrum
-//       from the pair, conj, F, times w_N^{n1 k2} -- the forward's last pass
-//       and the inverse's first pass are one kernel
-//   A2: columns (length N2) again, then the real product, rint, int64 store.
-// The inverse runs at half length (even and odd coefficients of the real
-// product as one complex value: B's second transform has N1/2 points, A2
-// reads N1/2 columns).  Pass A has a pipelined form for columns of 512 points
-// or more (one workgroup per CU, the next tile's loads in flight during a
-// transform).
+//       from the pair, the packed spectrum D of the half-length inverse,
+//       conj, the N1/2-point F, times w_{N/2}^{k2 m1} -- the forward's last
+//       pass and the inverse's first pass are one kernel
+//   A2: the N1/2 columns (length N2), c_{2m} and c_{2m+1} from each
+//       element, rint, int64 store.
+// Pass A has a pipelined form for columns of 512 points or more (one
+// workgroup per CU, the next tile's loads in flight during a transform).
 #include <atomic>
 
 #include "io.hpp"
