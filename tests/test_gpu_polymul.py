@@ -58,6 +58,8 @@ def test_small_exact(dev, la, lb, batch):
     (1 << 20, (1 << 20) - 7, 1 << 21, 1),
     (1 << 21, 1 << 21, 1 << 22, 1),  # 1024-point columns, two tiles per workgroup
     (70000, 10, 1 << 17, 2),       # a longer than N/2: the plain pass A
+    (600000, 100, 1 << 20, 1),     # the same with rows of 2048
+    (5, 3000000, 1 << 22, 1),      # b longer than N/2, rows of 4096
 ])
 def test_larger_against_oracle(dev, la, lb, n, batch):
     print("case la=%d lb=%d n=%d batch=%d" % (la, lb, n, batch), flush=True)
@@ -68,6 +70,28 @@ def test_larger_against_oracle(dev, la, lb, n, batch):
     assert np.array_equal(c, ref)
     ks = np.unique(np.concatenate([[0, 1, la + lb - 2], np.random.default_rng(0).integers(0, la + lb - 1, 50)]))
     assert np.array_equal(c[:, ks], oracle.schoolbook_sample(a, b, ks))
+    assert resid < 0.1
+
+
+@pytest.mark.parametrize("logn", list(range(13, 23)))
+def test_random_split_sizes(dev, logn):
+    """Every four-step size (N = 2^13 .. 2^22: rows of 64 .. 4096, columns
+    of 128 .. 1024), with operand lengths and batch drawn from a seed: ragged
+    lengths, either operand longer than N/2 or both within it, a batch not
+    a multiple of anything.  Bit-exact against the oracle's fp64 FFT route."""
+    n = 1 << logn
+    rng = np.random.default_rng(1000 + logn)
+    batch = int(rng.integers(1, 4))
+    la = int(rng.integers(1, n))
+    lb = int(rng.integers(max(1, n // 2 - la), n - la + 2))
+    if la + lb - 1 > n:
+        lb = n - la + 1
+    print("case logn=%d la=%d lb=%d batch=%d" % (logn, la, lb, batch), flush=True)
+    a, b = wl.random_polys(max(la, lb), batch, seed=logn)
+    a, b = a[:, :la], b[:, :lb]
+    c, resid = _gpu_mul(a, b, n, dev)
+    ref, _ = oracle.polymul_fft(a, b, n=n)
+    assert np.array_equal(c, ref)
     assert resid < 0.1
 
 
