@@ -54,7 +54,10 @@ def test_c2c_c128_sweep(dev, logn, batch):
         assert rel_rms_rows(y, ref).max() <= fft_tol(n, True)
 
 
-@pytest.mark.parametrize("logn,batch", [(14, 2), (15, 3), (16, 1), (18, 2), (20, 1), (22, 1)])
+# every multi-pass size below the largest (2^26, test_gpu_max_sizes): each
+# has its own split into super-stages (2 passes up to 2^18, 3 beyond)
+@pytest.mark.parametrize("logn,batch", [(14, 2), (15, 3), (16, 1), (17, 2), (18, 2), (19, 1), (20, 1), (21, 1),
+                                        (22, 1), (23, 1), (25, 1)])
 def test_c2c_c64_multipass(dev, logn, batch):
     n = 1 << logn
     x = _case(n, batch, np.complex64, 300 + logn)
@@ -66,7 +69,8 @@ def test_c2c_c64_multipass(dev, logn, batch):
         assert rel_rms_rows(y, ref).max() <= fft_tol(n)
 
 
-@pytest.mark.parametrize("logn,batch", [(13, 2), (14, 1), (16, 3), (19, 1)])
+@pytest.mark.parametrize("logn,batch", [(13, 2), (14, 1), (15, 2), (16, 3), (17, 1), (18, 1), (19, 1), (20, 1),
+                                        (21, 1), (22, 1), (23, 1)])
 def test_c2c_c128_multipass(dev, logn, batch):
     n = 1 << logn
     x = _case(n, batch, np.complex128, 400 + logn)
