@@ -66,7 +66,10 @@ EXPORTS = (
     "fft_exec_planar", "fft_planar_workspace_size", "fft_stream_copy", "fft_status_string", "fft_last_error",
 )
 
-_lock = threading.Lock()
+# Reentrant: a finalizer that the garbage collector runs while lib() is
+# loading the library (its allocations can trigger a collection) may call
+# back into the binding on the same thread.
+_lock = threading.RLock()
 _lib = None
 
 
@@ -269,6 +272,20 @@ def fft_stream_copy(src, dst, nbytes: int, stream=None) -> None:
 # Conveniences over torch tensors (allocation and shape checks only)
 # --------------------------------------------------------------------------
 
+def _release(obj) -> None:
+    """Free a plan object's handle through the library that created it (a
+    finalizer: no lock, no library loading, and the right library even after
+    the binding has been pointed at another build)."""
+    h = getattr(obj, "handle", None)
+    L = getattr(obj, "_lib", None)
+    if h and L is not None:
+        try:
+            L.fft_plan_destroy(h)
+        except Exception:
+            pass
+    obj.handle = None
+
+
 class Plan:
     """A plan handle.  ``Plan(n)``, ``Plan((h, w))`` or ``Plan((d, h, w))``; dtype torch.complex64/128."""
 
@@ -283,15 +300,10 @@ class Plan:
         self.dims = (int(dims),) if isinstance(dims, int) else tuple(int(d) for d in dims)
         self.rank = len(self.dims)
         self.handle = fft_plan_create(self.rank, self.dims, self.prec)
+        self._lib = lib()  # the library that made the handle, which frees it
 
     def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            try:
-                fft_plan_destroy(h)
-            except Exception:
-                pass
-            self.handle = None
+        _release(self)
 
     def describe(self) -> str:
         return fft_plan_describe(self.handle)
@@ -427,15 +439,10 @@ class RealPlan:
             self.handle = fft_plan_create_real_2d(self.dims[0], self.dims[1], self.prec)
         else:
             raise ValueError("real plans have one or two dims")
+        self._lib = lib()  # the library that made the handle, which frees it
 
     def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            try:
-                fft_plan_destroy(h)
-            except Exception:
-                pass
-            self.handle = None
+        _release(self)
 
     def describe(self) -> str:
         return fft_plan_describe(self.handle)
