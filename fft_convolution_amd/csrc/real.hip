@@ -21,6 +21,7 @@
 // handles the bins k and H - k together.  Rows of odd length have no half
 // length: they go through the N-point complex transform of the row itself
 // (real_odd_kernel, at the end).
+#include "io.hpp"
 #include "launch.hpp"
 #include "stockham.hpp"
 #include "tile_common.hpp"
@@ -28,23 +29,43 @@
 namespace fftmi {
 
 template <typename V> __device__ __forceinline__ V chalf(V a) { return V{a.x * 0.5f, a.y * 0.5f}; }
+__device__ __forceinline__ float fmar(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fmar(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
-// X_k from a = Z_k, b = Z_{H-k} and w = w_N^k.
-template <typename V> __device__ __forceinline__ V real_split(V a, V b, V w)
+// X_k from a = Z_k, b = Z_{H-k} and wh = w_N^k / 2:
+//   X_k = (a + conj b) / 2 - i (a - conj b) w_N^k / 2,
+// the halves folded into wh and into fused multiply-adds (10 operations).
+template <typename V> __device__ __forceinline__ V real_split(V a, V b, V wh)
 {
-    const V zc = cconj(b);
-    const V e = chalf(cadd(a, zc));
-    const V o = cmul_mi(chalf(csub(a, zc)));
-    return cadd(e, cmul(o, w));
+    using Rl = typename real_of<V>::type;
+    const Rl px = a.x + b.x, py = a.y - b.y;  // a + conj b
+    const Rl qx = a.x - b.x, qy = a.y + b.y;  // a - conj b
+    // -i q wh = (qy, -qx)(c, d) = (qy c + qx d, qy d - qx c)
+    return V{fmar((Rl)0.5, px, fmar(qy, wh.x, qx * wh.y)), fmar((Rl)0.5, py, fmar(qy, wh.y, -(qx * wh.x)))};
 }
 
-// Z_k from a = X_k, b = X_{H-k} and w = w_N^k.
-template <typename V> __device__ __forceinline__ V real_merge(V a, V b, V w)
+// Z_k from a = X_k, b = X_{H-k} and wh = w_N^k / 2:
+//   Z_k = (a + conj b) / 2 + i (a - conj b) conj(w_N^k) / 2.
+template <typename V> __device__ __forceinline__ V real_merge(V a, V b, V wh)
 {
-    const V xc = cconj(b);
-    const V e = chalf(cadd(a, xc));
-    const V o = cmul(chalf(csub(a, xc)), cconj(w));
-    return cadd(e, cmul_pi(o));
+    using Rl = typename real_of<V>::type;
+    const Rl px = a.x + b.x, py = a.y - b.y;  // a + conj b
+    const Rl qx = a.x - b.x, qy = a.y + b.y;  // a - conj b
+    // i q conj(wh) = i (qx c + qy d, qy c - qx d) = (qx d - qy c, qx c + qy d)
+    return V{fmar((Rl)0.5, px, fmar(qx, wh.y, -(qy * wh.x))), fmar((Rl)0.5, py, fmar(qx, wh.x, qy * wh.y))};
+}
+
+// The partner H - k of a thread's bin k = t + i T in the LDS row (H + 1
+// slots, the last one bin H): (T - t) + (E - 1 - i) T, for T a multiple of 16
+// one base per thread plus compile-time offsets (the layout pads one slot per
+// 16, so a delta that is a multiple of 16 adds a fixed number of slots);
+// smaller rows compute each slot.
+template <typename V, int T, int E> __device__ __forceinline__ V partner(const LdsLines<V, 1>& L, int t, int i)
+{
+    if constexpr (T % 16 == 0)
+        return L.ptr(T - t)[LdsLines<V, 1>::off((E - 1 - i) * T)];
+    else
+        return *L.ptr((T - t) + (E - 1 - i) * T);
 }
 
 // Slots per row in LDS: the H-point exchange layout plus one for X_H.
@@ -83,16 +104,18 @@ void r2c_rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ t
     for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
     __syncthreads();
     if (!live) return;
-    const V w0 = wlo[t];
+    const V wh0 = chalf(wlo[t]);  // w_N^k / 2 = whi[i] (wlo[t] / 2), exact
     V* dst = out + row * (H + 1);
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         const int k = t + i * T;
+        // bin 0 pairs with itself (H - 0 wraps to 0)
+        const V b = (i == 0 && t == 0) ? v[0] : partner<V, T, E>(L, t, i);
         // rows of H + 1 bins start anywhere in a 128-byte line: nontemporal
         // stores write some lines partially twice (16384 x 8192 real rows:
         // 527 MiB written against 512.5 with plain stores), but plain stores
         // measured slower (186.5 -> 193.6 us, same-box A/B)
-        st_stream(dst + k, real_split(v[i], *L.ptr((H - k) & (H - 1)), cmul(whi[i], w0)));
+        st_stream(at_bytes(dst, (unsigned)k * (unsigned)sizeof(V)), real_split(v[i], b, cmul(whi[i], wh0)));
     }
     if (t == 0) st_stream(dst + H, V{v[0].x - v[0].y, 0});
 }
@@ -131,12 +154,12 @@ void c2r_rows_kernel(const V* in, V* out, int64_t nrows, const V* __restrict__ t
 #pragma unroll
     for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
     __syncthreads();
-    const V w0 = wlo[t];
+    const V wh0 = chalf(wlo[t]);  // w_N^k / 2 = whi[i] (wlo[t] / 2), exact
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-        const int k = t + i * T;
-        // inverse transform as conj(F(conj Z)) / H
-        v[i] = cconj(real_merge(v[i], *L.ptr(H - k), cmul(whi[i], w0)));
+        // inverse transform as conj(F(conj Z)) / H; the partner of bin 0 is
+        // bin H, held in the slot after the row
+        v[i] = cconj(real_merge(v[i], partner<V, T, E>(L, t, i), cmul(whi[i], wh0)));
     }
     __syncthreads();  // partners are read before the transform reuses the LDS
     if constexpr (LOGH > 0) fft_regs<LOGH>(v, t, tb, L);
@@ -164,7 +187,7 @@ __global__ void r2c_pairs_kernel(const V* __restrict__ z, V* __restrict__ out, i
                 continue;
             }
             const V a = zr[k], b = zr[h - k];
-            const V w = wn(k);
+            const V w = chalf(wn(k));
             xr[k] = real_split(a, b, w);
             if (2 * k != h) xr[h - k] = real_split(b, a, V{-w.x, w.y});  // w_N^{H-k} = -conj w_N^k
         }
@@ -187,7 +210,7 @@ __global__ void c2r_pairs_kernel(const V* __restrict__ x, V* __restrict__ z, int
                 continue;
             }
             const V a = xr[k], b = xr[h - k];
-            const V w = wn(k);
+            const V w = chalf(wn(k));
             zr[k] = real_merge(a, b, w);
             if (2 * k != h) zr[h - k] = real_merge(b, a, V{-w.x, w.y});
         }
@@ -301,12 +324,12 @@ void r2c_fold_kernel(const V* in, V* out, int64_t ngroups, int log_lc, const V* 
 #pragma unroll
     for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
     __syncthreads();
-    const V w0 = wlo[t];
+    const V wh0 = chalf(wlo[t]);  // w_N^k / 2 = whi[i] (wlo[t] / 2), exact
     V y[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-        const int k = t + i * T;
-        y[i] = real_split(v[i], *L.ptr((H - k) & (H - 1)), cmul(whi[i], w0));
+        const V b = (i == 0 && t == 0) ? v[0] : partner<V, T, E>(L, t, i);
+        y[i] = real_split(v[i], b, cmul(whi[i], wh0));
     }
     const V yh{v[0].x - v[0].y, 0};  // bin H, from Z_0 (thread 0)
     __syncthreads();  // every partner read is done
