@@ -46,6 +46,13 @@ template <typename V> __device__ __forceinline__ V cmul_pinned(V a, V w)
     return V{fma_r(a.x, w.x, -p), fma_r(a.x, w.y, q)};
 }
 
+// Rows of one wavefront or less (T <= 64) are packed 256 threads to a
+// workgroup and order their exchanges with wavefront-scope fences; longer rows
+// take a workgroup each, so that a barrier holds only that row's waves (M =
+// 2048, complex64, 1009-point rows: two rows per workgroup 526 us, one 466 us).
+template <typename V, int LOGM> constexpr bool bl_in_wave() { return Geom<V, LOGM>::T <= 64; }
+template <typename V, int LOGM> constexpr int bl_rows_per_wg() { return bl_in_wave<V, LOGM>() ? 256 / Geom<V, LOGM>::T : 1; }
+
 // The whole chirp-z transform of a row in one kernel, for M = 2^LOGM within
 // the row kernel's range: the row is loaded once (times the chirp, zero
 // padded to M in registers), transformed, multiplied by B, transformed back
@@ -55,14 +62,14 @@ template <typename V> __device__ __forceinline__ V cmul_pinned(V a, V w)
 // out).  The twiddle bases are loaded again for the second transform rather
 // than held in registers across the first.
 template <typename V, int LOGM, bool PL, bool INV>
-__global__ __launch_bounds__((Geom<V, LOGM>::T * rows_per_wg<V, LOGM>()))
+__global__ __launch_bounds__((Geom<V, LOGM>::T * bl_rows_per_wg<V, LOGM>()))
 void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n, const V* __restrict__ tw,
                            const V* __restrict__ chirp, const V* __restrict__ bspec, typename real_of<V>::type scale)
 {
     using G = Geom<V, LOGM>;
     static_assert(G::E >= 2, "positions t + i T with i >= E/2 are the upper half");
     using Rl = typename real_of<V>::type;
-    constexpr int RPW = rows_per_wg<V, LOGM>();
+    constexpr int RPW = bl_rows_per_wg<V, LOGM>();
     __shared__ V lds[G::LDS > 0 ? G::LDS * RPW : 1];
 
     const int tid = threadIdx.x;
@@ -70,7 +77,7 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
     const int t = tid % G::T;
     const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
     const bool live = row < nrows;
-    const LdsLines<V, 1> L{lds + rloc * G::LDS, 0};
+    const LdsLines<V, 1, 4, bl_in_wave<V, LOGM>()> L{lds + rloc * G::LDS, 0};
 
     V v[G::E];
     const int64_t base = row * n;
@@ -95,7 +102,7 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
     // W B, conjugated for the inverse transform
 #pragma unroll
     for (int i = 0; i < G::E; ++i) v[i] = cconj(cmul_pinned(v[i], bspec[t + i * G::T]));
-    __syncthreads();  // the forward transform's last exchange is read by now
+    L.sync();  // the forward transform's last exchange is read by now
     {
         TwBases<V, LOGM> tb;
         tb.load(tw, t);
@@ -117,7 +124,7 @@ template <typename V, int LOGM, bool PL, bool INV>
 static hipError_t bluestein_rows_t(const Io& io, int64_t nrows, int n, const void* tw, const void* chirp,
                                    const void* bspec, double scale, hipStream_t s)
 {
-    constexpr int RPW = rows_per_wg<V, LOGM>();
+    constexpr int RPW = bl_rows_per_wg<V, LOGM>();
     constexpr int BLOCK = Geom<V, LOGM>::T * RPW;
     const int64_t blocks = (nrows + RPW - 1) / RPW;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
