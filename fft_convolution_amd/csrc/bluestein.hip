@@ -84,16 +84,23 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
     {
         TwBases<V, LOGM> tb;
         tb.load(tw, t);
+        // Every load is issued unconditionally, from an address clamped into
+        // the row (a dead row reads row 0), and the value is dropped after:
+        // loads under a branch each end in a wait for memory, which would
+        // serialise the row's loads.
+        const auto src = in.at((live ? row : 0) * n);
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
             const int p = t + i * G::T;
             V x{0, 0};
             // positions from M/2 on are zero padding (n <= M/2): a
             // compile-time zero, so the first stage's x + 0 terms can go
-            if (i < G::E / 2 && live && p < n) {
-                x = in.ld(base + p);
-                if (INV) x = cconj(x);
-                x = cmul_pinned(x, chirp[p]);
+            if (i < G::E / 2) {
+                const int pc = p < n ? p : n - 1;
+                V y = src.ld32((unsigned)pc);
+                if (INV) y = cconj(y);
+                y = cmul_pinned(y, chirp[pc]);
+                x = live && p < n ? y : V{0, 0};
             }
             v[i] = x;
         }
@@ -108,15 +115,27 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
         tb.load(tw, t);
         fft_regs<LOGM>(v, t, tb, L);
     }
-    if (!live) return;
     const Rl inv_m = (Rl)1 / (Rl)(1 << LOGM);
+    // outputs from M/2 on are never stored; the chirp factors and products
+    // are formed for every position (clamped), so that only the stores sit
+    // under a branch and no load waits inside one
+    V y[G::E / 2];
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) {
+    for (int i = 0; i < G::E / 2; ++i) {
         const int p = t + i * G::T;
-        if (i < G::E / 2 && p < n) {  // outputs from M/2 on are never stored
-            const V y = cmul_pinned(V{v[i].x * inv_m, -v[i].y * inv_m}, chirp[p]);
-            out.st(base + p, INV ? V{y.x * scale, -y.y * scale} : y);
-        }
+        y[i] = chirp[p < n ? p : n - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < G::E / 2; ++i) asm volatile("" ::"v"(y[i].x), "v"(y[i].y));  // loaded here, together
+#pragma unroll
+    for (int i = 0; i < G::E / 2; ++i) {
+        y[i] = cmul_pinned(V{v[i].x * inv_m, -v[i].y * inv_m}, y[i]);
+        if (INV) y[i] = V{y[i].x * scale, -y[i].y * scale};
+    }
+#pragma unroll
+    for (int i = 0; i < G::E / 2; ++i) {
+        const int p = t + i * G::T;
+        if (live && p < n) out.st(base + p, y[i]);
     }
 }
 
