@@ -539,10 +539,14 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
                    ? 0
                    : ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
     if (p->path == PATH_REAL && p->rank == 2 && p->real_nd) {
-        // [Z: the half spectrum (C2R)][Y: an axis of two or more passes][the rows' own]
-        const size_t half = (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem;
-        const size_t zy = p->nx_k ? half * (p->nx_np[0] >= 2 ? 2 : 1) : 0;
-        return zy + c2c_workspace(p->inner, batch * p->dims[0]);
+        // [Z: the half spectrum (C2R)][Y: an axis of two or more passes, or
+        // the transposed half spectrum][the rows' own][the transposed
+        // columns' plan's own]
+        const int64_t wc = p->dims[1] / 2 + 1;
+        const size_t half = (size_t)batch * (size_t)p->dims[0] * (size_t)wc * p->elem;
+        const bool tr = p->nx_k && p->nx_np[0] == 0;
+        const size_t zy = p->nx_k ? half * (p->nx_np[0] == 1 ? 1 : 2) : 0;
+        return zy + c2c_workspace(p->inner, batch * p->dims[0]) + (tr ? c2c_workspace(p->nx_plan[0], batch * wc) : 0);
     }
     if (p->path == PATH_REAL && p->rank == 2)  // the half spectrum of every image (C2R; R2C with a column stage)
         return p->dims[0] > 1 ? (size_t)batch * (size_t)p->dims[0] * (size_t)(p->dims[1] / 2 + 1) * p->elem : 0;
@@ -1018,6 +1022,13 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
                                    : p->inner->real_odd ? "odd" : p->inner->real_fused ? "fused" : "pairs");
                 if (p->nx_k && off > 0 && (size_t)off < len) {
                     off += snprintf(buf + off, len - off, " axis1=");
+                    if (p->nx_np[0] == 0 && p->nx_plan[0]) {  // transposed: the rank-1 plan's route
+                        char ab[160] = "?";
+                        fft_plan_describe(p->nx_plan[0], ab, sizeof ab);
+                        const char* at = strstr(ab, "path=");
+                        if (at) memmove(ab, at + 5, strlen(at + 5) + 1);
+                        off += snprintf(buf + off, len - off, "transposed[%s]", ab);
+                    }
                     for (int q = 0; q < p->nx_np[0] && off > 0 && (size_t)off < len; ++q)
                         off += snprintf(buf + off, len - off, q ? "x%d" : "%d", p->passes[q].r);
                 }
@@ -1640,12 +1651,15 @@ static int real_2d_any(fft_plan** out_plan, int64_t h, int64_t w, int prec)
     if (h * wc > max_n(prec))
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "%lld x %lld half-spectrum points exceed %lld", (long long)h,
                     (long long)wc, (long long)max_n(prec));
+    // columns of 13-smooth height: super-stage passes over the half
+    // spectrum; any other height: transposed, as rows of the rank-1 plan of
+    // that length (chirp-z), and transposed back
     MixedSchedule chk;
     int rs[3] = {(int)h, 0, 0};
-    const int np = h == 1 ? 0 : axis_split(h, rs);
-    if (h > 1 && (!mixed_factor(h, &chk) || np == 0))
-        return fail(FFT_ERR_UNSUPPORTED_SIZE, "image height %lld: columns take 2^a 3^b 5^c 7^d 11^e 13^f points",
-                    (long long)h);
+    const int np = h == 1 || !mixed_factor(h, &chk) ? 0 : axis_split(h, rs);
+    if (h > 1 && np == 0 && h > kBluesteinMax)
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "image height %lld exceeds %lld", (long long)h,
+                    (long long)kBluesteinMax);
     fft_plan* p = new (std::nothrow) fft_plan;
     if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
     p->rank = 2;
@@ -1676,6 +1690,7 @@ static int real_2d_any(fft_plan** out_plan, int64_t h, int64_t w, int prec)
         return hip_fail(e, "hipGetDevice");
     }
     int st = fft_plan_create_real(&p->inner, w, prec);
+    if (st == FFT_OK && h > 1 && np == 0) st = fft_plan_create(&p->nx_plan[0], 1, &p->nx_len[0], prec);
     for (int q = 0; q < p->nx_np[0] && st == FFT_OK; ++q) {
         PassPlan& pp = p->passes[q];
         st = upload(mixed_table(pp.ms), prec, &p->pass_tw[q]);
@@ -1786,10 +1801,32 @@ static int exec_real_2d_any(const fft_plan* plan, bool c2r, const void* in, void
     const size_t half = (size_t)batch * (size_t)plan->n * plan->elem;
     const bool cols = plan->nx_k > 0;
     char* z = (char*)workspace;
-    char* y = cols && plan->nx_np[0] >= 2 ? z + half : nullptr;
+    char* y = cols && plan->nx_np[0] != 1 ? z + half : nullptr;
     void* rows_ws = cols ? (void*)(z + half * (y ? 2 : 1)) : workspace;
     const char* what = c2r ? "fft_exec_c2r" : "fft_exec_r2c";
     hipError_t e = hipSuccess;
+    if (cols && plan->nx_np[0] == 0) {
+        // [b][H][Wc] -> [b][Wc][H] in Y, the H-point rows there, and back
+        const int64_t wc = plan->dims[1] / 2 + 1;
+        void* tws = (char*)rows_ws + c2c_workspace(plan->inner, batch * h);
+        const Io tio{y, nullptr, y, nullptr};
+        if (!c2r) {
+            int st = fft_exec_r2c(plan->inner, in, out, batch * h, rows_ws, s);
+            if (st != FFT_OK) return st;
+            e = launch_transpose(plan->prec, out, nullptr, y, nullptr, h, wc, batch, s);
+            if (e != hipSuccess) return hip_fail(e, what);
+            st = run_1d(plan->nx_plan[0], false, tio, batch * wc, tws, s);
+            if (st != FFT_OK) return st;
+            return real_done(launch_transpose(plan->prec, y, nullptr, out, nullptr, wc, h, batch, s), what, s);
+        }
+        e = launch_transpose(plan->prec, in, nullptr, y, nullptr, h, wc, batch, s);
+        if (e != hipSuccess) return hip_fail(e, what);
+        int st = run_1d(plan->nx_plan[0], true, tio, batch * wc, tws, s);
+        if (st != FFT_OK) return st;
+        e = launch_transpose(plan->prec, y, nullptr, z, nullptr, wc, h, batch, s);
+        if (e != hipSuccess) return hip_fail(e, what);
+        return fft_exec_c2r(plan->inner, z, out, batch * h, rows_ws, s);
+    }
     if (!c2r) {
         int st = fft_exec_r2c(plan->inner, in, out, batch * h, rows_ws, s);
         if (st != FFT_OK) return st;

@@ -313,10 +313,14 @@ int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
  * the half spectrum (one column per lane; for H > 512 a radix-F column stage
  * first, as for complex plans).  The same fft_exec_r2c / fft_exec_c2r calls
  * take it; fft_plan_describe shows path=real2d.
- * Other shapes: any W, H = 2^a 3^b 5^c 7^d 11^e 13^f, at most
- * FFT_MAX_N_* points in the half spectrum: the rows by the real-row plan of
- * length W (fft_plan_create_real), then the column axis as mixed-radix
- * super-stage passes over the half spectrum (path=real2dmixed); a workspace of
+ * Other shapes: any W, any H <= FFT_MAX_BLUESTEIN_N, at most FFT_MAX_N_*
+ * points in the half spectrum: the rows by the real-row plan of length W
+ * (fft_plan_create_real), then the column axis -- for H = 2^a 3^b 5^c 7^d
+ * 11^e 13^f as mixed-radix super-stage passes over the half spectrum; for
+ * other H ("FFT on GPU", section "Algorithm per signal Length": the chirp-z
+ * route for any length) transposed to [W/2 + 1][H], run as rows by the rank-1
+ * plan of length H, and transposed back (fft_plan_describe:
+ * "axis1=transposed[...]") -- (path=real2dmixed); a workspace of
  * fft_workspace_size bytes on every call (C2R runs the columns into it and
  * leaves its input as it was).
  * Errors: INVALID_ARG, UNSUPPORTED_SIZE, DEVICE.

@@ -178,8 +178,7 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     (0, 8, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 0, 0, fm.FFT_ERR_INVALID_ARG),
     (8, 8, 3, fm.FFT_ERR_INVALID_ARG),
-    (97, 8, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),    # height with a prime factor above 13
-    (51, 16, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (8388617, 1, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # prime height beyond the chirp-z range
     (65536, 2048, 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # half spectrum beyond 2^26 points
     (16384, 2048, 1, fm.FFT_ERR_UNSUPPORTED_SIZE),  # beyond 2^24 points
 ])
@@ -191,7 +190,8 @@ def test_real_2d_plan_create_rejects(h, w, prec, status):
 
 @pytest.mark.skipif(_have_gpu(), reason="host without a GPU only")
 def test_valid_real_2d_plan_without_gpu_is_a_device_error():
-    for h, w, prec in ((1, 1, 0), (8192, 16384, 0), (4096, 8192, 1), (64, 2, 0), (8, 7, 0), (6, 15, 1)):
+    for h, w, prec in ((1, 1, 0), (8192, 16384, 0), (4096, 8192, 1), (64, 2, 0), (8, 7, 0), (6, 15, 1),
+                       (97, 8, 0), (51, 16, 1)):
         hd = ctypes.c_void_p(12345)
         assert fm.lib().fft_plan_create_real_2d(ctypes.byref(hd), h, w, prec) == fm.FFT_ERR_DEVICE
         assert hd.value is None

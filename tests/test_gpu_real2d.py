@@ -56,7 +56,8 @@ def test_real_2d(dev, h, w, dtype, batch):
 
 # Shapes outside the power-of-two route: the real rows of any even width by
 # their route, the H-point column axis as mixed-radix passes over the half
-# spectrum.
+# spectrum, or, for heights with a prime factor above 13, transposed and run
+# as rows by the chirp-z plan of that height.
 CASES_ANY = [
     (100, 8, torch.float32, 2), (7, 100, torch.float32, 2), (12, 30, torch.float32, 3), (1, 100, torch.float32, 2),
     (100, 1, torch.float32, 2), (30, 194, torch.float32, 2), (1000, 600, torch.float32, 1),
@@ -65,7 +66,20 @@ CASES_ANY = [
     # odd widths: the rows by the N-point complex plan of their length
     (12, 15, torch.float32, 2), (8, 7, torch.float32, 3), (100, 99, torch.float32, 2), (16, 1001, torch.float32, 1),
     (6, 97, torch.float64, 2), (1, 5, torch.float32, 2),
+    # heights with a prime factor above 13: the transposed column route
+    (97, 8, torch.float32, 2), (51, 16, torch.float64, 1), (1009, 64, torch.float32, 1), (323, 30, torch.float32, 2),
+    (97, 15, torch.float32, 1), (4099, 6, torch.float32, 1), (17, 1, torch.float32, 3), (34, 100, torch.float64, 1),
 ]
+
+
+def _prime_factors(n):
+    out, p = [], 2
+    while p * p <= n:
+        while n % p == 0:
+            out.append(p)
+            n //= p
+        p += 1
+    return out + ([n] if n > 1 else [])
 
 
 @pytest.mark.parametrize("h,w,dtype,batch", CASES_ANY, ids=lambda v: str(v))
@@ -76,6 +90,8 @@ def test_real_2d_any_shape(dev, h, w, dtype, batch):
     x_np = wl.real_normal(h * w, batch, seed=h + 5 * w, dtype=npdt).reshape(batch, h, w)
     plan = fm.RealPlan((h, w), dtype)
     assert "path=real2dmixed" in plan.describe()
+    big_prime = max(_prime_factors(h), default=1) > 13
+    assert ("axis1=transposed[bluestein" in plan.describe()) == big_prime, plan.describe()
     x = torch.from_numpy(x_np).to(dev)
     tol = fft_tol(h * w, dtype == torch.float64)
     oracle.set_threads(8)
