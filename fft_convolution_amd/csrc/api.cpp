@@ -1571,7 +1571,8 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (d_max_residual) e = launch_zero_resid(d_max_residual, s);
+    // the four-step route clears the residual in its first kernel
+    if (d_max_residual && plan->path != PATH_MULTIPASS) e = launch_zero_resid(d_max_residual, s);
     if (e == hipSuccess) {
         if (plan->path == PATH_MULTIPASS) {
             const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};

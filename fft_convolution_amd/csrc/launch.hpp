@@ -135,7 +135,8 @@ hipError_t launch_stock_pass(int prec, int logr, int kind, const void* in, void*
                              double scale, hipStream_t stream, const void* in_im = nullptr,
                              void* out_im = nullptr);
 
-// Polynomial products, N = 2^logn <= LDS range: one fused kernel per row pair.
+// Polynomial products, N = 2^logn <= LDS range: one fused kernel per row pair
+// (raises *d_resid, which the caller clears first).
 hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int64_t* b, int64_t lb,
                                int64_t* c, int64_t batch, const void* tw, double* d_resid,
                                hipStream_t stream);
@@ -147,6 +148,8 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
 //      real product's even / odd coefficients, N1/2-point FFT, twiddle -> ws
 //  A2: the N1/2 column FFTs, two coefficients per element, rint      -> c
 // tw_half: the stage table for N1/2 points (the inverse runs at half length).
+// d_resid (may be NULL): cleared by A, raised to the largest rounding
+// residual by A2 (no separate clearing launch).
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la,
                                    const int64_t* b, int64_t lb, int64_t* c, int64_t batch,
                                    void* ws, const void* tw_row, const void* tw_col, const void* tw_half,

@@ -53,6 +53,14 @@ __device__ __forceinline__ void resid_max(double r, double* d_resid)
 
 __global__ void zero_resid_kernel(double* d) { *d = 0.0; }
 
+// The first kernel of the four-step product clears the residual that its
+// last kernel raises (kernels on one stream run one after another): one
+// thread of workgroup 0, no launch of its own.
+__device__ __forceinline__ void clear_resid(double* d_resid)
+{
+    if (d_resid && blockIdx.x == 0 && threadIdx.x == 0) *d_resid = 0.0;
+}
+
 // The residual of one output value val (= Re(y) / N) rounded to r = rint(val):
 // |val - r|, or +infinity where that cannot vouch for the result -- |val| >=
 // 2^53, where every double is an integer and a rounding error no longer shows
@@ -141,11 +149,13 @@ template <int LOGN2> using PolyTile = Tile<double2, LOGN2, (LOGN2 <= 9 ? 16 : 8)
 template <int LOGN2>
 __global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
-                       double2* __restrict__ ws, int logn1, const double2* __restrict__ tw, BigTw<double2> big)
+                       double2* __restrict__ ws, int logn1, const double2* __restrict__ tw, BigTw<double2> big,
+                       double* __restrict__ d_resid)
 {
     using G = Geom<double2, LOGN2>;
     using TL = PolyTile<LOGN2>;
     __shared__ double2 lds[TL::LDS];
+    clear_resid(d_resid);
     const int c0 = threadIdx.x % TL::CL, t = threadIdx.x / TL::CL;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t tps = ((int64_t)1 << logn1) / TL::C;
@@ -181,8 +191,9 @@ template <int LOGN2>
 __global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
                             double2* __restrict__ ws, int logn1, unsigned ntiles, const double2* __restrict__ tw,
-                            BigTw<double2> big)
+                            BigTw<double2> big, double* __restrict__ d_resid)
 {
+    clear_resid(d_resid);
     using G = Geom<double2, LOGN2>;
     using TL = PolyTile<LOGN2>;
     constexpr int H = G::E / 2;
@@ -499,7 +510,7 @@ static int64_t pipe_grid()
 
 template <int LOGN2>
 static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* ws,
-                               int64_t batch, const void* tw_col, BigTw<double2> big, hipStream_t s)
+                               int64_t batch, const void* tw_col, BigTw<double2> big, double* d_resid, hipStream_t s)
 {
     using TL = PolyTile<LOGN2>;
     const int64_t n1 = (int64_t)1 << logn1;
@@ -514,12 +525,12 @@ static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const in
         if (la <= half && lb <= half) {
             const int64_t grid = std::min<int64_t>(blocks, pipe_grid());
             hipLaunchKernelGGL((polypack_a_pipe_kernel<LOGN2>), dim3((unsigned)grid), dim3(TL::THREADS), 0, s, a, la,
-                               b, lb, (double2*)ws, logn1, (unsigned)blocks, (const double2*)tw_col, big);
+                               b, lb, (double2*)ws, logn1, (unsigned)blocks, (const double2*)tw_col, big, d_resid);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((polypack_a_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s, a, la, b, lb,
-                       (double2*)ws, logn1, (const double2*)tw_col, big);
+                       (double2*)ws, logn1, (const double2*)tw_col, big, d_resid);
     return hipGetLastError();
 }
 
@@ -568,7 +579,7 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
         return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     switch (logn2) {
-#define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, s); break;
+#define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, d_resid, s); break;
         PA(5) PA(6) PA(7) PA(8) PA(9) PA(10)
 #undef PA
         default: return hipErrorInvalidValue;
