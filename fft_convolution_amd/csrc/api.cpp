@@ -1515,6 +1515,13 @@ int fft_exec_planar(const fft_plan* plan, int dir, const void* in_re, const void
     return sync_if_asked(s, "fft_exec_planar (FFTMI_SYNC)");
 }
 
+// Poly-mul plans whose N is not a power of two: the plan's own transforms
+// between element-wise pack, product and rounding kernels.
+static bool poly_any_route(const fft_plan* p)
+{
+    return p->path == PATH_BLUESTEIN || p->path == PATH_MIXED || p->path == PATH_MIXPASS;
+}
+
 int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
 {
     if (!plan || !bytes) return fail(FFT_ERR_INVALID_ARG, "plan or bytes is NULL");
@@ -1522,9 +1529,12 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (plan->rank != 1 || plan->path == PATH_REAL) return fail(FFT_ERR_RANK, "poly-mul needs a complex rank-1 plan");
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
-    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED || plan->path == PATH_MIXPASS)
-        return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
-    if (plan->logn > kPolyMaxLog) return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
+    if (plan->n > (int64_t(1) << kPolyMaxLog))
+        return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
+    if (poly_any_route(plan)) {  // [z: batch x N complex128][the plan's own workspace]
+        *bytes = (size_t)batch * (size_t)plan->n * plan->elem + c2c_workspace(plan, batch);
+        return FFT_OK;
+    }
     *bytes = plan->path == PATH_MULTIPASS ? (size_t)batch * (size_t)plan->n * plan->elem : 0;
     return FFT_OK;
 }
@@ -1537,9 +1547,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
     if (plan->prec != FFT_C64) return fail(FFT_ERR_PRECISION, "poly-mul needs an FFT_C64 plan");
     if (batch < 0) return fail(FFT_ERR_INVALID_ARG, "batch < 0");
     if (la < 1 || lb < 1) return fail(FFT_ERR_INVALID_ARG, "la and lb must be >= 1");
-    if (plan->path == PATH_BLUESTEIN || plan->path == PATH_MIXED || plan->path == PATH_MIXPASS)
-        return fail(FFT_ERR_NOT_POW2, "poly-mul needs a power-of-two plan");
-    if (plan->logn > kPolyMaxLog)
+    if (plan->n > (int64_t(1) << kPolyMaxLog))
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
     if (la > plan->n || lb > plan->n || la + lb - 1 > plan->n)
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "la + lb - 1 = %lld exceeds the plan's N = %lld",
@@ -1571,9 +1579,25 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    // the four-step route clears the residual in its first kernel
-    if (d_max_residual && plan->path != PATH_MULTIPASS) e = launch_zero_resid(d_max_residual, s);
-    if (e == hipSuccess) {
+    if (poly_any_route(plan)) {
+        void* z = workspace;
+        void* tws = (char*)workspace + (size_t)batch * (size_t)plan->n * plan->elem;
+        const Io zio{z, nullptr, z, nullptr};
+        if (d_max_residual) e = launch_zero_resid(d_max_residual, s);
+        if (e == hipSuccess) e = launch_polyany_pack(a, la, b, lb, z, plan->n, batch, s);
+        if (e != hipSuccess) return hip_fail(e, "fft_poly_mul launch");
+        st = run_1d(plan, false, zio, batch, tws, s);
+        if (st != FFT_OK) return st;
+        e = launch_polyany_product(z, plan->n, batch, s);
+        if (e != hipSuccess) return hip_fail(e, "fft_poly_mul launch");
+        st = run_1d(plan, true, zio, batch, tws, s);
+        if (st != FFT_OK) return st;
+        e = launch_polyany_round(z, plan->n, c, lc, batch, d_max_residual, s);
+    } else if (d_max_residual && plan->path != PATH_MULTIPASS) {
+        // (the four-step route clears the residual in its first kernel)
+        e = launch_zero_resid(d_max_residual, s);
+    }
+    if (e == hipSuccess && !poly_any_route(plan)) {
         if (plan->path == PATH_MULTIPASS) {
             const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
             e = launch_polymul_fourstep(plan->log_a, plan->log_b, a, la, b, lb, c, batch, workspace, plan->tw_a,

@@ -155,6 +155,16 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
                                    void* ws, const void* tw_row, const void* tw_col, const void* tw_half,
                                    BigTwiddle big, double* d_resid, hipStream_t stream);
 
+// Polynomial products by a plan whose N is not a power of two: z = a + i b
+// zero padded to N (complex128, batch x N) -> the plan's forward transform ->
+// the product spectrum in place -> the plan's inverse -> rint(Re) and the
+// residual (raised; the caller clears it first).
+hipError_t launch_polyany_pack(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* z, int64_t n,
+                               int64_t batch, hipStream_t stream);
+hipError_t launch_polyany_product(void* z, int64_t n, int64_t batch, hipStream_t stream);
+hipError_t launch_polyany_round(const void* y, int64_t n, int64_t* c, int64_t lc, int64_t batch, double* d_resid,
+                                hipStream_t stream);
+
 // The whole Bluestein transform of each row in one kernel, M = 2^logm within
 // the row kernel's range (logm <= 13 complex64, 12 complex128); tw: stage
 // table for M.  Inverse: conjugate in, conjugate and scale out.  Planar needs

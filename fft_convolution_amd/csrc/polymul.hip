@@ -462,6 +462,84 @@ void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_
 }
 
 // ---------------------------------------------------------------------------
+// Plans whose length N is not a power of two: the plan's own transforms (mixed
+// radix or chirp-z, complex128) run between three element-wise kernels --
+//   pack:    z = a + i b, zero padded to N;
+//   product: Z -> C, C_k = A_k B_k = (Z_k^2 - conj(Z_{-k})^2) / (4i), in place
+//            (one thread per pair k, N - k);
+//   round:   c = rint(Re y) of the inverse transform y (scaled 1/N), with the
+//            residual.
+// ---------------------------------------------------------------------------
+static inline dim3 pm_grid(int64_t total)
+{
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > (1 << 20)) blocks = 1 << 20;  // grid-stride beyond this
+    return dim3((unsigned)(blocks > 0 ? blocks : 1));
+}
+
+__global__ void polyany_pack_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b,
+                                    int64_t lb, double2* __restrict__ z, int64_t n, int64_t total)
+{
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = e / n, k = e - p * n;
+        z[e] = double2{k < la ? (double)a[p * la + k] : 0.0, k < lb ? (double)b[p * lb + k] : 0.0};
+    }
+}
+
+__global__ void polyany_product_kernel(double2* __restrict__ z, int64_t n, int64_t total)
+{
+    const int64_t h = n / 2 + 1;  // pairs (k, N - k) per signal, k = 0 .. N/2
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = e / h, k = e - p * h, q = k == 0 ? 0 : n - k;
+        double2* row = z + p * n;
+        const double2 zk = row[k], zq = row[q];
+        // s = Z_k^2 - conj(Z_q)^2, C_k = s / (4i) = (s.y / 4, -s.x / 4); the
+        // partner's C_q the same with k and q swapped
+        const double skx = (zk.x * zk.x - zk.y * zk.y) - (zq.x * zq.x - zq.y * zq.y);
+        const double sky = 2.0 * zk.x * zk.y + 2.0 * zq.x * zq.y;
+        row[k] = double2{0.25 * sky, -0.25 * skx};
+        if (q != k) row[q] = double2{0.25 * sky, 0.25 * skx};
+    }
+}
+
+__global__ void polyany_round_kernel(const double2* __restrict__ y, int64_t n, int64_t* __restrict__ c, int64_t lc,
+                                     int64_t total, double* __restrict__ d_resid)
+{
+    double worst = 0.0;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = e / lc, k = e - p * lc;
+        const double val = y[p * n + k].x, r = rint(val);
+        c[e] = to_int64(r);
+        worst = fmax(worst, out_residual(val, r));
+    }
+    resid_max(worst, d_resid);
+}
+
+hipError_t launch_polyany_pack(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* z, int64_t n,
+                               int64_t batch, hipStream_t s)
+{
+    const int64_t total = batch * n;
+    hipLaunchKernelGGL(polyany_pack_kernel, pm_grid(total), dim3(256), 0, s, a, la, b, lb, (double2*)z, n, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_polyany_product(void* z, int64_t n, int64_t batch, hipStream_t s)
+{
+    const int64_t total = batch * (n / 2 + 1);
+    hipLaunchKernelGGL(polyany_product_kernel, pm_grid(total), dim3(256), 0, s, (double2*)z, n, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_polyany_round(const void* y, int64_t n, int64_t* c, int64_t lc, int64_t batch, double* d_resid,
+                                hipStream_t s)
+{
+    const int64_t total = batch * lc;
+    hipLaunchKernelGGL(polyany_round_kernel, pm_grid(total), dim3(256), 0, s, (const double2*)y, n, c, lc, total,
+                       d_resid);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_zero_resid(double* d, hipStream_t s)

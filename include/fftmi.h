@@ -58,7 +58,7 @@ enum fft_direction { FFT_FORWARD = 0, FFT_INVERSE = 1 };
 enum fft_status {
     FFT_OK = 0,
     FFT_ERR_INVALID_ARG = -1,      /* NULL pointer, batch < 0, bad rank/dir/prec value */
-    FFT_ERR_NOT_POW2 = -2,         /* the length of a poly-mul plan is not a power of two */
+    FFT_ERR_NOT_POW2 = -2,         /* a length is not a power of two (no call returns it now) */
     FFT_ERR_UNSUPPORTED_SIZE = -3, /* a dimension outside the supported range, or
                                       la + lb - 1 > N for fft_poly_mul */
     FFT_ERR_PRECISION = -4,        /* operation needs another precision (poly-mul: FFT_C64) */
@@ -266,8 +266,13 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
  * computed as: zero-pad a and b to N, forward FFT of both (fp64), pointwise
  * product, inverse FFT (scaled 1/N), round the real part to the nearest
  * integer (ties to even).
- *   plan:  rank 1, FFT_C64, N a power of two (else FFT_ERR_NOT_POW2) with
- *          N >= la + lb - 1.
+ *   plan:  rank 1, FFT_C64, N >= la + lb - 1, N <= 2^22.  N a power of two:
+ *          the fused kernels (one per row pair within the LDS, else three
+ *          four-step passes).  Any other N: the plan's own transforms (mixed
+ *          radix or chirp-z, "FFT on GPU", section "Algorithm per signal
+ *          Length") between three element-wise kernels -- z = a + i b zero
+ *          padded to N, the forward transform, the product spectrum
+ *          (Z_k^2 - conj(Z_{-k})^2) / 4i in place, the inverse, rint.
  *   a:     [batch][la] int64;  b: [batch][lb] int64;  c: [batch][la+lb-1] int64.
  *          c must not overlap a, b or the workspace.
  *   workspace: fft_poly_mul_workspace_size(plan, batch) bytes.
@@ -279,8 +284,8 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
  *          vouched for.  The result is exact when this stays well below 0.5;
  *          callers with large coefficients should check it.  Outputs beyond
  *          the int64 range (or not finite) are stored as INT64_MIN.
- * Errors: INVALID_ARG, RANK, PRECISION, NOT_POW2, UNSUPPORTED_SIZE, ALIGN,
- *         OVERLAP, WORKSPACE, DEVICE.
+ * Errors: INVALID_ARG, RANK, PRECISION, UNSUPPORTED_SIZE, ALIGN, OVERLAP,
+ *         WORKSPACE, DEVICE.
  */
 int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64_t* b,
                  int64_t lb, int64_t* c, int64_t batch, void* workspace,

@@ -64,9 +64,15 @@ def test_bluestein_in_place_and_poly_mul_rejected(dev):
     plan.fft(z, out=z)
     torch.cuda.synchronize()
     assert torch.equal(y, z)
+    # a poly-mul plan of a length that is not a power of two runs the plan's
+    # own transforms: (1 + z + ... + z^399)^2 has coefficients min(k + 1, 799 - k)
     p64 = fm.Plan(1000, torch.complex128)
     a = torch.ones(1, 400, dtype=torch.int64, device=dev)
     c = torch.empty(1, 799, dtype=torch.int64, device=dev)
     with pytest.raises(fm.FFTError) as e:
-        fm.fft_poly_mul(p64.handle, a, 400, a, 400, c, 1)
-    assert e.value.status == fm.FFT_ERR_NOT_POW2
+        fm.fft_poly_mul(p64.handle, a, 400, a, 400, c, 1)  # no workspace
+    assert e.value.status == fm.FFT_ERR_WORKSPACE
+    ws = torch.empty(fm.fft_poly_mul_workspace_size(p64.handle, 1), dtype=torch.uint8, device=dev)
+    fm.fft_poly_mul(p64.handle, a, 400, a, 400, c, 1, ws)
+    k = np.arange(799)
+    assert np.array_equal(c.cpu().numpy()[0], np.minimum(k + 1, 799 - k))

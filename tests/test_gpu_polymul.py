@@ -179,3 +179,38 @@ def test_residual_flags_results_past_2p53(dev, n):
     torch.cuda.synchronize()
     assert int(c3[0, 0]) == -(1 << 63)
     assert math.isinf(float(resid))
+
+# Plans whose N is not a power of two: the plan's own transforms (mixed radix
+# in one kernel or in passes, chirp-z fused or in passes) between the
+# element-wise pack, product and rounding kernels.  Bit-exact against the
+# oracle's FFT route (at the next power of two) and the schoolbook product.
+@pytest.mark.parametrize("la,lb,n,batch", [
+    (1, 1, 3, 2),               # smallest odd N: bins 1 and 2 pair
+    (7, 6, 12, 2),              # even N: bin N/2 pairs with itself
+    (500, 501, 1000, 3),        # mixed radix, one kernel
+    (600, 409, 1009, 2),        # prime: chirp-z, one kernel (M = 2048)
+    (6000, 6289, 12288, 2),     # mixed-radix passes (beyond 4096 complex128 points)
+    (3000, 2004, 5003, 1),      # prime: chirp-z passes (M = 16384)
+    (1, 200003, 200003, 1),     # a = constant, b fills N
+    (100000, 100001, 200003, 1),  # prime N of 2 x 10^5: chirp-z passes, M = 2^19
+])
+def test_any_length_plan(dev, la, lb, n, batch):
+    print("case la=%d lb=%d n=%d batch=%d" % (la, lb, n, batch), flush=True)
+    rng = np.random.default_rng(la + 7 * lb + n)
+    a = rng.integers(-1000, 1000, size=(batch, la))
+    b = rng.integers(-1000, 1000, size=(batch, lb))
+    plan = fm.Plan(n, torch.complex128)
+    assert any(k in plan.describe() for k in ("path=mixed", "path=mixpass", "path=bluestein")), plan.describe()
+    ws = fm.fft_poly_mul_workspace_size(plan.handle, batch)
+    assert ws >= batch * n * 16
+    c, resid = _gpu_mul(a, b, n, dev)
+    oracle.set_threads(8)
+    ref, _ = oracle.polymul_fft(a, b)
+    assert np.array_equal(c, ref)
+    if la * lb <= 4 * 10 ** 7:
+        assert np.array_equal(c, oracle.schoolbook(a, b))
+    else:
+        ks = np.unique(np.concatenate([[0, 1, la + lb - 2], rng.integers(0, la + lb - 1, 30)]))
+        assert np.array_equal(c[:, ks], oracle.schoolbook_sample(a, b, ks))
+    assert 0.0 <= resid < 0.1
+
