@@ -302,8 +302,10 @@ class Plan:
         self.handle = fft_plan_create(self.rank, self.dims, self.prec)
         self._lib = lib()  # the library that made the handle, which frees it
 
-    def __del__(self):
-        _release(self)
+    # the finalizer is bound at class creation: at interpreter exit the
+    # module's globals may already be gone when a plan is collected
+    def __del__(self, _free=_release):
+        _free(self)
 
     def describe(self) -> str:
         return fft_plan_describe(self.handle)
@@ -441,8 +443,10 @@ class RealPlan:
             raise ValueError("real plans have one or two dims")
         self._lib = lib()  # the library that made the handle, which frees it
 
-    def __del__(self):
-        _release(self)
+    # the finalizer is bound at class creation: at interpreter exit the
+    # module's globals may already be gone when a plan is collected
+    def __del__(self, _free=_release):
+        _free(self)
 
     def describe(self) -> str:
         return fft_plan_describe(self.handle)
