@@ -17,7 +17,10 @@ Prints ONE JSON line with:
              scaled by a copy kernel of known size), read from profiles/ and
              null once the kernel sources have changed
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same rows, with
-             the thread count and the host CPU model
+             the thread count and the host CPU model; for row workloads also
+             `parity`: the largest per-row relative RMS error of the timed
+             output's first rows against the oracle's result for them, and
+             the bound 1e-6 log2 N
   launch_us  a separate pass with a pair of events around every launch: mean /
              median / min / max of the per-launch durations
   copy_ceiling  the library's streaming copy (fft_stream_copy: every byte read
@@ -33,8 +36,8 @@ Other workloads (--workload) time the 2^24-point multi-pass transform, the
 transform the same way, and the R2C transform of 16384 real rows of 8192
 points (value = batch * 2.5 N log2 N / t, half the complex count), and rows
 of 1000 (mixed radix) and 1009 (Bluestein) points, the 2D R2C transform of
-eight real 2048 x 2048 images, and 64 rows of 10^6 points (mixed-radix
-super-stage passes, 100 x 100 x 100).
+eight real 2048 x 2048 images, and 64 rows of 10^6 points (two mixed-radix
+super-stage passes of radix 1000).
 """
 from __future__ import annotations
 
@@ -133,7 +136,8 @@ def setup_workload(name, dev, fm, torch, sets=1):
         info = dict(n=n, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=2 * x0.numel() * 8,
                     plan=desc, kernels=kernels, sample_rows=lambda rows: x_np[:rows],
                     oracle_fn="fft" if pow2 else ("dft" if n <= 16384 else "dft_bins"),
-                    oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))
+                    oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs),
+                    out_rows=lambda rows: bufs[0][1][:rows].cpu().numpy())
         return step, info
     if name.startswith("c2cpl_n"):
         # split planes: re and im of the same seeded complex rows
@@ -152,7 +156,8 @@ def setup_workload(name, dev, fm, torch, sets=1):
             fm.fft_exec_planar(plan.handle, fm.FFT_FORWARD, xr, xi, yr, yi, batch, ws, stream)
         info = dict(n=n, batch=batch, dtype="f32", flops=batch * 5.0 * n * math.log2(n), bytes=4 * re0.numel() * 4,
                     plan=plan.describe() + " layout=planar", kernels=1, sample_rows=lambda rows: x_np[:rows],
-                    oracle_fn="fft", oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs))
+                    oracle_fn="fft", oracle_unit=5.0 * n * math.log2(n), keep=(plan, bufs),
+                    out_rows=lambda rows: bufs[0][2][:rows].cpu().numpy() + 1j * bufs[0][3][:rows].cpu().numpy())
         return step, info
     if name.startswith("c2c2d") or name.startswith("c2c3d"):
         three = name.startswith("c2c3d")
@@ -239,6 +244,7 @@ def cpu_baseline(name, info, budget_s):
     import oracle
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
+    parity = None
     if name.startswith("polymul"):
         total = info["batch"]
         a, b = info["sample_pairs"](1)
@@ -298,13 +304,24 @@ def cpu_baseline(name, info, budget_s):
         reps, dt = 0, 0.0
         while reps == 0 or dt < budget_s:
             t0 = time.perf_counter()
-            fn(x)
+            ref = fn(x)
             dt += time.perf_counter() - t0
             reps += 1
         units = rows * reps
         sample = "first %d of %d rows, transformed %d time(s)" % (rows, total, reps)
-    return {"value": units * info["oracle_unit"] / dt / 1e9, "unit": "GFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3), "cpu": cpu_model()}
+        if "out_rows" in info:
+            # the timed output's rows against the oracle's, which this leg has
+            # just computed: the largest per-row relative RMS error
+            k = min(rows, 256)
+            y = np.asarray(info["out_rows"](k), dtype=np.complex128)
+            r = np.asarray(ref[:k], dtype=np.complex128)
+            err = np.sqrt(np.sum(np.abs(y - r) ** 2, axis=1) / np.sum(np.abs(r) ** 2, axis=1))
+            parity = {"rows": k, "max_rel_rms": float(err.max()), "bound": 1e-6 * math.log2(info["n"])}
+    out = {"value": units * info["oracle_unit"] / dt / 1e9, "unit": "GFLOP/s", "cores": threads,
+           "kind": "oracle", "sample": sample, "seconds": round(dt, 3), "cpu": cpu_model()}
+    if parity is not None:
+        out["parity"] = parity
+    return out
 
 
 def cpu_model() -> str:
@@ -443,6 +460,8 @@ def main():
                          "frac_of_copy": round((info["bytes"] / ms) / (2 * copy_bytes / copy_ms), 4)},
         "rotated": rotated,
         "gpu": torch.cuda.get_device_name(dev),
+        "gpu_arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+        "hip": torch.version.hip,
     }
     if info["kernels"] == 1:
         # One kernel per step: algorithmic bytes (input read once + output

@@ -48,7 +48,7 @@ WORKLOADS = {
     "c2c_n1009_b65536": dict(kind="normal", n=1009, batch=65536, seed=9),
     # real 2048 x 2048 images, the 2D R2C transform
     "r2c2d_2048x2048_b8": dict(kind="real_images", h=2048, w=2048, batch=8, seed=10),
-    # 10^6 = 100 x 100 x 100: three mixed-radix super-stage passes (~500 MiB in)
+    # 10^6 = 1000 x 1000: two mixed-radix super-stage passes (~500 MiB in)
     "c2c_n1000000_b64": dict(kind="normal", n=10 ** 6, batch=64, seed=11),
     # the 4096 x 16384 transform on split re / im planes (the [2][N] signal
     # layout): 256 MiB per plane each way
