@@ -321,6 +321,9 @@ struct fft_plan {
     // rank 1, any N (Bluestein): chirp c_j (N entries), B = F_M(b) (M entries),
     // the power-of-two plan of length M = 2^logm it runs on.
     int logm = 0;
+    // set before the layout is chosen: a power-of-two plan beyond the LDS range
+    // stays in super-stage passes (the chirp-z passes read its pass layout)
+    bool passes_only = false;
     // mixed radix: the stage schedule; tw_a = its twiddle table
     MixedSchedule mixed{};
     // real rows of N = 2H points: inner = the complex plan of length H,
@@ -361,6 +364,9 @@ struct fft_plan {
     bool real_nd = false;
     size_t elem = 8;
 };
+
+// plan creation with the layout choice open to the library's own sub-plans
+static int plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec, bool passes_only);
 
 namespace {
 
@@ -576,6 +582,9 @@ size_t nd_workspace(const fft_plan* p, int64_t batch, bool in_place)
 // 189 us against 209 us with 1024-point columns and 207 us with 256-point ones.
 constexpr int kMaxPassLog = 9;
 constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
+// complex64 rows of 2^14 points still run as one kernel: one 1024-thread
+// workgroup holds a row in LDS (128 KiB + pad) -- rank-1 plans only
+constexpr int64_t kBigRowN = int64_t(1) << 14;
 constexpr int64_t kBluesteinMax = FFT_MAX_BLUESTEIN_N;  // largest length that is not a power of two
 int col_pref_log(int) { return 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
@@ -649,7 +658,7 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
             }
         } else if (n == 1) {
             p->path = PATH_COPY;
-        } else if (n <= max_lds_n(prec)) {
+        } else if (n <= max_lds_n(prec) || (n == kBigRowN && prec == FFT_C32 && !p->passes_only)) {
             p->path = PATH_ROWS;
             p->log_a = p->logn;
         } else {
@@ -761,7 +770,7 @@ int bluestein_tables(fft_plan* p)
     if (st != FFT_OK) return st;
     fft_plan* sub = nullptr;
     const int64_t mdim = m;
-    st = fft_plan_create(&sub, 1, &mdim, FFT_C64);
+    st = plan_create(&sub, 1, &mdim, FFT_C64, false);
     void* ws = nullptr;
     const size_t wsb = st == FFT_OK ? c2c_workspace(sub, 1) : 0;
     if (st == FFT_OK && wsb) {
@@ -789,7 +798,8 @@ int bluestein_tables(fft_plan* p)
     if (ws) (void)hipFree(ws);
     if (bdev) (void)hipFree(bdev);
     if (sub) fft_plan_destroy(sub);
-    if (st == FFT_OK) st = fft_plan_create(&p->inner, 1, &mdim, p->prec);
+    // beyond one workgroup the chirp-z route runs on the M-point passes
+    if (st == FFT_OK) st = plan_create(&p->inner, 1, &mdim, p->prec, m > max_lds_n(p->prec));
     return st;
 }
 
@@ -952,10 +962,16 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
 
 int fft_plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec)
 {
+    return plan_create(out_plan, rank, dims, prec, false);
+}
+
+static int plan_create(fft_plan** out_plan, int rank, const int64_t* dims, int prec, bool passes_only)
+{
     if (!out_plan) return fail(FFT_ERR_INVALID_ARG, "plan pointer is NULL");
     *out_plan = nullptr;
     fft_plan* p = new (std::nothrow) fft_plan;
     if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");
+    p->passes_only = passes_only;
     // 1. Layout, on the host only.
     int st = plan_prepare(p, rank, dims, prec);
     if (st != FFT_OK) {

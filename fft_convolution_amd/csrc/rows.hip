@@ -130,6 +130,9 @@ hipError_t launch_rows(int prec, int logn, bool ci, bool co, const void* in, voi
         case 13:
             if (prec == 0) return launch_rows_dir<float2, 13>(ci, co, io, nrows, tw, scale, s);
             return hipErrorInvalidValue;
+        case 14:  // one 1024-thread workgroup per row, 136 KiB of LDS
+            if (prec == 0) return launch_rows_dir<float2, 14>(ci, co, io, nrows, tw, scale, s);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 #undef FFTMI_ROW_CASE

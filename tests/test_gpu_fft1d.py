@@ -29,7 +29,7 @@ def _case(n, batch, dtype, seed):
     return wl.batched_uniform(n, batch, seed, dtype=dtype)
 
 
-@pytest.mark.parametrize("logn", list(range(0, 14)))
+@pytest.mark.parametrize("logn", list(range(0, 15)))  # to 16384: one 1024-thread workgroup a row
 @pytest.mark.parametrize("batch", [1, 3, 67])
 def test_c2c_c64_sweep(dev, logn, batch):
     n = 1 << logn
@@ -55,8 +55,9 @@ def test_c2c_c128_sweep(dev, logn, batch):
 
 
 # every multi-pass size below the largest (2^26, test_gpu_max_sizes): each
-# has its own split into super-stages (2 passes up to 2^18, 3 beyond)
-@pytest.mark.parametrize("logn,batch", [(14, 2), (15, 3), (16, 1), (17, 2), (18, 2), (19, 1), (20, 1), (21, 1),
+# has its own split into super-stages (2 passes up to 2^18, 3 beyond); the
+# 2^14-point passes run under the chirp-z route (test_gpu_bluestein)
+@pytest.mark.parametrize("logn,batch", [(15, 3), (16, 1), (17, 2), (18, 2), (19, 1), (20, 1), (21, 1),
                                         (22, 1), (23, 1), (25, 1)])
 def test_c2c_c64_multipass(dev, logn, batch):
     n = 1 << logn

@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 
 def _cases():
     c = []
-    for logn in range(1, 14):
+    for logn in range(1, 15):  # up to 16384 points: one 1024-thread workgroup a row
         c.append(("c2c", (1 << logn,), torch.complex64, 5))
     for logn in range(1, 13):
         c.append(("c2c", (1 << logn,), torch.complex128, 3))

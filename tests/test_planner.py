@@ -37,8 +37,11 @@ def test_power_of_two_paths(prec):
         d = _q(1, [n], prec)
         if n == 1:
             assert "path=copy" in d
-        elif n <= LDS_MAX[prec]:
-            assert "path=rows" in d
+        elif n <= LDS_MAX[prec] or (prec == 0 and n == 2 * LDS_MAX[0]):
+            # complex64 rows of 16384 points: one 1024-thread workgroup a row
+            assert "path=rows" in d, d
+            if n == 2 * LDS_MAX[0] and prec == 0:
+                assert "stages=4" in d, d
         else:
             assert "path=multipass" in d
             r = [int(x) for x in _field(d, "radices").split("x")]
