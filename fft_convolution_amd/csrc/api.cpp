@@ -582,9 +582,11 @@ size_t nd_workspace(const fft_plan* p, int64_t batch, bool in_place)
 // 189 us against 209 us with 1024-point columns and 207 us with 256-point ones.
 constexpr int kMaxPassLog = 9;
 constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
-// complex64 rows of 2^14 points still run as one kernel: one 1024-thread
-// workgroup holds a row in LDS (128 KiB + pad) -- rank-1 plans only
-constexpr int64_t kBigRowN = int64_t(1) << 14;
+constexpr int kPolyRowsMaxLog = 12;  // the fused poly-mul row kernel: N <= 4096
+// Rows of twice the LDS range (2^14 complex64 / 2^13 complex128 points) still
+// run as one kernel: one 1024-thread workgroup holds a row in LDS (128 KiB +
+// pad) -- rank-1 plans only
+int64_t big_row_n(int prec) { return prec == FFT_C32 ? int64_t(1) << 14 : int64_t(1) << 13; }
 constexpr int64_t kBluesteinMax = FFT_MAX_BLUESTEIN_N;  // largest length that is not a power of two
 int col_pref_log(int) { return 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
@@ -658,7 +660,7 @@ int plan_layout(fft_plan* p, int rank, const int64_t* dims, int prec)
             }
         } else if (n == 1) {
             p->path = PATH_COPY;
-        } else if (n <= max_lds_n(prec) || (n == kBigRowN && prec == FFT_C32 && !p->passes_only)) {
+        } else if (n <= max_lds_n(prec) || (n == big_row_n(prec) && !p->passes_only)) {
             p->path = PATH_ROWS;
             p->log_a = p->logn;
         } else {
@@ -1531,11 +1533,16 @@ int fft_exec_planar(const fft_plan* plan, int dir, const void* in_re, const void
     return sync_if_asked(s, "fft_exec_planar (FFTMI_SYNC)");
 }
 
-// Poly-mul plans whose N is not a power of two: the plan's own transforms
-// between element-wise pack, product and rounding kernels.
+// Poly-mul plans whose N is not a power of two, and power-of-two plans whose
+// rows are too long for the fused poly-mul row kernel but still one kernel:
+// the plan's own transforms between element-wise pack, product and rounding
+// kernels.
 static bool poly_any_route(const fft_plan* p)
 {
-    return p->path == PATH_BLUESTEIN || p->path == PATH_MIXED || p->path == PATH_MIXPASS;
+    // (8192-point complex128 rows run as one kernel of their own, beyond the
+    // fused poly-mul row kernel's 4096)
+    return p->path == PATH_BLUESTEIN || p->path == PATH_MIXED || p->path == PATH_MIXPASS ||
+           (p->path == PATH_ROWS && p->log_a > kPolyRowsMaxLog);
 }
 
 int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)

@@ -122,14 +122,14 @@ hipError_t launch_rows(int prec, int logn, bool ci, bool co, const void* in, voi
 #define FFTMI_ROW_CASE(L) \
     case L: return prec == 0 ? launch_rows_dir<float2, L>(ci, co, io, nrows, tw, scale, s) \
                              : launch_rows_dir<double2, L>(ci, co, io, nrows, tw, scale, s);
-    if (prec == 1 && logn > 12) return hipErrorInvalidValue;
+    if (prec == 1 && logn > 13) return hipErrorInvalidValue;
     switch (logn) {
         FFTMI_ROW_CASE(1) FFTMI_ROW_CASE(2) FFTMI_ROW_CASE(3) FFTMI_ROW_CASE(4)
         FFTMI_ROW_CASE(5) FFTMI_ROW_CASE(6) FFTMI_ROW_CASE(7) FFTMI_ROW_CASE(8)
         FFTMI_ROW_CASE(9) FFTMI_ROW_CASE(10) FFTMI_ROW_CASE(11) FFTMI_ROW_CASE(12)
-        case 13:
-            if (prec == 0) return launch_rows_dir<float2, 13>(ci, co, io, nrows, tw, scale, s);
-            return hipErrorInvalidValue;
+        case 13:  // complex128: one 1024-thread workgroup per row, 144 KiB of LDS
+            return prec == 0 ? launch_rows_dir<float2, 13>(ci, co, io, nrows, tw, scale, s)
+                             : launch_rows_dir<double2, 13>(ci, co, io, nrows, tw, scale, s);
         case 14:  // one 1024-thread workgroup per row, 136 KiB of LDS
             if (prec == 0) return launch_rows_dir<float2, 14>(ci, co, io, nrows, tw, scale, s);
             return hipErrorInvalidValue;

@@ -81,9 +81,9 @@ enum fft_status {
  * Create a plan.
  *   rank 1: dims = {N};      1 <= N <= FFT_MAX_N_C32 (C32) / FFT_MAX_N_C64 (C64).
  *           N <= FFT_MAX_LDS_N_* runs as one LDS-resident kernel per batch of
- *           rows, and so does N = 2 FFT_MAX_LDS_N_C32 = 16384 for C32 (one
- *           1024-thread workgroup a row, 136 KiB of LDS); larger N runs as
- *           two or three Stockham super-stage passes (radix <= 512 each)
+ *           rows, and so does N = 2 FFT_MAX_LDS_N_* (16384 C32, 8192 C64: one
+ *           1024-thread workgroup a row, 136 / 144 KiB of LDS); larger N runs
+ *           as two or three Stockham super-stage passes (radix <= 512 each)
  *           through HBM and needs a workspace of one batch of signals.
  *           N not a power of two (N <= FFT_MAX_BLUESTEIN_N), the two routes
  *           "FFT on GPU" (section "Algorithm per signal Length") names for

@@ -31,7 +31,7 @@ def _cases():
     c = []
     for logn in range(1, 15):  # up to 16384 points: one 1024-thread workgroup a row
         c.append(("c2c", (1 << logn,), torch.complex64, 5))
-    for logn in range(1, 13):
+    for logn in range(1, 14):
         c.append(("c2c", (1 << logn,), torch.complex128, 3))
     c += [("c2c", (1 << 16,), torch.complex64, 2), ("c2c", (1 << 20,), torch.complex64, 1),
           ("c2c", (1 << 16,), torch.complex128, 1), ("c2c", (1009,), torch.complex64, 3),

@@ -46,7 +46,8 @@ def test_small_exact(dev, la, lb, batch):
 
 @pytest.mark.parametrize("la,lb,n,batch", [
     (3000, 1097, 4096, 2),     # LDS-resident, largest fp64 row
-    (4096, 4097, 8192, 2),     # smallest four-step
+    (4096, 4097, 8192, 2),     # 8192-point rows in one kernel, the general route
+    (8192, 8193, 16384, 2),    # smallest four-step
     (5000, 3000, 16384, 3),    # four-step, ragged lengths
     (1 << 15, 1 << 15, 1 << 16, 2),
     (10, 20, 1 << 16, 1),      # mostly zero padding

@@ -37,11 +37,10 @@ def test_power_of_two_paths(prec):
         d = _q(1, [n], prec)
         if n == 1:
             assert "path=copy" in d
-        elif n <= LDS_MAX[prec] or (prec == 0 and n == 2 * LDS_MAX[0]):
-            # complex64 rows of 16384 points: one 1024-thread workgroup a row
+        elif n <= 2 * LDS_MAX[prec]:
+            # rows of twice the LDS range (16384 complex64, 8192 complex128):
+            # one 1024-thread workgroup a row
             assert "path=rows" in d, d
-            if n == 2 * LDS_MAX[0] and prec == 0:
-                assert "stages=4" in d, d
         else:
             assert "path=multipass" in d
             r = [int(x) for x in _field(d, "radices").split("x")]
@@ -181,9 +180,11 @@ def test_transposed_axes_planned():
 
 
 def test_poly_mul_split_described():
-    """complex128 plans beyond the LDS range carry the poly-mul split N1 x N2
-    (columns of at most 512 points, 1024 beyond 2^21; rows of at most 4096)."""
-    for logn, n1, n2 in [(13, 64, 128), (17, 256, 512), (19, 1024, 512), (20, 2048, 512), (21, 4096, 512),
+    """complex128 plans in passes carry the poly-mul split N1 x N2 (columns of
+    at most 512 points, 1024 beyond 2^21; rows of at most 4096); 8192 points
+    run as one kernel and carry none."""
+    assert "poly=" not in _q(1, [1 << 13], 1)
+    for logn, n1, n2 in [(14, 128, 128), (17, 256, 512), (19, 1024, 512), (20, 2048, 512), (21, 4096, 512),
                          (22, 4096, 1024)]:
         d = _q(1, [1 << logn], 1)
         assert _field(d, "poly") == "%dx%d" % (n1, n2), d
