@@ -373,6 +373,12 @@ namespace {
 size_t elem_bytes(int prec) { return prec == FFT_C32 ? 8 : 16; }
 
 int64_t max_lds_n(int prec) { return prec == FFT_C32 ? FFT_MAX_LDS_N_C32 : FFT_MAX_LDS_N_C64; }
+// Rows of twice the LDS range (2^14 complex64 / 2^13 complex128 points) still
+// run as one kernel: one 1024-thread workgroup holds a row in LDS (128 KiB +
+// pad) -- rank-1 plans and the chirp-z rows only
+int64_t big_row_n(int prec) { return prec == FFT_C32 ? int64_t(1) << 14 : int64_t(1) << 13; }
+// the chirp-z route in one kernel per row (else on the M-point passes)
+bool bluestein_fused(const fft_plan* p) { return (int64_t(1) << p->logm) <= big_row_n(p->prec); }
 int64_t max_n(int prec) { return prec == FFT_C32 ? FFT_MAX_N_C32 : FFT_MAX_N_C64; }
 
 // Upload interleaved fp64 values rounded to the plan precision.
@@ -541,7 +547,7 @@ size_t c2c_workspace(const fft_plan* p, int64_t batch)
 {
     if (p->path == PATH_NDX) return ndx_workspace(p, batch, false);
     if (p->path == PATH_BLUESTEIN)  // none when M is within one workgroup (one kernel)
-        return (int64_t(1) << p->logm) <= max_lds_n(p->prec)
+        return bluestein_fused(p)
                    ? 0
                    : ((size_t)batch << p->logm) * p->elem + c2c_workspace(p->inner, batch);
     if (p->path == PATH_REAL && p->rank == 2 && p->real_nd) {
@@ -583,10 +589,6 @@ size_t nd_workspace(const fft_plan* p, int64_t batch, bool in_place)
 constexpr int kMaxPassLog = 9;
 constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
 constexpr int kPolyRowsMaxLog = 12;  // the fused poly-mul row kernel: N <= 4096
-// Rows of twice the LDS range (2^14 complex64 / 2^13 complex128 points) still
-// run as one kernel: one 1024-thread workgroup holds a row in LDS (128 KiB +
-// pad) -- rank-1 plans only
-int64_t big_row_n(int prec) { return prec == FFT_C32 ? int64_t(1) << 14 : int64_t(1) << 13; }
 constexpr int64_t kBluesteinMax = FFT_MAX_BLUESTEIN_N;  // largest length that is not a power of two
 int col_pref_log(int) { return 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
@@ -801,7 +803,7 @@ int bluestein_tables(fft_plan* p)
     if (bdev) (void)hipFree(bdev);
     if (sub) fft_plan_destroy(sub);
     // beyond one workgroup the chirp-z route runs on the M-point passes
-    if (st == FFT_OK) st = plan_create(&p->inner, 1, &mdim, p->prec, m > max_lds_n(p->prec));
+    if (st == FFT_OK) st = plan_create(&p->inner, 1, &mdim, p->prec, !bluestein_fused(p));
     return st;
 }
 
@@ -1024,7 +1026,7 @@ int fft_plan_describe(const fft_plan* p, char* buf, size_t len)
             break;
         case PATH_BLUESTEIN:
             snprintf(buf, len, "rank=1 n=%lld prec=%s path=bluestein m=%lld %s", (long long)p->n, prec,
-                     1LL << p->logm, (int64_t(1) << p->logm) <= max_lds_n(p->prec) ? "fused" : "passes");
+                     1LL << p->logm, bluestein_fused(p) ? "fused" : "passes");
             break;
         case PATH_MIXED: {
             int off = snprintf(buf, len, "rank=1 n=%lld prec=%s path=mixed radices=", (long long)p->n, prec);
@@ -1201,7 +1203,7 @@ static int run_1d(const fft_plan* plan, bool inv, const Io& io, int64_t batch, v
         }
         case PATH_BLUESTEIN: {
             // w = pad(x . c) ; w = F^{-1}(F(w) . B) ; X = c . w  (conjugated for the inverse)
-            if ((int64_t(1) << plan->logm) <= max_lds_n(plan->prec)) {  // one kernel
+            if (bluestein_fused(plan)) {  // one kernel
                 e = launch_bluestein_rows(plan->prec, plan->logm, (int)plan->n, io.in, io.out, batch,
                                           plan->inner->tw_a, plan->chirp, plan->bspec, inv, scale, s, io.in_im,
                                           io.out_im);

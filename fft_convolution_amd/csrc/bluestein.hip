@@ -78,6 +78,7 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
     const int64_t row = (int64_t)blockIdx.x * RPW + rloc;
     const bool live = row < nrows;
     const LdsLines<V, 1, 4, bl_in_wave<V, LOGM>()> L{lds + rloc * G::LDS, 0};
+    constexpr bool BL_COMPACT = G::T * RPW >= 1024;
 
     V v[G::E];
     const int64_t base = row * n;
@@ -87,7 +88,8 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
         // Every load is issued unconditionally, from an address clamped into
         // the row (a dead row reads row 0), and the value is dropped after:
         // loads under a branch each end in a wait for memory, which would
-        // serialise the row's loads.
+        // serialise the row's loads.  1024-thread rows (registers capped at
+        // 128) keep the branches: their clamped form spills.
         const auto src = in.at((live ? row : 0) * n);
 #pragma unroll
         for (int i = 0; i < G::E; ++i) {
@@ -95,7 +97,13 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
             V x{0, 0};
             // positions from M/2 on are zero padding (n <= M/2): a
             // compile-time zero, so the first stage's x + 0 terms can go
-            if (i < G::E / 2) {
+            if constexpr (BL_COMPACT) {
+                if (i < G::E / 2 && live && p < n) {
+                    x = src.ld32((unsigned)p);
+                    if (INV) x = cconj(x);
+                    x = cmul_pinned(x, chirp[p]);
+                }
+            } else if (i < G::E / 2) {
                 const int pc = p < n ? p : n - 1;
                 V y = src.ld32((unsigned)pc);
                 if (INV) y = cconj(y);
@@ -116,6 +124,18 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
         fft_regs<LOGM>(v, t, tb, L);
     }
     const Rl inv_m = (Rl)1 / (Rl)(1 << LOGM);
+    if constexpr (BL_COMPACT) {
+        if (!live) return;
+#pragma unroll
+        for (int i = 0; i < G::E / 2; ++i) {
+            const int p = t + i * G::T;
+            if (p < n) {
+                const V y = cmul_pinned(V{v[i].x * inv_m, -v[i].y * inv_m}, chirp[p]);
+                out.st(base + p, INV ? V{y.x * scale, -y.y * scale} : y);
+            }
+        }
+        return;
+    }
     // outputs from M/2 on are never stored; the chirp factors and products
     // are formed for every position (clamped), so that only the stores sit
     // under a branch and no load waits inside one
@@ -172,17 +192,17 @@ hipError_t launch_bluestein_rows(int prec, int logm, int n, const void* in, void
     const Io io{in, in_im, out, out_im};
     if ((in_im != nullptr) != (out_im != nullptr)) return hipErrorInvalidValue;
     // the kernel takes every position from M/2 on as zero padding
-    if (n < 1 || logm < 1 || logm > 13 || 2 * (int64_t)n - 1 > (int64_t(1) << logm)) return hipErrorInvalidValue;
+    if (n < 1 || logm < 1 || logm > 14 || 2 * (int64_t)n - 1 > (int64_t(1) << logm)) return hipErrorInvalidValue;
 #define FFTMI_BL(L)                                                                                          \
     case L:                                                                                                  \
         return prec == 0 ? bluestein_rows_pl<float2, L>(io, nrows, n, tw, chirp, bspec, inverse, scale, s)   \
                          : bluestein_rows_pl<double2, L>(io, nrows, n, tw, chirp, bspec, inverse, scale, s);
-    if (prec == 1 && logm > 12) return hipErrorInvalidValue;
+    if (prec == 1 && logm > 13) return hipErrorInvalidValue;
     switch (logm) {
         FFTMI_BL(2) FFTMI_BL(3) FFTMI_BL(4) FFTMI_BL(5) FFTMI_BL(6) FFTMI_BL(7) FFTMI_BL(8) FFTMI_BL(9)
-        FFTMI_BL(10) FFTMI_BL(11) FFTMI_BL(12)
-        case 13:
-            if (prec == 0) return bluestein_rows_pl<float2, 13>(io, nrows, n, tw, chirp, bspec, inverse, scale, s);
+        FFTMI_BL(10) FFTMI_BL(11) FFTMI_BL(12) FFTMI_BL(13)
+        case 14:  // one 1024-thread workgroup a row, 136 KiB of LDS
+            if (prec == 0) return bluestein_rows_pl<float2, 14>(io, nrows, n, tw, chirp, bspec, inverse, scale, s);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }

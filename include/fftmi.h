@@ -101,9 +101,10 @@ enum fft_status {
  *             with c_j = e^{-i pi j^2/N}, the convolution done cyclically at
  *             the power-of-two M >= 2N - 1 by the library's own transforms.
  *             Plan creation then also runs one fp64 M-point transform on the
- *             device (the spectrum of the chirp).  M <= FFT_MAX_LDS_N_*: one
- *             kernel, no workspace; larger M: five passes and a workspace of
- *             batch * M elements plus that of the M-point plan.
+ *             device (the spectrum of the chirp).  M <= 2 FFT_MAX_LDS_N_*
+ *             (16384 C32, 8192 C64): one kernel, no workspace; larger M: five
+ *             passes and a workspace of batch * M elements plus that of the
+ *             M-point plan.
  *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
  *           Parallel GLSL", section "Multi-Dimensional Transforms and
  *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*.

@@ -35,7 +35,8 @@ def _cases():
         c.append(("c2c", (1 << logn,), torch.complex128, 3))
     c += [("c2c", (1 << 16,), torch.complex64, 2), ("c2c", (1 << 20,), torch.complex64, 1),
           ("c2c", (1 << 16,), torch.complex128, 1), ("c2c", (1009,), torch.complex64, 3),
-          ("c2c", (100003,), torch.complex64, 1), ("c2c", (64, 128), torch.complex64, 2),
+          ("c2c", (100003,), torch.complex64, 1), ("c2c", (5003,), torch.complex64, 1),
+          ("c2c", (4093,), torch.complex128, 1), ("c2c", (64, 128), torch.complex64, 2),
           ("c2c", (2048, 64), torch.complex64, 1), ("c2c", (8192, 2), torch.complex64, 2),
           ("c2c", (1024, 1024), torch.complex64, 1), ("c2c", (1024, 64), torch.complex128, 1),
           ("c2c", (16, 32, 64), torch.complex64, 1),
