@@ -1664,7 +1664,7 @@ int fft_plan_create_real(fft_plan** out_plan, int64_t n, int prec)
     p->dims[0] = p->n = n;
     p->logn = is_pow2(n) ? ilog2(n) : 31;  // 31: w_N lookups of any N take no index mask (k < N)
     p->log_a = is_pow2(n) && p->logn > 0 ? p->logn - 1 : 0;
-    p->real_fused = is_pow2(n) && n >= 2 && (n / 2) <= max_lds_n(prec);
+    p->real_fused = is_pow2(n) && n >= 2 && (n / 2) <= big_row_n(prec);
     p->real_odd = odd;
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) {
@@ -1762,7 +1762,7 @@ int fft_plan_create_real_2d(fft_plan** out_plan, int64_t h, int64_t w, int prec)
     *out_plan = nullptr;
     if (prec != FFT_C32 && prec != FFT_C64) return fail(FFT_ERR_INVALID_ARG, "precision %d unknown", prec);
     if (h < 1 || w < 1) return fail(FFT_ERR_INVALID_ARG, "dims %lld x %lld < 1", (long long)h, (long long)w);
-    if (!(is_pow2(h) && is_pow2(w) && h <= max_lds_n(prec) && w <= 2 * max_lds_n(prec)))
+    if (!(is_pow2(h) && is_pow2(w) && h <= max_lds_n(prec) && w <= 2 * big_row_n(prec)))
         return real_2d_any(out_plan, h, w, prec);
     fft_plan* p = new (std::nothrow) fft_plan;
     if (!p) return fail(FFT_ERR_DEVICE, "out of host memory");

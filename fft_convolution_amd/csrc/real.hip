@@ -254,13 +254,14 @@ hipError_t launch_real_rows(int prec, int logh, bool c2r, const void* in, void* 
 #define FFTMI_REAL_CASE(L) \
     case L: return prec == 0 ? launch_real_rows_t<float2, L>(c2r, in, out, nrows, tw, whi, wlo, s) \
                              : launch_real_rows_t<double2, L>(c2r, in, out, nrows, tw, whi, wlo, s);
-    if (prec == 1 && logh > 12) return hipErrorInvalidValue;
+    if (prec == 1 && logh > 13) return hipErrorInvalidValue;
     switch (logh) {
         FFTMI_REAL_CASE(0) FFTMI_REAL_CASE(1) FFTMI_REAL_CASE(2) FFTMI_REAL_CASE(3) FFTMI_REAL_CASE(4)
         FFTMI_REAL_CASE(5) FFTMI_REAL_CASE(6) FFTMI_REAL_CASE(7) FFTMI_REAL_CASE(8)
         FFTMI_REAL_CASE(9) FFTMI_REAL_CASE(10) FFTMI_REAL_CASE(11) FFTMI_REAL_CASE(12)
-        case 13:
-            if (prec == 0) return launch_real_rows_t<float2, 13>(c2r, in, out, nrows, tw, whi, wlo, s);
+        FFTMI_REAL_CASE(13)
+        case 14:  // one 1024-thread workgroup a row, 136 KiB of LDS
+            if (prec == 0) return launch_real_rows_t<float2, 14>(c2r, in, out, nrows, tw, whi, wlo, s);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }

@@ -314,7 +314,7 @@ int fft_plan_create_real(fft_plan** plan, int64_t n, int prec);
 
 /*
  * Plan for real images [H][W] -- H, W powers of two, 1 <= H <= FFT_MAX_LDS_N_*,
- * 1 <= W <= 2 FFT_MAX_LDS_N_*: the 2D transform's columns 0 .. W/2, the rest
+ * 1 <= W <= 4 FFT_MAX_LDS_N_*: the 2D transform's columns 0 .. W/2, the rest
  * following from X[u][v] = conj X[-u][-v].  The rows go through the real-row
  * kernels, then the H-point column transforms run over the W/2 + 1 columns of
  * the half spectrum (one column per lane; for H > 512 a radix-F column stage
@@ -342,7 +342,7 @@ int fft_plan_create_real_2d(fft_plan** plan, int64_t h, int64_t w, int prec);
  *              must not overlap (FFT_ERR_OVERLAP); both aligned to the complex
  *              element size (8 bytes C32, 16 bytes C64).
  *   workspace: fft_workspace_size(plan, batch) bytes: none for powers of two
- *              with N/2 <= FFT_MAX_LDS_N_* (one kernel); batch * N/2 complex
+ *              with N/2 <= 2 FFT_MAX_LDS_N_* (one kernel); batch * N/2 complex
  *              values beyond (even N; plus the N/2-point plan's own workspace
  *              where N/2 is not a power of two); batch * N complex values
  *              plus the N-point plan's workspace for odd N.

@@ -43,6 +43,7 @@ def _cases():
           ("poly", (1000,), torch.complex128, 2), ("poly", (3000,), torch.complex128, 2),
           ("poly", (40000,), torch.complex128, 2), ("poly", (1 << 19,), torch.complex128, 1),
           ("real", (1024,), torch.float32, 4), ("real", (1 << 15,), torch.float32, 2),
+          ("real", (1 << 16,), torch.float32, 1), ("real", (1 << 14,), torch.float64, 2),
           ("real", (1024, 512), torch.float32, 1), ("real", (64, 64), torch.float64, 2)]
     return c
 

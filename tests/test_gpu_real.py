@@ -16,8 +16,8 @@ from conftest import fft_tol, rel_rms_rows
 
 pytestmark = pytest.mark.gpu
 
-F32_FUSED = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14]
-F64_FUSED = [0, 1, 2, 3, 4, 5, 8, 11, 12, 13]
+F32_FUSED = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15]
+F64_FUSED = [0, 1, 2, 3, 4, 5, 8, 11, 12, 13, 14]
 
 
 def _run(logn, batch, dtype, seed):
@@ -57,13 +57,13 @@ def test_real_fused_f64(dev, logn):
     assert ("fused" in plan.describe()) == (logn >= 1)
 
 
-@pytest.mark.parametrize("logn,batch", [(15, 3), (16, 2), (18, 2), (21, 1), (24, 1)])
+@pytest.mark.parametrize("logn,batch", [(16, 3), (17, 2), (18, 2), (21, 1), (24, 1)])
 def test_real_pairs_f32(dev, logn, batch):
     plan = _run(logn, batch, np.float32, 300 + logn)
     assert "pairs" in plan.describe()
 
 
-@pytest.mark.parametrize("logn,batch", [(14, 3), (15, 2), (17, 1), (20, 1)])
+@pytest.mark.parametrize("logn,batch", [(15, 3), (16, 2), (17, 1), (20, 1)])
 def test_real_pairs_f64(dev, logn, batch):
     plan = _run(logn, batch, np.float64, 400 + logn)
     assert "pairs" in plan.describe()
@@ -137,8 +137,10 @@ def test_real_errors_and_kinds(dev):
     assert e.value.status == fm.FFT_ERR_RANK
     # batch 0 is a no-op; fused plans need no workspace
     fm.fft_exec_r2c(rp.handle, x, X, 0, None)
-    assert fm.fft_workspace_size(fm.RealPlan(1 << 14, torch.float32).handle, 5) == 0
-    assert fm.fft_workspace_size(fm.RealPlan(1 << 14, torch.float64).handle, 5) == 5 * (1 << 13) * 16
+    assert fm.fft_workspace_size(fm.RealPlan(1 << 15, torch.float32).handle, 5) == 0
+    assert fm.fft_workspace_size(fm.RealPlan(1 << 14, torch.float64).handle, 5) == 0
+    assert fm.fft_workspace_size(fm.RealPlan(1 << 16, torch.float32).handle, 5) == 5 * (1 << 15) * 8
+    assert fm.fft_workspace_size(fm.RealPlan(1 << 15, torch.float64).handle, 5) == 5 * (1 << 14) * 16
     # input untouched by both directions
     xr = torch.randn(3, 4096, device=dev)
     x0 = xr.clone()

@@ -26,6 +26,9 @@ CASES = [
     (4096, 2, torch.float64, 2), (2048, 8192, torch.float64, 1),
     # column stages of radix 8 and 16 folded into the real row pass, complex128 too
     (4096, 256, torch.float32, 2), (8192, 1024, torch.float32, 1), (2048, 256, torch.float64, 2),
+    # rows of 32768 (float32) / 16384 (float64) points: 1024-thread row kernels
+    (16, 32768, torch.float32, 1), (1024, 32768, torch.float32, 1), (8, 16384, torch.float64, 2),
+    (1024, 16384, torch.float64, 1),
 ]
 
 
