@@ -588,7 +588,7 @@ size_t nd_workspace(const fft_plan* p, int64_t batch, bool in_place)
 // 189 us against 209 us with 1024-point columns and 207 us with 256-point ones.
 constexpr int kMaxPassLog = 9;
 constexpr int kPolyMaxLog = 22;  // largest poly-mul transform, 2^22 points
-constexpr int kPolyRowsMaxLog = 12;  // the fused poly-mul row kernel: N <= 4096
+constexpr int kPolyRowsMaxLog = 13;  // the fused poly-mul row kernels: N <= 8192
 constexpr int64_t kBluesteinMax = FFT_MAX_BLUESTEIN_N;  // largest length that is not a power of two
 int col_pref_log(int) { return 9; }
 int col_cap_log(int prec) { return prec == FFT_C32 ? 11 : 10; }
@@ -1535,17 +1535,19 @@ int fft_exec_planar(const fft_plan* plan, int dir, const void* in_re, const void
     return sync_if_asked(s, "fft_exec_planar (FFTMI_SYNC)");
 }
 
-// Poly-mul plans whose N is not a power of two, and power-of-two plans whose
-// rows are too long for the fused poly-mul row kernel but still one kernel:
-// the plan's own transforms between element-wise pack, product and rounding
+// Poly-mul plans whose N is not a power of two (and power-of-two rows beyond
+// the fused poly-mul row kernels, should the row range outgrow them): the
+// plan's own transforms between element-wise pack, product and rounding
 // kernels.
 static bool poly_any_route(const fft_plan* p)
 {
-    // (8192-point complex128 rows run as one kernel of their own, beyond the
-    // fused poly-mul row kernel's 4096)
     return p->path == PATH_BLUESTEIN || p->path == PATH_MIXED || p->path == PATH_MIXPASS ||
            (p->path == PATH_ROWS && p->log_a > kPolyRowsMaxLog);
 }
+
+// The packed routes' exponent balance at the end of the workspace: per pair
+// kPolyExpBlocks partial maxima (int2) and the shift (int, 8 bytes kept).
+static size_t poly_shift_bytes(int64_t batch) { return (size_t)batch * (kPolyExpBlocks * 8 + 8); }
 
 int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* bytes)
 {
@@ -1556,11 +1558,13 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
     if (batch > INT64_MAX / (int64_t)(2 * plan->n * plan->elem)) return fail(FFT_ERR_INVALID_ARG, "batch too large");
     if (plan->n > (int64_t(1) << kPolyMaxLog))
         return fail(FFT_ERR_UNSUPPORTED_SIZE, "poly-mul supports N <= 2^%d", kPolyMaxLog);
-    if (poly_any_route(plan)) {  // [z: batch x N complex128][the plan's own workspace]
-        *bytes = (size_t)batch * (size_t)plan->n * plan->elem + c2c_workspace(plan, batch);
+    if (poly_any_route(plan)) {  // [z: batch x N complex128][the plan's own workspace][shifts]
+        *bytes = (size_t)batch * (size_t)plan->n * plan->elem + c2c_workspace(plan, batch) + poly_shift_bytes(batch);
         return FFT_OK;
     }
-    *bytes = plan->path == PATH_MULTIPASS ? (size_t)batch * (size_t)plan->n * plan->elem : 0;
+    // four-step: [batch x N complex128][shifts]
+    *bytes = plan->path == PATH_MULTIPASS
+                 ? (size_t)batch * (size_t)plan->n * plan->elem + poly_shift_bytes(batch) : 0;
     return FFT_OK;
 }
 
@@ -1604,12 +1608,19 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
+    // the exponent balance of the packed routes, at the workspace's end
+    void* part = ws ? (char*)workspace + ws - poly_shift_bytes(batch) : nullptr;
+    int* shift = ws ? (int*)((char*)part + (size_t)batch * kPolyExpBlocks * 8) : nullptr;
+    if (ws) {
+        e = launch_poly_shift(a, la, b, lb, batch, part, shift, s);
+        if (e != hipSuccess) return hip_fail(e, "fft_poly_mul launch");
+    }
     if (poly_any_route(plan)) {
         void* z = workspace;
         void* tws = (char*)workspace + (size_t)batch * (size_t)plan->n * plan->elem;
         const Io zio{z, nullptr, z, nullptr};
         if (d_max_residual) e = launch_zero_resid(d_max_residual, s);
-        if (e == hipSuccess) e = launch_polyany_pack(a, la, b, lb, z, plan->n, batch, s);
+        if (e == hipSuccess) e = launch_polyany_pack(a, la, b, lb, z, plan->n, batch, shift, s);
         if (e != hipSuccess) return hip_fail(e, "fft_poly_mul launch");
         st = run_1d(plan, false, zio, batch, tws, s);
         if (st != FFT_OK) return st;
@@ -1617,7 +1628,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
         if (e != hipSuccess) return hip_fail(e, "fft_poly_mul launch");
         st = run_1d(plan, true, zio, batch, tws, s);
         if (st != FFT_OK) return st;
-        e = launch_polyany_round(z, plan->n, c, lc, batch, d_max_residual, s);
+        e = launch_polyany_round(z, plan->n, c, lc, batch, shift, d_max_residual, s);
     } else if (d_max_residual && plan->path != PATH_MULTIPASS) {
         // (the four-step route clears the residual in its first kernel)
         e = launch_zero_resid(d_max_residual, s);
@@ -1626,7 +1637,7 @@ int fft_poly_mul(const fft_plan* plan, const int64_t* a, int64_t la, const int64
         if (plan->path == PATH_MULTIPASS) {
             const BigTwiddle big{plan->big_hi, plan->big_lo, plan->big_lbits, plan->logn};
             e = launch_polymul_fourstep(plan->log_a, plan->log_b, a, la, b, lb, c, batch, workspace, plan->tw_a,
-                                        plan->tw_b, plan->tw_c, big, d_max_residual, s);
+                                        plan->tw_b, plan->tw_c, big, shift, d_max_residual, s);
         } else if (plan->path == PATH_ROWS) {
             e = launch_polymul_rows(plan->log_a, a, la, b, lb, c, batch, plan->tw_a, d_max_residual, s);
         } else {

@@ -135,35 +135,44 @@ hipError_t launch_stock_pass(int prec, int logr, int kind, const void* in, void*
                              double scale, hipStream_t stream, const void* in_im = nullptr,
                              void* out_im = nullptr);
 
-// Polynomial products, N = 2^logn <= LDS range: one fused kernel per row pair
-// (raises *d_resid, which the caller clears first).
+// Polynomial products, N = 2^logn <= 8192: one fused kernel per row pair
+// (z = a + i b packed; raises *d_resid, which the caller clears first).
 hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int64_t* b, int64_t lb,
                                int64_t* c, int64_t batch, const void* tw, double* d_resid,
                                hipStream_t stream);
 
 // Polynomial products, N = 2^(logn1 + logn2) beyond the LDS range (fp64),
 // ws = batch x N complex128:
-//  A : z = a + i b -> column FFTs (length 2^logn2) + w_N^{n1 k2}    -> ws
+//  A : z = a + i 2^s b -> column FFTs (length 2^logn2) + w_N^{n1 k2} -> ws
 //  B : rows k2, N2 - k2: FFT, product spectrum, the packed spectrum of the
 //      real product's even / odd coefficients, N1/2-point FFT, twiddle -> ws
-//  A2: the N1/2 column FFTs, two coefficients per element, rint      -> c
+//  A2: the N1/2 column FFTs, two coefficients per element, 2^-s, rint -> c
+// shift: s per pair (launch_poly_shift, run first).
 // tw_half: the stage table for N1/2 points (the inverse runs at half length).
 // d_resid (may be NULL): cleared by A, raised to the largest rounding
 // residual by A2 (no separate clearing launch).
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la,
                                    const int64_t* b, int64_t lb, int64_t* c, int64_t batch,
                                    void* ws, const void* tw_row, const void* tw_col, const void* tw_half,
-                                   BigTwiddle big, double* d_resid, hipStream_t stream);
+                                   BigTwiddle big, const int* shift, double* d_resid, hipStream_t stream);
 
 // Polynomial products by a plan whose N is not a power of two: z = a + i b
 // zero padded to N (complex128, batch x N) -> the plan's forward transform ->
 // the product spectrum in place -> the plan's inverse -> rint(Re) and the
 // residual (raised; the caller clears it first).
 hipError_t launch_polyany_pack(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* z, int64_t n,
-                               int64_t batch, hipStream_t stream);
+                               int64_t batch, const int* shift, hipStream_t stream);
 hipError_t launch_polyany_product(void* z, int64_t n, int64_t batch, hipStream_t stream);
-hipError_t launch_polyany_round(const void* y, int64_t n, int64_t* c, int64_t lc, int64_t batch, double* d_resid,
-                                hipStream_t stream);
+hipError_t launch_polyany_round(const void* y, int64_t n, int64_t* c, int64_t lc, int64_t batch, const int* shift,
+                                double* d_resid, hipStream_t stream);
+
+// The exponent balance of the packed routes: shift[p] = s for pair p, the
+// difference of the binary exponents of max|a_p| and max|b_p| (0 if either
+// is all zero); z = a + i 2^s b and the outputs scaled by 2^-s.  part:
+// batch x kPolyExpBlocks int2 scratch.  Two kernels on `stream`.
+constexpr int kPolyExpBlocks = 64;
+hipError_t launch_poly_shift(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, int64_t batch,
+                             void* part, int* shift, hipStream_t stream);
 
 // The whole Bluestein transform of each row in one kernel, M = 2^logm within
 // the row kernel's range (logm <= 13 complex64, 12 complex128); tw: stage

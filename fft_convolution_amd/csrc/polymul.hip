@@ -6,10 +6,11 @@
 // Inverse transforms are evaluated as conj(F(conj(P))) / N with the forward
 // engine.
 //
-// N <= 4096: one fused kernel per pair (int64 load with implicit zero
-// padding, two forward transforms, product, third transform, the real part,
-// rint, int64 store) -- the whole product never leaves the chip.
-// N > 4096: z = a + i b as one complex signal, split N = N1 N2, with the
+// N <= 8192: one fused kernel per pair (int64 load with implicit zero
+// padding, z = a + i b transformed once, the product spectrum from the bin
+// pairs k, N - k through LDS, the inverse transform, the real part, rint,
+// int64 store) -- the whole product never leaves the chip.
+// N > 8192: z = a + i b as one complex signal, split N = N1 N2, with the
 // pointwise product fused between the forward and the inverse row transforms,
 // and the inverse at half length (the real product's even and odd
 // coefficients as one complex value, N/2 points):
@@ -131,6 +132,176 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
     resid_max(worst, d_resid);
 }
 
+// ---------------------------------------------------------------------------
+// Single-kernel product for N = 8192, packed: one forward transform of
+// z = a + i 2^s b instead of one each for a and b.  With A, B the spectra of
+// the real rows a, 2^s b, Z_k = A_k + i B_k and conj Z_{N-k} = A_k - i B_k, so
+//     A_k B_k = (Z_k^2 - conj(Z_{N-k})^2) / (4i),
+// formed after one LDS exchange that brings each thread the partner bins of
+// its own; then one inverse transform (as conj F conj / N, of which only the
+// real part is kept), the exact scaling by 2^-s and the rounding.  One row of
+// values per thread instead of two: the row fits the 128 registers of a
+// 1024-thread workgroup.
+//
+// The packed spectra carry the rounding error of |z|: where max|a| and
+// max|b| lie far apart, the smaller operand's spectrum is off by the larger
+// one's error, and the product's by about max|a|/max|b| times the unpacked
+// form's.  The power of two 2^s (s = the difference of their binary
+// exponents, per pair) puts both operands in one binade, which leaves about
+// twice the unpacked error (fp64 model, 4096 x 4096 coefficients of 2^20 and
+// 2^12: unpacked 9.8e-4, packed 2.6e-2, balanced 1.5e-3).  Shorter rows keep
+// the unpacked kernel above, whose error is that of the pages' method.
+// ---------------------------------------------------------------------------
+// The maximum of x over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ int wave_max16(int x)
+{
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, true));  // row_ror 4
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true));  // row_ror 8
+    return x;
+}
+
+// The maximum of x over the wavefront (a uniform value): rows of 16 by DPP,
+// then the four rows by lane reads.  (Lane exchanges through LDS addresses
+// would share those addresses with the residual's reduction at a kernel's
+// end and hold them in registers in between.)
+__device__ __forceinline__ int wave_max(int x)
+{
+    x = wave_max16(x);
+    return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// The shift s of the packed kernel for row pair rloc of the workgroup (T
+// consecutive threads a row; T a multiple of 64 or at most 64): the
+// difference of the binary exponents of max|a| and max|b| over the row, 0
+// where either row is all zero.  The values are integers, so the exponent
+// of frexp is 0 for zero and at least 1 otherwise; the maxima are taken over
+// those exponents.
+template <int T, int E>
+__device__ __forceinline__ int balance_shift(const double2 (&v)[E], int rloc)
+{
+    double ma = 0.0, mb = 0.0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        ma = fmax(ma, fabs(v[i].x));
+        mb = fmax(mb, fabs(v[i].y));
+    }
+    int ea = __builtin_amdgcn_frexp_exp(ma), eb = __builtin_amdgcn_frexp_exp(mb);
+    if constexpr (T >= 64) {
+        ea = wave_max(ea);
+        eb = wave_max(eb);
+    } else {
+#pragma unroll
+        for (int off = 1; off < T; off <<= 1) {
+            ea = max(ea, __shfl_xor(ea, off, 64));
+            eb = max(eb, __shfl_xor(eb, off, 64));
+        }
+    }
+    if constexpr (T > 64) {
+        static_assert(T % 64 == 0, "rows of whole wavefronts");
+        __shared__ int wmax[2][16];
+        if ((threadIdx.x & 63) == 0) {
+            wmax[0][threadIdx.x >> 6] = ea;
+            wmax[1][threadIdx.x >> 6] = eb;
+        }
+        __syncthreads();
+        const int w0 = rloc * (T / 64);
+#pragma unroll
+        for (int w = 0; w < T / 64; ++w) {
+            ea = max(ea, wmax[0][w0 + w]);
+            eb = max(eb, wmax[1][w0 + w]);
+        }
+    }
+    return ea > 0 && eb > 0 ? ea - eb : 0;
+}
+
+template <int LOGN>
+__global__ __launch_bounds__((Geom<double2, LOGN>::T * poly_rows_per_wg<LOGN>()))
+void polypack_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
+                          int64_t* __restrict__ c, int64_t batch, const double2* __restrict__ tw,
+                          double* __restrict__ d_resid)
+{
+    using G = Geom<double2, LOGN>;
+    constexpr int N = G::N, T = G::T, E = G::E;
+    constexpr int RPW = poly_rows_per_wg<LOGN>();
+    using Lds = LdsLines<double2, 1, 3>;  // one pad slot per 8 (16-byte values)
+    constexpr int SL = lds_padded(N, 3);
+    __shared__ double2 lds[SL * RPW];
+    const int tid = threadIdx.x;
+    const int rloc = tid / T, t = tid % T;
+    const int64_t pair = (int64_t)blockIdx.x * RPW + rloc;
+    const bool live = pair < batch;
+    const Lds L{lds + rloc * SL, 0};
+
+    // loads from addresses clamped into the rows (a dead group reads pair 0),
+    // the values dropped after: a load under a branch would wait alone
+    const int64_t* ar = a + (live ? pair : 0) * la;
+    const int64_t* br = b + (live ? pair : 0) * lb;
+    double2 v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int n = t + i * T;
+        const int64_t xa = *at_bytes(ar, 8u * (unsigned)(n < la ? n : la - 1));
+        const int64_t xb = *at_bytes(br, 8u * (unsigned)(n < lb ? n : lb - 1));
+        v[i] = double2{live && n < la ? (double)xa : 0.0, live && n < lb ? (double)xb : 0.0};
+    }
+    const int sh = balance_shift<T>(v, rloc);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i].y = __builtin_ldexp(v[i].y, sh);
+    {
+        // the twiddle bases are loaded again for the inverse transform rather
+        // than held in registers across the product.  Each load takes the
+        // table pointer through an empty asm statement, so that it is not
+        // hoisted above the reduction or the first transform: bases held
+        // early spill at 1024 threads.
+        const double2* tw1 = tw;
+        asm volatile("" : "+s"(tw1));
+        TwBases<double2, LOGN> tb;
+        tb.load(tw1, t);
+        fft_regs<LOGN>(v, t, tb, L);
+    }
+    __syncthreads();  // the transform's last exchange is read by now
+#pragma unroll
+    for (int i = 0; i < E; ++i) *L.ptr(t + i * T) = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int k = t + i * T;
+        const double2 zk = v[i], zq = *L.ptr((N - k) & (N - 1));
+        // s = Z_k^2 - conj(Z_q)^2; C_k = s / (4i) = (s.y / 4, -s.x / 4); the
+        // inverse transform takes conj C_k
+        const double sx = (zk.x * zk.x - zk.y * zk.y) - (zq.x * zq.x - zq.y * zq.y);
+        const double sy = 2.0 * zk.x * zk.y + 2.0 * zq.x * zq.y;
+        v[i] = double2{0.25 * sy, 0.25 * sx};
+    }
+    __syncthreads();  // partners are read before the transform reuses the LDS
+    {
+        const double2* tw2 = tw;
+        asm volatile("" : "+s"(tw2));
+        TwBases<double2, LOGN> tb;
+        tb.load(tw2, t);
+        fft_regs<LOGN>(v, t, tb, L);
+    }
+
+    const int64_t lc = la + lb - 1;
+    int64_t* cr = c + pair * lc;
+    const double inv_n = __builtin_ldexp(1.0 / (double)N, -sh);  // a power of two: exact
+    double worst = 0.0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int n = t + i * T;
+        if (live && n < lc) {
+            const double val = v[i].x * inv_n;
+            const double r = rint(val);
+            *at_bytes(cr, 8u * n) = to_int64(r);
+            worst = fmax(worst, out_residual(val, r));
+        }
+    }
+    resid_max(worst, d_resid);
+}
+
 // Tiles of the column passes A and A2: they also move int64 values (8 bytes
 // per lane), so 16 lanes per row segment make those 128-byte segments too
 // (measured on MI355X, 32 x 2^18 products: 329 -> 322 us); 1024-point columns
@@ -150,7 +321,7 @@ template <int LOGN2>
 __global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
                        double2* __restrict__ ws, int logn1, const double2* __restrict__ tw, BigTw<double2> big,
-                       double* __restrict__ d_resid)
+                       const int* __restrict__ shift, double* __restrict__ d_resid)
 {
     using G = Geom<double2, LOGN2>;
     using TL = PolyTile<LOGN2>;
@@ -163,12 +334,13 @@ void polypack_a_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t*
     const int64_t col = (tile % tps) * TL::C + c0;  // n1
     const int64_t* pa = a + pair * la;
     const int64_t* pb = b + pair * lb;
+    const int sh = shift[pair];  // z = a + i 2^s b
 
     double2 v[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
         const int64_t n = col + ((int64_t)(t + i * G::T) << logn1);
-        v[i] = double2{n < la ? (double)pa[n] : 0.0, n < lb ? (double)pb[n] : 0.0};
+        v[i] = double2{n < la ? (double)pa[n] : 0.0, n < lb ? __builtin_ldexp((double)pb[n], sh) : 0.0};
     }
     TwBases<double2, LOGN2> tb;
     tb.load(tw, t);
@@ -191,7 +363,7 @@ template <int LOGN2>
 __global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b, int64_t lb,
                             double2* __restrict__ ws, int logn1, unsigned ntiles, const double2* __restrict__ tw,
-                            BigTw<double2> big, double* __restrict__ d_resid)
+                            BigTw<double2> big, const int* __restrict__ shift, double* __restrict__ d_resid)
 {
     clear_resid(d_resid);
     using G = Geom<double2, LOGN2>;
@@ -226,9 +398,9 @@ void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int
             rb[i] = *at_bytes(pb, (unsigned)min((int64_t)n, lb - 1) * 8u);
         }
     };
-    auto value = [&](int i, unsigned n0) {
+    auto value = [&](int i, unsigned n0, int sh) {  // z = a + i 2^s b
         const int64_t n = (int64_t)(n0 + i * step);
-        return double2{n < la ? (double)ra[i] : 0.0, n < lb ? (double)rb[i] : 0.0};
+        return double2{n < la ? (double)ra[i] : 0.0, n < lb ? __builtin_ldexp((double)rb[i], sh) : 0.0};
     };
     if (blockIdx.x >= ntiles) return;  // the whole workgroup
     // a loop body of one basic block (no early exit), so that the compiler
@@ -240,9 +412,10 @@ void polypack_a_pipe_kernel(const int64_t* __restrict__ a, int64_t la, const int
         const unsigned tile = (unsigned)xcd_tile(vb, ntiles);
         const unsigned col = ((tile & ((1u << lt) - 1)) << LC) + c0;  // n1
         double2* dst = ws + ((int64_t)(tile >> lt) << (logn1 + LOGN2));
+        const int sh = shift[tile >> lt];
         double2 v[G::E];
 #pragma unroll
-        for (int i = 0; i < G::E; ++i) v[i] = i < H ? value(i, col - c0 + lane) : double2{0.0, 0.0};
+        for (int i = 0; i < G::E; ++i) v[i] = i < H ? value(i, col - c0 + lane, sh) : double2{0.0, 0.0};
         // The stage twiddle bases are loaded per tile, not held across the
         // loop (the empty asm hides that their offset is loop-invariant), and
         // before the next tile's loads: loads complete in issue order, so a
@@ -422,7 +595,7 @@ void polypack_b_kernel(double2* __restrict__ ws, int64_t ngroups, int logn2, con
 template <int LOGN2>
 __global__ __launch_bounds__((PolyTile<LOGN2>::THREADS))
 void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_out, int64_t lc, int logn1,
-                         const double2* __restrict__ tw, double* __restrict__ d_resid)
+                         const double2* __restrict__ tw, const int* __restrict__ shift, double* __restrict__ d_resid)
 {
     using G = Geom<double2, LOGN2>;
     using TL = PolyTile<LOGN2>;
@@ -441,7 +614,8 @@ void polypack_a2_kernel(const double2* __restrict__ ws, int64_t* __restrict__ c_
     tb.load(tw, t);
     fft_regs<LOGN2>(v, t, tb, LdsLines<double2, TL::CL>{lds, c0});
 
-    const double inv_n = 1.0 / (double)((int64_t)1 << (logn1 + LOGN2));
+    // 1/N and the pair's 2^-s: a power of two, exact
+    const double inv_n = __builtin_ldexp(1.0 / (double)((int64_t)1 << (logn1 + LOGN2)), -shift[pair]);
     double worst = 0.0;
     int64_t* dst = c_out + pair * lc;
 #pragma unroll
@@ -477,12 +651,94 @@ static inline dim3 pm_grid(int64_t total)
     return dim3((unsigned)(blocks > 0 ? blocks : 1));
 }
 
+// ---------------------------------------------------------------------------
+// Exponent balance of the packed routes (the four-step passes, and the plan's
+// own transforms for N not a power of two): z = a + i 2^s b, with s per pair
+// the difference of the binary exponents of max|a| and max|b|, and the
+// outputs scaled by 2^-s (both exact).  The packed spectra carry the
+// rounding error of |z|, so without it the smaller operand's spectrum -- and
+// the product -- takes the larger one's error (fp64 model, 4096 x 4096
+// coefficients of 2^26 and 2^4: error 51 unbalanced, 4.6e-5 balanced, 3.1e-5
+// with separate transforms).  Two kernels ahead of the passes: the exponents
+// of blocks of each pair's coefficients, then their maxima and s.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void polyexp_kernel(const int64_t* __restrict__ a, int64_t la,
+                                                      const int64_t* __restrict__ b, int64_t lb,
+                                                      int2* __restrict__ part, int nblk)
+{
+    const int64_t pair = blockIdx.x / nblk;
+    const int64_t blk = blockIdx.x % nblk;
+    const int64_t ca = (la + nblk - 1) / nblk, cb = (lb + nblk - 1) / nblk;
+    const int64_t* pa = a + pair * la;
+    const int64_t* pb = b + pair * lb;
+    const int64_t a0 = blk * ca, a1 = min(a0 + ca, la), b0 = blk * cb, b1 = min(b0 + cb, lb);
+    double ma = 0.0, mb = 0.0;
+    // 8 loads of each operand in flight per lane; indices past the block's
+    // end are clamped to its last coefficient (a repeat leaves the maximum
+    // as it is), so that no load waits alone under a branch
+    constexpr int U = 8;
+    for (int64_t base = 0; base < max(a1 - a0, b1 - b0); base += 256 * U) {
+        int64_t xa[U], xb[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t o = base + threadIdx.x + j * 256;
+            xa[j] = pa[min(a0 + o, a1 - 1)];
+            xb[j] = pb[min(b0 + o, b1 - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            ma = fmax(ma, fabs((double)xa[j]));
+            mb = fmax(mb, fabs((double)xb[j]));
+        }
+    }
+    if (a1 <= a0) ma = 0.0;  // an empty block reads the coefficient before it
+    if (b1 <= b0) mb = 0.0;
+    // integers: the frexp exponent is 0 for zero and at least 1 otherwise
+    const int ea = wave_max(__builtin_amdgcn_frexp_exp(ma));
+    const int eb = wave_max(__builtin_amdgcn_frexp_exp(mb));
+    __shared__ int2 w[4];
+    if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = int2{ea, eb};
+    __syncthreads();
+    if (threadIdx.x == 0)
+        part[blockIdx.x] = int2{max(max(w[0].x, w[1].x), max(w[2].x, w[3].x)),
+                                max(max(w[0].y, w[1].y), max(w[2].y, w[3].y))};
+}
+
+__global__ void polyshift_kernel(const int2* __restrict__ part, int nblk, int* __restrict__ shift, int64_t batch)
+{
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < batch; p += (int64_t)gridDim.x * blockDim.x) {
+        int ea = 0, eb = 0;
+        for (int j = 0; j < nblk; ++j) {
+            const int2 e = part[p * nblk + j];
+            ea = max(ea, e.x);
+            eb = max(eb, e.y);
+        }
+        shift[p] = ea > 0 && eb > 0 ? ea - eb : 0;
+    }
+}
+
+hipError_t launch_poly_shift(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, int64_t batch,
+                             void* part, int* shift, hipStream_t s)
+{
+    const int64_t longest = la > lb ? la : lb;
+    const int nblk = (int)std::min<int64_t>(kPolyExpBlocks, std::max<int64_t>(1, (longest + 8191) / 8192));
+    if (batch * nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(polyexp_kernel, dim3((unsigned)(batch * nblk)), dim3(256), 0, s, a, la, b, lb, (int2*)part,
+                       nblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(polyshift_kernel, pm_grid(batch), dim3(256), 0, s, (const int2*)part, nblk, shift, batch);
+    return hipGetLastError();
+}
+
 __global__ void polyany_pack_kernel(const int64_t* __restrict__ a, int64_t la, const int64_t* __restrict__ b,
-                                    int64_t lb, double2* __restrict__ z, int64_t n, int64_t total)
+                                    int64_t lb, double2* __restrict__ z, int64_t n, int64_t total,
+                                    const int* __restrict__ shift)
 {
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = e / n, k = e - p * n;
-        z[e] = double2{k < la ? (double)a[p * la + k] : 0.0, k < lb ? (double)b[p * lb + k] : 0.0};
+        z[e] = double2{k < la ? (double)a[p * la + k] : 0.0,
+                       k < lb ? __builtin_ldexp((double)b[p * lb + k], shift[p]) : 0.0};  // a + i 2^s b
     }
 }
 
@@ -503,12 +759,12 @@ __global__ void polyany_product_kernel(double2* __restrict__ z, int64_t n, int64
 }
 
 __global__ void polyany_round_kernel(const double2* __restrict__ y, int64_t n, int64_t* __restrict__ c, int64_t lc,
-                                     int64_t total, double* __restrict__ d_resid)
+                                     int64_t total, const int* __restrict__ shift, double* __restrict__ d_resid)
 {
     double worst = 0.0;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = e / lc, k = e - p * lc;
-        const double val = y[p * n + k].x, r = rint(val);
+        const double val = __builtin_ldexp(y[p * n + k].x, -shift[p]), r = rint(val);
         c[e] = to_int64(r);
         worst = fmax(worst, out_residual(val, r));
     }
@@ -516,10 +772,11 @@ __global__ void polyany_round_kernel(const double2* __restrict__ y, int64_t n, i
 }
 
 hipError_t launch_polyany_pack(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* z, int64_t n,
-                               int64_t batch, hipStream_t s)
+                               int64_t batch, const int* shift, hipStream_t s)
 {
     const int64_t total = batch * n;
-    hipLaunchKernelGGL(polyany_pack_kernel, pm_grid(total), dim3(256), 0, s, a, la, b, lb, (double2*)z, n, total);
+    hipLaunchKernelGGL(polyany_pack_kernel, pm_grid(total), dim3(256), 0, s, a, la, b, lb, (double2*)z, n, total,
+                       shift);
     return hipGetLastError();
 }
 
@@ -530,12 +787,12 @@ hipError_t launch_polyany_product(void* z, int64_t n, int64_t batch, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_polyany_round(const void* y, int64_t n, int64_t* c, int64_t lc, int64_t batch, double* d_resid,
-                                hipStream_t s)
+hipError_t launch_polyany_round(const void* y, int64_t n, int64_t* c, int64_t lc, int64_t batch, const int* shift,
+                                double* d_resid, hipStream_t s)
 {
     const int64_t total = batch * lc;
     hipLaunchKernelGGL(polyany_round_kernel, pm_grid(total), dim3(256), 0, s, (const double2*)y, n, c, lc, total,
-                       d_resid);
+                       shift, d_resid);
     return hipGetLastError();
 }
 
@@ -560,6 +817,18 @@ static hipError_t polymul_rows_t(const int64_t* a, int64_t la, const int64_t* b,
     return hipGetLastError();
 }
 
+template <int LOGN>
+static hipError_t polypack_rows_t(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, int64_t* c,
+                                  int64_t batch, const void* tw, double* d_resid, hipStream_t s)
+{
+    constexpr int RPW = poly_rows_per_wg<LOGN>();
+    const int64_t blocks = (batch + RPW - 1) / RPW;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((polypack_rows_kernel<LOGN>), dim3((unsigned)blocks), dim3(Geom<double2, LOGN>::T * RPW), 0,
+                       s, a, la, b, lb, c, batch, (const double2*)tw, d_resid);
+    return hipGetLastError();
+}
+
 hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, int64_t* c,
                                int64_t batch, const void* tw, double* d_resid, hipStream_t s)
 {
@@ -567,6 +836,7 @@ hipError_t launch_polymul_rows(int logn, const int64_t* a, int64_t la, const int
 #define PR(L) case L: return polymul_rows_t<L>(a, la, b, lb, c, batch, tw, d_resid, s);
         PR(1) PR(2) PR(3) PR(4) PR(5) PR(6) PR(7) PR(8) PR(9) PR(10) PR(11) PR(12)
 #undef PR
+        case 13: return polypack_rows_t<13>(a, la, b, lb, c, batch, tw, d_resid, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -588,7 +858,8 @@ static int64_t pipe_grid()
 
 template <int LOGN2>
 static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const int64_t* b, int64_t lb, void* ws,
-                               int64_t batch, const void* tw_col, BigTw<double2> big, double* d_resid, hipStream_t s)
+                               int64_t batch, const void* tw_col, BigTw<double2> big, const int* shift,
+                               double* d_resid, hipStream_t s)
 {
     using TL = PolyTile<LOGN2>;
     const int64_t n1 = (int64_t)1 << logn1;
@@ -603,12 +874,13 @@ static hipError_t polypack_a_t(int logn1, const int64_t* a, int64_t la, const in
         if (la <= half && lb <= half) {
             const int64_t grid = std::min<int64_t>(blocks, pipe_grid());
             hipLaunchKernelGGL((polypack_a_pipe_kernel<LOGN2>), dim3((unsigned)grid), dim3(TL::THREADS), 0, s, a, la,
-                               b, lb, (double2*)ws, logn1, (unsigned)blocks, (const double2*)tw_col, big, d_resid);
+                               b, lb, (double2*)ws, logn1, (unsigned)blocks, (const double2*)tw_col, big, shift,
+                               d_resid);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((polypack_a_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s, a, la, b, lb,
-                       (double2*)ws, logn1, (const double2*)tw_col, big, d_resid);
+                       (double2*)ws, logn1, (const double2*)tw_col, big, shift, d_resid);
     return hipGetLastError();
 }
 
@@ -627,7 +899,7 @@ static hipError_t polypack_b_t(int logn2, void* ws, int64_t batch, const void* t
 
 template <int LOGN2>
 static hipError_t polypack_a2_t(int logn1, const void* ws, int64_t* c, int64_t lc, int64_t batch,
-                                 const void* tw_col, double* d_resid, hipStream_t s)
+                                 const void* tw_col, const int* shift, double* d_resid, hipStream_t s)
 {
     using TL = PolyTile<LOGN2>;
     const int64_t h1 = (int64_t)1 << (logn1 - 1);
@@ -635,13 +907,14 @@ static hipError_t polypack_a2_t(int logn1, const void* ws, int64_t* c, int64_t l
     const int64_t blocks = batch * (h1 / TL::C);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((polypack_a2_kernel<LOGN2>), dim3((unsigned)blocks), dim3(TL::THREADS), 0, s,
-                       (const double2*)ws, c, lc, logn1, (const double2*)tw_col, d_resid);
+                       (const double2*)ws, c, lc, logn1, (const double2*)tw_col, shift, d_resid);
     return hipGetLastError();
 }
 
 hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64_t la, const int64_t* b, int64_t lb,
                                    int64_t* c, int64_t batch, void* ws, const void* tw_row, const void* tw_col,
-                                   const void* tw_half, BigTwiddle bigt, double* d_resid, hipStream_t s)
+                                   const void* tw_half, BigTwiddle bigt, const int* shift, double* d_resid,
+                                   hipStream_t s)
 {
     const BigTw<double2> big{(const double2*)bigt.hi, (const double2*)bigt.lo, bigt.lbits, bigt.logn};
     // the half-length inverse: rows of N1/2 points in B, whose N1/2 columns
@@ -657,7 +930,7 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
         return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     switch (logn2) {
-#define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, d_resid, s); break;
+#define PA(L) case L: e = polypack_a_t<L>(logn1, a, la, b, lb, ws, batch, tw_col, big, shift, d_resid, s); break;
         PA(5) PA(6) PA(7) PA(8) PA(9) PA(10)
 #undef PA
         default: return hipErrorInvalidValue;
@@ -672,7 +945,7 @@ hipError_t launch_polymul_fourstep(int logn1, int logn2, const int64_t* a, int64
     if (e != hipSuccess) return e;
     const int64_t lc = la + lb - 1;
     switch (logn2) {
-#define PA2(L) case L: e = polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, d_resid, s); break;
+#define PA2(L) case L: e = polypack_a2_t<L>(logn1, ws, c, lc, batch, tw_col, shift, d_resid, s); break;
         PA2(5) PA2(6) PA2(7) PA2(8) PA2(9) PA2(10)
 #undef PA2
         default: return hipErrorInvalidValue;

@@ -269,15 +269,23 @@ int fft_poly_mul_workspace_size(const fft_plan* plan, int64_t batch, size_t* byt
  * product, inverse FFT (scaled 1/N), round the real part to the nearest
  * integer (ties to even).
  *   plan:  rank 1, FFT_C64, N >= la + lb - 1, N <= 2^22.  N a power of two:
- *          the fused kernels (one per row pair within the LDS, else three
- *          four-step passes).  Any other N: the plan's own transforms (mixed
- *          radix or chirp-z, "FFT on GPU", section "Algorithm per signal
- *          Length") between three element-wise kernels -- z = a + i b zero
- *          padded to N, the forward transform, the product spectrum
+ *          the fused kernels (one per row pair: a and b transformed apart up
+ *          to N = 4096; for N = 8192 z = a + i b transformed once, the
+ *          product spectrum from the bin pairs k and N - k, the inverse;
+ *          beyond, three four-step passes on z).  Any other N: the plan's
+ *          own transforms (mixed radix or chirp-z, "FFT on GPU", section
+ *          "Algorithm per signal Length") between element-wise kernels --
+ *          z zero padded to N, the forward transform, the product spectrum
  *          (Z_k^2 - conj(Z_{-k})^2) / 4i in place, the inverse, rint.
+ *          Wherever a and b are packed into z, b is scaled by 2^s first and
+ *          the outputs by 2^-s (exact), s = the difference of the binary
+ *          exponents of max|a| and max|b| per pair, so that operands of
+ *          unlike magnitudes keep the rounding error of separate transforms.
  *   a:     [batch][la] int64;  b: [batch][lb] int64;  c: [batch][la+lb-1] int64.
  *          c must not overlap a, b or the workspace.
- *   workspace: fft_poly_mul_workspace_size(plan, batch) bytes.
+ *   workspace: fft_poly_mul_workspace_size(plan, batch) bytes (none for
+ *          N <= 8192 powers of two; else the transforms' space plus 520
+ *          bytes per pair for the exponent balance).
  *   d_max_residual: NULL, or a device double that receives
  *          max |Re(y)/N - rint(Re(y)/N)| over all outputs (overwritten, not
  *          accumulated), or +infinity if any output has |Re(y)/N| >= 2^53 or

@@ -46,7 +46,9 @@ def test_small_exact(dev, la, lb, batch):
 
 @pytest.mark.parametrize("la,lb,n,batch", [
     (3000, 1097, 4096, 2),     # LDS-resident, largest fp64 row
-    (4096, 4097, 8192, 2),     # 8192-point rows in one kernel, the general route
+    (4096, 4097, 8192, 2),     # 8192 points: the packed one-kernel product (1024 threads)
+    (1, 8192, 8192, 3),        # b filling the row, a one coefficient
+    (5000, 700, 8192, 5),      # ragged, a longer than N/2
     (8192, 8193, 16384, 2),    # smallest four-step
     (5000, 3000, 16384, 3),    # four-step, ragged lengths
     (1 << 15, 1 << 15, 1 << 16, 2),
@@ -94,6 +96,30 @@ def test_random_split_sizes(dev, logn):
     ref, _ = oracle.polymul_fft(a, b, n=n)
     assert np.array_equal(c, ref)
     assert resid < 0.1
+
+
+@pytest.mark.parametrize("n", [8192, 16384, 1 << 17, 12288, 10006])
+def test_unbalanced_operands(dev, n):
+    """Coefficients of 2^26 against 2^4: the packed routes (z = a + i b) give
+    the smaller operand the larger one's rounding error unless b is scaled
+    to a's binade first (fp64 model at N = 8192: error 51 unscaled, 5e-5
+    scaled).  Every packed route: one kernel (8192), four-step passes (16384,
+    2^17 with the pipelined pass A), mixed radix (12288) and chirp-z (10006)
+    transforms between element-wise kernels.  Exact against the oracle's
+    separate transforms, and both ways round (a small, b large)."""
+    print("case unbalanced n=%d" % n, flush=True)
+    rng = np.random.default_rng(n)
+    la = lb = n // 2
+    big = rng.integers(-(1 << 26), 1 << 26, size=(2, la))
+    small = rng.integers(-(1 << 4), 1 << 4, size=(2, lb))
+    oracle.set_threads(8)
+    for a, b in ((big, small), (small, big)):
+        c, resid = _gpu_mul(a, b, n, dev)
+        ref, _ = oracle.polymul_fft(a, b)  # (the oracle's own power-of-two length)
+        assert np.array_equal(c, ref)
+        ks = np.unique(np.concatenate([[0, la + lb - 2], rng.integers(0, la + lb - 1, 30)]))
+        assert np.array_equal(c[:, ks], oracle.schoolbook_sample(a, b, ks))
+        assert resid < 0.1, resid
 
 
 def test_closed_forms(dev):
@@ -150,12 +176,12 @@ def test_validation_on_device(dev):
     fm.fft_poly_mul(plan.handle, a, 20, b, 30, c, 0)        # batch 0: no-op
 
 
-@pytest.mark.parametrize("n", [64, 8192])
+@pytest.mark.parametrize("n", [64, 8192, 16384])
 def test_residual_flags_results_past_2p53(dev, n):
     """Products of at least 2^53 cannot be vouched for by the rounding
     residual (every double there is an integer): the residual must then read
-    +inf, and values beyond int64 come back as INT64_MIN.  Both the one-kernel
-    route (N = 64) and the split route (N = 8192)."""
+    +inf, and values beyond int64 come back as INT64_MIN.  The one-kernel
+    routes (N = 64, and N = 8192 packed) and the split route (N = 16384)."""
     print("case residual flag n=%d" % n, flush=True)
     plan = fm.Plan(n, torch.complex128)
     resid = torch.full((1,), -1.0, dtype=torch.float64, device=dev)
