@@ -660,7 +660,8 @@ static inline dim3 pm_grid(int64_t total)
 // the product -- takes the larger one's error (fp64 model, 4096 x 4096
 // coefficients of 2^26 and 2^4: error 51 unbalanced, 4.6e-5 balanced, 3.1e-5
 // with separate transforms).  Two kernels ahead of the passes: the exponents
-// of blocks of each pair's coefficients, then their maxima and s.
+// of blocks of 4096 coefficients (at most 64 blocks a pair), then their
+// maxima and s.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void polyexp_kernel(const int64_t* __restrict__ a, int64_t la,
                                                       const int64_t* __restrict__ b, int64_t lb,
@@ -673,10 +674,11 @@ __global__ __launch_bounds__(256) void polyexp_kernel(const int64_t* __restrict_
     const int64_t* pb = b + pair * lb;
     const int64_t a0 = blk * ca, a1 = min(a0 + ca, la), b0 = blk * cb, b1 = min(b0 + cb, lb);
     double ma = 0.0, mb = 0.0;
-    // 8 loads of each operand in flight per lane; indices past the block's
-    // end are clamped to its last coefficient (a repeat leaves the maximum
-    // as it is), so that no load waits alone under a branch
-    constexpr int U = 8;
+    // 16 loads of each operand in flight per lane (a block of 4096 takes one
+    // round); indices past the block's end are clamped to its last
+    // coefficient (a repeat leaves the maximum as it is), so that no load
+    // waits alone under a branch
+    constexpr int U = 16;
     for (int64_t base = 0; base < max(a1 - a0, b1 - b0); base += 256 * U) {
         int64_t xa[U], xb[U];
 #pragma unroll
@@ -704,30 +706,31 @@ __global__ __launch_bounds__(256) void polyexp_kernel(const int64_t* __restrict_
                                 max(max(w[0].y, w[1].y), max(w[2].y, w[3].y))};
 }
 
-__global__ void polyshift_kernel(const int2* __restrict__ part, int nblk, int* __restrict__ shift, int64_t batch)
+// One wavefront per pair: lane j takes block j's exponents (nblk <= 64).
+__global__ __launch_bounds__(256) void polyshift_kernel(const int2* __restrict__ part, int nblk,
+                                                        int* __restrict__ shift, int64_t batch)
 {
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < batch; p += (int64_t)gridDim.x * blockDim.x) {
-        int ea = 0, eb = 0;
-        for (int j = 0; j < nblk; ++j) {
-            const int2 e = part[p * nblk + j];
-            ea = max(ea, e.x);
-            eb = max(eb, e.y);
-        }
-        shift[p] = ea > 0 && eb > 0 ? ea - eb : 0;
-    }
+    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int j = threadIdx.x & 63;
+    const bool in = p < batch && j < nblk;
+    const int2 e = part[in ? p * nblk + j : 0];
+    const int ea = wave_max(in ? e.x : 0), eb = wave_max(in ? e.y : 0);
+    if (j == 0 && p < batch) shift[p] = ea > 0 && eb > 0 ? ea - eb : 0;
 }
 
 hipError_t launch_poly_shift(const int64_t* a, int64_t la, const int64_t* b, int64_t lb, int64_t batch,
                              void* part, int* shift, hipStream_t s)
 {
     const int64_t longest = la > lb ? la : lb;
-    const int nblk = (int)std::min<int64_t>(kPolyExpBlocks, std::max<int64_t>(1, (longest + 8191) / 8192));
+    const int nblk = (int)std::min<int64_t>(kPolyExpBlocks, std::max<int64_t>(1, (longest + 4095) / 4096));
     if (batch * nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(polyexp_kernel, dim3((unsigned)(batch * nblk)), dim3(256), 0, s, a, la, b, lb, (int2*)part,
                        nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(polyshift_kernel, pm_grid(batch), dim3(256), 0, s, (const int2*)part, nblk, shift, batch);
+    if ((batch + 3) / 4 > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(polyshift_kernel, dim3((unsigned)((batch + 3) / 4)), dim3(256), 0, s, (const int2*)part, nblk,
+                       shift, batch);
     return hipGetLastError();
 }
 
