@@ -939,6 +939,10 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
                             (long long)kBluesteinMax);
         }
     }
+    // the innermost axis of length > 1: its rows may take the one-kernel rows
+    // of twice the LDS range; the other axes run as columns
+    int inner = rank - 1;
+    while (inner > 0 && dims[inner] == 1) --inner;
     for (int d = 0; d < rank; ++d) {
         if (!is_pow2(dims[d])) {
             if (rank > 1) continue;
@@ -947,7 +951,7 @@ static int plan_prepare(fft_plan* p, int rank, const int64_t* dims, int prec)
                             (long long)dims[d], (long long)kBluesteinMax);
             continue;
         }
-        const int64_t lim = rank == 1 || !all_pow2 ? max_n(prec) : max_lds_n(prec);
+        const int64_t lim = rank == 1 || !all_pow2 ? max_n(prec) : d == inner ? big_row_n(prec) : max_lds_n(prec);
         if (dims[d] > lim)
             return fail(FFT_ERR_UNSUPPORTED_SIZE, "dims[%d] = %lld exceeds %lld", d, (long long)dims[d],
                         (long long)lim);

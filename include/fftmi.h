@@ -107,7 +107,10 @@ enum fft_status {
  *             M-point plan.
  *   rank 2: dims = {H, W}, row-major with W contiguous ("Stockham FFT ... in
  *           Parallel GLSL", section "Multi-Dimensional Transforms and
- *           Separability": rows, then columns); 1 <= H, W <= FFT_MAX_LDS_N_*.
+ *           Separability": rows, then columns); 1 <= H <= FFT_MAX_LDS_N_*,
+ *           1 <= W <= 2 FFT_MAX_LDS_N_* (rows of 16384 C32 / 8192 C64 take
+ *           the one-kernel rows of one 1024-thread workgroup each; only the
+ *           innermost axis longer than 1 may exceed FFT_MAX_LDS_N_*).
  *           Columns longer than 512 points are split H = F * Lc: the radix-F
  *           column stage is folded into the row pass, or, where F rows of
  *           W points do not fit one workgroup's LDS (e.g. 8192 x 8192

@@ -83,11 +83,12 @@ def _create_status(rank, dims, prec):
     (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 25], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [8, 16384], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),  # rows beyond 8192 (complex128)
     (3, [0, 8, 8], 0, fm.FFT_ERR_INVALID_ARG),
     (3, [4096, 8, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # depth beyond the column-pass range
     (3, [2048, 8, 8], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (3, [8, 8, 16384], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (3, [8, 8, 32768], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),  # rows beyond 16384 (complex64)
+    (3, [8, 16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
 ])
 def test_plan_create_rejects(rank, dims, prec, status):
     st, h = _create_status(rank, dims, prec)

@@ -23,6 +23,8 @@ def _flat(a):
     (32, 64, 3), (64, 32, 2), (8, 8192, 1), (8192, 8, 1), (128, 256, 2), (512, 512, 1),
     (1024, 64, 1), (2048, 2048, 1),
     (8192, 4, 1), (4096, 8192, 1),   # 2048-point column passes (the cap)
+    # rows of 16384 (one 1024-thread workgroup a row), short to the cap
+    (1, 16384, 2), (2, 16384, 2), (64, 16384, 1), (1024, 16384, 1), (8192, 16384, 1),
 ])
 def test_fft2_c64(dev, h, w, batch):
     print("case h=%d w=%d batch=%d" % (h, w, batch), flush=True)
@@ -39,7 +41,8 @@ def test_fft2_c64(dev, h, w, batch):
 
 @pytest.mark.parametrize("h,w,batch", [(1, 8, 2), (8, 1, 2), (16, 32, 3), (256, 128, 2), (4096, 16, 1),
                                        (16, 4096, 1), (1024, 1024, 1),
-                                       (2048, 2, 2), (4096, 4, 1), (4096, 2048, 1)])  # 1024-point columns
+                                       (2048, 2, 2), (4096, 4, 1), (4096, 2048, 1),  # 1024-point columns
+                                       (2, 8192, 2), (512, 8192, 1), (4096, 8192, 1)])  # rows of 8192
 def test_fft2_c128(dev, h, w, batch):
     x_np = wl.batched_uniform(h * w, batch, seed=h * 17 + w, dtype=np.complex128).reshape(batch, h, w)
     plan = fm.Plan((h, w), torch.complex128)

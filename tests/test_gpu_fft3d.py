@@ -22,6 +22,7 @@ def _flat(a):
 @pytest.mark.parametrize("d,h,w,batch", [
     (1, 1, 1, 2), (1, 4, 8, 2), (8, 1, 1, 3), (8, 1, 16, 2), (8, 16, 1, 2), (2, 2, 2, 1), (16, 8, 32, 2),
     (64, 64, 64, 1), (128, 16, 8, 1), (4, 2048, 16, 1), (2048, 4, 4, 1), (8, 8, 4096, 1), (32, 256, 128, 1),
+    (2, 4, 16384, 2), (16, 1, 16384, 1),   # rows of 16384
 ])
 def test_fft3_c64(dev, d, h, w, batch):
     print("case d=%d h=%d w=%d batch=%d" % (d, h, w, batch), flush=True)
@@ -36,7 +37,8 @@ def test_fft3_c64(dev, d, h, w, batch):
         assert err.max() <= fft_tol(d * h * w), (inverse, err.max())
 
 
-@pytest.mark.parametrize("d,h,w,batch", [(4, 8, 16, 2), (16, 1024, 8, 1), (1024, 4, 4, 1), (8, 32, 2048, 1)])
+@pytest.mark.parametrize("d,h,w,batch", [(4, 8, 16, 2), (16, 1024, 8, 1), (1024, 4, 4, 1), (8, 32, 2048, 1),
+                                         (4, 8, 8192, 1)])
 def test_fft3_c128(dev, d, h, w, batch):
     x_np = wl.batched_normal(d * h * w, batch, seed=d + h + w, dtype=np.complex128).reshape(batch, d, h, w)
     plan = fm.Plan((d, h, w), torch.complex128)

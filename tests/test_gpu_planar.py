@@ -93,7 +93,8 @@ def test_planar_equals_interleaved(dev, dims, dtype, batch):
 
 @pytest.mark.parametrize("dims,dtype", [((4096,), torch.complex64), ((1 << 18,), torch.complex128),
                                         ((999,), torch.complex64), ((1001,), torch.complex64),
-                                        ((128, 256), torch.complex64)])
+                                        ((128, 256), torch.complex64), ((16, 16384), torch.complex64),
+                                        ((8, 8192), torch.complex128)])
 def test_planar_against_oracle(dev, dims, dtype):
     n = int(np.prod(dims))
     npdt = np.complex64 if dtype == torch.complex64 else np.complex128

@@ -119,7 +119,10 @@ def test_3d_layouts():
     (2, [(1 << 23) + 1, 2], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [(1 << 23) + 1], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
     (1, [1 << 27], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
-    (2, [8, 8192], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),
+    (2, [8, 16384], 1, fm.FFT_ERR_UNSUPPORTED_SIZE),   # rows beyond 8192 (complex128)
+    (2, [8, 32768], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # rows beyond 16384 (complex64)
+    (2, [16384, 8], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),   # an outer axis beyond 8192
+    (3, [4, 16384, 4], 0, fm.FFT_ERR_UNSUPPORTED_SIZE),
 ])
 def test_query_rejects_as_create_does(rank, dims, prec, status):
     with pytest.raises(fm.FFTError) as e:
