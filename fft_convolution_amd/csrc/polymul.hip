@@ -706,6 +706,36 @@ __global__ __launch_bounds__(256) void polyexp_kernel(const int64_t* __restrict_
                                 max(max(w[0].y, w[1].y), max(w[2].y, w[3].y))};
 }
 
+// Pairs of at most 1024 coefficients an operand: one wavefront a pair, 16
+// loads in flight per lane, part[pair] its exponents (one block a pair), so
+// that large batches of short products do not take a workgroup each.
+__global__ __launch_bounds__(256) void polyexp_small_kernel(const int64_t* __restrict__ a, int64_t la,
+                                                            const int64_t* __restrict__ b, int64_t lb,
+                                                            int2* __restrict__ part, int64_t batch)
+{
+    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t pc = pair < batch ? pair : batch - 1;  // the whole wave stays active
+    const int64_t* pa = a + pc * la;
+    const int64_t* pb = b + pc * lb;
+    const int j = (int)(threadIdx.x & 63);
+    constexpr int U = 16;
+    int64_t xa[U], xb[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        xa[i] = pa[min((int64_t)(j + 64 * i), la - 1)];
+        xb[i] = pb[min((int64_t)(j + 64 * i), lb - 1)];
+    }
+    double ma = 0.0, mb = 0.0;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        ma = fmax(ma, fabs((double)xa[i]));
+        mb = fmax(mb, fabs((double)xb[i]));
+    }
+    const int ea = wave_max(__builtin_amdgcn_frexp_exp(ma));
+    const int eb = wave_max(__builtin_amdgcn_frexp_exp(mb));
+    if (j == 0 && pair < batch) part[pair] = int2{ea, eb};
+}
+
 // One wavefront per pair: lane j takes block j's exponents (nblk <= 64).
 __global__ __launch_bounds__(256) void polyshift_kernel(const int2* __restrict__ part, int nblk,
                                                         int* __restrict__ shift, int64_t batch)
@@ -724,8 +754,12 @@ hipError_t launch_poly_shift(const int64_t* a, int64_t la, const int64_t* b, int
     const int64_t longest = la > lb ? la : lb;
     const int nblk = (int)std::min<int64_t>(kPolyExpBlocks, std::max<int64_t>(1, (longest + 4095) / 4096));
     if (batch * nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(polyexp_kernel, dim3((unsigned)(batch * nblk)), dim3(256), 0, s, a, la, b, lb, (int2*)part,
-                       nblk);
+    if (la <= 1024 && lb <= 1024)  // (nblk is 1)
+        hipLaunchKernelGGL(polyexp_small_kernel, dim3((unsigned)((batch + 3) / 4)), dim3(256), 0, s, a, la, b, lb,
+                           (int2*)part, batch);
+    else
+        hipLaunchKernelGGL(polyexp_kernel, dim3((unsigned)(batch * nblk)), dim3(256), 0, s, a, la, b, lb,
+                           (int2*)part, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((batch + 3) / 4 > 0x7fffffff) return hipErrorInvalidConfiguration;
