@@ -98,23 +98,37 @@ void polymul_rows_kernel(const int64_t* __restrict__ a, int64_t la, const int64_
     const int64_t pair = (int64_t)blockIdx.x * RPW + rloc;
     const bool live = pair < batch;
     const LdsLines<double2, 1> at{lds + rloc * G::LDS, 0};
-    TwBases<double2, LOGN> tb;
-    tb.load(tw, t);
+    // each transform loads the twiddle bases anew, through a pointer passed
+    // through an empty asm statement so that the loads are not hoisted and
+    // held across the other transforms
+    auto transform = [&](double2 (&v)[G::E]) {
+        const double2* twp = tw;
+        asm volatile("" : "+s"(twp));
+        TwBases<double2, LOGN> tb;
+        tb.load(twp, t);
+        fft_regs<LOGN>(v, t, tb, at);
+    };
 
+    // loads from addresses clamped into the rows (a dead row reads pair 0),
+    // the values dropped after: a load under a branch would wait alone
+    const int64_t* ar = a + (live ? pair : 0) * la;
+    const int64_t* br = b + (live ? pair : 0) * lb;
     double2 va[G::E], vb[G::E];
 #pragma unroll
     for (int i = 0; i < G::E; ++i) {
         const int n = t + i * G::T;
-        va[i] = double2{(live && n < la) ? (double)a[pair * la + n] : 0.0, 0.0};
-        vb[i] = double2{(live && n < lb) ? (double)b[pair * lb + n] : 0.0, 0.0};
+        const int64_t xa = *at_bytes(ar, 8u * (unsigned)(n < la ? n : la - 1));
+        const int64_t xb = *at_bytes(br, 8u * (unsigned)(n < lb ? n : lb - 1));
+        va[i] = double2{live && n < la ? (double)xa : 0.0, 0.0};
+        vb[i] = double2{live && n < lb ? (double)xb : 0.0, 0.0};
     }
-    fft_regs<LOGN>(va, t, tb, at);
+    transform(va);
     if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN>(vb, t, tb, at);
+    transform(vb);
 #pragma unroll
     for (int i = 0; i < G::E; ++i) va[i] = cconj(cmul(va[i], vb[i]));
     if constexpr (G::S > 1) __syncthreads();
-    fft_regs<LOGN>(va, t, tb, at);
+    transform(va);
 
     const int64_t lc = la + lb - 1;
     const double inv_n = 1.0 / (double)G::N;
