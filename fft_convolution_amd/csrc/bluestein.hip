@@ -119,8 +119,12 @@ void bluestein_rows_kernel(CIn<V, PL> in, COut<V, PL> out, int64_t nrows, int n,
     for (int i = 0; i < G::E; ++i) v[i] = cconj(cmul_pinned(v[i], bspec[t + i * G::T]));
     L.sync();  // the forward transform's last exchange is read by now
     {
+        // the table pointer through an empty asm statement: these loads are
+        // not hoisted above the forward transform and held across it
+        const V* tw2 = tw;
+        asm volatile("" : "+s"(tw2));
         TwBases<V, LOGM> tb;
-        tb.load(tw, t);
+        tb.load(tw2, t);
         fft_regs<LOGM>(v, t, tb, L);
     }
     const Rl inv_m = (Rl)1 / (Rl)(1 << LOGM);
